@@ -1,0 +1,135 @@
+"""Naive float64 attention over packed documents: forward and exact gradient.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring). Plain NumPy, float64, explicit mask.
+
+Layout: packed tokens × heads × head-dim, row-major. ``q`` is ``[T, hq, d]``; ``k`` and ``v``
+are ``[T, hkv, d]``. Document ``n`` owns packed rows ``cu_seqlens[n] .. cu_seqlens[n+1]-1``;
+attention never crosses a document boundary (document-local, packed layout: FLAMIA page,
+"FLAMIA Mimarisi ve Temel Tasarım İlkeleri"). Query head ``h`` reads kv head
+``h // (hq // hkv)`` (consecutive query heads share a kv head).
+"""
+
+import numpy as np
+
+ROW_BLOCK = 512  # query rows per explicit score block (memory bound only; rows are independent)
+
+
+def _check(q, k, v, cu_seqlens):
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T, hq, d = q.shape
+    assert k.shape[0] == T and v.shape[0] == T and k.shape == v.shape and k.shape[2] == d
+    hkv = k.shape[1]
+    assert hq % hkv == 0
+    assert cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0)
+    return q, k, v, cu, T, hq, hkv, d
+
+
+def causal_mask(n_rows, row0, n_cols, causal):
+    """Explicit additive mask: 0 where key j may be seen by query i, -inf where j > i.
+
+    "GPT Kernel Programlama" §4: a query must not see later tokens, so their scores are set to
+    minus infinity before the softmax. ``i`` and ``j`` are document-local indices; ``row0`` is
+    the first query row of the block.
+    """
+    m = np.zeros((n_rows, n_cols), dtype=np.float64)
+    if causal:
+        i = (row0 + np.arange(n_rows))[:, None]
+        j = np.arange(n_cols)[None, :]
+        m[j > i] = -np.inf
+    return m
+
+
+def _probabilities(qb, kd, scale, row0, causal):
+    """Scores, explicit mask and the two-pass (max, then sum) softmax of one row block.
+
+    "GPT Kernel Programlama" §3 (S = Q·Kᵀ/√d, here with the scale passed in), §4 (mask),
+    §5 (subtract the row maximum, exponentiate, divide by the row sum).
+    Returns P and the row log-sum-exp m + ln(l) of the masked, scaled scores.
+    """
+    s = scale * (qb @ kd.T)
+    z = s + causal_mask(qb.shape[0], row0, kd.shape[0], causal)
+    m = z.max(axis=1)
+    e = np.exp(z - m[:, None])
+    l = e.sum(axis=1)
+    p = e / l[:, None]
+    return p, m + np.log(l)
+
+
+def attn_fwd(q, k, v, cu_seqlens, scale, causal=True, row_block=ROW_BLOCK):
+    """Forward pass: O = softmax(scale·QKᵀ + mask)·V per document and head; also LSE.
+
+    "GPT Kernel Programlama" §2 (the three equations), §6 (O[i,r] = Σ_j P[i,j]·V[j,r]);
+    "FlashAttention (HU)", "A szabványos attention problematikája" (softmax(QKᵀ/√d_k)V).
+
+    Returns ``o [T, hq, d]`` and ``lse [hq, T]`` (natural log of Σ_j exp(scaled masked score)).
+    Rows of empty documents do not exist; a packed token belongs to exactly one document.
+    """
+    q, k, v, cu, T, hq, hkv, d = _check(q, k, v, cu_seqlens)
+    group = hq // hkv
+    o = np.zeros((T, hq, d), dtype=np.float64)
+    lse = np.zeros((hq, T), dtype=np.float64)
+    for n in range(len(cu) - 1):
+        s0, s1 = int(cu[n]), int(cu[n + 1])
+        L = s1 - s0
+        if L == 0:
+            continue
+        for h in range(hq):
+            g = h // group
+            kd = k[s0:s1, g, :]
+            vd = v[s0:s1, g, :]
+            for r0 in range(0, L, row_block):
+                r1 = min(L, r0 + row_block)
+                p, rl = _probabilities(q[s0 + r0:s0 + r1, h, :], kd, scale, r0, causal)
+                o[s0 + r0:s0 + r1, h, :] = p @ vd
+                lse[h, s0 + r0:s0 + r1] = rl
+    return o, lse
+
+
+def attn_bwd(q, k, v, do, cu_seqlens, scale, causal=True, row_block=ROW_BLOCK):
+    """Exact gradient of ``attn_fwd`` for an upstream gradient ``do`` (no LSE gradient).
+
+    The pages only name the backward pass (FLAMIA page, "FLAMIA Mimarisi ve Temel Tasarım
+    İlkeleri": forward and backward must agree numerically); these are the derivatives of the
+    forward definition above, with the oracle's own float64 O and P:
+
+        D_i    = Σ_r dO[i,r]·O[i,r]
+        dP_ij  = Σ_r dO[i,r]·V[j,r]
+        dS_ij  = P_ij·(dP_ij − D_i)
+        dQ[i]  = scale·Σ_j dS_ij·K[j]
+        dK[j]  = scale·Σ_{h in group} Σ_i dS_ij·Q[i]
+        dV[j]  = Σ_{h in group} Σ_i P_ij·dO[i]
+
+    Returns ``dq [T, hq, d]``, ``dk, dv [T, hkv, d]``.
+    """
+    q, k, v, cu, T, hq, hkv, d = _check(q, k, v, cu_seqlens)
+    do = np.asarray(do, dtype=np.float64)
+    assert do.shape == q.shape
+    group = hq // hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for n in range(len(cu) - 1):
+        s0, s1 = int(cu[n]), int(cu[n + 1])
+        L = s1 - s0
+        if L == 0:
+            continue
+        for h in range(hq):
+            g = h // group
+            kd = k[s0:s1, g, :]
+            vd = v[s0:s1, g, :]
+            for r0 in range(0, L, row_block):
+                r1 = min(L, r0 + row_block)
+                qb = q[s0 + r0:s0 + r1, h, :]
+                dob = do[s0 + r0:s0 + r1, h, :]
+                p, _ = _probabilities(qb, kd, scale, r0, causal)
+                ob = p @ vd
+                D = np.sum(dob * ob, axis=1)
+                dp = dob @ vd.T
+                ds = p * (dp - D[:, None])
+                dq[s0 + r0:s0 + r1, h, :] = scale * (ds @ kd)
+                dk[s0:s1, g, :] += scale * (ds.T @ qb)
+                dv[s0:s1, g, :] += p.T @ dob
+    return dq, dk, dv

@@ -1,0 +1,152 @@
+"""Reference MX (microscaling) quantiser: FP8 E4M3 elements with one E8M0 scale per 32.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The FLAMIA page ("FLAMIA Mimarisi ve Temel Tasarım İlkeleri") names an MXFP8 attention path
+with token-block scaling and document-local scales, but not the bit-level rules. The rules
+below are the public definitions of the formats and the plainest MX scale rule:
+
+* E4M3 ("FN" variant): 1 sign, 4 exponent (bias 7), 3 mantissa bits; subnormals kept
+  (step 2^-9 below 2^-6); largest finite 448; no infinities; NaN is S.1111.111.
+* E8M0 scale byte b: the power of two 2^(b-127); b = 0xFF is NaN.
+* Per block of 32 elements: amax = max |x|; shared exponent e = floor(log2 amax) - 8 (8 is the
+  exponent of 448, the largest E4M3 power of two), clamped to [-127, 127]; e = -127 for an
+  all-zero block; scale byte e + 127. Elements x·2^-e are saturated to ±448 and rounded to the
+  nearest E4M3 value, ties to even mantissa; the sign of zero is kept. A block holding a NaN
+  or an infinity gets scale byte 0xFF and NaN codes 0x7F.
+
+Two blockings, both document-local when tokens are blocked:
+
+* along d  (``quantize_d``): channels [32c, 32c+32) of one (token, head);
+* along tokens (``quantize_t``): doc-local tokens [32b, 32b+32) of one (head, channel), the
+  last block of a document holding only its real tokens. Blocks never span two documents.
+"""
+
+import numpy as np
+
+E4M3_MAX = 448.0
+E4M3_EMAX = 8          # exponent of the largest power of two not above 448
+BLOCK = 32
+
+
+def e4m3_decode(codes):
+    """Value of each E4M3 byte (float64); 0x7F/0xFF decode to NaN."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    E = (c >> 3) & 0xF
+    m = c & 0x7
+    sub = m * 2.0 ** -9
+    nrm = (1.0 + m / 8.0) * np.ldexp(1.0, (E - 7).astype(np.int64))
+    val = sign * np.where(E == 0, sub, nrm)
+    return np.where((E == 15) & (m == 7), np.nan, val)
+
+
+def e8m0_decode(scale_bytes):
+    """2^(b-127) for each E8M0 byte; 0xFF is NaN."""
+    b = np.asarray(scale_bytes, dtype=np.int64)
+    return np.where(b == 0xFF, np.nan, np.ldexp(1.0, b - 127))
+
+
+def _e4m3_encode_scaled(y):
+    """Round already-scaled, finite values y (|y| <= 448) to E4M3 bytes, RNE, sign kept."""
+    a = np.abs(y)
+    neg = np.signbit(y)
+    code = np.zeros(y.shape, dtype=np.int64)
+    small = a < 2.0 ** -6
+    # subnormal range: integer multiples of 2^-9; rint rounds halves to even.
+    # A result of 8 is 2^-6, whose normal code 0x08 equals the integer 8.
+    code = np.where(small, np.rint(a * 2.0 ** 9).astype(np.int64), code)
+    # normal range: exponent from the binary representation, 3 fraction bits
+    _, ex = np.frexp(np.where(small, 1.0, a))      # a = f·2^ex, f in [0.5, 1)
+    E = ex - 1                                       # floor(log2 a)
+    mant = np.rint(np.ldexp(np.where(small, 1.0, a), 3 - E)).astype(np.int64)  # in [8, 16]
+    carry = mant == 16
+    E = np.where(carry, E + 1, E)
+    mant = np.where(carry, 8, mant)
+    ncode = ((E + 7) << 3) | (mant - 8)
+    code = np.where(small, code, ncode)
+    return code | np.where(neg, 0x80, 0)
+
+
+def quantize_blocks(x):
+    """Quantise rows of 32 (or fewer) values: x is [..., n] with n <= 32, one block per row.
+
+    Returns (codes uint8 [..., n], scale bytes uint8 [...]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    finite = np.all(np.isfinite(x), axis=-1)
+    xs = np.where(np.isfinite(x), x, 0.0)
+    amax = np.max(np.abs(xs), axis=-1) if x.shape[-1] else np.zeros(x.shape[:-1])
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    e = np.clip(ex - 1 - E4M3_EMAX, -127, 127)
+    e = np.where(amax > 0, e, -127)
+    y = np.ldexp(xs, -e[..., None])
+    y = np.clip(y, -E4M3_MAX, E4M3_MAX)
+    codes = _e4m3_encode_scaled(y)
+    codes = np.where(finite[..., None], codes, 0x7F)
+    scales = np.where(finite, e + 127, 0xFF)
+    return codes.astype(np.uint8), scales.astype(np.uint8)
+
+
+def quantize_d(x):
+    """Blocks along the head dim: x [T, h, d] (d % 32 == 0) -> codes [T, h, d], scales [T, h, d/32]."""
+    x = np.asarray(x, dtype=np.float64)
+    T, h, d = x.shape
+    assert d % BLOCK == 0
+    codes, scales = quantize_blocks(x.reshape(T, h, d // BLOCK, BLOCK))
+    return codes.reshape(T, h, d), scales
+
+
+def padded_offsets(cu_seqlens):
+    """Start of each document in the token-blocked layout: P_n = Σ_{m<n} 32·ceil(L_m/32).
+
+    Returns an int64 array of n_docs+1 entries; the last one is T_pad.
+    """
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    L = np.diff(cu)
+    return np.concatenate([[0], np.cumsum((L + BLOCK - 1) // BLOCK * BLOCK)])
+
+
+def quantize_t(x, cu_seqlens):
+    """Blocks along doc-local tokens: x [T, h, d] -> codes [h, d, T_pad], scales [h, d, T_pad/32].
+
+    Document n occupies columns [P_n, P_n + 32·ceil(L_n/32)); its block b covers doc-local tokens
+    [32b, min(32b+32, L_n)). Columns past the document's end (padding) hold code 0x00.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T, h, d = x.shape
+    P = padded_offsets(cu)
+    Tp = int(P[-1])
+    codes = np.zeros((h, d, Tp), dtype=np.uint8)
+    scales = np.zeros((h, d, Tp // BLOCK), dtype=np.uint8)
+    xt = np.transpose(x, (1, 2, 0))  # [h, d, T]
+    for n in range(len(cu) - 1):
+        s0, s1, p0 = int(cu[n]), int(cu[n + 1]), int(P[n])
+        for b0 in range(0, s1 - s0, BLOCK):
+            b1 = min(s1 - s0, b0 + BLOCK)
+            c, s = quantize_blocks(xt[:, :, s0 + b0:s0 + b1])
+            codes[:, :, p0 + b0:p0 + b1] = c
+            scales[:, :, (p0 + b0) // BLOCK] = s
+    return codes, scales
+
+
+def dequantize_d(codes, scales):
+    """Values of a d-blocked tensor: codes [T, h, d], scales [T, h, d/32] -> float64 [T, h, d]."""
+    T, h, d = codes.shape
+    v = e4m3_decode(codes).reshape(T, h, d // BLOCK, BLOCK) * e8m0_decode(scales)[..., None]
+    return v.reshape(T, h, d)
+
+
+def dequantize_t(codes, scales, cu_seqlens):
+    """Values of a token-blocked tensor back in packed layout: -> float64 [T, h, d]."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    h, d, Tp = codes.shape
+    P = padded_offsets(cu)
+    full = e4m3_decode(codes) * np.repeat(e8m0_decode(scales), BLOCK, axis=2)
+    T = int(cu[-1])
+    out = np.zeros((T, h, d), dtype=np.float64)
+    for n in range(len(cu) - 1):
+        s0, s1, p0 = int(cu[n]), int(cu[n + 1]), int(P[n])
+        out[s0:s1] = np.transpose(full[:, :, p0:p0 + (s1 - s0)], (2, 0, 1))
+    return out

@@ -1,0 +1,129 @@
+"""Attention oracle fed with MX-quantised operand copies (forward and backward).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+FLAMIA page, "FLAMIA Mimarisi ve Temel Tasarım İlkeleri": an MXFP8 path whose quantised
+operands are reused across matrix orientations (token-block scaling), with safeguards so that
+a shared scale never carries a later token's data into an earlier query, and with the forward
+and backward passes numerically consistent. The page gives no mechanism; the reading here is:
+
+* Every GEMM is blocked along its contraction axis. QKᵀ and dO·Vᵀ contract over the head dim:
+  their operands are the d-blocked copies ``X_d``. P·V, Pᵀ·dO, dS·K and dSᵀ·Q contract over
+  tokens: their operands are the token-blocked, document-local copies ``X_t``.
+* A d-block holds one token's channels, so it cannot leak. A token block can: its scale mixes
+  32 neighbouring tokens. Pairs (i, j) lying in the same doc-local C×C tile (C = 128) -- the
+  diagonal tiles of the causal mask -- therefore use the unquantised bf16 values ``X_b`` in
+  every token-contracted GEMM, and only pairs in off-diagonal tiles use ``X_t``. When
+  ``causal`` is false no tile is treated as diagonal.
+* The backward reuses the forward's ``Q_d``/``K_d`` bytes, so it sees the same scores.
+
+Computed exactly in float64 from the decoded copies (the decoding is exact):
+
+    S_ij  = scale·Q_d[i]·K_d[j]                        P = softmax(S + mask) (two-pass)
+    O[i]  = Σ_j P_ij·(diag ? V_b[j] : V_t[j])           LSE_i = max + ln(sum)
+    dP_ij = dO_d[i]·V_d[j]                              D_i = dO_b[i]·O[i]
+    dS_ij = P_ij·(dP_ij − D_i)
+    dV[j] = Σ_{h in group} Σ_i P_ij·(diag ? dO_b[i] : dO_t[i])
+    dQ[i] = scale·Σ_j dS_ij·(diag ? K_b[j] : K_t[j])
+    dK[j] = scale·Σ_{h in group} Σ_i dS_ij·(diag ? Q_b[i] : Q_t[i])
+
+Not modelled: the rounding of P and dS before a matrix-core product and fp32 accumulation on
+the device.
+"""
+
+import numpy as np
+
+from . import attention as _att
+from . import mx as _mx
+
+DIAG_TILE = 128
+
+
+def operand_copies(x_b, cu_seqlens):
+    """Decoded d-blocked and token-blocked copies of a bf16-valued tensor [T, h, d]."""
+    cd, sd = _mx.quantize_d(x_b)
+    ct, st = _mx.quantize_t(x_b, cu_seqlens)
+    return _mx.dequantize_d(cd, sd), _mx.dequantize_t(ct, st, cu_seqlens)
+
+
+def diag_pairs(n_rows, row0, n_cols, causal, tile=DIAG_TILE):
+    """Boolean [rows, cols]: true where doc-local query i and key j share a tile×tile tile."""
+    if not causal:
+        return np.zeros((n_rows, n_cols), dtype=bool)
+    i = (row0 + np.arange(n_rows))[:, None] // tile
+    j = np.arange(n_cols)[None, :] // tile
+    return i == j
+
+
+def attn_mx_fwd(q_b, k_b, v_b, cu_seqlens, scale, causal=True, tile=DIAG_TILE,
+                row_block=_att.ROW_BLOCK):
+    """Forward with MX operands; returns o [T, hq, d], lse [hq, T] (float64)."""
+    q_b = np.asarray(q_b, np.float64)
+    k_b = np.asarray(k_b, np.float64)
+    v_b = np.asarray(v_b, np.float64)
+    cu = np.asarray(cu_seqlens, np.int64)
+    T, hq, d = q_b.shape
+    hkv = k_b.shape[1]
+    group = hq // hkv
+    q_d, _ = operand_copies(q_b, cu)
+    k_d, _ = operand_copies(k_b, cu)
+    _, v_t = operand_copies(v_b, cu)
+    o = np.zeros((T, hq, d))
+    lse = np.zeros((hq, T))
+    for n in range(len(cu) - 1):
+        s0, s1 = int(cu[n]), int(cu[n + 1])
+        L = s1 - s0
+        if L == 0:
+            continue
+        for h in range(hq):
+            g = h // group
+            for r0 in range(0, L, row_block):
+                r1 = min(L, r0 + row_block)
+                p, rl = _att._probabilities(q_d[s0 + r0:s0 + r1, h], k_d[s0:s1, g], scale, r0, causal)
+                dg = diag_pairs(r1 - r0, r0, L, causal, tile)
+                o[s0 + r0:s0 + r1, h] = np.where(dg, p, 0.0) @ v_b[s0:s1, g] + \
+                    np.where(dg, 0.0, p) @ v_t[s0:s1, g]
+                lse[h, s0 + r0:s0 + r1] = rl
+    return o, lse
+
+
+def attn_mx_bwd(q_b, k_b, v_b, do_b, cu_seqlens, scale, causal=True, tile=DIAG_TILE,
+                row_block=_att.ROW_BLOCK):
+    """Backward with MX operands; returns dq [T, hq, d], dk, dv [T, hkv, d] (float64)."""
+    q_b = np.asarray(q_b, np.float64)
+    k_b = np.asarray(k_b, np.float64)
+    v_b = np.asarray(v_b, np.float64)
+    do_b = np.asarray(do_b, np.float64)
+    cu = np.asarray(cu_seqlens, np.int64)
+    T, hq, d = q_b.shape
+    hkv = k_b.shape[1]
+    group = hq // hkv
+    q_d, q_t = operand_copies(q_b, cu)
+    k_d, k_t = operand_copies(k_b, cu)
+    v_d, v_t = operand_copies(v_b, cu)
+    do_d, do_t = operand_copies(do_b, cu)
+    dq = np.zeros((T, hq, d))
+    dk = np.zeros((T, hkv, d))
+    dv = np.zeros((T, hkv, d))
+    for n in range(len(cu) - 1):
+        s0, s1 = int(cu[n]), int(cu[n + 1])
+        L = s1 - s0
+        if L == 0:
+            continue
+        for h in range(hq):
+            g = h // group
+            for r0 in range(0, L, row_block):
+                r1 = min(L, r0 + row_block)
+                rows = slice(s0 + r0, s0 + r1)
+                p, _ = _att._probabilities(q_d[rows, h], k_d[s0:s1, g], scale, r0, causal)
+                dg = diag_pairs(r1 - r0, r0, L, causal, tile)
+                p_diag, p_off = np.where(dg, p, 0.0), np.where(dg, 0.0, p)
+                o = p_diag @ v_b[s0:s1, g] + p_off @ v_t[s0:s1, g]
+                D = np.sum(do_b[rows, h] * o, axis=1)
+                dp = do_d[rows, h] @ v_d[s0:s1, g].T
+                ds = p * (dp - D[:, None])
+                ds_diag, ds_off = np.where(dg, ds, 0.0), np.where(dg, 0.0, ds)
+                dv[s0:s1, g] += p_diag.T @ do_b[rows, h] + p_off.T @ do_t[rows, h]
+                dq[rows, h] = scale * (ds_diag @ k_b[s0:s1, g] + ds_off @ k_t[s0:s1, g])
+                dk[s0:s1, g] += scale * (ds_diag.T @ q_b[rows, h] + ds_off.T @ q_t[rows, h])
+    return dq, dk, dv
