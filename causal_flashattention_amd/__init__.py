@@ -1,1 +1,157 @@
-"""Causal packed flash attention for MI355X (gfx950): Python binding of the C-ABI library."""
+"""Causal packed flash attention for AMD MI355X (gfx950).
+
+Thin Python binding of the C ABI in ``include/cfa.h`` (``libcfa.so`` in this directory).
+PyTorch provides device memory and the current HIP stream; every step of the computation runs
+in the library's HIP kernels. There is no CPU or PyTorch fallback: a missing library or a
+failing call raises.
+
+    o, lse, saved = attn_fwd(q, k, v, cu_seqlens)          # q [T, hq, d], k/v [T, hkv, d]
+    dq, dk, dv = attn_bwd(q, k, v, o, lse, do, cu_seqlens, saved=saved)
+    codes, scales = mx_quantize(x, cu_seqlens, axis=0)     # MXFP8 E4M3 + E8M0, blocks of 32
+"""
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import CFA_BF16, CFA_F32, CFA_MXFP8, CfaError
+
+__all__ = ["attn_fwd", "attn_bwd", "mx_quantize", "workspace_bytes", "saved_bytes", "CfaError",
+           "CFA_F32", "CFA_BF16", "CFA_MXFP8", "library_path"]
+
+
+def library_path():
+    return _lib.LIB_PATH
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _host_cu(cu_seqlens, cu_seqlens_host):
+    if cu_seqlens_host is None:
+        return None
+    h = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous()
+    assert h.device.type == "cpu"
+    return h
+
+
+def _dtype_code(x, mx):
+    if mx:
+        if x.dtype != torch.bfloat16:
+            raise TypeError("the MXFP8 path takes bf16 inputs")
+        return CFA_MXFP8
+    if x.dtype == torch.bfloat16:
+        return CFA_BF16
+    if x.dtype == torch.float32:
+        return CFA_F32
+    raise TypeError(f"unsupported dtype {x.dtype}")
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def workspace_bytes(pass_, total_tokens, n_docs, hq, hkv, d, dtype):
+    return _lib.lib().cfa_workspace_bytes(pass_, total_tokens, n_docs, hq, hkv, d, dtype)
+
+
+def saved_bytes(total_tokens, n_docs, hq, hkv, d, dtype):
+    return _lib.lib().cfa_saved_bytes(total_tokens, n_docs, hq, hkv, d, dtype)
+
+
+def attn_fwd(q, k, v, cu_seqlens, *, scale=None, causal=True, cu_seqlens_host=None, max_seqlen=0,
+             mx=False, out=None, lse=None, saved=None, workspace=None):
+    """Forward pass. Returns (o, lse, saved); ``saved`` is None unless ``mx``."""
+    L = _lib.lib()
+    _check_dev(q, k, v, cu_seqlens)
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    n_docs = cu_seqlens.numel() - 1
+    dt = _dtype_code(q, mx)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((hq, T), dtype=torch.float32, device=dev)
+    if mx and saved is None:
+        saved = torch.empty(L.cfa_saved_bytes(T, n_docs, hq, hkv, d, dt), dtype=torch.uint8, device=dev)
+    if workspace is None:
+        nb = L.cfa_workspace_bytes(0, T, n_docs, hq, hkv, d, dt)
+        workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+    hcu = _host_cu(cu_seqlens, cu_seqlens_host)
+    _lib.check(L.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens),
+                          _ptr(hcu) if hcu is not None else None, n_docs, T, int(max_seqlen), hq, hkv, d,
+                          scale, int(bool(causal)), dt, _ptr(saved) if mx else None, _ptr(workspace),
+                          workspace.numel(), _stream()))
+    return out, lse, saved
+
+
+def attn_bwd(q, k, v, o, lse, dout, cu_seqlens, *, scale=None, causal=True, cu_seqlens_host=None,
+             max_seqlen=0, mx=False, saved=None, dq=None, dk=None, dv=None, workspace=None):
+    """Backward pass. Returns (dq, dk, dv) with the layouts and dtype of (q, k, v)."""
+    L = _lib.lib()
+    _check_dev(q, k, v, o, lse, dout, cu_seqlens, saved)
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    n_docs = cu_seqlens.numel() - 1
+    dt = _dtype_code(q, mx)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        nb = L.cfa_workspace_bytes(1, T, n_docs, hq, hkv, d, dt)
+        workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device)
+    hcu = _host_cu(cu_seqlens, cu_seqlens_host)
+    _lib.check(L.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                          _ptr(saved) if saved is not None else None, _ptr(dq), _ptr(dk), _ptr(dv),
+                          _ptr(cu_seqlens), _ptr(hcu) if hcu is not None else None, n_docs, T,
+                          int(max_seqlen), hq, hkv, d, scale, int(bool(causal)), dt, _ptr(workspace),
+                          workspace.numel(), _stream()))
+    return dq, dk, dv
+
+
+def mx_quantize(x, cu_seqlens, axis, *, cu_seqlens_host=None, t_pad=None, codes=None, scales=None,
+                workspace=None):
+    """MX-quantise bf16 ``x [T, h, d]``. axis 0: blocks along d; axis 1: doc-local token blocks.
+
+    Returns (codes uint8, scales uint8): [T, h, d] / [T, h, d/32] for axis 0, and
+    [h, d, t_pad] / [h, d, t_pad/32] for axis 1 (t_pad defaults to the size bound).
+    """
+    L = _lib.lib()
+    _check_dev(x, cu_seqlens)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("mx_quantize takes bf16 input")
+    T, h, d = x.shape
+    n_docs = cu_seqlens.numel() - 1
+    dev = x.device
+    if axis == 0:
+        t_pad = 0
+        codes = torch.empty((T, h, d), dtype=torch.uint8, device=dev) if codes is None else codes
+        scales = torch.empty((T, h, d // 32), dtype=torch.uint8, device=dev) if scales is None else scales
+    else:
+        if t_pad is None:
+            t_pad = L.mx_padded_tokens(T, n_docs)
+        codes = torch.zeros((h, d, t_pad), dtype=torch.uint8, device=dev) if codes is None else codes
+        scales = torch.zeros((h, d, t_pad // 32), dtype=torch.uint8, device=dev) if scales is None else scales
+        if workspace is None:
+            workspace = torch.empty(max(L.mx_workspace_bytes(n_docs), 256), dtype=torch.uint8, device=dev)
+    hcu = _host_cu(cu_seqlens, cu_seqlens_host)
+    _lib.check(L.mx_quantize(_ptr(x), T, h, d, _ptr(cu_seqlens), _ptr(hcu) if hcu is not None else None,
+                             n_docs, axis, _ptr(codes), _ptr(scales), int(t_pad),
+                             _ptr(workspace) if workspace is not None else None,
+                             workspace.numel() if workspace is not None else 0, _stream()))
+    return codes, scales

@@ -1,0 +1,330 @@
+// Fused causal attention forward for gfx950: bf16 MFMA path and an fp32 path.
+//
+// What is computed (per document, query head h, kv head g = h / (hq/hkv)):
+//   S = scale·Q Kᵀ, masked by index (key j visible to query i iff j <= i), P = softmax(S),
+//   O = P V, LSE = ln Σ_j exp(S_ij)   -- "GPT Kernel Programlama" §2-§6.
+// How: Q/K/V are cut into tiles that live on chip; each workgroup walks the key tiles of its
+// query tile with a running row maximum and running sum (online softmax) and writes O once;
+// tiles wholly above the diagonal are skipped -- "GPT Kernel Programlama" §4 and §7,
+// "FlashAttention (HU)" sections "Tiling és blokkos feldolgozás", "Online Softmax-számítás",
+// "Műveletek összevonása egyetlen CUDA-kernelbe".
+//
+// bf16 kernel layout (d = 64 or 128), one workgroup = 4 waves of 64 lanes:
+//  * Each wave owns 32 query rows of one head. HPW heads of one GQA group share a workgroup
+//    (HPW = 1, 2 or 4), so a K/V tile staged in LDS serves 128 (row, head) pairs.
+//  * Scores are formed transposed, Sᵀ = K Qᵀ, with v_mfma_f32_32x32x16_bf16: the wave's Qᵀ
+//    fragment stays in registers for the whole key loop, and each lane ends up holding one
+//    query column, so the row max and row sum are in-lane plus one swap between lane halves.
+//  * The probabilities in that layout are already the B operand of Oᵀ += Vᵀ Pᵀ (only a
+//    convert to bf16); Vᵀ comes from the row-major V tile through ds_read_b64_tr_b16.
+//  * K/V tiles of 64 keys are double-buffered in LDS: the next tile's global loads are in
+//    flight while the current tile is multiplied.
+//  * exp2 with scale·log2(e) folded into the scores; LSE converted back to natural log.
+#include "cfa_device.h"
+
+namespace cfa {
+
+template <int D>
+struct FwdTile {
+  static constexpr int BN = 64;                  // keys per tile
+  static constexpr int KSTR = D * 2 + 16;        // LDS row stride (bytes) of the K tile
+  static constexpr int VSTR = D * 2 + 32;        // LDS row stride (bytes) of the V tile
+  static constexpr int KBYTES = BN * KSTR;
+  static constexpr int VBYTES = BN * VSTR;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int CHUNKS = BN * D / 8;      // 16-byte chunks per tile and tensor
+  static constexpr int PER_THREAD = CHUNKS / 256;
+  static constexpr int DS = D / 16;              // k-steps of the QKᵀ MFMA
+  static constexpr int DB = D / 32;              // 32-wide d blocks of Oᵀ
+};
+
+template <int D, int HPW>
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    __bf16* __restrict__ o, float* __restrict__ lse, Plan plan, int total_tokens, int hq, int hkv,
+    int n_hb, float scale_log2, int causal) {
+  using C = FwdTile<D>;
+  constexpr int BMW = 128 / HPW;  // query rows per workgroup
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int wid = blockIdx.x;
+  const int p = wid / n_hb, hb = wid % n_hb;
+  int s0, L, t;
+  if (!decode_item(plan, p, BMW, true, s0, L, t)) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int G = hq / hkv;
+  const int h = hb * HPW + (w % HPW);
+  const int g = h / G;
+  const int wr0 = t * BMW + 32 * (w / HPW);      // first doc-local row of this wave
+  const int wg_rows_end = min(L, (t + 1) * BMW);
+  const int kv_end = causal ? wg_rows_end : L;   // keys the workgroup needs
+  const int n_kt = (kv_end + C::BN - 1) / C::BN;
+  const int wave_last_key = causal ? min(L, wr0 + 32) - 1 : L - 1;
+  const int qrow = wr0 + (lane & 31);            // this lane's query (doc-local)
+  const int half = lane >> 5;
+
+  // ---- Qᵀ fragments (B operand): lane holds Q[qrow][16s + 8·half .. +8]
+  bf16x8 qf[C::DS];
+  {
+    const bool ok = qrow < L;
+    const __bf16* src = q + ((size_t)(s0 + (ok ? qrow : 0)) * hq + h) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < C::DS; ++s) {
+      i32x4 u = ok ? *(const i32x4*)(src + 16 * s) : i32x4{0, 0, 0, 0};
+      qf[s] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+
+  f32x16 oacc[C::DB];
+#pragma unroll
+  for (int b = 0; b < C::DB; ++b) oacc[b] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // ---- global -> registers -> LDS staging of one K/V tile
+  i32x4 kreg[C::PER_THREAD], vreg[C::PER_THREAD];
+  auto load_tile = [&](int kt) {
+    const int k0 = kt * C::BN;
+#pragma unroll
+    for (int i = 0; i < C::PER_THREAD; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int key = c / (D / 8), col = c % (D / 8);
+      const bool ok = (k0 + key) < kv_end;
+      const size_t off = ((size_t)(s0 + (ok ? k0 + key : 0)) * hkv + g) * D + col * 8;
+      kreg[i] = ok ? *(const i32x4*)(k + off) : i32x4{0, 0, 0, 0};
+      vreg[i] = ok ? *(const i32x4*)(v + off) : i32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_tile = [&](int buf) {
+    char* kb = smem + buf * C::STAGE;
+    char* vb = kb + C::KBYTES;
+#pragma unroll
+    for (int i = 0; i < C::PER_THREAD; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int key = c / (D / 8), col = c % (D / 8);
+      *(i32x4*)(kb + key * C::KSTR + col * 16) = kreg[i];
+      *(i32x4*)(vb + key * C::VSTR + col * 16) = vreg[i];
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int k0 = kt * C::BN;
+    if (kt + 1 < n_kt) load_tile(kt + 1);
+    if (k0 <= wave_last_key) {
+      const char* kb = smem + (kt & 1) * C::STAGE;
+      const char* vb = kb + C::KBYTES;
+      // ---- Sᵀ = K Qᵀ for the tile's two 32-key blocks
+      f32x16 sacc[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        sacc[b] = f32x16{};
+        const char* krow = kb + (32 * b + (lane & 31)) * C::KSTR + 16 * half;
+#pragma unroll
+        for (int s = 0; s < C::DS; ++s) {
+          bf16x8 a = __builtin_bit_cast(bf16x8, *(const i32x4*)(krow + 32 * s));
+          sacc[b] = mfma32(a, qf[s], sacc[b]);
+        }
+      }
+      // ---- online softmax on this lane's query column
+      const bool need_mask = causal ? (k0 + C::BN - 1 > wr0) : (k0 + C::BN > L);
+      float mt = -INFINITY;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          float x = sacc[b][j] * scale_log2;
+          if (need_mask) {
+            const int key = k0 + 32 * b + 8 * (j >> 2) + 4 * half + (j & 3);
+            const bool masked = causal ? (key > qrow) : (key >= L);
+            x = masked ? -INFINITY : x;
+          }
+          sacc[b][j] = x;
+          mt = fmaxf(mt, x);
+        }
+      mt = wave_max_xor32(mt);
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = exp2f(m_run - m_new);
+      m_run = m_new;
+      float ls = 0.f;
+      bf16x8 pf[4];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+          const float p0 = exp2f(sacc[b][j] - m_new);
+          const float p1 = exp2f(sacc[b][j + 1] - m_new);
+          ls += p0 + p1;
+          const uint32_t pk = pack_bf16x2(p0, p1);
+          i32x4 u = __builtin_bit_cast(i32x4, pf[2 * b + (j >> 3)]);
+          u[(j & 7) >> 1] = (int)pk;
+          pf[2 * b + (j >> 3)] = __builtin_bit_cast(bf16x8, u);
+        }
+      l_run = l_run * alpha + ls;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+      // ---- Oᵀ += Vᵀ Pᵀ; Vᵀ fragments via transposing LDS reads
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int kbase = 32 * (kk >> 1) + 16 * (kk & 1);
+        const int key = kbase + 4 * half + ((lane & 15) >> 2);
+        const int dsub = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const char* p0 = vb + key * C::VSTR + (32 * db + dsub) * 2;
+          i16x4 r0 = lds_read_tr16(p0);
+          i16x4 r1 = lds_read_tr16(p0 + 8 * C::VSTR);
+          oacc[db] = mfma32(concat_tr(r0, r1), pf[kk], oacc[db]);
+        }
+      }
+    }
+    if (kt + 1 < n_kt) store_tile((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = Oᵀ / l, LSE = (m + log2 l)·ln 2
+  const float l_tot = wave_sum_xor32(l_run);
+  if (qrow < L) {
+    const float inv = 1.f / l_tot;
+    __bf16* dst = o + ((size_t)(s0 + qrow) * hq + h) * D + 4 * half;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        i32x2 u;
+        u.x = (int)pack_bf16x2(oacc[db][4 * jg] * inv, oacc[db][4 * jg + 1] * inv);
+        u.y = (int)pack_bf16x2(oacc[db][4 * jg + 2] * inv, oacc[db][4 * jg + 3] * inv);
+        *(i32x2*)(dst + 32 * db + 8 * jg) = u;
+      }
+    if (half == 0) lse[(size_t)h * total_tokens + s0 + qrow] = (m_run + __log2f(l_tot)) * LN2;
+  }
+}
+
+// ------------------------------------------------------------------ fp32 path
+// One wave per workgroup, one query row per lane, 64-row query tiles, key tiles of KT keys in
+// LDS; plain fp32 FMA arithmetic with the same online softmax.
+template <int D>
+__global__ __launch_bounds__(64) void attn_fwd_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    float* __restrict__ o, float* __restrict__ lse, Plan plan, int total_tokens, int hq, int hkv,
+    float scale_log2, int causal) {
+  constexpr int KT = (D <= 64) ? 64 : 32;
+  __shared__ float ks[KT][D + 1];
+  __shared__ float vs[KT][D + 1];
+  const int p = blockIdx.x / hq, h = blockIdx.x % hq;
+  int s0, L, t;
+  if (!decode_item(plan, p, 64, true, s0, L, t)) return;
+  const int g = h / (hq / hkv);
+  const int lane = threadIdx.x;
+  const int qrow = t * 64 + lane;
+  const bool ok = qrow < L;
+  float qr[D], acc[D];
+  for (int r = 0; r < D; ++r) {
+    qr[r] = ok ? q[((size_t)(s0 + qrow) * hq + h) * D + r] : 0.f;
+    acc[r] = 0.f;
+  }
+  const int kv_end = causal ? min(L, (t + 1) * 64) : L;
+  float m_run = -INFINITY, l_run = 0.f;
+  for (int k0 = 0; k0 < kv_end; k0 += KT) {
+    __syncthreads();
+    for (int i = lane; i < KT * D; i += 64) {
+      const int key = i / D, r = i % D;
+      const bool in = k0 + key < kv_end;
+      const size_t off = ((size_t)(s0 + (in ? k0 + key : 0)) * hkv + g) * D + r;
+      ks[key][r] = in ? k[off] : 0.f;
+      vs[key][r] = in ? v[off] : 0.f;
+    }
+    __syncthreads();
+    float s[KT];
+    float mt = -INFINITY;
+    for (int j = 0; j < KT; ++j) {
+      float x = 0.f;
+      for (int r = 0; r < D; ++r) x = fmaf(qr[r], ks[j][r], x);
+      x *= scale_log2;
+      const int key = k0 + j;
+      const bool masked = (key >= kv_end) || (causal && key > qrow);
+      s[j] = masked ? -INFINITY : x;
+      mt = fmaxf(mt, s[j]);
+    }
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = exp2f(m_run - m_new);
+    l_run *= alpha;
+    for (int r = 0; r < D; ++r) acc[r] *= alpha;
+    for (int j = 0; j < KT; ++j) {
+      const float pj = exp2f(s[j] - m_new);
+      l_run += pj;
+      for (int r = 0; r < D; ++r) acc[r] = fmaf(pj, vs[j][r], acc[r]);
+    }
+    m_run = m_new;
+  }
+  if (ok) {
+    const float inv = 1.f / l_run;
+    for (int r = 0; r < D; ++r) o[((size_t)(s0 + qrow) * hq + h) * D + r] = acc[r] * inv;
+    lse[(size_t)h * total_tokens + s0 + qrow] = (m_run + __log2f(l_run)) * LN2;
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, const Plan& plan_any,
+                           const int* pref_base, int total_tokens, int hq, int hkv, int d, float scale, int causal,
+                           hipStream_t stream) {
+  const int G = hq / hkv;
+  const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
+  const int rows = 128 / hpw;
+  Plan plan = plan_any;
+  plan.pref = pref_base + pref_slot(rows) * (plan.n_docs + 1);
+  const int n_hb = hq / hpw;
+  // upper bound of items for this tile height: ceil(T/rows) + n_docs
+  const long items = (long)(total_tokens + rows - 1) / rows + plan.n_docs;
+  const long grid = items * n_hb;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const float sl2 = scale * LOG2E;
+  const __bf16* Q = (const __bf16*)q;
+  const __bf16* K = (const __bf16*)k;
+  const __bf16* V = (const __bf16*)v;
+  __bf16* O = (__bf16*)o;
+#define CFA_FWD_LAUNCH(DD, HH)                                                                         \
+  do {                                                                                                 \
+    auto kern = attn_fwd_bf16_kernel<DD, HH>;                                                          \
+    const int lds = 2 * FwdTile<DD>::STAGE;                                                            \
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds))       \
+      return hipErrorInvalidConfiguration;                                                             \
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, stream, Q, K, V, O, lse, plan,      \
+                       total_tokens, hq, hkv, n_hb, sl2, causal);                                      \
+  } while (0)
+  if (d == 128) {
+    if (hpw == 4) CFA_FWD_LAUNCH(128, 4);
+    else if (hpw == 2) CFA_FWD_LAUNCH(128, 2);
+    else CFA_FWD_LAUNCH(128, 1);
+  } else {
+    if (hpw == 4) CFA_FWD_LAUNCH(64, 4);
+    else if (hpw == 2) CFA_FWD_LAUNCH(64, 2);
+    else CFA_FWD_LAUNCH(64, 1);
+  }
+#undef CFA_FWD_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, const Plan& plan_any,
+                          const int* pref_base, int total_tokens, int hq, int hkv, int d, float scale, int causal,
+                          hipStream_t stream) {
+  Plan plan = plan_any;
+  plan.pref = pref_base + pref_slot(64) * (plan.n_docs + 1);
+  const long items = (long)(total_tokens + 63) / 64 + plan.n_docs;
+  const long grid = items * hq;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const float sl2 = scale * LOG2E;
+  if (d == 64)
+    hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, dim3((unsigned)grid), dim3(64), 0, stream, (const float*)q,
+                       (const float*)k, (const float*)v, (float*)o, lse, plan, total_tokens, hq, hkv, sl2, causal);
+  else
+    hipLaunchKernelGGL(attn_fwd_f32_kernel<128>, dim3((unsigned)grid), dim3(64), 0, stream, (const float*)q,
+                       (const float*)k, (const float*)v, (float*)o, lse, plan, total_tokens, hq, hkv, sl2, causal);
+  return hipGetLastError();
+}
+
+}  // namespace cfa

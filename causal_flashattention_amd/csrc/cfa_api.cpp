@@ -1,0 +1,205 @@
+// Host side of the C ABI declared in include/cfa.h: argument validation, workspace layout,
+// work-list construction and kernel launch order. Every check runs before the first HIP call,
+// so a rejected call launches nothing and writes nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "cfa.h"
+#include "cfa_device.h"
+#include "cfa_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_hip(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(CFA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return CFA_OK;
+}
+
+// Host mirror of cu_seqlens: cu[0] = 0, non-decreasing, cu[n] = total.
+int check_cu_host(const int32_t* cu, int n_docs, int total, int max_seqlen) {
+  if (!cu) return CFA_OK;
+  if (cu[0] != 0) return fail(CFA_ERR_SHAPE, "cu_seqlens_host[0] = %d, expected 0", cu[0]);
+  for (int n = 0; n < n_docs; ++n) {
+    if (cu[n + 1] < cu[n])
+      return fail(CFA_ERR_SHAPE, "cu_seqlens_host decreases at %d (%d -> %d)", n, cu[n], cu[n + 1]);
+    if (max_seqlen > 0 && cu[n + 1] - cu[n] > max_seqlen)
+      return fail(CFA_ERR_SHAPE, "document %d has length %d > max_seqlen %d", n, cu[n + 1] - cu[n], max_seqlen);
+  }
+  if (cu[n_docs] != total)
+    return fail(CFA_ERR_SHAPE, "cu_seqlens_host[%d] = %d, expected total_tokens %d", n_docs, cu[n_docs], total);
+  return CFA_OK;
+}
+
+struct Sizes {
+  int T, n_docs, hq, hkv, d, dtype;
+};
+
+int check_sizes(const Sizes& s, bool bwd) {
+  if (s.T < 0) return fail(CFA_ERR_SHAPE, "total_tokens = %d < 0", s.T);
+  if (s.n_docs < 1) return fail(CFA_ERR_SHAPE, "n_docs = %d < 1", s.n_docs);
+  if (s.hq < 1 || s.hkv < 1) return fail(CFA_ERR_SHAPE, "hq = %d, hkv = %d must be >= 1", s.hq, s.hkv);
+  if (s.hq % s.hkv) return fail(CFA_ERR_SHAPE, "hq = %d is not a multiple of hkv = %d", s.hq, s.hkv);
+  if ((long)s.T * s.hq * s.d > 0x7fffffffL * 8L) return fail(CFA_ERR_SHAPE, "tensor too large");
+  if (s.dtype != CFA_F32 && s.dtype != CFA_BF16 && s.dtype != CFA_MXFP8)
+    return fail(CFA_ERR_UNSUPPORTED, "dtype %d unknown", s.dtype);
+  if (s.dtype == CFA_MXFP8) {
+    if (s.d != 128) return fail(CFA_ERR_UNSUPPORTED, "MXFP8 supports d = 128 only (got %d)", s.d);
+  } else if (s.d != 64 && s.d != 128) {
+    return fail(CFA_ERR_UNSUPPORTED, "head dim %d unsupported (64 or 128)", s.d);
+  }
+  if (bwd && s.dtype == CFA_F32) return fail(CFA_ERR_UNSUPPORTED, "the fp32 path is forward-only");
+  return CFA_OK;
+}
+
+struct WsLayout {
+  size_t plan_end;
+  size_t delta;  // bwd: float [hq, T]
+  size_t total;
+};
+
+WsLayout ws_layout(int pass, const Sizes& s) {
+  WsLayout w{};
+  cfa::PlanLayout pl(s.n_docs);
+  w.plan_end = pl.end;
+  size_t off = pl.end;
+  if (pass == 1) {
+    w.delta = off;
+    off = cfa::align256(off + sizeof(float) * (size_t)s.hq * (size_t)s.T);
+  }
+  w.total = off;
+  return w;
+}
+
+cfa::Plan make_plan(void* ws, int n_docs) {
+  cfa::PlanLayout pl(n_docs);
+  char* b = (char*)ws;
+  cfa::Plan p;
+  p.docinfo = (const int2*)(b + pl.docinfo);
+  p.order = (const int*)(b + pl.order);
+  p.pref = (const int*)(b + pl.pref);
+  p.n_docs = n_docs;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cfa_version(void) { return (1 << 16) | 0; }
+
+const char* cfa_status_string(int s) {
+  switch (s) {
+    case CFA_OK: return "CFA_OK";
+    case CFA_ERR_NULL: return "CFA_ERR_NULL";
+    case CFA_ERR_SHAPE: return "CFA_ERR_SHAPE";
+    case CFA_ERR_UNSUPPORTED: return "CFA_ERR_UNSUPPORTED";
+    case CFA_ERR_ALIGN: return "CFA_ERR_ALIGN";
+    case CFA_ERR_WORKSPACE: return "CFA_ERR_WORKSPACE";
+    case CFA_ERR_HIP: return "CFA_ERR_HIP";
+    default: return "CFA_ERR_UNKNOWN";
+  }
+}
+
+const char* cfa_last_error(void) { return g_err; }
+
+size_t cfa_workspace_bytes(int pass, int total_tokens, int n_docs, int hq, int hkv, int d, int dtype) {
+  Sizes s{total_tokens, n_docs, hq, hkv, d, dtype};
+  if ((pass != 0 && pass != 1) || check_sizes(s, pass == 1) != CFA_OK) return 0;
+  return ws_layout(pass, s).total;
+}
+
+size_t cfa_saved_bytes(int total_tokens, int n_docs, int hq, int hkv, int d, int dtype) {
+  (void)total_tokens; (void)n_docs; (void)hq; (void)hkv; (void)d; (void)dtype;
+  return 0;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
+             const int32_t* cu_seqlens_host, int n_docs, int total_tokens, int max_seqlen, int hq, int hkv, int d,
+             float scale, int causal, int dtype, void* saved, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  g_err[0] = 0;
+  const Sizes s{total_tokens, n_docs, hq, hkv, d, dtype};
+  if (int st = check_sizes(s, false)) return st;
+  if (!cu_seqlens || !workspace) return fail(CFA_ERR_NULL, "cu_seqlens and workspace must not be NULL");
+  if (total_tokens > 0 && (!q || !k || !v || !o || !lse))
+    return fail(CFA_ERR_NULL, "q, k, v, o and lse must not be NULL");
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(CFA_ERR_SHAPE, "scale must be finite and > 0");
+  if (dtype == CFA_MXFP8) return fail(CFA_ERR_UNSUPPORTED, "MXFP8 forward not available in this build");
+  (void)saved;
+  for (const void* p : {q, k, v, (const void*)o, (const void*)lse, (const void*)cu_seqlens})
+    if (!aligned(p, 16)) return fail(CFA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (!aligned(workspace, 256)) return fail(CFA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const WsLayout wl = ws_layout(0, s);
+  if (workspace_bytes < wl.total)
+    return fail(CFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, wl.total);
+  if (int st = check_cu_host(cu_seqlens_host, n_docs, total_tokens, max_seqlen)) return st;
+
+  hipStream_t st = (hipStream_t)stream;
+  if (int r = check_hip(cfa::launch_plan(cu_seqlens, n_docs, total_tokens, workspace, st), "plan kernel")) return r;
+  if (total_tokens == 0) return CFA_OK;
+  const cfa::Plan plan = make_plan(workspace, n_docs);
+  hipError_t e;
+  if (dtype == CFA_F32)
+    e = cfa::launch_fwd_f32(q, k, v, o, lse, plan, plan.pref, total_tokens, hq, hkv, d, scale, causal, st);
+  else
+    e = cfa::launch_fwd_bf16(q, k, v, o, lse, plan, plan.pref, total_tokens, hq, hkv, d, scale, causal, st);
+  return check_hip(e, "forward kernel");
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+             const void* saved, void* dq, void* dk, void* dv, const int32_t* cu_seqlens,
+             const int32_t* cu_seqlens_host, int n_docs, int total_tokens, int max_seqlen, int hq, int hkv, int d,
+             float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  (void)q; (void)k; (void)v; (void)o; (void)lse; (void)dout; (void)saved; (void)dq; (void)dk; (void)dv;
+  (void)cu_seqlens; (void)cu_seqlens_host; (void)n_docs; (void)total_tokens; (void)max_seqlen; (void)hq;
+  (void)hkv; (void)d; (void)scale; (void)causal; (void)dtype; (void)workspace; (void)workspace_bytes; (void)stream;
+  return fail(CFA_ERR_UNSUPPORTED, "backward not available in this build");
+}
+
+int mx_padded_tokens(int total_tokens, int n_docs) {
+  if (total_tokens < 0 || n_docs < 0) return 0;
+  return (total_tokens + 31) / 32 * 32 + 32 * n_docs;
+}
+
+size_t mx_workspace_bytes(int n_docs) { return n_docs >= 1 ? cfa::PlanLayout(n_docs).end : 0; }
+
+int mx_quantize(const void* x, int total_tokens, int h, int d, const int32_t* cu_seqlens,
+                const int32_t* cu_seqlens_host, int n_docs, int axis, uint8_t* codes, uint8_t* scales, int t_pad,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  (void)x; (void)total_tokens; (void)h; (void)d; (void)cu_seqlens; (void)cu_seqlens_host; (void)n_docs;
+  (void)axis; (void)codes; (void)scales; (void)t_pad; (void)workspace; (void)workspace_bytes; (void)stream;
+  return fail(CFA_ERR_UNSUPPORTED, "mx_quantize not available in this build");
+}
+
+int cfa_device_error(const void* workspace, void* stream, int* flag) {
+  g_err[0] = 0;
+  if (!workspace || !flag) return fail(CFA_ERR_NULL, "workspace and flag must not be NULL");
+  hipStream_t st = (hipStream_t)stream;
+  int host = 0;
+  if (int r = check_hip(hipMemcpyAsync(&host, workspace, sizeof(int), hipMemcpyDeviceToHost, st), "read flag"))
+    return r;
+  if (int r = check_hip(hipStreamSynchronize(st), "synchronize")) return r;
+  *flag = host;
+  return CFA_OK;
+}
+
+}  // extern "C"

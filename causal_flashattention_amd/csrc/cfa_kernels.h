@@ -1,0 +1,19 @@
+// Launchers of the gfx950 kernels, called by the C-ABI host code.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "cfa_device.h"
+
+namespace cfa {
+
+hipError_t launch_plan(const int* cu, int n_docs, int total_tokens, void* ws, hipStream_t stream);
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, const Plan& plan,
+                           const int* pref_base, int total_tokens, int hq, int hkv, int d, float scale, int causal,
+                           hipStream_t stream);
+
+hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, const Plan& plan,
+                          const int* pref_base, int total_tokens, int hq, int hkv, int d, float scale, int causal,
+                          hipStream_t stream);
+
+}  // namespace cfa

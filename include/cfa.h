@@ -1,0 +1,147 @@
+/*
+ * cfa.h -- C ABI of the causal packed flash-attention library for AMD MI355X (gfx950).
+ *
+ * What the calls compute (sources are web pages, cited by title and section):
+ *
+ *   S = scale * Q K^T,  P = softmax(S + causal mask),  O = P V
+ *     "GPT Kernel Programlama: MatMul, Softmax ve Attention Hesabı" (dehayz.com), §2 and §3
+ *     (the equations and the score sum), §4 (a query never sees later tokens; the mask is
+ *     applied by index and never stored), §5 (softmax with the row maximum subtracted),
+ *     §6 (the value sum), §7 (tiles of Q/K/V on chip, online softmax, O written once).
+ *     "FlashAttention (HU)" (systems-analysis.info), sections "Tiling és blokkos feldolgozás",
+ *     "Online Softmax-számítás", "Műveletek összevonása egyetlen CUDA-kernelbe".
+ *   Packed variable-length documents, document-local attention, an MXFP8 path with
+ *   document-local token-block scales, a causal-leakage safeguard and forward/backward
+ *   consistency:
+ *     "FLAMIA: Blackwell Üzerinde Hızlı ve Nedensel Olarak Güvenli Eğitim İçin Flash
+ *     Mikro-Ölçeklemeli Dikkat Mekanizması" (blog.edumints.com), section "FLAMIA Mimarisi ve
+ *     Temel Tasarım İlkeleri".
+ *
+ * Conventions for every call
+ * --------------------------
+ *  - Tensors are packed tokens x heads x head-dim, row-major and contiguous:
+ *      q, o, dout, dq : [total_tokens, hq,  d]
+ *      k, v, dk, dv   : [total_tokens, hkv, d]
+ *      lse            : [hq, total_tokens] float32, natural log of sum_j exp(scaled masked score)
+ *    Element type: float32 for CFA_F32, bfloat16 (raw 16-bit patterns) otherwise.
+ *  - cu_seqlens: int32 [n_docs + 1] in DEVICE memory, cu[0] = 0, non-decreasing,
+ *    cu[n_docs] = total_tokens. Document n owns packed rows cu[n] .. cu[n+1]-1; attention
+ *    never crosses documents. Empty documents are allowed. cu_seqlens_host is an optional
+ *    host copy: when given it is validated before anything is launched.
+ *  - Query head h reads kv head h / (hq / hkv) (consecutive query heads share a kv head).
+ *  - causal != 0: doc-local key j is visible to doc-local query i iff j <= i.
+ *  - Ownership: the caller owns every buffer. The library allocates no device memory, keeps no
+ *    state between calls and never synchronises the stream; every call only enqueues work on
+ *    `stream` (a hipStream_t; NULL is the default stream). Inputs are never written.
+ *  - Pointers must be 16-byte aligned. Scratch memory is the caller's `workspace`, at least
+ *    cfa_workspace_bytes(...) bytes, 256-byte aligned.
+ *  - Errors: every precondition the host can check is checked before any launch; on failure the
+ *    call returns a non-zero cfa_status, writes nothing, and cfa_last_error() describes it.
+ *    A device-only cu_seqlens that turns out malformed is clamped (bad documents become empty)
+ *    and a flag is raised in the workspace, readable with cfa_device_error().
+ */
+#ifndef CFA_H
+#define CFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { CFA_F32 = 0, CFA_BF16 = 1, CFA_MXFP8 = 2 } cfa_dtype;
+
+typedef enum {
+  CFA_OK = 0,
+  CFA_ERR_NULL = 1,         /* a required pointer is NULL */
+  CFA_ERR_SHAPE = 2,        /* inconsistent sizes or a malformed host cu_seqlens */
+  CFA_ERR_UNSUPPORTED = 3,  /* valid but not implemented (head dim, dtype/pass combination) */
+  CFA_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned (workspace: 256) */
+  CFA_ERR_WORKSPACE = 5,    /* workspace smaller than cfa_workspace_bytes() */
+  CFA_ERR_HIP = 6           /* a HIP runtime call or kernel launch failed */
+} cfa_status;
+
+/* Library version, (major << 16) | minor. */
+int cfa_version(void);
+
+/* Human-readable name of a status code. Static storage. */
+const char* cfa_status_string(int status);
+
+/* Detail of the last failure on the calling thread (thread-local, static storage). */
+const char* cfa_last_error(void);
+
+/* Scratch bytes needed by attn_fwd (pass 0) or attn_bwd (pass 1) for these sizes. Depends only
+ * on the sizes, never on the values of cu_seqlens. Returns 0 for invalid sizes. */
+size_t cfa_workspace_bytes(int pass, int total_tokens, int n_docs, int hq, int hkv, int d, int dtype);
+
+/* Bytes of the forward-to-backward buffer `saved` (MXFP8 only: the d-blocked E4M3 copies of Q
+ * and K with their scales, reused by the backward so both passes see identical scores).
+ * 0 for the other dtypes. */
+size_t cfa_saved_bytes(int total_tokens, int n_docs, int hq, int hkv, int d, int dtype);
+
+/*
+ * Forward pass. Writes o and lse.
+ *   max_seqlen : upper bound on any document length (0 = unknown; then total_tokens is used).
+ *   scale      : multiplier of Q K^T (usually 1/sqrt(d)); finite and > 0.
+ *   dtype      : CFA_F32 (d = 64 or 128), CFA_BF16 (d = 64 or 128), CFA_MXFP8 (d = 128).
+ *   saved      : CFA_MXFP8: cfa_saved_bytes() bytes written here for attn_bwd; otherwise NULL.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+             int n_docs, int total_tokens, int max_seqlen, int hq, int hkv, int d,
+             float scale, int causal, int dtype, void* saved,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass: dq, dk, dv (same layouts and element type as q, k, v) from q, k, v, the
+ * forward's o and lse, and the upstream gradient dout. The gradient is that of O only (no
+ * gradient flows into lse). dtype CFA_BF16 or CFA_MXFP8 (CFA_F32 is forward-only).
+ *   saved : CFA_MXFP8: the buffer attn_fwd filled, unmodified; otherwise NULL.
+ * Deterministic: two calls on the same inputs give bit-identical outputs.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, const void* saved, void* dq, void* dk, void* dv,
+             const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+             int n_docs, int total_tokens, int max_seqlen, int hq, int hkv, int d,
+             float scale, int causal, int dtype,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * MX quantiser: bf16 x [total_tokens, h, d] -> E4M3 codes + E8M0 scales, one scale per block of
+ * 32 elements. Rule per block: amax = max|x|; e = floor(log2 amax) - 8 clamped to [-127, 127]
+ * (e = -127 for an all-zero block); scale byte e + 127; element = x * 2^-e saturated to +-448
+ * and rounded to nearest E4M3 (ties to even, sign of zero kept); a block holding NaN or Inf gets
+ * scale byte 0xFF and codes 0x7F.
+ *   axis 0 : blocks of 32 channels along d.   codes [T, h, d], scales [T, h, d/32].
+ *   axis 1 : blocks of 32 doc-local tokens.   codes [h, d, t_pad], scales [h, d, t_pad/32],
+ *            document n starting at column P_n = sum_{m<n} 32*ceil(L_m/32); a document's last
+ *            block holds only its own tokens; padding columns get code 0x00 and belong to no
+ *            scale. t_pad is the row stride of both outputs: a multiple of 32 and at least
+ *            mx_padded_tokens(total_tokens, n_docs) (columns past P_{n_docs} are left as is).
+ * workspace: at least mx_workspace_bytes(n_docs) bytes (axis 1 only; may be NULL for axis 0).
+ */
+int mx_quantize(const void* x, int total_tokens, int h, int d,
+                const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int n_docs, int axis,
+                uint8_t* codes, uint8_t* scales, int t_pad,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Upper bound of P_{n_docs} for any cu_seqlens with these sizes, rounded up to 32:
+ * 32*ceil(total_tokens/32) + 32*n_docs. */
+int mx_padded_tokens(int total_tokens, int n_docs);
+
+/* Scratch bytes of mx_quantize along tokens. */
+size_t mx_workspace_bytes(int n_docs);
+
+/*
+ * Reads the device-side validation flag left in `workspace` by the last attn_fwd / attn_bwd /
+ * mx_quantize call that used it. Synchronises `stream`. *flag = 0: cu_seqlens was well formed;
+ * otherwise bit 0 = cu[0] != 0, bit 1 = a decreasing entry, bit 2 = cu[n_docs] != total_tokens.
+ */
+int cfa_device_error(const void* workspace, void* stream, int* flag);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CFA_H */
