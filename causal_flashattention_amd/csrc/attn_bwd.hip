@@ -1,0 +1,429 @@
+// Recomputing causal attention backward for gfx950 (bf16 MFMA), deterministic.
+//
+// The pages only name the backward pass (FLAMIA page, "FLAMIA Mimarisi ve Temel Tasarım
+// İlkeleri": forward and backward must agree numerically). The kernels compute the exact
+// derivative of the forward definition ("GPT Kernel Programlama" §2-§6), recomputing the
+// probabilities tile by tile from the saved row log-sum-exp instead of storing P:
+//   P_ij  = exp(scale·q_i·k_j − LSE_i)           (0 where key j is masked)
+//   D_i   = Σ_r dO_ir O_ir                        -- bwd_pre_kernel
+//   dP_ij = dO_i·v_j,  dS_ij = P_ij (dP_ij − D_i)
+//   dV_j  = Σ_{h in group} Σ_i P_ij dO_i           -- attn_bwd_dkdv_kernel
+//   dK_j  = scale Σ_{h in group} Σ_i dS_ij q_i     -- attn_bwd_dkdv_kernel
+//   dQ_i  = scale Σ_j dS_ij k_j                    -- attn_bwd_dq_kernel (separate pass)
+// No floating-point atomics: each output element is summed by one lane in a fixed order, so
+// reruns are bit-identical and a token never receives contributions through shared state.
+//
+// dK/dV kernel: a workgroup owns 128 keys of one kv head (4 waves × 32 keys). Each wave keeps
+// its K and V rows in registers as MFMA B operands and accumulates dKᵀ and dVᵀ (d × 32 keys).
+// It walks the query tiles (64 queries, double-buffered in LDS with their LSE and D) of every
+// query head of the group, from the diagonal to the end of the document:
+//   S  = Q Kᵀ        A = Q tile rows (LDS)          -> lane holds one key, 16 queries
+//   dP = dO Vᵀ       A = dO tile rows (LDS)
+//   dVᵀ += dOᵀ P     A = dOᵀ via ds_read_b64_tr_b16, B = P as computed (bf16)
+//   dKᵀ += Qᵀ dS     A = Qᵀ via ds_read_b64_tr_b16, B = dS as computed (bf16)
+// dQ kernel: the forward's layout (a wave owns 32 queries, Qᵀ and dOᵀ fragments in registers),
+// key tiles of 64 double-buffered in LDS:
+//   Sᵀ = K Qᵀ, dPᵀ = V dOᵀ (A = K / V tile rows), dQᵀ += Kᵀ dSᵀ (A = Kᵀ via transposing reads).
+#include "cfa_device.h"
+
+namespace cfa {
+
+// ------------------------------------------------------------------ D = rowsum(dO ∘ O)
+// 16 lanes per (token, head) row of 128 (8 lanes for d = 64), 16 bytes per lane.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
+                                                      float* __restrict__ delta, int total_tokens, int hq) {
+  constexpr int LPR = D / 8;  // lanes per row
+  const long row = (long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int sub = threadIdx.x % LPR;
+  const long rows = (long)total_tokens * hq;
+  float acc = 0.f;
+  if (row < rows) {
+    const i32x4 a = *(const i32x4*)(o + row * D + sub * 8);
+    const i32x4 b = *(const i32x4*)(dout + row * D + sub * 8);
+    const bf16x8 x = __builtin_bit_cast(bf16x8, a), y = __builtin_bit_cast(bf16x8, b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && sub == 0) {
+    const int t = (int)(row / hq), h = (int)(row % hq);
+    delta[(size_t)h * total_tokens + t] = acc;
+  }
+}
+
+template <int D>
+struct BwdTile {
+  static constexpr int RSTR = D * 2 + 16;   // LDS row stride (bytes), tiles read row-wise and transposed
+  static constexpr int DS = D / 16;
+  static constexpr int DB = D / 32;
+};
+
+// ------------------------------------------------------------------ dK / dV
+template <int D>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    __bf16* __restrict__ dk, __bf16* __restrict__ dv, Plan plan, int total_tokens, int hq, int hkv,
+    float scale, int causal) {
+  using C = BwdTile<D>;
+  constexpr int BM = 64;                         // queries per step
+  constexpr int TILE = BM * C::RSTR;             // bytes of one Q (or dO) tile
+  constexpr int STAGE = 2 * TILE + 2 * BM * 4;   // Q, dO, lse2, delta
+  constexpr int CH = BM * D / 8;                 // 16-byte chunks per tile
+  constexpr int PT = CH / 256;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int p = blockIdx.x / hkv, g = blockIdx.x % hkv;
+  int s0, L, t;
+  if (!decode_item(plan, p, 128, false, s0, L, t)) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5;
+  const int G = hq / hkv;
+  const int kw0 = t * 128 + 32 * w;              // first doc-local key of this wave
+  const int mykey = kw0 + (lane & 31);
+  const float sl2 = scale * LOG2E;
+
+  // K and V rows of this wave as B operands (lane: key mykey, d = 16s + 8·half ..)
+  bf16x8 kf[C::DS], vf[C::DS];
+  {
+    const bool ok = mykey < L;
+    const size_t off = ((size_t)(s0 + (ok ? mykey : 0)) * hkv + g) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < C::DS; ++s) {
+      kf[s] = __builtin_bit_cast(bf16x8, ok ? *(const i32x4*)(k + off + 16 * s) : i32x4{0, 0, 0, 0});
+      vf[s] = __builtin_bit_cast(bf16x8, ok ? *(const i32x4*)(v + off + 16 * s) : i32x4{0, 0, 0, 0});
+    }
+  }
+  f32x16 dka[C::DB], dva[C::DB];
+#pragma unroll
+  for (int b = 0; b < C::DB; ++b) { dka[b] = f32x16{}; dva[b] = f32x16{}; }
+
+  const int q_begin = causal ? t * 128 : 0;      // first query that can see this tile (64-aligned)
+  const int n_qt = (L - q_begin + BM - 1) / BM;  // query tiles per head
+  const int n_steps = n_qt * G;
+  const int wave_first_q = causal ? kw0 : 0;
+
+  i32x4 qreg[PT], oreg[PT];
+  float lreg = 0.f, dreg = 0.f;
+  auto load_step = [&](int st) {
+    const int h = g * G + st / n_qt;
+    const int q0 = q_begin + (st % n_qt) * BM;
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int row = c / (D / 8), col = c % (D / 8);
+      const bool ok = q0 + row < L;
+      const size_t off = ((size_t)(s0 + (ok ? q0 + row : 0)) * hq + h) * D + col * 8;
+      qreg[i] = ok ? *(const i32x4*)(q + off) : i32x4{0, 0, 0, 0};
+      oreg[i] = ok ? *(const i32x4*)(dout + off) : i32x4{0, 0, 0, 0};
+    }
+    if (threadIdx.x < BM) {
+      const int qi = q0 + threadIdx.x;
+      const bool ok = qi < L;
+      // masked-out rows get an LSE of +inf so that their probabilities are exactly 0
+      lreg = ok ? lse[(size_t)h * total_tokens + s0 + qi] * LOG2E : INFINITY;
+      dreg = ok ? delta[(size_t)h * total_tokens + s0 + qi] : 0.f;
+    }
+  };
+  auto store_step = [&](int buf) {
+    char* qb = smem + buf * STAGE;
+    char* ob = qb + TILE;
+    float* lb = (float*)(ob + TILE);
+    float* db = lb + BM;
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int row = c / (D / 8), col = c % (D / 8);
+      *(i32x4*)(qb + row * C::RSTR + col * 16) = qreg[i];
+      *(i32x4*)(ob + row * C::RSTR + col * 16) = oreg[i];
+    }
+    if (threadIdx.x < BM) { lb[threadIdx.x] = lreg; db[threadIdx.x] = dreg; }
+  };
+
+  if (n_steps > 0) {
+    load_step(0);
+    store_step(0);
+  }
+  __syncthreads();
+  for (int st = 0; st < n_steps; ++st) {
+    if (st + 1 < n_steps) load_step(st + 1);
+    const int q0 = q_begin + (st % n_qt) * BM;
+    if (q0 + BM - 1 >= wave_first_q && mykey - (lane & 31) < L) {
+      const char* qb = smem + (st & 1) * STAGE;
+      const char* ob = qb + TILE;
+      const float* lb = (const float*)(ob + TILE);
+      const float* db = lb + BM;
+      const bool need_mask = causal && (q0 < kw0 + 31);
+      bf16x8 pf[4], sf[4];
+#pragma unroll
+      for (int qb2 = 0; qb2 < 2; ++qb2) {
+        f32x16 sacc = f32x16{}, pacc = f32x16{};
+        const char* qrow = qb + (32 * qb2 + (lane & 31)) * C::RSTR + 16 * half;
+        const char* orow = ob + (32 * qb2 + (lane & 31)) * C::RSTR + 16 * half;
+#pragma unroll
+        for (int s = 0; s < C::DS; ++s) {
+          sacc = mfma32(__builtin_bit_cast(bf16x8, *(const i32x4*)(qrow + 32 * s)), kf[s], sacc);
+          pacc = mfma32(__builtin_bit_cast(bf16x8, *(const i32x4*)(orow + 32 * s)), vf[s], pacc);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+          float pv[2], dsv[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int qi_t = 32 * qb2 + 8 * ((j + u) >> 2) + 4 * half + ((j + u) & 3);  // tile-local query
+            float x = exp2f(sacc[j + u] * sl2 - lb[qi_t]);
+            if (need_mask && mykey > q0 + qi_t) x = 0.f;
+            pv[u] = x;
+            dsv[u] = x * (pacc[j + u] - db[qi_t]);
+          }
+          const int fi = 2 * qb2 + (j >> 3);
+          i32x4 up = __builtin_bit_cast(i32x4, pf[fi]);
+          i32x4 us = __builtin_bit_cast(i32x4, sf[fi]);
+          up[(j & 7) >> 1] = (int)pack_bf16x2(pv[0], pv[1]);
+          us[(j & 7) >> 1] = (int)pack_bf16x2(dsv[0], dsv[1]);
+          pf[fi] = __builtin_bit_cast(bf16x8, up);
+          sf[fi] = __builtin_bit_cast(bf16x8, us);
+        }
+      }
+      // dVᵀ += dOᵀ P,  dKᵀ += Qᵀ dS  (A operands through transposing LDS reads)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int rbase = 32 * (kk >> 1) + 16 * (kk & 1);
+        const int row = rbase + 4 * half + ((lane & 15) >> 2);
+        const int dsub = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+        for (int dbk = 0; dbk < C::DB; ++dbk) {
+          const int boff = row * C::RSTR + (32 * dbk + dsub) * 2;
+          const bf16x8 ao = concat_tr(lds_read_tr16(ob + boff), lds_read_tr16(ob + boff + 8 * C::RSTR));
+          dva[dbk] = mfma32(ao, pf[kk], dva[dbk]);
+          const bf16x8 aq = concat_tr(lds_read_tr16(qb + boff), lds_read_tr16(qb + boff + 8 * C::RSTR));
+          dka[dbk] = mfma32(aq, sf[kk], dka[dbk]);
+        }
+      }
+    }
+    if (st + 1 < n_steps) store_step((st + 1) & 1);
+    __syncthreads();
+  }
+
+  // write dK = scale·dKᵀ and dV (lane: key mykey, d = 32 db + 8 jg + 4·half + 0..3)
+  if (mykey < L) {
+    const size_t base = ((size_t)(s0 + mykey) * hkv + g) * D + 4 * half;
+#pragma unroll
+    for (int dbk = 0; dbk < C::DB; ++dbk)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        i32x2 uk, uv;
+        uk.x = (int)pack_bf16x2(dka[dbk][4 * jg] * scale, dka[dbk][4 * jg + 1] * scale);
+        uk.y = (int)pack_bf16x2(dka[dbk][4 * jg + 2] * scale, dka[dbk][4 * jg + 3] * scale);
+        uv.x = (int)pack_bf16x2(dva[dbk][4 * jg], dva[dbk][4 * jg + 1]);
+        uv.y = (int)pack_bf16x2(dva[dbk][4 * jg + 2], dva[dbk][4 * jg + 3]);
+        *(i32x2*)(dk + base + 32 * dbk + 8 * jg) = uk;
+        *(i32x2*)(dv + base + 32 * dbk + 8 * jg) = uv;
+      }
+  }
+}
+
+// ------------------------------------------------------------------ dQ
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    __bf16* __restrict__ dq, Plan plan, int total_tokens, int hq, int hkv, float scale, int causal) {
+  using C = BwdTile<D>;
+  constexpr int BN = 64;
+  constexpr int TILE = BN * C::RSTR;
+  constexpr int STAGE = 2 * TILE;
+  constexpr int CH = BN * D / 8;
+  constexpr int PT = CH / 256;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int p = blockIdx.x / hq, h = blockIdx.x % hq;
+  int s0, L, t;
+  if (!decode_item(plan, p, 128, true, s0, L, t)) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5;
+  const int g = h / (hq / hkv);
+  const int wr0 = t * 128 + 32 * w;
+  const int qrow = wr0 + (lane & 31);
+  const int kv_end = causal ? min(L, (t + 1) * 128) : L;
+  const int n_kt = (kv_end + BN - 1) / BN;
+  const int wave_last_key = causal ? min(L, wr0 + 32) - 1 : L - 1;
+  const float sl2 = scale * LOG2E;
+
+  bf16x8 qf[C::DS], of[C::DS];
+  float lse2 = INFINITY, dl = 0.f;
+  {
+    const bool ok = qrow < L;
+    const size_t off = ((size_t)(s0 + (ok ? qrow : 0)) * hq + h) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < C::DS; ++s) {
+      qf[s] = __builtin_bit_cast(bf16x8, ok ? *(const i32x4*)(q + off + 16 * s) : i32x4{0, 0, 0, 0});
+      of[s] = __builtin_bit_cast(bf16x8, ok ? *(const i32x4*)(dout + off + 16 * s) : i32x4{0, 0, 0, 0});
+    }
+    if (ok) {
+      lse2 = lse[(size_t)h * total_tokens + s0 + qrow] * LOG2E;
+      dl = delta[(size_t)h * total_tokens + s0 + qrow];
+    }
+  }
+  f32x16 dqa[C::DB];
+#pragma unroll
+  for (int b = 0; b < C::DB; ++b) dqa[b] = f32x16{};
+
+  i32x4 kreg[PT], vreg[PT];
+  auto load_tile = [&](int kt) {
+    const int k0 = kt * BN;
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int key = c / (D / 8), col = c % (D / 8);
+      const bool ok = (k0 + key) < kv_end;
+      const size_t off = ((size_t)(s0 + (ok ? k0 + key : 0)) * hkv + g) * D + col * 8;
+      kreg[i] = ok ? *(const i32x4*)(k + off) : i32x4{0, 0, 0, 0};
+      vreg[i] = ok ? *(const i32x4*)(v + off) : i32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_tile = [&](int buf) {
+    char* kb = smem + buf * STAGE;
+    char* vb = kb + TILE;
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int key = c / (D / 8), col = c % (D / 8);
+      *(i32x4*)(kb + key * C::RSTR + col * 16) = kreg[i];
+      *(i32x4*)(vb + key * C::RSTR + col * 16) = vreg[i];
+    }
+  };
+
+  if (n_kt > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int k0 = kt * BN;
+    if (kt + 1 < n_kt) load_tile(kt + 1);
+    if (k0 <= wave_last_key) {
+      const char* kb = smem + (kt & 1) * STAGE;
+      const char* vb = kb + TILE;
+      const bool need_mask = causal ? (k0 + BN - 1 > wr0) : (k0 + BN > L);
+      bf16x8 sf[4];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        f32x16 sacc = f32x16{}, pacc = f32x16{};
+        const char* krow = kb + (32 * b + (lane & 31)) * C::RSTR + 16 * half;
+        const char* vrow = vb + (32 * b + (lane & 31)) * C::RSTR + 16 * half;
+#pragma unroll
+        for (int s = 0; s < C::DS; ++s) {
+          sacc = mfma32(__builtin_bit_cast(bf16x8, *(const i32x4*)(krow + 32 * s)), qf[s], sacc);
+          pacc = mfma32(__builtin_bit_cast(bf16x8, *(const i32x4*)(vrow + 32 * s)), of[s], pacc);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+          float dsv[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            float x = exp2f(sacc[j + u] * sl2 - lse2);
+            if (need_mask) {
+              const int key = k0 + 32 * b + 8 * ((j + u) >> 2) + 4 * half + ((j + u) & 3);
+              if (causal ? (key > qrow) : (key >= L)) x = 0.f;
+            }
+            dsv[u] = x * (pacc[j + u] - dl);
+          }
+          const int fi = 2 * b + (j >> 3);
+          i32x4 us = __builtin_bit_cast(i32x4, sf[fi]);
+          us[(j & 7) >> 1] = (int)pack_bf16x2(dsv[0], dsv[1]);
+          sf[fi] = __builtin_bit_cast(bf16x8, us);
+        }
+      }
+      // dQᵀ += Kᵀ dSᵀ
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int kbase = 32 * (kk >> 1) + 16 * (kk & 1);
+        const int key = kbase + 4 * half + ((lane & 15) >> 2);
+        const int dsub = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+        for (int dbk = 0; dbk < C::DB; ++dbk) {
+          const char* p0 = kb + key * C::RSTR + (32 * dbk + dsub) * 2;
+          dqa[dbk] = mfma32(concat_tr(lds_read_tr16(p0), lds_read_tr16(p0 + 8 * C::RSTR)), sf[kk], dqa[dbk]);
+        }
+      }
+    }
+    if (kt + 1 < n_kt) store_tile((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  if (qrow < L) {
+    __bf16* dst = dq + ((size_t)(s0 + qrow) * hq + h) * D + 4 * half;
+#pragma unroll
+    for (int dbk = 0; dbk < C::DB; ++dbk)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        i32x2 u;
+        u.x = (int)pack_bf16x2(dqa[dbk][4 * jg] * scale, dqa[dbk][4 * jg + 1] * scale);
+        u.y = (int)pack_bf16x2(dqa[dbk][4 * jg + 2] * scale, dqa[dbk][4 * jg + 3] * scale);
+        *(i32x2*)(dst + 32 * dbk + 8 * jg) = u;
+      }
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+hipError_t launch_bwd_pre(const void* o, const void* dout, float* delta, int total_tokens, int hq, int d,
+                          hipStream_t stream) {
+  const long rows = (long)total_tokens * hq;
+  if (rows == 0) return hipSuccess;
+  const int rpb = 256 / (d / 8);
+  const long grid = (rows + rpb - 1) / rpb;
+  if (d == 128)
+    hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)o,
+                       (const __bf16*)dout, delta, total_tokens, hq);
+  else
+    hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)o,
+                       (const __bf16*)dout, delta, total_tokens, hq);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bwd_main_d(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                                    const float* delta, void* dq, void* dk, void* dv, const Plan& plan_any,
+                                    const int* pref_base, int T, int hq, int hkv, float scale, int causal,
+                                    hipStream_t stream) {
+  Plan plan = plan_any;
+  plan.pref = pref_base + pref_slot(128) * (plan.n_docs + 1);
+  const long items = (long)(T + 127) / 128 + plan.n_docs;
+  {
+    constexpr int STAGE = 2 * 64 * BwdTile<D>::RSTR + 2 * 64 * 4;
+    auto kern = attn_bwd_dkdv_kernel<D>;
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE))
+      return hipErrorInvalidConfiguration;
+    const long grid = items * hkv;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 2 * STAGE, stream, (const __bf16*)q, (const __bf16*)k,
+                       (const __bf16*)v, (const __bf16*)dout, lse, delta, (__bf16*)dk, (__bf16*)dv, plan, T, hq, hkv,
+                       scale, causal);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  {
+    constexpr int STAGE = 2 * 64 * BwdTile<D>::RSTR;
+    auto kern = attn_bwd_dq_kernel<D>;
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE))
+      return hipErrorInvalidConfiguration;
+    const long grid = items * hq;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 2 * STAGE, stream, (const __bf16*)q, (const __bf16*)k,
+                       (const __bf16*)v, (const __bf16*)dout, lse, delta, (__bf16*)dq, plan, T, hq, hkv, scale,
+                       causal);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                           const float* delta, void* dq, void* dk, void* dv, const Plan& plan, const int* pref_base,
+                           int T, int hq, int hkv, int d, float scale, int causal, hipStream_t stream) {
+  if (d == 128)
+    return launch_bwd_main_d<128>(q, k, v, dout, lse, delta, dq, dk, dv, plan, pref_base, T, hq, hkv, scale, causal,
+                                  stream);
+  return launch_bwd_main_d<64>(q, k, v, dout, lse, delta, dq, dk, dv, plan, pref_base, T, hq, hkv, scale, causal,
+                               stream);
+}
+
+}  // namespace cfa

@@ -168,10 +168,32 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              const int32_t* cu_seqlens_host, int n_docs, int total_tokens, int max_seqlen, int hq, int hkv, int d,
              float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
-  (void)q; (void)k; (void)v; (void)o; (void)lse; (void)dout; (void)saved; (void)dq; (void)dk; (void)dv;
-  (void)cu_seqlens; (void)cu_seqlens_host; (void)n_docs; (void)total_tokens; (void)max_seqlen; (void)hq;
-  (void)hkv; (void)d; (void)scale; (void)causal; (void)dtype; (void)workspace; (void)workspace_bytes; (void)stream;
-  return fail(CFA_ERR_UNSUPPORTED, "backward not available in this build");
+  const Sizes s{total_tokens, n_docs, hq, hkv, d, dtype};
+  if (int st = check_sizes(s, true)) return st;
+  if (!cu_seqlens || !workspace) return fail(CFA_ERR_NULL, "cu_seqlens and workspace must not be NULL");
+  if (total_tokens > 0 && (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv))
+    return fail(CFA_ERR_NULL, "q, k, v, o, lse, dout, dq, dk and dv must not be NULL");
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(CFA_ERR_SHAPE, "scale must be finite and > 0");
+  if (dtype == CFA_MXFP8) return fail(CFA_ERR_UNSUPPORTED, "MXFP8 backward not available in this build");
+  (void)saved;
+  for (const void* p : {q, k, v, o, (const void*)lse, dout, (const void*)dq, (const void*)dk, (const void*)dv,
+                        (const void*)cu_seqlens})
+    if (!aligned(p, 16)) return fail(CFA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (!aligned(workspace, 256)) return fail(CFA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const WsLayout wl = ws_layout(1, s);
+  if (workspace_bytes < wl.total)
+    return fail(CFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, wl.total);
+  if (int st = check_cu_host(cu_seqlens_host, n_docs, total_tokens, max_seqlen)) return st;
+
+  hipStream_t st = (hipStream_t)stream;
+  if (int r = check_hip(cfa::launch_plan(cu_seqlens, n_docs, total_tokens, workspace, st), "plan kernel")) return r;
+  if (total_tokens == 0) return CFA_OK;
+  const cfa::Plan plan = make_plan(workspace, n_docs);
+  float* delta = (float*)((char*)workspace + wl.delta);
+  if (int r = check_hip(cfa::launch_bwd_pre(o, dout, delta, total_tokens, hq, d, st), "bwd preprocess")) return r;
+  return check_hip(cfa::launch_bwd_main(q, k, v, dout, lse, delta, dq, dk, dv, plan, plan.pref, total_tokens, hq,
+                                        hkv, d, scale, causal, st),
+                   "backward kernels");
 }
 
 int mx_padded_tokens(int total_tokens, int n_docs) {

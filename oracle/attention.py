@@ -133,3 +133,53 @@ def attn_bwd(q, k, v, do, cu_seqlens, scale, causal=True, row_block=ROW_BLOCK):
                 dk[s0:s1, g, :] += scale * (ds.T @ qb)
                 dv[s0:s1, g, :] += p.T @ dob
     return dq, dk, dv
+
+
+def attn_rows(q, k, v, do, rows, scale, causal=True):
+    """Selected query rows of ONE document (doc-local arrays), forward and backward by definition.
+
+    For large documents where the full oracle is too slow: every quantity of query row i
+    depends only on row i's softmax over keys 0..i (or all keys when not causal), so rows can
+    be computed one block at a time. ``q, do [L, hq, d]``, ``k, v [L, hkv, d]``; ``rows`` is a
+    sorted 1-D array of doc-local query indices. Returns
+
+        o [len(rows), hq, d], lse [hq, len(rows)], dq [len(rows), hq, d],
+        dk_part, dv_part [L, hkv, d] -- the contributions of the selected rows only; for a key j
+        they are the complete dK/dV when ``rows`` covers every query that can see j.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    do = np.asarray(do, np.float64)
+    rows = np.asarray(rows, np.int64)
+    L, hq, d = q.shape
+    hkv = k.shape[1]
+    group = hq // hkv
+    n = len(rows)
+    o = np.zeros((n, hq, d))
+    lse = np.zeros((hq, n))
+    dq = np.zeros((n, hq, d))
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for h in range(hq):
+        g = h // group
+        for r0 in range(0, n, 256):
+            rs = rows[r0:r0 + 256]
+            s = scale * (q[rs, h] @ k[:, g].T)
+            mask = np.zeros_like(s)
+            if causal:
+                mask[np.arange(L)[None, :] > rs[:, None]] = -np.inf
+            z = s + mask
+            m = z.max(axis=1)
+            e = np.exp(z - m[:, None])
+            l = e.sum(axis=1)
+            p = e / l[:, None]
+            ob = p @ v[:, g]
+            o[r0:r0 + len(rs), h] = ob
+            lse[h, r0:r0 + len(rs)] = m + np.log(l)
+            D = np.sum(do[rs, h] * ob, axis=1)
+            ds = p * (do[rs, h] @ v[:, g].T - D[:, None])
+            dq[r0:r0 + len(rs), h] = scale * (ds @ k[:, g])
+            dk[:, g] += scale * (ds.T @ q[rs, h])
+            dv[:, g] += p.T @ do[rs, h]
+    return o, lse, dq, dk, dv

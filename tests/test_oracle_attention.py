@@ -275,3 +275,21 @@ def test_mask_is_explicit_upper_triangle():
         for j in range(7):
             assert m[i, j] == (-np.inf if j > i + 2 else 0.0)
     assert np.all(att.causal_mask(3, 0, 5, False) == 0)
+
+
+def test_row_subset_matches_full_oracle():
+    lengths = [150]
+    q, k, v, do, cu = _rand_case(lengths, 4, 2, 8, seed=14)
+    o, lse = att.attn_fwd(q, k, v, cu, 0.3)
+    dq, dk, dv = att.attn_bwd(q, k, v, do, cu, 0.3)
+    rows = np.array([0, 7, 64, 149])
+    ro, rl, rdq, _, _ = att.attn_rows(q, k, v, do, rows, 0.3)
+    np.testing.assert_allclose(ro, o[rows], atol=1e-12)
+    np.testing.assert_allclose(rl, lse[:, rows], atol=1e-12)
+    np.testing.assert_allclose(rdq, dq[rows], atol=1e-12)
+    # rows 100.. cover every query that sees keys 100..149
+    _, _, _, pdk, pdv = att.attn_rows(q, k, v, do, np.arange(100, 150), 0.3)
+    np.testing.assert_allclose(pdk[100:], dk[100:], atol=1e-12)
+    np.testing.assert_allclose(pdv[100:], dv[100:], atol=1e-12)
+    _, _, _, fdk, fdv = att.attn_rows(q, k, v, do, np.arange(150), 0.3, causal=True)
+    np.testing.assert_allclose(fdk, dk, atol=1e-12)
