@@ -383,47 +383,54 @@ hipError_t launch_bwd_pre(const void* o, const void* dout, float* delta, int tot
 }
 
 template <int D>
-static hipError_t launch_bwd_main_d(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                                    const float* delta, void* dq, void* dk, void* dv, const Plan& plan_any,
-                                    const int* pref_base, int T, int hq, int hkv, float scale, int causal,
-                                    hipStream_t stream) {
-  Plan plan = plan_any;
-  plan.pref = pref_base + pref_slot(128) * (plan.n_docs + 1);
+static hipError_t launch_dkdv_d(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                                const float* delta, void* dk, void* dv, const Plan& plan, int T, int hq, int hkv,
+                                float scale, int causal, hipStream_t stream) {
   const long items = (long)(T + 127) / 128 + plan.n_docs;
-  {
-    constexpr int STAGE = 2 * 64 * BwdTile<D>::RSTR + 2 * 64 * 4;
-    auto kern = attn_bwd_dkdv_kernel<D>;
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE))
-      return hipErrorInvalidConfiguration;
-    const long grid = items * hkv;
-    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 2 * STAGE, stream, (const __bf16*)q, (const __bf16*)k,
-                       (const __bf16*)v, (const __bf16*)dout, lse, delta, (__bf16*)dk, (__bf16*)dv, plan, T, hq, hkv,
-                       scale, causal);
-    if (hipError_t e = hipGetLastError()) return e;
-  }
-  {
-    constexpr int STAGE = 2 * 64 * BwdTile<D>::RSTR;
-    auto kern = attn_bwd_dq_kernel<D>;
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE))
-      return hipErrorInvalidConfiguration;
-    const long grid = items * hq;
-    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 2 * STAGE, stream, (const __bf16*)q, (const __bf16*)k,
-                       (const __bf16*)v, (const __bf16*)dout, lse, delta, (__bf16*)dq, plan, T, hq, hkv, scale,
-                       causal);
-  }
+  constexpr int STAGE = 2 * 64 * BwdTile<D>::RSTR + 2 * 64 * 4;
+  auto kern = attn_bwd_dkdv_kernel<D>;
+  if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE))
+    return hipErrorInvalidConfiguration;
+  const long grid = items * hkv;
+  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 2 * STAGE, stream, (const __bf16*)q, (const __bf16*)k,
+                     (const __bf16*)v, (const __bf16*)dout, lse, delta, (__bf16*)dk, (__bf16*)dv, plan, T, hq, hkv,
+                     scale, causal);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                           const float* delta, void* dq, void* dk, void* dv, const Plan& plan, const int* pref_base,
-                           int T, int hq, int hkv, int d, float scale, int causal, hipStream_t stream) {
-  if (d == 128)
-    return launch_bwd_main_d<128>(q, k, v, dout, lse, delta, dq, dk, dv, plan, pref_base, T, hq, hkv, scale, causal,
-                                  stream);
-  return launch_bwd_main_d<64>(q, k, v, dout, lse, delta, dq, dk, dv, plan, pref_base, T, hq, hkv, scale, causal,
-                               stream);
+template <int D>
+static hipError_t launch_dq_d(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                              const float* delta, void* dq, const Plan& plan, int T, int hq, int hkv, float scale,
+                              int causal, hipStream_t stream) {
+  const long items = (long)(T + 127) / 128 + plan.n_docs;
+  constexpr int STAGE = 2 * 64 * BwdTile<D>::RSTR;
+  auto kern = attn_bwd_dq_kernel<D>;
+  if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE))
+    return hipErrorInvalidConfiguration;
+  const long grid = items * hq;
+  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 2 * STAGE, stream, (const __bf16*)q, (const __bf16*)k,
+                     (const __bf16*)v, (const __bf16*)dout, lse, delta, (__bf16*)dq, plan, T, hq, hkv, scale, causal);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                           const float* delta, void* dk, void* dv, const Plan& plan_any, const int* pref_base, int T,
+                           int hq, int hkv, int d, float scale, int causal, hipStream_t stream) {
+  Plan plan = plan_any;
+  plan.pref = pref_base + pref_slot(128) * (plan.n_docs + 1);
+  if (d == 128) return launch_dkdv_d<128>(q, k, v, dout, lse, delta, dk, dv, plan, T, hq, hkv, scale, causal, stream);
+  return launch_dkdv_d<64>(q, k, v, dout, lse, delta, dk, dv, plan, T, hq, hkv, scale, causal, stream);
+}
+
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                         const float* delta, void* dq, const Plan& plan_any, const int* pref_base, int T, int hq,
+                         int hkv, int d, float scale, int causal, hipStream_t stream) {
+  Plan plan = plan_any;
+  plan.pref = pref_base + pref_slot(128) * (plan.n_docs + 1);
+  if (d == 128) return launch_dq_d<128>(q, k, v, dout, lse, delta, dq, plan, T, hq, hkv, scale, causal, stream);
+  return launch_dq_d<64>(q, k, v, dout, lse, delta, dq, plan, T, hq, hkv, scale, causal, stream);
 }
 
 }  // namespace cfa

@@ -17,6 +17,15 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+// Optional per-kernel timing events (diagnostics), see cfa_set_kernel_events().
+thread_local void* const* g_events = nullptr;
+thread_local int g_event_pairs = 0;
+
+void mark(int kernel, int end, hipStream_t st) {
+  if (g_events && kernel < g_event_pairs && g_events[2 * kernel + end])
+    (void)hipEventRecord((hipEvent_t)g_events[2 * kernel + end], st);
+}
+
 int fail(int status, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -156,10 +165,12 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, c
   if (total_tokens == 0) return CFA_OK;
   const cfa::Plan plan = make_plan(workspace, n_docs);
   hipError_t e;
+  mark(0, 0, st);
   if (dtype == CFA_F32)
     e = cfa::launch_fwd_f32(q, k, v, o, lse, plan, plan.pref, total_tokens, hq, hkv, d, scale, causal, st);
   else
     e = cfa::launch_fwd_bf16(q, k, v, o, lse, plan, plan.pref, total_tokens, hq, hkv, d, scale, causal, st);
+  mark(0, 1, st);
   return check_hip(e, "forward kernel");
 }
 
@@ -190,10 +201,21 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   if (total_tokens == 0) return CFA_OK;
   const cfa::Plan plan = make_plan(workspace, n_docs);
   float* delta = (float*)((char*)workspace + wl.delta);
+  mark(0, 0, st);
   if (int r = check_hip(cfa::launch_bwd_pre(o, dout, delta, total_tokens, hq, d, st), "bwd preprocess")) return r;
-  return check_hip(cfa::launch_bwd_main(q, k, v, dout, lse, delta, dq, dk, dv, plan, plan.pref, total_tokens, hq,
-                                        hkv, d, scale, causal, st),
-                   "backward kernels");
+  mark(0, 1, st);
+  mark(1, 0, st);
+  if (int r = check_hip(cfa::launch_bwd_dkdv(q, k, v, dout, lse, delta, dk, dv, plan, plan.pref, total_tokens, hq,
+                                             hkv, d, scale, causal, st),
+                        "dK/dV kernel"))
+    return r;
+  mark(1, 1, st);
+  mark(2, 0, st);
+  int r = check_hip(cfa::launch_bwd_dq(q, k, v, dout, lse, delta, dq, plan, plan.pref, total_tokens, hq, hkv, d,
+                                       scale, causal, st),
+                    "dQ kernel");
+  mark(2, 1, st);
+  return r;
 }
 
 int mx_padded_tokens(int total_tokens, int n_docs) {
@@ -210,6 +232,14 @@ int mx_quantize(const void* x, int total_tokens, int h, int d, const int32_t* cu
   (void)x; (void)total_tokens; (void)h; (void)d; (void)cu_seqlens; (void)cu_seqlens_host; (void)n_docs;
   (void)axis; (void)codes; (void)scales; (void)t_pad; (void)workspace; (void)workspace_bytes; (void)stream;
   return fail(CFA_ERR_UNSUPPORTED, "mx_quantize not available in this build");
+}
+
+int cfa_set_kernel_events(void* const* events, int n_pairs) {
+  g_err[0] = 0;
+  if (n_pairs < 0 || (n_pairs > 0 && !events)) return fail(CFA_ERR_NULL, "events must hold 2*n_pairs handles");
+  g_events = n_pairs ? events : nullptr;
+  g_event_pairs = n_pairs;
+  return CFA_OK;
 }
 
 int cfa_device_error(const void* workspace, void* stream, int* flag) {

@@ -31,7 +31,8 @@
  *  - Query head h reads kv head h / (hq / hkv) (consecutive query heads share a kv head).
  *  - causal != 0: doc-local key j is visible to doc-local query i iff j <= i.
  *  - Ownership: the caller owns every buffer. The library allocates no device memory, keeps no
- *    state between calls and never synchronises the stream; every call only enqueues work on
+ *    state between calls (apart from the thread-local error text and the optional timing events
+ *    of cfa_set_kernel_events) and never synchronises the stream; every call only enqueues work on
  *    `stream` (a hipStream_t; NULL is the default stream). Inputs are never written.
  *  - Pointers must be 16-byte aligned. Scratch memory is the caller's `workspace`, at least
  *    cfa_workspace_bytes(...) bytes, 256-byte aligned.
@@ -132,6 +133,17 @@ int mx_padded_tokens(int total_tokens, int n_docs);
 
 /* Scratch bytes of mx_quantize along tokens. */
 size_t mx_workspace_bytes(int n_docs);
+
+/*
+ * Per-kernel timing for measurement tools. While set on the calling thread, the attention
+ * calls record events[2*i] on their stream just before launching their i-th main kernel and
+ * events[2*i+1] just after it (the work-list kernel is not counted). Kernel order:
+ *   attn_fwd: 0 = forward attention;
+ *   attn_bwd: 0 = D = rowsum(dO*O), 1 = dK/dV, 2 = dQ.
+ * Entries may be NULL (not recorded). The caller owns the hipEvent_t handles and keeps the
+ * array alive while it is set; n_pairs = 0 (events NULL) switches recording off.
+ */
+int cfa_set_kernel_events(void* const* events, int n_pairs);
 
 /*
  * Reads the device-side validation flag left in `workspace` by the last attn_fwd / attn_bwd /
