@@ -229,9 +229,30 @@ int mx_quantize(const void* x, int total_tokens, int h, int d, const int32_t* cu
                 const int32_t* cu_seqlens_host, int n_docs, int axis, uint8_t* codes, uint8_t* scales, int t_pad,
                 void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
-  (void)x; (void)total_tokens; (void)h; (void)d; (void)cu_seqlens; (void)cu_seqlens_host; (void)n_docs;
-  (void)axis; (void)codes; (void)scales; (void)t_pad; (void)workspace; (void)workspace_bytes; (void)stream;
-  return fail(CFA_ERR_UNSUPPORTED, "mx_quantize not available in this build");
+  if (total_tokens < 0 || h < 1) return fail(CFA_ERR_SHAPE, "total_tokens = %d, h = %d", total_tokens, h);
+  if (d != 64 && d != 128) return fail(CFA_ERR_UNSUPPORTED, "mx_quantize supports d = 64 or 128 (got %d)", d);
+  if (axis != 0 && axis != 1) return fail(CFA_ERR_SHAPE, "axis must be 0 or 1 (got %d)", axis);
+  if (total_tokens > 0 && (!x || !codes || !scales)) return fail(CFA_ERR_NULL, "x, codes and scales must not be NULL");
+  for (const void* p : {x, (const void*)codes})
+    if (!aligned(p, 16)) return fail(CFA_ERR_ALIGN, "x and codes must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  if (axis == 0) {
+    if (total_tokens == 0) return CFA_OK;
+    return check_hip(cfa::launch_mx_quantize_d(x, (long)total_tokens * h * d, codes, scales, st), "mx_quantize_d");
+  }
+  if (n_docs < 1) return fail(CFA_ERR_SHAPE, "n_docs = %d < 1", n_docs);
+  if (!cu_seqlens || !workspace) return fail(CFA_ERR_NULL, "cu_seqlens and workspace must not be NULL for axis 1");
+  if (t_pad % 32 || t_pad < mx_padded_tokens(total_tokens, n_docs))
+    return fail(CFA_ERR_SHAPE, "t_pad = %d must be a multiple of 32 and >= %d", t_pad,
+                mx_padded_tokens(total_tokens, n_docs));
+  if (!aligned(workspace, 256)) return fail(CFA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (workspace_bytes < mx_workspace_bytes(n_docs))
+    return fail(CFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, mx_workspace_bytes(n_docs));
+  if (int r = check_cu_host(cu_seqlens_host, n_docs, total_tokens, 0)) return r;
+  if (int r = check_hip(cfa::launch_plan(cu_seqlens, n_docs, total_tokens, workspace, st), "plan kernel")) return r;
+  if (total_tokens == 0) return CFA_OK;
+  return check_hip(cfa::launch_mx_quantize_t(x, total_tokens, h, d, workspace, n_docs, codes, scales, t_pad, st),
+                   "mx_quantize_t");
 }
 
 int cfa_set_kernel_events(void* const* events, int n_pairs) {

@@ -27,4 +27,9 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
                          const float* delta, void* dq, const Plan& plan, const int* pref_base, int T, int hq,
                          int hkv, int d, float scale, int causal, hipStream_t stream);
 
+hipError_t launch_mx_quantize_d(const void* x, long n_elems, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+hipError_t launch_mx_quantize_t(const void* x, int total_tokens, int h, int d, const void* ws, int n_docs,
+                                uint8_t* codes, uint8_t* scales, int t_pad, hipStream_t stream);
+
 }  // namespace cfa

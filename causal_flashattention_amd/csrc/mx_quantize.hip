@@ -1,0 +1,161 @@
+// MX quantiser for gfx950: bf16 -> FP8 E4M3 codes + E8M0 scales, one scale per 32 elements.
+//
+// The MXFP8 attention path and its document-local token-block scaling are named on the FLAMIA
+// page ("FLAMIA Mimarisi ve Temel Tasarım İlkeleri"); the bit-level rule is the public MX one:
+// per block, amax = max|x|, e = floor(log2 amax) - 8 clamped to [-127, 127] (-127 for a zero
+// block), scale byte e + 127; elements x·2^-e saturated to ±448 and rounded to nearest E4M3
+// (ties to even, sign of zero kept; v_cvt_pk_fp8_f32 rounds to nearest even and does not
+// saturate, hence the clamp); a block holding NaN/Inf gets scale 0xFF and codes 0x7F.
+//
+// Both kernels are HBM-bound streaming passes (2 bytes read, 1 + 1/32 bytes written per
+// element):
+//  * along d: 4 lanes per 32-channel block, 16 bytes per lane, amax by two lane swaps;
+//  * along doc-local tokens: a workgroup per (32-token block, head) reads the 32 × d tile with
+//    lanes along channels (coalesced rows), each lane reduces 16 tokens of one channel, the
+//    two halves meet in LDS, and each lane writes 16 contiguous code bytes of its channel row
+//    in the transposed [h, d, t_pad] layout.
+#include "cfa_device.h"
+
+namespace cfa {
+
+__device__ inline int mx_exponent(float amax) {
+  if (!(amax > 0.f)) return -127;
+  const int ex = __builtin_amdgcn_frexp_expf(amax);  // amax = f·2^ex, f in [0.5, 1)
+  return min(max(ex - 1 - 8, -127), 127);
+}
+
+// Quantise 8 values with a shared exponent e into 8 E4M3 bytes (little-endian in a uint2).
+__device__ inline i32x2 mx_encode8(const float* x, int e) {
+  i32x2 r;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = fminf(fmaxf(__builtin_amdgcn_ldexpf(x[4 * w + i], -e), -448.f), 448.f);
+    int word = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);   // bytes 0, 1
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], word, true);     // bytes 2, 3
+    r[w] = word;
+  }
+  return r;
+}
+
+__global__ __launch_bounds__(256) void mx_quantize_d_kernel(const __bf16* __restrict__ x, uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales, long n_blocks) {
+  const long blk = (long)blockIdx.x * 64 + threadIdx.x / 4;
+  const int sub = threadIdx.x & 3;
+  float v[8];
+  float amax = 0.f;
+  bool bad = false;
+  if (blk < n_blocks) {
+    const bf16x8 u = __builtin_bit_cast(bf16x8, *(const i32x4*)(x + blk * 32 + sub * 8));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[e] = (float)u[e];
+      bad |= !__builtin_isfinite(v[e]);
+      amax = fmaxf(amax, fabsf(v[e]));
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  int badi = bad ? 1 : 0;
+  badi |= __shfl_xor(badi, 1);
+  badi |= __shfl_xor(badi, 2);
+  if (blk >= n_blocks) return;
+  const int e = mx_exponent(amax);
+  i32x2 c = badi ? i32x2{0x7F7F7F7F, 0x7F7F7F7F} : mx_encode8(v, e);
+  *(i32x2*)(codes + blk * 32 + sub * 8) = c;
+  if (sub == 0) scales[blk] = badi ? 0xFF : (uint8_t)(e + 127);
+}
+
+// grid: (padded 32-token blocks upper bound) × h; block 256 threads; D = head dim (<= 256)
+template <int D>
+__global__ __launch_bounds__(256) void mx_quantize_t_kernel(const __bf16* __restrict__ x, uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales, const int2* __restrict__ docinfo,
+                                                            const int* __restrict__ padoff, int n_docs, int h,
+                                                            int t_pad) {
+  static_assert(D <= 128, "one channel per lane pair");
+  __shared__ float s_amax[2][D];
+  __shared__ int s_bad[2][D];
+  const int pb = blockIdx.x;           // padded block index (column pb*32)
+  const int hh = blockIdx.y;
+  const int total_cols = padoff[n_docs];
+  if (pb * 32 >= total_cols) return;
+  // document holding column pb*32: padoff[n] <= pb*32 < padoff[n+1]
+  int lo = 0, hi = n_docs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (padoff[mid] <= pb * 32) lo = mid; else hi = mid - 1;
+  }
+  const int2 di = docinfo[lo];
+  const int b0 = pb * 32 - padoff[lo];            // doc-local first token of this block
+  const int ntok = min(32, di.y - b0);            // real tokens in the block
+  const int c = threadIdx.x % D;                  // channel
+  const int half = threadIdx.x / D;               // 0 / 1: tokens [0,16) / [16,32)
+  const bool active = threadIdx.x < 2 * D;
+  float v[16];
+  float amax = 0.f;
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int tok = 16 * half + i;
+    float val = 0.f;
+    if (active && tok < ntok) val = (float)x[((size_t)(di.x + b0 + tok) * h + hh) * D + c];
+    v[i] = val;
+    bad |= !__builtin_isfinite(val);
+    amax = fmaxf(amax, fabsf(val));
+  }
+  if (active) { s_amax[half][c] = amax; s_bad[half][c] = bad; }
+  __syncthreads();
+  if (!active) return;
+  amax = fmaxf(s_amax[0][c], s_amax[1][c]);
+  bad = s_bad[0][c] | s_bad[1][c];
+  const int e = mx_exponent(amax);
+  i32x4 out;
+  if (bad) {
+    out = i32x4{0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F};
+  } else {
+    const i32x2 lo8 = mx_encode8(v, e), hi8 = mx_encode8(v + 8, e);
+    out = i32x4{lo8.x, lo8.y, hi8.x, hi8.y};
+  }
+  // padding tokens of a partial last block encode 0x00 (not -0 or NaN)
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (16 * half + i >= ntok) out[i / 4] &= ~(0xFF << (8 * (i % 4)));
+  const size_t row = (size_t)hh * D + c;
+  *(i32x4*)(codes + row * t_pad + pb * 32 + 16 * half) = out;
+  if (half == 0) scales[row * (t_pad / 32) + pb] = bad ? 0xFF : (uint8_t)(e + 127);
+}
+
+hipError_t launch_mx_quantize_d(const void* x, long n_elems, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  const long n_blocks = n_elems / 32;
+  if (n_blocks == 0) return hipSuccess;
+  const long grid = (n_blocks + 63) / 64;
+  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(mx_quantize_d_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)x, codes, scales,
+                     n_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quantize_t(const void* x, int total_tokens, int h, int d, const void* ws, int n_docs,
+                                uint8_t* codes, uint8_t* scales, int t_pad, hipStream_t stream) {
+  const PlanLayout lay(n_docs);
+  const char* b = (const char*)ws;
+  const int2* docinfo = (const int2*)(b + lay.docinfo);
+  const int* padoff = (const int*)(b + lay.padoff);
+  const long nb = (long)(total_tokens + 31) / 32 + n_docs;   // bound on padded blocks
+  if (nb == 0 || h == 0) return hipSuccess;
+  if (d == 128)
+    hipLaunchKernelGGL(mx_quantize_t_kernel<128>, dim3((unsigned)nb, (unsigned)h), dim3(256), 0, stream,
+                       (const __bf16*)x, codes, scales, docinfo, padoff, n_docs, h, t_pad);
+  else if (d == 64)
+    hipLaunchKernelGGL(mx_quantize_t_kernel<64>, dim3((unsigned)nb, (unsigned)h), dim3(256), 0, stream,
+                       (const __bf16*)x, codes, scales, docinfo, padoff, n_docs, h, t_pad);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace cfa

@@ -1,0 +1,105 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol, and rejects
+bad arguments with the documented status before touching the device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from causal_flashattention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000          # aligned, never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    txt = open(os.path.join(ROOT, "include", "cfa.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s+([a-z_0-9]+)\s*\(", txt, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert "attn_fwd" in names and "attn_bwd" in names and "mx_quantize" in names
+    L = _lib.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_status_strings():
+    L = _lib.lib()
+    assert L.cfa_status_string(0) == b"CFA_OK"
+    assert L.cfa_status_string(5) == b"CFA_ERR_WORKSPACE"
+    assert L.cfa_version() >> 16 == 1
+
+
+def test_workspace_sizes():
+    L = _lib.lib()
+    assert L.cfa_workspace_bytes(0, 8192, 9, 16, 16, 128, 1) > 0
+    assert L.cfa_workspace_bytes(1, 8192, 9, 16, 16, 128, 1) >= 16 * 8192 * 4
+    assert L.cfa_workspace_bytes(0, 8192, 9, 16, 5, 128, 1) == 0       # hq % hkv
+    assert L.cfa_workspace_bytes(0, 8192, 9, 16, 16, 96, 1) == 0       # head dim
+    assert L.cfa_workspace_bytes(1, 256, 1, 1, 1, 64, 0) == 0          # fp32 is forward-only
+    assert L.cfa_workspace_bytes(2, 256, 1, 1, 1, 64, 1) == 0          # no such pass
+    assert L.mx_padded_tokens(100, 3) == 128 + 96
+
+
+def _fwd(**over):
+    L = _lib.lib()
+    cu_h = np.array([0, 40, 100], dtype=np.int32)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, cu=FAKE, cu_h=cu_h.ctypes.data, n_docs=2, T=100, maxs=0,
+             hq=4, hkv=2, d=128, scale=0.088, causal=1, dtype=1, saved=None, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(over)
+    return L.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["cu_h"], a["n_docs"], a["T"], a["maxs"],
+                      a["hq"], a["hkv"], a["d"], a["scale"], a["causal"], a["dtype"], a["saved"], a["ws"], a["wsb"],
+                      a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), 1), (dict(cu=None), 1), (dict(ws=None), 1),
+    (dict(hkv=3), 2), (dict(n_docs=0), 2), (dict(T=-1), 2), (dict(scale=float("nan")), 2), (dict(scale=0.0), 2),
+    (dict(d=96), 3), (dict(dtype=7), 3), (dict(dtype=2, d=64), 3),
+    (dict(q=FAKE + 8), 4), (dict(ws=FAKE + 16), 4),
+    (dict(wsb=16), 5),
+])
+def test_fwd_rejects(over, status):
+    assert _fwd(**over) == status
+    assert _lib.lib().cfa_last_error()
+
+
+def test_fwd_rejects_bad_host_cu():
+    for bad in ([1, 40, 100], [0, 50, 40], [0, 40, 99]):
+        arr = np.array(bad, dtype=np.int32)
+        assert _fwd(cu_h=arr.ctypes.data) == 2
+    arr = np.array([0, 40, 100], dtype=np.int32)
+    assert _fwd(cu_h=arr.ctypes.data, maxs=50) == 2     # a document longer than max_seqlen
+
+
+def test_bwd_rejects():
+    L = _lib.lib()
+    cu_h = np.array([0, 100], dtype=np.int32)
+    args = [FAKE] * 10 + [FAKE, cu_h.ctypes.data, 1, 100, 0, 4, 2, 128, 0.088, 1, 1, FAKE, 1 << 30, None]
+    bad = list(args); bad[6] = None                      # saved may be NULL for bf16: not an error by itself
+    bad[7] = None                                        # dq NULL
+    assert L.attn_bwd(*bad) == 1
+    bad = list(args); bad[20] = 0                        # dtype fp32 is forward-only
+    assert L.attn_bwd(*bad) == 3
+    bad = list(args); bad[22] = 8                        # workspace too small
+    assert L.attn_bwd(*bad) == 5
+
+
+def test_mx_quantize_rejects():
+    L = _lib.lib()
+    assert L.mx_quantize(FAKE, 100, 2, 128, FAKE, None, 1, 2, FAKE, FAKE, 0, None, 0, None) == 2   # axis
+    assert L.mx_quantize(FAKE, 100, 2, 96, FAKE, None, 1, 0, FAKE, FAKE, 0, None, 0, None) == 3    # d
+    assert L.mx_quantize(FAKE, 100, 2, 128, FAKE, None, 1, 1, FAKE, FAKE, 100, FAKE, 1 << 20, None) == 2  # t_pad
+    assert L.mx_quantize(FAKE, 100, 2, 128, FAKE, None, 1, 1, FAKE, FAKE, 160, None, 0, None) == 1   # workspace
+
+
+def test_kernel_events_hook_validates():
+    L = _lib.lib()
+    assert L.cfa_set_kernel_events(None, 2) == 1
+    assert L.cfa_set_kernel_events(None, 0) == 0

@@ -1,0 +1,74 @@
+"""GPU mx_quantize against the reference quantiser: codes and scale bytes bit-identical."""
+import numpy as np
+import pytest
+import torch
+
+import causal_flashattention_amd as cfa
+from causal_flashattention_amd import workloads as W
+from oracle import mx
+from gpu_helpers import announce, to_dev, DEV
+
+pytestmark = pytest.mark.gpu
+
+
+def _special_tensor(T, h, d, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, h, d)).astype(np.float32)
+    x *= np.exp(rng.uniform(-30, 30, size=(T, h, 1))).astype(np.float32)   # per-row magnitudes
+    x[:, :, 5] *= 20.0                                                      # an outlier channel
+    flat = x.reshape(-1)
+    n = flat.size
+    idx = rng.choice(n, size=min(n, 200), replace=False)
+    specials = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 1e-39, -1e-39, 3e38, -3e38, 448.0, 464.0, 479.0],
+                        dtype=np.float32)
+    flat[idx] = specials[rng.integers(0, len(specials), size=len(idx))]
+    x[1] = 0.0                     # an all-zero token
+    x[2] = -0.0
+    return W.f32_to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("lengths", [[1, 31, 32, 33, 0, 100, 7], [64], [300, 1, 1, 1]])
+@pytest.mark.parametrize("d", [128, 64])
+def test_mx_quantize_both_axes_bit_exact(lengths, d):
+    h = 3
+    T = sum(lengths)
+    xb = _special_tensor(T, h, d, seed=len(lengths) + d)
+    cu = W.cu_from_lengths(lengths)
+    announce("mx_quantize", lengths, d)
+    x = to_dev(xb)
+    cud = torch.from_numpy(cu).to(DEV)
+    x64 = W.bf16_bits_to_f64(xb)
+    # along d
+    c0, s0 = cfa.mx_quantize(x, cud, 0)
+    rc, rs = mx.quantize_d(x64)
+    torch.cuda.synchronize()
+    assert np.array_equal(c0.cpu().numpy(), rc)
+    assert np.array_equal(s0.cpu().numpy(), rs)
+    # along doc-local tokens
+    c1, s1 = cfa.mx_quantize(x, cud, 1, cu_seqlens_host=cu)
+    torch.cuda.synchronize()
+    rc, rs = mx.quantize_t(x64, cu)
+    tp = rc.shape[2]
+    assert np.array_equal(c1.cpu().numpy()[:, :, :tp], rc)
+    assert np.array_equal(s1.cpu().numpy()[:, :, :tp // 32], rs)
+
+
+def test_mx_quantize_workload_4_sampled_heads():
+    w = W.make_workload(4, with_grad=False)
+    announce("mx_quantize workload 4", w.n_docs)
+    cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+    for name in ("q", "v"):
+        x = to_dev(getattr(w, name))
+        c0, s0 = cfa.mx_quantize(x, cu, 0)
+        c1, s1 = cfa.mx_quantize(x, cu, 1, cu_seqlens_host=w.cu_seqlens)
+        torch.cuda.synchronize()
+        for hh in (0, 31):
+            x64 = W.bf16_bits_to_f64(getattr(w, name)[:, [hh]])
+            rc, rs = mx.quantize_d(x64)
+            assert np.array_equal(c0[:, hh:hh + 1].cpu().numpy(), rc)
+            assert np.array_equal(s0[:, hh:hh + 1].cpu().numpy(), rs)
+            rc, rs = mx.quantize_t(x64, w.cu_seqlens)
+            tp = rc.shape[2]
+            assert np.array_equal(c1[hh:hh + 1, :, :tp].cpu().numpy(), rc)
+            assert np.array_equal(s1[hh:hh + 1, :, :tp // 32].cpu().numpy(), rs)
+        del x, c0, s0, c1, s1
