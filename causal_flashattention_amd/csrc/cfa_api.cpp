@@ -77,9 +77,35 @@ int check_sizes(const Sizes& s, bool bwd) {
   return CFA_OK;
 }
 
+// An MX-quantised tensor: E4M3 codes and E8M0 scales, 256-byte aligned sections.
+struct MxBuf {
+  size_t codes, scales;
+};
+
+int t_pad_of(const Sizes& s) { return (s.T + 31) / 32 * 32 + 32 * s.n_docs; }
+
+// d-blocked copy of a [T, h, d] tensor: codes [T, h, d], scales [T, h, d/32]
+size_t add_mx_d(size_t off, const Sizes& s, int h, MxBuf& b) {
+  b.codes = off;
+  off = cfa::align256(off + (size_t)s.T * h * s.d);
+  b.scales = off;
+  return cfa::align256(off + (size_t)s.T * h * (s.d / 32));
+}
+
+// token-blocked copy: codes [h, d, t_pad], scales [h, d, t_pad/32]
+size_t add_mx_t(size_t off, const Sizes& s, int h, MxBuf& b) {
+  const size_t tp = (size_t)t_pad_of(s);
+  b.codes = off;
+  off = cfa::align256(off + (size_t)h * s.d * tp);
+  b.scales = off;
+  return cfa::align256(off + (size_t)h * s.d * (tp / 32));
+}
+
 struct WsLayout {
   size_t plan_end;
-  size_t delta;  // bwd: float [hq, T]
+  size_t delta;             // bwd: float [hq, T]
+  MxBuf vt;                 // fwd MX: V along tokens
+  MxBuf dod, dot, vd, qt, kt;  // bwd MX
   size_t total;
 };
 
@@ -92,8 +118,34 @@ WsLayout ws_layout(int pass, const Sizes& s) {
     w.delta = off;
     off = cfa::align256(off + sizeof(float) * (size_t)s.hq * (size_t)s.T);
   }
+  if (s.dtype == CFA_MXFP8) {
+    if (pass == 0) {
+      off = add_mx_t(off, s, s.hkv, w.vt);
+    } else {
+      off = add_mx_d(off, s, s.hq, w.dod);
+      off = add_mx_t(off, s, s.hq, w.dot);
+      off = add_mx_d(off, s, s.hkv, w.vd);
+      off = add_mx_t(off, s, s.hq, w.qt);
+      off = add_mx_t(off, s, s.hkv, w.kt);
+    }
+  }
   w.total = off;
   return w;
+}
+
+// forward-to-backward buffer of the MX path: Q_d and K_d
+struct SavedLayout {
+  MxBuf qd, kd;
+  size_t total;
+};
+
+SavedLayout saved_layout(const Sizes& s) {
+  SavedLayout v{};
+  size_t off = 0;
+  off = add_mx_d(off, s, s.hq, v.qd);
+  off = add_mx_d(off, s, s.hkv, v.kd);
+  v.total = off;
+  return v;
 }
 
 cfa::Plan make_plan(void* ws, int n_docs) {
@@ -135,8 +187,9 @@ size_t cfa_workspace_bytes(int pass, int total_tokens, int n_docs, int hq, int h
 }
 
 size_t cfa_saved_bytes(int total_tokens, int n_docs, int hq, int hkv, int d, int dtype) {
-  (void)total_tokens; (void)n_docs; (void)hq; (void)hkv; (void)d; (void)dtype;
-  return 0;
+  Sizes s{total_tokens, n_docs, hq, hkv, d, dtype};
+  if (dtype != CFA_MXFP8 || check_sizes(s, false) != CFA_OK) return 0;
+  return saved_layout(s).total;
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens,
@@ -150,8 +203,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, c
   if (total_tokens > 0 && (!q || !k || !v || !o || !lse))
     return fail(CFA_ERR_NULL, "q, k, v, o and lse must not be NULL");
   if (!(std::isfinite(scale) && scale > 0.f)) return fail(CFA_ERR_SHAPE, "scale must be finite and > 0");
-  if (dtype == CFA_MXFP8) return fail(CFA_ERR_UNSUPPORTED, "MXFP8 forward not available in this build");
-  (void)saved;
+  if (dtype == CFA_MXFP8 && !saved) return fail(CFA_ERR_NULL, "MXFP8 needs the `saved` buffer");
+  if (dtype == CFA_MXFP8 && !aligned(saved, 256)) return fail(CFA_ERR_ALIGN, "saved must be 256-byte aligned");
   for (const void* p : {q, k, v, (const void*)o, (const void*)lse, (const void*)cu_seqlens})
     if (!aligned(p, 16)) return fail(CFA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
   if (!aligned(workspace, 256)) return fail(CFA_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -165,6 +218,31 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, c
   if (total_tokens == 0) return CFA_OK;
   const cfa::Plan plan = make_plan(workspace, n_docs);
   hipError_t e;
+  if (dtype == CFA_MXFP8) {
+    char* ws = (char*)workspace;
+    char* sv = (char*)saved;
+    const SavedLayout sl = saved_layout(s);
+    const cfa::PlanLayout pl(n_docs);
+    const int tp = t_pad_of(s);
+    mark(1, 0, st);
+    if (int r = check_hip(cfa::launch_mx_quantize_d(q, (long)total_tokens * hq * d, (uint8_t*)sv + sl.qd.codes,
+                                                    (uint8_t*)sv + sl.qd.scales, st), "quantize Q"))
+      return r;
+    if (int r = check_hip(cfa::launch_mx_quantize_d(k, (long)total_tokens * hkv * d, (uint8_t*)sv + sl.kd.codes,
+                                                    (uint8_t*)sv + sl.kd.scales, st), "quantize K"))
+      return r;
+    if (int r = check_hip(cfa::launch_mx_quantize_t(v, total_tokens, hkv, d, ws, n_docs, (uint8_t*)ws + wl.vt.codes,
+                                                    (uint8_t*)ws + wl.vt.scales, tp, st), "quantize V"))
+      return r;
+    mark(1, 1, st);
+    mark(0, 0, st);
+    e = cfa::launch_fwd_mx((const uint8_t*)sv + sl.qd.codes, (const uint8_t*)sv + sl.qd.scales,
+                           (const uint8_t*)sv + sl.kd.codes, (const uint8_t*)sv + sl.kd.scales,
+                           (const uint8_t*)ws + wl.vt.codes, (const uint8_t*)ws + wl.vt.scales, v, o, lse, plan,
+                           plan.pref, (const int*)(ws + pl.padoff), total_tokens, tp, hq, hkv, scale, causal, st);
+    mark(0, 1, st);
+    return check_hip(e, "MX forward kernel");
+  }
   mark(0, 0, st);
   if (dtype == CFA_F32)
     e = cfa::launch_fwd_f32(q, k, v, o, lse, plan, plan.pref, total_tokens, hq, hkv, d, scale, causal, st);

@@ -54,7 +54,7 @@ __host__ __device__ inline int pref_slot(int tile_rows) { return tile_rows == 32
 // tile with the most causal key tiles first); otherwise it counts up (dK/dV: key tile 0 sees
 // every query tile).
 __device__ inline bool decode_item(const Plan& pl, int p, int tile_rows, bool expensive_first,
-                                   int& s0, int& L, int& tile) {
+                                   int& s0, int& L, int& tile, int* doc_out = nullptr) {
   const int total = pl.pref[pl.n_docs];
   if (p >= total) return false;
   int lo = 0, hi = pl.n_docs - 1;  // find i: pref[i] <= p < pref[i+1]
@@ -63,6 +63,7 @@ __device__ inline bool decode_item(const Plan& pl, int p, int tile_rows, bool ex
     if (pl.pref[mid] <= p) lo = mid; else hi = mid - 1;
   }
   const int doc = pl.order[lo];
+  if (doc_out) *doc_out = doc;
   const int2 di = pl.docinfo[doc];
   s0 = di.x;
   L = di.y;
@@ -94,6 +95,19 @@ __device__ inline bf16x8 concat_tr(i16x4 a, i16x4 b) {
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
   __bf16 x = (__bf16)a, y = (__bf16)b;
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// Scaled FP8 MFMA, E4M3 operands, E8M0 scales (bits 7:0 of sa / sb). Operand layout per lane l:
+// row (A) or column (B) l%32; bytes 0-15 hold k = 16·(l/32) + 0..15, bytes 16-31 hold
+// k = 32 + 16·(l/32) + 0..15; lane l supplies the scale of row/column l%32 for k-block l/32.
+__device__ inline f32x16 mfma32_mx(i32x8 a, int sa, i32x8 b, int sb, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// Four floats -> four E4M3 bytes (round to nearest even; inputs must already lie in ±448).
+__device__ inline int pack_fp8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
 __device__ inline float wave_max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }

@@ -32,4 +32,9 @@ hipError_t launch_mx_quantize_d(const void* x, long n_elems, uint8_t* codes, uin
 hipError_t launch_mx_quantize_t(const void* x, int total_tokens, int h, int d, const void* ws, int n_docs,
                                 uint8_t* codes, uint8_t* scales, int t_pad, hipStream_t stream);
 
+hipError_t launch_fwd_mx(const uint8_t* qd, const uint8_t* qd_sc, const uint8_t* kd, const uint8_t* kd_sc,
+                         const uint8_t* vt, const uint8_t* vt_sc, const void* v, void* o, float* lse,
+                         const Plan& plan, const int* pref_base, const int* padoff, int total_tokens, int t_pad,
+                         int hq, int hkv, float scale, int causal, hipStream_t stream);
+
 }  // namespace cfa
