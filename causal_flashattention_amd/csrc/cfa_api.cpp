@@ -263,8 +263,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   if (total_tokens > 0 && (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv))
     return fail(CFA_ERR_NULL, "q, k, v, o, lse, dout, dq, dk and dv must not be NULL");
   if (!(std::isfinite(scale) && scale > 0.f)) return fail(CFA_ERR_SHAPE, "scale must be finite and > 0");
-  if (dtype == CFA_MXFP8) return fail(CFA_ERR_UNSUPPORTED, "MXFP8 backward not available in this build");
-  (void)saved;
+  if (dtype == CFA_MXFP8 && !saved) return fail(CFA_ERR_NULL, "MXFP8 needs the forward's `saved` buffer");
+  if (dtype == CFA_MXFP8 && !aligned(saved, 256)) return fail(CFA_ERR_ALIGN, "saved must be 256-byte aligned");
   for (const void* p : {q, k, v, o, (const void*)lse, dout, (const void*)dq, (const void*)dk, (const void*)dv,
                         (const void*)cu_seqlens})
     if (!aligned(p, 16)) return fail(CFA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
@@ -282,6 +282,43 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   mark(0, 0, st);
   if (int r = check_hip(cfa::launch_bwd_pre(o, dout, delta, total_tokens, hq, d, st), "bwd preprocess")) return r;
   mark(0, 1, st);
+  if (dtype == CFA_MXFP8) {
+    char* ws = (char*)workspace;
+    const char* sv = (const char*)saved;
+    const SavedLayout sl = saved_layout(s);
+    const cfa::PlanLayout pl(n_docs);
+    const int tp = t_pad_of(s);
+    const int* padoff = (const int*)(ws + pl.padoff);
+    auto U = [&](const MxBuf& b, bool codes) { return (uint8_t*)ws + (codes ? b.codes : b.scales); };
+    mark(3, 0, st);
+    hipError_t e = cfa::launch_mx_quantize_d(dout, (long)total_tokens * hq * d, U(wl.dod, true), U(wl.dod, false), st);
+    if (!e) e = cfa::launch_mx_quantize_t(dout, total_tokens, hq, d, ws, n_docs, U(wl.dot, true), U(wl.dot, false), tp, st);
+    if (!e) e = cfa::launch_mx_quantize_d(v, (long)total_tokens * hkv * d, U(wl.vd, true), U(wl.vd, false), st);
+    if (!e) e = cfa::launch_mx_quantize_t(q, total_tokens, hq, d, ws, n_docs, U(wl.qt, true), U(wl.qt, false), tp, st);
+    if (!e) e = cfa::launch_mx_quantize_t(k, total_tokens, hkv, d, ws, n_docs, U(wl.kt, true), U(wl.kt, false), tp, st);
+    mark(3, 1, st);
+    if (int r = check_hip(e, "backward quantisation")) return r;
+    cfa::MxOperands m;
+    m.qd = (const uint8_t*)sv + sl.qd.codes; m.qd_sc = (const uint8_t*)sv + sl.qd.scales;
+    m.kd = (const uint8_t*)sv + sl.kd.codes; m.kd_sc = (const uint8_t*)sv + sl.kd.scales;
+    m.dod = U(wl.dod, true); m.dod_sc = U(wl.dod, false);
+    m.vd = U(wl.vd, true); m.vd_sc = U(wl.vd, false);
+    m.qt = U(wl.qt, true); m.qt_sc = U(wl.qt, false);
+    m.kt = U(wl.kt, true); m.kt_sc = U(wl.kt, false);
+    m.dot = U(wl.dot, true); m.dot_sc = U(wl.dot, false);
+    mark(1, 0, st);
+    if (int r = check_hip(cfa::launch_bwd_dkdv_mx(m, q, dout, lse, delta, dk, dv, plan, plan.pref, padoff, total_tokens,
+                                                  tp, hq, hkv, scale, causal, st),
+                          "MX dK/dV kernel"))
+      return r;
+    mark(1, 1, st);
+    mark(2, 0, st);
+    int r = check_hip(cfa::launch_bwd_dq_mx(m, k, lse, delta, dq, plan, plan.pref, padoff, total_tokens, tp, hq, hkv,
+                                            scale, causal, st),
+                      "MX dQ kernel");
+    mark(2, 1, st);
+    return r;
+  }
   mark(1, 0, st);
   if (int r = check_hip(cfa::launch_bwd_dkdv(q, k, v, dout, lse, delta, dk, dv, plan, plan.pref, total_tokens, hq,
                                              hkv, d, scale, causal, st),

@@ -6,6 +6,12 @@
 
 namespace cfa {
 
+// MX-quantised operands of the MXFP8 backward (codes + scales): d-blocked *_d, token-blocked *_t.
+struct MxOperands {
+  const uint8_t *qd, *qd_sc, *kd, *kd_sc, *dod, *dod_sc, *vd, *vd_sc;
+  const uint8_t *qt, *qt_sc, *kt, *kt_sc, *dot, *dot_sc;
+};
+
 hipError_t launch_plan(const int* cu, int n_docs, int total_tokens, void* ws, hipStream_t stream);
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, const Plan& plan,
@@ -36,5 +42,14 @@ hipError_t launch_fwd_mx(const uint8_t* qd, const uint8_t* qd_sc, const uint8_t*
                          const uint8_t* vt, const uint8_t* vt_sc, const void* v, void* o, float* lse,
                          const Plan& plan, const int* pref_base, const int* padoff, int total_tokens, int t_pad,
                          int hq, int hkv, float scale, int causal, hipStream_t stream);
+
+hipError_t launch_bwd_dkdv_mx(const MxOperands& m, const void* q, const void* dout, const float* lse,
+                              const float* delta, void* dk, void* dv, const Plan& plan, const int* pref_base,
+                              const int* padoff, int T, int t_pad, int hq, int hkv, float scale, int causal,
+                              hipStream_t stream);
+
+hipError_t launch_bwd_dq_mx(const MxOperands& m, const void* k, const float* lse, const float* delta, void* dq,
+                            const Plan& plan, const int* pref_base, const int* padoff, int T, int t_pad, int hq,
+                            int hkv, float scale, int causal, hipStream_t stream);
 
 }  // namespace cfa

@@ -138,8 +138,9 @@ size_t mx_workspace_bytes(int n_docs);
  * Per-kernel timing for measurement tools. While set on the calling thread, the attention
  * calls record events[2*i] on their stream just before launching their i-th main kernel and
  * events[2*i+1] just after it (the work-list kernel is not counted). Kernel order:
- *   attn_fwd: 0 = forward attention;
- *   attn_bwd: 0 = D = rowsum(dO*O), 1 = dK/dV, 2 = dQ.
+ *   attn_fwd: 0 = forward attention, 1 = (MXFP8) the Q, K, V quantisation passes together;
+ *   attn_bwd: 0 = D = rowsum(dO*O), 1 = dK/dV, 2 = dQ, 3 = (MXFP8) the dO, V, Q, K
+ *             quantisation passes together.
  * Entries may be NULL (not recorded). The caller owns the hipEvent_t handles and keeps the
  * array alive while it is set; n_pairs = 0 (events NULL) switches recording off.
  */

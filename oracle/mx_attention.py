@@ -127,3 +127,61 @@ def attn_mx_bwd(q_b, k_b, v_b, do_b, cu_seqlens, scale, causal=True, tile=DIAG_T
                 dq[rows, h] = scale * (ds_diag @ k_b[s0:s1, g] + ds_off @ k_t[s0:s1, g])
                 dk[s0:s1, g] += scale * (ds_diag.T @ q_b[rows, h] + ds_off.T @ q_t[rows, h])
     return dq, dk, dv
+
+
+def attn_mx_rows(q_b, k_b, v_b, do_b, rows, scale, causal=True, tile=DIAG_TILE):
+    """Selected query rows of ONE document with MX operands (doc-local arrays).
+
+    The MX counterpart of ``oracle.attention.attn_rows`` for documents too long for the full
+    oracle: the quantised copies are built for the whole document (blocks are doc-local), then
+    each selected row follows the definitions in the module docstring. Returns
+    ``o [n, hq, d], lse [hq, n], dq [n, hq, d]`` and the partial ``dk, dv [L, hkv, d]`` summed
+    over the selected rows only.
+    """
+    q_b = np.asarray(q_b, np.float64)
+    k_b = np.asarray(k_b, np.float64)
+    v_b = np.asarray(v_b, np.float64)
+    do_b = np.asarray(do_b, np.float64)
+    rows = np.asarray(rows, np.int64)
+    L, hq, d = q_b.shape
+    hkv = k_b.shape[1]
+    group = hq // hkv
+    cu = np.array([0, L])
+    q_d, q_t = operand_copies(q_b, cu)
+    k_d, k_t = operand_copies(k_b, cu)
+    v_d, v_t = operand_copies(v_b, cu)
+    do_d, do_t = operand_copies(do_b, cu)
+    n = len(rows)
+    o = np.zeros((n, hq, d))
+    lse = np.zeros((hq, n))
+    dq = np.zeros((n, hq, d))
+    dk = np.zeros_like(k_b)
+    dv = np.zeros_like(v_b)
+    for h in range(hq):
+        g = h // group
+        for r0 in range(0, n, 256):
+            rs = rows[r0:r0 + 256]
+            s = scale * (q_d[rs, h] @ k_d[:, g].T)
+            mask = np.zeros_like(s)
+            if causal:
+                mask[np.arange(L)[None, :] > rs[:, None]] = -np.inf
+            z = s + mask
+            m = z.max(axis=1)
+            e = np.exp(z - m[:, None])
+            l = e.sum(axis=1)
+            p = e / l[:, None]
+            if causal:
+                dg = (rs[:, None] // tile) == (np.arange(L)[None, :] // tile)
+            else:
+                dg = np.zeros_like(p, dtype=bool)
+            p_diag, p_off = np.where(dg, p, 0.0), np.where(dg, 0.0, p)
+            ob = p_diag @ v_b[:, g] + p_off @ v_t[:, g]
+            o[r0:r0 + len(rs), h] = ob
+            lse[h, r0:r0 + len(rs)] = m + np.log(l)
+            D = np.sum(do_b[rs, h] * ob, axis=1)
+            ds = p * (do_d[rs, h] @ v_d[:, g].T - D[:, None])
+            ds_diag, ds_off = np.where(dg, ds, 0.0), np.where(dg, 0.0, ds)
+            dq[r0:r0 + len(rs), h] = scale * (ds_diag @ k_b[:, g] + ds_off @ k_t[:, g])
+            dk[:, g] += scale * (ds_diag.T @ q_b[rs, h] + ds_off.T @ q_t[rs, h])
+            dv[:, g] += p_diag.T @ do_b[rs, h] + p_off.T @ do_t[rs, h]
+    return o, lse, dq, dk, dv

@@ -122,3 +122,21 @@ def test_operand_selection_by_tile():
         np.testing.assert_allclose(o[i, 0], ref, atol=1e-12)
     assert not np.array_equal(vt, v)
     np.testing.assert_array_equal(mx.padded_offsets(cu), [0, 320])
+
+
+def test_mx_rows_match_full_mx_oracle():
+    rng = np.random.default_rng(6)
+    L = 300
+    cu = np.array([0, L])
+    mk = lambda h: np.round(rng.standard_normal((L, h, 32)) * 128) / 128
+    q, k, v, do = mk(2), mk(1), mk(1), mk(2)
+    o, lse = mxa.attn_mx_fwd(q, k, v, cu, 0.2)
+    dq, dk, dv = mxa.attn_mx_bwd(q, k, v, do, cu, 0.2)
+    rows = np.array([0, 31, 128, 129, 299])
+    ro, rl, rdq, _, _ = mxa.attn_mx_rows(q, k, v, do, rows, 0.2)
+    np.testing.assert_allclose(ro, o[rows], atol=1e-12)
+    np.testing.assert_allclose(rl, lse[:, rows], atol=1e-12)
+    np.testing.assert_allclose(rdq, dq[rows], atol=1e-12)
+    _, _, _, pdk, pdv = mxa.attn_mx_rows(q, k, v, do, np.arange(200, L), 0.2)
+    np.testing.assert_allclose(pdk[200:], dk[200:], atol=1e-12)
+    np.testing.assert_allclose(pdv[200:], dv[200:], atol=1e-12)
