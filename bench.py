@@ -36,17 +36,31 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp32": 157.3}   # MI355X dense MF
 HBM_PEAK_GBS = 8000.0
 METRIC = "causal fwd+bwd attention TFLOP/s and % of MFMA peak (bf16, MXFP8), 1 GPU"
 
-KERNELS = {  # name -> (call, index in that call's event list, GEMM units counted)
+# name -> (call, index in that call's event list, GEMM units counted); see cfa_set_kernel_events
+KERNELS_BF16 = {
     "attn_fwd_bf16_kernel": ("fwd", 0, 2.0),
     "bwd_pre_kernel": ("bwd", 0, 0.0),
     "attn_bwd_dkdv_kernel": ("bwd", 1, 4.0),
     "attn_bwd_dq_kernel": ("bwd", 2, 1.0),
+}
+KERNELS_MX = {
+    "attn_fwd_mx_kernel": ("fwd", 0, 2.0),
+    "mx_quantize_fwd": ("fwd", 1, 0.0),
+    "bwd_pre_kernel": ("bwd", 0, 0.0),
+    "attn_bwd_dkdv_mx_kernel": ("bwd", 1, 4.0),
+    "attn_bwd_dq_mx_kernel": ("bwd", 2, 1.0),
+    "mx_quantize_bwd": ("bwd", 3, 0.0),
 }
 KERNEL_SOURCES = {
     "attn_fwd_bf16_kernel": "attn_fwd.hip",
     "bwd_pre_kernel": "attn_bwd.hip",
     "attn_bwd_dkdv_kernel": "attn_bwd.hip",
     "attn_bwd_dq_kernel": "attn_bwd.hip",
+    "attn_fwd_mx_kernel": "attn_fwd_mx.hip",
+    "attn_bwd_dkdv_mx_kernel": "attn_bwd_mx.hip",
+    "attn_bwd_dq_mx_kernel": "attn_bwd_mx.hip",
+    "mx_quantize_fwd": "mx_quantize.hip",
+    "mx_quantize_bwd": "mx_quantize.hip",
 }
 
 
@@ -56,7 +70,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 5],
-                    help="seeded workload number (3 = one 32K-token document, 32 q / 8 kv heads)")
+                    help="bf16 workload (3 = one 32K-token document, 32 q / 8 kv heads)")
+    ap.add_argument("--mx-workload", type=int, default=4, choices=[0, 4, 5],
+                    help="MXFP8 workload reported under 'mxfp8' (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     return ap.parse_args()
@@ -113,18 +129,13 @@ def _f64(a):
     return W.bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the attention path has no multi-GPU exchange in this "
-              "library; run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
+def measure(w, mx, steps, warmup):
+    """Warm up, then time `steps` fwd+bwd steps; per-kernel HIP events inside the timed region."""
+    import ctypes
     import torch
     import causal_flashattention_amd as cfa
-    from causal_flashattention_amd import workloads as W
     from causal_flashattention_amd import _lib
 
-    w = W.make_workload(args.workload)
     dev = "cuda:0"
 
     def up(a):
@@ -134,40 +145,45 @@ def main():
     cu = torch.from_numpy(w.cu_seqlens).to(dev)
     cu_h = torch.from_numpy(w.cu_seqlens)
     T, hq, hkv, d = w.total_tokens, w.hq, w.hkv, w.d
+    dt = cfa.CFA_MXFP8 if mx else cfa.CFA_BF16
     o = torch.empty_like(q)
     lse = torch.empty((hq, T), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws_f = torch.empty(cfa.workspace_bytes(0, T, w.n_docs, hq, hkv, d, cfa.CFA_BF16), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(cfa.workspace_bytes(1, T, w.n_docs, hq, hkv, d, cfa.CFA_BF16), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(cfa.workspace_bytes(0, T, w.n_docs, hq, hkv, d, dt), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(cfa.workspace_bytes(1, T, w.n_docs, hq, hkv, d, dt), dtype=torch.uint8, device=dev)
+    saved = torch.empty(max(cfa.saved_bytes(T, w.n_docs, hq, hkv, d, dt), 256), dtype=torch.uint8, device=dev) \
+        if mx else None
     L = _lib.lib()
-    import ctypes
+    kernels = KERNELS_MX if mx else KERNELS_BF16
 
-    def step():
-        cfa.attn_fwd(q, k, v, cu, scale=w.scale, cu_seqlens_host=cu_h, out=o, lse=lse, workspace=ws_f)
+    def fwd():
+        cfa.attn_fwd(q, k, v, cu, scale=w.scale, cu_seqlens_host=cu_h, out=o, lse=lse, workspace=ws_f, mx=mx,
+                     saved=saved)
+
+    def bwd():
         cfa.attn_bwd(q, k, v, o, lse, do, cu, scale=w.scale, cu_seqlens_host=cu_h, dq=dq, dk=dk, dv=dv,
-                     workspace=ws_b)
+                     workspace=ws_b, mx=mx, saved=saved)
 
-    for _ in range(args.warmup):
-        step()
+    for _ in range(warmup):
+        fwd()
+        bwd()
     torch.cuda.synchronize()
-
-    # per-kernel events, recorded by the library around each main kernel of each timed step
-    K = args.steps
-    ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-          for name in KERNELS}
-    for name in ev:
-        for a, b in ev[name]:
-            a.record(); b.record()          # create the underlying HIP events
+    K = steps
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+          for n in kernels}
+    for n in ev:
+        for a, b in ev[n]:
+            a.record()
+            b.record()          # creates the underlying HIP events
     torch.cuda.synchronize()
 
     def handles(call, i):
-        names = [n for n, (c, _, _) in KERNELS.items() if c == call]
-        names.sort(key=lambda n: KERNELS[n][1])
+        names = sorted([n for n, (c, _, _) in kernels.items() if c == call], key=lambda n: kernels[n][1])
         arr = (ctypes.c_void_p * (2 * len(names)))()
-        for j, n in enumerate(names):
+        for n in names:
             a, b = ev[n][i]
-            arr[2 * j] = a.cuda_event
-            arr[2 * j + 1] = b.cuda_event
+            arr[2 * kernels[n][1]] = a.cuda_event
+            arr[2 * kernels[n][1] + 1] = b.cuda_event
         return arr, len(names)
 
     fwd_h = [handles("fwd", i) for i in range(K)]
@@ -176,41 +192,60 @@ def main():
     t0 = time.perf_counter()
     for i in range(K):
         _lib.check(L.cfa_set_kernel_events(fwd_h[i][0], fwd_h[i][1]))
-        cfa.attn_fwd(q, k, v, cu, scale=w.scale, cu_seqlens_host=cu_h, out=o, lse=lse, workspace=ws_f)
+        fwd()
         _lib.check(L.cfa_set_kernel_events(bwd_h[i][0], bwd_h[i][1]))
-        cfa.attn_bwd(q, k, v, o, lse, do, cu, scale=w.scale, cu_seqlens_host=cu_h, dq=dq, dk=dk, dv=dv,
-                     workspace=ws_b)
+        bwd()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     _lib.check(L.cfa_set_kernel_events(None, 0))
 
     elapsed = t1 - t0
-    ms_per_step = elapsed / K * 1e3
     flops = w.flops_fwd_bwd()
     value = flops / (elapsed / K) / 1e12
-    unit_flops = w.flops_fwd() / 2.0          # one GEMM unit over the causal pairs
-    kern = {}
-    for name, (_, _, units) in KERNELS.items():
-        ms = float(np.mean([a.elapsed_time(b) for a, b in ev[name]]))
-        kern[name] = {"ms": ms, "units": units}
+    unit_flops = w.flops_fwd() / 2.0
+    kern = {n: {"ms": float(np.mean([a.elapsed_time(b) for a, b in ev[n]])), "units": u}
+            for n, (_, _, u) in kernels.items()}
     dom = max(kern, key=lambda n: kern[n]["ms"])
     dom_flops = kern[dom]["units"] * unit_flops
+    peak = PEAK_TFLOPS["fp8" if mx else "bf16"]
     achieved = dom_flops / (kern[dom]["ms"] * 1e-3) / 1e12
-    roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
-            "frac": achieved / PEAK_TFLOPS["bf16"], "traffic": traffic_for(dom, w.name),
+    roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            "frac": achieved / peak, "traffic": traffic_for(dom, w.name),
             "algorithmic_flop_per_launch": dom_flops, "mean_launch_ms": kern[dom]["ms"]}
+    res = {"value": value, "ms_per_step": elapsed / K * 1e3, "pct_of_peak": 100.0 * value / peak, "peak": peak,
+           "config": {"workload": w.name, "total_tokens": T, "n_docs": w.n_docs, "hq": hq, "hkv": hkv, "d": d,
+                      "causal": True, "seed": w.info["seed"], "causal_tflop_per_step": flops / 1e12},
+           "kernels_ms": {n: round(kern[n]["ms"], 4) for n in kern}, "roofline": roof}
+    del q, k, v, do, o, lse, dq, dk, dv, ws_f, ws_b, saved
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention path has no multi-GPU exchange in this "
+              "library; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    from causal_flashattention_amd import workloads as W
+
+    w = W.make_workload(args.workload)
+    head = measure(w, False, args.steps, args.warmup)
     out = {
-        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
-        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "pct_of_peak": 100.0 * value / PEAK_TFLOPS["bf16"],
-        "config": {"workload": w.name, "total_tokens": T, "n_docs": w.n_docs, "hq": hq, "hkv": hkv, "d": d,
-                   "causal": True, "seed": w.info["seed"], "causal_tflop_per_step": flops / 1e12},
-        "kernels_ms": {n: round(kern[n]["ms"], 4) for n in kern},
-        "roofline": roof,
+        "metric": METRIC, "value": head["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "pct_of_peak": head["pct_of_peak"],
+        "config": head["config"], "kernels_ms": head["kernels_ms"], "roofline": head["roofline"],
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
+    del w
+    if args.mx_workload:
+        wm = W.make_workload(args.mx_workload)
+        mres = measure(wm, True, args.steps, args.warmup)
+        mres["dtype"] = "mxfp8 (E4M3 + E8M0 per 32; bf16 diagonal tiles)"
+        mres["unit"] = "TFLOP/s"
+        out["mxfp8"] = mres
     print(json.dumps(out))
 
 
