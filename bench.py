@@ -74,6 +74,9 @@ def parse():
     ap.add_argument("--mx-workload", type=int, default=4, choices=[0, 4, 5],
                     help="MXFP8 workload reported under 'mxfp8' (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes 3 times (to scale the "
+                         "FETCH_SIZE/WRITE_SIZE counters against a kernel of known traffic) and exit")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     return ap.parse_args()
 
@@ -227,6 +230,15 @@ def main():
         print("bench.py measures one GPU only: the attention path has no multi-GPU exchange in this "
               "library; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        import torch
+        a = torch.empty(args.copy_calibration // 2, dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": a.numel() * 2}))
+        return
     from causal_flashattention_amd import workloads as W
 
     w = W.make_workload(args.workload)

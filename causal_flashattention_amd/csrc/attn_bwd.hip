@@ -55,9 +55,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
 
 template <int D>
 struct BwdTile {
-  static constexpr int RSTR = D * 2 + 16;   // LDS row stride (bytes), tiles read row-wise and transposed
+  using S = SwzTile<D>;                     // tiles read row-wise and transposed (cfa_device.h)
+  static constexpr int RSTR = S::STR;
   static constexpr int DS = D / 16;
   static constexpr int DB = D / 32;
+  static constexpr int QB = 1;              // 32-query blocks per dK/dV step
+  static constexpr int BM = 32 * QB;        // queries per dK/dV step
+  static constexpr int DKDV_STAGE = 2 * BM * RSTR + 2 * BM * 4;   // Q, dO tiles, lse2, D
 };
 
 // ------------------------------------------------------------------ dK / dV
@@ -68,12 +72,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     __bf16* __restrict__ dk, __bf16* __restrict__ dv, Plan plan, int total_tokens, int hq, int hkv,
     float scale, int causal) {
   using C = BwdTile<D>;
-  constexpr int BM = 64;                         // queries per step
+  constexpr int BM = C::BM;                      // queries per step
+  constexpr int QB = C::QB;
   constexpr int TILE = BM * C::RSTR;             // bytes of one Q (or dO) tile
-  constexpr int STAGE = 2 * TILE + 2 * BM * 4;   // Q, dO, lse2, delta
+  constexpr int STAGE = C::DKDV_STAGE;           // Q, dO, lse2, delta
   constexpr int CH = BM * D / 8;                 // 16-byte chunks per tile
-  constexpr int PT = CH / 256;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int PT = (CH + 255) / 256;
+  __shared__ __attribute__((aligned(16))) char lds_a[STAGE];
+  __shared__ __attribute__((aligned(16))) char lds_b[STAGE];
 
   const int p = blockIdx.x / hkv, g = blockIdx.x % hkv;
   int s0, L, t;
@@ -83,6 +89,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
   const int kw0 = t * 128 + 32 * w;              // first doc-local key of this wave
   const int mykey = kw0 + (lane & 31);
   const float sl2 = scale * LOG2E;
+  const SwzOffsets<D> so(lane);
 
   // K and V rows of this wave as B operands (lane: key mykey, d = 16s + 8·half ..)
   bf16x8 kf[C::DS], vf[C::DS];
@@ -99,83 +106,116 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
 #pragma unroll
   for (int b = 0; b < C::DB; ++b) { dka[b] = f32x16{}; dva[b] = f32x16{}; }
 
-  const int q_begin = causal ? t * 128 : 0;      // first query that can see this tile (64-aligned)
+  const int q_begin = causal ? t * 128 : 0;      // first query that can see this tile (BM-aligned)
   const int n_qt = (L - q_begin + BM - 1) / BM;  // query tiles per head
   const int n_steps = n_qt * G;
   const int wave_first_q = causal ? kw0 : 0;
 
-  i32x4 qreg[PT], oreg[PT];
+  // Staging of one step (Q and dO rows of one query head, their LSE and D) into an LDS buffer.
+  // d = 128: direct global -> LDS copies. Rows past the document end are clamped into it and
+  // masked in the arithmetic (P = 0), so nothing depends on their values.
   float lreg = 0.f, dreg = 0.f;
-  auto load_step = [&](int st) {
+  auto stage = [&](int st, char* qb) {
     const int h = g * G + st / n_qt;
     const int q0 = q_begin + (st % n_qt) * BM;
-#pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      const int row = c / (D / 8), col = c % (D / 8);
-      const bool ok = q0 + row < L;
-      const size_t off = ((size_t)(s0 + (ok ? q0 + row : 0)) * hq + h) * D + col * 8;
-      qreg[i] = ok ? *(const i32x4*)(q + off) : i32x4{0, 0, 0, 0};
-      oreg[i] = ok ? *(const i32x4*)(dout + off) : i32x4{0, 0, 0, 0};
-    }
-    if (threadIdx.x < BM) {
-      const int qi = q0 + threadIdx.x;
-      const bool ok = qi < L;
-      // masked-out rows get an LSE of +inf so that their probabilities are exactly 0
-      lreg = ok ? lse[(size_t)h * total_tokens + s0 + qi] * LOG2E : INFINITY;
-      dreg = ok ? delta[(size_t)h * total_tokens + s0 + qi] : 0.f;
-    }
-  };
-  auto store_step = [&](int buf) {
-    char* qb = smem + buf * STAGE;
     char* ob = qb + TILE;
-    float* lb = (float*)(ob + TILE);
-    float* db = lb + BM;
+    char* lb = ob + TILE;
+    if constexpr (D == 128) {
+      auto qrow = [&](int r) { return (const char*)(q + ((size_t)(s0 + min(q0 + r, L - 1)) * hq + h) * D); };
+      auto orow = [&](int r) { return (const char*)(dout + ((size_t)(s0 + min(q0 + r, L - 1)) * hq + h) * D); };
+      stage_rows_lds<BM>(qb, qrow, w, lane);
+      stage_rows_lds<BM>(ob, orow, w, lane);
+      if (threadIdx.x < BM) {   // LSE and D through registers, written to LDS by stage_finish
+        const size_t li = (size_t)h * total_tokens + s0 + min(q0 + (int)threadIdx.x, L - 1);
+        lreg = lse[li];
+        dreg = delta[li];
+      }
+    } else {
+      i32x4 qreg[PT], oreg[PT];
 #pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      const int row = c / (D / 8), col = c % (D / 8);
-      *(i32x4*)(qb + row * C::RSTR + col * 16) = qreg[i];
-      *(i32x4*)(ob + row * C::RSTR + col * 16) = oreg[i];
+      for (int i = 0; i < PT; ++i) {
+        const int c = min(threadIdx.x + 256 * i, CH - 1);
+        const int row = c / (D / 8), col = c % (D / 8);
+        const size_t off = ((size_t)(s0 + min(q0 + row, L - 1)) * hq + h) * D + col * 8;
+        qreg[i] = *(const i32x4*)(q + off);
+        oreg[i] = *(const i32x4*)(dout + off);
+      }
+#pragma unroll
+      for (int i = 0; i < PT; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        const int row = c / (D / 8), col = c % (D / 8);
+        if (c < CH) {
+          *(i32x4*)(qb + C::S::chunk(row, col)) = qreg[i];
+          *(i32x4*)(ob + C::S::chunk(row, col)) = oreg[i];
+        }
+      }
+      if (threadIdx.x < BM) {
+        const size_t li = (size_t)h * total_tokens + s0 + min(q0 + (int)threadIdx.x, L - 1);
+        ((float*)lb)[threadIdx.x] = lse[li];
+        ((float*)lb)[BM + threadIdx.x] = delta[li];
+      }
     }
-    if (threadIdx.x < BM) { lb[threadIdx.x] = lreg; db[threadIdx.x] = dreg; }
   };
 
-  if (n_steps > 0) {
-    load_step(0);
-    store_step(0);
-  }
-  __syncthreads();
-  for (int st = 0; st < n_steps; ++st) {
-    if (st + 1 < n_steps) load_step(st + 1);
+  auto stage_finish = [&](char* qb) {   // d = 128: LSE and D registers -> LDS (after compute)
+    if constexpr (D == 128) {
+      if (threadIdx.x < BM) {
+        float* lb = (float*)(qb + 2 * TILE);
+        lb[threadIdx.x] = lreg;
+        lb[BM + threadIdx.x] = dreg;
+      }
+    }
+  };
+
+  auto iter = [&](int st, const char* qb, char* nxt) __attribute__((always_inline)) {
+    if (st + 1 < n_steps) stage(st + 1, nxt);
     const int q0 = q_begin + (st % n_qt) * BM;
-    if (q0 + BM - 1 >= wave_first_q && mykey - (lane & 31) < L) {
-      const char* qb = smem + (st & 1) * STAGE;
+    if (q0 + BM - 1 >= wave_first_q && kw0 < L) {
       const char* ob = qb + TILE;
       const float* lb = (const float*)(ob + TILE);
       const float* db = lb + BM;
       const bool need_mask = causal && (q0 < kw0 + 31);
-      bf16x8 pf[4], sf[4];
+      const bool ragged = q0 + BM > L;
+      // ---- S = Q Kᵀ and dP = dO Vᵀ for the two 32-query blocks (operand rows read as a batch)
+      f32x16 sacc[QB], pacc[QB];
 #pragma unroll
-      for (int qb2 = 0; qb2 < 2; ++qb2) {
-        f32x16 sacc = f32x16{}, pacc = f32x16{};
-        const char* qrow = qb + (32 * qb2 + (lane & 31)) * C::RSTR + 16 * half;
-        const char* orow = ob + (32 * qb2 + (lane & 31)) * C::RSTR + 16 * half;
+      for (int qb2 = 0; qb2 < QB; ++qb2) {
+        i32x4 fq[C::DS], fo[C::DS];
 #pragma unroll
         for (int s = 0; s < C::DS; ++s) {
-          sacc = mfma32(__builtin_bit_cast(bf16x8, *(const i32x4*)(qrow + 32 * s)), kf[s], sacc);
-          pacc = mfma32(__builtin_bit_cast(bf16x8, *(const i32x4*)(orow + 32 * s)), vf[s], pacc);
+          fq[s] = *(const i32x4*)(qb + qb2 * 32 * C::RSTR + so.row[s]);
+          fo[s] = *(const i32x4*)(ob + qb2 * 32 * C::RSTR + so.row[s]);
         }
+        sacc[qb2] = f32x16{};
+        pacc[qb2] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < C::DS; ++s) {
+          sacc[qb2] = mfma32(as_bf16x8(fq[s]), kf[s], sacc[qb2]);
+          pacc[qb2] = mfma32(as_bf16x8(fo[s]), vf[s], pacc[qb2]);
+        }
+        // issue the operand reads well ahead of the products they feed
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // 8 LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+      }
+      // ---- P = exp(S - LSE) (masked), dS = P (dP - D), packed to bf16 B operands
+      bf16x8 pf[2 * QB], sf[2 * QB];
+#pragma unroll
+      for (int qb2 = 0; qb2 < QB; ++qb2)
 #pragma unroll
         for (int j = 0; j < 16; j += 2) {
           float pv[2], dsv[2];
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int qi_t = 32 * qb2 + 8 * ((j + u) >> 2) + 4 * half + ((j + u) & 3);  // tile-local query
-            float x = exp2f(sacc[j + u] * sl2 - lb[qi_t]);
+            float x = exp2f(sacc[qb2][j + u] * sl2 - lb[qi_t] * LOG2E);
             if (need_mask && mykey > q0 + qi_t) x = 0.f;
+            if (ragged && q0 + qi_t >= L) x = 0.f;      // rows past the document end
             pv[u] = x;
-            dsv[u] = x * (pacc[j + u] - db[qi_t]);
+            dsv[u] = x * (pacc[qb2][j + u] - db[qi_t]);
           }
           const int fi = 2 * qb2 + (j >> 3);
           i32x4 up = __builtin_bit_cast(i32x4, pf[fi]);
@@ -185,25 +225,41 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
           pf[fi] = __builtin_bit_cast(bf16x8, up);
           sf[fi] = __builtin_bit_cast(bf16x8, us);
         }
-      }
-      // dVᵀ += dOᵀ P,  dKᵀ += Qᵀ dS  (A operands through transposing LDS reads)
+      // ---- dVᵀ += dOᵀ P, dKᵀ += Qᵀ dS (A operands through transposing LDS reads, batched per kk)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int rbase = 32 * (kk >> 1) + 16 * (kk & 1);
-        const int row = rbase + 4 * half + ((lane & 15) >> 2);
-        const int dsub = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      for (int kk = 0; kk < 2 * QB; ++kk) {
+        const int rb = (32 * (kk >> 1) + 16 * (kk & 1)) * C::RSTR;
+        bf16x8 ao[C::DB], aq[C::DB];
 #pragma unroll
         for (int dbk = 0; dbk < C::DB; ++dbk) {
-          const int boff = row * C::RSTR + (32 * dbk + dsub) * 2;
-          const bf16x8 ao = concat_tr(lds_read_tr16(ob + boff), lds_read_tr16(ob + boff + 8 * C::RSTR));
-          dva[dbk] = mfma32(ao, pf[kk], dva[dbk]);
-          const bf16x8 aq = concat_tr(lds_read_tr16(qb + boff), lds_read_tr16(qb + boff + 8 * C::RSTR));
-          dka[dbk] = mfma32(aq, sf[kk], dka[dbk]);
+          ao[dbk] = concat_tr(lds_read_tr16(ob + rb + so.tr0[dbk]), lds_read_tr16(ob + rb + so.tr1[dbk]));
+          aq[dbk] = concat_tr(lds_read_tr16(qb + rb + so.tr0[dbk]), lds_read_tr16(qb + rb + so.tr1[dbk]));
         }
+#pragma unroll
+        for (int dbk = 0; dbk < C::DB; ++dbk) {
+          dva[dbk] = mfma32(ao[dbk], pf[kk], dva[dbk]);
+          dka[dbk] = mfma32(aq[dbk], sf[kk], dka[dbk]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // 8 transposed reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
       }
     }
-    if (st + 1 < n_steps) store_step((st + 1) & 1);
+    if (st + 1 < n_steps) stage_finish(nxt);
+    wait_vmem();
     __syncthreads();
+  };
+
+  if (n_steps > 0) {
+    stage(0, lds_a);
+    stage_finish(lds_a);
+  }
+  wait_vmem();
+  __syncthreads();
+  for (int st = 0; st < n_steps; st += 2) {
+    iter(st, lds_a, lds_b);
+    if (st + 1 < n_steps) iter(st + 1, lds_b, lds_a);
   }
 
   // write dK = scale·dKᵀ and dV (lane: key mykey, d = 32 db + 8 jg + 4·half + 0..3)
@@ -236,7 +292,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   constexpr int STAGE = 2 * TILE;
   constexpr int CH = BN * D / 8;
   constexpr int PT = CH / 256;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  // two separate buffers so that the compiler sees the copy into one never aliases the other
+  __shared__ __attribute__((aligned(16))) char lds_a[STAGE];
+  __shared__ __attribute__((aligned(16))) char lds_b[STAGE];
 
   const int p = blockIdx.x / hq, h = blockIdx.x % hq;
   int s0, L, t;
@@ -249,6 +307,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   const int n_kt = (kv_end + BN - 1) / BN;
   const int wave_last_key = causal ? min(L, wr0 + 32) - 1 : L - 1;
   const float sl2 = scale * LOG2E;
+  const SwzOffsets<D> so(lane);
 
   bf16x8 qf[C::DS], of[C::DS];
   float lse2 = INFINITY, dl = 0.f;
@@ -269,54 +328,65 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 #pragma unroll
   for (int b = 0; b < C::DB; ++b) dqa[b] = f32x16{};
 
-  i32x4 kreg[PT], vreg[PT];
-  auto load_tile = [&](int kt) {
+  // K/V tile kt -> LDS buffer; keys past kv_end are clamped into the document (masked, P = 0)
+  auto stage = [&](int kt, char* kb) {
     const int k0 = kt * BN;
-#pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      const int key = c / (D / 8), col = c % (D / 8);
-      const bool ok = (k0 + key) < kv_end;
-      const size_t off = ((size_t)(s0 + (ok ? k0 + key : 0)) * hkv + g) * D + col * 8;
-      kreg[i] = ok ? *(const i32x4*)(k + off) : i32x4{0, 0, 0, 0};
-      vreg[i] = ok ? *(const i32x4*)(v + off) : i32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_tile = [&](int buf) {
-    char* kb = smem + buf * STAGE;
     char* vb = kb + TILE;
+    if constexpr (D == 128) {
+      auto krow = [&](int r) { return (const char*)(k + ((size_t)(s0 + min(k0 + r, kv_end - 1)) * hkv + g) * D); };
+      auto vrow = [&](int r) { return (const char*)(v + ((size_t)(s0 + min(k0 + r, kv_end - 1)) * hkv + g) * D); };
+      stage_rows_lds<BN>(kb, krow, w, lane);
+      stage_rows_lds<BN>(vb, vrow, w, lane);
+    } else {
+      i32x4 kreg[PT], vreg[PT];
 #pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      const int key = c / (D / 8), col = c % (D / 8);
-      *(i32x4*)(kb + key * C::RSTR + col * 16) = kreg[i];
-      *(i32x4*)(vb + key * C::RSTR + col * 16) = vreg[i];
+      for (int i = 0; i < PT; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        const int key = c / (D / 8), col = c % (D / 8);
+        const size_t off = ((size_t)(s0 + min(k0 + key, kv_end - 1)) * hkv + g) * D + col * 8;
+        kreg[i] = *(const i32x4*)(k + off);
+        vreg[i] = *(const i32x4*)(v + off);
+      }
+#pragma unroll
+      for (int i = 0; i < PT; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        const int key = c / (D / 8), col = c % (D / 8);
+        *(i32x4*)(kb + C::S::chunk(key, col)) = kreg[i];
+        *(i32x4*)(vb + C::S::chunk(key, col)) = vreg[i];
+      }
     }
   };
 
-  if (n_kt > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
+  auto iter = [&](int kt, const char* kb, char* nxt) __attribute__((always_inline)) {
     const int k0 = kt * BN;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
+    if (kt + 1 < n_kt) stage(kt + 1, nxt);
     if (k0 <= wave_last_key) {
-      const char* kb = smem + (kt & 1) * STAGE;
       const char* vb = kb + TILE;
       const bool need_mask = causal ? (k0 + BN - 1 > wr0) : (k0 + BN > L);
       bf16x8 sf[4];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        f32x16 sacc = f32x16{}, pacc = f32x16{};
-        const char* krow = kb + (32 * b + (lane & 31)) * C::RSTR + 16 * half;
-        const char* vrow = vb + (32 * b + (lane & 31)) * C::RSTR + 16 * half;
+        // Sᵀ = K Qᵀ and dPᵀ = V dOᵀ for one 32-key block, operand rows read as a batch
+        i32x4 fk[C::DS], fv[C::DS];
 #pragma unroll
         for (int s = 0; s < C::DS; ++s) {
-          sacc = mfma32(__builtin_bit_cast(bf16x8, *(const i32x4*)(krow + 32 * s)), qf[s], sacc);
-          pacc = mfma32(__builtin_bit_cast(bf16x8, *(const i32x4*)(vrow + 32 * s)), of[s], pacc);
+          fk[s] = *(const i32x4*)(kb + b * 32 * C::RSTR + so.row[s]);
+          fv[s] = *(const i32x4*)(vb + b * 32 * C::RSTR + so.row[s]);
         }
+        f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+        for (int s = 0; s < C::DS; ++s) {
+          sacc = mfma32(as_bf16x8(fk[s]), qf[s], sacc);
+          pacc = mfma32(as_bf16x8(fv[s]), of[s], pacc);
+        }
+        // keep ~4 operand reads in flight ahead of the products (occupancy 2 register budget)
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < C::DS - 2; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 #pragma unroll
         for (int j = 0; j < 16; j += 2) {
           float dsv[2];
@@ -335,21 +405,28 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
           sf[fi] = __builtin_bit_cast(bf16x8, us);
         }
       }
-      // dQᵀ += Kᵀ dSᵀ
+      // dQᵀ += Kᵀ dSᵀ (Kᵀ through transposing reads, batched per kk)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const int kbase = 32 * (kk >> 1) + 16 * (kk & 1);
-        const int key = kbase + 4 * half + ((lane & 15) >> 2);
-        const int dsub = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const int rb = (32 * (kk >> 1) + 16 * (kk & 1)) * C::RSTR;
+        bf16x8 ak[C::DB];
 #pragma unroll
-        for (int dbk = 0; dbk < C::DB; ++dbk) {
-          const char* p0 = kb + key * C::RSTR + (32 * dbk + dsub) * 2;
-          dqa[dbk] = mfma32(concat_tr(lds_read_tr16(p0), lds_read_tr16(p0 + 8 * C::RSTR)), sf[kk], dqa[dbk]);
-        }
+        for (int dbk = 0; dbk < C::DB; ++dbk)
+          ak[dbk] = concat_tr(lds_read_tr16(kb + rb + so.tr0[dbk]), lds_read_tr16(kb + rb + so.tr1[dbk]));
+#pragma unroll
+        for (int dbk = 0; dbk < C::DB; ++dbk) dqa[dbk] = mfma32(ak[dbk], sf[kk], dqa[dbk]);
       }
     }
-    if (kt + 1 < n_kt) store_tile((kt + 1) & 1);
+    wait_vmem();
     __syncthreads();
+  };
+
+  if (n_kt > 0) stage(0, lds_a);
+  wait_vmem();
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    iter(kt, lds_a, lds_b);
+    if (kt + 1 < n_kt) iter(kt + 1, lds_b, lds_a);
   }
 
   if (qrow < L) {
@@ -387,13 +464,13 @@ static hipError_t launch_dkdv_d(const void* q, const void* k, const void* v, con
                                 const float* delta, void* dk, void* dv, const Plan& plan, int T, int hq, int hkv,
                                 float scale, int causal, hipStream_t stream) {
   const long items = (long)(T + 127) / 128 + plan.n_docs;
-  constexpr int STAGE = 2 * 64 * BwdTile<D>::RSTR + 2 * 64 * 4;
+  constexpr int STAGE = BwdTile<D>::DKDV_STAGE;
   auto kern = attn_bwd_dkdv_kernel<D>;
   if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE))
     return hipErrorInvalidConfiguration;
   const long grid = items * hkv;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 2 * STAGE, stream, (const __bf16*)q, (const __bf16*)k,
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)q, (const __bf16*)k,
                      (const __bf16*)v, (const __bf16*)dout, lse, delta, (__bf16*)dk, (__bf16*)dv, plan, T, hq, hkv,
                      scale, causal);
   return hipGetLastError();
@@ -404,13 +481,10 @@ static hipError_t launch_dq_d(const void* q, const void* k, const void* v, const
                               const float* delta, void* dq, const Plan& plan, int T, int hq, int hkv, float scale,
                               int causal, hipStream_t stream) {
   const long items = (long)(T + 127) / 128 + plan.n_docs;
-  constexpr int STAGE = 2 * 64 * BwdTile<D>::RSTR;
   auto kern = attn_bwd_dq_kernel<D>;
-  if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE))
-    return hipErrorInvalidConfiguration;
   const long grid = items * hq;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 2 * STAGE, stream, (const __bf16*)q, (const __bf16*)k,
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)q, (const __bf16*)k,
                      (const __bf16*)v, (const __bf16*)dout, lse, delta, (__bf16*)dq, plan, T, hq, hkv, scale, causal);
   return hipGetLastError();
 }

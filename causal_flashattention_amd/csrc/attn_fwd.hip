@@ -27,16 +27,19 @@ namespace cfa {
 template <int D>
 struct FwdTile {
   static constexpr int BN = 64;                  // keys per tile
-  static constexpr int KSTR = D * 2 + 16;        // LDS row stride (bytes) of the K tile
-  static constexpr int VSTR = D * 2 + 32;        // LDS row stride (bytes) of the V tile
-  static constexpr int KBYTES = BN * KSTR;
-  static constexpr int VBYTES = BN * VSTR;
+  using S = SwzTile<D>;                          // swizzled rows, see cfa_device.h
+  static constexpr int KBYTES = BN * S::STR;
+  static constexpr int VBYTES = BN * S::STR;
   static constexpr int STAGE = KBYTES + VBYTES;
   static constexpr int CHUNKS = BN * D / 8;      // 16-byte chunks per tile and tensor
   static constexpr int PER_THREAD = CHUNKS / 256;
   static constexpr int DS = D / 16;              // k-steps of the QKᵀ MFMA
   static constexpr int DB = D / 32;              // 32-wide d blocks of Oᵀ
 };
+
+// The running maximum is only moved when a tile's maximum exceeds it by more than this (log2
+// units), which skips most rescalings of the O accumulator.
+constexpr float RESCALE_LOG2 = 8.f;
 
 template <int D, int HPW>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
@@ -45,7 +48,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     int n_hb, float scale_log2, int causal) {
   using C = FwdTile<D>;
   constexpr int BMW = 128 / HPW;  // query rows per workgroup
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  // two separate LDS buffers (not one array indexed at run time) so that the compiler can
+  // tell that the copy into one buffer never aliases the reads of the other
+  __shared__ __attribute__((aligned(16))) char lds_a[C::STAGE];
+  __shared__ __attribute__((aligned(16))) char lds_b[C::STAGE];
 
   const int wid = blockIdx.x;
   const int p = wid / n_hb, hb = wid % n_hb;
@@ -62,6 +68,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   const int wave_last_key = causal ? min(L, wr0 + 32) - 1 : L - 1;
   const int qrow = wr0 + (lane & 31);            // this lane's query (doc-local)
   const int half = lane >> 5;
+  const SwzOffsets<D> so(lane);
 
   // ---- Qᵀ fragments (B operand): lane holds Q[qrow][16s + 8·half .. +8]
   bf16x8 qf[C::DS];
@@ -80,53 +87,67 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   for (int b = 0; b < C::DB; ++b) oacc[b] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // ---- global -> registers -> LDS staging of one K/V tile
-  i32x4 kreg[C::PER_THREAD], vreg[C::PER_THREAD];
-  auto load_tile = [&](int kt) {
+  // ---- staging of one K/V tile into an LDS buffer. d = 128: direct global -> LDS copies
+  // (no registers, completion tracked by vmcnt); d = 64: through registers. Keys past kv_end
+  // are clamped into the document: they are masked (P = 0).
+  auto stage = [&](int kt, char* kb) {
     const int k0 = kt * C::BN;
-#pragma unroll
-    for (int i = 0; i < C::PER_THREAD; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      const int key = c / (D / 8), col = c % (D / 8);
-      const bool ok = (k0 + key) < kv_end;
-      const size_t off = ((size_t)(s0 + (ok ? k0 + key : 0)) * hkv + g) * D + col * 8;
-      kreg[i] = ok ? *(const i32x4*)(k + off) : i32x4{0, 0, 0, 0};
-      vreg[i] = ok ? *(const i32x4*)(v + off) : i32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_tile = [&](int buf) {
-    char* kb = smem + buf * C::STAGE;
     char* vb = kb + C::KBYTES;
+    if constexpr (D == 128) {
+      auto krow = [&](int r) { return (const char*)(k + ((size_t)(s0 + min(k0 + r, kv_end - 1)) * hkv + g) * D); };
+      auto vrow = [&](int r) { return (const char*)(v + ((size_t)(s0 + min(k0 + r, kv_end - 1)) * hkv + g) * D); };
+      stage_rows_lds<C::BN>(kb, krow, w, lane);
+      stage_rows_lds<C::BN>(vb, vrow, w, lane);
+    } else {
+      i32x4 kreg[C::PER_THREAD], vreg[C::PER_THREAD];
 #pragma unroll
-    for (int i = 0; i < C::PER_THREAD; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      const int key = c / (D / 8), col = c % (D / 8);
-      *(i32x4*)(kb + key * C::KSTR + col * 16) = kreg[i];
-      *(i32x4*)(vb + key * C::VSTR + col * 16) = vreg[i];
+      for (int i = 0; i < C::PER_THREAD; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        const int key = c / (D / 8), col = c % (D / 8);
+        const size_t off = ((size_t)(s0 + min(k0 + key, kv_end - 1)) * hkv + g) * D + col * 8;
+        kreg[i] = *(const i32x4*)(k + off);
+        vreg[i] = *(const i32x4*)(v + off);
+      }
+#pragma unroll
+      for (int i = 0; i < C::PER_THREAD; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        const int key = c / (D / 8), col = c % (D / 8);
+        *(i32x4*)(kb + C::S::chunk(key, col)) = kreg[i];
+        *(i32x4*)(vb + C::S::chunk(key, col)) = vreg[i];
+      }
     }
   };
 
-  load_tile(0);
-  store_tile(0);
+  stage(0, lds_a);
+  wait_vmem();
   __syncthreads();
 
-  for (int kt = 0; kt < n_kt; ++kt) {
+  // one key tile: copy tile kt+1 into `nxt` while multiplying tile kt from `cur`
+  auto iter = [&](int kt, const char* cur, char* nxt) __attribute__((always_inline)) {
     const int k0 = kt * C::BN;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
+    if (kt + 1 < n_kt) stage(kt + 1, nxt);
     if (k0 <= wave_last_key) {
-      const char* kb = smem + (kt & 1) * C::STAGE;
+      const char* kb = cur;
       const char* vb = kb + C::KBYTES;
-      // ---- Sᵀ = K Qᵀ for the tile's two 32-key blocks
-      f32x16 sacc[2];
+      // ---- Sᵀ = K Qᵀ for the tile's two 32-key blocks: operand rows read as a batch, the
+      // two accumulators interleaved so consecutive MFMAs are independent
+      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+      {
+        i32x4 fk[2][C::DS];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        sacc[b] = f32x16{};
-        const char* krow = kb + (32 * b + (lane & 31)) * C::KSTR + 16 * half;
+        for (int s = 0; s < C::DS; ++s)
 #pragma unroll
-        for (int s = 0; s < C::DS; ++s) {
-          bf16x8 a = __builtin_bit_cast(bf16x8, *(const i32x4*)(krow + 32 * s));
-          sacc[b] = mfma32(a, qf[s], sacc[b]);
-        }
+          for (int b = 0; b < 2; ++b) fk[b][s] = *(const i32x4*)(kb + b * 32 * C::S::STR + so.row[s]);
+#pragma unroll
+        for (int s = 0; s < C::DS; ++s)
+#pragma unroll
+          for (int b = 0; b < 2; ++b) sacc[b] = mfma32(as_bf16x8(fk[b][s]), qf[s], sacc[b]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::DS - 4, 0);
       }
       // ---- online softmax on this lane's query column
       const bool need_mask = causal ? (k0 + C::BN - 1 > wr0) : (k0 + C::BN > L);
@@ -145,43 +166,51 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
           mt = fmaxf(mt, x);
         }
       mt = wave_max_xor32(mt);
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = exp2f(m_run - m_new);
-      m_run = m_new;
+      // Lazy rescaling: the reference maximum only moves when the tile's maximum exceeds it
+      // by more than RESCALE_LOG2 (then P <= 2^RESCALE_LOG2, harmless in fp32 / bf16); LSE and
+      // O are exact for any reference value.
+      const bool upd = mt > m_run + RESCALE_LOG2;
+      if (__any(upd)) {
+        const float m_new = upd ? mt : m_run;
+        const float alpha = exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+      }
       float ls = 0.f;
       bf16x8 pf[4];
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int j = 0; j < 16; j += 2) {
-          const float p0 = exp2f(sacc[b][j] - m_new);
-          const float p1 = exp2f(sacc[b][j + 1] - m_new);
+          const float p0 = exp2f(sacc[b][j] - m_run);
+          const float p1 = exp2f(sacc[b][j + 1] - m_run);
           ls += p0 + p1;
           const uint32_t pk = pack_bf16x2(p0, p1);
           i32x4 u = __builtin_bit_cast(i32x4, pf[2 * b + (j >> 3)]);
           u[(j & 7) >> 1] = (int)pk;
           pf[2 * b + (j >> 3)] = __builtin_bit_cast(bf16x8, u);
         }
-      l_run = l_run * alpha + ls;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+      l_run += ls;
       // ---- Oᵀ += Vᵀ Pᵀ; Vᵀ fragments via transposing LDS reads
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const int kbase = 32 * (kk >> 1) + 16 * (kk & 1);
-        const int key = kbase + 4 * half + ((lane & 15) >> 2);
-        const int dsub = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const int rb = (32 * (kk >> 1) + 16 * (kk & 1)) * C::S::STR;
+        bf16x8 av[C::DB];
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const char* p0 = vb + key * C::VSTR + (32 * db + dsub) * 2;
-          i16x4 r0 = lds_read_tr16(p0);
-          i16x4 r1 = lds_read_tr16(p0 + 8 * C::VSTR);
-          oacc[db] = mfma32(concat_tr(r0, r1), pf[kk], oacc[db]);
-        }
+        for (int db = 0; db < C::DB; ++db)
+          av[db] = concat_tr(lds_read_tr16(vb + rb + so.tr0[db]), lds_read_tr16(vb + rb + so.tr1[db]));
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) oacc[db] = mfma32(av[db], pf[kk], oacc[db]);
       }
     }
-    if (kt + 1 < n_kt) store_tile((kt + 1) & 1);
+    wait_vmem();
     __syncthreads();
+  };
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    iter(kt, lds_a, lds_b);
+    if (kt + 1 < n_kt) iter(kt + 1, lds_b, lds_a);
   }
 
   // ---- epilogue: O = Oᵀ / l, LSE = (m + log2 l)·ln 2
@@ -288,12 +317,8 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   __bf16* O = (__bf16*)o;
 #define CFA_FWD_LAUNCH(DD, HH)                                                                         \
   do {                                                                                                 \
-    auto kern = attn_fwd_bf16_kernel<DD, HH>;                                                          \
-    const int lds = 2 * FwdTile<DD>::STAGE;                                                            \
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds))       \
-      return hipErrorInvalidConfiguration;                                                             \
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, stream, Q, K, V, O, lse, plan,      \
-                       total_tokens, hq, hkv, n_hb, sl2, causal);                                      \
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DD, HH>), dim3((unsigned)grid), dim3(256), 0, stream, Q, K, V, \
+                       O, lse, plan, total_tokens, hq, hkv, n_hb, sl2, causal);                        \
   } while (0)
   if (d == 128) {
     if (hpw == 4) CFA_FWD_LAUNCH(128, 4);

@@ -110,6 +110,76 @@ __device__ inline int pack_fp8x4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
+// LDS layout of a bf16 tile with rows of D elements that is read both row-wise (ds_read_b128:
+// 16 lanes take one 16-byte chunk of 16 consecutive rows) and transposed (ds_read_b64_tr_b16:
+// 32 lanes take 4 rows × 4 consecutive chunks). For D = 128, rows are 256 bytes (no padding)
+// and chunk c of row r is stored at chunk position c ^ f(r), f(r) = 4·(r%4) + (r/4)%4:
+// f is a bijection on 16 consecutive rows (row reads hit 16 distinct chunk slots) and, for
+// 4 rows r ≡ 0..3 (mod 4), moves the 4-chunk group by a different multiple of 4 (transposed
+// reads hit 16 distinct slots), so both patterns cover the 64 banks once. D = 64 uses a padded
+// 144-byte row instead.
+template <int D>
+struct SwzTile {
+  static constexpr int STR = (D == 128) ? 256 : D * 2 + 16;
+  __device__ static inline int f(int r) { return D == 128 ? (4 * (r & 3) + ((r >> 2) & 3)) : 0; }
+  // byte offset of 16-byte chunk c of row r
+  __device__ static inline int chunk(int r, int c) { return r * STR + ((c ^ f(r)) << 4); }
+  // byte offset of element d of row r (d % 4 == 0 for 8-byte transposed reads)
+  __device__ static inline int elem(int r, int d) { return r * STR + (((d >> 3) ^ f(r)) << 4) + ((d & 7) << 1); }
+};
+
+// Lane-constant byte offsets of the two read patterns on a SwzTile (row blocks of 32 rows and
+// 16-row groups move the offsets by whole rows, which never changes f, so the swizzle is folded
+// into these few registers and the rest are immediate offsets):
+//  row reads:   lane reads chunk 2s + half of row (lane & 31)               -> row[s]
+//  transposed:  lane reads d = 32·db + 16·((lane>>4)&1) + 4·(lane&3) of rows
+//               4·half + (lane&15)/4 (+0 and +8)                            -> tr0[db], tr1[db]
+template <int D>
+struct SwzOffsets {
+  int row[D / 16];
+  int tr0[D / 32], tr1[D / 32];
+  __device__ explicit SwzOffsets(int lane) {
+    using S = SwzTile<D>;
+    const int half = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) row[s] = S::chunk(lane & 31, 2 * s + half);
+    const int r = 4 * half + ((lane & 15) >> 2);
+    const int dsub = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      tr0[db] = S::elem(r, 32 * db + dsub);
+      tr1[db] = S::elem(r + 8, 32 * db + dsub);
+    }
+  }
+};
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): the wave writes
+// 1 KB at lds_wave_base + 16·lane; lds_wave_base must be the same for the whole wave.
+__device__ inline void g2lds16(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+__device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Stage ROWS rows of 128 bf16 (256 bytes) into a SwzTile<128> LDS tile with direct loads.
+// Called by all 4 waves; wave w copies the 1 KB blocks [w·ROWS/16, (w+1)·ROWS/16), block I
+// holding rows 4I..4I+3. Lane i fills physical chunk i%16 of row 4I + i/16, i.e. logical chunk
+// (i%16) ^ f(row): the swizzle is applied on the global side. rowptr(r) returns the global
+// address (bytes) of tile row r.
+template <int ROWS, typename RowPtr>
+__device__ inline void stage_rows_lds(char* tile, RowPtr rowptr, int wave, int lane) {
+  static_assert(ROWS % 16 == 0, "4 waves × 4 rows per block");
+  constexpr int PER_WAVE = ROWS / 16;
+#pragma unroll
+  for (int j = 0; j < PER_WAVE; ++j) {
+    const int I = wave * PER_WAVE + j;
+    const int r = 4 * I + (lane >> 4);
+    const int c = (lane & 15) ^ SwzTile<128>::f(r);
+    g2lds16(rowptr(r) + c * 16, tile + I * 1024);
+  }
+}
+
+__device__ inline bf16x8 as_bf16x8(const i32x4& u) { return __builtin_bit_cast(bf16x8, u); }
+
 __device__ inline float wave_max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 __device__ inline float wave_sum_xor32(float x) { return x + __shfl_xor(x, 32); }
 
