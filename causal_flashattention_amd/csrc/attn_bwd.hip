@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int qi_t = 32 * qb2 + 8 * ((j + u) >> 2) + 4 * half + ((j + u) & 3);  // tile-local query
-            float x = exp2f(sacc[qb2][j + u] * sl2 - lb[qi_t] * LOG2E);
+            float x = exp2_fast(sacc[qb2][j + u] * sl2 - lb[qi_t] * LOG2E);
             if (need_mask && mykey > q0 + qi_t) x = 0.f;
             if (ragged && q0 + qi_t >= L) x = 0.f;      // rows past the document end
             pv[u] = x;
@@ -276,6 +276,228 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
         uv.y = (int)pack_bf16x2(dva[dbk][4 * jg + 2], dva[dbk][4 * jg + 3]);
         *(i32x2*)(dk + base + 32 * dbk + 8 * jg) = uk;
         *(i32x2*)(dv + base + 32 * dbk + 8 * jg) = uv;
+      }
+  }
+}
+
+// ------------------------------------------------------------------ dK / dV, d = 128, wave pairs
+// 8 waves own 128 keys of one kv head, as 4 pairs of 32 keys. In a pair, the "P wave" (w < 4)
+// holds K and computes S = Q Kᵀ, P = exp(S − LSE), dVᵀ += dOᵀ P; the "dS wave" (w + 4) holds V
+// and computes dP = dO Vᵀ, dS = P (dP − D), dKᵀ += Qᵀ dS with the fp32 P that its partner left
+// in LDS one step earlier. Running the dS wave one step behind removes every wait between the
+// two inside a step; the two waves of a pair sit on the same SIMD, so one wave's exponentials
+// and packing overlap the other's matrix products. Each wave holds one accumulator (dVᵀ or
+// dKᵀ) and one operand set (K or V), which is what brings two waves per SIMD within the
+// register file. Staging buffers: step i (Q, dO tiles, LSE·log2 e, D) lives in buffer i mod 3
+// and P of step i in exchange buffer i mod 3, so the loop is unrolled three times and every
+// buffer is a distinct static array (no aliasing between the copies in flight and the reads).
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    __bf16* __restrict__ dk, __bf16* __restrict__ dv, Plan plan, int total_tokens, int hq, int hkv,
+    float scale, int causal) {
+  constexpr int D = 128;
+  using C = BwdTile<D>;
+  constexpr int BM = 32;                          // queries per step
+  constexpr int TILE = BM * C::RSTR;              // 8 KB
+  constexpr int STAGE = 2 * TILE + 2 * BM * 4;    // Q, dO, LSE·log2 e, D
+  constexpr int XP = 4 * 4 * 64;                  // f32x4 per exchange buffer: [pair][j/4][lane]
+  __shared__ __attribute__((aligned(16))) char st_a[STAGE];
+  __shared__ __attribute__((aligned(16))) char st_b[STAGE];
+  __shared__ __attribute__((aligned(16))) char st_c[STAGE];
+  __shared__ f32x4 xp_a[XP];
+  __shared__ f32x4 xp_b[XP];
+  __shared__ f32x4 xp_c[XP];
+
+  const int p = blockIdx.x / hkv, g = blockIdx.x % hkv;
+  int s0, L, t;
+  if (!decode_item(plan, p, 128, false, s0, L, t)) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5;
+  const int pair = w & 3;
+  const bool ds_wave = w >= 4;
+  const int G = hq / hkv;
+  const int kw0 = t * 128 + 32 * pair;            // first doc-local key of this pair
+  const int mykey = kw0 + (lane & 31);
+  const float sl2 = scale * LOG2E;
+  const SwzOffsets<D> so(lane);
+
+  // B operand rows (lane: key mykey, d = 16s + 8·half ..): K for the P wave, V for the dS wave
+  bf16x8 kv[C::DS];
+  {
+    const bool ok = mykey < L;
+    const __bf16* src = ds_wave ? v : k;
+    const size_t off = ((size_t)(s0 + (ok ? mykey : 0)) * hkv + g) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < C::DS; ++s)
+      kv[s] = __builtin_bit_cast(bf16x8, ok ? *(const i32x4*)(src + off + 16 * s) : i32x4{0, 0, 0, 0});
+  }
+  f32x16 acc[C::DB];                              // dVᵀ (P wave) or dKᵀ (dS wave)
+#pragma unroll
+  for (int b = 0; b < C::DB; ++b) acc[b] = f32x16{};
+
+  const int q_begin = causal ? t * 128 : 0;
+  const int n_qt = (L - q_begin + BM - 1) / BM;
+  const int n_steps = n_qt * G;
+  const int wave_first_q = causal ? kw0 : 0;
+
+  // Step st -> buffer: P waves copy the Q tile, dS waves the dO tile (direct global -> LDS);
+  // lanes 0..31 of wave 0 fetch LSE and D into registers, written by stage_finish. Rows past
+  // the document end are clamped into it and masked (P = 0).
+  float lreg = 0.f, dreg = 0.f;
+  auto stage = [&](int st, char* buf) {
+    const int h = g * G + st / n_qt;
+    const int q0 = q_begin + (st % n_qt) * BM;
+    const __bf16* src = ds_wave ? dout : q;
+    auto row = [&](int r) { return (const char*)(src + ((size_t)(s0 + min(q0 + r, L - 1)) * hq + h) * D); };
+    stage_rows_lds<BM>(buf + (ds_wave ? TILE : 0), row, pair, lane);
+    if (threadIdx.x < BM) {
+      const size_t li = (size_t)h * total_tokens + s0 + min(q0 + (int)threadIdx.x, L - 1);
+      lreg = lse[li];
+      dreg = delta[li];
+    }
+  };
+  auto stage_finish = [&](char* buf) {
+    if (threadIdx.x < BM) {
+      float* lb = (float*)(buf + 2 * TILE);
+      lb[threadIdx.x] = lreg * LOG2E;
+      lb[BM + threadIdx.x] = dreg;
+    }
+  };
+  auto active = [&](int st) {
+    const int q0 = q_begin + (st % n_qt) * BM;
+    return q0 + BM - 1 >= wave_first_q && kw0 < L;
+  };
+
+  // P wave, step st: S, P (to the exchange buffer and, as bf16, to the dV product), dVᵀ += dOᵀ P
+  auto step_p = [&](int st, const char* buf, f32x4* xw) __attribute__((always_inline)) {
+    const int q0 = q_begin + (st % n_qt) * BM;
+    const char* ob = buf + TILE;
+    const f32x4* l2 = (const f32x4*)(buf + 2 * TILE);
+    i32x4 fq[C::DS];
+#pragma unroll
+    for (int s = 0; s < C::DS; ++s) fq[s] = *(const i32x4*)(buf + so.row[s]);
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < C::DS; ++s) sacc = mfma32(as_bf16x8(fq[s]), kv[s], sacc);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    const bool need_mask = causal && (q0 < kw0 + 31);
+    const bool ragged = q0 + BM > L;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {              // rows 8·jj + 4·half + u
+      const f32x4 lr = l2[2 * jj + half];
+      f32x4 pv;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int qi = 8 * jj + 4 * half + u;
+        float x = exp2_fast(fmaf(sacc[4 * jj + u], sl2, -lr[u]));
+        if (need_mask && mykey > q0 + qi) x = 0.f;
+        if (ragged && q0 + qi >= L) x = 0.f;
+        pv[u] = x;
+      }
+      xw[(pair * 4 + jj) * 64 + lane] = pv;
+      i32x4 up = __builtin_bit_cast(i32x4, pf[jj >> 1]);
+      up[2 * (jj & 1)] = (int)pack_bf16x2(pv[0], pv[1]);
+      up[2 * (jj & 1) + 1] = (int)pack_bf16x2(pv[2], pv[3]);
+      pf[jj >> 1] = __builtin_bit_cast(bf16x8, up);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int rb = 16 * kk * C::RSTR;
+      bf16x8 ao[C::DB];
+#pragma unroll
+      for (int dbk = 0; dbk < C::DB; ++dbk)
+        ao[dbk] = concat_tr(lds_read_tr16(ob + rb + so.tr0[dbk]), lds_read_tr16(ob + rb + so.tr1[dbk]));
+#pragma unroll
+      for (int dbk = 0; dbk < C::DB; ++dbk) acc[dbk] = mfma32(ao[dbk], pf[kk], acc[dbk]);
+    }
+  };
+
+  // dS wave, step st (one iteration after its P wave): dP, dS = P (dP − D), dKᵀ += Qᵀ dS
+  auto step_ds = [&](int st, const char* buf, const f32x4* xr) __attribute__((always_inline)) {
+    const char* ob = buf + TILE;
+    const f32x4* db = (const f32x4*)(buf + 2 * TILE + BM * 4);
+    i32x4 fo[C::DS];
+#pragma unroll
+    for (int s = 0; s < C::DS; ++s) fo[s] = *(const i32x4*)(ob + so.row[s]);
+    f32x16 pacc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < C::DS; ++s) pacc = mfma32(as_bf16x8(fo[s]), kv[s], pacc);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    bf16x8 sf[2];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const f32x4 pv = xr[(pair * 4 + jj) * 64 + lane];
+      const f32x4 dd = db[2 * jj + half];
+      float dsv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) dsv[u] = pv[u] * (pacc[4 * jj + u] - dd[u]);
+      i32x4 us = __builtin_bit_cast(i32x4, sf[jj >> 1]);
+      us[2 * (jj & 1)] = (int)pack_bf16x2(dsv[0], dsv[1]);
+      us[2 * (jj & 1) + 1] = (int)pack_bf16x2(dsv[2], dsv[3]);
+      sf[jj >> 1] = __builtin_bit_cast(bf16x8, us);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int rb = 16 * kk * C::RSTR;
+      bf16x8 aq[C::DB];
+#pragma unroll
+      for (int dbk = 0; dbk < C::DB; ++dbk)
+        aq[dbk] = concat_tr(lds_read_tr16(buf + rb + so.tr0[dbk]), lds_read_tr16(buf + rb + so.tr1[dbk]));
+#pragma unroll
+      for (int dbk = 0; dbk < C::DB; ++dbk) acc[dbk] = mfma32(aq[dbk], sf[kk], acc[dbk]);
+    }
+  };
+
+  // Iteration i: copy step i+1 into `nxt`; P waves run step i on `cur`; dS waves run step i-1
+  // on `prv`. The conditions depend on i only, so every wave meets the same barriers.
+  auto iter = [&](int i, char* cur, char* prv, char* nxt, f32x4* xcur, const f32x4* xprv)
+      __attribute__((always_inline)) {
+    if (i + 1 < n_steps) stage(i + 1, nxt);
+    if (!ds_wave) {
+      if (i < n_steps && active(i)) step_p(i, cur, xcur);
+    } else {
+      if (i >= 1 && active(i - 1)) step_ds(i - 1, prv, xprv);
+    }
+    if (i + 1 < n_steps) stage_finish(nxt);
+    wait_vmem();
+    __syncthreads();
+  };
+
+  if (n_steps > 0) {
+    stage(0, st_a);
+    stage_finish(st_a);
+  }
+  wait_vmem();
+  __syncthreads();
+  for (int i = 0; i <= n_steps; i += 3) {
+    iter(i, st_a, st_c, st_b, xp_a, xp_c);
+    if (i + 1 <= n_steps) iter(i + 1, st_b, st_a, st_c, xp_b, xp_a);
+    if (i + 2 <= n_steps) iter(i + 2, st_c, st_b, st_a, xp_c, xp_b);
+  }
+
+  // dS wave: dK = scale·dKᵀ; P wave: dV (lane: key mykey, d = 32 db + 8 jg + 4·half + 0..3)
+  if (mykey < L) {
+    const float f = ds_wave ? scale : 1.f;
+    __bf16* dst = (ds_wave ? dk : dv) + ((size_t)(s0 + mykey) * hkv + g) * D + 4 * half;
+#pragma unroll
+    for (int dbk = 0; dbk < C::DB; ++dbk)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        i32x2 u;
+        u.x = (int)pack_bf16x2(acc[dbk][4 * jg] * f, acc[dbk][4 * jg + 1] * f);
+        u.y = (int)pack_bf16x2(acc[dbk][4 * jg + 2] * f, acc[dbk][4 * jg + 3] * f);
+        *(i32x2*)(dst + 32 * dbk + 8 * jg) = u;
       }
   }
 }
@@ -392,7 +614,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
           float dsv[2];
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            float x = exp2f(sacc[j + u] * sl2 - lse2);
+            float x = exp2_fast(sacc[j + u] * sl2 - lse2);
             if (need_mask) {
               const int key = k0 + 32 * b + 8 * ((j + u) >> 2) + 4 * half + ((j + u) & 3);
               if (causal ? (key > qrow) : (key >= L)) x = 0.f;
@@ -464,6 +686,14 @@ static hipError_t launch_dkdv_d(const void* q, const void* k, const void* v, con
                                 const float* delta, void* dk, void* dv, const Plan& plan, int T, int hq, int hkv,
                                 float scale, int causal, hipStream_t stream) {
   const long items = (long)(T + 127) / 128 + plan.n_docs;
+  if constexpr (D == 128) {
+    const long grid = items * hkv;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(attn_bwd_dkdv_pair_kernel, dim3((unsigned)grid), dim3(512), 0, stream, (const __bf16*)q,
+                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, lse, delta, (__bf16*)dk, (__bf16*)dv,
+                       plan, T, hq, hkv, scale, causal);
+    return hipGetLastError();
+  }
   constexpr int STAGE = BwdTile<D>::DKDV_STAGE;
   auto kern = attn_bwd_dkdv_kernel<D>;
   if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE))

@@ -317,7 +317,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mx_kernel(
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int qi_t = 32 * qb2 + 8 * (j >> 2) + 4 * half + (j & 3);
-          float x = exp2f(sacc[j] * sl2 - lb[qi_t]);
+          float x = exp2_fast(sacc[j] * sl2 - lb[qi_t]);
           if (need_mask && mykey > q0 + qi_t) x = 0.f;
           pv[qb2][j] = x;
           dsv[qb2][j] = x * (pacc[j] - db[qi_t]);
@@ -546,7 +546,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_mx_kernel(
         }
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          float x = exp2f(sacc[j] * sl2 - lse2);
+          float x = exp2_fast(sacc[j] * sl2 - lse2);
           if (need_mask) {
             const int key = k0 + 32 * b + 8 * (j >> 2) + 4 * half + (j & 3);
             if (causal ? (key > qrow) : (key >= L)) x = 0.f;

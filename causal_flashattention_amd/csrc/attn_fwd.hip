@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       const bool upd = mt > m_run + RESCALE_LOG2;
       if (__any(upd)) {
         const float m_new = upd ? mt : m_run;
-        const float alpha = exp2f(m_run - m_new);
+        const float alpha = exp2_fast(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
 #pragma unroll
@@ -184,8 +184,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int j = 0; j < 16; j += 2) {
-          const float p0 = exp2f(sacc[b][j] - m_run);
-          const float p1 = exp2f(sacc[b][j + 1] - m_run);
+          const float p0 = exp2_fast(sacc[b][j] - m_run);
+          const float p1 = exp2_fast(sacc[b][j + 1] - m_run);
           ls += p0 + p1;
           const uint32_t pk = pack_bf16x2(p0, p1);
           i32x4 u = __builtin_bit_cast(i32x4, pf[2 * b + (j >> 3)]);
@@ -278,11 +278,11 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(
       mt = fmaxf(mt, s[j]);
     }
     const float m_new = fmaxf(m_run, mt);
-    const float alpha = exp2f(m_run - m_new);
+    const float alpha = exp2_fast(m_run - m_new);
     l_run *= alpha;
     for (int r = 0; r < D; ++r) acc[r] *= alpha;
     for (int j = 0; j < KT; ++j) {
-      const float pj = exp2f(s[j] - m_new);
+      const float pj = exp2_fast(s[j] - m_new);
       l_run += pj;
       for (int r = 0; r < D; ++r) acc[r] = fmaf(pj, vs[j][r], acc[r]);
     }

@@ -206,14 +206,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
         }
       mt = wave_max_xor32(mt);
       const float m_new = fmaxf(m_run, mt);
-      const float alpha = exp2f(m_run - m_new);
+      const float alpha = exp2_fast(m_run - m_new);
       m_run = m_new;
       float ls = 0.f;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const float pj = exp2f(sacc[b][j] - m_new);
+          const float pj = exp2_fast(sacc[b][j] - m_new);
           sacc[b][j] = pj;
           ls += pj;
         }

@@ -180,6 +180,10 @@ __device__ inline void stage_rows_lds(char* tile, RowPtr rowptr, int wave, int l
 
 __device__ inline bf16x8 as_bf16x8(const i32x4& u) { return __builtin_bit_cast(bf16x8, u); }
 
+// 2^x with the bare v_exp_f32: results below 2^-126 may flush to zero, which is negligible in
+// every use here (probabilities and rescale factors next to a row sum of at least 1).
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ inline float wave_max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 __device__ inline float wave_sum_xor32(float x) { return x + __shfl_xor(x, 32); }
 
