@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int qi_t = 32 * qb2 + 8 * ((j + u) >> 2) + 4 * half + ((j + u) & 3);  // tile-local query
-            float x = exp2_fast(sacc[qb2][j + u] * sl2 - lb[qi_t] * LOG2E);
+            float x = exp2_fast(fmaf(sacc[qb2][j + u], sl2, -lb[qi_t] * LOG2E));
             if (need_mask && mykey > q0 + qi_t) x = 0.f;
             if (ragged && q0 + qi_t >= L) x = 0.f;      // rows past the document end
             pv[u] = x;
@@ -385,25 +385,26 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-    const bool need_mask = causal && (q0 < kw0 + 31);
-    const bool ragged = q0 + BM > L;
+    // masked scores -> -inf (wave-uniform branch: only steps that cross the diagonal or the
+    // document end), so P = 2^(s·c − LSE·log2 e) is exactly 0 there
+    if ((causal && q0 < kw0 + 31) || q0 + BM > L) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int qi = q0 + 8 * (j >> 2) + 4 * half + (j & 3);
+        if ((causal && mykey > qi) || qi >= L) sacc[j] = -INFINITY;
+      }
+    }
+    float x[16];
     bf16x8 pf[2];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {              // rows 8·jj + 4·half + u
       const f32x4 lr = l2[2 * jj + half];
-      f32x4 pv;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int qi = 8 * jj + 4 * half + u;
-        float x = exp2_fast(fmaf(sacc[4 * jj + u], sl2, -lr[u]));
-        if (need_mask && mykey > q0 + qi) x = 0.f;
-        if (ragged && q0 + qi >= L) x = 0.f;
-        pv[u] = x;
-      }
-      xw[(pair * 4 + jj) * 64 + lane] = pv;
+      for (int u = 0; u < 4; ++u) x[4 * jj + u] = exp2_fast(fmaf(sacc[4 * jj + u], sl2, -lr[u]));
+      xw[(pair * 4 + jj) * 64 + lane] = f32x4{x[4 * jj], x[4 * jj + 1], x[4 * jj + 2], x[4 * jj + 3]};
       i32x4 up = __builtin_bit_cast(i32x4, pf[jj >> 1]);
-      up[2 * (jj & 1)] = (int)pack_bf16x2(pv[0], pv[1]);
-      up[2 * (jj & 1) + 1] = (int)pack_bf16x2(pv[2], pv[3]);
+      up[2 * (jj & 1)] = (int)pack_bf16x2(x[4 * jj], x[4 * jj + 1]);
+      up[2 * (jj & 1) + 1] = (int)pack_bf16x2(x[4 * jj + 2], x[4 * jj + 3]);
       pf[jj >> 1] = __builtin_bit_cast(bf16x8, up);
     }
 #pragma unroll
@@ -609,21 +610,22 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        // masked scores -> -inf (wave-uniform branch: diagonal or document-end tiles only),
+        // so P = 2^(s·c − LSE·log2 e) is exactly 0 there
+        if (need_mask) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int key = k0 + 32 * b + 8 * (j >> 2) + 4 * half + (j & 3);
+            if (causal ? (key > qrow) : (key >= L)) sacc[j] = -INFINITY;
+          }
+        }
 #pragma unroll
         for (int j = 0; j < 16; j += 2) {
-          float dsv[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            float x = exp2_fast(sacc[j + u] * sl2 - lse2);
-            if (need_mask) {
-              const int key = k0 + 32 * b + 8 * ((j + u) >> 2) + 4 * half + ((j + u) & 3);
-              if (causal ? (key > qrow) : (key >= L)) x = 0.f;
-            }
-            dsv[u] = x * (pacc[j + u] - dl);
-          }
+          const float x0 = exp2_fast(fmaf(sacc[j], sl2, -lse2));
+          const float x1 = exp2_fast(fmaf(sacc[j + 1], sl2, -lse2));
           const int fi = 2 * b + (j >> 3);
           i32x4 us = __builtin_bit_cast(i32x4, sf[fi]);
-          us[(j & 7) >> 1] = (int)pack_bf16x2(dsv[0], dsv[1]);
+          us[(j & 7) >> 1] = (int)pack_bf16x2(x0 * (pacc[j] - dl), x1 * (pacc[j + 1] - dl));
           sf[fi] = __builtin_bit_cast(bf16x8, us);
         }
       }

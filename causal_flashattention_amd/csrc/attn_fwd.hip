@@ -149,23 +149,27 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::DS - 4, 0);
       }
-      // ---- online softmax on this lane's query column
+      // ---- online softmax on this lane's query column. The maximum is taken on the raw scores
+      // (scale_log2 > 0) and the scale is folded into the exponent, p = 2^(s·c − m). Masking
+      // is a separate, wave-uniform branch taken only by tiles that cross the diagonal or the
+      // document end.
       const bool need_mask = causal ? (k0 + C::BN - 1 > wr0) : (k0 + C::BN > L);
+      if (need_mask) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int key = k0 + 32 * b + 8 * (j >> 2) + 4 * half + (j & 3);
+            const bool masked = causal ? (key > qrow) : (key >= L);
+            if (masked) sacc[b][j] = -INFINITY;
+          }
+      }
       float mt = -INFINITY;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          float x = sacc[b][j] * scale_log2;
-          if (need_mask) {
-            const int key = k0 + 32 * b + 8 * (j >> 2) + 4 * half + (j & 3);
-            const bool masked = causal ? (key > qrow) : (key >= L);
-            x = masked ? -INFINITY : x;
-          }
-          sacc[b][j] = x;
-          mt = fmaxf(mt, x);
-        }
-      mt = wave_max_xor32(mt);
+        for (int j = 0; j < 16; j += 2) mt = fmaxf(mt, fmaxf(sacc[b][j], sacc[b][j + 1]));
+      mt = wave_max_xor32(mt) * scale_log2;
       // Lazy rescaling: the reference maximum only moves when the tile's maximum exceeds it
       // by more than RESCALE_LOG2 (then P <= 2^RESCALE_LOG2, harmless in fp32 / bf16); LSE and
       // O are exact for any reference value.
@@ -184,8 +188,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int j = 0; j < 16; j += 2) {
-          const float p0 = exp2_fast(sacc[b][j] - m_run);
-          const float p1 = exp2_fast(sacc[b][j + 1] - m_run);
+          const float p0 = exp2_fast(fmaf(sacc[b][j], scale_log2, -m_run));
+          const float p1 = exp2_fast(fmaf(sacc[b][j + 1], scale_log2, -m_run));
           ls += p0 + p1;
           const uint32_t pk = pack_bf16x2(p0, p1);
           i32x4 u = __builtin_bit_cast(i32x4, pf[2 * b + (j >> 3)]);

@@ -92,9 +92,12 @@ __device__ inline bf16x8 concat_tr(i16x4 a, i16x4 b) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32; a in bits 15:0.
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 // Scaled FP8 MFMA, E4M3 operands, E8M0 scales (bits 7:0 of sa / sb). Operand layout per lane l:
