@@ -28,48 +28,44 @@ __device__ inline int mx_exp_of(float amax) {
 }
 
 // Encode 2 × 16 values (two 32-element contraction blocks, 16 per lane each) as the B operand:
-// bytes 0-15 block 0 with exponent e0, bytes 16-31 block 1 with exponent e1.
+// bytes 0-15 block 0 with exponent e0, bytes 16-31 block 1 with exponent e1. The exponents come
+// from fit_exp, so every scaled value lies within ±448 and needs no clamp.
 __device__ inline i32x8 encode_b_fp8(const f32x16& x0, const f32x16& x1, int e0, int e1) {
   i32x8 r;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    float a[4], b[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      a[u] = fminf(fmaxf(__builtin_amdgcn_ldexpf(x0[4 * e + u], -e0), -448.f), 448.f);
-      b[u] = fminf(fmaxf(__builtin_amdgcn_ldexpf(x1[4 * e + u], -e1), -448.f), 448.f);
-    }
-    r[e] = pack_fp8x4(a[0], a[1], a[2], a[3]);
-    r[4 + e] = pack_fp8x4(b[0], b[1], b[2], b[3]);
+    r[e] = pack_fp8x4(__builtin_amdgcn_ldexpf(x0[4 * e], -e0), __builtin_amdgcn_ldexpf(x0[4 * e + 1], -e0),
+                      __builtin_amdgcn_ldexpf(x0[4 * e + 2], -e0), __builtin_amdgcn_ldexpf(x0[4 * e + 3], -e0));
+    r[4 + e] = pack_fp8x4(__builtin_amdgcn_ldexpf(x1[4 * e], -e1), __builtin_amdgcn_ldexpf(x1[4 * e + 1], -e1),
+                          __builtin_amdgcn_ldexpf(x1[4 * e + 2], -e1), __builtin_amdgcn_ldexpf(x1[4 * e + 3], -e1));
   }
   return r;
 }
 
-typedef __attribute__((ext_vector_type(2))) float f32x2;
-
-// Residual of a B-operand encoding: x - decode(codes)·2^e for both blocks.
+// Residual of a B-operand encoding: x - decode(codes)·2^e for both blocks (one fma each).
 __device__ inline void residual_fp8(const f32x16& x0, const f32x16& x1, const i32x8& c, int e0, int e1, f32x16& r0,
                                     f32x16& r1) {
+  const float p0 = __builtin_amdgcn_ldexpf(1.f, e0), p1 = __builtin_amdgcn_ldexpf(1.f, e1);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const f32x2 a01 = __builtin_amdgcn_cvt_pk_f32_fp8(c[e], false), a23 = __builtin_amdgcn_cvt_pk_f32_fp8(c[e], true);
     const f32x2 b01 = __builtin_amdgcn_cvt_pk_f32_fp8(c[4 + e], false);
     const f32x2 b23 = __builtin_amdgcn_cvt_pk_f32_fp8(c[4 + e], true);
-    r0[4 * e + 0] = x0[4 * e + 0] - __builtin_amdgcn_ldexpf(a01.x, e0);
-    r0[4 * e + 1] = x0[4 * e + 1] - __builtin_amdgcn_ldexpf(a01.y, e0);
-    r0[4 * e + 2] = x0[4 * e + 2] - __builtin_amdgcn_ldexpf(a23.x, e0);
-    r0[4 * e + 3] = x0[4 * e + 3] - __builtin_amdgcn_ldexpf(a23.y, e0);
-    r1[4 * e + 0] = x1[4 * e + 0] - __builtin_amdgcn_ldexpf(b01.x, e1);
-    r1[4 * e + 1] = x1[4 * e + 1] - __builtin_amdgcn_ldexpf(b01.y, e1);
-    r1[4 * e + 2] = x1[4 * e + 2] - __builtin_amdgcn_ldexpf(b23.x, e1);
-    r1[4 * e + 3] = x1[4 * e + 3] - __builtin_amdgcn_ldexpf(b23.y, e1);
+    r0[4 * e + 0] = fmaf(-a01.x, p0, x0[4 * e + 0]);
+    r0[4 * e + 1] = fmaf(-a01.y, p0, x0[4 * e + 1]);
+    r0[4 * e + 2] = fmaf(-a23.x, p0, x0[4 * e + 2]);
+    r0[4 * e + 3] = fmaf(-a23.y, p0, x0[4 * e + 3]);
+    r1[4 * e + 0] = fmaf(-b01.x, p1, x1[4 * e + 0]);
+    r1[4 * e + 1] = fmaf(-b01.y, p1, x1[4 * e + 1]);
+    r1[4 * e + 2] = fmaf(-b23.x, p1, x1[4 * e + 2]);
+    r1[4 * e + 3] = fmaf(-b23.y, p1, x1[4 * e + 3]);
   }
 }
 
 __device__ inline float amax16(const f32x16& x) {
   float m = 0.f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(x[j]));
+  for (int j = 0; j < 16; j += 2) m = fmaxf(m, fmaxf(fabsf(x[j]), fabsf(x[j + 1])));   // v_max3 with |.|
   return m;
 }
 
@@ -314,11 +310,15 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mx_kernel(
           pacc = mfma32_mx(load_a_fp8(sb + O_OD + qr * C::DSTR + 64 * s, half), (osc >> (8 * (2 * s + half))) & 0xFF,
                            vb[s], vs[s], pacc);
         }
+        if (need_mask) {                 // wave-uniform: steps that cross the diagonal
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (mykey > q0 + 32 * qb2 + 8 * (j >> 2) + 4 * half + (j & 3)) sacc[j] = -INFINITY;
+        }
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int qi_t = 32 * qb2 + 8 * (j >> 2) + 4 * half + (j & 3);
-          float x = exp2_fast(sacc[j] * sl2 - lb[qi_t]);
-          if (need_mask && mykey > q0 + qi_t) x = 0.f;
+          const float x = exp2_fast(fmaf(sacc[j], sl2, -lb[qi_t]));
           pv[qb2][j] = x;
           dsv[qb2][j] = x * (pacc[j] - db[qi_t]);
         }
@@ -544,15 +544,15 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_mx_kernel(
           pacc = mfma32_mx(load_a_fp8(sb + O_VD + kr * C::DSTR + 64 * s, half), (vsc >> (8 * (2 * s + half))) & 0xFF,
                            oa[s], os[s], pacc);
         }
+        if (need_mask) {                 // wave-uniform: diagonal or document-end tiles
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          float x = exp2_fast(sacc[j] * sl2 - lse2);
-          if (need_mask) {
+          for (int j = 0; j < 16; ++j) {
             const int key = k0 + 32 * b + 8 * (j >> 2) + 4 * half + (j & 3);
-            if (causal ? (key > qrow) : (key >= L)) x = 0.f;
+            if (causal ? (key > qrow) : (key >= L)) sacc[j] = -INFINITY;
           }
-          dsv[b][j] = x * (pacc[j] - dl);
         }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dsv[b][j] = exp2_fast(fmaf(sacc[j], sl2, -lse2)) * (pacc[j] - dl);
       }
       if (tile_is_diag(ktile)) {
         bf16x8 sf[4];

@@ -24,6 +24,12 @@
 
 namespace cfa {
 
+// The running maximum moves as soon as a tile's maximum exceeds it (threshold 0, log2 units),
+// so P̃ <= 1 and P̃·2^8 fits E4M3 with 2^-8 as its fixed scale; a larger threshold would push
+// typical probabilities into E4M3's subnormal range. Only the rescaling of O is skipped when
+// no lane's maximum grew.
+constexpr float RESCALE_LOG2_MX = 0.f;
+
 struct MxFwdTile {
   static constexpr int BN = 64;
   static constexpr int D = 128;
@@ -189,37 +195,43 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
           sacc[b] = mfma32_mx(a, sa, qa[s], qs[s], sacc[b]);
         }
       }
-      // ---- online softmax
+      // ---- online softmax: maximum on the raw scores (scale_log2 > 0), scale folded into the
+      // exponent, masks only on tiles crossing the diagonal or the document end (wave-uniform)
       const bool need_mask = causal ? (k0 + C::BN - 1 > wr0) : (k0 + C::BN > L);
+      if (need_mask) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int key = k0 + 32 * b + 8 * (j >> 2) + 4 * half + (j & 3);
+            if (causal ? (key > qrow) : (key >= L)) sacc[b][j] = -INFINITY;
+          }
+      }
       float mt = -INFINITY;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          float x = sacc[b][j] * scale_log2;
-          if (need_mask) {
-            const int key = k0 + 32 * b + 8 * (j >> 2) + 4 * half + (j & 3);
-            x = (causal ? (key > qrow) : (key >= L)) ? -INFINITY : x;
-          }
-          sacc[b][j] = x;
-          mt = fmaxf(mt, x);
-        }
-      mt = wave_max_xor32(mt);
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = exp2_fast(m_run - m_new);
-      m_run = m_new;
+        for (int j = 0; j < 16; j += 2) mt = fmaxf(mt, fmaxf(sacc[b][j], sacc[b][j + 1]));
+      mt = wave_max_xor32(mt) * scale_log2;
+      const bool upd = mt > m_run + RESCALE_LOG2_MX;
+      if (__any(upd)) {
+        const float m_new = upd ? mt : m_run;
+        const float alpha = exp2_fast(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+      }
       float ls = 0.f;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const float pj = exp2_fast(sacc[b][j] - m_new);
+          const float pj = exp2_fast(fmaf(sacc[b][j], scale_log2, -m_run));
           sacc[b][j] = pj;
           ls += pj;
         }
-      l_run = l_run * alpha + ls;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+      l_run += ls;
       if (tile_is_diag(kt)) {
         // ---- diagonal tile: bf16 P and V
         bf16x8 pf[4];
