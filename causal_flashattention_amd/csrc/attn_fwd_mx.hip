@@ -8,18 +8,20 @@
 //    32 channels (a scale never mixes tokens), on every tile, through
 //    v_mfma_scale_f32_32x32x64_f8f6f4. The backward reuses the very same Q_d/K_d bytes.
 //  * O += P V contracts over keys. Off the diagonal, V_t carries one scale per channel and
-//    32 doc-local keys, and P (in [0, 1] after the running-max shift) is encoded E4M3 with the
-//    fixed scale 2^-8 (P·256 <= 256 < 448). On the diagonal 128×128 tile of each document the
-//    token blocks would share a scale between a query and keys after it, so there P and V stay
-//    bf16 and use v_mfma_f32_32x32x16_bf16.
-// Everything else (work list, online softmax, double-buffered LDS staging, Sᵀ orientation)
-// follows the bf16 kernel in attn_fwd.hip.
+//    32 doc-local keys, and P̃ (in [0, 1] after the running-max shift) is encoded E4M3 with the
+//    fixed scale 2^-8 (P̃·2^8 <= 256 < 448; the 2^8 is folded into the exponent). On the
+//    diagonal 128×128 tile of each document the token blocks would share a scale between a
+//    query and keys after it, so there P and V stay bf16 and use v_mfma_f32_32x32x16_bf16.
+// Work list, online softmax, Sᵀ orientation and the two static LDS buffers filled by direct
+// global -> LDS copies follow the bf16 kernel in attn_fwd.hip.
 //
-// Operand staging. K_d rows go to LDS as 128 code bytes (+16 pad) plus 4 scale bytes per key.
-// The scaled MFMA takes, per lane, 16 consecutive k bytes twice; the probabilities of lane
-// group h hold keys {8·(j/4) + 4h + j%4} of each 32-key block, so the V_t tile is written to
-// LDS with its 4-byte chunks of each 32-key block reordered to (0,2,4,6,1,3,5,7): the A read
-// at offset 16h then yields exactly the keys whose probabilities the lane holds.
+// LDS tile (64 keys): K_d codes as 128-byte rows whose 16-byte chunks are XOR-swizzled with
+// (row / 2) % 8, then 4 scale bytes per key; then either the bf16 V rows of a diagonal tile
+// (SwzTile<128>) or the V_t codes as 64-byte channel rows swizzled with (row / 4) % 4 and the
+// 2 × 128 scale bytes of the tile's two key blocks. Both swizzles send the 16 rows read by a
+// 16-lane group to 16 distinct 16-byte bank groups. V_t comes in the kernels' token-blocked
+// layout (mx_quantize.hip): the bytes 16g..16g+15 of each 32-key block hold exactly the keys
+// whose probabilities lane group g holds, so no data is permuted on chip.
 #include "cfa_device.h"
 
 namespace cfa {
@@ -33,20 +35,18 @@ constexpr float RESCALE_LOG2_MX = 0.f;
 struct MxFwdTile {
   static constexpr int BN = 64;
   static constexpr int D = 128;
-  static constexpr int KSTR = 144;                 // K_d code row stride (bytes)
-  static constexpr int K_CODES = BN * KSTR;        // 9216
-  static constexpr int K_SC = BN * 4;              // 256
-  static constexpr int VT_STR = 80;                // V_t code row stride: 64 keys + 16 pad
-  static constexpr int VT_CODES = D * VT_STR;      // 10240
-  static constexpr int VT_SC = D * 2;              // 256 (2 key blocks per channel)
-  static constexpr int VB_STR = D * 2 + 32;        // bf16 V row stride (transposed reads)
-  static constexpr int VB = BN * VB_STR;           // 18432
-  static constexpr int OFF_KSC = K_CODES;
-  static constexpr int OFF_VT = OFF_KSC + K_SC;
-  static constexpr int OFF_VTSC = OFF_VT + VT_CODES;
-  static constexpr int OFF_VB = OFF_VTSC + VT_SC;
-  static constexpr int STAGE = OFF_VB + VB;        // 38400
+  static constexpr int OFF_KSC = BN * 128;           // K_d codes: 64 rows × 128 B
+  static constexpr int OFF_V = OFF_KSC + BN * 4;     // K_d scales: 4 B per key
+  static constexpr int OFF_VTSC = OFF_V + D * 64;    // V_t codes: 128 channel rows × 64 B
+  static constexpr int STAGE = OFF_V + BN * 256;     // union with the bf16 V rows (64 × 256 B)
 };
+
+__device__ inline int kd_swz(int r) { return (r >> 1) & 7; }
+__device__ inline int vt_swz(int r) { return (r >> 2) & 3; }
+
+__device__ inline void g2lds4(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 4, 0, 0);
+}
 
 template <int HPW>
 __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
@@ -58,14 +58,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
   using C = MxFwdTile;
   constexpr int D = C::D;
   constexpr int BMW = 128 / HPW;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ __attribute__((aligned(16))) char lds_a[C::STAGE];
+  __shared__ __attribute__((aligned(16))) char lds_b[C::STAGE];
 
   const int wid = blockIdx.x;
   const int p = wid / n_hb, hb = wid % n_hb;
   int s0, L, t, doc;
   if (!decode_item(plan, p, BMW, true, s0, L, t, &doc)) return;
   const int pcol = padoff[doc];                 // first token-blocked column of the document
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5;
+  const int lp = 32 * ((L + 31) / 32);          // padded document length (columns)
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5, r32 = lane & 31;
   const int G = hq / hkv;
   const int h = hb * HPW + (w % HPW);
   const int g = h / G;
@@ -74,8 +76,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
   const int kv_end = causal ? wg_rows_end : L;
   const int n_kt = (kv_end + C::BN - 1) / C::BN;
   const int wave_last_key = causal ? min(L, wr0 + 32) - 1 : L - 1;
-  const int qrow = wr0 + (lane & 31);
+  const int qrow = wr0 + r32;
   const int diag_blk = causal ? (t * BMW) / 128 : -1;   // the wg's 128-row block
+  const SwzOffsets<D> so(lane);
+  int ko[2][2], vo[2];                          // lane-constant swizzled chunk offsets
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) ko[s][u] = 16 * ((4 * s + 2 * u + half) ^ kd_swz(r32));
+#pragma unroll
+  for (int u = 0; u < 2; ++u) vo[u] = 16 * ((2 * u + half) ^ vt_swz(r32));
 
   // ---- Q_d fragments (B operand of Sᵀ = K Qᵀ): two 64-channel halves
   i32x8 qa[2];
@@ -96,105 +106,59 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
   for (int b = 0; b < 4; ++b) oacc[b] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // ---- staging registers
-  i32x4 kreg[2], vreg[4];
-  int ksreg = 0, vsreg = 0;
   auto tile_is_diag = [&](int kt) { return (kt * C::BN) / 128 == diag_blk; };
-  auto load_tile = [&](int kt) {
+  // Tile kt -> LDS with direct copies. Keys past kv_end are clamped into the document (K_d,
+  // bf16 V) or into its last token block (V_t); they are masked (P = 0).
+  auto stage = [&](int kt, char* tb) {
     const int k0 = kt * C::BN;
-    const int tid = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {  // K_d codes: 64 rows × 8 chunks
-      const int c = tid + 256 * i, key = c >> 3, col = c & 7;
-      const bool ok = k0 + key < kv_end;
-      kreg[i] = ok ? *(const i32x4*)(kd + ((size_t)(s0 + k0 + key) * hkv + g) * D + col * 16) : i32x4{0, 0, 0, 0};
+    for (int j = 0; j < 2; ++j) {               // K_d codes: 8 blocks of 8 rows, 2 per wave
+      const int I = 2 * w + j, r = 8 * I + (lane >> 3);
+      const int c = (lane & 7) ^ kd_swz(r);
+      g2lds16(kd + ((size_t)(s0 + min(k0 + r, kv_end - 1)) * hkv + g) * D + 16 * c, tb + I * 1024);
     }
-    if (tid < 64) {  // K_d scales: one int (4 bytes) per key
-      const bool ok = k0 + tid < kv_end;
-      ksreg = ok ? *(const int*)(kd_sc + ((size_t)(s0 + k0 + tid) * hkv + g) * 4) : 0x7f7f7f7f;
-    }
-    if (tile_is_diag(kt)) {  // bf16 V rows: 64 × 16 chunks
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i, key = c >> 4, col = c & 15;
-        const bool ok = k0 + key < kv_end;
-        vreg[i] = ok ? *(const i32x4*)(v + ((size_t)(s0 + k0 + key) * hkv + g) * D + col * 8) : i32x4{0, 0, 0, 0};
-      }
-    } else {  // V_t codes: 128 channel rows × 4 chunks of 16 keys, and 2 scale bytes per row
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int c = tid + 256 * i, ch = c >> 2, kc = c & 3;
-        const bool ok = k0 + 16 * kc < kv_end;
-        vreg[i] = ok ? *(const i32x4*)(vt + ((size_t)g * D + ch) * t_pad + pcol + k0 + 16 * kc) : i32x4{0, 0, 0, 0};
-      }
-      if (tid < D) {
-        const size_t srow = ((size_t)g * D + tid) * (t_pad / 32) + (pcol + k0) / 32;
-        const int b0 = vt_sc[srow];
-        const int b1 = (k0 + 32 < kv_end) ? vt_sc[srow + 1] : 127;
-        vsreg = b0 | (b1 << 8);
-      }
-    }
-  };
-  auto store_tile = [&](int buf, int kt) {
-    char* st = smem + buf * C::STAGE;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i, key = c >> 3, col = c & 7;
-      *(i32x4*)(st + key * C::KSTR + col * 16) = kreg[i];
-    }
-    if (tid < 64) *(int*)(st + C::OFF_KSC + tid * 4) = ksreg;
+    if (w == 0) g2lds4(kd_sc + ((size_t)(s0 + min(k0 + lane, kv_end - 1)) * hkv + g) * 4, tb + C::OFF_KSC);
     if (tile_is_diag(kt)) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i, key = c >> 4, col = c & 15;
-        *(i32x4*)(st + C::OFF_VB + key * C::VB_STR + col * 16) = vreg[i];
-      }
+      auto vrow = [&](int r) { return (const char*)(v + ((size_t)(s0 + min(k0 + r, kv_end - 1)) * hkv + g) * D); };
+      stage_rows_lds<C::BN>(tb + C::OFF_V, vrow, w, lane);
     } else {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int c = tid + 256 * i, ch = c >> 2, kc = c & 3;
-        // chunk of 16 keys = 4-byte pieces q = 4kc..4kc+3 of the row; piece q (keys 4q..4q+3)
-        // of 32-key block bb = q/8 goes to position (q%8 even ? (q%8)/2 : 4 + (q%8)/2)
-        char* rowp = st + C::OFF_VT + ch * C::VT_STR;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int q = 4 * kc + e;
-          const int bb = q >> 3, qq = q & 7;
-          const int pos = (qq & 1) ? 4 + (qq >> 1) : (qq >> 1);
-          *(int*)(rowp + 32 * bb + 4 * pos) = vreg[i][e];
-        }
+      for (int j = 0; j < 2; ++j) {             // V_t codes: 8 blocks of 16 channel rows, 2 per wave
+        const int I = 2 * w + j, r = 16 * I + (lane >> 2);
+        const int c = (lane & 3) ^ vt_swz(r);
+        const int col = min(k0 + 16 * c, lp - 16);
+        g2lds16(vt + ((size_t)g * D + r) * t_pad + pcol + col, tb + C::OFF_V + I * 1024);
       }
-      if (tid < D) *(uint16_t*)(st + C::OFF_VTSC + tid * 2) = (uint16_t)vsreg;
+      if (w == 1 && lane < 16) {                // V_t scales of the two key blocks
+        const int blk = min((k0 >> 5) + (lane >> 3), lp / 32 - 1);
+        g2lds16(vt_sc + ((size_t)g * (t_pad / 32) + (pcol >> 5) + blk) * D + 16 * (lane & 7), tb + C::OFF_VTSC);
+      }
     }
   };
 
-  load_tile(0);
-  store_tile(0, 0);
+  stage(0, lds_a);
+  wait_vmem();
   __syncthreads();
 
-  for (int kt = 0; kt < n_kt; ++kt) {
+  auto iter = [&](int kt, const char* tb, char* nxt) __attribute__((always_inline)) {
     const int k0 = kt * C::BN;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
+    if (kt + 1 < n_kt) stage(kt + 1, nxt);
     if (k0 <= wave_last_key) {
-      const char* st = smem + (kt & 1) * C::STAGE;
-      // ---- Sᵀ = K_d Q_dᵀ (scaled fp8)
-      f32x16 sacc[2];
+      // ---- Sᵀ = K_d Q_dᵀ (scaled fp8), the two 32-key blocks interleaved
+      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+      int ksc[2];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        sacc[b] = f32x16{};
-        const int krow = 32 * b + (lane & 31);
-        const char* kr = st + krow * C::KSTR;
-        const int ksc = *(const int*)(st + C::OFF_KSC + krow * 4);
+      for (int b = 0; b < 2; ++b) ksc[b] = *(const int*)(tb + C::OFF_KSC + (32 * b + r32) * 4);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const i32x4 lo = *(const i32x4*)(kr + 64 * s + 16 * half);
-          const i32x4 hi = *(const i32x4*)(kr + 64 * s + 32 + 16 * half);
-          const i32x8 a = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-          const int sa = (ksc >> (8 * (2 * s + half))) & 0xFF;
-          sacc[b] = mfma32_mx(a, sa, qa[s], qs[s], sacc[b]);
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const char* kr = tb + (32 * b + r32) * 128;
+          const i32x4 lo = *(const i32x4*)(kr + ko[s][0]);
+          const i32x4 hi = *(const i32x4*)(kr + ko[s][1]);
+          sacc[b] = mfma32_mx(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w},
+                              (ksc[b] >> (8 * (2 * s + half))) & 0xFF, qa[s], qs[s], sacc[b]);
         }
-      }
       // ---- online softmax: maximum on the raw scores (scale_log2 > 0), scale folded into the
       // exponent, masks only on tiles crossing the diagonal or the document end (wave-uniform)
       const bool need_mask = causal ? (k0 + C::BN - 1 > wr0) : (k0 + C::BN > L);
@@ -222,18 +186,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
 #pragma unroll
         for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
       }
+      const bool diag = tile_is_diag(kt);
+      // diagonal tiles: P̃ (bf16); other tiles: P̃·2^8 (E4M3 with scale 2^-8)
+      const float bias = diag ? -m_run : 8.f - m_run;
       float ls = 0.f;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const float pj = exp2_fast(fmaf(sacc[b][j], scale_log2, -m_run));
+          const float pj = exp2_fast(fmaf(sacc[b][j], scale_log2, bias));
           sacc[b][j] = pj;
           ls += pj;
         }
-      l_run += ls;
-      if (tile_is_diag(kt)) {
-        // ---- diagonal tile: bf16 P and V
+      l_run += diag ? ls : ls * (1.f / 256.f);
+      if (diag) {
         bf16x8 pf[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -243,41 +209,41 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
             u[e] = (int)pack_bf16x2(sacc[kk >> 1][8 * (kk & 1) + 2 * e], sacc[kk >> 1][8 * (kk & 1) + 2 * e + 1]);
           pf[kk] = __builtin_bit_cast(bf16x8, u);
         }
-        const char* vb = st + C::OFF_VB;
+        const char* vb = tb + C::OFF_V;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const int kbase = 32 * (kk >> 1) + 16 * (kk & 1);
-          const int key = kbase + 4 * half + ((lane & 15) >> 2);
-          const int dsub = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+          const int rb = (32 * (kk >> 1) + 16 * (kk & 1)) * 256;
+          bf16x8 av[4];
 #pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const char* p0 = vb + key * C::VB_STR + (32 * db + dsub) * 2;
-            oacc[db] = mfma32(concat_tr(lds_read_tr16(p0), lds_read_tr16(p0 + 8 * C::VB_STR)), pf[kk], oacc[db]);
-          }
+          for (int db = 0; db < 4; ++db)
+            av[db] = concat_tr(lds_read_tr16(vb + rb + so.tr0[db]), lds_read_tr16(vb + rb + so.tr1[db]));
+#pragma unroll
+          for (int db = 0; db < 4; ++db) oacc[db] = mfma32(av[db], pf[kk], oacc[db]);
         }
       } else {
-        // ---- off-diagonal tile: P·2^8 as E4M3 (scale byte 127-8), V_t token-blocked
         i32x8 pb;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            pb[4 * b + e] = pack_fp8x4(sacc[b][4 * e] * 256.f, sacc[b][4 * e + 1] * 256.f,
-                                       sacc[b][4 * e + 2] * 256.f, sacc[b][4 * e + 3] * 256.f);
+            pb[4 * b + e] = pack_fp8x4(sacc[b][4 * e], sacc[b][4 * e + 1], sacc[b][4 * e + 2], sacc[b][4 * e + 3]);
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const int ch = 32 * db + (lane & 31);
-          const char* vr = st + C::OFF_VT + ch * C::VT_STR;
-          const i32x4 lo = *(const i32x4*)(vr + 16 * half);
-          const i32x4 hi = *(const i32x4*)(vr + 32 + 16 * half);
-          const i32x8 a = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-          const int sa = (*(const uint16_t*)(st + C::OFF_VTSC + ch * 2) >> (8 * half)) & 0xFF;
-          oacc[db] = mfma32_mx(a, sa, pb, 127 - 8, oacc[db]);
+          const int ch = 32 * db + r32;
+          const char* vr = tb + C::OFF_V + ch * 64;
+          const i32x4 lo = *(const i32x4*)(vr + vo[0]);
+          const i32x4 hi = *(const i32x4*)(vr + vo[1]);
+          const int sa = *(const uint8_t*)(tb + C::OFF_VTSC + half * 128 + ch);
+          oacc[db] = mfma32_mx(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, sa, pb, 127 - 8, oacc[db]);
         }
       }
     }
-    if (kt + 1 < n_kt) store_tile((kt + 1) & 1, kt + 1);
+    wait_vmem();
     __syncthreads();
+  };
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    iter(kt, lds_a, lds_b);
+    if (kt + 1 < n_kt) iter(kt + 1, lds_b, lds_a);
   }
 
   const float l_tot = wave_sum_xor32(l_run);
@@ -311,16 +277,10 @@ hipError_t launch_fwd_mx(const uint8_t* qd, const uint8_t* qd_sc, const uint8_t*
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
   const float sl2 = scale * LOG2E;
-  const int lds = 2 * MxFwdTile::STAGE;
 #define CFA_MXF_LAUNCH(HH)                                                                                    \
-  do {                                                                                                        \
-    auto kern = attn_fwd_mx_kernel<HH>;                                                                       \
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds))              \
-      return hipErrorInvalidConfiguration;                                                                    \
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, stream, qd, qd_sc, kd, kd_sc, vt, vt_sc,   \
-                       (const __bf16*)v, (__bf16*)o, lse, plan, padoff, total_tokens, t_pad, hq, hkv, n_hb, sl2, \
-                       causal);                                                                               \
-  } while (0)
+  hipLaunchKernelGGL(attn_fwd_mx_kernel<HH>, dim3((unsigned)grid), dim3(256), 0, stream, qd, qd_sc, kd, kd_sc, vt, \
+                     vt_sc, (const __bf16*)v, (__bf16*)o, lse, plan, padoff, total_tokens, t_pad, hq, hkv, n_hb, sl2, \
+                     causal)
   if (hpw == 4) CFA_MXF_LAUNCH(4);
   else if (hpw == 2) CFA_MXF_LAUNCH(2);
   else CFA_MXF_LAUNCH(1);

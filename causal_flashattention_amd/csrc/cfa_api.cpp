@@ -232,7 +232,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, c
                                                     (uint8_t*)sv + sl.kd.scales, st), "quantize K"))
       return r;
     if (int r = check_hip(cfa::launch_mx_quantize_t(v, total_tokens, hkv, d, ws, n_docs, (uint8_t*)ws + wl.vt.codes,
-                                                    (uint8_t*)ws + wl.vt.scales, tp, st), "quantize V"))
+                                                    (uint8_t*)ws + wl.vt.scales, tp, true, st), "quantize V"))
       return r;
     mark(1, 1, st);
     mark(0, 0, st);
@@ -292,10 +292,10 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
     auto U = [&](const MxBuf& b, bool codes) { return (uint8_t*)ws + (codes ? b.codes : b.scales); };
     mark(3, 0, st);
     hipError_t e = cfa::launch_mx_quantize_d(dout, (long)total_tokens * hq * d, U(wl.dod, true), U(wl.dod, false), st);
-    if (!e) e = cfa::launch_mx_quantize_t(dout, total_tokens, hq, d, ws, n_docs, U(wl.dot, true), U(wl.dot, false), tp, st);
+    if (!e) e = cfa::launch_mx_quantize_t(dout, total_tokens, hq, d, ws, n_docs, U(wl.dot, true), U(wl.dot, false), tp, false, st);
     if (!e) e = cfa::launch_mx_quantize_d(v, (long)total_tokens * hkv * d, U(wl.vd, true), U(wl.vd, false), st);
-    if (!e) e = cfa::launch_mx_quantize_t(q, total_tokens, hq, d, ws, n_docs, U(wl.qt, true), U(wl.qt, false), tp, st);
-    if (!e) e = cfa::launch_mx_quantize_t(k, total_tokens, hkv, d, ws, n_docs, U(wl.kt, true), U(wl.kt, false), tp, st);
+    if (!e) e = cfa::launch_mx_quantize_t(q, total_tokens, hq, d, ws, n_docs, U(wl.qt, true), U(wl.qt, false), tp, false, st);
+    if (!e) e = cfa::launch_mx_quantize_t(k, total_tokens, hkv, d, ws, n_docs, U(wl.kt, true), U(wl.kt, false), tp, false, st);
     mark(3, 1, st);
     if (int r = check_hip(e, "backward quantisation")) return r;
     cfa::MxOperands m;
@@ -366,7 +366,7 @@ int mx_quantize(const void* x, int total_tokens, int h, int d, const int32_t* cu
   if (int r = check_cu_host(cu_seqlens_host, n_docs, total_tokens, 0)) return r;
   if (int r = check_hip(cfa::launch_plan(cu_seqlens, n_docs, total_tokens, workspace, st), "plan kernel")) return r;
   if (total_tokens == 0) return CFA_OK;
-  return check_hip(cfa::launch_mx_quantize_t(x, total_tokens, h, d, workspace, n_docs, codes, scales, t_pad, st),
+  return check_hip(cfa::launch_mx_quantize_t(x, total_tokens, h, d, workspace, n_docs, codes, scales, t_pad, false, st),
                    "mx_quantize_t");
 }
 

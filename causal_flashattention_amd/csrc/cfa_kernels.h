@@ -35,8 +35,11 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
 
 hipError_t launch_mx_quantize_d(const void* x, long n_elems, uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
+// kernel_layout: the attention kernels' internal token-blocked layout (pieces of 4 tokens in
+// the order 0,2,4,6,1,3,5,7 within each 32-token block; scales [h, t_pad/32, d]); otherwise the
+// public layout of mx_quantize.
 hipError_t launch_mx_quantize_t(const void* x, int total_tokens, int h, int d, const void* ws, int n_docs,
-                                uint8_t* codes, uint8_t* scales, int t_pad, hipStream_t stream);
+                                uint8_t* codes, uint8_t* scales, int t_pad, bool kernel_layout, hipStream_t stream);
 
 hipError_t launch_fwd_mx(const uint8_t* qd, const uint8_t* qd_sc, const uint8_t* kd, const uint8_t* kd_sc,
                          const uint8_t* vt, const uint8_t* vt_sc, const void* v, void* o, float* lse,

@@ -11,9 +11,9 @@
 // element):
 //  * along d: 4 lanes per 32-channel block, 16 bytes per lane, amax by two lane swaps;
 //  * along doc-local tokens: a workgroup per (32-token block, head) reads the 32 × d tile with
-//    lanes along channels (coalesced rows), each lane reduces 16 tokens of one channel, the
-//    two halves meet in LDS, and each lane writes 16 contiguous code bytes of its channel row
-//    in the transposed [h, d, t_pad] layout.
+//    16-byte loads into LDS, each lane reduces 16 tokens of one channel, the two lanes of a
+//    channel meet in LDS, and each lane writes 16 code bytes of its channel row in the
+//    transposed [h, d, t_pad] layout.
 #include "cfa_device.h"
 
 namespace cfa {
@@ -70,13 +70,24 @@ __global__ __launch_bounds__(256) void mx_quantize_d_kernel(const __bf16* __rest
   if (sub == 0) scales[blk] = badi ? 0xFF : (uint8_t)(e + 127);
 }
 
-// grid: (padded 32-token blocks upper bound) × h; block 256 threads; D = head dim (<= 256)
-template <int D>
+// grid: (padded 32-token blocks upper bound) × h; block 256 threads; D = head dim (64 or 128).
+// The 32 × D tile is read with 16-byte loads along channels into LDS, then each lane of the
+// first 2·D threads reduces 16 tokens of one channel; the two lanes of a channel meet in LDS.
+// KL selects the layout:
+//  * KL = false (public): codes [h, d, t_pad] in token order, scales [h, d, t_pad/32];
+//  * KL = true (attention kernels' internal copies): within each 32-token block the 4-byte
+//    pieces (4 tokens each) are stored in the order 0,2,4,6,1,3,5,7 -- the order in which a
+//    matrix-core lane group holds probabilities (tokens 8m + 4g + 0..3 for lane group g) --
+//    and scales are block-major [h, t_pad/32, d], so a block's 128 scale bytes are contiguous.
+//    Lane group g (g = 0, 1) then handles exactly the tokens stored in bytes 16g..16g+15.
+template <int D, bool KL>
 __global__ __launch_bounds__(256) void mx_quantize_t_kernel(const __bf16* __restrict__ x, uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales, const int2* __restrict__ docinfo,
                                                             const int* __restrict__ padoff, int n_docs, int h,
                                                             int t_pad) {
-  static_assert(D <= 128, "one channel per lane pair");
+  static_assert(D == 64 || D == 128, "head dim");
+  constexpr int RSTR = D + 8;                      // bf16 elements per LDS row (16-byte pad)
+  __shared__ __attribute__((aligned(16))) __bf16 tile[32 * RSTR];
   __shared__ float s_amax[2][D];
   __shared__ int s_bad[2][D];
   const int pb = blockIdx.x;           // padded block index (column pb*32)
@@ -92,17 +103,28 @@ __global__ __launch_bounds__(256) void mx_quantize_t_kernel(const __bf16* __rest
   const int2 di = docinfo[lo];
   const int b0 = pb * 32 - padoff[lo];            // doc-local first token of this block
   const int ntok = min(32, di.y - b0);            // real tokens in the block
+  constexpr int CPR = D / 8;                      // 16-byte chunks per token row
+#pragma unroll
+  for (int i = 0; i < (32 * CPR + 255) / 256; ++i) {
+    const int cidx = threadIdx.x + 256 * i;
+    if (cidx < 32 * CPR) {
+      const int row = cidx / CPR, col = cidx % CPR;
+      i32x4 u = i32x4{0, 0, 0, 0};
+      if (row < ntok) u = *(const i32x4*)(x + ((size_t)(di.x + b0 + row) * h + hh) * D + col * 8);
+      *(i32x4*)(tile + row * RSTR + col * 8) = u;
+    }
+  }
+  __syncthreads();
   const int c = threadIdx.x % D;                  // channel
-  const int half = threadIdx.x / D;               // 0 / 1: tokens [0,16) / [16,32)
+  const int half = threadIdx.x / D;               // lane group: 16 of the 32 tokens
   const bool active = threadIdx.x < 2 * D;
+  auto token = [&](int i) { return KL ? 8 * (i >> 2) + 4 * half + (i & 3) : 16 * half + i; };
   float v[16];
   float amax = 0.f;
   int bad = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int tok = 16 * half + i;
-    float val = 0.f;
-    if (active && tok < ntok) val = (float)x[((size_t)(di.x + b0 + tok) * h + hh) * D + c];
+    const float val = active ? (float)tile[token(i) * RSTR + c] : 0.f;
     v[i] = val;
     bad |= !__builtin_isfinite(val);
     amax = fmaxf(amax, fabsf(val));
@@ -123,10 +145,14 @@ __global__ __launch_bounds__(256) void mx_quantize_t_kernel(const __bf16* __rest
   // padding tokens of a partial last block encode 0x00 (not -0 or NaN)
 #pragma unroll
   for (int i = 0; i < 16; ++i)
-    if (16 * half + i >= ntok) out[i / 4] &= ~(0xFF << (8 * (i % 4)));
+    if (token(i) >= ntok) out[i / 4] &= ~(0xFF << (8 * (i % 4)));
   const size_t row = (size_t)hh * D + c;
   *(i32x4*)(codes + row * t_pad + pb * 32 + 16 * half) = out;
-  if (half == 0) scales[row * (t_pad / 32) + pb] = bad ? 0xFF : (uint8_t)(e + 127);
+  const uint8_t sb = bad ? 0xFF : (uint8_t)(e + 127);
+  if (half == 0) {
+    if (KL) scales[((size_t)hh * (t_pad / 32) + pb) * D + c] = sb;
+    else scales[row * (t_pad / 32) + pb] = sb;
+  }
 }
 
 hipError_t launch_mx_quantize_d(const void* x, long n_elems, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
@@ -140,21 +166,23 @@ hipError_t launch_mx_quantize_d(const void* x, long n_elems, uint8_t* codes, uin
 }
 
 hipError_t launch_mx_quantize_t(const void* x, int total_tokens, int h, int d, const void* ws, int n_docs,
-                                uint8_t* codes, uint8_t* scales, int t_pad, hipStream_t stream) {
+                                uint8_t* codes, uint8_t* scales, int t_pad, bool kernel_layout, hipStream_t stream) {
   const PlanLayout lay(n_docs);
   const char* b = (const char*)ws;
   const int2* docinfo = (const int2*)(b + lay.docinfo);
   const int* padoff = (const int*)(b + lay.padoff);
   const long nb = (long)(total_tokens + 31) / 32 + n_docs;   // bound on padded blocks
   if (nb == 0 || h == 0) return hipSuccess;
-  if (d == 128)
-    hipLaunchKernelGGL(mx_quantize_t_kernel<128>, dim3((unsigned)nb, (unsigned)h), dim3(256), 0, stream,
-                       (const __bf16*)x, codes, scales, docinfo, padoff, n_docs, h, t_pad);
-  else if (d == 64)
-    hipLaunchKernelGGL(mx_quantize_t_kernel<64>, dim3((unsigned)nb, (unsigned)h), dim3(256), 0, stream,
-                       (const __bf16*)x, codes, scales, docinfo, padoff, n_docs, h, t_pad);
-  else
-    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)nb, (unsigned)h);
+#define CFA_MXQT(DD, KK)                                                                                     \
+  hipLaunchKernelGGL((mx_quantize_t_kernel<DD, KK>), grid, dim3(256), 0, stream, (const __bf16*)x, codes, scales, \
+                     docinfo, padoff, n_docs, h, t_pad)
+  if (d == 128 && kernel_layout) CFA_MXQT(128, true);
+  else if (d == 128) CFA_MXQT(128, false);
+  else if (d == 64 && kernel_layout) CFA_MXQT(64, true);
+  else if (d == 64) CFA_MXQT(64, false);
+  else return hipErrorInvalidValue;
+#undef CFA_MXQT
   return hipGetLastError();
 }
 
