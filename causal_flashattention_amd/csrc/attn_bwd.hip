@@ -121,10 +121,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     char* ob = qb + TILE;
     char* lb = ob + TILE;
     if constexpr (D == 128) {
-      auto qrow = [&](int r) { return (const char*)(q + ((size_t)(s0 + min(q0 + r, L - 1)) * hq + h) * D); };
-      auto orow = [&](int r) { return (const char*)(dout + ((size_t)(s0 + min(q0 + r, L - 1)) * hq + h) * D); };
-      stage_rows_lds<BM>(qb, qrow, w, lane);
-      stage_rows_lds<BM>(ob, orow, w, lane);
+      const size_t row0 = ((size_t)(s0 + q0) * hq + h) * D;
+      const uint32_t stride = (uint32_t)hq * D * 2;
+      stage_rows_lds<BM>(qb, (const char*)(q + row0), stride, L - 1 - q0, w, lane);
+      stage_rows_lds<BM>(ob, (const char*)(dout + row0), stride, L - 1 - q0, w, lane);
       if (threadIdx.x < BM) {   // LSE and D through registers, written to LDS by stage_finish
         const size_t li = (size_t)h * total_tokens + s0 + min(q0 + (int)threadIdx.x, L - 1);
         lreg = lse[li];
@@ -348,8 +348,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(
     const int h = g * G + st / n_qt;
     const int q0 = q_begin + (st % n_qt) * BM;
     const __bf16* src = ds_wave ? dout : q;
-    auto row = [&](int r) { return (const char*)(src + ((size_t)(s0 + min(q0 + r, L - 1)) * hq + h) * D); };
-    stage_rows_lds<BM>(buf + (ds_wave ? TILE : 0), row, pair, lane);
+    stage_rows_lds<BM>(buf + (ds_wave ? TILE : 0), (const char*)(src + ((size_t)(s0 + q0) * hq + h) * D),
+                       (uint32_t)hq * D * 2, L - 1 - q0, pair, lane);
     if (threadIdx.x < BM) {
       const size_t li = (size_t)h * total_tokens + s0 + min(q0 + (int)threadIdx.x, L - 1);
       lreg = lse[li];
@@ -556,10 +556,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const int k0 = kt * BN;
     char* vb = kb + TILE;
     if constexpr (D == 128) {
-      auto krow = [&](int r) { return (const char*)(k + ((size_t)(s0 + min(k0 + r, kv_end - 1)) * hkv + g) * D); };
-      auto vrow = [&](int r) { return (const char*)(v + ((size_t)(s0 + min(k0 + r, kv_end - 1)) * hkv + g) * D); };
-      stage_rows_lds<BN>(kb, krow, w, lane);
-      stage_rows_lds<BN>(vb, vrow, w, lane);
+      const size_t row0 = ((size_t)(s0 + k0) * hkv + g) * D;
+      const uint32_t stride = (uint32_t)hkv * D * 2;
+      stage_rows_lds<BN>(kb, (const char*)(k + row0), stride, kv_end - 1 - k0, w, lane);
+      stage_rows_lds<BN>(vb, (const char*)(v + row0), stride, kv_end - 1 - k0, w, lane);
     } else {
       i32x4 kreg[PT], vreg[PT];
 #pragma unroll

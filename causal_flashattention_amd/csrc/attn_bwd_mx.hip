@@ -69,6 +69,30 @@ __device__ inline float amax16(const f32x16& x) {
   return m;
 }
 
+// One 32-element contraction block, this lane's 16 values: encode with exponent e into the
+// 4 words the lane contributes to a B operand (exponents from fit_exp: no clamp needed).
+__device__ inline i32x4 encode16(const f32x16& x, int e) {
+  i32x4 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    r[k] = pack_fp8x4(__builtin_amdgcn_ldexpf(x[4 * k], -e), __builtin_amdgcn_ldexpf(x[4 * k + 1], -e),
+                      __builtin_amdgcn_ldexpf(x[4 * k + 2], -e), __builtin_amdgcn_ldexpf(x[4 * k + 3], -e));
+  return r;
+}
+
+// x -= decode(c)·2^e in place (the rounding residual of encode16).
+__device__ inline void residual16(f32x16& x, const i32x4& c, int e) {
+  const float pe = __builtin_amdgcn_ldexpf(1.f, e);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f32x2 a01 = __builtin_amdgcn_cvt_pk_f32_fp8(c[k], false), a23 = __builtin_amdgcn_cvt_pk_f32_fp8(c[k], true);
+    x[4 * k + 0] = fmaf(-a01.x, pe, x[4 * k + 0]);
+    x[4 * k + 1] = fmaf(-a01.y, pe, x[4 * k + 1]);
+    x[4 * k + 2] = fmaf(-a23.x, pe, x[4 * k + 2]);
+    x[4 * k + 3] = fmaf(-a23.y, pe, x[4 * k + 3]);
+  }
+}
+
 // Block exponent for values quantised inside the kernel (P, dS): the smallest power of two
 // that maps amax to at most 448, so the largest element is never clipped (the operand rule
 // of mx_quantize may clip it by up to 1/8, which the oracle models for Q/K/V/dO but not here).
@@ -87,8 +111,11 @@ __device__ inline void block_exps(const f32x16& x0, const f32x16& x1, int& e0, i
   e1 = fit_exp(a1);
 }
 
-// Two E4M3 terms for one B operand: x ≈ hi·2^e_hi + lo·2^e_lo, each with MX block exponents.
-// One E4M3 rounding has a relative error up to 2^-4; the residual term brings it to ~2^-8.
+// Two E4M3 terms for one B operand: x ≈ hi·2^e + lo·2^(e−4), e the block exponent from
+// fit_exp. With every |x|·2^-e <= 448 the rounding residual of hi is at most 16·2^e (half the
+// E4M3 spacing 32 of [256, 448]), so residual·2^(4−e) <= 256 fits E4M3 without a second block
+// maximum. One E4M3 rounding has a relative error up to 2^-4; the residual term brings it to
+// ~2^-8.
 struct Fp8Pair {
   i32x8 hi, lo;
   int shi, slo;  // this lane's scale bytes (k-block = l/32)
@@ -101,12 +128,33 @@ __device__ inline Fp8Pair encode_two_term(const f32x16& x0, const f32x16& x1, in
   r.hi = encode_b_fp8(x0, x1, e0, e1);
   f32x16 r0, r1;
   residual_fp8(x0, x1, r.hi, e0, e1, r0, r1);
-  int f0, f1;
-  block_exps(r0, r1, f0, f1);
+  const int f0 = max(e0 - 4, -127), f1 = max(e1 - 4, -127);
   r.lo = encode_b_fp8(r0, r1, f0, f1);
   r.shi = (half ? e1 : e0) + 127;
   r.slo = (half ? f1 : f0) + 127;
   return r;
+}
+
+// Block-wise form of encode_two_term for block b (0 or 1) of a B operand: consumes x (its
+// storage becomes the residual), writes words 4b..4b+3 of hi and lo and, in the lane group
+// that supplies block b's scale (half == b), the two scale bytes.
+__device__ inline void encode_two_term_block(f32x16& x, int b, int half, Fp8Pair& r) {
+  float a = amax16(x);
+  a = fmaxf(a, __shfl_xor(a, 32));
+  const int e = fit_exp(a);
+  const i32x4 h4 = encode16(x, e);
+  residual16(x, h4, e);
+  const int f = max(e - 4, -127);
+  const i32x4 l4 = encode16(x, f);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    r.hi[4 * b + k] = h4[k];
+    r.lo[4 * b + k] = l4[k];
+  }
+  if (half == b) {
+    r.shi = e + 127;
+    r.slo = f + 127;
+  }
 }
 
 // Store a 16-byte chunk (16 consecutive tokens of one channel row) of a token-blocked tile into
@@ -394,40 +442,54 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mx_kernel(
 }
 
 // ------------------------------------------------------------------ dQ
-// LDS stage: [Kd codes][Kd sc][Vd codes][Vd sc][union: {Kt, Kt sc} | {Kb}]
-template <int DUMMY>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dq_mx_kernel(
+// A wave owns 32 queries of one head (Q_d, dO_d in registers as B operands); the workgroup
+// walks key tiles of 64, staged by direct global -> LDS copies into two static buffers:
+//   [K_d codes 64 × 128 B][K_d scales 64 × 4][V_d codes][V_d scales]
+//   [diagonal: K bf16 rows (SwzTile<128>) | otherwise: K_t codes 128 channel rows × 64 B, scales 2 × 128]
+// (code rows XOR-swizzled as in the MX forward kernel).
+struct MxDqTile {
+  static constexpr int BN = 64;
+  static constexpr int OFF_KDSC = BN * 128;
+  static constexpr int OFF_VD = OFF_KDSC + BN * 4;
+  static constexpr int OFF_VDSC = OFF_VD + BN * 128;
+  static constexpr int OFF_U = OFF_VDSC + BN * 4;
+  static constexpr int OFF_KTSC = OFF_U + 128 * 64;
+  static constexpr int STAGE = OFF_U + BN * 256;
+};
+
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
     const uint8_t* __restrict__ qd, const uint8_t* __restrict__ qd_sc, const uint8_t* __restrict__ kd,
     const uint8_t* __restrict__ kd_sc, const uint8_t* __restrict__ dod, const uint8_t* __restrict__ dod_sc,
     const uint8_t* __restrict__ vd, const uint8_t* __restrict__ vd_sc, const uint8_t* __restrict__ kt,
     const uint8_t* __restrict__ kt_sc, const __bf16* __restrict__ k, const float* __restrict__ lse,
     const float* __restrict__ delta, __bf16* __restrict__ dq, Plan plan, const int* __restrict__ padoff,
     int total_tokens, int t_pad, int hq, int hkv, float scale, int causal) {
-  using C = MxBwdTile;
-  constexpr int D = C::D, BN = C::BM;
-  constexpr int O_KDSC = C::DCODES;
-  constexpr int O_VD = O_KDSC + C::DSC;
-  constexpr int O_VDSC = O_VD + C::DCODES;
-  constexpr int O_U = O_VDSC + C::DSC;
-  constexpr int O_KT = O_U, O_KTSC = O_KT + C::TCODES;
-  constexpr int O_KB = O_U;
-  constexpr int U_BYTES = (C::BTILE > C::TCODES + C::TSC) ? C::BTILE : C::TCODES + C::TSC;
-  constexpr int STAGE = O_U + U_BYTES;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  using C = MxDqTile;
+  constexpr int D = 128, BN = C::BN;
+  __shared__ __attribute__((aligned(16))) char lds_a[C::STAGE];
+  __shared__ __attribute__((aligned(16))) char lds_b[C::STAGE];
 
   const int p = blockIdx.x / hq, h = blockIdx.x % hq;
   int s0, L, t, doc;
   if (!decode_item(plan, p, 128, true, s0, L, t, &doc)) return;
   const int pcol = padoff[doc];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5;
+  const int lp = 32 * ((L + 31) / 32);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5, r32 = lane & 31;
   const int g = h / (hq / hkv);
   const int wr0 = t * 128 + 32 * w;
-  const int qrow = wr0 + (lane & 31);
+  const int qrow = wr0 + r32;
   const int kv_end = causal ? min(L, (t + 1) * 128) : L;
   const int n_kt = (kv_end + BN - 1) / BN;
   const int wave_last_key = causal ? min(L, wr0 + 32) - 1 : L - 1;
   const float sl2 = scale * LOG2E;
   auto tile_is_diag = [&](int ktile) { return causal && ((ktile * BN) / 128 == t); };
+  int ko[2][2], to[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) ko[s][u] = 16 * ((4 * s + 2 * u + half) ^ kd_swz(r32));
+#pragma unroll
+  for (int u = 0; u < 2; ++u) to[u] = 16 * ((2 * u + half) ^ vt_swz(r32));
 
   i32x8 qa[2], oa[2];
   int qs[2], os[2];
@@ -451,145 +513,140 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_mx_kernel(
 #pragma unroll
   for (int b = 0; b < 4; ++b) dqa[b] = f32x16{};
 
-  i32x4 r_kd[2], r_vd[2], r_u[4];
-  int r_ks = 0, r_vs = 0, r_ts = 0;
-  auto load_tile = [&](int ktile) {
+  // key tile -> LDS; keys past kv_end are clamped into the document (K_d, V_d, bf16 K) or its
+  // last token block (K_t); they are masked (P = 0)
+  // Addresses: a wave-uniform 64-bit tile base plus a 32-bit lane offset within the tile.
+  const uint32_t krow_b = (uint32_t)hkv * D;      // bytes between consecutive tokens (codes, bf16/2)
+  auto stage = [&](int ktile, char* tb) {
     const int k0 = ktile * BN;
-    const int tid = threadIdx.x;
+    const int rmax = kv_end - 1 - k0;             // last row inside the document
+    const size_t tok0 = (size_t)(s0 + k0) * hkv + g;
+    const uint8_t* kdb = kd + tok0 * D;
+    const uint8_t* vdb = vd + tok0 * D;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, col = c & 7;
-      const bool ok = k0 + row < kv_end;
-      const size_t off = ((size_t)(s0 + k0 + row) * hkv + g) * D + col * 16;
-      r_kd[i] = ok ? *(const i32x4*)(kd + off) : i32x4{0, 0, 0, 0};
-      r_vd[i] = ok ? *(const i32x4*)(vd + off) : i32x4{0, 0, 0, 0};
+    for (int j = 0; j < 2; ++j) {               // K_d and V_d codes: 8 blocks of 8 rows each
+      const int I = 2 * w + j, r = 8 * I + (lane >> 3);
+      const uint32_t off = (uint32_t)min(r, rmax) * krow_b + 16 * ((lane & 7) ^ kd_swz(r));
+      g2lds16(kdb + off, tb + I * 1024);
+      g2lds16(vdb + off, tb + C::OFF_VD + I * 1024);
     }
-    if (tid < 64) {
-      const bool ok = k0 + tid < kv_end;
-      const size_t off = ((size_t)(s0 + k0 + tid) * hkv + g) * 4;
-      r_ks = ok ? *(const int*)(kd_sc + off) : 0x7f7f7f7f;
-      r_vs = ok ? *(const int*)(vd_sc + off) : 0x7f7f7f7f;
-    }
+    const uint32_t soff = (uint32_t)min(lane, rmax) * (uint32_t)hkv * 4;
+    if (w == 0) g2lds4(kd_sc + tok0 * 4 + soff, tb + C::OFF_KDSC);
+    if (w == 1) g2lds4(vd_sc + tok0 * 4 + soff, tb + C::OFF_VDSC);
     if (tile_is_diag(ktile)) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i, row = c >> 4, col = c & 15;
-        const bool ok = k0 + row < kv_end;
-        r_u[i] = ok ? *(const i32x4*)(k + ((size_t)(s0 + k0 + row) * hkv + g) * D + col * 8) : i32x4{0, 0, 0, 0};
-      }
+      stage_rows_lds<BN>(tb + C::OFF_U, (const char*)(k + tok0 * D), krow_b * 2, rmax, w, lane);
     } else {
+      const uint8_t* ktb = kt + (size_t)g * D * t_pad + pcol + k0;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int c = tid + 256 * i, ch = c >> 2, kc = c & 3;
-        const bool ok = k0 + 16 * kc < kv_end;
-        r_u[i] = ok ? *(const i32x4*)(kt + ((size_t)g * D + ch) * t_pad + pcol + k0 + 16 * kc) : i32x4{0, 0, 0, 0};
+      for (int j = 0; j < 2; ++j) {             // K_t codes: 8 blocks of 16 channel rows
+        const int I = 2 * w + j, r = 16 * I + (lane >> 2);
+        const int col = min(16 * ((lane & 3) ^ vt_swz(r)), lp - 16 - k0);
+        g2lds16(ktb + (uint32_t)(r * t_pad + col), tb + C::OFF_U + I * 1024);
       }
-      if (tid < D) {
-        const size_t srow = ((size_t)g * D + tid) * (t_pad / 32) + (pcol + k0) / 32;
-        r_ts = kt_sc[srow] | (((k0 + 32 < kv_end) ? kt_sc[srow + 1] : 127) << 8);
+      if (w == 2 && lane < 16) {
+        const int blk = min((k0 >> 5) + (lane >> 3), lp / 32 - 1);
+        g2lds16(kt_sc + ((size_t)g * (t_pad / 32) + (pcol >> 5) + blk) * D + 16 * (lane & 7), tb + C::OFF_KTSC);
       }
-    }
-  };
-  auto store_tile = [&](int buf, int ktile) {
-    char* sb = smem + buf * STAGE;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, col = c & 7;
-      *(i32x4*)(sb + row * C::DSTR + col * 16) = r_kd[i];
-      *(i32x4*)(sb + O_VD + row * C::DSTR + col * 16) = r_vd[i];
-    }
-    if (tid < 64) {
-      *(int*)(sb + O_KDSC + tid * 4) = r_ks;
-      *(int*)(sb + O_VDSC + tid * 4) = r_vs;
-    }
-    if (tile_is_diag(ktile)) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i, row = c >> 4, col = c & 15;
-        *(i32x4*)(sb + O_KB + row * C::BSTR + col * 16) = r_u[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int c = tid + 256 * i, ch = c >> 2, kc = c & 3;
-        store_tblocked(sb + O_KT + ch * C::TSTR, kc, r_u[i]);
-      }
-      if (tid < D) *(uint16_t*)(sb + O_KTSC + tid * 2) = (uint16_t)r_ts;
     }
   };
 
-  if (n_kt > 0) {
-    load_tile(0);
-    store_tile(0, 0);
-  }
-  __syncthreads();
-  for (int ktile = 0; ktile < n_kt; ++ktile) {
-    const int k0 = ktile * BN;
-    if (ktile + 1 < n_kt) load_tile(ktile + 1);
-    if (k0 <= wave_last_key) {
-      const char* sb = smem + (ktile & 1) * STAGE;
-      const bool need_mask = causal ? (k0 + BN - 1 > wr0) : (k0 + BN > L);
-      f32x16 dsv[2];
+  // dS of one 32-key block b of the tile (this lane: query qrow, keys k0 + 32b + 8(j/4) + 4·half + j%4)
+  auto ds_block = [&](const char* tb, int k0, int b, bool need_mask) __attribute__((always_inline)) {
+    const int kr = 32 * b + r32;
+    const int ksc = *(const int*)(tb + C::OFF_KDSC + kr * 4);
+    const int vsc = *(const int*)(tb + C::OFF_VDSC + kr * 4);
+    f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int kr = 32 * b + (lane & 31);
-        const int ksc = *(const int*)(sb + O_KDSC + kr * 4);
-        const int vsc = *(const int*)(sb + O_VDSC + kr * 4);
-        f32x16 sacc = f32x16{}, pacc = f32x16{};
+    for (int s = 0; s < 2; ++s) {
+      const char* kp = tb + kr * 128;
+      const char* vp = tb + C::OFF_VD + kr * 128;
+      const i32x4 klo = *(const i32x4*)(kp + ko[s][0]), khi = *(const i32x4*)(kp + ko[s][1]);
+      const i32x4 vlo = *(const i32x4*)(vp + ko[s][0]), vhi = *(const i32x4*)(vp + ko[s][1]);
+      sacc = mfma32_mx(i32x8{klo.x, klo.y, klo.z, klo.w, khi.x, khi.y, khi.z, khi.w},
+                       (ksc >> (8 * (2 * s + half))) & 0xFF, qa[s], qs[s], sacc);
+      pacc = mfma32_mx(i32x8{vlo.x, vlo.y, vlo.z, vlo.w, vhi.x, vhi.y, vhi.z, vhi.w},
+                       (vsc >> (8 * (2 * s + half))) & 0xFF, oa[s], os[s], pacc);
+    }
+    if (need_mask) {                     // wave-uniform: diagonal or document-end tiles
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          sacc = mfma32_mx(load_a_fp8(sb + kr * C::DSTR + 64 * s, half), (ksc >> (8 * (2 * s + half))) & 0xFF, qa[s],
-                           qs[s], sacc);
-          pacc = mfma32_mx(load_a_fp8(sb + O_VD + kr * C::DSTR + 64 * s, half), (vsc >> (8 * (2 * s + half))) & 0xFF,
-                           oa[s], os[s], pacc);
-        }
-        if (need_mask) {                 // wave-uniform: diagonal or document-end tiles
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = k0 + 32 * b + 8 * (j >> 2) + 4 * half + (j & 3);
-            if (causal ? (key > qrow) : (key >= L)) sacc[j] = -INFINITY;
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) dsv[b][j] = exp2_fast(fmaf(sacc[j], sl2, -lse2)) * (pacc[j] - dl);
-      }
-      if (tile_is_diag(ktile)) {
-        bf16x8 sf[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          i32x4 us;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            us[e] = (int)pack_bf16x2(dsv[kk >> 1][8 * (kk & 1) + 2 * e], dsv[kk >> 1][8 * (kk & 1) + 2 * e + 1]);
-          sf[kk] = __builtin_bit_cast(bf16x8, us);
-        }
-        const char* kbt = sb + O_KB;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int kbase = 32 * (kk >> 1) + 16 * (kk & 1);
-          const int key = kbase + 4 * half + ((lane & 15) >> 2);
-          const int dsub = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-          for (int dbk = 0; dbk < 4; ++dbk) {
-            const char* p0 = kbt + key * C::BSTR + (32 * dbk + dsub) * 2;
-            dqa[dbk] = mfma32(concat_tr(lds_read_tr16(p0), lds_read_tr16(p0 + 8 * C::BSTR)), sf[kk], dqa[dbk]);
-          }
-        }
-      } else {
-        const Fp8Pair ds2 = encode_two_term(dsv[0], dsv[1], half);
-#pragma unroll
-        for (int dbk = 0; dbk < 4; ++dbk) {
-          const int ch = 32 * dbk + (lane & 31);
-          const int ksa = (*(const uint16_t*)(sb + O_KTSC + ch * 2) >> (8 * half)) & 0xFF;
-          const i32x8 ak = load_a_fp8(sb + O_KT + ch * C::TSTR, half);
-          dqa[dbk] = mfma32_mx(ak, ksa, ds2.hi, ds2.shi, dqa[dbk]);
-          dqa[dbk] = mfma32_mx(ak, ksa, ds2.lo, ds2.slo, dqa[dbk]);
-        }
+      for (int j = 0; j < 16; ++j) {
+        const int key = k0 + 32 * b + 8 * (j >> 2) + 4 * half + (j & 3);
+        if (causal ? (key > qrow) : (key >= L)) sacc[j] = -INFINITY;
       }
     }
-    if (ktile + 1 < n_kt) store_tile((ktile + 1) & 1, ktile + 1);
+    f32x16 x;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = exp2_fast(fmaf(sacc[j], sl2, -lse2)) * (pacc[j] - dl);
+    return x;
+  };
+
+  // diagonal tile: bf16 dS and bf16 K (transposing reads)
+  auto tile_diag = [&](const char* tb, int k0, bool need_mask) __attribute__((always_inline)) {
+    bf16x8 sf[4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const f32x16 x = ds_block(tb, k0, b, need_mask);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        i32x4 us;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) us[e] = (int)pack_bf16x2(x[8 * u + 2 * e], x[8 * u + 2 * e + 1]);
+        sf[2 * b + u] = __builtin_bit_cast(bf16x8, us);
+      }
+    }
+    const SwzOffsets<D> so(lane);
+    const char* kb = tb + C::OFF_U;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int rb = (32 * (kk >> 1) + 16 * (kk & 1)) * 256;
+      bf16x8 ak[4];
+#pragma unroll
+      for (int dbk = 0; dbk < 4; ++dbk)
+        ak[dbk] = concat_tr(lds_read_tr16(kb + rb + so.tr0[dbk]), lds_read_tr16(kb + rb + so.tr1[dbk]));
+#pragma unroll
+      for (int dbk = 0; dbk < 4; ++dbk) dqa[dbk] = mfma32(ak[dbk], sf[kk], dqa[dbk]);
+    }
+  };
+
+  // other tiles: two-term E4M3 dS and token-blocked K_t
+  auto tile_off = [&](const char* tb, int k0, bool need_mask) __attribute__((always_inline)) {
+    Fp8Pair ds2;
+    ds2.shi = ds2.slo = 127;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      f32x16 x = ds_block(tb, k0, b, need_mask);
+      encode_two_term_block(x, b, half, ds2);
+    }
+#pragma unroll
+    for (int dbk = 0; dbk < 4; ++dbk) {
+      const int ch = 32 * dbk + r32;
+      const char* kr = tb + C::OFF_U + ch * 64;
+      const i32x4 lo = *(const i32x4*)(kr + to[0]), hi = *(const i32x4*)(kr + to[1]);
+      const i32x8 ak = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      const int ksa = *(const uint8_t*)(tb + C::OFF_KTSC + half * 128 + ch);
+      dqa[dbk] = mfma32_mx(ak, ksa, ds2.hi, ds2.shi, dqa[dbk]);
+      dqa[dbk] = mfma32_mx(ak, ksa, ds2.lo, ds2.slo, dqa[dbk]);
+    }
+  };
+
+  auto iter = [&](int ktile, const char* tb, char* nxt) __attribute__((always_inline)) {
+    const int k0 = ktile * BN;
+    if (ktile + 1 < n_kt) stage(ktile + 1, nxt);
+    if (k0 <= wave_last_key) {
+      const bool need_mask = causal ? (k0 + BN - 1 > wr0) : (k0 + BN > L);
+      if (tile_is_diag(ktile)) tile_diag(tb, k0, need_mask);
+      else tile_off(tb, k0, need_mask);
+    }
+    wait_vmem();
     __syncthreads();
+  };
+
+  if (n_kt > 0) stage(0, lds_a);
+  wait_vmem();
+  __syncthreads();
+  for (int ktile = 0; ktile < n_kt; ktile += 2) {
+    iter(ktile, lds_a, lds_b);
+    if (ktile + 1 < n_kt) iter(ktile + 1, lds_b, lds_a);
   }
 
   if (qrow < L) {
@@ -611,11 +668,6 @@ static int dkdv_mx_stage() {
   using C = MxBwdTile;
   constexpr int U = (2 * C::BTILE > 2 * (C::TCODES + C::TSC)) ? 2 * C::BTILE : 2 * (C::TCODES + C::TSC);
   return 2 * (C::DCODES + C::DSC) + U + 2 * C::BM * 4;
-}
-static int dq_mx_stage() {
-  using C = MxBwdTile;
-  constexpr int U = (C::BTILE > C::TCODES + C::TSC) ? C::BTILE : C::TCODES + C::TSC;
-  return 2 * (C::DCODES + C::DSC) + U;
 }
 
 hipError_t launch_bwd_dkdv_mx(const MxOperands& m, const void* q, const void* dout, const float* lse,
@@ -645,13 +697,9 @@ hipError_t launch_bwd_dq_mx(const MxOperands& m, const void* k, const float* lse
   const long grid = ((long)(T + 127) / 128 + plan.n_docs) * hq;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  const int lds = 2 * dq_mx_stage();
-  auto kern = attn_bwd_dq_mx_kernel<0>;
-  if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds))
-    return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, stream, m.qd, m.qd_sc, m.kd, m.kd_sc, m.dod, m.dod_sc,
-                     m.vd, m.vd_sc, m.kt, m.kt_sc, (const __bf16*)k, lse, delta, (__bf16*)dq, plan, padoff, T, t_pad,
-                     hq, hkv, scale, causal);
+  hipLaunchKernelGGL(attn_bwd_dq_mx_kernel, dim3((unsigned)grid), dim3(256), 0, stream, m.qd, m.qd_sc, m.kd, m.kd_sc,
+                     m.dod, m.dod_sc, m.vd, m.vd_sc, m.kt, m.kt_sc, (const __bf16*)k, lse, delta, (__bf16*)dq, plan,
+                     padoff, T, t_pad, hq, hkv, scale, causal);
   return hipGetLastError();
 }
 

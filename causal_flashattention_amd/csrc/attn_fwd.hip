@@ -94,10 +94,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     const int k0 = kt * C::BN;
     char* vb = kb + C::KBYTES;
     if constexpr (D == 128) {
-      auto krow = [&](int r) { return (const char*)(k + ((size_t)(s0 + min(k0 + r, kv_end - 1)) * hkv + g) * D); };
-      auto vrow = [&](int r) { return (const char*)(v + ((size_t)(s0 + min(k0 + r, kv_end - 1)) * hkv + g) * D); };
-      stage_rows_lds<C::BN>(kb, krow, w, lane);
-      stage_rows_lds<C::BN>(vb, vrow, w, lane);
+      const size_t row0 = ((size_t)(s0 + k0) * hkv + g) * D;
+      const uint32_t stride = (uint32_t)hkv * D * 2;
+      stage_rows_lds<C::BN>(kb, (const char*)(k + row0), stride, kv_end - 1 - k0, w, lane);
+      stage_rows_lds<C::BN>(vb, (const char*)(v + row0), stride, kv_end - 1 - k0, w, lane);
     } else {
       i32x4 kreg[C::PER_THREAD], vreg[C::PER_THREAD];
 #pragma unroll

@@ -41,13 +41,6 @@ struct MxFwdTile {
   static constexpr int STAGE = OFF_V + BN * 256;     // union with the bf16 V rows (64 × 256 B)
 };
 
-__device__ inline int kd_swz(int r) { return (r >> 1) & 7; }
-__device__ inline int vt_swz(int r) { return (r >> 2) & 3; }
-
-__device__ inline void g2lds4(const void* gsrc, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 4, 0, 0);
-}
-
 template <int HPW>
 __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
     const uint8_t* __restrict__ qd, const uint8_t* __restrict__ qd_sc, const uint8_t* __restrict__ kd,
@@ -109,25 +102,28 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
   auto tile_is_diag = [&](int kt) { return (kt * C::BN) / 128 == diag_blk; };
   // Tile kt -> LDS with direct copies. Keys past kv_end are clamped into the document (K_d,
   // bf16 V) or into its last token block (V_t); they are masked (P = 0).
+  // Addresses: a wave-uniform 64-bit tile base plus a 32-bit lane offset within the tile.
+  const uint32_t tok_b = (uint32_t)hkv * D;     // bytes between consecutive tokens of K_d
   auto stage = [&](int kt, char* tb) {
     const int k0 = kt * C::BN;
+    const int rmax = kv_end - 1 - k0;
+    const size_t tok0 = (size_t)(s0 + k0) * hkv + g;
+    const uint8_t* kdb = kd + tok0 * D;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {               // K_d codes: 8 blocks of 8 rows, 2 per wave
       const int I = 2 * w + j, r = 8 * I + (lane >> 3);
-      const int c = (lane & 7) ^ kd_swz(r);
-      g2lds16(kd + ((size_t)(s0 + min(k0 + r, kv_end - 1)) * hkv + g) * D + 16 * c, tb + I * 1024);
+      g2lds16(kdb + ((uint32_t)min(r, rmax) * tok_b + 16 * ((lane & 7) ^ kd_swz(r))), tb + I * 1024);
     }
-    if (w == 0) g2lds4(kd_sc + ((size_t)(s0 + min(k0 + lane, kv_end - 1)) * hkv + g) * 4, tb + C::OFF_KSC);
+    if (w == 0) g2lds4(kd_sc + tok0 * 4 + (uint32_t)min(lane, rmax) * (uint32_t)hkv * 4, tb + C::OFF_KSC);
     if (tile_is_diag(kt)) {
-      auto vrow = [&](int r) { return (const char*)(v + ((size_t)(s0 + min(k0 + r, kv_end - 1)) * hkv + g) * D); };
-      stage_rows_lds<C::BN>(tb + C::OFF_V, vrow, w, lane);
+      stage_rows_lds<C::BN>(tb + C::OFF_V, (const char*)(v + tok0 * D), tok_b * 2, rmax, w, lane);
     } else {
+      const uint8_t* vtb = vt + (size_t)g * D * t_pad + pcol + k0;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {             // V_t codes: 8 blocks of 16 channel rows, 2 per wave
         const int I = 2 * w + j, r = 16 * I + (lane >> 2);
-        const int c = (lane & 3) ^ vt_swz(r);
-        const int col = min(k0 + 16 * c, lp - 16);
-        g2lds16(vt + ((size_t)g * D + r) * t_pad + pcol + col, tb + C::OFF_V + I * 1024);
+        const int col = min(16 * ((lane & 3) ^ vt_swz(r)), lp - 16 - k0);
+        g2lds16(vtb + (uint32_t)(r * t_pad + col), tb + C::OFF_V + I * 1024);
       }
       if (w == 1 && lane < 16) {                // V_t scales of the two key blocks
         const int blk = min((k0 >> 5) + (lane >> 3), lp / 32 - 1);

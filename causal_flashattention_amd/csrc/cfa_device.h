@@ -161,23 +161,36 @@ struct SwzOffsets {
 __device__ inline void g2lds16(const void* gsrc, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
+// Direct global -> LDS copy of 4 bytes per lane: LDS[lds_wave_base + 4·lane].
+__device__ inline void g2lds4(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 4, 0, 0);
+}
+
+// XOR swizzles of the 16-byte chunks of E4M3 code tiles in LDS, chosen so that the 16 rows
+// read by a 16-lane group at one logical chunk land in 16 distinct 16-byte bank groups:
+// d-blocked rows of 128 bytes (8 chunks): rows r and r+1 share a 256-byte bank window, so the
+// chunk moves with r/2; token-blocked rows of 64 bytes (4 chunks): 4 rows share a window.
+__device__ inline int kd_swz(int r) { return (r >> 1) & 7; }
+__device__ inline int vt_swz(int r) { return (r >> 2) & 3; }
+
 __device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Stage ROWS rows of 128 bf16 (256 bytes) into a SwzTile<128> LDS tile with direct loads.
-// Called by all 4 waves; wave w copies the 1 KB blocks [w·ROWS/16, (w+1)·ROWS/16), block I
+// Called by 4 waves; wave w copies the 1 KB blocks [w·ROWS/16, (w+1)·ROWS/16), block I
 // holding rows 4I..4I+3. Lane i fills physical chunk i%16 of row 4I + i/16, i.e. logical chunk
-// (i%16) ^ f(row): the swizzle is applied on the global side. rowptr(r) returns the global
-// address (bytes) of tile row r.
-template <int ROWS, typename RowPtr>
-__device__ inline void stage_rows_lds(char* tile, RowPtr rowptr, int wave, int lane) {
+// (i%16) ^ f(row): the swizzle is applied on the global side. Tile row r is read from
+// base + min(r, rmax)·stride: `base` is wave-uniform (the tile's first row), so each copy is a
+// scalar base plus a 32-bit lane offset; rows past rmax repeat row rmax.
+template <int ROWS>
+__device__ inline void stage_rows_lds(char* tile, const char* base, uint32_t stride, int rmax, int wave, int lane) {
   static_assert(ROWS % 16 == 0, "4 waves × 4 rows per block");
   constexpr int PER_WAVE = ROWS / 16;
 #pragma unroll
   for (int j = 0; j < PER_WAVE; ++j) {
     const int I = wave * PER_WAVE + j;
     const int r = 4 * I + (lane >> 4);
-    const int c = (lane & 15) ^ SwzTile<128>::f(r);
-    g2lds16(rowptr(r) + c * 16, tile + I * 1024);
+    const uint32_t c = (uint32_t)((lane & 15) ^ SwzTile<128>::f(r));
+    g2lds16(base + ((uint32_t)min(r, rmax) * stride + c * 16), tile + I * 1024);
   }
 }
 
