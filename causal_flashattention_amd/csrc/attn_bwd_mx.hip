@@ -27,39 +27,35 @@ __device__ inline int mx_exp_of(float amax) {
   return min(max(ex - 1 - 8, -127), 127);
 }
 
-// Encode 2 × 16 values (two 32-element contraction blocks, 16 per lane each) as the B operand:
-// bytes 0-15 block 0 with exponent e0, bytes 16-31 block 1 with exponent e1. The exponents come
-// from fit_exp, so every scaled value lies within ±448 and needs no clamp.
-__device__ inline i32x8 encode_b_fp8(const f32x16& x0, const f32x16& x1, int e0, int e1) {
-  i32x8 r;
+// One 32-element contraction block, this lane's 16 values: encode x·2^-e into the 4 words the
+// lane contributes to a B operand (exponents from fit_exp keep |x|·2^-e <= 448).
+__device__ inline i32x4 encode16(const f32x16& x, int e) {
+  const float s = pow2i(e);
+  i32x4 r;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    r[e] = pack_fp8x4(__builtin_amdgcn_ldexpf(x0[4 * e], -e0), __builtin_amdgcn_ldexpf(x0[4 * e + 1], -e0),
-                      __builtin_amdgcn_ldexpf(x0[4 * e + 2], -e0), __builtin_amdgcn_ldexpf(x0[4 * e + 3], -e0));
-    r[4 + e] = pack_fp8x4(__builtin_amdgcn_ldexpf(x1[4 * e], -e1), __builtin_amdgcn_ldexpf(x1[4 * e + 1], -e1),
-                          __builtin_amdgcn_ldexpf(x1[4 * e + 2], -e1), __builtin_amdgcn_ldexpf(x1[4 * e + 3], -e1));
-  }
+  for (int k = 0; k < 4; ++k) r[k] = pack_fp8x4_scaled(x[4 * k], x[4 * k + 1], x[4 * k + 2], x[4 * k + 3], s);
   return r;
 }
 
-// Residual of a B-operand encoding: x - decode(codes)·2^e for both blocks (one fma each).
-__device__ inline void residual_fp8(const f32x16& x0, const f32x16& x1, const i32x8& c, int e0, int e1, f32x16& r0,
-                                    f32x16& r1) {
-  const float p0 = __builtin_amdgcn_ldexpf(1.f, e0), p1 = __builtin_amdgcn_ldexpf(1.f, e1);
+// x -= decode(c)·2^e in place (the rounding residual of encode16).
+__device__ inline void residual16(f32x16& x, const i32x4& c, int e) {
+  const float s = pow2i(e);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const f32x2 a01 = __builtin_amdgcn_cvt_pk_f32_fp8(c[e], false), a23 = __builtin_amdgcn_cvt_pk_f32_fp8(c[e], true);
-    const f32x2 b01 = __builtin_amdgcn_cvt_pk_f32_fp8(c[4 + e], false);
-    const f32x2 b23 = __builtin_amdgcn_cvt_pk_f32_fp8(c[4 + e], true);
-    r0[4 * e + 0] = fmaf(-a01.x, p0, x0[4 * e + 0]);
-    r0[4 * e + 1] = fmaf(-a01.y, p0, x0[4 * e + 1]);
-    r0[4 * e + 2] = fmaf(-a23.x, p0, x0[4 * e + 2]);
-    r0[4 * e + 3] = fmaf(-a23.y, p0, x0[4 * e + 3]);
-    r1[4 * e + 0] = fmaf(-b01.x, p1, x1[4 * e + 0]);
-    r1[4 * e + 1] = fmaf(-b01.y, p1, x1[4 * e + 1]);
-    r1[4 * e + 2] = fmaf(-b23.x, p1, x1[4 * e + 2]);
-    r1[4 * e + 3] = fmaf(-b23.y, p1, x1[4 * e + 3]);
+  for (int k = 0; k < 4; ++k) {
+    const f32x2 a01 = unpack_fp8x2_scaled<false>(c[k], s), a23 = unpack_fp8x2_scaled<true>(c[k], s);
+    x[4 * k + 0] -= a01.x;
+    x[4 * k + 1] -= a01.y;
+    x[4 * k + 2] -= a23.x;
+    x[4 * k + 3] -= a23.y;
   }
+}
+
+// Encode 2 × 16 values (two 32-element contraction blocks, 16 per lane each) as the B operand:
+// bytes 0-15 block 0 with exponent e0, bytes 16-31 block 1 with exponent e1 (exponents from
+// fit_exp, so every scaled value lies within ±448).
+__device__ inline i32x8 encode_b_fp8(const f32x16& x0, const f32x16& x1, int e0, int e1) {
+  const i32x4 a = encode16(x0, e0), b = encode16(x1, e1);
+  return i32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 }
 
 __device__ inline float amax16(const f32x16& x) {
@@ -67,30 +63,6 @@ __device__ inline float amax16(const f32x16& x) {
 #pragma unroll
   for (int j = 0; j < 16; j += 2) m = fmaxf(m, fmaxf(fabsf(x[j]), fabsf(x[j + 1])));   // v_max3 with |.|
   return m;
-}
-
-// One 32-element contraction block, this lane's 16 values: encode with exponent e into the
-// 4 words the lane contributes to a B operand (exponents from fit_exp: no clamp needed).
-__device__ inline i32x4 encode16(const f32x16& x, int e) {
-  i32x4 r;
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    r[k] = pack_fp8x4(__builtin_amdgcn_ldexpf(x[4 * k], -e), __builtin_amdgcn_ldexpf(x[4 * k + 1], -e),
-                      __builtin_amdgcn_ldexpf(x[4 * k + 2], -e), __builtin_amdgcn_ldexpf(x[4 * k + 3], -e));
-  return r;
-}
-
-// x -= decode(c)·2^e in place (the rounding residual of encode16).
-__device__ inline void residual16(f32x16& x, const i32x4& c, int e) {
-  const float pe = __builtin_amdgcn_ldexpf(1.f, e);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const f32x2 a01 = __builtin_amdgcn_cvt_pk_f32_fp8(c[k], false), a23 = __builtin_amdgcn_cvt_pk_f32_fp8(c[k], true);
-    x[4 * k + 0] = fmaf(-a01.x, pe, x[4 * k + 0]);
-    x[4 * k + 1] = fmaf(-a01.y, pe, x[4 * k + 1]);
-    x[4 * k + 2] = fmaf(-a23.x, pe, x[4 * k + 2]);
-    x[4 * k + 3] = fmaf(-a23.y, pe, x[4 * k + 3]);
-  }
 }
 
 // Block exponent for values quantised inside the kernel (P, dS): the smallest power of two
@@ -121,21 +93,7 @@ struct Fp8Pair {
   int shi, slo;  // this lane's scale bytes (k-block = l/32)
 };
 
-__device__ inline Fp8Pair encode_two_term(const f32x16& x0, const f32x16& x1, int half) {
-  Fp8Pair r;
-  int e0, e1;
-  block_exps(x0, x1, e0, e1);
-  r.hi = encode_b_fp8(x0, x1, e0, e1);
-  f32x16 r0, r1;
-  residual_fp8(x0, x1, r.hi, e0, e1, r0, r1);
-  const int f0 = max(e0 - 4, -127), f1 = max(e1 - 4, -127);
-  r.lo = encode_b_fp8(r0, r1, f0, f1);
-  r.shi = (half ? e1 : e0) + 127;
-  r.slo = (half ? f1 : f0) + 127;
-  return r;
-}
-
-// Block-wise form of encode_two_term for block b (0 or 1) of a B operand: consumes x (its
+// Two-term encoding of block b (0 or 1) of a B operand: consumes x (its
 // storage becomes the residual), writes words 4b..4b+3 of hi and lo and, in the lane group
 // that supplies block b's scale (half == b), the two scale bytes.
 __device__ inline void encode_two_term_block(f32x16& x, int b, int half, Fp8Pair& r) {
@@ -157,41 +115,37 @@ __device__ inline void encode_two_term_block(f32x16& x, int b, int half, Fp8Pair
   }
 }
 
-// Store a 16-byte chunk (16 consecutive tokens of one channel row) of a token-blocked tile into
-// LDS with the per-32-block chunk order (0,2,4,6,1,3,5,7).
-__device__ inline void store_tblocked(char* rowp, int kc, const i32x4& v) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int q = 4 * kc + e;
-    const int bb = q >> 3, qq = q & 7;
-    const int pos = (qq & 1) ? 4 + (qq >> 1) : (qq >> 1);
-    *(int*)(rowp + 32 * bb + 4 * pos) = v[e];
-  }
-}
-
 __device__ inline i32x8 load_a_fp8(const char* row, int half) {
   const i32x4 lo = *(const i32x4*)(row + 16 * half);
   const i32x4 hi = *(const i32x4*)(row + 32 + 16 * half);
   return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
-struct MxBwdTile {
-  static constexpr int D = 128;
-  static constexpr int BM = 64;                       // tokens per step / tile
-  static constexpr int DSTR = 144;                    // d-blocked code row stride
-  static constexpr int DCODES = BM * DSTR;            // 9216
-  static constexpr int DSC = BM * 4;                  // 256
-  static constexpr int TSTR = 80;                     // token-blocked row stride (64 tokens + 16)
-  static constexpr int TCODES = D * TSTR;             // 10240
-  static constexpr int TSC = D * 2;                   // 256
-  static constexpr int BSTR = D * 2 + 16;             // bf16 row stride (272)
-  static constexpr int BTILE = BM * BSTR;             // 17408
+// ------------------------------------------------------------------ dK / dV (wave pairs)
+// 8 waves own 128 keys of one kv head as 4 pairs of 32 keys; a step is 64 queries of one query
+// head (two 32-query blocks: one MX block along the token-contracted products).
+//  * P wave (w < 4): K_d of its keys in registers. S = Q_d K_dᵀ (scaled fp8), P = exp(S − LSE),
+//    P to the exchange buffer (bf16), dVᵀ += dO_tᵀ P with P MX-encoded per 32-query block, or
+//    dOᵀ P in bf16 on diagonal steps.
+//  * dS wave (w + 4), one step behind: V_d in registers. dP = dO_d V_dᵀ, dS = P (dP − D) with
+//    its partner's P, dKᵀ += Q_tᵀ dS (two-term E4M3) or Qᵀ dS in bf16 on diagonal steps.
+// Each role stages its own operands by direct global -> LDS copies into two static buffers:
+//   P wave:  [Q_d codes 64 × 128 B][Q_d scales 64 × 4][LSE·log2 e][dO_t 128 × 64 B + 2 × 128 scales | bf16 dO rows]
+//   dS wave: [dO_d codes][dO_d scales][D][Q_t + scales | bf16 Q rows]
+// Iteration i: P waves copy step i+1 and compute step i; dS waves copy step i and compute step
+// i−1 (P of step i−1 sits in exchange buffer (i−1) mod 2). Every buffer is a separate static
+// array and the loop is unrolled twice, so no copy in flight aliases a buffer being read.
+struct MxDkdvTile {
+  static constexpr int BM = 64;
+  static constexpr int OFF_SC = BM * 128;            // d-blocked codes: 64 rows × 128 B (kd_swz)
+  static constexpr int OFF_ROW = OFF_SC + BM * 4;    // 4 scale bytes per row
+  static constexpr int OFF_U = OFF_ROW + BM * 4;     // LSE·log2 e or D: 64 floats
+  static constexpr int OFF_TSC = OFF_U + 128 * 64;   // token-blocked codes: 128 rows × 64 B (vt_swz)
+  static constexpr int BUF = OFF_U + BM * 256;       // union with 64 bf16 rows (SwzTile<128>)
+  static constexpr int XP = 4 * 4 * 64;              // exchange: i32x4 [pair][2·qb + u][lane]
 };
 
-// ------------------------------------------------------------------ dK / dV
-// LDS stage: [Qd codes][Qd sc][dOd codes][dOd sc][union: {Qt, Qt sc, dOt, dOt sc} | {Qb, dOb}][lse2][D]
-template <int DUMMY>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mx_kernel(
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
     const uint8_t* __restrict__ qd, const uint8_t* __restrict__ qd_sc, const uint8_t* __restrict__ kd,
     const uint8_t* __restrict__ kd_sc, const uint8_t* __restrict__ dod, const uint8_t* __restrict__ dod_sc,
     const uint8_t* __restrict__ vd, const uint8_t* __restrict__ vd_sc, const uint8_t* __restrict__ qt,
@@ -199,244 +153,293 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mx_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, __bf16* __restrict__ dk, __bf16* __restrict__ dv, Plan plan,
     const int* __restrict__ padoff, int total_tokens, int t_pad, int hq, int hkv, float scale, int causal) {
-  using C = MxBwdTile;
-  constexpr int D = C::D, BM = C::BM;
-  constexpr int O_QDSC = C::DCODES;
-  constexpr int O_OD = O_QDSC + C::DSC;
-  constexpr int O_ODSC = O_OD + C::DCODES;
-  constexpr int O_U = O_ODSC + C::DSC;
-  constexpr int O_QT = O_U, O_QTSC = O_QT + C::TCODES, O_OT = O_QTSC + C::TSC, O_OTSC = O_OT + C::TCODES;
-  constexpr int O_QB = O_U, O_OB = O_U + C::BTILE;
-  constexpr int U_BYTES = (2 * C::BTILE > 2 * (C::TCODES + C::TSC)) ? 2 * C::BTILE : 2 * (C::TCODES + C::TSC);
-  constexpr int O_L = O_U + U_BYTES;
-  constexpr int STAGE = O_L + 2 * BM * 4;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  using C = MxDkdvTile;
+  constexpr int D = 128, BM = C::BM;
+  __shared__ i32x4 xp_a[C::XP];
+  __shared__ i32x4 xp_b[C::XP];
+  __shared__ __attribute__((aligned(16))) char pb_a[C::BUF];
+  __shared__ __attribute__((aligned(16))) char pb_b[C::BUF];
+  __shared__ __attribute__((aligned(16))) char sb_a[C::BUF];
+  __shared__ __attribute__((aligned(16))) char sb_b[C::BUF];
 
   const int p = blockIdx.x / hkv, g = blockIdx.x % hkv;
   int s0, L, t, doc;
   if (!decode_item(plan, p, 128, false, s0, L, t, &doc)) return;
   const int pcol = padoff[doc];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5;
+  const int lp = 32 * ((L + 31) / 32);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5, r32 = lane & 31;
+  const int pair = w & 3;
+  const bool ds_wave = w >= 4;
   const int G = hq / hkv;
-  const int kw0 = t * 128 + 32 * w;
-  const int mykey = kw0 + (lane & 31);
+  const int kw0 = t * 128 + 32 * pair;
+  const int mykey = kw0 + r32;
   const float sl2 = scale * LOG2E;
+  int ko[2][2], to[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) ko[s][u] = 16 * ((4 * s + 2 * u + half) ^ kd_swz(r32));
+#pragma unroll
+  for (int u = 0; u < 2; ++u) to[u] = 16 * ((2 * u + half) ^ vt_swz(r32));
 
-  // K_d and V_d of this wave's keys as B operands
-  i32x8 kb[2], vb[2];
-  int ks[2], vs[2];
+  // B operand rows of key mykey: K_d (P wave) or V_d (dS wave)
+  i32x8 kvb[2];
+  int kvs[2];
   {
     const bool ok = mykey < L;
+    const uint8_t* src = ds_wave ? vd : kd;
+    const uint8_t* ssrc = ds_wave ? vd_sc : kd_sc;
     const size_t row = (size_t)(s0 + (ok ? mykey : 0)) * hkv + g;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      kb[s] = ok ? load_a_fp8((const char*)(kd + row * D + 64 * s), half) : i32x8{};
-      vb[s] = ok ? load_a_fp8((const char*)(vd + row * D + 64 * s), half) : i32x8{};
-      ks[s] = ok ? kd_sc[row * 4 + 2 * s + half] : 127;
-      vs[s] = ok ? vd_sc[row * 4 + 2 * s + half] : 127;
+      kvb[s] = ok ? load_a_fp8((const char*)(src + row * D + 64 * s), half) : i32x8{};
+      kvs[s] = ok ? ssrc[row * 4 + 2 * s + half] : 127;
     }
   }
-  f32x16 dka[4], dva[4];
+  f32x16 acc[4];                                  // dVᵀ (P wave) or dKᵀ (dS wave)
 #pragma unroll
-  for (int b = 0; b < 4; ++b) { dka[b] = f32x16{}; dva[b] = f32x16{}; }
+  for (int b = 0; b < 4; ++b) acc[b] = f32x16{};
 
   const int q_begin = causal ? t * 128 : 0;
   const int n_qt = (L - q_begin + BM - 1) / BM;
   const int n_steps = n_qt * G;
   const int wave_first_q = causal ? kw0 : 0;
-  auto step_is_diag = [&](int st) { return causal && ((q_begin + (st % n_qt) * BM) / 128 == t); };
+  auto q0_of = [&](int st) { return q_begin + (st % n_qt) * BM; };
+  auto step_is_diag = [&](int st) { return causal && (q0_of(st) / 128 == t); };
+  auto active = [&](int st) { return q0_of(st) + BM - 1 >= wave_first_q && kw0 < L; };
 
-  i32x4 r_qd[2], r_od[2], r_u[8];
-  int r_qs = 0, r_os = 0, r_ts = 0;
-  float r_l = 0.f, r_d = 0.f;
-  auto load_step = [&](int st) {
+  // Operands of step st for this wave's role -> buffer. Rows past the document end are clamped
+  // into it (d-blocked, bf16) or into its last token block (token-blocked); they are masked.
+  // Lanes 0..63 of the first wave of each role fetch LSE or D into a register (stage_finish
+  // writes it after the step's compute).
+  float rreg = 0.f;
+  auto stage = [&](int st, char* buf) {
     const int h = g * G + st / n_qt;
-    const int q0 = q_begin + (st % n_qt) * BM;
-    const int tid = threadIdx.x;
+    const int q0 = q0_of(st);
+    const int rmax = L - 1 - q0;
+    const size_t tok0 = (size_t)(s0 + q0) * hq + h;
+    const uint32_t tok_b = (uint32_t)hq * D;
+    const uint8_t* dsrc = (ds_wave ? dod : qd) + tok0 * D;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, col = c & 7;
-      const bool ok = q0 + row < L;
-      const size_t off = ((size_t)(s0 + q0 + row) * hq + h) * D + col * 16;
-      r_qd[i] = ok ? *(const i32x4*)(qd + off) : i32x4{0, 0, 0, 0};
-      r_od[i] = ok ? *(const i32x4*)(dod + off) : i32x4{0, 0, 0, 0};
+    for (int j = 0; j < 2; ++j) {               // d-blocked codes: 8 blocks of 8 rows
+      const int I = 2 * pair + j, r = 8 * I + (lane >> 3);
+      g2lds16(dsrc + ((uint32_t)min(r, rmax) * tok_b + 16 * ((lane & 7) ^ kd_swz(r))), buf + I * 1024);
     }
-    if (tid < 64) {
-      const bool ok = q0 + tid < L;
-      const size_t off = ((size_t)(s0 + q0 + tid) * hq + h) * 4;
-      r_qs = ok ? *(const int*)(qd_sc + off) : 0x7f7f7f7f;
-      r_os = ok ? *(const int*)(dod_sc + off) : 0x7f7f7f7f;
-      r_l = ok ? lse[(size_t)h * total_tokens + s0 + q0 + tid] * LOG2E : INFINITY;
-      r_d = ok ? delta[(size_t)h * total_tokens + s0 + q0 + tid] : 0.f;
-    }
+    if (pair == 0)
+      g2lds4((ds_wave ? dod_sc : qd_sc) + tok0 * 4 + (uint32_t)min(lane, rmax) * (uint32_t)hq * 4, buf + C::OFF_SC);
+    if (pair == 1) rreg = (ds_wave ? delta : lse)[(size_t)h * total_tokens + s0 + q0 + min(lane, rmax)];
     if (step_is_diag(st)) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i, row = c >> 4, col = c & 15;
-        const bool ok = q0 + row < L;
-        const size_t off = ((size_t)(s0 + q0 + row) * hq + h) * D + col * 8;
-        r_u[i] = ok ? *(const i32x4*)(q + off) : i32x4{0, 0, 0, 0};
-        r_u[4 + i] = ok ? *(const i32x4*)(dout + off) : i32x4{0, 0, 0, 0};
-      }
+      stage_rows_lds<BM>(buf + C::OFF_U, (const char*)((ds_wave ? q : dout) + tok0 * D), tok_b * 2, rmax, pair, lane);
     } else {
+      const uint8_t* tsrc = (ds_wave ? qt : dot) + (size_t)h * D * t_pad + pcol + q0;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int c = tid + 256 * i, ch = c >> 2, kc = c & 3;
-        const bool ok = q0 + 16 * kc < L;
-        const size_t off = ((size_t)h * D + ch) * t_pad + pcol + q0 + 16 * kc;
-        r_u[i] = ok ? *(const i32x4*)(qt + off) : i32x4{0, 0, 0, 0};
-        r_u[2 + i] = ok ? *(const i32x4*)(dot + off) : i32x4{0, 0, 0, 0};
+      for (int j = 0; j < 2; ++j) {             // token-blocked codes: 8 blocks of 16 channel rows
+        const int I = 2 * pair + j, r = 16 * I + (lane >> 2);
+        const int col = min(16 * ((lane & 3) ^ vt_swz(r)), lp - 16 - q0);
+        g2lds16(tsrc + (uint32_t)(r * t_pad + col), buf + C::OFF_U + I * 1024);
       }
-      if (tid < D) {
-        const size_t srow = ((size_t)h * D + tid) * (t_pad / 32) + (pcol + q0) / 32;
-        const bool ok1 = q0 + 32 < L;
-        r_ts = qt_sc[srow] | ((ok1 ? qt_sc[srow + 1] : 127) << 8) | (dot_sc[srow] << 16) |
-               ((ok1 ? dot_sc[srow + 1] : 127) << 24);
+      if (pair == 2 && lane < 16) {
+        const int blk = min((q0 >> 5) + (lane >> 3), lp / 32 - 1);
+        g2lds16((ds_wave ? qt_sc : dot_sc) + ((size_t)h * (t_pad / 32) + (pcol >> 5) + blk) * D + 16 * (lane & 7),
+                buf + C::OFF_TSC);
       }
     }
   };
-  auto store_step = [&](int buf, int st) {
-    char* sb = smem + buf * STAGE;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, col = c & 7;
-      *(i32x4*)(sb + row * C::DSTR + col * 16) = r_qd[i];
-      *(i32x4*)(sb + O_OD + row * C::DSTR + col * 16) = r_od[i];
-    }
-    if (tid < 64) {
-      *(int*)(sb + O_QDSC + tid * 4) = r_qs;
-      *(int*)(sb + O_ODSC + tid * 4) = r_os;
-      ((float*)(sb + O_L))[tid] = r_l;
-      ((float*)(sb + O_L))[BM + tid] = r_d;
-    }
-    if (step_is_diag(st)) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i, row = c >> 4, col = c & 15;
-        *(i32x4*)(sb + O_QB + row * C::BSTR + col * 16) = r_u[i];
-        *(i32x4*)(sb + O_OB + row * C::BSTR + col * 16) = r_u[4 + i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int c = tid + 256 * i, ch = c >> 2, kc = c & 3;
-        store_tblocked(sb + O_QT + ch * C::TSTR, kc, r_u[i]);
-        store_tblocked(sb + O_OT + ch * C::TSTR, kc, r_u[2 + i]);
-      }
-      if (tid < D) {
-        *(uint16_t*)(sb + O_QTSC + tid * 2) = (uint16_t)(r_ts & 0xFFFF);
-        *(uint16_t*)(sb + O_OTSC + tid * 2) = (uint16_t)(r_ts >> 16);
-      }
-    }
+  auto stage_finish = [&](char* buf) {
+    if (pair == 1) ((float*)(buf + C::OFF_ROW))[lane] = ds_wave ? rreg : rreg * LOG2E;
   };
 
-  if (n_steps > 0) {
-    load_step(0);
-    store_step(0, 0);
-  }
-  __syncthreads();
-  for (int st = 0; st < n_steps; ++st) {
-    if (st + 1 < n_steps) load_step(st + 1);
-    const int q0 = q_begin + (st % n_qt) * BM;
-    if (q0 + BM - 1 >= wave_first_q && kw0 < L) {
-      const char* sb = smem + (st & 1) * STAGE;
-      const float* lb = (const float*)(sb + O_L);
-      const float* db = lb + BM;
-      const bool need_mask = causal && (q0 < kw0 + 31);
-      f32x16 pv[2], dsv[2];
+  // scores of 32-query block qb of the step against this pair's keys (A = d-blocked rows)
+  auto dscores = [&](const char* buf, int qb) __attribute__((always_inline)) {
+    const int qr = 32 * qb + r32;
+    const int sc = *(const int*)(buf + C::OFF_SC + qr * 4);
+    const char* rp = buf + qr * 128;
+    f32x16 a = f32x16{};
 #pragma unroll
-      for (int qb2 = 0; qb2 < 2; ++qb2) {
-        const int qr = 32 * qb2 + (lane & 31);
-        const int qsc = *(const int*)(sb + O_QDSC + qr * 4);
-        const int osc = *(const int*)(sb + O_ODSC + qr * 4);
-        f32x16 sacc = f32x16{}, pacc = f32x16{};
+    for (int s = 0; s < 2; ++s) {
+      const i32x4 lo = *(const i32x4*)(rp + ko[s][0]), hi = *(const i32x4*)(rp + ko[s][1]);
+      a = mfma32_mx(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, (sc >> (8 * (2 * s + half))) & 0xFF,
+                    kvb[s], kvs[s], a);
+    }
+    return a;
+  };
+
+  // P wave, step st; the two query blocks one after the other
+  auto step_p = [&](int st, const char* buf, i32x4* xw) __attribute__((always_inline)) {
+    const int q0 = q0_of(st);
+    const bool diag = step_is_diag(st);
+    const bool masked = (causal && q0 < kw0 + 31) || q0 + BM > L;   // wave-uniform
+    const f32x4* l2 = (const f32x4*)(buf + C::OFF_ROW);
+    i32x4 pw[4];                                // bf16 P: exchange words and diagonal B operands
+    i32x8 pb8;                                  // E4M3 P (off-diagonal steps)
+    int psc = 127;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          sacc = mfma32_mx(load_a_fp8(sb + qr * C::DSTR + 64 * s, half), (qsc >> (8 * (2 * s + half))) & 0xFF, kb[s],
-                           ks[s], sacc);
-          pacc = mfma32_mx(load_a_fp8(sb + O_OD + qr * C::DSTR + 64 * s, half), (osc >> (8 * (2 * s + half))) & 0xFF,
-                           vb[s], vs[s], pacc);
-        }
-        if (need_mask) {                 // wave-uniform: steps that cross the diagonal
-#pragma unroll
-          for (int j = 0; j < 16; ++j)
-            if (mykey > q0 + 32 * qb2 + 8 * (j >> 2) + 4 * half + (j & 3)) sacc[j] = -INFINITY;
-        }
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x16 x = dscores(buf, qb);
+      if (masked) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int qi_t = 32 * qb2 + 8 * (j >> 2) + 4 * half + (j & 3);
-          const float x = exp2_fast(fmaf(sacc[j], sl2, -lb[qi_t]));
-          pv[qb2][j] = x;
-          dsv[qb2][j] = x * (pacc[j] - db[qi_t]);
+          const int qi = q0 + 32 * qb + 8 * (j >> 2) + 4 * half + (j & 3);
+          if ((causal && mykey > qi) || qi >= L) x[j] = -INFINITY;
         }
       }
-      if (step_is_diag(st)) {
-        bf16x8 pf[4], sf[4];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          i32x4 up, us;
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 lr = l2[8 * qb + 2 * jj + half];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            up[e] = (int)pack_bf16x2(pv[kk >> 1][8 * (kk & 1) + 2 * e], pv[kk >> 1][8 * (kk & 1) + 2 * e + 1]);
-            us[e] = (int)pack_bf16x2(dsv[kk >> 1][8 * (kk & 1) + 2 * e], dsv[kk >> 1][8 * (kk & 1) + 2 * e + 1]);
-          }
-          pf[kk] = __builtin_bit_cast(bf16x8, up);
-          sf[kk] = __builtin_bit_cast(bf16x8, us);
-        }
-        const char* qbt = sb + O_QB;
-        const char* obt = sb + O_OB;
+        for (int u = 0; u < 4; ++u) x[4 * jj + u] = exp2_fast(fmaf(x[4 * jj + u], sl2, -lr[u]));
+        pw[2 * qb + (jj >> 1)][2 * (jj & 1)] = (int)pack_bf16x2(x[4 * jj], x[4 * jj + 1]);
+        pw[2 * qb + (jj >> 1)][2 * (jj & 1) + 1] = (int)pack_bf16x2(x[4 * jj + 2], x[4 * jj + 3]);
+      }
+      xw[(pair * 4 + 2 * qb) * 64 + lane] = pw[2 * qb];
+      xw[(pair * 4 + 2 * qb + 1) * 64 + lane] = pw[2 * qb + 1];
+      if (!diag) {                              // MX block of 32 queries: exponent over the lane pair
+        float a = amax16(x);
+        a = fmaxf(a, __shfl_xor(a, 32));
+        const int e = fit_exp(a);
+        const i32x4 c = encode16(x, e);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int rbase = 32 * (kk >> 1) + 16 * (kk & 1);
-          const int row = rbase + 4 * half + ((lane & 15) >> 2);
-          const int dsub = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-          for (int dbk = 0; dbk < 4; ++dbk) {
-            const int boff = row * C::BSTR + (32 * dbk + dsub) * 2;
-            dva[dbk] = mfma32(concat_tr(lds_read_tr16(obt + boff), lds_read_tr16(obt + boff + 8 * C::BSTR)), pf[kk],
-                              dva[dbk]);
-            dka[dbk] = mfma32(concat_tr(lds_read_tr16(qbt + boff), lds_read_tr16(qbt + boff + 8 * C::BSTR)), sf[kk],
-                              dka[dbk]);
-          }
-        }
-      } else {
-        // P (normalised, ~1/L: needs its own block scale) with an MX exponent per (key,
-        // 32-query block); dS as two E4M3 terms with MX exponents
-        int pe0, pe1;
-        block_exps(pv[0], pv[1], pe0, pe1);
-        const i32x8 pb = encode_b_fp8(pv[0], pv[1], pe0, pe1);
-        const int psc = (half ? pe1 : pe0) + 127;
-        const Fp8Pair ds2 = encode_two_term(dsv[0], dsv[1], half);
-#pragma unroll
-        for (int dbk = 0; dbk < 4; ++dbk) {
-          const int ch = 32 * dbk + (lane & 31);
-          const int osa = (*(const uint16_t*)(sb + O_OTSC + ch * 2) >> (8 * half)) & 0xFF;
-          const int qsa = (*(const uint16_t*)(sb + O_QTSC + ch * 2) >> (8 * half)) & 0xFF;
-          dva[dbk] = mfma32_mx(load_a_fp8(sb + O_OT + ch * C::TSTR, half), osa, pb, psc, dva[dbk]);
-          const i32x8 aq = load_a_fp8(sb + O_QT + ch * C::TSTR, half);
-          dka[dbk] = mfma32_mx(aq, qsa, ds2.hi, ds2.shi, dka[dbk]);
-          dka[dbk] = mfma32_mx(aq, qsa, ds2.lo, ds2.slo, dka[dbk]);
-        }
+        for (int k = 0; k < 4; ++k) pb8[4 * qb + k] = c[k];
+        if (half == qb) psc = e + 127;
       }
     }
-    if (st + 1 < n_steps) store_step((st + 1) & 1, st + 1);
+    if (diag) {
+      const SwzOffsets<D> so(lane);
+      const char* ob = buf + C::OFF_U;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int rb = (32 * (kk >> 1) + 16 * (kk & 1)) * 256;
+        bf16x8 ao[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          ao[db] = concat_tr(lds_read_tr16(ob + rb + so.tr0[db]), lds_read_tr16(ob + rb + so.tr1[db]));
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[db] = mfma32(ao[db], __builtin_bit_cast(bf16x8, pw[kk]), acc[db]);
+      }
+    } else {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int ch = 32 * db + r32;
+        const char* rp = buf + C::OFF_U + ch * 64;
+        const i32x4 lo = *(const i32x4*)(rp + to[0]), hi = *(const i32x4*)(rp + to[1]);
+        const int sa = *(const uint8_t*)(buf + C::OFF_TSC + half * 128 + ch);
+        acc[db] = mfma32_mx(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, sa, pb8, psc, acc[db]);
+      }
+    }
+  };
+
+  // dS wave, step st (one iteration after its P wave); the query blocks one after the other
+  auto step_ds = [&](int st, const char* buf, const i32x4* xr) __attribute__((always_inline)) {
+    const bool diag = step_is_diag(st);
+    const f32x4* dd = (const f32x4*)(buf + C::OFF_ROW);
+    bf16x8 sf[4];                               // diagonal steps: bf16 dS
+    Fp8Pair ds2;                                // other steps: two-term E4M3 dS
+    ds2.shi = ds2.slo = 127;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x16 x = dscores(buf, qb);              // dP
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const i32x4 pw = xr[(pair * 4 + 2 * qb + u) * 64 + lane];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const f32x4 dr = dd[8 * qb + 2 * (2 * u + jj) + half];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const uint32_t word = (uint32_t)pw[2 * jj + e];
+            const int j = 8 * u + 4 * jj + 2 * e;
+            x[j] = __builtin_bit_cast(float, word << 16) * (x[j] - dr[2 * e]);
+            x[j + 1] = __builtin_bit_cast(float, word & 0xFFFF0000u) * (x[j + 1] - dr[2 * e + 1]);
+          }
+        }
+      }
+      if (diag) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          i32x4 us;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) us[e] = (int)pack_bf16x2(x[8 * u + 2 * e], x[8 * u + 2 * e + 1]);
+          sf[2 * qb + u] = __builtin_bit_cast(bf16x8, us);
+        }
+      } else {
+        encode_two_term_block(x, qb, half, ds2);
+      }
+    }
+    if (diag) {
+      const SwzOffsets<D> so(lane);
+      const char* qb_ = buf + C::OFF_U;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int rb = (32 * (kk >> 1) + 16 * (kk & 1)) * 256;
+        bf16x8 aq[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          aq[db] = concat_tr(lds_read_tr16(qb_ + rb + so.tr0[db]), lds_read_tr16(qb_ + rb + so.tr1[db]));
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[db] = mfma32(aq[db], sf[kk], acc[db]);
+      }
+    } else {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int ch = 32 * db + r32;
+        const char* rp = buf + C::OFF_U + ch * 64;
+        const i32x4 lo = *(const i32x4*)(rp + to[0]), hi = *(const i32x4*)(rp + to[1]);
+        const i32x8 aq = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        const int sa = *(const uint8_t*)(buf + C::OFF_TSC + half * 128 + ch);
+        acc[db] = mfma32_mx(aq, sa, ds2.hi, ds2.shi, acc[db]);
+        acc[db] = mfma32_mx(aq, sa, ds2.lo, ds2.slo, acc[db]);
+      }
+    }
+  };
+
+  // Iteration i. The two roles run separate loops (so each keeps only its own addresses live);
+  // both execute one barrier per iteration, n_steps + 1 iterations after the prologue barrier.
+  auto iter_p = [&](int i, const char* pcur, char* pnxt, i32x4* xw) __attribute__((always_inline)) {
+    if (i + 1 < n_steps) stage(i + 1, pnxt);
+    if (i < n_steps && active(i)) step_p(i, pcur, xw);
+    if (i + 1 < n_steps) stage_finish(pnxt);
+    wait_vmem();
     __syncthreads();
+  };
+  auto iter_ds = [&](int i, char* sload, const char* suse, const i32x4* xr) __attribute__((always_inline)) {
+    if (i < n_steps) stage(i, sload);
+    if (i >= 1 && active(i - 1)) step_ds(i - 1, suse, xr);
+    if (i < n_steps) stage_finish(sload);
+    wait_vmem();
+    __syncthreads();
+  };
+
+  if (!ds_wave) {
+    if (n_steps > 0) {
+      stage(0, pb_a);
+      stage_finish(pb_a);
+    }
+    wait_vmem();
+    __syncthreads();
+    for (int i = 0; i <= n_steps; i += 2) {
+      iter_p(i, pb_a, pb_b, xp_a);
+      if (i + 1 <= n_steps) iter_p(i + 1, pb_b, pb_a, xp_b);
+    }
+  } else {
+    __syncthreads();
+    for (int i = 0; i <= n_steps; i += 2) {
+      iter_ds(i, sb_a, sb_b, xp_b);
+      if (i + 1 <= n_steps) iter_ds(i + 1, sb_b, sb_a, xp_a);
+    }
   }
 
+  // dS wave: dK = scale·dKᵀ; P wave: dV (lane: key mykey, d = 32 db + 8 jg + 4·half + 0..3)
   if (mykey < L) {
-    const size_t base = ((size_t)(s0 + mykey) * hkv + g) * D + 4 * half;
+    const float f = ds_wave ? scale : 1.f;
+    __bf16* dst = (ds_wave ? dk : dv) + ((size_t)(s0 + mykey) * hkv + g) * D + 4 * half;
 #pragma unroll
-    for (int dbk = 0; dbk < 4; ++dbk)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
-        i32x2 uk, uv;
-        uk.x = (int)pack_bf16x2(dka[dbk][4 * jg] * scale, dka[dbk][4 * jg + 1] * scale);
-        uk.y = (int)pack_bf16x2(dka[dbk][4 * jg + 2] * scale, dka[dbk][4 * jg + 3] * scale);
-        uv.x = (int)pack_bf16x2(dva[dbk][4 * jg], dva[dbk][4 * jg + 1]);
-        uv.y = (int)pack_bf16x2(dva[dbk][4 * jg + 2], dva[dbk][4 * jg + 3]);
-        *(i32x2*)(dk + base + 32 * dbk + 8 * jg) = uk;
-        *(i32x2*)(dv + base + 32 * dbk + 8 * jg) = uv;
+        i32x2 u;
+        u.x = (int)pack_bf16x2(acc[db][4 * jg] * f, acc[db][4 * jg + 1] * f);
+        u.y = (int)pack_bf16x2(acc[db][4 * jg + 2] * f, acc[db][4 * jg + 3] * f);
+        *(i32x2*)(dst + 32 * db + 8 * jg) = u;
       }
   }
 }
@@ -664,12 +667,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
 }
 
 // ------------------------------------------------------------------ launchers
-static int dkdv_mx_stage() {
-  using C = MxBwdTile;
-  constexpr int U = (2 * C::BTILE > 2 * (C::TCODES + C::TSC)) ? 2 * C::BTILE : 2 * (C::TCODES + C::TSC);
-  return 2 * (C::DCODES + C::DSC) + U + 2 * C::BM * 4;
-}
-
 hipError_t launch_bwd_dkdv_mx(const MxOperands& m, const void* q, const void* dout, const float* lse,
                               const float* delta, void* dk, void* dv, const Plan& plan_any, const int* pref_base,
                               const int* padoff, int T, int t_pad, int hq, int hkv, float scale, int causal,
@@ -679,13 +676,10 @@ hipError_t launch_bwd_dkdv_mx(const MxOperands& m, const void* q, const void* do
   const long grid = ((long)(T + 127) / 128 + plan.n_docs) * hkv;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  const int lds = 2 * dkdv_mx_stage();
-  auto kern = attn_bwd_dkdv_mx_kernel<0>;
-  if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds))
-    return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, stream, m.qd, m.qd_sc, m.kd, m.kd_sc, m.dod, m.dod_sc,
-                     m.vd, m.vd_sc, m.qt, m.qt_sc, m.dot, m.dot_sc, (const __bf16*)q, (const __bf16*)dout, lse, delta,
-                     (__bf16*)dk, (__bf16*)dv, plan, padoff, T, t_pad, hq, hkv, scale, causal);
+  hipLaunchKernelGGL(attn_bwd_dkdv_mx_kernel, dim3((unsigned)grid), dim3(512), 0, stream, m.qd, m.qd_sc, m.kd,
+                     m.kd_sc, m.dod, m.dod_sc, m.vd, m.vd_sc, m.qt, m.qt_sc, m.dot, m.dot_sc, (const __bf16*)q,
+                     (const __bf16*)dout, lse, delta, (__bf16*)dk, (__bf16*)dv, plan, padoff, T, t_pad, hq, hkv, scale,
+                     causal);
   return hipGetLastError();
 }
 

@@ -292,9 +292,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
     auto U = [&](const MxBuf& b, bool codes) { return (uint8_t*)ws + (codes ? b.codes : b.scales); };
     mark(3, 0, st);
     hipError_t e = cfa::launch_mx_quantize_d(dout, (long)total_tokens * hq * d, U(wl.dod, true), U(wl.dod, false), st);
-    if (!e) e = cfa::launch_mx_quantize_t(dout, total_tokens, hq, d, ws, n_docs, U(wl.dot, true), U(wl.dot, false), tp, false, st);
+    if (!e) e = cfa::launch_mx_quantize_t(dout, total_tokens, hq, d, ws, n_docs, U(wl.dot, true), U(wl.dot, false), tp, true, st);
     if (!e) e = cfa::launch_mx_quantize_d(v, (long)total_tokens * hkv * d, U(wl.vd, true), U(wl.vd, false), st);
-    if (!e) e = cfa::launch_mx_quantize_t(q, total_tokens, hq, d, ws, n_docs, U(wl.qt, true), U(wl.qt, false), tp, false, st);
+    if (!e) e = cfa::launch_mx_quantize_t(q, total_tokens, hq, d, ws, n_docs, U(wl.qt, true), U(wl.qt, false), tp, true, st);
     if (!e) e = cfa::launch_mx_quantize_t(k, total_tokens, hkv, d, ws, n_docs, U(wl.kt, true), U(wl.kt, false), tp, true, st);
     mark(3, 1, st);
     if (int r = check_hip(e, "backward quantisation")) return r;

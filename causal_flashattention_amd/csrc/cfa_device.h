@@ -113,6 +113,25 @@ __device__ inline int pack_fp8x4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
+typedef __attribute__((ext_vector_type(2))) short i16x2;
+
+// Four floats -> four E4M3 bytes of x / s for a power of two s, in two v_cvt_scalef32_pk_fp8_f32
+// (round to nearest even, no saturation: callers keep |x / s| <= 448).
+__device__ inline int pack_fp8x4_scaled(float a, float b, float c, float d, float s) {
+  i16x2 w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2{0, 0}, a, b, s, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, s, true);
+  return __builtin_bit_cast(int, w);
+}
+
+// Two E4M3 bytes (bytes 0-1, or 2-3 when HI) -> floats × s for a power of two s.
+template <bool HI>
+__device__ inline f32x2 unpack_fp8x2_scaled(int word, float s) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, s, HI);
+}
+
+// 2^e as a float for -126 <= e <= 127 (exponent field only); 2^-127 is built by ldexp.
+__device__ inline float pow2i(int e) { return e >= -126 ? __builtin_bit_cast(float, (e + 127) << 23) : 0x1p-127f; }
+
 // LDS layout of a bf16 tile with rows of D elements that is read both row-wise (ds_read_b128:
 // 16 lanes take one 16-byte chunk of 16 consecutive rows) and transposed (ds_read_b64_tr_b16:
 // 32 lanes take 4 rows × 4 consecutive chunks). For D = 128, rows are 256 bytes (no padding)
