@@ -32,9 +32,18 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
+# The attention kernels take no non-finite inputs (masked scores are -inf, never NaN), so they
+# are built without NaN semantics and with the IEEE mode bit off: max/min then need no
+# canonicalising instruction before each use of a matrix-core result. The quantiser keeps
+# both, since it must detect NaN/Inf blocks.
+NO_NAN_SOURCES = {"attn_fwd.hip", "attn_fwd_mx.hip", "attn_bwd_mx.hip"}
+NO_NAN_FLAGS = ["-fno-honor-nans", "-mno-amdgpu-ieee"]
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", src, "-o", obj]
+    extra = NO_NAN_FLAGS if os.path.basename(src) in NO_NAN_SOURCES else []
+    cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
