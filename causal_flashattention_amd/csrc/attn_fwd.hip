@@ -9,9 +9,10 @@
 // "FlashAttention (HU)" sections "Tiling és blokkos feldolgozás", "Online Softmax-számítás",
 // "Műveletek összevonása egyetlen CUDA-kernelbe".
 //
-// bf16 kernel layout (d = 64 or 128), one workgroup = 4 waves of 64 lanes:
+// bf16 kernel layout (d = 64 or 128), one workgroup = NW waves of 64 lanes (8 for d = 128, 4 for 64):
 //  * Each wave owns 32 query rows of one head. HPW heads of one GQA group share a workgroup
-//    (HPW = 1, 2 or 4), so a K/V tile staged in LDS serves 128 (row, head) pairs.
+//    (HPW = 1, 2 or 4), so a K/V tile staged in LDS serves 32·NW (row, head) pairs: with 8 waves
+//    each staged byte feeds twice the products of a 4-wave workgroup (one workgroup per CU).
 //  * Scores are formed transposed, Sᵀ = K Qᵀ, with v_mfma_f32_32x32x16_bf16: the wave's Qᵀ
 //    fragment stays in registers for the whole key loop, and each lane ends up holding one
 //    query column, so the row max and row sum are in-lane plus one swap between lane halves.
@@ -19,7 +20,7 @@
 //    convert to bf16); Vᵀ comes from the row-major V tile through ds_read_b64_tr_b16.
 //  * K/V tiles of 64 keys are double-buffered in LDS: the next tile's global loads are in
 //    flight while the current tile is multiplied.
-//  * exp2 with scale·log2(e) folded into the scores; LSE converted back to natural log.
+//  * exp2 with scale·log2(e) folded into the exponent; LSE converted back to natural log.
 #include "cfa_device.h"
 
 namespace cfa {
@@ -41,13 +42,13 @@ struct FwdTile {
 // units), which skips most rescalings of the O accumulator.
 constexpr float RESCALE_LOG2 = 8.f;
 
-template <int D, int HPW>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
+template <int D, int HPW, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, Plan plan, int total_tokens, int hq, int hkv,
     int n_hb, float scale_log2, int causal) {
   using C = FwdTile<D>;
-  constexpr int BMW = 128 / HPW;  // query rows per workgroup
+  constexpr int BMW = 32 * NW / HPW;  // query rows per workgroup
   // two separate LDS buffers (not one array indexed at run time) so that the compiler can
   // tell that the copy into one buffer never aliases the reads of the other
   __shared__ __attribute__((aligned(16))) char lds_a[C::STAGE];
@@ -87,17 +88,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   for (int b = 0; b < C::DB; ++b) oacc[b] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // ---- staging of one K/V tile into an LDS buffer. d = 128: direct global -> LDS copies
-  // (no registers, completion tracked by vmcnt); d = 64: through registers. Keys past kv_end
-  // are clamped into the document: they are masked (P = 0).
+  // ---- staging of one K/V tile into an LDS buffer: [K rows][V rows]. d = 128: direct global ->
+  // LDS copies shared out among the NW waves (no registers, completion tracked by vmcnt);
+  // d = 64: through registers. Keys past kv_end are clamped into the document: they are masked
+  // (P = 0).
   auto stage = [&](int kt, char* kb) {
     const int k0 = kt * C::BN;
     char* vb = kb + C::KBYTES;
     if constexpr (D == 128) {
       const size_t row0 = ((size_t)(s0 + k0) * hkv + g) * D;
       const uint32_t stride = (uint32_t)hkv * D * 2;
-      stage_rows_lds<C::BN>(kb, (const char*)(k + row0), stride, kv_end - 1 - k0, w, lane);
-      stage_rows_lds<C::BN>(vb, (const char*)(v + row0), stride, kv_end - 1 - k0, w, lane);
+      stage_rows_lds<C::BN, NW>(kb, (const char*)(k + row0), stride, kv_end - 1 - k0, w, lane);
+      stage_rows_lds<C::BN, NW>(vb, (const char*)(v + row0), stride, kv_end - 1 - k0, w, lane);
     } else {
       i32x4 kreg[C::PER_THREAD], vreg[C::PER_THREAD];
 #pragma unroll
@@ -122,13 +124,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   wait_vmem();
   __syncthreads();
 
-  // one key tile: copy tile kt+1 into `nxt` while multiplying tile kt from `cur`
-  auto iter = [&](int kt, const char* cur, char* nxt) __attribute__((always_inline)) {
-    const int k0 = kt * C::BN;
-    if (kt + 1 < n_kt) stage(kt + 1, nxt);
+  // the 64-key tile at doc-local key k0, its K rows at kb and V rows at vb
+  auto subtile = [&](int k0, const char* kb, const char* vb) __attribute__((always_inline)) {
     if (k0 <= wave_last_key) {
-      const char* kb = cur;
-      const char* vb = kb + C::KBYTES;
       // ---- Sᵀ = K Qᵀ for the tile's two 32-key blocks: operand rows read as a batch, the
       // two accumulators interleaved so consecutive MFMAs are independent
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
@@ -209,6 +207,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
         for (int db = 0; db < C::DB; ++db) oacc[db] = mfma32(av[db], pf[kk], oacc[db]);
       }
     }
+  };
+  // one key tile: copy tile kt+1 into `nxt` while multiplying tile kt from `cur`
+  auto iter = [&](int kt, const char* cur, char* nxt) __attribute__((always_inline)) {
+    if (kt + 1 < n_kt) stage(kt + 1, nxt);
+    subtile(kt * C::BN, cur, cur + C::KBYTES);
     wait_vmem();
     __syncthreads();
   };
@@ -305,7 +308,8 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            hipStream_t stream) {
   const int G = hq / hkv;
   const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
-  const int rows = 128 / hpw;
+  const int nw = (d == 128) ? 8 : 4;              // waves per workgroup (one K/V tile for all of them)
+  const int rows = 32 * nw / hpw;
   Plan plan = plan_any;
   plan.pref = pref_base + pref_slot(rows) * (plan.n_docs + 1);
   const int n_hb = hq / hpw;
@@ -319,19 +323,19 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   const __bf16* K = (const __bf16*)k;
   const __bf16* V = (const __bf16*)v;
   __bf16* O = (__bf16*)o;
-#define CFA_FWD_LAUNCH(DD, HH)                                                                         \
-  do {                                                                                                 \
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DD, HH>), dim3((unsigned)grid), dim3(256), 0, stream, Q, K, V, \
-                       O, lse, plan, total_tokens, hq, hkv, n_hb, sl2, causal);                        \
+#define CFA_FWD_LAUNCH(DD, HH, NN)                                                                         \
+  do {                                                                                                     \
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DD, HH, NN>), dim3((unsigned)grid), dim3(64 * NN), 0, stream, Q, K, \
+                       V, O, lse, plan, total_tokens, hq, hkv, n_hb, sl2, causal);                         \
   } while (0)
   if (d == 128) {
-    if (hpw == 4) CFA_FWD_LAUNCH(128, 4);
-    else if (hpw == 2) CFA_FWD_LAUNCH(128, 2);
-    else CFA_FWD_LAUNCH(128, 1);
+    if (hpw == 4) CFA_FWD_LAUNCH(128, 4, 8);
+    else if (hpw == 2) CFA_FWD_LAUNCH(128, 2, 8);
+    else CFA_FWD_LAUNCH(128, 1, 8);
   } else {
-    if (hpw == 4) CFA_FWD_LAUNCH(64, 4);
-    else if (hpw == 2) CFA_FWD_LAUNCH(64, 2);
-    else CFA_FWD_LAUNCH(64, 1);
+    if (hpw == 4) CFA_FWD_LAUNCH(64, 4, 4);
+    else if (hpw == 2) CFA_FWD_LAUNCH(64, 2, 4);
+    else CFA_FWD_LAUNCH(64, 1, 4);
   }
 #undef CFA_FWD_LAUNCH
   return hipGetLastError();

@@ -23,7 +23,7 @@ constexpr float LN2 = 0.6931471805599453f;
 //   header   int[64]              flag (bit0 cu[0]!=0, bit1 decreasing, bit2 cu[n]!=T), spare
 //   docinfo  int2[n_docs]         (first packed row, length) after clamping
 //   order    int[n_docs]          documents sorted by length, longest first
-//   pref     int[3][n_docs+1]     item prefix over `order` for tiles of 32, 64, 128 rows
+//   pref     int[4][n_docs+1]     item prefix over `order` for tiles of 32, 64, 128, 256 rows
 //   padoff   int[n_docs+1]        MX token-block column offsets P_n (document order)
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -34,7 +34,7 @@ struct PlanLayout {
     docinfo = align256(header + 64 * sizeof(int));
     order = align256(docinfo + size_t(n_docs) * 2 * sizeof(int));
     pref = align256(order + size_t(n_docs) * sizeof(int));
-    padoff = align256(pref + 3 * size_t(n_docs + 1) * sizeof(int));
+    padoff = align256(pref + 4 * size_t(n_docs + 1) * sizeof(int));
     end = align256(padoff + size_t(n_docs + 1) * sizeof(int));
   }
 };
@@ -46,7 +46,9 @@ struct Plan {
   int n_docs;
 };
 
-__host__ __device__ inline int pref_slot(int tile_rows) { return tile_rows == 32 ? 0 : (tile_rows == 64 ? 1 : 2); }
+__host__ __device__ inline int pref_slot(int tile_rows) {
+  return tile_rows == 32 ? 0 : (tile_rows == 64 ? 1 : (tile_rows == 128 ? 2 : 3));
+}
 
 // Decode work item p (0-based position in the longest-first list) into a document and a tile.
 // Returns false when p is past the end of the list (the grid is sized by an upper bound).
@@ -193,17 +195,26 @@ __device__ inline int kd_swz(int r) { return (r >> 1) & 7; }
 __device__ inline int vt_swz(int r) { return (r >> 2) & 3; }
 
 __device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector-memory operations of this wave are outstanding (the N most recent
+// may still be in flight).
+template <int N>
+__device__ inline void wait_vmem_keep() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// Workgroup barrier after this wave's LDS operations have completed, without the fence of
+// __syncthreads (which would also wait for every outstanding global -> LDS copy). Used where
+// the caller has already waited for the copies that the other waves are about to read.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Stage ROWS rows of 128 bf16 (256 bytes) into a SwzTile<128> LDS tile with direct loads.
-// Called by 4 waves; wave w copies the 1 KB blocks [w·ROWS/16, (w+1)·ROWS/16), block I
+// Called by NW waves; wave w copies the 1 KB blocks [w·ROWS/(4·NW), (w+1)·ROWS/(4·NW)), block I
 // holding rows 4I..4I+3. Lane i fills physical chunk i%16 of row 4I + i/16, i.e. logical chunk
 // (i%16) ^ f(row): the swizzle is applied on the global side. Tile row r is read from
 // base + min(r, rmax)·stride: `base` is wave-uniform (the tile's first row), so each copy is a
 // scalar base plus a 32-bit lane offset; rows past rmax repeat row rmax.
-template <int ROWS>
+template <int ROWS, int NW = 4>
 __device__ inline void stage_rows_lds(char* tile, const char* base, uint32_t stride, int rmax, int wave, int lane) {
-  static_assert(ROWS % 16 == 0, "4 waves × 4 rows per block");
-  constexpr int PER_WAVE = ROWS / 16;
+  static_assert(ROWS % (4 * NW) == 0, "NW waves × 4 rows per block");
+  constexpr int PER_WAVE = ROWS / (4 * NW);
 #pragma unroll
   for (int j = 0; j < PER_WAVE; ++j) {
     const int I = wave * PER_WAVE + j;
