@@ -77,8 +77,8 @@ __device__ inline int fit_exp(float amax) {
 // Exponents of the two 32-element contraction blocks held by a lane pair (l, l^32).
 __device__ inline void block_exps(const f32x16& x0, const f32x16& x1, int& e0, int& e1) {
   float a0 = amax16(x0), a1 = amax16(x1);
-  a0 = fmaxf(a0, __shfl_xor(a0, 32));
-  a1 = fmaxf(a1, __shfl_xor(a1, 32));
+  a0 = wave_max_xor32(a0);
+  a1 = wave_max_xor32(a1);
   e0 = fit_exp(a0);
   e1 = fit_exp(a1);
 }
@@ -98,7 +98,7 @@ struct Fp8Pair {
 // that supplies block b's scale (half == b), the two scale bytes.
 __device__ inline void encode_two_term_block(f32x16& x, int b, int half, Fp8Pair& r) {
   float a = amax16(x);
-  a = fmaxf(a, __shfl_xor(a, 32));
+  a = wave_max_xor32(a);
   const int e = fit_exp(a);
   const i32x4 h4 = encode16(x, e);
   residual16(x, h4, e);
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
       xw[(pair * 4 + 2 * qb + 1) * 64 + lane] = pw[2 * qb + 1];
       if (!diag) {                              // MX block of 32 queries: exponent over the lane pair
         float a = amax16(x);
-        a = fmaxf(a, __shfl_xor(a, 32));
+        a = wave_max_xor32(a);
         const int e = fit_exp(a);
         const i32x4 c = encode16(x, e);
 #pragma unroll

@@ -230,7 +230,23 @@ __device__ inline bf16x8 as_bf16x8(const i32x4& u) { return __builtin_bit_cast(b
 // every use here (probabilities and rescale factors next to a row sum of at least 1).
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ inline float wave_max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ inline float wave_sum_xor32(float x) { return x + __shfl_xor(x, 32); }
+// Reductions over the lane pair (l, l ^ 32) with one v_permlane32_swap (no LDS round trip).
+// With x in both operands, the first result holds, in the upper half-wave, the lower half's
+// values (the lower half keeps its own) and the second result the converse, so the pair
+// maximum / sum is one operation on the two results in every lane; addition being commutative,
+// both lanes of a pair get the identical sum.
+__device__ inline f32x2 pair_swap32(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return f32x2{__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1])};
+}
+__device__ inline float wave_max_xor32(float x) {
+  const f32x2 r = pair_swap32(x);
+  return fmaxf(r.x, r.y);
+}
+__device__ inline float wave_sum_xor32(float x) {
+  const f32x2 r = pair_swap32(x);
+  return r.x + r.y;
+}
 
 }  // namespace cfa
