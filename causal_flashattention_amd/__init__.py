@@ -100,10 +100,15 @@ def attn_fwd(q, k, v, cu_seqlens, *, scale=None, causal=True, cu_seqlens_host=No
 
 
 def attn_bwd(q, k, v, o, lse, dout, cu_seqlens, *, scale=None, causal=True, cu_seqlens_host=None,
-             max_seqlen=0, mx=False, saved=None, dq=None, dk=None, dv=None, workspace=None):
-    """Backward pass. Returns (dq, dk, dv) with the layouts and dtype of (q, k, v)."""
+             max_seqlen=0, mx=False, saved=None, dlse=None, dq=None, dk=None, dv=None, workspace=None):
+    """Backward pass. Returns (dq, dk, dv) with the layouts and dtype of (q, k, v).
+
+    ``dlse`` (float32 ``[hq, T]``, optional) is the gradient flowing into the forward's lse.
+    """
     L = _lib.lib()
-    _check_dev(q, k, v, o, lse, dout, cu_seqlens, saved)
+    _check_dev(q, k, v, o, lse, dout, cu_seqlens, saved, dlse)
+    if dlse is not None and (dlse.dtype != torch.float32 or dlse.shape != lse.shape):
+        raise ValueError("dlse must be float32 with the shape of lse")
     T, hq, d = q.shape
     hkv = k.shape[1]
     n_docs = cu_seqlens.numel() - 1
@@ -117,7 +122,7 @@ def attn_bwd(q, k, v, o, lse, dout, cu_seqlens, *, scale=None, causal=True, cu_s
         workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device)
     hcu = _host_cu(cu_seqlens, cu_seqlens_host)
     _lib.check(L.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
-                          _ptr(saved) if saved is not None else None, _ptr(dq), _ptr(dk), _ptr(dv),
+                          _ptr(dlse) if dlse is not None else None, _ptr(saved) if saved is not None else None, _ptr(dq), _ptr(dk), _ptr(dv),
                           _ptr(cu_seqlens), _ptr(hcu) if hcu is not None else None, n_docs, T,
                           int(max_seqlen), hq, hkv, d, scale, int(bool(causal)), dt, _ptr(workspace),
                           workspace.numel(), _stream()))

@@ -22,7 +22,7 @@ SIGNATURES = {
     "cfa_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I]),
     "cfa_saved_bytes": (_S, [_I, _I, _I, _I, _I, _I]),
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P, _S, _P]),
-    "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I,
+    "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I,
                       _P, _S, _P]),
     "mx_quantize": (_I, [_P, _I, _I, _I, _P, _P, _I, _I, _P, _P, _I, _P, _S, _P]),
     "mx_padded_tokens": (_I, [_I, _I]),

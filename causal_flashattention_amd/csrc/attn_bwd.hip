@@ -5,7 +5,7 @@
 // derivative of the forward definition ("GPT Kernel Programlama" §2-§6), recomputing the
 // probabilities tile by tile from the saved row log-sum-exp instead of storing P:
 //   P_ij  = exp(scale·q_i·k_j − LSE_i)           (0 where key j is masked)
-//   D_i   = Σ_r dO_ir O_ir                        -- bwd_pre_kernel
+//   D_i   = Σ_r dO_ir O_ir − dLSE_i               -- bwd_pre_kernel (dLSE optional, else 0)
 //   dP_ij = dO_i·v_j,  dS_ij = P_ij (dP_ij − D_i)
 //   dV_j  = Σ_{h in group} Σ_i P_ij dO_i           -- attn_bwd_dkdv_kernel
 //   dK_j  = scale Σ_{h in group} Σ_i dS_ij q_i     -- attn_bwd_dkdv_kernel
@@ -28,11 +28,14 @@
 
 namespace cfa {
 
-// ------------------------------------------------------------------ D = rowsum(dO ∘ O)
-// 16 lanes per (token, head) row of 128 (8 lanes for d = 64), 16 bytes per lane.
+// ------------------------------------------------------------------ D = rowsum(dO ∘ O) − dLSE
+// 16 lanes per (token, head) row of 128 (8 lanes for d = 64), 16 bytes per lane. A gradient
+// dLSE_i flowing into the row log-sum-exp adds P_ij·dLSE_i to dS_ij (∂LSE_i/∂S_ij = P_ij), which
+// is the same as lowering D_i by dLSE_i.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
-                                                      float* __restrict__ delta, int total_tokens, int hq) {
+                                                      const float* __restrict__ dlse, float* __restrict__ delta,
+                                                      int total_tokens, int hq) {
   constexpr int LPR = D / 8;  // lanes per row
   const long row = (long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
   const int sub = threadIdx.x % LPR;
@@ -49,7 +52,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
   for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
   if (row < rows && sub == 0) {
     const int t = (int)(row / hq), h = (int)(row % hq);
-    delta[(size_t)h * total_tokens + t] = acc;
+    const size_t i = (size_t)h * total_tokens + t;
+    delta[i] = dlse ? acc - dlse[i] : acc;
   }
 }
 
@@ -668,18 +672,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 }
 
 // ------------------------------------------------------------------ launchers
-hipError_t launch_bwd_pre(const void* o, const void* dout, float* delta, int total_tokens, int hq, int d,
-                          hipStream_t stream) {
+hipError_t launch_bwd_pre(const void* o, const void* dout, const float* dlse, float* delta, int total_tokens, int hq,
+                          int d, hipStream_t stream) {
   const long rows = (long)total_tokens * hq;
   if (rows == 0) return hipSuccess;
   const int rpb = 256 / (d / 8);
   const long grid = (rows + rpb - 1) / rpb;
   if (d == 128)
     hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)o,
-                       (const __bf16*)dout, delta, total_tokens, hq);
+                       (const __bf16*)dout, dlse, delta, total_tokens, hq);
   else
     hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)o,
-                       (const __bf16*)dout, delta, total_tokens, hq);
+                       (const __bf16*)dout, dlse, delta, total_tokens, hq);
   return hipGetLastError();
 }
 

@@ -253,7 +253,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, c
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-             const void* saved, void* dq, void* dk, void* dv, const int32_t* cu_seqlens,
+             const float* dlse, const void* saved, void* dq, void* dk, void* dv, const int32_t* cu_seqlens,
              const int32_t* cu_seqlens_host, int n_docs, int total_tokens, int max_seqlen, int hq, int hkv, int d,
              float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
@@ -265,8 +265,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   if (!(std::isfinite(scale) && scale > 0.f)) return fail(CFA_ERR_SHAPE, "scale must be finite and > 0");
   if (dtype == CFA_MXFP8 && !saved) return fail(CFA_ERR_NULL, "MXFP8 needs the forward's `saved` buffer");
   if (dtype == CFA_MXFP8 && !aligned(saved, 256)) return fail(CFA_ERR_ALIGN, "saved must be 256-byte aligned");
-  for (const void* p : {q, k, v, o, (const void*)lse, dout, (const void*)dq, (const void*)dk, (const void*)dv,
-                        (const void*)cu_seqlens})
+  for (const void* p : {q, k, v, o, (const void*)lse, dout, (const void*)dlse, (const void*)dq, (const void*)dk,
+                        (const void*)dv, (const void*)cu_seqlens})
     if (!aligned(p, 16)) return fail(CFA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
   if (!aligned(workspace, 256)) return fail(CFA_ERR_ALIGN, "workspace must be 256-byte aligned");
   const WsLayout wl = ws_layout(1, s);
@@ -280,7 +280,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   const cfa::Plan plan = make_plan(workspace, n_docs);
   float* delta = (float*)((char*)workspace + wl.delta);
   mark(0, 0, st);
-  if (int r = check_hip(cfa::launch_bwd_pre(o, dout, delta, total_tokens, hq, d, st), "bwd preprocess")) return r;
+  if (int r = check_hip(cfa::launch_bwd_pre(o, dout, dlse, delta, total_tokens, hq, d, st), "bwd preprocess")) return r;
   mark(0, 1, st);
   if (dtype == CFA_MXFP8) {
     char* ws = (char*)workspace;

@@ -22,8 +22,8 @@ hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, 
                           const int* pref_base, int total_tokens, int hq, int hkv, int d, float scale, int causal,
                           hipStream_t stream);
 
-hipError_t launch_bwd_pre(const void* o, const void* dout, float* delta, int total_tokens, int hq, int d,
-                          hipStream_t stream);
+hipError_t launch_bwd_pre(const void* o, const void* dout, const float* dlse, float* delta, int total_tokens, int hq,
+                          int d, hipStream_t stream);
 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                            const float* delta, void* dk, void* dv, const Plan& plan, const int* pref_base, int T,

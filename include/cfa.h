@@ -96,13 +96,17 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Backward pass: dq, dk, dv (same layouts and element type as q, k, v) from q, k, v, the
- * forward's o and lse, and the upstream gradient dout. The gradient is that of O only (no
- * gradient flows into lse). dtype CFA_BF16 or CFA_MXFP8 (CFA_F32 is forward-only).
+ * forward's o and lse, and the upstream gradients dout (of O) and dlse (of LSE). dtype CFA_BF16
+ * or CFA_MXFP8 (CFA_F32 is forward-only).
+ *   dlse  : float32 [hq, total_tokens] like lse, or NULL for no gradient into lse. The pages do
+ *           not name it; it is the exact derivative of the lse output the forward returns:
+ *           d lse_i / d S_ij = P_ij, so it enters as dS_ij = P_ij (dP_ij - (D_i - dlse_i)) with
+ *           D_i = sum_r dout_ir o_ir. Shares the 16-byte alignment rule.
  *   saved : CFA_MXFP8: the buffer attn_fwd filled, unmodified; otherwise NULL.
  * Deterministic: two calls on the same inputs give bit-identical outputs.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-             const void* dout, const void* saved, void* dq, void* dk, void* dv,
+             const void* dout, const float* dlse, const void* saved, void* dq, void* dk, void* dv,
              const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
              int n_docs, int total_tokens, int max_seqlen, int hq, int hkv, int d,
              float scale, int causal, int dtype,

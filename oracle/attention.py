@@ -88,8 +88,8 @@ def attn_fwd(q, k, v, cu_seqlens, scale, causal=True, row_block=ROW_BLOCK):
     return o, lse
 
 
-def attn_bwd(q, k, v, do, cu_seqlens, scale, causal=True, row_block=ROW_BLOCK):
-    """Exact gradient of ``attn_fwd`` for an upstream gradient ``do`` (no LSE gradient).
+def attn_bwd(q, k, v, do, cu_seqlens, scale, causal=True, row_block=ROW_BLOCK, dlse=None):
+    """Exact gradient of ``attn_fwd`` for upstream gradients ``do`` (of O) and ``dlse`` (of LSE).
 
     The pages only name the backward pass (FLAMIA page, "FLAMIA Mimarisi ve Temel Tasarım
     İlkeleri": forward and backward must agree numerically); these are the derivatives of the
@@ -97,16 +97,20 @@ def attn_bwd(q, k, v, do, cu_seqlens, scale, causal=True, row_block=ROW_BLOCK):
 
         D_i    = Σ_r dO[i,r]·O[i,r]
         dP_ij  = Σ_r dO[i,r]·V[j,r]
-        dS_ij  = P_ij·(dP_ij − D_i)
+        dS_ij  = P_ij·(dP_ij − D_i) + P_ij·dLSE_i
         dQ[i]  = scale·Σ_j dS_ij·K[j]
         dK[j]  = scale·Σ_{h in group} Σ_i dS_ij·Q[i]
         dV[j]  = Σ_{h in group} Σ_i P_ij·dO[i]
 
+    The dLSE term is the derivative of LSE_i = log Σ_j exp(S_ij), which is P_ij (the pages do
+    not name an LSE gradient; ``dlse [hq, T]`` defaults to zero).
     Returns ``dq [T, hq, d]``, ``dk, dv [T, hkv, d]``.
     """
     q, k, v, cu, T, hq, hkv, d = _check(q, k, v, cu_seqlens)
     do = np.asarray(do, dtype=np.float64)
     assert do.shape == q.shape
+    dlse = np.zeros((hq, T)) if dlse is None else np.asarray(dlse, dtype=np.float64)
+    assert dlse.shape == (hq, T)
     group = hq // hkv
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
@@ -128,7 +132,7 @@ def attn_bwd(q, k, v, do, cu_seqlens, scale, causal=True, row_block=ROW_BLOCK):
                 ob = p @ vd
                 D = np.sum(dob * ob, axis=1)
                 dp = dob @ vd.T
-                ds = p * (dp - D[:, None])
+                ds = p * (dp - D[:, None]) + p * dlse[h, s0 + r0:s0 + r1][:, None]
                 dq[s0 + r0:s0 + r1, h, :] = scale * (ds @ kd)
                 dk[s0:s1, g, :] += scale * (ds.T @ qb)
                 dv[s0:s1, g, :] += p.T @ dob

@@ -22,7 +22,7 @@ Computed exactly in float64 from the decoded copies (the decoding is exact):
     S_ij  = scale·Q_d[i]·K_d[j]                        P = softmax(S + mask) (two-pass)
     O[i]  = Σ_j P_ij·(diag ? V_b[j] : V_t[j])           LSE_i = max + ln(sum)
     dP_ij = dO_d[i]·V_d[j]                              D_i = dO_b[i]·O[i]
-    dS_ij = P_ij·(dP_ij − D_i)
+    dS_ij = P_ij·(dP_ij − D_i) + P_ij·dLSE_i             (dLSE optional, else 0)
     dV[j] = Σ_{h in group} Σ_i P_ij·(diag ? dO_b[i] : dO_t[i])
     dQ[i] = scale·Σ_j dS_ij·(diag ? K_b[j] : K_t[j])
     dK[j] = scale·Σ_{h in group} Σ_i dS_ij·(diag ? Q_b[i] : Q_t[i])
@@ -88,7 +88,7 @@ def attn_mx_fwd(q_b, k_b, v_b, cu_seqlens, scale, causal=True, tile=DIAG_TILE,
 
 
 def attn_mx_bwd(q_b, k_b, v_b, do_b, cu_seqlens, scale, causal=True, tile=DIAG_TILE,
-                row_block=_att.ROW_BLOCK):
+                row_block=_att.ROW_BLOCK, dlse=None):
     """Backward with MX operands; returns dq [T, hq, d], dk, dv [T, hkv, d] (float64)."""
     q_b = np.asarray(q_b, np.float64)
     k_b = np.asarray(k_b, np.float64)
@@ -102,6 +102,7 @@ def attn_mx_bwd(q_b, k_b, v_b, do_b, cu_seqlens, scale, causal=True, tile=DIAG_T
     k_d, k_t = operand_copies(k_b, cu)
     v_d, v_t = operand_copies(v_b, cu)
     do_d, do_t = operand_copies(do_b, cu)
+    dlse = np.zeros((hq, T)) if dlse is None else np.asarray(dlse, np.float64)
     dq = np.zeros((T, hq, d))
     dk = np.zeros((T, hkv, d))
     dv = np.zeros((T, hkv, d))
@@ -121,7 +122,7 @@ def attn_mx_bwd(q_b, k_b, v_b, do_b, cu_seqlens, scale, causal=True, tile=DIAG_T
                 o = p_diag @ v_b[s0:s1, g] + p_off @ v_t[s0:s1, g]
                 D = np.sum(do_b[rows, h] * o, axis=1)
                 dp = do_d[rows, h] @ v_d[s0:s1, g].T
-                ds = p * (dp - D[:, None])
+                ds = p * (dp - D[:, None]) + p * dlse[h, rows][:, None]
                 ds_diag, ds_off = np.where(dg, ds, 0.0), np.where(dg, 0.0, ds)
                 dv[s0:s1, g] += p_diag.T @ do_b[rows, h] + p_off.T @ do_t[rows, h]
                 dq[rows, h] = scale * (ds_diag @ k_b[s0:s1, g] + ds_off @ k_t[s0:s1, g])

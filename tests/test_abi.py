@@ -81,14 +81,17 @@ def test_fwd_rejects_bad_host_cu():
 def test_bwd_rejects():
     L = _lib.lib()
     cu_h = np.array([0, 100], dtype=np.int32)
-    args = [FAKE] * 10 + [FAKE, cu_h.ctypes.data, 1, 100, 0, 4, 2, 128, 0.088, 1, 1, FAKE, 1 << 30, None]
-    bad = list(args); bad[6] = None                      # saved may be NULL for bf16: not an error by itself
-    bad[7] = None                                        # dq NULL
+    args = [FAKE] * 6 + [None] + [FAKE] * 4 + [FAKE, cu_h.ctypes.data, 1, 100, 0, 4, 2, 128, 0.088, 1, 1, FAKE,
+                                                1 << 30, None]   # dlse (index 6) may be NULL
+    bad = list(args); bad[7] = None                      # saved may be NULL for bf16: not an error by itself
+    bad[8] = None                                        # dq NULL
     assert L.attn_bwd(*bad) == 1
-    bad = list(args); bad[20] = 0                        # dtype fp32 is forward-only
+    bad = list(args); bad[21] = 0                        # dtype fp32 is forward-only
     assert L.attn_bwd(*bad) == 3
-    bad = list(args); bad[22] = 8                        # workspace too small
+    bad = list(args); bad[23] = 8                        # workspace too small
     assert L.attn_bwd(*bad) == 5
+    bad = list(args); bad[6] = FAKE + 4                  # a misaligned dlse
+    assert L.attn_bwd(*bad) == 4
 
 
 def test_mx_quantize_rejects():

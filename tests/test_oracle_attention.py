@@ -181,6 +181,44 @@ def test_finite_differences():
         assert rel < 1e-6, (name, rel)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_finite_differences_with_lse_gradient(causal):
+    """Loss Σ O·dO + Σ LSE·dLSE: the oracle backward with ``dlse`` against central differences."""
+    lengths = [2, 4, 3]
+    hq, hkv, d = 2, 1, 3
+    q, k, v, do, cu = _rand_case(lengths, hq, hkv, d, seed=11)
+    dlse = np.random.default_rng(12).standard_normal((hq, sum(lengths)))
+    sc = 0.7
+    dq, dk, dv = att.attn_bwd(q, k, v, do, cu, sc, causal=causal, dlse=dlse)
+    eps = 1e-6
+
+    def loss(args):
+        o, lse = att.attn_fwd(args["q"], args["k"], args["v"], cu, sc, causal=causal)
+        return float(np.sum(o * do) + np.sum(lse * dlse))
+
+    for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            a1 = arr.copy(); a1[idx] += eps
+            a2 = arr.copy(); a2[idx] -= eps
+            base = {"q": q, "k": k, "v": v}
+            num[idx] = (loss({**base, name: a1}) - loss({**base, name: a2})) / (2 * eps)
+        rel = np.linalg.norm(num - grad) / max(np.linalg.norm(grad), 1e-30)
+        assert rel < 1e-6, (name, rel)
+
+
+def test_lse_gradient_closed_form_single_tokens():
+    """One-token documents: LSE = scale·q·k, so dQ = scale·dLSE·k, dK = scale·Σ_h dLSE·q, dV = 0."""
+    lengths = [1, 1, 1, 1]
+    q, k, v, _, cu = _rand_case(lengths, 2, 1, 5, seed=13)
+    do = np.zeros_like(q)
+    dlse = np.random.default_rng(14).standard_normal((2, 4))
+    dq, dk, dv = att.attn_bwd(q, k, v, do, cu, 0.3, dlse=dlse)
+    np.testing.assert_allclose(dq, 0.3 * dlse.T[:, :, None] * k, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(dk[:, 0], 0.3 * np.einsum("th,thd->td", dlse.T, q), rtol=1e-13, atol=1e-15)
+    assert not np.any(dv)
+
+
 def test_gradient_closed_forms_q_zero():
     lengths = [6, 11]
     q, k, v, do, cu = _rand_case(lengths, 2, 2, 8, seed=8)

@@ -43,6 +43,14 @@ def test_transparent_inputs_reduce_to_plain_oracle():
     g0 = att.attn_bwd(q, k, v, do, cu, sc)
     for a, b in zip(g, g0):
         np.testing.assert_allclose(a, b, rtol=0, atol=1e-11 * np.abs(b).max())
+    dlse = np.random.default_rng(5).standard_normal((4, sum(lengths)))
+    g = mxa.attn_mx_bwd(q, k, v, do, cu, sc, dlse=dlse)
+    g1 = att.attn_bwd(q, k, v, do, cu, sc, dlse=dlse)
+    for a, b in zip(g, g1):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-11 * np.abs(b).max())
+    for b, c in zip(g1[:2], g0[:2]):                              # dQ, dK move; dV does not
+        assert np.abs(b - c).max() > 1e-3 * np.abs(c).max()
+    assert np.array_equal(g1[2], g0[2])
 
 
 def test_causality_bit_exact_under_mx():
