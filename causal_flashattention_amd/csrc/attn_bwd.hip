@@ -284,8 +284,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
   }
 }
 
-// ------------------------------------------------------------------ dK / dV, d = 128, wave pairs
-// 8 waves own 128 keys of one kv head, as 4 pairs of 32 keys. In a pair, the "P wave" (w < 4)
+// ------------------------------------------------------------------ dK / dV, d = 128 / 256, wave pairs
+// 2·NP waves own 32·NP keys of one kv head, as NP pairs of 32 keys (d = 128: 4 pairs, two waves
+// per SIMD; d = 256: 2 pairs, one wave per SIMD with twice the registers). In a pair, the "P wave" (w < 4)
 // holds K and computes S = Q Kᵀ, P = exp(S − LSE), dVᵀ += dOᵀ P; the "dS wave" (w + 4) holds V
 // and computes dP = dO Vᵀ, dS = P (dP − D), dKᵀ += Qᵀ dS with the fp32 P that its partner left
 // in LDS one step earlier. Running the dS wave one step behind removes every wait between the
@@ -295,17 +296,20 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
 // register file. Staging buffers: step i (Q, dO tiles, LSE·log2 e, D) lives in buffer i mod 3
 // and P of step i in exchange buffer i mod 3, so the loop is unrolled three times and every
 // buffer is a distinct static array (no aliasing between the copies in flight and the reads).
-__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(
+template <int D, int NP>
+__global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     __bf16* __restrict__ dk, __bf16* __restrict__ dv, Plan plan, int total_tokens, int hq, int hkv,
     float scale, int causal) {
-  constexpr int D = 128;
   using C = BwdTile<D>;
+  constexpr int KT = 32 * NP;                     // keys per workgroup
   constexpr int BM = 32;                          // queries per step
-  constexpr int TILE = BM * C::RSTR;              // 8 KB
+  constexpr int TILE = BM * C::RSTR;              // 8 KB (d = 256: 16 KB)
   constexpr int STAGE = 2 * TILE + 2 * BM * 4;    // Q, dO, LSE·log2 e, D
-  constexpr int XP = 4 * 4 * 64;                  // f32x4 per exchange buffer: [pair][j/4][lane]
+  constexpr int XP = NP * 4 * 64;                 // f32x4 per exchange buffer: [pair][j/4][lane]
+  constexpr int SB = D == 256 ? 4 : C::DS;        // k-steps per operand batch
+  constexpr int DBC = D == 256 ? 4 : C::DB;       // d blocks per transposed-read batch
   __shared__ __attribute__((aligned(16))) char st_a[STAGE];
   __shared__ __attribute__((aligned(16))) char st_b[STAGE];
   __shared__ __attribute__((aligned(16))) char st_c[STAGE];
@@ -315,12 +319,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(
 
   const int p = blockIdx.x / hkv, g = blockIdx.x % hkv;
   int s0, L, t;
-  if (!decode_item(plan, p, 128, false, s0, L, t)) return;
+  if (!decode_item(plan, p, KT, false, s0, L, t)) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5;
-  const int pair = w & 3;
-  const bool ds_wave = w >= 4;
+  const int pair = w % NP;
+  const bool ds_wave = w >= NP;
   const int G = hq / hkv;
-  const int kw0 = t * 128 + 32 * pair;            // first doc-local key of this pair
+  const int kw0 = t * KT + 32 * pair;             // first doc-local key of this pair
   const int mykey = kw0 + (lane & 31);
   const float sl2 = scale * LOG2E;
   const SwzOffsets<D> so(lane);
@@ -339,7 +343,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(
 #pragma unroll
   for (int b = 0; b < C::DB; ++b) acc[b] = f32x16{};
 
-  const int q_begin = causal ? t * 128 : 0;
+  const int q_begin = causal ? t * KT : 0;
   const int n_qt = (L - q_begin + BM - 1) / BM;
   const int n_steps = n_qt * G;
   const int wave_first_q = causal ? kw0 : 0;
@@ -352,8 +356,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(
     const int h = g * G + st / n_qt;
     const int q0 = q_begin + (st % n_qt) * BM;
     const __bf16* src = ds_wave ? dout : q;
-    stage_rows_lds<BM>(buf + (ds_wave ? TILE : 0), (const char*)(src + ((size_t)(s0 + q0) * hq + h) * D),
-                       (uint32_t)hq * D * 2, L - 1 - q0, pair, lane);
+    stage_rows_lds<BM, NP, D>(buf + (ds_wave ? TILE : 0), (const char*)(src + ((size_t)(s0 + q0) * hq + h) * D),
+                              (uint32_t)hq * D * 2, L - 1 - q0, pair, lane);
     if (threadIdx.x < BM) {
       const size_t li = (size_t)h * total_tokens + s0 + min(q0 + (int)threadIdx.x, L - 1);
       lreg = lse[li];
@@ -377,18 +381,23 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(
     const int q0 = q_begin + (st % n_qt) * BM;
     const char* ob = buf + TILE;
     const f32x4* l2 = (const f32x4*)(buf + 2 * TILE);
-    i32x4 fq[C::DS];
-#pragma unroll
-    for (int s = 0; s < C::DS; ++s) fq[s] = *(const i32x4*)(buf + so.row[s]);
     f32x16 sacc = f32x16{};
 #pragma unroll
-    for (int s = 0; s < C::DS; ++s) sacc = mfma32(as_bf16x8(fq[s]), kv[s], sacc);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    for (int sc = 0; sc < C::DS; sc += SB) {
+      i32x4 fq[SB];
+#pragma unroll
+      for (int s = 0; s < SB; ++s) fq[s] = *(const i32x4*)(buf + so.row[sc + s]);
+#pragma unroll
+      for (int s = 0; s < SB; ++s) sacc = mfma32(as_bf16x8(fq[s]), kv[sc + s], sacc);
+      if constexpr (D == 128) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+      }
+    }
     // masked scores -> -inf (wave-uniform branch: only steps that cross the diagonal or the
     // document end), so P = 2^(s·c − LSE·log2 e) is exactly 0 there
     if ((causal && q0 < kw0 + 31) || q0 + BM > L) {
@@ -414,12 +423,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int rb = 16 * kk * C::RSTR;
-      bf16x8 ao[C::DB];
 #pragma unroll
-      for (int dbk = 0; dbk < C::DB; ++dbk)
-        ao[dbk] = concat_tr(lds_read_tr16(ob + rb + so.tr0[dbk]), lds_read_tr16(ob + rb + so.tr1[dbk]));
+      for (int dc = 0; dc < C::DB; dc += DBC) {
+        bf16x8 ao[DBC];
 #pragma unroll
-      for (int dbk = 0; dbk < C::DB; ++dbk) acc[dbk] = mfma32(ao[dbk], pf[kk], acc[dbk]);
+        for (int i = 0; i < DBC; ++i)
+          ao[i] = concat_tr(lds_read_tr16(ob + rb + so.tr0[dc + i]), lds_read_tr16(ob + rb + so.tr1[dc + i]));
+#pragma unroll
+        for (int i = 0; i < DBC; ++i) acc[dc + i] = mfma32(ao[i], pf[kk], acc[dc + i]);
+      }
     }
   };
 
@@ -427,18 +439,23 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(
   auto step_ds = [&](int st, const char* buf, const f32x4* xr) __attribute__((always_inline)) {
     const char* ob = buf + TILE;
     const f32x4* db = (const f32x4*)(buf + 2 * TILE + BM * 4);
-    i32x4 fo[C::DS];
-#pragma unroll
-    for (int s = 0; s < C::DS; ++s) fo[s] = *(const i32x4*)(ob + so.row[s]);
     f32x16 pacc = f32x16{};
 #pragma unroll
-    for (int s = 0; s < C::DS; ++s) pacc = mfma32(as_bf16x8(fo[s]), kv[s], pacc);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    for (int sc = 0; sc < C::DS; sc += SB) {
+      i32x4 fo[SB];
+#pragma unroll
+      for (int s = 0; s < SB; ++s) fo[s] = *(const i32x4*)(ob + so.row[sc + s]);
+#pragma unroll
+      for (int s = 0; s < SB; ++s) pacc = mfma32(as_bf16x8(fo[s]), kv[sc + s], pacc);
+      if constexpr (D == 128) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+      }
+    }
     bf16x8 sf[2];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
@@ -455,12 +472,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int rb = 16 * kk * C::RSTR;
-      bf16x8 aq[C::DB];
 #pragma unroll
-      for (int dbk = 0; dbk < C::DB; ++dbk)
-        aq[dbk] = concat_tr(lds_read_tr16(buf + rb + so.tr0[dbk]), lds_read_tr16(buf + rb + so.tr1[dbk]));
+      for (int dc = 0; dc < C::DB; dc += DBC) {
+        bf16x8 aq[DBC];
 #pragma unroll
-      for (int dbk = 0; dbk < C::DB; ++dbk) acc[dbk] = mfma32(aq[dbk], sf[kk], acc[dbk]);
+        for (int i = 0; i < DBC; ++i)
+          aq[i] = concat_tr(lds_read_tr16(buf + rb + so.tr0[dc + i]), lds_read_tr16(buf + rb + so.tr1[dc + i]));
+#pragma unroll
+        for (int i = 0; i < DBC; ++i) acc[dc + i] = mfma32(aq[i], sf[kk], acc[dc + i]);
+      }
     }
   };
 
@@ -509,7 +529,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(
 
 // ------------------------------------------------------------------ dQ
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_bwd_dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     __bf16* __restrict__ dq, Plan plan, int total_tokens, int hq, int hkv, float scale, int causal) {
@@ -519,6 +539,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   constexpr int STAGE = 2 * TILE;
   constexpr int CH = BN * D / 8;
   constexpr int PT = CH / 256;
+  constexpr int SB = D == 256 ? 4 : C::DS;       // k-steps per operand batch
   // two separate buffers so that the compiler sees the copy into one never aliases the other
   __shared__ __attribute__((aligned(16))) char lds_a[STAGE];
   __shared__ __attribute__((aligned(16))) char lds_b[STAGE];
@@ -559,11 +580,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   auto stage = [&](int kt, char* kb) {
     const int k0 = kt * BN;
     char* vb = kb + TILE;
-    if constexpr (D == 128) {
+    if constexpr (D >= 128) {
       const size_t row0 = ((size_t)(s0 + k0) * hkv + g) * D;
       const uint32_t stride = (uint32_t)hkv * D * 2;
-      stage_rows_lds<BN>(kb, (const char*)(k + row0), stride, kv_end - 1 - k0, w, lane);
-      stage_rows_lds<BN>(vb, (const char*)(v + row0), stride, kv_end - 1 - k0, w, lane);
+      stage_rows_lds<BN, 4, D>(kb, (const char*)(k + row0), stride, kv_end - 1 - k0, w, lane);
+      stage_rows_lds<BN, 4, D>(vb, (const char*)(v + row0), stride, kv_end - 1 - k0, w, lane);
     } else {
       i32x4 kreg[PT], vreg[PT];
 #pragma unroll
@@ -593,27 +614,33 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
       bf16x8 sf[4];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        // Sᵀ = K Qᵀ and dPᵀ = V dOᵀ for one 32-key block, operand rows read as a batch
-        i32x4 fk[C::DS], fv[C::DS];
-#pragma unroll
-        for (int s = 0; s < C::DS; ++s) {
-          fk[s] = *(const i32x4*)(kb + b * 32 * C::RSTR + so.row[s]);
-          fv[s] = *(const i32x4*)(vb + b * 32 * C::RSTR + so.row[s]);
-        }
+        // Sᵀ = K Qᵀ and dPᵀ = V dOᵀ for one 32-key block, operand rows read as a batch (d = 256:
+        // four batches of 4 k-steps)
         f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-        for (int s = 0; s < C::DS; ++s) {
-          sacc = mfma32(as_bf16x8(fk[s]), qf[s], sacc);
-          pacc = mfma32(as_bf16x8(fv[s]), of[s], pacc);
-        }
-        // keep ~4 operand reads in flight ahead of the products (occupancy 2 register budget)
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        for (int sc = 0; sc < C::DS; sc += SB) {
+          i32x4 fk[SB], fv[SB];
 #pragma unroll
-        for (int i = 0; i < C::DS - 2; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          for (int s = 0; s < SB; ++s) {
+            fk[s] = *(const i32x4*)(kb + b * 32 * C::RSTR + so.row[sc + s]);
+            fv[s] = *(const i32x4*)(vb + b * 32 * C::RSTR + so.row[sc + s]);
+          }
+#pragma unroll
+          for (int s = 0; s < SB; ++s) {
+            sacc = mfma32(as_bf16x8(fk[s]), qf[sc + s], sacc);
+            pacc = mfma32(as_bf16x8(fv[s]), of[sc + s], pacc);
+          }
+          if constexpr (D <= 128) {
+            // keep ~4 operand reads in flight ahead of the products (occupancy 2 register budget)
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < C::DS - 2; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          }
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         // masked scores -> -inf (wave-uniform branch: diagonal or document-end tiles only),
         // so P = 2^(s·c − LSE·log2 e) is exactly 0 there
         if (need_mask) {
@@ -678,7 +705,10 @@ hipError_t launch_bwd_pre(const void* o, const void* dout, const float* dlse, fl
   if (rows == 0) return hipSuccess;
   const int rpb = 256 / (d / 8);
   const long grid = (rows + rpb - 1) / rpb;
-  if (d == 128)
+  if (d == 256)
+    hipLaunchKernelGGL(bwd_pre_kernel<256>, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)o,
+                       (const __bf16*)dout, dlse, delta, total_tokens, hq);
+  else if (d == 128)
     hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)o,
                        (const __bf16*)dout, dlse, delta, total_tokens, hq);
   else
@@ -689,26 +719,23 @@ hipError_t launch_bwd_pre(const void* o, const void* dout, const float* dlse, fl
 
 template <int D>
 static hipError_t launch_dkdv_d(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                                const float* delta, void* dk, void* dv, const Plan& plan, int T, int hq, int hkv,
-                                float scale, int causal, hipStream_t stream) {
-  const long items = (long)(T + 127) / 128 + plan.n_docs;
-  if constexpr (D == 128) {
-    const long grid = items * hkv;
-    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(attn_bwd_dkdv_pair_kernel, dim3((unsigned)grid), dim3(512), 0, stream, (const __bf16*)q,
-                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, lse, delta, (__bf16*)dk, (__bf16*)dv,
-                       plan, T, hq, hkv, scale, causal);
-    return hipGetLastError();
-  }
-  constexpr int STAGE = BwdTile<D>::DKDV_STAGE;
-  auto kern = attn_bwd_dkdv_kernel<D>;
-  if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE))
-    return hipErrorInvalidConfiguration;
+                                const float* delta, void* dk, void* dv, const Plan& plan_any, const int* pref_base,
+                                int T, int hq, int hkv, float scale, int causal, hipStream_t stream) {
+  constexpr int NP = D == 256 ? 2 : 4;            // wave pairs (d = 64: waves) per workgroup
+  constexpr int KT = D == 256 ? 64 : 128;         // keys per workgroup
+  Plan plan = plan_any;
+  plan.pref = pref_base + pref_slot(KT) * (plan.n_docs + 1);
+  const long items = (long)(T + KT - 1) / KT + plan.n_docs;
   const long grid = items * hkv;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)q, (const __bf16*)k,
-                     (const __bf16*)v, (const __bf16*)dout, lse, delta, (__bf16*)dk, (__bf16*)dv, plan, T, hq, hkv,
-                     scale, causal);
+  if constexpr (D >= 128)
+    hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<D, NP>), dim3((unsigned)grid), dim3(128 * NP), 0, stream,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, lse, delta,
+                       (__bf16*)dk, (__bf16*)dv, plan, T, hq, hkv, scale, causal);
+  else
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)q,
+                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, lse, delta, (__bf16*)dk, (__bf16*)dv,
+                       plan, T, hq, hkv, scale, causal);
   return hipGetLastError();
 }
 
@@ -728,10 +755,11 @@ static hipError_t launch_dq_d(const void* q, const void* k, const void* v, const
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                            const float* delta, void* dk, void* dv, const Plan& plan_any, const int* pref_base, int T,
                            int hq, int hkv, int d, float scale, int causal, hipStream_t stream) {
-  Plan plan = plan_any;
-  plan.pref = pref_base + pref_slot(128) * (plan.n_docs + 1);
-  if (d == 128) return launch_dkdv_d<128>(q, k, v, dout, lse, delta, dk, dv, plan, T, hq, hkv, scale, causal, stream);
-  return launch_dkdv_d<64>(q, k, v, dout, lse, delta, dk, dv, plan, T, hq, hkv, scale, causal, stream);
+  if (d == 128)
+    return launch_dkdv_d<128>(q, k, v, dout, lse, delta, dk, dv, plan_any, pref_base, T, hq, hkv, scale, causal, stream);
+  if (d == 256)
+    return launch_dkdv_d<256>(q, k, v, dout, lse, delta, dk, dv, plan_any, pref_base, T, hq, hkv, scale, causal, stream);
+  return launch_dkdv_d<64>(q, k, v, dout, lse, delta, dk, dv, plan_any, pref_base, T, hq, hkv, scale, causal, stream);
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
@@ -740,6 +768,7 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
   Plan plan = plan_any;
   plan.pref = pref_base + pref_slot(128) * (plan.n_docs + 1);
   if (d == 128) return launch_dq_d<128>(q, k, v, dout, lse, delta, dq, plan, T, hq, hkv, scale, causal, stream);
+  if (d == 256) return launch_dq_d<256>(q, k, v, dout, lse, delta, dq, plan, T, hq, hkv, scale, causal, stream);
   return launch_dq_d<64>(q, k, v, dout, lse, delta, dq, plan, T, hq, hkv, scale, causal, stream);
 }
 

@@ -9,7 +9,8 @@
 // "FlashAttention (HU)" sections "Tiling és blokkos feldolgozás", "Online Softmax-számítás",
 // "Műveletek összevonása egyetlen CUDA-kernelbe".
 //
-// bf16 kernel layout (d = 64 or 128), one workgroup = NW waves of 64 lanes (8 for d = 128, 4 for 64):
+// bf16 kernel layout (d = 64, 128 or 256), one workgroup = NW waves of 64 lanes (8 for d = 128, 4
+// for 64 and 256; d = 256 holds a 128-register Oᵀ accumulator per wave, so one wave per SIMD):
 //  * Each wave owns 32 query rows of one head. HPW heads of one GQA group share a workgroup
 //    (HPW = 1, 2 or 4), so a K/V tile staged in LDS serves 32·NW (row, head) pairs: with 8 waves
 //    each staged byte feeds twice the products of a 4-wave workgroup (one workgroup per CU).
@@ -43,7 +44,7 @@ struct FwdTile {
 constexpr float RESCALE_LOG2 = 8.f;
 
 template <int D, int HPW, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16_kernel(
+__global__ __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, Plan plan, int total_tokens, int hq, int hkv,
     int n_hb, float scale_log2, int causal) {
@@ -88,18 +89,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16_kernel(
   for (int b = 0; b < C::DB; ++b) oacc[b] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // ---- staging of one K/V tile into an LDS buffer: [K rows][V rows]. d = 128: direct global ->
+  // ---- staging of one K/V tile into an LDS buffer: [K rows][V rows]. d >= 128: direct global ->
   // LDS copies shared out among the NW waves (no registers, completion tracked by vmcnt);
   // d = 64: through registers. Keys past kv_end are clamped into the document: they are masked
   // (P = 0).
   auto stage = [&](int kt, char* kb) {
     const int k0 = kt * C::BN;
     char* vb = kb + C::KBYTES;
-    if constexpr (D == 128) {
+    if constexpr (D >= 128) {
       const size_t row0 = ((size_t)(s0 + k0) * hkv + g) * D;
       const uint32_t stride = (uint32_t)hkv * D * 2;
-      stage_rows_lds<C::BN, NW>(kb, (const char*)(k + row0), stride, kv_end - 1 - k0, w, lane);
-      stage_rows_lds<C::BN, NW>(vb, (const char*)(v + row0), stride, kv_end - 1 - k0, w, lane);
+      stage_rows_lds<C::BN, NW, D>(kb, (const char*)(k + row0), stride, kv_end - 1 - k0, w, lane);
+      stage_rows_lds<C::BN, NW, D>(vb, (const char*)(v + row0), stride, kv_end - 1 - k0, w, lane);
     } else {
       i32x4 kreg[C::PER_THREAD], vreg[C::PER_THREAD];
 #pragma unroll
@@ -127,25 +128,30 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16_kernel(
   // the 64-key tile at doc-local key k0, its K rows at kb and V rows at vb
   auto subtile = [&](int k0, const char* kb, const char* vb) __attribute__((always_inline)) {
     if (k0 <= wave_last_key) {
-      // ---- Sᵀ = K Qᵀ for the tile's two 32-key blocks: operand rows read as a batch, the
-      // two accumulators interleaved so consecutive MFMAs are independent
+      // ---- Sᵀ = K Qᵀ for the tile's two 32-key blocks: operand rows read as a batch (d = 256:
+      // four batches of 4 k-steps), the two accumulators interleaved so consecutive MFMAs are
+      // independent
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
-      {
-        i32x4 fk[2][C::DS];
+      constexpr int SB = D == 256 ? 4 : C::DS;
 #pragma unroll
-        for (int s = 0; s < C::DS; ++s)
+      for (int sc = 0; sc < C::DS; sc += SB) {
+        i32x4 fk[2][SB];
 #pragma unroll
-          for (int b = 0; b < 2; ++b) fk[b][s] = *(const i32x4*)(kb + b * 32 * C::S::STR + so.row[s]);
+        for (int s = 0; s < SB; ++s)
 #pragma unroll
-        for (int s = 0; s < C::DS; ++s)
+          for (int b = 0; b < 2; ++b) fk[b][s] = *(const i32x4*)(kb + b * 32 * C::S::STR + so.row[sc + s]);
 #pragma unroll
-          for (int b = 0; b < 2; ++b) sacc[b] = mfma32(as_bf16x8(fk[b][s]), qf[s], sacc[b]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::DS - 4, 0);
+        for (int s = 0; s < SB; ++s)
+#pragma unroll
+          for (int b = 0; b < 2; ++b) sacc[b] = mfma32(as_bf16x8(fk[b][s]), qf[sc + s], sacc[b]);
+        if constexpr (D <= 128) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::DS - 4, 0);
+        }
       }
       // ---- online softmax on this lane's query column. The maximum is taken on the raw scores
       // (scale_log2 > 0) and the scale is folded into the exponent, p = 2^(s·c − m). Masking
@@ -332,6 +338,10 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
     if (hpw == 4) CFA_FWD_LAUNCH(128, 4, 8);
     else if (hpw == 2) CFA_FWD_LAUNCH(128, 2, 8);
     else CFA_FWD_LAUNCH(128, 1, 8);
+  } else if (d == 256) {
+    if (hpw == 4) CFA_FWD_LAUNCH(256, 4, 4);
+    else if (hpw == 2) CFA_FWD_LAUNCH(256, 2, 4);
+    else CFA_FWD_LAUNCH(256, 1, 4);
   } else {
     if (hpw == 4) CFA_FWD_LAUNCH(64, 4, 4);
     else if (hpw == 2) CFA_FWD_LAUNCH(64, 2, 4);

@@ -70,8 +70,10 @@ int check_sizes(const Sizes& s, bool bwd) {
     return fail(CFA_ERR_UNSUPPORTED, "dtype %d unknown", s.dtype);
   if (s.dtype == CFA_MXFP8) {
     if (s.d != 128) return fail(CFA_ERR_UNSUPPORTED, "MXFP8 supports d = 128 only (got %d)", s.d);
-  } else if (s.d != 64 && s.d != 128) {
-    return fail(CFA_ERR_UNSUPPORTED, "head dim %d unsupported (64 or 128)", s.d);
+  } else if (s.dtype == CFA_F32 && s.d != 64 && s.d != 128) {
+    return fail(CFA_ERR_UNSUPPORTED, "the fp32 path supports d = 64 or 128 (got %d)", s.d);
+  } else if (s.d != 64 && s.d != 128 && s.d != 256) {
+    return fail(CFA_ERR_UNSUPPORTED, "head dim %d unsupported (64, 128 or 256)", s.d);
   }
   if (bwd && s.dtype == CFA_F32) return fail(CFA_ERR_UNSUPPORTED, "the fp32 path is forward-only");
   return CFA_OK;

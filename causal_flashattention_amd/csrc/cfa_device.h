@@ -140,16 +140,20 @@ __device__ inline float pow2i(int e) { return e >= -126 ? __builtin_bit_cast(flo
 // and chunk c of row r is stored at chunk position c ^ f(r), f(r) = 4·(r%4) + (r/4)%4:
 // f is a bijection on 16 consecutive rows (row reads hit 16 distinct chunk slots) and, for
 // 4 rows r ≡ 0..3 (mod 4), moves the 4-chunk group by a different multiple of 4 (transposed
-// reads hit 16 distinct slots), so both patterns cover the 64 banks once. D = 64 uses a padded
-// 144-byte row instead.
+// reads hit 16 distinct slots), so both patterns cover the 64 banks once. D = 256: rows of 512
+// bytes, each 256-byte half swizzled as a D = 128 row (a 512-byte stride maps onto the banks as
+// a 256-byte one). D = 64 uses a padded 144-byte row instead.
 template <int D>
 struct SwzTile {
-  static constexpr int STR = (D == 128) ? 256 : D * 2 + 16;
-  __device__ static inline int f(int r) { return D == 128 ? (4 * (r & 3) + ((r >> 2) & 3)) : 0; }
+  static constexpr bool SWZ = D >= 128;
+  static constexpr int STR = SWZ ? 2 * D : D * 2 + 16;
+  __device__ static inline int f(int r) { return SWZ ? (4 * (r & 3) + ((r >> 2) & 3)) : 0; }
   // byte offset of 16-byte chunk c of row r
-  __device__ static inline int chunk(int r, int c) { return r * STR + ((c ^ f(r)) << 4); }
+  __device__ static inline int chunk(int r, int c) {
+    return SWZ ? r * STR + ((c >> 4) << 8) + (((c & 15) ^ f(r)) << 4) : r * STR + (c << 4);
+  }
   // byte offset of element d of row r (d % 4 == 0 for 8-byte transposed reads)
-  __device__ static inline int elem(int r, int d) { return r * STR + (((d >> 3) ^ f(r)) << 4) + ((d & 7) << 1); }
+  __device__ static inline int elem(int r, int d) { return chunk(r, d >> 3) + ((d & 7) << 1); }
 };
 
 // Lane-constant byte offsets of the two read patterns on a SwzTile (row blocks of 32 rows and
@@ -164,15 +168,23 @@ struct SwzOffsets {
   int tr0[D / 32], tr1[D / 32];
   __device__ explicit SwzOffsets(int lane) {
     using S = SwzTile<D>;
+    constexpr int W = D < 128 ? D : 128;          // d = 256: the upper half is the lower + 256 B
     const int half = lane >> 5;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) row[s] = S::chunk(lane & 31, 2 * s + half);
+    for (int s = 0; s < W / 16; ++s) row[s] = S::chunk(lane & 31, 2 * s + half);
     const int r = 4 * half + ((lane & 15) >> 2);
     const int dsub = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int db = 0; db < W / 32; ++db) {
       tr0[db] = S::elem(r, 32 * db + dsub);
       tr1[db] = S::elem(r + 8, 32 * db + dsub);
+    }
+#pragma unroll
+    for (int s = W / 16; s < D / 16; ++s) row[s] = row[s - W / 16] + 256;
+#pragma unroll
+    for (int db = W / 32; db < D / 32; ++db) {
+      tr0[db] = tr0[db - W / 32] + 256;
+      tr1[db] = tr1[db - W / 32] + 256;
     }
   }
 };
@@ -205,21 +217,25 @@ __device__ inline void wait_vmem_keep() { asm volatile("s_waitcnt vmcnt(%0)" ::"
 // the caller has already waited for the copies that the other waves are about to read.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Stage ROWS rows of 128 bf16 (256 bytes) into a SwzTile<128> LDS tile with direct loads.
-// Called by NW waves; wave w copies the 1 KB blocks [w·ROWS/(4·NW), (w+1)·ROWS/(4·NW)), block I
-// holding rows 4I..4I+3. Lane i fills physical chunk i%16 of row 4I + i/16, i.e. logical chunk
-// (i%16) ^ f(row): the swizzle is applied on the global side. Tile row r is read from
+// Stage ROWS rows of D bf16 (D = 128: 256 bytes, 256: 512 bytes) into a SwzTile<D> LDS tile
+// with direct loads. Called by NW waves; wave w copies the 1 KB blocks
+// [w·ROWS/(RB·NW), (w+1)·ROWS/(RB·NW)), block I holding the RB = 1024 / (2·D) rows RB·I ...
+// Lane i fills physical chunk i % (D/8) of row RB·I + i / (D/8), i.e. the logical chunk whose
+// swizzled position that is: the swizzle is applied on the global side. Tile row r is read from
 // base + min(r, rmax)·stride: `base` is wave-uniform (the tile's first row), so each copy is a
 // scalar base plus a 32-bit lane offset; rows past rmax repeat row rmax.
-template <int ROWS, int NW = 4>
+template <int ROWS, int NW = 4, int D = 128>
 __device__ inline void stage_rows_lds(char* tile, const char* base, uint32_t stride, int rmax, int wave, int lane) {
-  static_assert(ROWS % (4 * NW) == 0, "NW waves × 4 rows per block");
-  constexpr int PER_WAVE = ROWS / (4 * NW);
+  static_assert(D == 128 || D == 256, "rows of 256 or 512 bytes");
+  constexpr int LPR = D / 8, RB = 64 / LPR;
+  static_assert(ROWS % (RB * NW) == 0, "NW waves × RB rows per block");
+  constexpr int PER_WAVE = ROWS / (RB * NW);
 #pragma unroll
   for (int j = 0; j < PER_WAVE; ++j) {
     const int I = wave * PER_WAVE + j;
-    const int r = 4 * I + (lane >> 4);
-    const uint32_t c = (uint32_t)((lane & 15) ^ SwzTile<128>::f(r));
+    const int r = RB * I + lane / LPR;
+    const int pc = lane % LPR;                    // physical chunk
+    const uint32_t c = (uint32_t)((pc & 16) | ((pc & 15) ^ SwzTile<D>::f(r)));
     g2lds16(base + ((uint32_t)min(r, rmax) * stride + c * 16), tile + I * 1024);
   }
 }

@@ -85,7 +85,8 @@ size_t cfa_saved_bytes(int total_tokens, int n_docs, int hq, int hkv, int d, int
  * Forward pass. Writes o and lse.
  *   max_seqlen : upper bound on any document length (0 = unknown; then total_tokens is used).
  *   scale      : multiplier of Q K^T (usually 1/sqrt(d)); finite and > 0.
- *   dtype      : CFA_F32 (d = 64 or 128), CFA_BF16 (d = 64 or 128), CFA_MXFP8 (d = 128).
+ *   dtype      : CFA_F32 (d = 64 or 128), CFA_BF16 (d = 64, 128 or 256; 256 is FlashAttention-2's
+ *                extension, "FlashAttention (HU)", FlashAttention-2 (2023)), CFA_MXFP8 (d = 128).
  *   saved      : CFA_MXFP8: cfa_saved_bytes() bytes written here for attn_bwd; otherwise NULL.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

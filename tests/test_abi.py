@@ -61,7 +61,8 @@ def _fwd(**over):
 @pytest.mark.parametrize("over,status", [
     (dict(q=None), 1), (dict(cu=None), 1), (dict(ws=None), 1),
     (dict(hkv=3), 2), (dict(n_docs=0), 2), (dict(T=-1), 2), (dict(scale=float("nan")), 2), (dict(scale=0.0), 2),
-    (dict(d=96), 3), (dict(dtype=7), 3), (dict(dtype=2, d=64), 3),
+    (dict(d=96), 3), (dict(dtype=7), 3), (dict(dtype=2, d=64), 3), (dict(dtype=0, d=256), 3),
+    (dict(dtype=2, d=256), 3),
     (dict(q=FAKE + 8), 4), (dict(ws=FAKE + 16), 4),
     (dict(wsb=16), 5),
 ])

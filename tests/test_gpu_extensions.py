@@ -2,8 +2,9 @@
 
 * A gradient flowing into the forward's LSE (``dlse``): bf16 and MXFP8 against the oracles'
   ``dlse`` term (pinned on the CPU by central differences of the forward).
-* Multi-query attention (one kv head for every query head), which FlashAttention-2 added
-  ("FlashAttention (HU)", "Evolúció és további fejlesztések", FlashAttention-2 (2023)).
+* Multi-query attention (one kv head for every query head) and head dim 256, both of which
+  FlashAttention-2 added ("FlashAttention (HU)", "Evolúció és további fejlesztések",
+  FlashAttention-2 (2023)).
 
 Tolerances as for the base case: bf16 O max-abs <= 1e-2 and gradients rel-L2 <= 1e-2; MXFP8
 rel-L2 <= 3e-2 against the MX oracle.
@@ -22,6 +23,7 @@ pytestmark = pytest.mark.gpu
 
 GRAD_TOL = 1e-2
 O_TOL = 1e-2
+LSE_TOL = 1e-3
 MX_TOL = 3e-2
 
 
@@ -109,3 +111,52 @@ def test_mqa_one_kv_head(mx):
         g = ref.attn_bwd(w.f64("q"), w.f64("k"), w.f64("v"), w.f64("do"), w.cu_seqlens, w.scale)
         for a, b in zip((dq, dk, dv), g):
             assert rel_l2(to_f64(a), b) <= GRAD_TOL
+
+
+@pytest.mark.parametrize("lengths,hq,hkv,causal", [
+    ([1, 5, 64, 127, 129, 300], 2, 2, True),
+    ([513, 31, 200], 8, 2, True),
+    ([700, 1], 4, 1, True),
+    ([100, 257], 2, 1, False),
+])
+def test_head_dim_256(lengths, hq, hkv, causal):
+    w = W.make_random(seed=340 + sum(lengths), lengths=lengths, hq=hq, hkv=hkv, d=256, causal=causal)
+    announce("d=256 fwd+bwd", lengths, hq, hkv, causal)
+    dev = upload(w)
+    o, lse, dq, dk, dv = _run(w, dev, False)
+    ro, rl = ref.attn_fwd(w.f64("q"), w.f64("k"), w.f64("v"), w.cu_seqlens, w.scale, causal)
+    assert np.max(np.abs(to_f64(o) - ro)) <= O_TOL
+    assert np.max(np.abs(to_f64(lse) - rl)) <= LSE_TOL
+    g = ref.attn_bwd(w.f64("q"), w.f64("k"), w.f64("v"), w.f64("do"), w.cu_seqlens, w.scale, causal)
+    errs = [rel_l2(to_f64(a), b) for a, b in zip((dq, dk, dv), g)]
+    print("rel-L2 dq dk dv", errs)
+    assert max(errs) <= GRAD_TOL
+
+
+def test_head_dim_256_determinism_isolation_causality():
+    lengths = [300, 129, 1, 64, 200]
+    w = W.make_random(seed=350, lengths=lengths, hq=4, hkv=2, d=256)
+    announce("d=256 invariants", lengths)
+    dev = upload(w)
+    r1 = _run(w, dev, False)
+    r2 = _run(w, dev, False)
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+    cu = w.cu_seqlens
+    for n in range(len(lengths)):
+        s0, s1 = int(cu[n]), int(cu[n + 1])
+        sub = W.Workload(name="doc", total_tokens=s1 - s0, hq=4, hkv=2, d=256, dtype="bf16", scale=w.scale,
+                         cu_seqlens=np.array([0, s1 - s0], np.int32), q=w.q[s0:s1], k=w.k[s0:s1], v=w.v[s0:s1],
+                         do=w.do[s0:s1])
+        ra = _run(sub, upload(sub), False)
+        assert torch.equal(ra[0], r1[0][s0:s1]) and torch.equal(ra[1], r1[1][:, s0:s1])
+        for a, b in zip(ra[2:], r1[2:]):
+            assert torch.equal(a, b[s0:s1])
+    for jl in (0, 63, 64, 150, 199):
+        j = int(cu[4]) + jl
+        dev2 = {kk: vv.clone() for kk, vv in dev.items()}
+        for name in ("q", "k", "v", "do"):
+            dev2[name][j] = dev2[name][j] * 3.0 + 1.0
+        r3 = _run(w, dev2, False)
+        assert torch.equal(r3[0][:j], r1[0][:j]), jl       # O of earlier queries
+        assert torch.equal(r3[2][:j], r1[2][:j]), jl       # dQ of earlier queries
