@@ -296,12 +296,17 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
 // register file. Staging buffers: step i (Q, dO tiles, LSE·log2 e, D) lives in buffer i mod 3
 // and P of step i in exchange buffer i mod 3, so the loop is unrolled three times and every
 // buffer is a distinct static array (no aliasing between the copies in flight and the reads).
+//
+// Head split (n_split > 1, for grids too small to fill the chip, e.g. MQA): workgroup
+// (item, split, kv head) runs only query heads [G·split/n_split, G·(split+1)/n_split) of the group
+// and writes its unscaled fp32 dKᵀ / dVᵀ sums to part_dk / part_dv [n_split][T][hkv][d]; the
+// reduce kernel adds the splits in index order (deterministic) and writes bf16.
 template <int D, int NP>
 __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     __bf16* __restrict__ dk, __bf16* __restrict__ dv, Plan plan, int total_tokens, int hq, int hkv,
-    float scale, int causal) {
+    float scale, int causal, int n_split, float* __restrict__ part_dk, float* __restrict__ part_dv) {
   using C = BwdTile<D>;
   constexpr int KT = 32 * NP;                     // keys per workgroup
   constexpr int BM = 32;                          // queries per step
@@ -317,13 +322,15 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
   __shared__ f32x4 xp_b[XP];
   __shared__ f32x4 xp_c[XP];
 
-  const int p = blockIdx.x / hkv, g = blockIdx.x % hkv;
+  const int p = blockIdx.x / (hkv * n_split), g = blockIdx.x % hkv, split = (blockIdx.x / hkv) % n_split;
   int s0, L, t;
   if (!decode_item(plan, p, KT, false, s0, L, t)) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5;
   const int pair = w % NP;
   const bool ds_wave = w >= NP;
   const int G = hq / hkv;
+  const int h_lo = g * G + (G * split) / n_split;              // this split's query heads
+  const int n_h = g * G + (G * (split + 1)) / n_split - h_lo;
   const int kw0 = t * KT + 32 * pair;             // first doc-local key of this pair
   const int mykey = kw0 + (lane & 31);
   const float sl2 = scale * LOG2E;
@@ -345,7 +352,7 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
 
   const int q_begin = causal ? t * KT : 0;
   const int n_qt = (L - q_begin + BM - 1) / BM;
-  const int n_steps = n_qt * G;
+  const int n_steps = n_qt * n_h;
   const int wave_first_q = causal ? kw0 : 0;
 
   // Step st -> buffer: P waves copy the Q tile, dS waves the dO tile (direct global -> LDS);
@@ -353,7 +360,7 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
   // the document end are clamped into it and masked (P = 0).
   float lreg = 0.f, dreg = 0.f;
   auto stage = [&](int st, char* buf) {
-    const int h = g * G + st / n_qt;
+    const int h = h_lo + st / n_qt;
     const int q0 = q_begin + (st % n_qt) * BM;
     const __bf16* src = ds_wave ? dout : q;
     stage_rows_lds<BM, NP, D>(buf + (ds_wave ? TILE : 0), (const char*)(src + ((size_t)(s0 + q0) * hq + h) * D),
@@ -513,19 +520,49 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
 
   // dS wave: dK = scale·dKᵀ; P wave: dV (lane: key mykey, d = 32 db + 8 jg + 4·half + 0..3)
   if (mykey < L) {
-    const float f = ds_wave ? scale : 1.f;
-    __bf16* dst = (ds_wave ? dk : dv) + ((size_t)(s0 + mykey) * hkv + g) * D + 4 * half;
+    const size_t row = ((size_t)(s0 + mykey) * hkv + g) * D + 4 * half;
+    if (n_split > 1) {
+      float* dst = (ds_wave ? part_dk : part_dv) + (size_t)split * total_tokens * hkv * D + row;
 #pragma unroll
-    for (int dbk = 0; dbk < C::DB; ++dbk)
+      for (int dbk = 0; dbk < C::DB; ++dbk)
 #pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        i32x2 u;
-        u.x = (int)pack_bf16x2(acc[dbk][4 * jg] * f, acc[dbk][4 * jg + 1] * f);
-        u.y = (int)pack_bf16x2(acc[dbk][4 * jg + 2] * f, acc[dbk][4 * jg + 3] * f);
-        *(i32x2*)(dst + 32 * dbk + 8 * jg) = u;
-      }
+        for (int jg = 0; jg < 4; ++jg)
+          *(f32x4*)(dst + 32 * dbk + 8 * jg) =
+              f32x4{acc[dbk][4 * jg], acc[dbk][4 * jg + 1], acc[dbk][4 * jg + 2], acc[dbk][4 * jg + 3]};
+    } else {
+      const float f = ds_wave ? scale : 1.f;
+      __bf16* dst = (ds_wave ? dk : dv) + row;
+#pragma unroll
+      for (int dbk = 0; dbk < C::DB; ++dbk)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          i32x2 u;
+          u.x = (int)pack_bf16x2(acc[dbk][4 * jg] * f, acc[dbk][4 * jg + 1] * f);
+          u.y = (int)pack_bf16x2(acc[dbk][4 * jg + 2] * f, acc[dbk][4 * jg + 3] * f);
+          *(i32x2*)(dst + 32 * dbk + 8 * jg) = u;
+        }
+    }
   }
 }
+
+// Sum of the head-split partial sums in split order: dK = scale·Σ_s part_dk[s], dV = Σ_s part_dv[s]
+// (bf16). One lane per 4 consecutive elements.
+__global__ __launch_bounds__(256) void dkdv_split_reduce_kernel(const float* __restrict__ part_dk,
+                                                                const float* __restrict__ part_dv,
+                                                                __bf16* __restrict__ dk, __bf16* __restrict__ dv,
+                                                                long n, int n_split, float scale) {
+  const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4 a = *(const f32x4*)(part_dk + i), b = *(const f32x4*)(part_dv + i);
+  for (int sp = 1; sp < n_split; ++sp) {
+    a += *(const f32x4*)(part_dk + (size_t)sp * n + i);
+    b += *(const f32x4*)(part_dv + (size_t)sp * n + i);
+  }
+  *(i32x2*)(dk + i) = i32x2{(int)pack_bf16x2(a[0] * scale, a[1] * scale), (int)pack_bf16x2(a[2] * scale, a[3] * scale)};
+  *(i32x2*)(dv + i) = i32x2{(int)pack_bf16x2(b[0], b[1]), (int)pack_bf16x2(b[2], b[3])};
+}
+
+
 
 // ------------------------------------------------------------------ dQ
 template <int D>
@@ -720,23 +757,39 @@ hipError_t launch_bwd_pre(const void* o, const void* dout, const float* dlse, fl
 template <int D>
 static hipError_t launch_dkdv_d(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                                 const float* delta, void* dk, void* dv, const Plan& plan_any, const int* pref_base,
-                                int T, int hq, int hkv, float scale, int causal, hipStream_t stream) {
+                                int T, int hq, int hkv, float scale, int causal, int n_split, float* part,
+                                hipStream_t stream) {
   constexpr int NP = D == 256 ? 2 : 4;            // wave pairs (d = 64: waves) per workgroup
   constexpr int KT = D == 256 ? 64 : 128;         // keys per workgroup
   Plan plan = plan_any;
   plan.pref = pref_base + pref_slot(KT) * (plan.n_docs + 1);
   const long items = (long)(T + KT - 1) / KT + plan.n_docs;
-  const long grid = items * hkv;
-  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  if constexpr (D >= 128)
+  if constexpr (D >= 128) {
+    const long grid = items * hkv * n_split;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    const long n = (long)T * hkv * D;
+    float* pdk = n_split > 1 ? part : nullptr;
+    float* pdv = n_split > 1 ? part + (size_t)n_split * n : nullptr;
     hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<D, NP>), dim3((unsigned)grid), dim3(128 * NP), 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, lse, delta,
-                       (__bf16*)dk, (__bf16*)dv, plan, T, hq, hkv, scale, causal);
-  else
+                       (__bf16*)dk, (__bf16*)dv, plan, T, hq, hkv, scale, causal, n_split, pdk, pdv);
+    if (n_split > 1 && n > 0)
+      hipLaunchKernelGGL(dkdv_split_reduce_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, stream, pdk,
+                         pdv, (__bf16*)dk, (__bf16*)dv, n, n_split, scale);
+  } else {
+    const long grid = items * hkv;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)q,
                        (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, lse, delta, (__bf16*)dk, (__bf16*)dv,
                        plan, T, hq, hkv, scale, causal);
+  }
   return hipGetLastError();
+}
+
+int dkdv_head_split(int hq, int hkv, int d) {
+  if (d != 128 && d != 256) return 1;
+  const int G = hq / hkv;
+  return std::max(1, std::min(G, 8 / hkv));
 }
 
 template <int D>
@@ -754,12 +807,16 @@ static hipError_t launch_dq_d(const void* q, const void* k, const void* v, const
 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                            const float* delta, void* dk, void* dv, const Plan& plan_any, const int* pref_base, int T,
-                           int hq, int hkv, int d, float scale, int causal, hipStream_t stream) {
+                           int hq, int hkv, int d, float scale, int causal, int n_split, float* part,
+                           hipStream_t stream) {
   if (d == 128)
-    return launch_dkdv_d<128>(q, k, v, dout, lse, delta, dk, dv, plan_any, pref_base, T, hq, hkv, scale, causal, stream);
+    return launch_dkdv_d<128>(q, k, v, dout, lse, delta, dk, dv, plan_any, pref_base, T, hq, hkv, scale, causal,
+                              n_split, part, stream);
   if (d == 256)
-    return launch_dkdv_d<256>(q, k, v, dout, lse, delta, dk, dv, plan_any, pref_base, T, hq, hkv, scale, causal, stream);
-  return launch_dkdv_d<64>(q, k, v, dout, lse, delta, dk, dv, plan_any, pref_base, T, hq, hkv, scale, causal, stream);
+    return launch_dkdv_d<256>(q, k, v, dout, lse, delta, dk, dv, plan_any, pref_base, T, hq, hkv, scale, causal,
+                              n_split, part, stream);
+  return launch_dkdv_d<64>(q, k, v, dout, lse, delta, dk, dv, plan_any, pref_base, T, hq, hkv, scale, causal, 1,
+                           nullptr, stream);
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,

@@ -106,6 +106,8 @@ size_t add_mx_t(size_t off, const Sizes& s, int h, MxBuf& b) {
 struct WsLayout {
   size_t plan_end;
   size_t delta;             // bwd: float [hq, T]
+  size_t dkdv_part;         // bwd bf16 with a head split: float [2][n_split][T][hkv][d]
+  int n_split;
   MxBuf vt;                 // fwd MX: V along tokens
   MxBuf dod, dot, vd, qt, kt;  // bwd MX
   size_t total;
@@ -116,9 +118,17 @@ WsLayout ws_layout(int pass, const Sizes& s) {
   cfa::PlanLayout pl(s.n_docs);
   w.plan_end = pl.end;
   size_t off = pl.end;
+  w.n_split = 1;
   if (pass == 1) {
     w.delta = off;
     off = cfa::align256(off + sizeof(float) * (size_t)s.hq * (size_t)s.T);
+    if (s.dtype == CFA_BF16) {
+      w.n_split = cfa::dkdv_head_split(s.hq, s.hkv, s.d);
+      if (w.n_split > 1) {
+        w.dkdv_part = off;
+        off = cfa::align256(off + sizeof(float) * 2 * (size_t)w.n_split * s.T * s.hkv * s.d);
+      }
+    }
   }
   if (s.dtype == CFA_MXFP8) {
     if (pass == 0) {
@@ -323,7 +333,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   }
   mark(1, 0, st);
   if (int r = check_hip(cfa::launch_bwd_dkdv(q, k, v, dout, lse, delta, dk, dv, plan, plan.pref, total_tokens, hq,
-                                             hkv, d, scale, causal, st),
+                                             hkv, d, scale, causal, wl.n_split,
+                                             (float*)((char*)workspace + wl.dkdv_part), st),
                         "dK/dV kernel"))
     return r;
   mark(1, 1, st);

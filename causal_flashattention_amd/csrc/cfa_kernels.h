@@ -25,9 +25,19 @@ hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, 
 hipError_t launch_bwd_pre(const void* o, const void* dout, const float* dlse, float* delta, int total_tokens, int hq,
                           int d, hipStream_t stream);
 
+// n_split > 1: the query heads of each group are split over n_split workgroups whose fp32
+// partial sums go to `part` (2·n_split·T·hkv·d floats, see dkdv_head_split) and are reduced in
+// split order.
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                            const float* delta, void* dk, void* dv, const Plan& plan, const int* pref_base, int T,
-                           int hq, int hkv, int d, float scale, int causal, hipStream_t stream);
+                           int hq, int hkv, int d, float scale, int causal, int n_split, float* part,
+                           hipStream_t stream);
+
+// Head split of the bf16 dK/dV pass (1 = none): with fewer than 8 kv heads the (key tile,
+// kv head) grid is split further over the query heads of each group, up to 8 workgroups per key
+// tile (MQA: min(hq, 8)). It depends on the head configuration only, never on the token count or
+// the documents, so a document's dK/dV are bit-identical whatever it is packed with.
+int dkdv_head_split(int hq, int hkv, int d);
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                          const float* delta, void* dq, const Plan& plan, const int* pref_base, int T, int hq,
