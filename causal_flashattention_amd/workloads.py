@@ -169,3 +169,76 @@ def make_random(seed, lengths, hq, hkv, d=128, dtype="bf16", scale=None, causal=
                     scale=(1.0 / math.sqrt(d)) if scale is None else scale,
                     cu_seqlens=cu_from_lengths(lengths), q=q, k=kk, v=v, do=do, causal=causal,
                     info={"seed": seed, "lengths": list(lengths)})
+
+
+# ---------------------------------------------------------------- decoding over a KV cache
+@dataclass
+class DecodeWorkload:
+    """One new query token per sequence over a packed KV cache.
+
+    ``q [B, hq, d]`` bf16 bits; the cache ``k, v [Tk, hkv, d]`` holds bf16 bits (kv "bf16") or
+    E4M3 codes (kv "mxfp8", with E8M0 block scales ``k_scales, v_scales [Tk, hkv, d/32]``);
+    sequence ``b`` owns cache rows ``cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1``.
+    """
+    name: str
+    hq: int
+    hkv: int
+    d: int
+    kv: str
+    scale: float
+    cu_seqlens_k: np.ndarray
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    k_scales: np.ndarray = None
+    v_scales: np.ndarray = None
+    info: dict = field(default_factory=dict)
+
+    @property
+    def n_seqs(self):
+        return len(self.cu_seqlens_k) - 1
+
+    @property
+    def total_k(self):
+        return int(self.cu_seqlens_k[-1])
+
+    def kv_bytes(self):
+        """Bytes of the cache read once (codes and scales, or bf16), K and V."""
+        per = self.d * (1 + 1 / 32) if self.kv == "mxfp8" else 2 * self.d
+        return 2.0 * self.total_k * self.hkv * per
+
+
+def make_decode(seed, lengths, hq, hkv, d=128, kv="bf16", scale=None):
+    """Seeded decode inputs. Draw order: Q (N(0,1) → bf16), then K, V: bf16 N(0,1) values, or
+    E4M3 codes uniform over the 254 finite byte values with E8M0 scale bytes uniform in
+    [117, 124] (2^-10 .. 2^-3), drawn K codes, K scales, V codes, V scales."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B = len(lengths)
+    Tk = int(sum(lengths))
+    q = f32_to_bf16_bits(_normals(rng, (B, hq, d)))
+    ks = vs = None
+    if kv == "bf16":
+        k = f32_to_bf16_bits(_normals(rng, (Tk, hkv, d)))
+        v = f32_to_bf16_bits(_normals(rng, (Tk, hkv, d)))
+    elif kv == "mxfp8":
+        def codes():
+            c = rng.integers(0, 254, size=(Tk, hkv, d), dtype=np.int64)
+            c = c + (c >= 0x7F)                   # skip 0x7F; 0xFF is never drawn (max 254)
+            return c.astype(np.uint8)
+
+        def scales():
+            return rng.integers(117, 125, size=(Tk, hkv, d // 32)).astype(np.uint8)
+        k, ks = codes(), scales()
+        v, vs = codes(), scales()
+    else:
+        raise ValueError(kv)
+    return DecodeWorkload(name="decode", hq=hq, hkv=hkv, d=d, kv=kv,
+                          scale=(1.0 / math.sqrt(d)) if scale is None else scale,
+                          cu_seqlens_k=cu_from_lengths(lengths), q=q, k=k, v=v, k_scales=ks, v_scales=vs,
+                          info={"seed": seed, "lengths": list(lengths)})
+
+
+def decode_batch_lengths(seed, n_seqs, lo=512, hi=32768):
+    """Context lengths of a serving batch: floor(exp(U(ln lo, ln hi))) per sequence."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return [int(math.floor(math.exp(rng.uniform(math.log(lo), math.log(hi))))) for _ in range(n_seqs)]

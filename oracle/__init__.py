@@ -18,16 +18,20 @@ Sources (web pages; cited by title and section):
   Mikro-Ölçeklemeli Dikkat Mekanizması" (blog.edumints.com) -- section "FLAMIA Mimarisi ve Temel
   Tasarım İlkeleri": MXFP8 path, token-block scaling, leakage safeguards, fwd/bwd consistency,
   document-local scaling over packed layouts.
+* "Flash Attention" (ai.ozdemir.be) -- sections "Tanım" and "Gerçek dünyadan örnek": local
+  inference reads a quantised K/V cache (8-bit at about half the memory of f16) through flash
+  attention.
 
 Modules:
 
 * ``attention``     -- naive two-pass forward with an explicit mask, and its exact gradient.
 * ``mx``            -- E4M3 / E8M0 block quantiser (along the head dim, or along doc-local tokens).
 * ``mx_attention``  -- the attention oracle fed with the quantised operand copies.
+* ``decode``        -- one query per sequence over a packed (optionally MX-quantised) KV cache.
 * ``baseline``      -- wall-clock timing of the oracle on host cores (CPU baseline only).
 
 Every function states the passage it follows; the readings taken where the pages are silent
 are listed in the repository's design notes.
 """
 
-from . import attention, mx, mx_attention  # noqa: F401
+from . import attention, decode, mx, mx_attention  # noqa: F401
