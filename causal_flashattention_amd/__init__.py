@@ -8,6 +8,7 @@ failing call raises.
     o, lse, saved = attn_fwd(q, k, v, cu_seqlens)          # q [T, hq, d], k/v [T, hkv, d]
     dq, dk, dv = attn_bwd(q, k, v, o, lse, do, cu_seqlens, saved=saved)
     codes, scales = mx_quantize(x, cu_seqlens, axis=0)     # MXFP8 E4M3 + E8M0, blocks of 32
+    o, lse = attn_decode(q1, k_cache, v_cache, cu_seqlens_k)  # one query per sequence, KV cache
 """
 import ctypes
 import math
@@ -17,7 +18,7 @@ import torch
 from . import _lib
 from ._lib import CFA_BF16, CFA_F32, CFA_MXFP8, CfaError
 
-__all__ = ["attn_fwd", "attn_bwd", "mx_quantize", "workspace_bytes", "saved_bytes", "CfaError",
+__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "mx_quantize", "workspace_bytes", "saved_bytes", "CfaError",
            "CFA_F32", "CFA_BF16", "CFA_MXFP8", "library_path"]
 
 
@@ -127,6 +128,40 @@ def attn_bwd(q, k, v, o, lse, dout, cu_seqlens, *, scale=None, causal=True, cu_s
                           int(max_seqlen), hq, hkv, d, scale, int(bool(causal)), dt, _ptr(workspace),
                           workspace.numel(), _stream()))
     return dq, dk, dv
+
+
+def attn_decode(q, k_cache, v_cache, cu_seqlens_k, *, k_scales=None, v_scales=None, scale=None,
+                cu_seqlens_k_host=None, out=None, lse=None, workspace=None):
+    """One query token per sequence over a packed KV cache. ``q [B, hq, d]`` bf16; the cache
+    ``[Tk, hkv, d]`` is bf16, or uint8 E4M3 codes with ``k_scales, v_scales [Tk, hkv, d/32]``
+    uint8 E8M0 bytes. Returns (o [B, hq, d] bf16, lse [hq, B] float32)."""
+    L = _lib.lib()
+    _check_dev(q, k_cache, v_cache, cu_seqlens_k, k_scales, v_scales)
+    B, hq, d = q.shape
+    Tk, hkv = k_cache.shape[0], k_cache.shape[1]
+    if q.dtype != torch.bfloat16:
+        raise TypeError("q must be bf16")
+    if k_cache.dtype == torch.uint8:
+        kv = CFA_MXFP8
+        if k_scales is None or v_scales is None:
+            raise ValueError("an MXFP8 cache needs k_scales and v_scales")
+    elif k_cache.dtype == torch.bfloat16:
+        kv = CFA_BF16
+    else:
+        raise TypeError(f"unsupported cache dtype {k_cache.dtype}")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((hq, B), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nb = L.cfa_decode_workspace_bytes(B, Tk, hq, hkv, d, kv)
+        workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device)
+    hcu = _host_cu(cu_seqlens_k, cu_seqlens_k_host)
+    _lib.check(L.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales), _ptr(out),
+                             _ptr(lse), _ptr(cu_seqlens_k), _ptr(hcu) if hcu is not None else None, B, Tk, hq, hkv,
+                             d, scale, kv, _ptr(workspace), workspace.numel(), _stream()))
+    return out, lse
 
 
 def mx_quantize(x, cu_seqlens, axis, *, cu_seqlens_host=None, t_pad=None, codes=None, scales=None,

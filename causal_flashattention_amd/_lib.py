@@ -27,6 +27,8 @@ SIGNATURES = {
     "mx_quantize": (_I, [_P, _I, _I, _I, _P, _P, _I, _I, _P, _P, _I, _P, _S, _P]),
     "mx_padded_tokens": (_I, [_I, _I]),
     "mx_workspace_bytes": (_S, [_I]),
+    "cfa_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I]),
+    "attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "cfa_set_kernel_events": (_I, [_P, _I]),
     "cfa_device_error": (_I, [_P, _P, ctypes.POINTER(ctypes.c_int)]),
 }

@@ -383,6 +383,76 @@ int mx_quantize(const void* x, int total_tokens, int h, int d, const int32_t* cu
                    "mx_quantize_t");
 }
 
+// ---------------------------------------------------------------- decoding over a KV cache
+namespace {
+struct DecLayout {
+  size_t part_o, part_ml, total;
+};
+DecLayout dec_layout(int n_seqs, int total_k, int hq, int d) {
+  DecLayout l{};
+  const cfa::PlanLayout pl(n_seqs);
+  const size_t slots = cfa::decode_partial_slots(total_k, n_seqs);
+  l.part_o = pl.end;
+  l.part_ml = cfa::align256(l.part_o + sizeof(float) * slots * hq * d);
+  l.total = cfa::align256(l.part_ml + 2 * sizeof(float) * slots * hq);
+  return l;
+}
+int check_decode_sizes(int n_seqs, int total_k, int hq, int hkv, int d, int kv_dtype) {
+  if (total_k < 0) return fail(CFA_ERR_SHAPE, "total_k = %d < 0", total_k);
+  if (n_seqs < 1) return fail(CFA_ERR_SHAPE, "n_seqs = %d < 1", n_seqs);
+  if (hq < 1 || hkv < 1) return fail(CFA_ERR_SHAPE, "hq = %d, hkv = %d must be >= 1", hq, hkv);
+  if (hq % hkv) return fail(CFA_ERR_SHAPE, "hq = %d is not a multiple of hkv = %d", hq, hkv);
+  if ((long)total_k * hkv * d > 0x7fffffffL * 8L || (long)n_seqs * hq * d > 0x7fffffffL)
+    return fail(CFA_ERR_SHAPE, "tensor too large");
+  if (kv_dtype != CFA_BF16 && kv_dtype != CFA_MXFP8)
+    return fail(CFA_ERR_UNSUPPORTED, "cache dtype %d unsupported (CFA_BF16 or CFA_MXFP8)", kv_dtype);
+  if (d != 64 && d != 128) return fail(CFA_ERR_UNSUPPORTED, "decoding supports d = 64 or 128 (got %d)", d);
+  return CFA_OK;
+}
+}  // namespace
+
+size_t cfa_decode_workspace_bytes(int n_seqs, int total_k, int hq, int hkv, int d, int kv_dtype) {
+  if (check_decode_sizes(n_seqs, total_k, hq, hkv, d, kv_dtype) != CFA_OK) return 0;
+  return dec_layout(n_seqs, total_k, hq, d).total;
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, const uint8_t* k_scales,
+                const uint8_t* v_scales, void* o, float* lse, const int32_t* cu_seqlens_k,
+                const int32_t* cu_seqlens_k_host, int n_seqs, int total_k, int hq, int hkv, int d, float scale,
+                int kv_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (int st = check_decode_sizes(n_seqs, total_k, hq, hkv, d, kv_dtype)) return st;
+  if (!cu_seqlens_k || !workspace || !q || !o || !lse)
+    return fail(CFA_ERR_NULL, "q, o, lse, cu_seqlens_k and workspace must not be NULL");
+  if (total_k > 0 && (!k_cache || !v_cache)) return fail(CFA_ERR_NULL, "k_cache and v_cache must not be NULL");
+  if (total_k > 0 && kv_dtype == CFA_MXFP8 && (!k_scales || !v_scales))
+    return fail(CFA_ERR_NULL, "an MXFP8 cache needs k_scales and v_scales");
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(CFA_ERR_SHAPE, "scale must be finite and > 0");
+  for (const void* p : {q, k_cache, v_cache, (const void*)o, (const void*)lse, (const void*)cu_seqlens_k})
+    if (!aligned(p, 16)) return fail(CFA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (!aligned(workspace, 256)) return fail(CFA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const DecLayout dl = dec_layout(n_seqs, total_k, hq, d);
+  if (workspace_bytes < dl.total)
+    return fail(CFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, dl.total);
+  if (int st = check_cu_host(cu_seqlens_k_host, n_seqs, total_k, 0)) return st;
+
+  hipStream_t st = (hipStream_t)stream;
+  if (int r = check_hip(cfa::launch_plan(cu_seqlens_k, n_seqs, total_k, workspace, st), "plan kernel")) return r;
+  const cfa::Plan plan = make_plan(workspace, n_seqs);
+  float* part_o = (float*)((char*)workspace + dl.part_o);
+  void* part_ml = (char*)workspace + dl.part_ml;
+  mark(0, 0, st);
+  if (int r = check_hip(cfa::launch_decode(q, k_cache, v_cache, k_scales, v_scales, plan, plan.pref, n_seqs, total_k,
+                                           hq, hkv, d, scale, kv_dtype == CFA_MXFP8, part_o, part_ml, st),
+                        "decode kernel"))
+    return r;
+  mark(0, 1, st);
+  mark(1, 0, st);
+  int r = check_hip(cfa::launch_decode_combine(part_o, part_ml, o, lse, plan, n_seqs, hq, d, st), "decode combine");
+  mark(1, 1, st);
+  return r;
+}
+
 int cfa_set_kernel_events(void* const* events, int n_pairs) {
   g_err[0] = 0;
   if (n_pairs < 0 || (n_pairs > 0 && !events)) return fail(CFA_ERR_NULL, "events must hold 2*n_pairs handles");

@@ -43,6 +43,16 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
                          const float* delta, void* dq, const Plan& plan, const int* pref_base, int T, int hq,
                          int hkv, int d, float scale, int causal, hipStream_t stream);
 
+// Decoding over a packed KV cache (bf16 or MX codes + E8M0 scales): per-chunk partials, then
+// their merge in chunk order. part_o: float [slots][hq][d], part_ml: float2 [slots][hq], with
+// slots = decode_partial_slots(total_k, n_seqs).
+size_t decode_partial_slots(int total_k, int n_seqs);
+hipError_t launch_decode(const void* q, const void* k, const void* v, const uint8_t* ks, const uint8_t* vs,
+                         const Plan& plan, const int* pref_base, int n_seqs, int total_k, int hq, int hkv, int d,
+                         float scale, bool mx, float* part_o, void* part_ml, hipStream_t stream);
+hipError_t launch_decode_combine(const float* part_o, const void* part_ml, void* o, float* lse, const Plan& plan,
+                                 int n_seqs, int hq, int d, hipStream_t stream);
+
 hipError_t launch_mx_quantize_d(const void* x, long n_elems, uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
 // kernel_layout: the attention kernels' internal token-blocked layout (pieces of 4 tokens in

@@ -140,12 +140,37 @@ int mx_padded_tokens(int total_tokens, int n_docs);
 size_t mx_workspace_bytes(int n_docs);
 
 /*
+ * Decoding: one new query token per sequence over a packed KV cache (the current token's K/V
+ * already appended), the last row of a causal document -- "GPT Kernel Programlama" §4-§6 -- read
+ * through flash attention from a quantised cache as local inference engines do ("Flash
+ * Attention", ai.ozdemir.be, sections "Tanım" and "Gerçek dünyadan örnek", which name an 8-bit
+ * cache type at about half the memory of f16; here: the MX format below, 8.25 bits per element).
+ *   q, o        : [n_seqs, hq, d] bf16; lse: [hq, n_seqs] float32 (natural log).
+ *   k_cache,
+ *   v_cache     : [total_k, hkv, d]; kv_dtype CFA_BF16: bf16 values; CFA_MXFP8: E4M3 codes with
+ *                 k_scales / v_scales [total_k, hkv, d/32] E8M0 bytes (mx_quantize axis 0);
+ *                 element value = code * 2^(scale - 127). Scales are NULL for CFA_BF16.
+ *   cu_seqlens_k: int32 [n_seqs + 1] in device memory (same rules as cu_seqlens); sequence b
+ *                 owns cache rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 and its query sees all
+ *                 of them. A sequence with no rows gets o = 0 and lse = -inf.
+ *   d           : 64 or 128. Query head h reads kv head h / (hq / hkv).
+ * Work is split over 256-key chunks; the chunk partials are merged in chunk order, so results
+ * are deterministic. Scratch: cfa_decode_workspace_bytes() bytes (256-byte aligned); no other
+ * allocation. Errors as for the other calls.
+ */
+size_t cfa_decode_workspace_bytes(int n_seqs, int total_k, int hq, int hkv, int d, int kv_dtype);
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, const uint8_t* k_scales,
+                const uint8_t* v_scales, void* o, float* lse, const int32_t* cu_seqlens_k,
+                const int32_t* cu_seqlens_k_host, int n_seqs, int total_k, int hq, int hkv, int d,
+                float scale, int kv_dtype, void* workspace, size_t workspace_bytes, void* stream);
+/*
  * Per-kernel timing for measurement tools. While set on the calling thread, the attention
  * calls record events[2*i] on their stream just before launching their i-th main kernel and
  * events[2*i+1] just after it (the work-list kernel is not counted). Kernel order:
  *   attn_fwd: 0 = forward attention, 1 = (MXFP8) the Q, K, V quantisation passes together;
  *   attn_bwd: 0 = D = rowsum(dO*O), 1 = dK/dV, 2 = dQ, 3 = (MXFP8) the dO, V, Q, K
- *             quantisation passes together.
+ *             quantisation passes together;
+ *   attn_decode: 0 = chunk partials, 1 = their merge.
  * Entries may be NULL (not recorded). The caller owns the hipEvent_t handles and keeps the
  * array alive while it is set; n_pairs = 0 (events NULL) switches recording off.
  */

@@ -107,3 +107,24 @@ def test_kernel_events_hook_validates():
     L = _lib.lib()
     assert L.cfa_set_kernel_events(None, 2) == 1
     assert L.cfa_set_kernel_events(None, 0) == 0
+
+
+def test_decode_rejects():
+    L = _lib.lib()
+    cu_h = np.array([0, 40, 100], dtype=np.int32)
+
+    def call(**over):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, o=FAKE, lse=FAKE, cu=FAKE, cu_h=cu_h.ctypes.data, B=2,
+                 Tk=100, hq=8, hkv=2, d=128, scale=0.088, kv=2, ws=FAKE, wsb=1 << 30)
+        a.update(over)
+        return L.attn_decode(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["o"], a["lse"], a["cu"], a["cu_h"], a["B"],
+                             a["Tk"], a["hq"], a["hkv"], a["d"], a["scale"], a["kv"], a["ws"], a["wsb"], None)
+    assert call(q=None) == 1
+    assert call(ks=None) == 1                            # an MXFP8 cache needs its scales
+    assert call(hkv=3) == 2 and call(B=0) == 2 and call(scale=-1.0) == 2
+    assert call(cu_h=np.array([0, 50, 99], dtype=np.int32).ctypes.data) == 2
+    assert call(d=256) == 3 and call(kv=0) == 3
+    assert call(o=FAKE + 4) == 4
+    assert call(wsb=64) == 5
+    assert L.cfa_decode_workspace_bytes(2, 100, 8, 2, 128, 2) > 0
+    assert L.cfa_decode_workspace_bytes(2, 100, 8, 2, 96, 2) == 0
