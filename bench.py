@@ -78,6 +78,8 @@ def parse():
                     help="only run a plain device-to-device copy of BYTES bytes 3 times (to scale the "
                          "FETCH_SIZE/WRITE_SIZE counters against a kernel of known traffic) and exit")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--decode", action="store_true",
+                    help="instead: time decoding over a packed KV cache (bf16 and MX caches; one JSON line)")
     return ap.parse_args()
 
 
@@ -224,6 +226,89 @@ def measure(w, mx, steps, warmup):
     return res
 
 
+def measure_decode(w, steps, warmup):
+    """Time attn_decode on resident inputs: wall clock over `steps` calls, and per-kernel HIP
+    events (0 = chunk partials, 1 = merge). Algorithmic bytes = the cache read once (K and V
+    codes + scales, or bf16) + Q read + O written."""
+    import ctypes
+    import torch
+    import causal_flashattention_amd as cfa
+    from causal_flashattention_amd import _lib
+
+    dev = "cuda:0"
+
+    def bf(a):
+        return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+
+    q = bf(w.q)
+    if w.kv == "mxfp8":
+        k, v = torch.from_numpy(w.k).to(dev), torch.from_numpy(w.v).to(dev)
+        ks, vs = torch.from_numpy(w.k_scales).to(dev), torch.from_numpy(w.v_scales).to(dev)
+    else:
+        k, v, ks, vs = bf(w.k), bf(w.v), None, None
+    cu = torch.from_numpy(w.cu_seqlens_k.astype(np.int32)).to(dev)
+    cu_h = torch.from_numpy(w.cu_seqlens_k.astype(np.int32))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.hq, w.n_seqs), dtype=torch.float32, device=dev)
+    kvd = cfa.CFA_MXFP8 if w.kv == "mxfp8" else cfa.CFA_BF16
+    ws = torch.empty(_lib.lib().cfa_decode_workspace_bytes(w.n_seqs, w.total_k, w.hq, w.hkv, w.d, kvd),
+                     dtype=torch.uint8, device=dev)
+    L = _lib.lib()
+
+    def call():
+        cfa.attn_decode(q, k, v, cu, k_scales=ks, v_scales=vs, scale=w.scale, cu_seqlens_k_host=cu_h, out=o,
+                        lse=lse, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for e in ev:
+        for x in e:
+            x.record()
+    torch.cuda.synchronize()
+    arrs = []
+    for e in ev:
+        a = (ctypes.c_void_p * 4)()
+        for j in range(4):
+            a[j] = e[j].cuda_event
+        arrs.append(a)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        _lib.check(L.cfa_set_kernel_events(arrs[i], 2))
+        call()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    _lib.check(L.cfa_set_kernel_events(None, 0))
+    main_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    comb_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    step_s = (t1 - t0) / steps
+    nbytes = w.kv_bytes() + 2 * 2.0 * w.n_seqs * w.hq * w.d
+    achieved = nbytes / (main_ms * 1e-3) / 1e9
+    return {"kv": w.kv, "value": nbytes / step_s / 1e9, "unit": "GB/s (algorithmic bytes / wall time per call)",
+            "ms_per_call": step_s * 1e3, "tokens_per_s": w.n_seqs / step_s,
+            "kernels_ms": {"attn_decode_kernel": round(main_ms, 4), "attn_decode_combine_kernel": round(comb_ms, 4)},
+            "roofline": {"kernel": "attn_decode_kernel", "bound": "hbm", "achieved": achieved,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "algorithmic_bytes_per_launch": nbytes, "mean_launch_ms": main_ms}}
+
+
+def main_decode(args):
+    from causal_flashattention_amd import workloads as W
+
+    cases = {"decode_batch64": (W.decode_batch_lengths(seed=7, n_seqs=64), 32, 8),
+             "decode_one_32k": ([32768], 32, 8)}
+    out = {"metric": "decode over a packed KV cache, GB/s of cache read (1 GPU)", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": True, "data": "synthetic", "results": []}
+    for name, (lengths, hq, hkv) in cases.items():
+        for kv in ("bf16", "mxfp8"):
+            w = W.make_decode(seed=11, lengths=lengths, hq=hq, hkv=hkv, kv=kv)
+            r = measure_decode(w, args.steps, args.warmup)
+            r["config"] = {"workload": name, "n_seqs": w.n_seqs, "total_k": w.total_k, "hq": hq, "hkv": hkv,
+                           "d": w.d, "seed": 11}
+            out["results"].append(r)
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -238,6 +323,9 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": a.numel() * 2}))
+        return
+    if args.decode:
+        main_decode(args)
         return
     from causal_flashattention_amd import workloads as W
 

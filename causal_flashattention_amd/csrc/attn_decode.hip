@@ -14,7 +14,7 @@
 //    transposed product, so each K/V byte read serves all of them.
 //  * 4 waves × 64 keys. A wave loads its keys' rows 32 at a time into registers (the next
 //    block's loads in flight during the current block's products), converts them to bf16
-//    (MX: v_cvt_scalef32_pk_f32_fp8 with the block scale; E4M3 × 2^e is exact in bf16) into its
+//    (MX: v_cvt_scalef32_pk_bf16_fp8 with the block scale; E4M3 × 2^e is exact in bf16) into its
 //    own swizzled LDS region, then Sᵀ = K Qᵀ and Oᵀ += Vᵀ Pᵀ with v_mfma_f32_32x32x16_bf16 and an
 //    online softmax per column. No barrier inside the key loop.
 //  * The four waves merge (max, sum, Oᵀ) through LDS; the workgroup writes one partial per
@@ -54,9 +54,13 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   __shared__ float mw[4][32], lw[4][32];
 
-  const int bid = blockIdx.x;
-  const int p = bid / (hkv * n_hb);
-  const int g = (bid / n_hb) % hkv, hb = bid % n_hb;
+  // Workgroups are dealt to the 8 XCDs round-robin. All (kv head, head block) workgroups of one
+  // chunk go to the same XCD back to back, so the cache rows of a chunk ([key][hkv][d], all kv
+  // heads contiguous) are read by one XCD at nearly the same time.
+  const int HB = hkv * n_hb;
+  const int xcd = blockIdx.x % 8, r = blockIdx.x / 8;
+  const int p = (r / HB) * 8 + xcd;
+  const int g = (r % HB) / n_hb, hb = (r % HB) % n_hb;
   int s0, L, t, b;
   if (!decode_item(plan, p, DEC_CHUNK, false, s0, L, t, &b)) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5;
@@ -82,49 +86,57 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(
   for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // ---- raw rows of one 32-key block (keys past k1 repeat key k1 - 1: masked below)
-  i32x4 kraw[LD::NL], vraw[LD::NL];
-  float ksf[LD::NL], vsf[LD::NL];
-  auto load = [&](int kb) {
+  // ---- raw rows of a 32-key block (keys past k1 repeat key k1 - 1: masked below). MX: both of
+  // the wave's blocks are loaded up front (two blocks of codes in flight per wave); bf16: one
+  // block ahead (its rows take twice the registers).
+  constexpr int NBUF = MX ? 2 : 1;
+  i32x4 kraw[NBUF][LD::NL], vraw[NBUF][LD::NL];
+  int kscw[NBUF][LD::NL], vscw[NBUF][LD::NL];   // MX: the row's D/32 scale bytes (D = 128: one word)
+  auto load = [&](int kb, int buf) {
 #pragma unroll
     for (int i = 0; i < LD::NL; ++i) {
       const int key = min(kb + i * LD::ROWS_PER_LOAD + lane / LD::LPR, k1 - 1);
       const size_t row = (size_t)(s0 + key) * hkv + g;
       const int piece = lane % LD::LPR;
-      kraw[i] = *(const i32x4*)(kc + row * LD::BYTES_PER_ROW + 16 * piece);
-      vraw[i] = *(const i32x4*)(vc + row * LD::BYTES_PER_ROW + 16 * piece);
-      if constexpr (MX) {                               // 16 codes = half of one 32-channel block
-        ksf[i] = pow2i((int)ksc[row * (D / 32) + piece / 2] - 127);
-        vsf[i] = pow2i((int)vsc[row * (D / 32) + piece / 2] - 127);
+      kraw[buf][i] = *(const i32x4*)(kc + row * LD::BYTES_PER_ROW + 16 * piece);
+      vraw[buf][i] = *(const i32x4*)(vc + row * LD::BYTES_PER_ROW + 16 * piece);
+      if constexpr (MX) {
+        if constexpr (D == 128) {
+          kscw[buf][i] = *(const int*)(ksc + row * 4);
+          vscw[buf][i] = *(const int*)(vsc + row * 4);
+        } else {
+          kscw[buf][i] = ksc[row * (D / 32) + piece / 2];
+          vscw[buf][i] = vsc[row * (D / 32) + piece / 2];
+        }
       }
     }
   };
   // ---- registers -> bf16 rows in this wave's LDS tiles
-  auto store = [&]() {
+  auto store = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < LD::NL; ++i) {
       const int r = i * LD::ROWS_PER_LOAD + lane / LD::LPR;
       const int piece = lane % LD::LPR;
       if constexpr (MX) {
+        // 16 codes = half of one 32-channel block: scale byte piece / 2 of the row
+        const int sh = D == 128 ? 8 * (piece >> 1) : 0;
+        const float ksf = pow2i(((kscw[buf][i] >> sh) & 0xFF) - 127);
+        const float vsf = pow2i(((vscw[buf][i] >> sh) & 0xFF) - 127);
         i32x4 ko[2], vo[2];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {                   // 4 codes per 32-bit word
-          const f32x2 ka = unpack_fp8x2_scaled<false>(kraw[i][u], ksf[i]);
-          const f32x2 kb2 = unpack_fp8x2_scaled<true>(kraw[i][u], ksf[i]);
-          const f32x2 va = unpack_fp8x2_scaled<false>(vraw[i][u], vsf[i]);
-          const f32x2 vb2 = unpack_fp8x2_scaled<true>(vraw[i][u], vsf[i]);
-          ko[u >> 1][2 * (u & 1)] = (int)pack_bf16x2(ka.x, ka.y);
-          ko[u >> 1][2 * (u & 1) + 1] = (int)pack_bf16x2(kb2.x, kb2.y);
-          vo[u >> 1][2 * (u & 1)] = (int)pack_bf16x2(va.x, va.y);
-          vo[u >> 1][2 * (u & 1) + 1] = (int)pack_bf16x2(vb2.x, vb2.y);
+          ko[u >> 1][2 * (u & 1)] = fp8x2_to_bf16x2_scaled<false>(kraw[buf][i][u], ksf);
+          ko[u >> 1][2 * (u & 1) + 1] = fp8x2_to_bf16x2_scaled<true>(kraw[buf][i][u], ksf);
+          vo[u >> 1][2 * (u & 1)] = fp8x2_to_bf16x2_scaled<false>(vraw[buf][i][u], vsf);
+          vo[u >> 1][2 * (u & 1) + 1] = fp8x2_to_bf16x2_scaled<true>(vraw[buf][i][u], vsf);
         }
         *(i32x4*)(kt + S::chunk(r, 2 * piece)) = ko[0];
         *(i32x4*)(kt + S::chunk(r, 2 * piece + 1)) = ko[1];
         *(i32x4*)(vt + S::chunk(r, 2 * piece)) = vo[0];
         *(i32x4*)(vt + S::chunk(r, 2 * piece + 1)) = vo[1];
       } else {
-        *(i32x4*)(kt + S::chunk(r, piece)) = kraw[i];
-        *(i32x4*)(vt + S::chunk(r, piece)) = vraw[i];
+        *(i32x4*)(kt + S::chunk(r, piece)) = kraw[buf][i];
+        *(i32x4*)(vt + S::chunk(r, piece)) = vraw[buf][i];
       }
     }
   };
@@ -174,14 +186,15 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(
   };
 
   if (kw0 < k1) {
-    load(kw0);
-    store();
     const bool second = kw0 + DEC_SUB < k1;
-    if (second) load(kw0 + DEC_SUB);                    // in flight during the first block
+    load(kw0, 0);
+    if (MX && second) load(kw0 + DEC_SUB, NBUF - 1);   // MX: both blocks in flight at once
+    store(0);
+    if (!MX && second) load(kw0 + DEC_SUB, 0);         // bf16: in flight during the first block
     block(kw0);
     if (second) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's tile reads are done
-      store();
+      store(NBUF - 1);
       block(kw0 + DEC_SUB);
     }
   }
@@ -219,31 +232,54 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(
   }
 }
 
-// Merge of a sequence's chunk partials in chunk order: o = Σ_t o_t 2^(m_t - M) / Σ_t l_t 2^(m_t - M),
-// lse = (M + log2 Σ) ln 2; a sequence without keys gets o = 0, lse = -inf. One workgroup of D
-// threads per (sequence, query head), thread d owns channel d.
+// Merge of a sequence's chunk partials: lane group c (of CL) folds chunks c, c + CL, ... with
+// the online rule (m, l, o) <- (max, l·2^(m-m') + l_t·2^(m_t-m'), o·2^(m-m') + o_t·2^(m_t-m')), then
+// the CL group results are folded in group order through LDS (a fixed order: deterministic).
+// o = o / l, lse = (m + log2 l) ln 2; a sequence without keys gets o = 0, lse = -inf. One
+// workgroup of 256 threads per (sequence, query head): D/4 threads per group, 4 channels each.
 template <int D>
-__global__ __launch_bounds__(D) void attn_decode_combine_kernel(const float* __restrict__ part_o,
-                                                                const float2* __restrict__ part_ml,
-                                                                __bf16* __restrict__ o, float* __restrict__ lse,
-                                                                Plan plan, int n_seqs, int hq) {
-  const int b = blockIdx.x / hq, h = blockIdx.x % hq, d = threadIdx.x;
+__global__ __launch_bounds__(256) void attn_decode_combine_kernel(const float* __restrict__ part_o,
+                                                                  const float2* __restrict__ part_ml,
+                                                                  __bf16* __restrict__ o, float* __restrict__ lse,
+                                                                  Plan plan, int n_seqs, int hq) {
+  constexpr int DQ = D / 4, CL = 256 / DQ;
+  __shared__ float4 so4[CL][DQ];
+  __shared__ float2 sml[CL];
+  const int b = blockIdx.x / hq, h = blockIdx.x % hq;
+  const int c0 = threadIdx.x / DQ, dq = threadIdx.x % DQ;
   const int2 di = plan.docinfo[b];
   const int s0 = di.x, L = di.y;
   const int n_ch = (L + DEC_CHUNK - 1) / DEC_CHUNK;
   const int base = dec_slot(s0, 0, b);
-  float M = -INFINITY;
-  for (int c = 0; c < n_ch; ++c) M = fmaxf(M, part_ml[(size_t)(base + c) * hq + h].x);
-  float acc = 0.f, lsum = 0.f;
-  for (int c = 0; c < n_ch; ++c) {
+  float m = -INFINITY, l = 0.f;
+  float4 acc = float4{0.f, 0.f, 0.f, 0.f};
+  for (int c = c0; c < n_ch; c += CL) {
     const float2 ml = part_ml[(size_t)(base + c) * hq + h];
-    const float f = exp2_fast(ml.x - M);
-    lsum += ml.y * f;
-    acc += part_o[((size_t)(base + c) * hq + h) * D + d] * f;
+    const float4 ot = *(const float4*)(part_o + ((size_t)(base + c) * hq + h) * D + 4 * dq);
+    const float mn = fmaxf(m, ml.x);
+    const float a = (m == -INFINITY) ? 0.f : exp2_fast(m - mn), f = exp2_fast(ml.x - mn);
+    l = l * a + ml.y * f;
+    acc = acc * a + ot * f;
+    m = mn;
   }
-  const float val = n_ch > 0 ? acc / lsum : 0.f;
-  o[((size_t)b * hq + h) * D + d] = (__bf16)val;
-  if (d == 0) lse[(size_t)h * n_seqs + b] = n_ch > 0 ? (M + __log2f(lsum)) * LN2 : -INFINITY;
+  so4[c0][dq] = acc;
+  if (dq == 0) sml[c0] = float2{m, l};
+  __syncthreads();
+  if (c0 == 0) {
+    for (int c = 1; c < CL; ++c) {
+      const float2 ml = sml[c];
+      if (ml.x == -INFINITY) continue;
+      const float mn = fmaxf(m, ml.x);
+      const float a = (m == -INFINITY) ? 0.f : exp2_fast(m - mn), f = exp2_fast(ml.x - mn);
+      l = l * a + ml.y * f;
+      acc = acc * a + so4[c][dq] * f;
+      m = mn;
+    }
+    const float inv = n_ch > 0 ? 1.f / l : 0.f;
+    __bf16* dst = o + ((size_t)b * hq + h) * D + 4 * dq;
+    *(i32x2*)dst = i32x2{(int)pack_bf16x2(acc.x * inv, acc.y * inv), (int)pack_bf16x2(acc.z * inv, acc.w * inv)};
+    if (dq == 0) lse[(size_t)h * n_seqs + b] = n_ch > 0 ? (m + __log2f(l)) * LN2 : -INFINITY;
+  }
 }
 
 size_t decode_partial_slots(int total_k, int n_seqs) {
@@ -257,7 +293,7 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const uint
   plan.pref = pref_base + pref_slot(DEC_CHUNK) * (plan.n_docs + 1);
   const int G = hq / hkv;
   const int n_hb = (G + 31) / 32;
-  const long grid = (long)decode_partial_slots(total_k, n_seqs) * hkv * n_hb;
+  const long grid = (long)((decode_partial_slots(total_k, n_seqs) + 7) / 8) * 8 * hkv * n_hb;
   if (total_k == 0) return hipSuccess;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
   const float sl2 = scale * LOG2E;
@@ -284,10 +320,10 @@ hipError_t launch_decode_combine(const float* part_o, const void* part_ml, void*
   const long grid = (long)n_seqs * hq;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
   if (d == 128)
-    hipLaunchKernelGGL(attn_decode_combine_kernel<128>, dim3((unsigned)grid), dim3(128), 0, stream, part_o,
+    hipLaunchKernelGGL(attn_decode_combine_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, part_o,
                        (const float2*)part_ml, (__bf16*)o, lse, plan, n_seqs, hq);
   else
-    hipLaunchKernelGGL(attn_decode_combine_kernel<64>, dim3((unsigned)grid), dim3(64), 0, stream, part_o,
+    hipLaunchKernelGGL(attn_decode_combine_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream, part_o,
                        (const float2*)part_ml, (__bf16*)o, lse, plan, n_seqs, hq);
   return hipGetLastError();
 }

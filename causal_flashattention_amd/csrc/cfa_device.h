@@ -131,6 +131,14 @@ __device__ inline f32x2 unpack_fp8x2_scaled(int word, float s) {
   return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, s, HI);
 }
 
+// Two E4M3 bytes (bytes 0-1, or 2-3 when HI) -> bf16 pair × s (s a power of two), packed in one
+// 32-bit word with byte 0 (2) in the low half; exact whenever the products are normal bf16
+// values (E4M3 has 3 mantissa bits): bit-identical to unpack_fp8x2_scaled + pack_bf16x2.
+template <bool HI>
+__device__ inline int fp8x2_to_bf16x2_scaled(int word, float s) {
+  return __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, s, HI));
+}
+
 // 2^e as a float for -126 <= e <= 127 (exponent field only); 2^-127 is built by ldexp.
 __device__ inline float pow2i(int e) { return e >= -126 ? __builtin_bit_cast(float, (e + 127) << 23) : 0x1p-127f; }
 
