@@ -1,4 +1,4 @@
-"""Reference MX (microscaling) quantiser: FP8 E4M3 elements with one E8M0 scale per 32.
+"""Reference MX (microscaling) quantiser: FP8 E4M3 (or FP4 E2M1) elements with one E8M0 scale per 32.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
@@ -95,6 +95,73 @@ def quantize_d(x):
     assert d % BLOCK == 0
     codes, scales = quantize_blocks(x.reshape(T, h, d // BLOCK, BLOCK))
     return codes.reshape(T, h, d), scales
+
+
+# ---------------------------------------------------------------- E2M1 (MXFP4) elements
+# E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit; no infinities or NaN; values
+# 0, 0.5 (subnormal), 1, 1.5, 2, 3, 4, 6. Same block rule as E4M3 with the format's own top
+# exponent: e = floor(log2 amax) - 2 (2 is the exponent of 4, the largest E2M1 power of two),
+# elements x·2^-e saturated to ±6 and rounded to the nearest E2M1 value, ties to the even
+# mantissa (even code). A block holding a NaN or an infinity gets scale byte 0xFF and codes 0.
+E2M1_MAX = 6.0
+E2M1_EMAX = 2
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_decode(codes):
+    """Value of each 4-bit E2M1 code (float64); bit 3 is the sign."""
+    c = np.asarray(codes, dtype=np.int64)
+    mag = E2M1_VALUES[c & 7]
+    return np.where(c & 8, -mag, mag)
+
+
+def _e2m1_encode_scaled(y):
+    """Round already-scaled, finite values y (|y| <= 6) to E2M1 codes, RNE, sign kept."""
+    a = np.abs(np.asarray(y, dtype=np.float64))
+    # nearest magnitude; on a tie (a midpoint) the even code, whose mantissa bit is 0
+    d = np.abs(a[..., None] - E2M1_VALUES)
+    best = np.argmin(d, axis=-1)
+    dmin = np.take_along_axis(d, best[..., None], axis=-1)[..., 0]
+    tie_up = (best + 1 <= 7) & np.isclose(np.abs(a - E2M1_VALUES[np.minimum(best + 1, 7)]), dmin, rtol=0, atol=0)
+    best = np.where(tie_up & (best % 2 == 1), best + 1, best)
+    return (best | np.where(np.signbit(y), 8, 0)).astype(np.int64)
+
+
+def quantize_blocks_fp4(x):
+    """Quantise rows of 32 values to E2M1 codes (one int per element, 0..15) and E8M0 scale bytes."""
+    x = np.asarray(x, dtype=np.float64)
+    finite = np.all(np.isfinite(x), axis=-1)
+    xs = np.where(np.isfinite(x), x, 0.0)
+    amax = np.max(np.abs(xs), axis=-1)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    e = np.clip(ex - 1 - E2M1_EMAX, -127, 127)
+    e = np.where(amax > 0, e, -127)
+    y = np.clip(np.ldexp(xs, -e[..., None]), -E2M1_MAX, E2M1_MAX)
+    codes = np.where(finite[..., None], _e2m1_encode_scaled(y), 0)
+    scales = np.where(finite, e + 127, 0xFF)
+    return codes.astype(np.uint8), scales.astype(np.uint8)
+
+
+def quantize_d_fp4(x):
+    """Blocks of 32 channels: x [T, h, d] -> E2M1 codes [T, h, d] (0..15), scales [T, h, d/32]."""
+    x = np.asarray(x, dtype=np.float64)
+    T, h, d = x.shape
+    assert d % BLOCK == 0
+    codes, scales = quantize_blocks_fp4(x.reshape(T, h, d // BLOCK, BLOCK))
+    return codes.reshape(T, h, d), scales
+
+
+def pack_fp4(codes):
+    """Storage layout: two codes per byte, element 2i in the low nibble -> [..., d/2] uint8."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def dequantize_d_fp4(codes, scales):
+    """Values of d-blocked E2M1 codes [T, h, d] (unpacked) with scales [T, h, d/32]."""
+    T, h, d = codes.shape
+    v = e2m1_decode(codes).reshape(T, h, d // BLOCK, BLOCK) * e8m0_decode(scales)[..., None]
+    return v.reshape(T, h, d)
 
 
 def padded_offsets(cu_seqlens):

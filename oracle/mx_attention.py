@@ -29,6 +29,11 @@ Computed exactly in float64 from the decoded copies (the decoding is exact):
 
 Not modelled: the rounding of P and dS before a matrix-core product and fp32 accumulation on
 the device.
+
+MXFP4/FP8 variant (``qk="e2m1"``): the page names a mixed NVFP4/FP8 path without saying which
+products take FP4. The reading here: the score product QKᵀ -- the one whose operands both
+passes share through ``saved`` -- takes E2M1 d-blocked copies ``Q_d``, ``K_d`` (same block rule
+with the E2M1 top exponent, see ``oracle.mx``); every other product is the MXFP8 path above.
 """
 
 import numpy as np
@@ -46,6 +51,16 @@ def operand_copies(x_b, cu_seqlens):
     return _mx.dequantize_d(cd, sd), _mx.dequantize_t(ct, st, cu_seqlens)
 
 
+def qk_copy(x_b, qk):
+    """Decoded d-blocked copy used by QKᵀ: E4M3 (``qk="e4m3"``) or E2M1 (``qk="e2m1"``)."""
+    if qk == "e2m1":
+        c, s = _mx.quantize_d_fp4(x_b)
+        return _mx.dequantize_d_fp4(c, s)
+    assert qk == "e4m3"
+    c, s = _mx.quantize_d(x_b)
+    return _mx.dequantize_d(c, s)
+
+
 def diag_pairs(n_rows, row0, n_cols, causal, tile=DIAG_TILE):
     """Boolean [rows, cols]: true where doc-local query i and key j share a tile×tile tile."""
     if not causal:
@@ -56,7 +71,7 @@ def diag_pairs(n_rows, row0, n_cols, causal, tile=DIAG_TILE):
 
 
 def attn_mx_fwd(q_b, k_b, v_b, cu_seqlens, scale, causal=True, tile=DIAG_TILE,
-                row_block=_att.ROW_BLOCK):
+                row_block=_att.ROW_BLOCK, qk="e4m3"):
     """Forward with MX operands; returns o [T, hq, d], lse [hq, T] (float64)."""
     q_b = np.asarray(q_b, np.float64)
     k_b = np.asarray(k_b, np.float64)
@@ -65,8 +80,8 @@ def attn_mx_fwd(q_b, k_b, v_b, cu_seqlens, scale, causal=True, tile=DIAG_TILE,
     T, hq, d = q_b.shape
     hkv = k_b.shape[1]
     group = hq // hkv
-    q_d, _ = operand_copies(q_b, cu)
-    k_d, _ = operand_copies(k_b, cu)
+    q_d = qk_copy(q_b, qk)
+    k_d = qk_copy(k_b, qk)
     _, v_t = operand_copies(v_b, cu)
     o = np.zeros((T, hq, d))
     lse = np.zeros((hq, T))
@@ -88,7 +103,7 @@ def attn_mx_fwd(q_b, k_b, v_b, cu_seqlens, scale, causal=True, tile=DIAG_TILE,
 
 
 def attn_mx_bwd(q_b, k_b, v_b, do_b, cu_seqlens, scale, causal=True, tile=DIAG_TILE,
-                row_block=_att.ROW_BLOCK, dlse=None):
+                row_block=_att.ROW_BLOCK, dlse=None, qk="e4m3"):
     """Backward with MX operands; returns dq [T, hq, d], dk, dv [T, hkv, d] (float64)."""
     q_b = np.asarray(q_b, np.float64)
     k_b = np.asarray(k_b, np.float64)
@@ -98,8 +113,9 @@ def attn_mx_bwd(q_b, k_b, v_b, do_b, cu_seqlens, scale, causal=True, tile=DIAG_T
     T, hq, d = q_b.shape
     hkv = k_b.shape[1]
     group = hq // hkv
-    q_d, q_t = operand_copies(q_b, cu)
-    k_d, k_t = operand_copies(k_b, cu)
+    _, q_t = operand_copies(q_b, cu)
+    _, k_t = operand_copies(k_b, cu)
+    q_d, k_d = qk_copy(q_b, qk), qk_copy(k_b, qk)
     v_d, v_t = operand_copies(v_b, cu)
     do_d, do_t = operand_copies(do_b, cu)
     dlse = np.zeros((hq, T)) if dlse is None else np.asarray(dlse, np.float64)
@@ -130,7 +146,7 @@ def attn_mx_bwd(q_b, k_b, v_b, do_b, cu_seqlens, scale, causal=True, tile=DIAG_T
     return dq, dk, dv
 
 
-def attn_mx_rows(q_b, k_b, v_b, do_b, rows, scale, causal=True, tile=DIAG_TILE):
+def attn_mx_rows(q_b, k_b, v_b, do_b, rows, scale, causal=True, tile=DIAG_TILE, qk="e4m3"):
     """Selected query rows of ONE document with MX operands (doc-local arrays).
 
     The MX counterpart of ``oracle.attention.attn_rows`` for documents too long for the full
@@ -148,8 +164,9 @@ def attn_mx_rows(q_b, k_b, v_b, do_b, rows, scale, causal=True, tile=DIAG_TILE):
     hkv = k_b.shape[1]
     group = hq // hkv
     cu = np.array([0, L])
-    q_d, q_t = operand_copies(q_b, cu)
-    k_d, k_t = operand_copies(k_b, cu)
+    _, q_t = operand_copies(q_b, cu)
+    _, k_t = operand_copies(k_b, cu)
+    q_d, k_d = qk_copy(q_b, qk), qk_copy(k_b, qk)
     v_d, v_t = operand_copies(v_b, cu)
     do_d, do_t = operand_copies(do_b, cu)
     n = len(rows)
