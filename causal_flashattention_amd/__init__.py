@@ -18,7 +18,7 @@ import torch
 from . import _lib
 from ._lib import CFA_BF16, CFA_F32, CFA_MXFP8, CfaError
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "mx_quantize", "workspace_bytes", "saved_bytes", "CfaError",
+__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "mx_quantize", "mx_quantize_fp4", "workspace_bytes", "saved_bytes", "CfaError",
            "CFA_F32", "CFA_BF16", "CFA_MXFP8", "library_path"]
 
 
@@ -162,6 +162,20 @@ def attn_decode(q, k_cache, v_cache, cu_seqlens_k, *, k_scales=None, v_scales=No
                              _ptr(lse), _ptr(cu_seqlens_k), _ptr(hcu) if hcu is not None else None, B, Tk, hq, hkv,
                              d, scale, kv, _ptr(workspace), workspace.numel(), _stream()))
     return out, lse
+
+
+def mx_quantize_fp4(x, *, codes=None, scales=None):
+    """MXFP4 (E2M1 + E8M0) quantisation of bf16 ``x [T, h, d]`` in blocks of 32 channels.
+    Returns (codes [T, h, d/2] uint8, two per byte, scales [T, h, d/32] uint8)."""
+    L = _lib.lib()
+    _check_dev(x, codes, scales)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bf16")
+    T, h, d = x.shape
+    codes = torch.empty((T, h, d // 2), dtype=torch.uint8, device=x.device) if codes is None else codes
+    scales = torch.empty((T, h, d // 32), dtype=torch.uint8, device=x.device) if scales is None else scales
+    _lib.check(L.mx_quantize_fp4(_ptr(x), T, h, d, _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales
 
 
 def mx_quantize(x, cu_seqlens, axis, *, cu_seqlens_host=None, t_pad=None, codes=None, scales=None,

@@ -25,6 +25,7 @@ SIGNATURES = {
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I,
                       _P, _S, _P]),
     "mx_quantize": (_I, [_P, _I, _I, _I, _P, _P, _I, _I, _P, _P, _I, _P, _S, _P]),
+    "mx_quantize_fp4": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "mx_padded_tokens": (_I, [_I, _I]),
     "mx_workspace_bytes": (_S, [_I]),
     "cfa_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I]),

@@ -383,6 +383,18 @@ int mx_quantize(const void* x, int total_tokens, int h, int d, const int32_t* cu
                    "mx_quantize_t");
 }
 
+int mx_quantize_fp4(const void* x, int total_tokens, int h, int d, uint8_t* codes, uint8_t* scales, void* stream) {
+  g_err[0] = 0;
+  if (total_tokens < 0 || h < 1) return fail(CFA_ERR_SHAPE, "total_tokens = %d, h = %d", total_tokens, h);
+  if (d != 64 && d != 128) return fail(CFA_ERR_UNSUPPORTED, "mx_quantize_fp4 supports d = 64 or 128 (got %d)", d);
+  if (total_tokens > 0 && (!x || !codes || !scales)) return fail(CFA_ERR_NULL, "x, codes and scales must not be NULL");
+  for (const void* p : {x, (const void*)codes})
+    if (!aligned(p, 16)) return fail(CFA_ERR_ALIGN, "x and codes must be 16-byte aligned");
+  if (total_tokens == 0) return CFA_OK;
+  return check_hip(cfa::launch_mx_quantize_d_fp4(x, (long)total_tokens * h * d, codes, scales, (hipStream_t)stream),
+                   "mx_quantize_d_fp4");
+}
+
 // ---------------------------------------------------------------- decoding over a KV cache
 namespace {
 struct DecLayout {

@@ -54,6 +54,8 @@ hipError_t launch_decode_combine(const float* part_o, const void* part_ml, void*
                                  int n_seqs, int hq, int d, hipStream_t stream);
 
 hipError_t launch_mx_quantize_d(const void* x, long n_elems, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+// E2M1 codes packed two per byte ([n_elems / 2] bytes), E8M0 scales [n_elems / 32].
+hipError_t launch_mx_quantize_d_fp4(const void* x, long n_elems, uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
 // kernel_layout: the attention kernels' internal token-blocked layout (pieces of 4 tokens in
 // the order 0,2,4,6,1,3,5,7 within each 32-token block; scales [h, t_pad/32, d]); otherwise the

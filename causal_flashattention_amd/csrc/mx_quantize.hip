@@ -1,4 +1,4 @@
-// MX quantiser for gfx950: bf16 -> FP8 E4M3 codes + E8M0 scales, one scale per 32 elements.
+// MX quantiser for gfx950: bf16 -> FP8 E4M3 (or FP4 E2M1) codes + E8M0 scales, one scale per 32.
 //
 // The MXFP8 attention path and its document-local token-block scaling are named on the FLAMIA
 // page ("FLAMIA Mimarisi ve Temel Tasarım İlkeleri"); the bit-level rule is the public MX one:
@@ -67,6 +67,59 @@ __global__ __launch_bounds__(256) void mx_quantize_d_kernel(const __bf16* __rest
   const int e = mx_exponent(amax);
   i32x2 c = badi ? i32x2{0x7F7F7F7F, 0x7F7F7F7F} : mx_encode8(v, e);
   *(i32x2*)(codes + blk * 32 + sub * 8) = c;
+  if (sub == 0) scales[blk] = badi ? 0xFF : (uint8_t)(e + 127);
+}
+
+// E2M1 (MXFP4) along d: the same block rule with the E2M1 top exponent 2, e = floor(log2 amax) - 2;
+// elements x·2^-e clamped to ±6 and rounded to the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to
+// the even code (mantissa bit 0); sign kept (also of zero). A NaN/Inf block gets scale 0xFF and
+// codes 0. Codes are packed two per byte, element 2i in the low nibble: [T, h, d/2].
+__device__ inline int mx_exponent_fp4(float amax) {
+  if (!(amax > 0.f)) return -127;
+  const int ex = __builtin_amdgcn_frexp_expf(amax);
+  return min(max(ex - 1 - 2, -127), 127);
+}
+__device__ inline int e2m1_code(float y) {
+  const float a = fabsf(y);
+  const int c = a <= 0.25f ? 0 : a < 0.75f ? 1 : a <= 1.25f ? 2 : a < 1.75f ? 3
+              : a <= 2.5f ? 4 : a < 3.5f ? 5 : a <= 5.f ? 6 : 7;
+  return c | (__builtin_signbit(y) ? 8 : 0);
+}
+
+__global__ __launch_bounds__(256) void mx_quantize_d_fp4_kernel(const __bf16* __restrict__ x,
+                                                                uint8_t* __restrict__ codes,
+                                                                uint8_t* __restrict__ scales, long n_blocks) {
+  const long blk = (long)blockIdx.x * 64 + threadIdx.x / 4;
+  const int sub = threadIdx.x & 3;
+  float v[8];
+  float amax = 0.f;
+  bool bad = false;
+  if (blk < n_blocks) {
+    const bf16x8 u = __builtin_bit_cast(bf16x8, *(const i32x4*)(x + blk * 32 + sub * 8));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[e] = (float)u[e];
+      bad |= !__builtin_isfinite(v[e]);
+      amax = fmaxf(amax, fabsf(v[e]));
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  int badi = bad ? 1 : 0;
+  badi |= __shfl_xor(badi, 1);
+  badi |= __shfl_xor(badi, 2);
+  if (blk >= n_blocks) return;
+  const int e = mx_exponent_fp4(amax);
+  uint32_t word = 0;
+  if (!badi) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      word |= (uint32_t)e2m1_code(fminf(fmaxf(__builtin_amdgcn_ldexpf(v[j], -e), -6.f), 6.f)) << (4 * j);
+  }
+  *(uint32_t*)(codes + blk * 16 + sub * 4) = word;
   if (sub == 0) scales[blk] = badi ? 0xFF : (uint8_t)(e + 127);
 }
 
@@ -162,6 +215,16 @@ hipError_t launch_mx_quantize_d(const void* x, long n_elems, uint8_t* codes, uin
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(mx_quantize_d_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)x, codes, scales,
                      n_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quantize_d_fp4(const void* x, long n_elems, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  const long n_blocks = n_elems / 32;
+  if (n_blocks == 0) return hipSuccess;
+  const long grid = (n_blocks + 63) / 64;
+  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(mx_quantize_d_fp4_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)x, codes,
+                     scales, n_blocks);
   return hipGetLastError();
 }
 

@@ -132,6 +132,15 @@ int mx_quantize(const void* x, int total_tokens, int h, int d,
                 uint8_t* codes, uint8_t* scales, int t_pad,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * MXFP4 quantiser along d: bf16 x [total_tokens, h, d] -> E2M1 codes packed two per byte
+ * (element 2i in the low nibble) [total_tokens, h, d/2] + E8M0 scales [total_tokens, h, d/32].
+ * Per 32-channel block: e = floor(log2 amax) - 2 clamped to [-127, 127] (-127 for a zero block);
+ * elements x * 2^-e saturated to +-6 and rounded to the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6
+ * (ties to the even code; sign of zero kept); a NaN/Inf block gets scale 0xFF and codes 0. The
+ * score operands of the CFA_MXFP4 attention path are these copies of Q and K.
+ */
+int mx_quantize_fp4(const void* x, int total_tokens, int h, int d, uint8_t* codes, uint8_t* scales, void* stream);
 /* Upper bound of P_{n_docs} for any cu_seqlens with these sizes, rounded up to 32:
  * 32*ceil(total_tokens/32) + 32*n_docs. */
 int mx_padded_tokens(int total_tokens, int n_docs);

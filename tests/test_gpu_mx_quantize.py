@@ -72,3 +72,22 @@ def test_mx_quantize_workload_4_sampled_heads():
             assert np.array_equal(c1[hh:hh + 1, :, :tp].cpu().numpy(), rc)
             assert np.array_equal(s1[hh:hh + 1, :, :tp // 32].cpu().numpy(), rs)
         del x, c0, s0, c1, s1
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_mx_quantize_fp4_bit_exact(d):
+    """E2M1 codes (packed) and scale bytes bit-identical to the reference, special values included;
+    plus a tensor whose scaled elements sit exactly on E2M1 midpoints (ties to the even code)."""
+    T, h = 97, 3
+    xb = _special_tensor(T, h, d, seed=40 + d)
+    rng = np.random.default_rng(41)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 4.0, -0.75, -5.0, 0.0], dtype=np.float32)
+    xm = rng.choice(mids, size=(T, h, d)).astype(np.float32)
+    xm[:, :, ::32] = 6.0                       # block max 6: e = 0, elements are the midpoints themselves
+    for xin in (xb, W.f32_to_bf16_bits(xm)):
+        announce("mx_quantize_fp4", d)
+        c, s = cfa.mx_quantize_fp4(to_dev(xin))
+        torch.cuda.synchronize()
+        rc, rs = mx.quantize_d_fp4(W.bf16_bits_to_f64(xin))
+        assert np.array_equal(c.cpu().numpy(), mx.pack_fp4(rc))
+        assert np.array_equal(s.cpu().numpy(), rs)
