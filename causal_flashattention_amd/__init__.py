@@ -16,10 +16,10 @@ import math
 import torch
 
 from . import _lib
-from ._lib import CFA_BF16, CFA_F32, CFA_MXFP8, CfaError
+from ._lib import CFA_BF16, CFA_F32, CFA_MXFP4, CFA_MXFP8, CfaError
 
 __all__ = ["attn_fwd", "attn_bwd", "attn_decode", "mx_quantize", "mx_quantize_fp4", "workspace_bytes", "saved_bytes", "CfaError",
-           "CFA_F32", "CFA_BF16", "CFA_MXFP8", "library_path"]
+           "CFA_F32", "CFA_BF16", "CFA_MXFP8", "CFA_MXFP4", "library_path"]
 
 
 def library_path():
@@ -43,10 +43,15 @@ def _host_cu(cu_seqlens, cu_seqlens_host):
 
 
 def _dtype_code(x, mx):
+    """mx: False (bf16 / fp32 by x.dtype), True or "mxfp8" (MXFP8), "mxfp4" (MXFP4/FP8)."""
     if mx:
         if x.dtype != torch.bfloat16:
-            raise TypeError("the MXFP8 path takes bf16 inputs")
-        return CFA_MXFP8
+            raise TypeError("the MX paths take bf16 inputs")
+        if mx == "mxfp4":
+            return CFA_MXFP4
+        if mx is True or mx == "mxfp8":
+            return CFA_MXFP8
+        raise ValueError(f"unknown MX path {mx!r}")
     if x.dtype == torch.bfloat16:
         return CFA_BF16
     if x.dtype == torch.float32:

@@ -9,7 +9,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcfa.so")
 
-CFA_F32, CFA_BF16, CFA_MXFP8 = 0, 1, 2
+CFA_F32, CFA_BF16, CFA_MXFP8, CFA_MXFP4 = 0, 1, 2, 3
 STATUS = {0: "CFA_OK", 1: "CFA_ERR_NULL", 2: "CFA_ERR_SHAPE", 3: "CFA_ERR_UNSUPPORTED",
           4: "CFA_ERR_ALIGN", 5: "CFA_ERR_WORKSPACE", 6: "CFA_ERR_HIP"}
 

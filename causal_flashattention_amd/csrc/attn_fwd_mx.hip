@@ -15,8 +15,12 @@
 // Work list, online softmax, Sᵀ orientation and the two static LDS buffers filled by direct
 // global -> LDS copies follow the bf16 kernel in attn_fwd.hip.
 //
+// MXFP4/FP8 (FP4 = true): the score product takes E2M1 copies Q_d, K_d (two codes per byte,
+// 64-byte rows for d = 128, blocks of 32 channels with E8M0 scales) through the same
+// instruction with format code 4 on both operands; the rest is the MXFP8 path unchanged.
+//
 // LDS tile (64 keys): K_d codes as 128-byte rows whose 16-byte chunks are XOR-swizzled with
-// (row / 2) % 8, then 4 scale bytes per key; then either the bf16 V rows of a diagonal tile
+// (row / 2) % 8 (FP4: 64-byte rows swizzled with (row / 4) % 4), then 4 scale bytes per key; then either the bf16 V rows of a diagonal tile
 // (SwzTile<128>) or the V_t codes as 64-byte channel rows swizzled with (row / 4) % 4 and the
 // 2 × 128 scale bytes of the tile's two key blocks. Both swizzles send the 16 rows read by a
 // 16-lane group to 16 distinct 16-byte bank groups. V_t comes in the kernels' token-blocked
@@ -32,23 +36,25 @@ namespace cfa {
 // no lane's maximum grew.
 constexpr float RESCALE_LOG2_MX = 0.f;
 
+template <bool FP4>
 struct MxFwdTile {
   static constexpr int BN = 64;
   static constexpr int D = 128;
-  static constexpr int OFF_KSC = BN * 128;           // K_d codes: 64 rows × 128 B
+  static constexpr int KROW = FP4 ? D / 2 : D;       // bytes of one K_d row
+  static constexpr int OFF_KSC = BN * KROW;          // K_d codes: 64 rows
   static constexpr int OFF_V = OFF_KSC + BN * 4;     // K_d scales: 4 B per key
   static constexpr int OFF_VTSC = OFF_V + D * 64;    // V_t codes: 128 channel rows × 64 B
   static constexpr int STAGE = OFF_V + BN * 256;     // union with the bf16 V rows (64 × 256 B)
 };
 
-template <int HPW>
+template <int HPW, bool FP4>
 __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
     const uint8_t* __restrict__ qd, const uint8_t* __restrict__ qd_sc, const uint8_t* __restrict__ kd,
     const uint8_t* __restrict__ kd_sc, const uint8_t* __restrict__ vt, const uint8_t* __restrict__ vt_sc,
     const __bf16* __restrict__ v, __bf16* __restrict__ o, float* __restrict__ lse, Plan plan,
     const int* __restrict__ padoff, int total_tokens, int t_pad, int hq, int hkv, int n_hb, float scale_log2,
     int causal) {
-  using C = MxFwdTile;
+  using C = MxFwdTile<FP4>;
   constexpr int D = C::D;
   constexpr int BMW = 128 / HPW;
   __shared__ __attribute__((aligned(16))) char lds_a[C::STAGE];
@@ -76,7 +82,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int u = 0; u < 2; ++u) ko[s][u] = 16 * ((4 * s + 2 * u + half) ^ kd_swz(r32));
+    for (int u = 0; u < 2; ++u)
+      ko[s][u] = FP4 ? 16 * ((2 * s + half) ^ vt_swz(r32)) : 16 * ((4 * s + 2 * u + half) ^ kd_swz(r32));
 #pragma unroll
   for (int u = 0; u < 2; ++u) vo[u] = 16 * ((2 * u + half) ^ vt_swz(r32));
 
@@ -88,9 +95,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
     const size_t row = (size_t)(s0 + (ok ? qrow : 0)) * hq + h;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const i32x4 lo = ok ? *(const i32x4*)(qd + row * D + 64 * s + 16 * half) : i32x4{0, 0, 0, 0};
-      const i32x4 hi = ok ? *(const i32x4*)(qd + row * D + 64 * s + 32 + 16 * half) : i32x4{0, 0, 0, 0};
-      qa[s] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      if constexpr (FP4) {   // channels 64s + 32·half .. +31: 16 bytes
+        qa[s] = fp4_operand(ok ? *(const i32x4*)(qd + row * (D / 2) + 32 * s + 16 * half) : i32x4{0, 0, 0, 0});
+      } else {
+        const i32x4 lo = ok ? *(const i32x4*)(qd + row * D + 64 * s + 16 * half) : i32x4{0, 0, 0, 0};
+        const i32x4 hi = ok ? *(const i32x4*)(qd + row * D + 64 * s + 32 + 16 * half) : i32x4{0, 0, 0, 0};
+        qa[s] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      }
       qs[s] = ok ? qd_sc[row * 4 + 2 * s + half] : 127;
     }
   }
@@ -103,16 +114,22 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
   // Tile kt -> LDS with direct copies. Keys past kv_end are clamped into the document (K_d,
   // bf16 V) or into its last token block (V_t); they are masked (P = 0).
   // Addresses: a wave-uniform 64-bit tile base plus a 32-bit lane offset within the tile.
-  const uint32_t tok_b = (uint32_t)hkv * D;     // bytes between consecutive tokens of K_d
+  const uint32_t tok_b = (uint32_t)hkv * D;     // bytes between consecutive tokens of K_d (E4M3)
   auto stage = [&](int kt, char* tb) {
     const int k0 = kt * C::BN;
     const int rmax = kv_end - 1 - k0;
     const size_t tok0 = (size_t)(s0 + k0) * hkv + g;
-    const uint8_t* kdb = kd + tok0 * D;
+    if constexpr (FP4) {                        // K_d codes: 4 blocks of 16 rows, 1 per wave
+      const uint8_t* kdb = kd + tok0 * (D / 2);
+      const int r = 16 * w + (lane >> 2);
+      g2lds16(kdb + ((uint32_t)min(r, rmax) * (tok_b / 2) + 16 * ((lane & 3) ^ vt_swz(r))), tb + w * 1024);
+    } else {
+      const uint8_t* kdb = kd + tok0 * D;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {               // K_d codes: 8 blocks of 8 rows, 2 per wave
-      const int I = 2 * w + j, r = 8 * I + (lane >> 3);
-      g2lds16(kdb + ((uint32_t)min(r, rmax) * tok_b + 16 * ((lane & 7) ^ kd_swz(r))), tb + I * 1024);
+      for (int j = 0; j < 2; ++j) {             // K_d codes: 8 blocks of 8 rows, 2 per wave
+        const int I = 2 * w + j, r = 8 * I + (lane >> 3);
+        g2lds16(kdb + ((uint32_t)min(r, rmax) * tok_b + 16 * ((lane & 7) ^ kd_swz(r))), tb + I * 1024);
+      }
     }
     if (w == 0) g2lds4(kd_sc + tok0 * 4 + (uint32_t)min(lane, rmax) * (uint32_t)hkv * 4, tb + C::OFF_KSC);
     if (tile_is_diag(kt)) {
@@ -140,7 +157,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
     const int k0 = kt * C::BN;
     if (kt + 1 < n_kt) stage(kt + 1, nxt);
     if (k0 <= wave_last_key) {
-      // ---- Sᵀ = K_d Q_dᵀ (scaled fp8), the two 32-key blocks interleaved
+      // ---- Sᵀ = K_d Q_dᵀ (scaled fp8, or fp4), the two 32-key blocks interleaved
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
       int ksc[2];
 #pragma unroll
@@ -149,11 +166,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-          const char* kr = tb + (32 * b + r32) * 128;
-          const i32x4 lo = *(const i32x4*)(kr + ko[s][0]);
-          const i32x4 hi = *(const i32x4*)(kr + ko[s][1]);
-          sacc[b] = mfma32_mx(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w},
-                              (ksc[b] >> (8 * (2 * s + half))) & 0xFF, qa[s], qs[s], sacc[b]);
+          const char* kr = tb + (32 * b + r32) * C::KROW;
+          const int sa = (ksc[b] >> (8 * (2 * s + half))) & 0xFF;
+          if constexpr (FP4) {
+            sacc[b] = mfma32_mx_fp4(fp4_operand(*(const i32x4*)(kr + ko[s][0])), sa, qa[s], qs[s], sacc[b]);
+          } else {
+            const i32x4 lo = *(const i32x4*)(kr + ko[s][0]);
+            const i32x4 hi = *(const i32x4*)(kr + ko[s][1]);
+            sacc[b] = mfma32_mx(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, sa, qa[s], qs[s], sacc[b]);
+          }
         }
       // ---- online softmax: maximum on the raw scores (scale_log2 > 0), scale folded into the
       // exponent, masks only on tiles crossing the diagonal or the document end (wave-uniform)
@@ -262,7 +283,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
 hipError_t launch_fwd_mx(const uint8_t* qd, const uint8_t* qd_sc, const uint8_t* kd, const uint8_t* kd_sc,
                          const uint8_t* vt, const uint8_t* vt_sc, const void* v, void* o, float* lse,
                          const Plan& plan_any, const int* pref_base, const int* padoff, int total_tokens, int t_pad,
-                         int hq, int hkv, float scale, int causal, hipStream_t stream) {
+                         int hq, int hkv, float scale, int causal, bool fp4, hipStream_t stream) {
   const int G = hq / hkv;
   const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
   const int rows = 128 / hpw;
@@ -273,13 +294,19 @@ hipError_t launch_fwd_mx(const uint8_t* qd, const uint8_t* qd_sc, const uint8_t*
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
   const float sl2 = scale * LOG2E;
-#define CFA_MXF_LAUNCH(HH)                                                                                    \
-  hipLaunchKernelGGL(attn_fwd_mx_kernel<HH>, dim3((unsigned)grid), dim3(256), 0, stream, qd, qd_sc, kd, kd_sc, vt, \
-                     vt_sc, (const __bf16*)v, (__bf16*)o, lse, plan, padoff, total_tokens, t_pad, hq, hkv, n_hb, sl2, \
+#define CFA_MXF_LAUNCH(HH, F4)                                                                                 \
+  hipLaunchKernelGGL((attn_fwd_mx_kernel<HH, F4>), dim3((unsigned)grid), dim3(256), 0, stream, qd, qd_sc, kd, kd_sc,  \
+                     vt, vt_sc, (const __bf16*)v, (__bf16*)o, lse, plan, padoff, total_tokens, t_pad, hq, hkv, n_hb, sl2, \
                      causal)
-  if (hpw == 4) CFA_MXF_LAUNCH(4);
-  else if (hpw == 2) CFA_MXF_LAUNCH(2);
-  else CFA_MXF_LAUNCH(1);
+  if (fp4) {
+    if (hpw == 4) CFA_MXF_LAUNCH(4, true);
+    else if (hpw == 2) CFA_MXF_LAUNCH(2, true);
+    else CFA_MXF_LAUNCH(1, true);
+  } else {
+    if (hpw == 4) CFA_MXF_LAUNCH(4, false);
+    else if (hpw == 2) CFA_MXF_LAUNCH(2, false);
+    else CFA_MXF_LAUNCH(1, false);
+  }
 #undef CFA_MXF_LAUNCH
   return hipGetLastError();
 }

@@ -66,10 +66,10 @@ int check_sizes(const Sizes& s, bool bwd) {
   if (s.hq < 1 || s.hkv < 1) return fail(CFA_ERR_SHAPE, "hq = %d, hkv = %d must be >= 1", s.hq, s.hkv);
   if (s.hq % s.hkv) return fail(CFA_ERR_SHAPE, "hq = %d is not a multiple of hkv = %d", s.hq, s.hkv);
   if ((long)s.T * s.hq * s.d > 0x7fffffffL * 8L) return fail(CFA_ERR_SHAPE, "tensor too large");
-  if (s.dtype != CFA_F32 && s.dtype != CFA_BF16 && s.dtype != CFA_MXFP8)
+  if (s.dtype != CFA_F32 && s.dtype != CFA_BF16 && s.dtype != CFA_MXFP8 && s.dtype != CFA_MXFP4)
     return fail(CFA_ERR_UNSUPPORTED, "dtype %d unknown", s.dtype);
-  if (s.dtype == CFA_MXFP8) {
-    if (s.d != 128) return fail(CFA_ERR_UNSUPPORTED, "MXFP8 supports d = 128 only (got %d)", s.d);
+  if (s.dtype == CFA_MXFP8 || s.dtype == CFA_MXFP4) {
+    if (s.d != 128) return fail(CFA_ERR_UNSUPPORTED, "the MX paths support d = 128 only (got %d)", s.d);
   } else if (s.dtype == CFA_F32 && s.d != 64 && s.d != 128) {
     return fail(CFA_ERR_UNSUPPORTED, "the fp32 path supports d = 64 or 128 (got %d)", s.d);
   } else if (s.d != 64 && s.d != 128 && s.d != 256) {
@@ -86,10 +86,12 @@ struct MxBuf {
 
 int t_pad_of(const Sizes& s) { return (s.T + 31) / 32 * 32 + 32 * s.n_docs; }
 
-// d-blocked copy of a [T, h, d] tensor: codes [T, h, d], scales [T, h, d/32]
-size_t add_mx_d(size_t off, const Sizes& s, int h, MxBuf& b) {
+bool is_mx(int dtype) { return dtype == CFA_MXFP8 || dtype == CFA_MXFP4; }
+
+// d-blocked copy of a [T, h, d] tensor: codes [T, h, d] (E2M1: [T, h, d/2]), scales [T, h, d/32]
+size_t add_mx_d(size_t off, const Sizes& s, int h, MxBuf& b, bool fp4 = false) {
   b.codes = off;
-  off = cfa::align256(off + (size_t)s.T * h * s.d);
+  off = cfa::align256(off + (size_t)s.T * h * (fp4 ? s.d / 2 : s.d));
   b.scales = off;
   return cfa::align256(off + (size_t)s.T * h * (s.d / 32));
 }
@@ -130,7 +132,7 @@ WsLayout ws_layout(int pass, const Sizes& s) {
       }
     }
   }
-  if (s.dtype == CFA_MXFP8) {
+  if (is_mx(s.dtype)) {
     if (pass == 0) {
       off = add_mx_t(off, s, s.hkv, w.vt);
     } else {
@@ -145,7 +147,7 @@ WsLayout ws_layout(int pass, const Sizes& s) {
   return w;
 }
 
-// forward-to-backward buffer of the MX path: Q_d and K_d
+// forward-to-backward buffer of the MX paths: Q_d and K_d (E4M3, or E2M1 for CFA_MXFP4)
 struct SavedLayout {
   MxBuf qd, kd;
   size_t total;
@@ -154,8 +156,9 @@ struct SavedLayout {
 SavedLayout saved_layout(const Sizes& s) {
   SavedLayout v{};
   size_t off = 0;
-  off = add_mx_d(off, s, s.hq, v.qd);
-  off = add_mx_d(off, s, s.hkv, v.kd);
+  const bool fp4 = s.dtype == CFA_MXFP4;
+  off = add_mx_d(off, s, s.hq, v.qd, fp4);
+  off = add_mx_d(off, s, s.hkv, v.kd, fp4);
   v.total = off;
   return v;
 }
@@ -200,7 +203,7 @@ size_t cfa_workspace_bytes(int pass, int total_tokens, int n_docs, int hq, int h
 
 size_t cfa_saved_bytes(int total_tokens, int n_docs, int hq, int hkv, int d, int dtype) {
   Sizes s{total_tokens, n_docs, hq, hkv, d, dtype};
-  if (dtype != CFA_MXFP8 || check_sizes(s, false) != CFA_OK) return 0;
+  if (!is_mx(dtype) || check_sizes(s, false) != CFA_OK) return 0;
   return saved_layout(s).total;
 }
 
@@ -215,8 +218,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, c
   if (total_tokens > 0 && (!q || !k || !v || !o || !lse))
     return fail(CFA_ERR_NULL, "q, k, v, o and lse must not be NULL");
   if (!(std::isfinite(scale) && scale > 0.f)) return fail(CFA_ERR_SHAPE, "scale must be finite and > 0");
-  if (dtype == CFA_MXFP8 && !saved) return fail(CFA_ERR_NULL, "MXFP8 needs the `saved` buffer");
-  if (dtype == CFA_MXFP8 && !aligned(saved, 256)) return fail(CFA_ERR_ALIGN, "saved must be 256-byte aligned");
+  if (is_mx(dtype) && !saved) return fail(CFA_ERR_NULL, "the MX paths need the `saved` buffer");
+  if (is_mx(dtype) && !aligned(saved, 256)) return fail(CFA_ERR_ALIGN, "saved must be 256-byte aligned");
   for (const void* p : {q, k, v, (const void*)o, (const void*)lse, (const void*)cu_seqlens})
     if (!aligned(p, 16)) return fail(CFA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
   if (!aligned(workspace, 256)) return fail(CFA_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -230,18 +233,20 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, c
   if (total_tokens == 0) return CFA_OK;
   const cfa::Plan plan = make_plan(workspace, n_docs);
   hipError_t e;
-  if (dtype == CFA_MXFP8) {
+  if (is_mx(dtype)) {
     char* ws = (char*)workspace;
     char* sv = (char*)saved;
     const SavedLayout sl = saved_layout(s);
     const cfa::PlanLayout pl(n_docs);
     const int tp = t_pad_of(s);
+    const bool fp4 = dtype == CFA_MXFP4;
+    auto quant_d = fp4 ? cfa::launch_mx_quantize_d_fp4 : cfa::launch_mx_quantize_d;
     mark(1, 0, st);
-    if (int r = check_hip(cfa::launch_mx_quantize_d(q, (long)total_tokens * hq * d, (uint8_t*)sv + sl.qd.codes,
-                                                    (uint8_t*)sv + sl.qd.scales, st), "quantize Q"))
+    if (int r = check_hip(quant_d(q, (long)total_tokens * hq * d, (uint8_t*)sv + sl.qd.codes,
+                                  (uint8_t*)sv + sl.qd.scales, st), "quantize Q"))
       return r;
-    if (int r = check_hip(cfa::launch_mx_quantize_d(k, (long)total_tokens * hkv * d, (uint8_t*)sv + sl.kd.codes,
-                                                    (uint8_t*)sv + sl.kd.scales, st), "quantize K"))
+    if (int r = check_hip(quant_d(k, (long)total_tokens * hkv * d, (uint8_t*)sv + sl.kd.codes,
+                                  (uint8_t*)sv + sl.kd.scales, st), "quantize K"))
       return r;
     if (int r = check_hip(cfa::launch_mx_quantize_t(v, total_tokens, hkv, d, ws, n_docs, (uint8_t*)ws + wl.vt.codes,
                                                     (uint8_t*)ws + wl.vt.scales, tp, true, st), "quantize V"))
@@ -251,7 +256,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, c
     e = cfa::launch_fwd_mx((const uint8_t*)sv + sl.qd.codes, (const uint8_t*)sv + sl.qd.scales,
                            (const uint8_t*)sv + sl.kd.codes, (const uint8_t*)sv + sl.kd.scales,
                            (const uint8_t*)ws + wl.vt.codes, (const uint8_t*)ws + wl.vt.scales, v, o, lse, plan,
-                           plan.pref, (const int*)(ws + pl.padoff), total_tokens, tp, hq, hkv, scale, causal, st);
+                           plan.pref, (const int*)(ws + pl.padoff), total_tokens, tp, hq, hkv, scale, causal, fp4, st);
     mark(0, 1, st);
     return check_hip(e, "MX forward kernel");
   }
@@ -275,6 +280,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   if (total_tokens > 0 && (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv))
     return fail(CFA_ERR_NULL, "q, k, v, o, lse, dout, dq, dk and dv must not be NULL");
   if (!(std::isfinite(scale) && scale > 0.f)) return fail(CFA_ERR_SHAPE, "scale must be finite and > 0");
+  if (dtype == CFA_MXFP4) return fail(CFA_ERR_UNSUPPORTED, "the MXFP4/FP8 backward is not built");
   if (dtype == CFA_MXFP8 && !saved) return fail(CFA_ERR_NULL, "MXFP8 needs the forward's `saved` buffer");
   if (dtype == CFA_MXFP8 && !aligned(saved, 256)) return fail(CFA_ERR_ALIGN, "saved must be 256-byte aligned");
   for (const void* p : {q, k, v, o, (const void*)lse, dout, (const void*)dlse, (const void*)dq, (const void*)dk,

@@ -109,6 +109,14 @@ __device__ inline f32x16 mfma32_mx(i32x8 a, int sa, i32x8 b, int sb, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
+// Scaled MFMA with E2M1 (FP4, format code 4) A and B: operand layout per lane l: row/column l%32,
+// k = 32·(l/32) + 0..31 in bytes 0-15, element 2i in the low nibble of byte i (bytes 16-31
+// unused); scales as above (pinned by a probe against a CPU product, also mixed with an E4M3 B).
+__device__ inline f32x16 mfma32_mx_fp4(i32x8 a, int sa, i32x8 b, int sb, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
+}
+__device__ inline i32x8 fp4_operand(i32x4 u) { return i32x8{u.x, u.y, u.z, u.w, 0, 0, 0, 0}; }
+
 // Four floats -> four E4M3 bytes (round to nearest even; inputs must already lie in ±448).
 __device__ inline int pack_fp8x4(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);

@@ -63,10 +63,11 @@ hipError_t launch_mx_quantize_d_fp4(const void* x, long n_elems, uint8_t* codes,
 hipError_t launch_mx_quantize_t(const void* x, int total_tokens, int h, int d, const void* ws, int n_docs,
                                 uint8_t* codes, uint8_t* scales, int t_pad, bool kernel_layout, hipStream_t stream);
 
+// fp4: Q_d, K_d are E2M1 copies (mx_quantize_fp4 layout) and the score product runs on FP4.
 hipError_t launch_fwd_mx(const uint8_t* qd, const uint8_t* qd_sc, const uint8_t* kd, const uint8_t* kd_sc,
                          const uint8_t* vt, const uint8_t* vt_sc, const void* v, void* o, float* lse,
                          const Plan& plan, const int* pref_base, const int* padoff, int total_tokens, int t_pad,
-                         int hq, int hkv, float scale, int causal, hipStream_t stream);
+                         int hq, int hkv, float scale, int causal, bool fp4, hipStream_t stream);
 
 hipError_t launch_bwd_dkdv_mx(const MxOperands& m, const void* q, const void* dout, const float* lse,
                               const float* delta, void* dk, void* dv, const Plan& plan, const int* pref_base,

@@ -51,7 +51,10 @@
 extern "C" {
 #endif
 
-typedef enum { CFA_F32 = 0, CFA_BF16 = 1, CFA_MXFP8 = 2 } cfa_dtype;
+/* CFA_MXFP4: the MXFP8 path with the score product QK^T on E2M1 copies of Q and K (mx_quantize_fp4),
+ * a reading of the mixed NVFP4/FP8 path the FLAMIA page names ("FLAMIA Mimarisi ve Temel Tasarım
+ * İlkeleri"). */
+typedef enum { CFA_F32 = 0, CFA_BF16 = 1, CFA_MXFP8 = 2, CFA_MXFP4 = 3 } cfa_dtype;
 
 typedef enum {
   CFA_OK = 0,
@@ -87,7 +90,8 @@ size_t cfa_saved_bytes(int total_tokens, int n_docs, int hq, int hkv, int d, int
  *   scale      : multiplier of Q K^T (usually 1/sqrt(d)); finite and > 0.
  *   dtype      : CFA_F32 (d = 64 or 128), CFA_BF16 (d = 64, 128 or 256; 256 is FlashAttention-2's
  *                extension, "FlashAttention (HU)", FlashAttention-2 (2023)), CFA_MXFP8 (d = 128).
- *   saved      : CFA_MXFP8: cfa_saved_bytes() bytes written here for attn_bwd; otherwise NULL.
+ *                CFA_MXFP4 (d = 128): as CFA_MXFP8 with an E2M1 score product.
+ *   saved      : CFA_MXFP8 / CFA_MXFP4: cfa_saved_bytes() bytes written here for attn_bwd; otherwise NULL.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
