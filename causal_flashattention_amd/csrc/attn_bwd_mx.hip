@@ -145,6 +145,9 @@ struct MxDkdvTile {
   static constexpr int XP = 4 * 4 * 64;              // exchange: i32x4 [pair][2·qb + u][lane]
 };
 
+// FP4 = true (MXFP4/FP8 path): the P wave's score product takes E2M1 Q_d rows (64 bytes, swizzled
+// with (row / 4) % 4) and E2M1 K_d registers; everything else is unchanged.
+template <bool FP4>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
     const uint8_t* __restrict__ qd, const uint8_t* __restrict__ qd_sc, const uint8_t* __restrict__ kd,
     const uint8_t* __restrict__ kd_sc, const uint8_t* __restrict__ dod, const uint8_t* __restrict__ dod_sc,
@@ -174,13 +177,16 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
   const int kw0 = t * 128 + 32 * pair;
   const int mykey = kw0 + r32;
   const float sl2 = scale * LOG2E;
-  int ko[2][2], to[2];
+  int ko[2][2], to[2], kq[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int u = 0; u < 2; ++u) ko[s][u] = 16 * ((4 * s + 2 * u + half) ^ kd_swz(r32));
 #pragma unroll
   for (int u = 0; u < 2; ++u) to[u] = 16 * ((2 * u + half) ^ vt_swz(r32));
+#pragma unroll
+  for (int s = 0; s < 2; ++s) kq[s] = 16 * ((2 * s + half) ^ vt_swz(r32));
+  const bool fp4_role = FP4 && !ds_wave;          // this wave's score operands are E2M1
 
   // B operand rows of key mykey: K_d (P wave) or V_d (dS wave)
   i32x8 kvb[2];
@@ -192,7 +198,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
     const size_t row = (size_t)(s0 + (ok ? mykey : 0)) * hkv + g;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      kvb[s] = ok ? load_a_fp8((const char*)(src + row * D + 64 * s), half) : i32x8{};
+      if (fp4_role)
+        kvb[s] = ok ? fp4_operand(*(const i32x4*)(kd + row * (D / 2) + 32 * s + 16 * half)) : i32x8{};
+      else
+        kvb[s] = ok ? load_a_fp8((const char*)(src + row * D + 64 * s), half) : i32x8{};
       kvs[s] = ok ? ssrc[row * 4 + 2 * s + half] : 127;
     }
   }
@@ -219,11 +228,17 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
     const int rmax = L - 1 - q0;
     const size_t tok0 = (size_t)(s0 + q0) * hq + h;
     const uint32_t tok_b = (uint32_t)hq * D;
-    const uint8_t* dsrc = (ds_wave ? dod : qd) + tok0 * D;
+    if (fp4_role) {                             // E2M1 Q_d codes: 4 blocks of 16 rows of 64 B
+      const uint8_t* dsrc = qd + tok0 * (D / 2);
+      const int r = 16 * pair + (lane >> 2);
+      g2lds16(dsrc + ((uint32_t)min(r, rmax) * (tok_b / 2) + 16 * ((lane & 3) ^ vt_swz(r))), buf + pair * 1024);
+    } else {
+      const uint8_t* dsrc = (ds_wave ? dod : qd) + tok0 * D;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {               // d-blocked codes: 8 blocks of 8 rows
-      const int I = 2 * pair + j, r = 8 * I + (lane >> 3);
-      g2lds16(dsrc + ((uint32_t)min(r, rmax) * tok_b + 16 * ((lane & 7) ^ kd_swz(r))), buf + I * 1024);
+      for (int j = 0; j < 2; ++j) {             // d-blocked codes: 8 blocks of 8 rows
+        const int I = 2 * pair + j, r = 8 * I + (lane >> 3);
+        g2lds16(dsrc + ((uint32_t)min(r, rmax) * tok_b + 16 * ((lane & 7) ^ kd_swz(r))), buf + I * 1024);
+      }
     }
     if (pair == 0)
       g2lds4((ds_wave ? dod_sc : qd_sc) + tok0 * 4 + (uint32_t)min(lane, rmax) * (uint32_t)hq * 4, buf + C::OFF_SC);
@@ -253,13 +268,21 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
   auto dscores = [&](const char* buf, int qb) __attribute__((always_inline)) {
     const int qr = 32 * qb + r32;
     const int sc = *(const int*)(buf + C::OFF_SC + qr * 4);
-    const char* rp = buf + qr * 128;
     f32x16 a = f32x16{};
+    if (fp4_role) {
+      const char* rp = buf + qr * (D / 2);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const i32x4 lo = *(const i32x4*)(rp + ko[s][0]), hi = *(const i32x4*)(rp + ko[s][1]);
-      a = mfma32_mx(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, (sc >> (8 * (2 * s + half))) & 0xFF,
-                    kvb[s], kvs[s], a);
+      for (int s = 0; s < 2; ++s)
+        a = mfma32_mx_fp4(fp4_operand(*(const i32x4*)(rp + kq[s])), (sc >> (8 * (2 * s + half))) & 0xFF, kvb[s],
+                          kvs[s], a);
+    } else {
+      const char* rp = buf + qr * 128;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const i32x4 lo = *(const i32x4*)(rp + ko[s][0]), hi = *(const i32x4*)(rp + ko[s][1]);
+        a = mfma32_mx(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, (sc >> (8 * (2 * s + half))) & 0xFF,
+                      kvb[s], kvs[s], a);
+      }
     }
     return a;
   };
@@ -460,6 +483,9 @@ struct MxDqTile {
   static constexpr int STAGE = OFF_U + BN * 256;
 };
 
+// FP4 = true: the score product takes E2M1 K_d rows (64 bytes, swizzled with (row / 4) % 4) and E2M1
+// Q_d registers.
+template <bool FP4>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
     const uint8_t* __restrict__ qd, const uint8_t* __restrict__ qd_sc, const uint8_t* __restrict__ kd,
     const uint8_t* __restrict__ kd_sc, const uint8_t* __restrict__ dod, const uint8_t* __restrict__ dod_sc,
@@ -493,6 +519,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
     for (int u = 0; u < 2; ++u) ko[s][u] = 16 * ((4 * s + 2 * u + half) ^ kd_swz(r32));
 #pragma unroll
   for (int u = 0; u < 2; ++u) to[u] = 16 * ((2 * u + half) ^ vt_swz(r32));
+  int kq[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) kq[s] = 16 * ((2 * s + half) ^ vt_swz(r32));
 
   i32x8 qa[2], oa[2];
   int qs[2], os[2];
@@ -502,7 +531,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
     const size_t row = (size_t)(s0 + (ok ? qrow : 0)) * hq + h;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      qa[s] = ok ? load_a_fp8((const char*)(qd + row * D + 64 * s), half) : i32x8{};
+      if constexpr (FP4)
+        qa[s] = ok ? fp4_operand(*(const i32x4*)(qd + row * (D / 2) + 32 * s + 16 * half)) : i32x8{};
+      else
+        qa[s] = ok ? load_a_fp8((const char*)(qd + row * D + 64 * s), half) : i32x8{};
       oa[s] = ok ? load_a_fp8((const char*)(dod + row * D + 64 * s), half) : i32x8{};
       qs[s] = ok ? qd_sc[row * 4 + 2 * s + half] : 127;
       os[s] = ok ? dod_sc[row * 4 + 2 * s + half] : 127;
@@ -530,8 +562,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
     for (int j = 0; j < 2; ++j) {               // K_d and V_d codes: 8 blocks of 8 rows each
       const int I = 2 * w + j, r = 8 * I + (lane >> 3);
       const uint32_t off = (uint32_t)min(r, rmax) * krow_b + 16 * ((lane & 7) ^ kd_swz(r));
-      g2lds16(kdb + off, tb + I * 1024);
+      if constexpr (!FP4) g2lds16(kdb + off, tb + I * 1024);
       g2lds16(vdb + off, tb + C::OFF_VD + I * 1024);
+    }
+    if constexpr (FP4) {                        // E2M1 K_d codes: 4 blocks of 16 rows of 64 B
+      const int r = 16 * w + (lane >> 2);
+      g2lds16(kd + tok0 * (D / 2) + ((uint32_t)min(r, rmax) * (krow_b / 2) + 16 * ((lane & 3) ^ vt_swz(r))),
+              tb + w * 1024);
     }
     const uint32_t soff = (uint32_t)min(lane, rmax) * (uint32_t)hkv * 4;
     if (w == 0) g2lds4(kd_sc + tok0 * 4 + soff, tb + C::OFF_KDSC);
@@ -561,12 +598,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
     f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const char* kp = tb + kr * 128;
       const char* vp = tb + C::OFF_VD + kr * 128;
-      const i32x4 klo = *(const i32x4*)(kp + ko[s][0]), khi = *(const i32x4*)(kp + ko[s][1]);
       const i32x4 vlo = *(const i32x4*)(vp + ko[s][0]), vhi = *(const i32x4*)(vp + ko[s][1]);
-      sacc = mfma32_mx(i32x8{klo.x, klo.y, klo.z, klo.w, khi.x, khi.y, khi.z, khi.w},
-                       (ksc >> (8 * (2 * s + half))) & 0xFF, qa[s], qs[s], sacc);
+      if constexpr (FP4) {
+        sacc = mfma32_mx_fp4(fp4_operand(*(const i32x4*)(tb + kr * (D / 2) + kq[s])),
+                             (ksc >> (8 * (2 * s + half))) & 0xFF, qa[s], qs[s], sacc);
+      } else {
+        const char* kp = tb + kr * 128;
+        const i32x4 klo = *(const i32x4*)(kp + ko[s][0]), khi = *(const i32x4*)(kp + ko[s][1]);
+        sacc = mfma32_mx(i32x8{klo.x, klo.y, klo.z, klo.w, khi.x, khi.y, khi.z, khi.w},
+                         (ksc >> (8 * (2 * s + half))) & 0xFF, qa[s], qs[s], sacc);
+      }
       pacc = mfma32_mx(i32x8{vlo.x, vlo.y, vlo.z, vlo.w, vhi.x, vhi.y, vhi.z, vhi.w},
                        (vsc >> (8 * (2 * s + half))) & 0xFF, oa[s], os[s], pacc);
     }
@@ -670,30 +712,31 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
 hipError_t launch_bwd_dkdv_mx(const MxOperands& m, const void* q, const void* dout, const float* lse,
                               const float* delta, void* dk, void* dv, const Plan& plan_any, const int* pref_base,
                               const int* padoff, int T, int t_pad, int hq, int hkv, float scale, int causal,
-                              hipStream_t stream) {
+                              bool fp4, hipStream_t stream) {
   Plan plan = plan_any;
   plan.pref = pref_base + pref_slot(128) * (plan.n_docs + 1);
   const long grid = ((long)(T + 127) / 128 + plan.n_docs) * hkv;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(attn_bwd_dkdv_mx_kernel, dim3((unsigned)grid), dim3(512), 0, stream, m.qd, m.qd_sc, m.kd,
-                     m.kd_sc, m.dod, m.dod_sc, m.vd, m.vd_sc, m.qt, m.qt_sc, m.dot, m.dot_sc, (const __bf16*)q,
-                     (const __bf16*)dout, lse, delta, (__bf16*)dk, (__bf16*)dv, plan, padoff, T, t_pad, hq, hkv, scale,
-                     causal);
+  auto kern = fp4 ? attn_bwd_dkdv_mx_kernel<true> : attn_bwd_dkdv_mx_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), 0, stream, m.qd, m.qd_sc, m.kd, m.kd_sc, m.dod, m.dod_sc,
+                     m.vd, m.vd_sc, m.qt, m.qt_sc, m.dot, m.dot_sc, (const __bf16*)q, (const __bf16*)dout, lse, delta,
+                     (__bf16*)dk, (__bf16*)dv, plan, padoff, T, t_pad, hq, hkv, scale, causal);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq_mx(const MxOperands& m, const void* k, const float* lse, const float* delta, void* dq,
                             const Plan& plan_any, const int* pref_base, const int* padoff, int T, int t_pad, int hq,
-                            int hkv, float scale, int causal, hipStream_t stream) {
+                            int hkv, float scale, int causal, bool fp4, hipStream_t stream) {
   Plan plan = plan_any;
   plan.pref = pref_base + pref_slot(128) * (plan.n_docs + 1);
   const long grid = ((long)(T + 127) / 128 + plan.n_docs) * hq;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(attn_bwd_dq_mx_kernel, dim3((unsigned)grid), dim3(256), 0, stream, m.qd, m.qd_sc, m.kd, m.kd_sc,
-                     m.dod, m.dod_sc, m.vd, m.vd_sc, m.kt, m.kt_sc, (const __bf16*)k, lse, delta, (__bf16*)dq, plan,
-                     padoff, T, t_pad, hq, hkv, scale, causal);
+  auto kern = fp4 ? attn_bwd_dq_mx_kernel<true> : attn_bwd_dq_mx_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, m.qd, m.qd_sc, m.kd, m.kd_sc, m.dod, m.dod_sc,
+                     m.vd, m.vd_sc, m.kt, m.kt_sc, (const __bf16*)k, lse, delta, (__bf16*)dq, plan, padoff, T, t_pad, hq,
+                     hkv, scale, causal);
   return hipGetLastError();
 }
 

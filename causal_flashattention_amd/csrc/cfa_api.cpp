@@ -280,9 +280,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   if (total_tokens > 0 && (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv))
     return fail(CFA_ERR_NULL, "q, k, v, o, lse, dout, dq, dk and dv must not be NULL");
   if (!(std::isfinite(scale) && scale > 0.f)) return fail(CFA_ERR_SHAPE, "scale must be finite and > 0");
-  if (dtype == CFA_MXFP4) return fail(CFA_ERR_UNSUPPORTED, "the MXFP4/FP8 backward is not built");
-  if (dtype == CFA_MXFP8 && !saved) return fail(CFA_ERR_NULL, "MXFP8 needs the forward's `saved` buffer");
-  if (dtype == CFA_MXFP8 && !aligned(saved, 256)) return fail(CFA_ERR_ALIGN, "saved must be 256-byte aligned");
+  if (is_mx(dtype) && !saved) return fail(CFA_ERR_NULL, "the MX paths need the forward's `saved` buffer");
+  if (is_mx(dtype) && !aligned(saved, 256)) return fail(CFA_ERR_ALIGN, "saved must be 256-byte aligned");
   for (const void* p : {q, k, v, o, (const void*)lse, dout, (const void*)dlse, (const void*)dq, (const void*)dk,
                         (const void*)dv, (const void*)cu_seqlens})
     if (!aligned(p, 16)) return fail(CFA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
@@ -300,7 +299,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   mark(0, 0, st);
   if (int r = check_hip(cfa::launch_bwd_pre(o, dout, dlse, delta, total_tokens, hq, d, st), "bwd preprocess")) return r;
   mark(0, 1, st);
-  if (dtype == CFA_MXFP8) {
+  if (is_mx(dtype)) {
     char* ws = (char*)workspace;
     const char* sv = (const char*)saved;
     const SavedLayout sl = saved_layout(s);
@@ -326,13 +325,13 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
     m.dot = U(wl.dot, true); m.dot_sc = U(wl.dot, false);
     mark(1, 0, st);
     if (int r = check_hip(cfa::launch_bwd_dkdv_mx(m, q, dout, lse, delta, dk, dv, plan, plan.pref, padoff, total_tokens,
-                                                  tp, hq, hkv, scale, causal, st),
+                                                  tp, hq, hkv, scale, causal, dtype == CFA_MXFP4, st),
                           "MX dK/dV kernel"))
       return r;
     mark(1, 1, st);
     mark(2, 0, st);
     int r = check_hip(cfa::launch_bwd_dq_mx(m, k, lse, delta, dq, plan, plan.pref, padoff, total_tokens, tp, hq, hkv,
-                                            scale, causal, st),
+                                            scale, causal, dtype == CFA_MXFP4, st),
                       "MX dQ kernel");
     mark(2, 1, st);
     return r;

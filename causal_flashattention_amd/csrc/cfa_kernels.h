@@ -71,11 +71,10 @@ hipError_t launch_fwd_mx(const uint8_t* qd, const uint8_t* qd_sc, const uint8_t*
 
 hipError_t launch_bwd_dkdv_mx(const MxOperands& m, const void* q, const void* dout, const float* lse,
                               const float* delta, void* dk, void* dv, const Plan& plan, const int* pref_base,
-                              const int* padoff, int T, int t_pad, int hq, int hkv, float scale, int causal,
-                              hipStream_t stream);
+                              const int* padoff, int T, int t_pad, int hq, int hkv, float scale, int causal, bool fp4, hipStream_t stream);
 
 hipError_t launch_bwd_dq_mx(const MxOperands& m, const void* k, const float* lse, const float* delta, void* dq,
                             const Plan& plan, const int* pref_base, const int* padoff, int T, int t_pad, int hq,
-                            int hkv, float scale, int causal, hipStream_t stream);
+                            int hkv, float scale, int causal, bool fp4, hipStream_t stream);
 
 }  // namespace cfa

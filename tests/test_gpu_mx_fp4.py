@@ -79,3 +79,54 @@ def test_fp4_forward_workload_4_one_head():
                              qk="e2m1")
     assert rel_l2(o[:, [hh]], ro) <= MX_TOL
     assert np.max(np.abs(lse[[hh]] - rl)) <= LSE_TOL
+
+
+def _fwd_bwd(w, dev):
+    o, lse, saved = _fwd(w, dev)
+    dq, dk, dv = cfa.attn_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], dev["cu"], scale=w.scale,
+                              causal=w.causal, cu_seqlens_host=dev["cu_host"], mx="mxfp4", saved=saved)
+    torch.cuda.synchronize()
+    return o, lse, dq, dk, dv
+
+
+@pytest.mark.parametrize("lengths,hq,hkv,causal", [
+    ([1, 5, 64, 127, 129, 300], 2, 2, True),
+    ([513, 31, 200, 33], 4, 2, True),
+    ([700, 1], 4, 1, True),
+    ([100, 257], 2, 1, False),
+])
+def test_fp4_backward_random_documents(lengths, hq, hkv, causal):
+    w = W.make_random(seed=900 + sum(lengths), lengths=lengths, hq=hq, hkv=hkv, causal=causal)
+    announce("mxfp4 bwd random", lengths, hq, hkv, causal)
+    _, _, dq, dk, dv = _fwd_bwd(w, upload(w))
+    ref = mxa.attn_mx_bwd(w.f64("q"), w.f64("k"), w.f64("v"), w.f64("do"), w.cu_seqlens, w.scale, causal, qk="e2m1")
+    errs = [rel_l2(to_f64(a), b) for a, b in zip((dq, dk, dv), ref)]
+    print("rel-L2 dq dk dv", errs)
+    assert max(errs) <= MX_TOL
+
+
+def test_fp4_backward_causality_isolation_determinism():
+    lengths = [300, 129, 1, 64, 700]
+    w = W.make_random(seed=944, lengths=lengths, hq=4, hkv=2)
+    announce("mxfp4 bwd invariants", lengths)
+    dev = upload(w)
+    r1 = _fwd_bwd(w, dev)
+    r2 = _fwd_bwd(w, dev)
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+    cu = w.cu_seqlens
+    for n in range(len(lengths)):
+        s0, s1 = int(cu[n]), int(cu[n + 1])
+        sub = W.Workload(name="doc", total_tokens=s1 - s0, hq=4, hkv=2, d=128, dtype="bf16", scale=w.scale,
+                         cu_seqlens=np.array([0, s1 - s0], np.int32), q=w.q[s0:s1], k=w.k[s0:s1], v=w.v[s0:s1],
+                         do=w.do[s0:s1])
+        ra = _fwd_bwd(sub, upload(sub))
+        for a, b in zip(ra[2:], r1[2:]):
+            assert torch.equal(a, b[s0:s1])
+    for jl in (0, 31, 32, 127, 128, 699):
+        j = int(cu[4]) + jl
+        dev2 = {kk: vv.clone() for kk, vv in dev.items()}
+        for name in ("q", "k", "v", "do"):
+            dev2[name][j] = dev2[name][j] * 7.5 + 30.0
+        r3 = _fwd_bwd(w, dev2)
+        assert torch.equal(r3[2][:j], r1[2][:j]), jl
