@@ -32,7 +32,18 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp32": 157.3}   # MI355X dense MFMA / vector fp32
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0, "fp32": 157.3}   # MI355X dense MFMA / vector fp32
+# Counted GEMM units per MX kernel and the format each runs in ("qk": the score product, E4M3 on
+# the MXFP8 path and E2M1 on the MXFP4/FP8 path). A mixed kernel's peak is the rate at which its
+# counted units would run if each ran at its format's peak: n / Σ 1/peak.
+MX_UNIT_FORMATS = {"attn_fwd_mx_kernel": ["qk", "fp8"], "attn_bwd_dkdv_mx_kernel": ["qk", "fp8", "fp8", "fp8"],
+                   "attn_bwd_dq_mx_kernel": ["fp8"]}
+# the whole fwd+bwd step under the 3.5× convention: S twice (fwd, bwd recompute), 5 other units
+MX_STEP_FORMATS = ["qk", "qk", "fp8", "fp8", "fp8", "fp8", "fp8"]
+
+
+def mixed_peak(formats, qk_fmt):
+    return len(formats) / sum(1.0 / PEAK_TFLOPS[qk_fmt if f == "qk" else f] for f in formats)
 HBM_PEAK_GBS = 8000.0
 METRIC = "causal fwd+bwd attention TFLOP/s and % of MFMA peak (bf16, MXFP8), 1 GPU"
 
@@ -73,6 +84,8 @@ def parse():
                     help="bf16 workload (3 = one 32K-token document, 32 q / 8 kv heads)")
     ap.add_argument("--mx-workload", type=int, default=4, choices=[0, 4, 5],
                     help="MXFP8 workload reported under 'mxfp8' (0 = skip)")
+    ap.add_argument("--mx4-workload", type=int, default=4, choices=[0, 4, 5],
+                    help="MXFP4/FP8 workload reported under 'mxfp4' (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 3 times (to scale the "
@@ -150,7 +163,8 @@ def measure(w, mx, steps, warmup):
     cu = torch.from_numpy(w.cu_seqlens).to(dev)
     cu_h = torch.from_numpy(w.cu_seqlens)
     T, hq, hkv, d = w.total_tokens, w.hq, w.hkv, w.d
-    dt = cfa.CFA_MXFP8 if mx else cfa.CFA_BF16
+    dt = cfa.CFA_MXFP4 if mx == "mxfp4" else (cfa.CFA_MXFP8 if mx else cfa.CFA_BF16)
+    qk_fmt = "fp4" if mx == "mxfp4" else "fp8"
     o = torch.empty_like(q)
     lse = torch.empty((hq, T), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -212,10 +226,11 @@ def measure(w, mx, steps, warmup):
             for n, (_, _, u) in kernels.items()}
     dom = max(kern, key=lambda n: kern[n]["ms"])
     dom_flops = kern[dom]["units"] * unit_flops
-    peak = PEAK_TFLOPS["fp8" if mx else "bf16"]
+    peak = mixed_peak(MX_STEP_FORMATS, qk_fmt) if mx else PEAK_TFLOPS["bf16"]
+    dom_peak = mixed_peak(MX_UNIT_FORMATS[dom], qk_fmt) if mx else PEAK_TFLOPS["bf16"]
     achieved = dom_flops / (kern[dom]["ms"] * 1e-3) / 1e12
-    roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-            "frac": achieved / peak, "traffic": traffic_for(dom, w.name),
+    roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": dom_peak, "unit": "TFLOP/s",
+            "frac": achieved / dom_peak, "traffic": traffic_for(dom, w.name),
             "algorithmic_flop_per_launch": dom_flops, "mean_launch_ms": kern[dom]["ms"]}
     res = {"value": value, "ms_per_step": elapsed / K * 1e3, "pct_of_peak": 100.0 * value / peak, "peak": peak,
            "config": {"workload": w.name, "total_tokens": T, "n_docs": w.n_docs, "hq": hq, "hkv": hkv, "d": d,
@@ -346,6 +361,13 @@ def main():
         mres["dtype"] = "mxfp8 (E4M3 + E8M0 per 32; bf16 diagonal tiles)"
         mres["unit"] = "TFLOP/s"
         out["mxfp8"] = mres
+    if args.mx4_workload:
+        wm = W.make_workload(args.mx4_workload)
+        mres = measure(wm, "mxfp4", args.steps, args.warmup)
+        mres["dtype"] = "mxfp4/fp8 (QK^T on E2M1 + E8M0 per 32, the rest as mxfp8)"
+        mres["unit"] = "TFLOP/s"
+        mres["peak_note"] = "peaks are n / sum(1/peak) over the counted GEMM units (fp4 10.1, fp8 5.0 PFLOP/s)"
+        out["mxfp4"] = mres
     print(json.dumps(out))
 
 
