@@ -187,3 +187,74 @@ def attn_rows(q, k, v, do, rows, scale, causal=True):
             dk[:, g] += scale * (ds.T @ q[rs, h])
             dv[:, g] += p.T @ do[rs, h]
     return o, lse, dq, dk, dv
+
+
+# ---------------------------------------------------------------- cross-attention
+def cross_mask(Lq, Lk, causal):
+    """Explicit additive mask of one document with separate query and key lengths.
+
+    Causal: query i sees key j iff j <= i + (Lk - Lq), the causal rule with the queries aligned to
+    the end of the keys (the queries are the last Lq positions of a sequence of Lk): for Lq = Lk it
+    is the self-attention mask of "GPT Kernel Programlama" §4, and a single query sees every key
+    (decoding). Queries with i + Lk - Lq < 0 see no key.
+    """
+    m = np.zeros((Lq, Lk), dtype=np.float64)
+    if causal:
+        i = np.arange(Lq)[:, None]
+        j = np.arange(Lk)[None, :]
+        m[j > i + (Lk - Lq)] = -np.inf
+    return m
+
+
+def attn_cross(q, k, v, do, cu_q, cu_k, scale, causal=True, dlse=None):
+    """Attention of packed query documents on packed key/value documents (document n: query rows
+    cu_q[n]..cu_q[n+1]-1, key rows cu_k[n]..cu_k[n+1]-1), forward and exact gradient.
+
+    Per document and head, with M the mask of ``cross_mask``: S = scale·QKᵀ + M, P = softmax(S)
+    by rows (two-pass, §5), O = PV, LSE = log Σ exp(S); a row that sees no key has the empty sum:
+    O = 0, LSE = -inf, P = 0, and so no gradient. Gradient as in ``attn_bwd`` (D_i = dO_i·O_i −
+    dLSE_i, dS = P∘(dP − D)). ``do`` may be None (forward only). Returns o, lse, dq, dk, dv.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    cq = np.asarray(cu_q, np.int64)
+    ck = np.asarray(cu_k, np.int64)
+    Tq, hq, d = q.shape
+    Tk, hkv = k.shape[0], k.shape[1]
+    assert len(cq) == len(ck) and cq[-1] == Tq and ck[-1] == Tk and v.shape == k.shape
+    group = hq // hkv
+    o = np.zeros((Tq, hq, d))
+    lse = np.full((hq, Tq), -np.inf)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dlse = np.zeros((hq, Tq)) if dlse is None else np.asarray(dlse, np.float64)
+    for n in range(len(cq) - 1):
+        q0, q1, k0, k1 = int(cq[n]), int(cq[n + 1]), int(ck[n]), int(ck[n + 1])
+        Lq, Lk = q1 - q0, k1 - k0
+        if Lq == 0:
+            continue
+        M = cross_mask(Lq, Lk, causal)
+        for h in range(hq):
+            g = h // group
+            if Lk == 0:
+                continue
+            z = scale * (q[q0:q1, h] @ k[k0:k1, g].T) + M
+            seen = np.isfinite(z).any(axis=1)
+            m = np.where(seen, z.max(axis=1), 0.0)
+            e = np.where(seen[:, None], np.exp(z - m[:, None]), 0.0)
+            l = e.sum(axis=1)
+            p = np.where(seen[:, None], e / np.where(seen, l, 1.0)[:, None], 0.0)
+            ob = p @ v[k0:k1, g]
+            o[q0:q1, h] = ob
+            lse[h, q0:q1] = np.where(seen, m + np.log(np.where(seen, l, 1.0)), -np.inf)
+            if do is None:
+                continue
+            dob = np.asarray(do, np.float64)[q0:q1, h]
+            D = np.sum(dob * ob, axis=1) - dlse[h, q0:q1]
+            ds = p * (dob @ v[k0:k1, g].T - D[:, None])
+            dq[q0:q1, h] = scale * (ds @ k[k0:k1, g])
+            dk[k0:k1, g] += scale * (ds.T @ q[q0:q1, h])
+            dv[k0:k1, g] += p.T @ dob
+    return o, lse, dq, dk, dv
