@@ -18,7 +18,7 @@ import torch
 from . import _lib
 from ._lib import CFA_BF16, CFA_F32, CFA_MXFP4, CFA_MXFP8, CfaError
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "mx_quantize", "mx_quantize_fp4", "workspace_bytes", "saved_bytes", "CfaError",
+__all__ = ["attn_fwd", "attn_bwd", "attn_fwd_cross", "attn_bwd_cross", "attn_decode", "mx_quantize", "mx_quantize_fp4", "workspace_bytes", "saved_bytes", "CfaError",
            "CFA_F32", "CFA_BF16", "CFA_MXFP8", "CFA_MXFP4", "library_path"]
 
 
@@ -132,6 +132,56 @@ def attn_bwd(q, k, v, o, lse, dout, cu_seqlens, *, scale=None, causal=True, cu_s
                           _ptr(cu_seqlens), _ptr(hcu) if hcu is not None else None, n_docs, T,
                           int(max_seqlen), hq, hkv, d, scale, int(bool(causal)), dt, _ptr(workspace),
                           workspace.numel(), _stream()))
+    return dq, dk, dv
+
+
+def attn_fwd_cross(q, k, v, cu_seqlens_q, cu_seqlens_k, *, scale=None, causal=True, cu_seqlens_q_host=None,
+                   cu_seqlens_k_host=None, out=None, lse=None, workspace=None):
+    """Cross-attention forward (bf16): query documents on their own key/value documents.
+    ``q [Tq, hq, d]``, ``k, v [Tk, hkv, d]``. Returns (o, lse [hq, Tq])."""
+    L = _lib.lib()
+    _check_dev(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    if q.dtype != torch.bfloat16:
+        raise TypeError("cross-attention takes bf16 inputs")
+    Tq, hq, d = q.shape
+    Tk, hkv = k.shape[0], k.shape[1]
+    n_docs = cu_seqlens_q.numel() - 1
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if workspace is None:
+        nb = L.cfa_cross_workspace_bytes(0, Tq, Tk, n_docs, hq, hkv, d)
+        workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device)
+    hq_cu, hk_cu = _host_cu(cu_seqlens_q, cu_seqlens_q_host), _host_cu(cu_seqlens_k, cu_seqlens_k_host)
+    _lib.check(L.attn_fwd_cross(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                                _ptr(cu_seqlens_k), _ptr(hq_cu) if hq_cu is not None else None,
+                                _ptr(hk_cu) if hk_cu is not None else None, n_docs, Tq, Tk, hq, hkv, d, scale,
+                                int(bool(causal)), _ptr(workspace), workspace.numel(), _stream()))
+    return out, lse
+
+
+def attn_bwd_cross(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, *, scale=None, causal=True,
+                   cu_seqlens_q_host=None, cu_seqlens_k_host=None, dlse=None, dq=None, dk=None, dv=None,
+                   workspace=None):
+    """Cross-attention backward (bf16). Returns (dq, dk, dv)."""
+    L = _lib.lib()
+    _check_dev(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, dlse)
+    Tq, hq, d = q.shape
+    Tk, hkv = k.shape[0], k.shape[1]
+    n_docs = cu_seqlens_q.numel() - 1
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        nb = L.cfa_cross_workspace_bytes(1, Tq, Tk, n_docs, hq, hkv, d)
+        workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device)
+    hq_cu, hk_cu = _host_cu(cu_seqlens_q, cu_seqlens_q_host), _host_cu(cu_seqlens_k, cu_seqlens_k_host)
+    _lib.check(L.attn_bwd_cross(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                _ptr(dlse) if dlse is not None else None, _ptr(dq), _ptr(dk), _ptr(dv),
+                                _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(hq_cu) if hq_cu is not None else None,
+                                _ptr(hk_cu) if hk_cu is not None else None, n_docs, Tq, Tk, hq, hkv, d, scale,
+                                int(bool(causal)), _ptr(workspace), workspace.numel(), _stream()))
     return dq, dk, dv
 
 

@@ -30,6 +30,10 @@ SIGNATURES = {
     "mx_workspace_bytes": (_S, [_I]),
     "cfa_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I]),
     "attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
+    "cfa_cross_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I]),
+    "attn_fwd_cross": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
+    "attn_bwd_cross": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
+                            _P, _S, _P]),
     "cfa_set_kernel_events": (_I, [_P, _I]),
     "cfa_device_error": (_I, [_P, _P, ctypes.POINTER(ctypes.c_int)]),
 }

@@ -69,12 +69,12 @@ struct BwdTile {
 };
 
 // ------------------------------------------------------------------ dK / dV
-template <int D>
+template <int D, bool CROSS>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     __bf16* __restrict__ dk, __bf16* __restrict__ dv, Plan plan, int total_tokens, int hq, int hkv,
-    float scale, int causal) {
+    float scale, int causal, const int2* __restrict__ qdoc) {
   using C = BwdTile<D>;
   constexpr int BM = C::BM;                      // queries per step
   constexpr int QB = C::QB;
@@ -86,8 +86,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(16))) char lds_b[STAGE];
 
   const int p = blockIdx.x / hkv, g = blockIdx.x % hkv;
-  int s0, L, t;
-  if (!decode_item(plan, p, 128, false, s0, L, t)) return;
+  int s0, L, t, doc;
+  if (!decode_item(plan, p, 128, false, s0, L, t, &doc)) return;
+  // key rows [s0, s0 + L); query rows [q_s0, q_s0 + Lq); off = L - Lq (0 for self-attention)
+  int q_s0 = s0, Lq = L;
+  if constexpr (CROSS) {
+    const int2 qd = qdoc[doc];
+    q_s0 = qd.x;
+    Lq = qd.y;
+  }
+  const int off = CROSS ? L - Lq : 0;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5;
   const int G = hq / hkv;
   const int kw0 = t * 128 + 32 * w;              // first doc-local key of this wave
@@ -99,21 +107,22 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
   bf16x8 kf[C::DS], vf[C::DS];
   {
     const bool ok = mykey < L;
-    const size_t off = ((size_t)(s0 + (ok ? mykey : 0)) * hkv + g) * D + 8 * half;
+    const size_t ro = ((size_t)(s0 + (ok ? mykey : 0)) * hkv + g) * D + 8 * half;
 #pragma unroll
     for (int s = 0; s < C::DS; ++s) {
-      kf[s] = __builtin_bit_cast(bf16x8, ok ? *(const i32x4*)(k + off + 16 * s) : i32x4{0, 0, 0, 0});
-      vf[s] = __builtin_bit_cast(bf16x8, ok ? *(const i32x4*)(v + off + 16 * s) : i32x4{0, 0, 0, 0});
+      kf[s] = __builtin_bit_cast(bf16x8, ok ? *(const i32x4*)(k + ro + 16 * s) : i32x4{0, 0, 0, 0});
+      vf[s] = __builtin_bit_cast(bf16x8, ok ? *(const i32x4*)(v + ro + 16 * s) : i32x4{0, 0, 0, 0});
     }
   }
   f32x16 dka[C::DB], dva[C::DB];
 #pragma unroll
   for (int b = 0; b < C::DB; ++b) { dka[b] = f32x16{}; dva[b] = f32x16{}; }
 
-  const int q_begin = causal ? t * 128 : 0;      // first query that can see this tile (BM-aligned)
-  const int n_qt = (L - q_begin + BM - 1) / BM;  // query tiles per head
+  // first query that can see this tile (self-attention: BM-aligned) and the query tiles per head
+  const int q_begin = causal ? (CROSS ? max(0, t * 128 - off) : t * 128) : 0;
+  const int n_qt = CROSS ? max(0, (Lq - q_begin + BM - 1) / BM) : (L - q_begin + BM - 1) / BM;
   const int n_steps = n_qt * G;
-  const int wave_first_q = causal ? kw0 : 0;
+  const int wave_first_q = causal ? kw0 - off : 0;
 
   // Staging of one step (Q and dO rows of one query head, their LSE and D) into an LDS buffer.
   // d = 128: direct global -> LDS copies. Rows past the document end are clamped into it and
@@ -125,13 +134,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     char* ob = qb + TILE;
     char* lb = ob + TILE;
     if constexpr (D == 128) {
-      const size_t row0 = ((size_t)(s0 + q0) * hq + h) * D;
+      const size_t row0 = ((size_t)(q_s0 + q0) * hq + h) * D;
       const uint32_t stride = (uint32_t)hq * D * 2;
-      stage_rows_lds<BM>(qb, (const char*)(q + row0), stride, L - 1 - q0, w, lane);
-      stage_rows_lds<BM>(ob, (const char*)(dout + row0), stride, L - 1 - q0, w, lane);
+      stage_rows_lds<BM>(qb, (const char*)(q + row0), stride, Lq - 1 - q0, w, lane);
+      stage_rows_lds<BM>(ob, (const char*)(dout + row0), stride, Lq - 1 - q0, w, lane);
       if (threadIdx.x < BM) {   // LSE and D through registers, written to LDS by stage_finish
-        const size_t li = (size_t)h * total_tokens + s0 + min(q0 + (int)threadIdx.x, L - 1);
+        const size_t li = (size_t)h * total_tokens + q_s0 + min(q0 + (int)threadIdx.x, Lq - 1);
         lreg = lse[li];
+        if (CROSS && lreg == -INFINITY) lreg = INFINITY;   // a row that sees no key: P = 0
         dreg = delta[li];
       }
     } else {
@@ -140,9 +150,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
       for (int i = 0; i < PT; ++i) {
         const int c = min(threadIdx.x + 256 * i, CH - 1);
         const int row = c / (D / 8), col = c % (D / 8);
-        const size_t off = ((size_t)(s0 + min(q0 + row, L - 1)) * hq + h) * D + col * 8;
-        qreg[i] = *(const i32x4*)(q + off);
-        oreg[i] = *(const i32x4*)(dout + off);
+        const size_t eo = ((size_t)(q_s0 + min(q0 + row, Lq - 1)) * hq + h) * D + col * 8;
+        qreg[i] = *(const i32x4*)(q + eo);
+        oreg[i] = *(const i32x4*)(dout + eo);
       }
 #pragma unroll
       for (int i = 0; i < PT; ++i) {
@@ -154,8 +164,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
         }
       }
       if (threadIdx.x < BM) {
-        const size_t li = (size_t)h * total_tokens + s0 + min(q0 + (int)threadIdx.x, L - 1);
-        ((float*)lb)[threadIdx.x] = lse[li];
+        const size_t li = (size_t)h * total_tokens + q_s0 + min(q0 + (int)threadIdx.x, Lq - 1);
+        const float lv = lse[li];
+        ((float*)lb)[threadIdx.x] = (CROSS && lv == -INFINITY) ? INFINITY : lv;
         ((float*)lb)[BM + threadIdx.x] = delta[li];
       }
     }
@@ -178,8 +189,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
       const char* ob = qb + TILE;
       const float* lb = (const float*)(ob + TILE);
       const float* db = lb + BM;
-      const bool need_mask = causal && (q0 < kw0 + 31);
-      const bool ragged = q0 + BM > L;
+      const bool need_mask = causal && (q0 + off < kw0 + 31);
+      const bool ragged = q0 + BM > Lq;
       // ---- S = Q Kᵀ and dP = dO Vᵀ for the two 32-query blocks (operand rows read as a batch)
       f32x16 sacc[QB], pacc[QB];
 #pragma unroll
@@ -216,8 +227,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
           for (int u = 0; u < 2; ++u) {
             const int qi_t = 32 * qb2 + 8 * ((j + u) >> 2) + 4 * half + ((j + u) & 3);  // tile-local query
             float x = exp2_fast(fmaf(sacc[qb2][j + u], sl2, -lb[qi_t] * LOG2E));
-            if (need_mask && mykey > q0 + qi_t) x = 0.f;
-            if (ragged && q0 + qi_t >= L) x = 0.f;      // rows past the document end
+            if (need_mask && mykey > q0 + qi_t + off) x = 0.f;
+            if (ragged && q0 + qi_t >= Lq) x = 0.f;     // rows past the document end
             pv[u] = x;
             dsv[u] = x * (pacc[qb2][j + u] - db[qi_t]);
           }
@@ -301,12 +312,18 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
 // (item, split, kv head) runs only query heads [G·split/n_split, G·(split+1)/n_split) of the group
 // and writes its unscaled fp32 dKᵀ / dVᵀ sums to part_dk / part_dv [n_split][T][hkv][d]; the
 // reduce kernel adds the splits in index order (deterministic) and writes bf16.
-template <int D, int NP>
+//
+// Cross-attention (CROSS = true): the work list is built on the key documents, `qdoc[doc]` gives
+// the query rows, off = Lk - Lq and key j is seen by query i iff j <= i + off; LSE = -inf (a query
+// that sees no key) is read as +inf so that its P is 0. total_tokens counts query rows (LSE, D),
+// total_k key rows (partial sums).
+template <int D, int NP, bool CROSS>
 __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     __bf16* __restrict__ dk, __bf16* __restrict__ dv, Plan plan, int total_tokens, int hq, int hkv,
-    float scale, int causal, int n_split, float* __restrict__ part_dk, float* __restrict__ part_dv) {
+    float scale, int causal, int n_split, float* __restrict__ part_dk, float* __restrict__ part_dv,
+    const int2* __restrict__ qdoc, int total_k) {
   using C = BwdTile<D>;
   constexpr int KT = 32 * NP;                     // keys per workgroup
   constexpr int BM = 32;                          // queries per step
@@ -323,8 +340,16 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
   __shared__ f32x4 xp_c[XP];
 
   const int p = blockIdx.x / (hkv * n_split), g = blockIdx.x % hkv, split = (blockIdx.x / hkv) % n_split;
-  int s0, L, t;
-  if (!decode_item(plan, p, KT, false, s0, L, t)) return;
+  int s0, L, t, doc;
+  if (!decode_item(plan, p, KT, false, s0, L, t, &doc)) return;
+  // key rows [s0, s0 + L); query rows [q_s0, q_s0 + Lq); off = L - Lq (0 for self-attention)
+  int q_s0 = s0, Lq = L;
+  if constexpr (CROSS) {
+    const int2 qd = qdoc[doc];
+    q_s0 = qd.x;
+    Lq = qd.y;
+  }
+  const int off = CROSS ? L - Lq : 0;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5;
   const int pair = w % NP;
   const bool ds_wave = w >= NP;
@@ -341,19 +366,19 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
   {
     const bool ok = mykey < L;
     const __bf16* src = ds_wave ? v : k;
-    const size_t off = ((size_t)(s0 + (ok ? mykey : 0)) * hkv + g) * D + 8 * half;
+    const size_t ro = ((size_t)(s0 + (ok ? mykey : 0)) * hkv + g) * D + 8 * half;
 #pragma unroll
     for (int s = 0; s < C::DS; ++s)
-      kv[s] = __builtin_bit_cast(bf16x8, ok ? *(const i32x4*)(src + off + 16 * s) : i32x4{0, 0, 0, 0});
+      kv[s] = __builtin_bit_cast(bf16x8, ok ? *(const i32x4*)(src + ro + 16 * s) : i32x4{0, 0, 0, 0});
   }
   f32x16 acc[C::DB];                              // dVᵀ (P wave) or dKᵀ (dS wave)
 #pragma unroll
   for (int b = 0; b < C::DB; ++b) acc[b] = f32x16{};
 
-  const int q_begin = causal ? t * KT : 0;
-  const int n_qt = (L - q_begin + BM - 1) / BM;
+  const int q_begin = causal ? (CROSS ? max(0, t * KT - off) : t * KT) : 0;
+  const int n_qt = CROSS ? max(0, (Lq - q_begin + BM - 1) / BM) : (L - q_begin + BM - 1) / BM;
   const int n_steps = n_qt * n_h;
-  const int wave_first_q = causal ? kw0 : 0;
+  const int wave_first_q = causal ? kw0 - off : 0;
 
   // Step st -> buffer: P waves copy the Q tile, dS waves the dO tile (direct global -> LDS);
   // lanes 0..31 of wave 0 fetch LSE and D into registers, written by stage_finish. Rows past
@@ -363,11 +388,12 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
     const int h = h_lo + st / n_qt;
     const int q0 = q_begin + (st % n_qt) * BM;
     const __bf16* src = ds_wave ? dout : q;
-    stage_rows_lds<BM, NP, D>(buf + (ds_wave ? TILE : 0), (const char*)(src + ((size_t)(s0 + q0) * hq + h) * D),
-                              (uint32_t)hq * D * 2, L - 1 - q0, pair, lane);
+    stage_rows_lds<BM, NP, D>(buf + (ds_wave ? TILE : 0), (const char*)(src + ((size_t)(q_s0 + q0) * hq + h) * D),
+                              (uint32_t)hq * D * 2, Lq - 1 - q0, pair, lane);
     if (threadIdx.x < BM) {
-      const size_t li = (size_t)h * total_tokens + s0 + min(q0 + (int)threadIdx.x, L - 1);
+      const size_t li = (size_t)h * total_tokens + q_s0 + min(q0 + (int)threadIdx.x, Lq - 1);
       lreg = lse[li];
+      if (CROSS && lreg == -INFINITY) lreg = INFINITY;
       dreg = delta[li];
     }
   };
@@ -407,11 +433,11 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
     }
     // masked scores -> -inf (wave-uniform branch: only steps that cross the diagonal or the
     // document end), so P = 2^(s·c − LSE·log2 e) is exactly 0 there
-    if ((causal && q0 < kw0 + 31) || q0 + BM > L) {
+    if ((causal && q0 + off < kw0 + 31) || q0 + BM > Lq) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int qi = q0 + 8 * (j >> 2) + 4 * half + (j & 3);
-        if ((causal && mykey > qi) || qi >= L) sacc[j] = -INFINITY;
+        if ((causal && mykey > qi + off) || qi >= Lq) sacc[j] = -INFINITY;
       }
     }
     float x[16];
@@ -522,7 +548,7 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
   if (mykey < L) {
     const size_t row = ((size_t)(s0 + mykey) * hkv + g) * D + 4 * half;
     if (n_split > 1) {
-      float* dst = (ds_wave ? part_dk : part_dv) + (size_t)split * total_tokens * hkv * D + row;
+      float* dst = (ds_wave ? part_dk : part_dv) + (size_t)split * (CROSS ? total_k : total_tokens) * hkv * D + row;
 #pragma unroll
       for (int dbk = 0; dbk < C::DB; ++dbk)
 #pragma unroll
@@ -565,11 +591,13 @@ __global__ __launch_bounds__(256) void dkdv_split_reduce_kernel(const float* __r
 
 
 // ------------------------------------------------------------------ dQ
-template <int D>
+// Cross-attention (CROSS = true): work list on the query documents, `kdoc[doc]` = key rows.
+template <int D, bool CROSS>
 __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_bwd_dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    __bf16* __restrict__ dq, Plan plan, int total_tokens, int hq, int hkv, float scale, int causal) {
+    __bf16* __restrict__ dq, Plan plan, int total_tokens, int hq, int hkv, float scale, int causal,
+    const int2* __restrict__ kdoc) {
   using C = BwdTile<D>;
   constexpr int BN = 64;
   constexpr int TILE = BN * C::RSTR;
@@ -582,15 +610,22 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_bwd_dq_kernel(
   __shared__ __attribute__((aligned(16))) char lds_b[STAGE];
 
   const int p = blockIdx.x / hq, h = blockIdx.x % hq;
-  int s0, L, t;
-  if (!decode_item(plan, p, 128, true, s0, L, t)) return;
+  int s0, L, t, doc;
+  if (!decode_item(plan, p, 128, true, s0, L, t, &doc)) return;
+  int k_s0 = s0, Lk = L;                         // key rows (cross-attention: their own documents)
+  if constexpr (CROSS) {
+    const int2 kd = kdoc[doc];
+    k_s0 = kd.x;
+    Lk = kd.y;
+  }
+  const int off = CROSS ? Lk - L : 0;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5;
   const int g = h / (hq / hkv);
   const int wr0 = t * 128 + 32 * w;
   const int qrow = wr0 + (lane & 31);
-  const int kv_end = causal ? min(L, (t + 1) * 128) : L;
-  const int n_kt = (kv_end + BN - 1) / BN;
-  const int wave_last_key = causal ? min(L, wr0 + 32) - 1 : L - 1;
+  const int kv_end = causal ? (CROSS ? min(Lk, min(L, (t + 1) * 128) + off) : min(L, (t + 1) * 128)) : Lk;
+  const int n_kt = (CROSS && kv_end <= 0) ? 0 : (kv_end + BN - 1) / BN;
+  const int wave_last_key = causal ? (CROSS ? min(Lk, min(L, wr0 + 32) + off) : min(L, wr0 + 32)) - 1 : Lk - 1;
   const float sl2 = scale * LOG2E;
   const SwzOffsets<D> so(lane);
 
@@ -598,14 +633,15 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_bwd_dq_kernel(
   float lse2 = INFINITY, dl = 0.f;
   {
     const bool ok = qrow < L;
-    const size_t off = ((size_t)(s0 + (ok ? qrow : 0)) * hq + h) * D + 8 * half;
+    const size_t ro = ((size_t)(s0 + (ok ? qrow : 0)) * hq + h) * D + 8 * half;
 #pragma unroll
     for (int s = 0; s < C::DS; ++s) {
-      qf[s] = __builtin_bit_cast(bf16x8, ok ? *(const i32x4*)(q + off + 16 * s) : i32x4{0, 0, 0, 0});
-      of[s] = __builtin_bit_cast(bf16x8, ok ? *(const i32x4*)(dout + off + 16 * s) : i32x4{0, 0, 0, 0});
+      qf[s] = __builtin_bit_cast(bf16x8, ok ? *(const i32x4*)(q + ro + 16 * s) : i32x4{0, 0, 0, 0});
+      of[s] = __builtin_bit_cast(bf16x8, ok ? *(const i32x4*)(dout + ro + 16 * s) : i32x4{0, 0, 0, 0});
     }
     if (ok) {
       lse2 = lse[(size_t)h * total_tokens + s0 + qrow] * LOG2E;
+      if (CROSS && lse2 == -INFINITY) lse2 = INFINITY;      // a row that sees no key: P = 0
       dl = delta[(size_t)h * total_tokens + s0 + qrow];
     }
   }
@@ -618,7 +654,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_bwd_dq_kernel(
     const int k0 = kt * BN;
     char* vb = kb + TILE;
     if constexpr (D >= 128) {
-      const size_t row0 = ((size_t)(s0 + k0) * hkv + g) * D;
+      const size_t row0 = ((size_t)(k_s0 + k0) * hkv + g) * D;
       const uint32_t stride = (uint32_t)hkv * D * 2;
       stage_rows_lds<BN, 4, D>(kb, (const char*)(k + row0), stride, kv_end - 1 - k0, w, lane);
       stage_rows_lds<BN, 4, D>(vb, (const char*)(v + row0), stride, kv_end - 1 - k0, w, lane);
@@ -628,9 +664,9 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_bwd_dq_kernel(
       for (int i = 0; i < PT; ++i) {
         const int c = threadIdx.x + 256 * i;
         const int key = c / (D / 8), col = c % (D / 8);
-        const size_t off = ((size_t)(s0 + min(k0 + key, kv_end - 1)) * hkv + g) * D + col * 8;
-        kreg[i] = *(const i32x4*)(k + off);
-        vreg[i] = *(const i32x4*)(v + off);
+        const size_t eo = ((size_t)(k_s0 + min(k0 + key, kv_end - 1)) * hkv + g) * D + col * 8;
+        kreg[i] = *(const i32x4*)(k + eo);
+        vreg[i] = *(const i32x4*)(v + eo);
       }
 #pragma unroll
       for (int i = 0; i < PT; ++i) {
@@ -647,7 +683,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_bwd_dq_kernel(
     if (kt + 1 < n_kt) stage(kt + 1, nxt);
     if (k0 <= wave_last_key) {
       const char* vb = kb + TILE;
-      const bool need_mask = causal ? (k0 + BN - 1 > wr0) : (k0 + BN > L);
+      const bool need_mask = causal ? (k0 + BN - 1 > wr0 + off) : (k0 + BN > Lk);
       bf16x8 sf[4];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
@@ -684,7 +720,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_bwd_dq_kernel(
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int key = k0 + 32 * b + 8 * (j >> 2) + 4 * half + (j & 3);
-            if (causal ? (key > qrow) : (key >= L)) sacc[j] = -INFINITY;
+            if (causal ? (key > qrow + off) : (key >= Lk)) sacc[j] = -INFINITY;
           }
         }
 #pragma unroll
@@ -754,34 +790,34 @@ hipError_t launch_bwd_pre(const void* o, const void* dout, const float* dlse, fl
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool CROSS>
 static hipError_t launch_dkdv_d(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                                 const float* delta, void* dk, void* dv, const Plan& plan_any, const int* pref_base,
                                 int T, int hq, int hkv, float scale, int causal, int n_split, float* part,
-                                hipStream_t stream) {
+                                hipStream_t stream, const int2* qdoc, int Tk) {
   constexpr int NP = D == 256 ? 2 : 4;            // wave pairs (d = 64: waves) per workgroup
   constexpr int KT = D == 256 ? 64 : 128;         // keys per workgroup
   Plan plan = plan_any;
   plan.pref = pref_base + pref_slot(KT) * (plan.n_docs + 1);
-  const long items = (long)(T + KT - 1) / KT + plan.n_docs;
+  const long items = (long)(Tk + KT - 1) / KT + plan.n_docs;   // key tiles (plan on the key documents)
   if constexpr (D >= 128) {
     const long grid = items * hkv * n_split;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    const long n = (long)T * hkv * D;
+    const long n = (long)Tk * hkv * D;
     float* pdk = n_split > 1 ? part : nullptr;
     float* pdv = n_split > 1 ? part + (size_t)n_split * n : nullptr;
-    hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<D, NP>), dim3((unsigned)grid), dim3(128 * NP), 0, stream,
+    hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<D, NP, CROSS>), dim3((unsigned)grid), dim3(128 * NP), 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, lse, delta,
-                       (__bf16*)dk, (__bf16*)dv, plan, T, hq, hkv, scale, causal, n_split, pdk, pdv);
+                       (__bf16*)dk, (__bf16*)dv, plan, T, hq, hkv, scale, causal, n_split, pdk, pdv, qdoc, Tk);
     if (n_split > 1 && n > 0)
       hipLaunchKernelGGL(dkdv_split_reduce_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, stream, pdk,
                          pdv, (__bf16*)dk, (__bf16*)dv, n, n_split, scale);
   } else {
     const long grid = items * hkv;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)q,
-                       (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, lse, delta, (__bf16*)dk, (__bf16*)dv,
-                       plan, T, hq, hkv, scale, causal);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CROSS>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, lse, delta,
+                       (__bf16*)dk, (__bf16*)dv, plan, T, hq, hkv, scale, causal, qdoc);
   }
   return hipGetLastError();
 }
@@ -795,38 +831,41 @@ int dkdv_head_split(int hq, int hkv, int d) {
 template <int D>
 static hipError_t launch_dq_d(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                               const float* delta, void* dq, const Plan& plan, int T, int hq, int hkv, float scale,
-                              int causal, hipStream_t stream) {
+                              int causal, hipStream_t stream, const int2* kdoc) {
   const long items = (long)(T + 127) / 128 + plan.n_docs;
-  auto kern = attn_bwd_dq_kernel<D>;
+  auto kern = kdoc ? attn_bwd_dq_kernel<D, true> : attn_bwd_dq_kernel<D, false>;
   const long grid = items * hq;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)q, (const __bf16*)k,
-                     (const __bf16*)v, (const __bf16*)dout, lse, delta, (__bf16*)dq, plan, T, hq, hkv, scale, causal);
+                     (const __bf16*)v, (const __bf16*)dout, lse, delta, (__bf16*)dq, plan, T, hq, hkv, scale, causal,
+                     kdoc);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                            const float* delta, void* dk, void* dv, const Plan& plan_any, const int* pref_base, int T,
                            int hq, int hkv, int d, float scale, int causal, int n_split, float* part,
-                           hipStream_t stream) {
-  if (d == 128)
-    return launch_dkdv_d<128>(q, k, v, dout, lse, delta, dk, dv, plan_any, pref_base, T, hq, hkv, scale, causal,
-                              n_split, part, stream);
-  if (d == 256)
-    return launch_dkdv_d<256>(q, k, v, dout, lse, delta, dk, dv, plan_any, pref_base, T, hq, hkv, scale, causal,
-                              n_split, part, stream);
-  return launch_dkdv_d<64>(q, k, v, dout, lse, delta, dk, dv, plan_any, pref_base, T, hq, hkv, scale, causal, 1,
-                           nullptr, stream);
+                           hipStream_t stream, const int2* qdoc, int Tk) {
+  if (!qdoc) Tk = T;
+#define CFA_DKDV(DD, NS, PP)                                                                                  \
+  (qdoc ? launch_dkdv_d<DD, true>(q, k, v, dout, lse, delta, dk, dv, plan_any, pref_base, T, hq, hkv, scale, causal, \
+                                  NS, PP, stream, qdoc, Tk)                                                    \
+        : launch_dkdv_d<DD, false>(q, k, v, dout, lse, delta, dk, dv, plan_any, pref_base, T, hq, hkv, scale,   \
+                                   causal, NS, PP, stream, qdoc, Tk))
+  if (d == 128) return CFA_DKDV(128, n_split, part);
+  if (d == 256) return CFA_DKDV(256, n_split, part);
+  return CFA_DKDV(64, 1, nullptr);
+#undef CFA_DKDV
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                          const float* delta, void* dq, const Plan& plan_any, const int* pref_base, int T, int hq,
-                         int hkv, int d, float scale, int causal, hipStream_t stream) {
+                         int hkv, int d, float scale, int causal, hipStream_t stream, const int2* kdoc) {
   Plan plan = plan_any;
   plan.pref = pref_base + pref_slot(128) * (plan.n_docs + 1);
-  if (d == 128) return launch_dq_d<128>(q, k, v, dout, lse, delta, dq, plan, T, hq, hkv, scale, causal, stream);
-  if (d == 256) return launch_dq_d<256>(q, k, v, dout, lse, delta, dq, plan, T, hq, hkv, scale, causal, stream);
-  return launch_dq_d<64>(q, k, v, dout, lse, delta, dq, plan, T, hq, hkv, scale, causal, stream);
+  if (d == 128) return launch_dq_d<128>(q, k, v, dout, lse, delta, dq, plan, T, hq, hkv, scale, causal, stream, kdoc);
+  if (d == 256) return launch_dq_d<256>(q, k, v, dout, lse, delta, dq, plan, T, hq, hkv, scale, causal, stream, kdoc);
+  return launch_dq_d<64>(q, k, v, dout, lse, delta, dq, plan, T, hq, hkv, scale, causal, stream, kdoc);
 }
 
 }  // namespace cfa

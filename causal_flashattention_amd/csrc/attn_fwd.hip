@@ -22,6 +22,10 @@
 //  * K/V tiles of 64 keys are double-buffered in LDS: the next tile's global loads are in
 //    flight while the current tile is multiplied.
 //  * exp2 with scale·log2(e) folded into the exponent; LSE converted back to natural log.
+// Cross-attention (CROSS = true): the work list is built on the query documents and `kdoc[doc]`
+// gives the document's key rows (start, length); with off = Lk - Lq, query i sees key j iff
+// j <= i + off (causal) -- the causal rule with the queries at the end of the keys. A row that
+// sees no key gets O = 0 and LSE = -inf, and the running maximum starts from -inf without NaN.
 #include "cfa_device.h"
 
 namespace cfa {
@@ -43,11 +47,11 @@ struct FwdTile {
 // units), which skips most rescalings of the O accumulator.
 constexpr float RESCALE_LOG2 = 8.f;
 
-template <int D, int HPW, int NW>
+template <int D, int HPW, int NW, bool CROSS>
 __global__ __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, Plan plan, int total_tokens, int hq, int hkv,
-    int n_hb, float scale_log2, int causal) {
+    int n_hb, float scale_log2, int causal, const int2* __restrict__ kdoc) {
   using C = FwdTile<D>;
   constexpr int BMW = 32 * NW / HPW;  // query rows per workgroup
   // two separate LDS buffers (not one array indexed at run time) so that the compiler can
@@ -57,17 +61,26 @@ __global__ __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW) void attn_fwd_bf16_
 
   const int wid = blockIdx.x;
   const int p = wid / n_hb, hb = wid % n_hb;
-  int s0, L, t;
-  if (!decode_item(plan, p, BMW, true, s0, L, t)) return;
+  int s0, L, t, doc;
+  if (!decode_item(plan, p, BMW, true, s0, L, t, &doc)) return;
+  // query rows [s0, s0 + L), key rows [k_s0, k_s0 + Lk); off = 0 for self-attention
+  int k_s0 = s0, Lk = L;
+  if constexpr (CROSS) {
+    const int2 kd = kdoc[doc];
+    k_s0 = kd.x;
+    Lk = kd.y;
+  }
+  const int off = CROSS ? Lk - L : 0;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int G = hq / hkv;
   const int h = hb * HPW + (w % HPW);
   const int g = h / G;
   const int wr0 = t * BMW + 32 * (w / HPW);      // first doc-local row of this wave
   const int wg_rows_end = min(L, (t + 1) * BMW);
-  const int kv_end = causal ? wg_rows_end : L;   // keys the workgroup needs
-  const int n_kt = (kv_end + C::BN - 1) / C::BN;
-  const int wave_last_key = causal ? min(L, wr0 + 32) - 1 : L - 1;
+  // keys the workgroup needs (cross-attention: possibly none)
+  const int kv_end = causal ? (CROSS ? min(Lk, wg_rows_end + off) : wg_rows_end) : Lk;
+  const int n_kt = (CROSS && kv_end <= 0) ? 0 : (kv_end + C::BN - 1) / C::BN;
+  const int wave_last_key = causal ? (CROSS ? min(Lk, min(L, wr0 + 32) + off) : min(L, wr0 + 32)) - 1 : Lk - 1;
   const int qrow = wr0 + (lane & 31);            // this lane's query (doc-local)
   const int half = lane >> 5;
   const SwzOffsets<D> so(lane);
@@ -97,7 +110,7 @@ __global__ __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW) void attn_fwd_bf16_
     const int k0 = kt * C::BN;
     char* vb = kb + C::KBYTES;
     if constexpr (D >= 128) {
-      const size_t row0 = ((size_t)(s0 + k0) * hkv + g) * D;
+      const size_t row0 = ((size_t)(k_s0 + k0) * hkv + g) * D;
       const uint32_t stride = (uint32_t)hkv * D * 2;
       stage_rows_lds<C::BN, NW, D>(kb, (const char*)(k + row0), stride, kv_end - 1 - k0, w, lane);
       stage_rows_lds<C::BN, NW, D>(vb, (const char*)(v + row0), stride, kv_end - 1 - k0, w, lane);
@@ -107,9 +120,9 @@ __global__ __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW) void attn_fwd_bf16_
       for (int i = 0; i < C::PER_THREAD; ++i) {
         const int c = threadIdx.x + 256 * i;
         const int key = c / (D / 8), col = c % (D / 8);
-        const size_t off = ((size_t)(s0 + min(k0 + key, kv_end - 1)) * hkv + g) * D + col * 8;
-        kreg[i] = *(const i32x4*)(k + off);
-        vreg[i] = *(const i32x4*)(v + off);
+        const size_t eo = ((size_t)(k_s0 + min(k0 + key, kv_end - 1)) * hkv + g) * D + col * 8;
+        kreg[i] = *(const i32x4*)(k + eo);
+        vreg[i] = *(const i32x4*)(v + eo);
       }
 #pragma unroll
       for (int i = 0; i < C::PER_THREAD; ++i) {
@@ -121,7 +134,7 @@ __global__ __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW) void attn_fwd_bf16_
     }
   };
 
-  stage(0, lds_a);
+  if (!CROSS || n_kt > 0) stage(0, lds_a);
   wait_vmem();
   __syncthreads();
 
@@ -157,14 +170,14 @@ __global__ __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW) void attn_fwd_bf16_
       // (scale_log2 > 0) and the scale is folded into the exponent, p = 2^(s·c − m). Masking
       // is a separate, wave-uniform branch taken only by tiles that cross the diagonal or the
       // document end.
-      const bool need_mask = causal ? (k0 + C::BN - 1 > wr0) : (k0 + C::BN > L);
+      const bool need_mask = causal ? (k0 + C::BN - 1 > wr0 + off) : (k0 + C::BN > Lk);
       if (need_mask) {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int key = k0 + 32 * b + 8 * (j >> 2) + 4 * half + (j & 3);
-            const bool masked = causal ? (key > qrow) : (key >= L);
+            const bool masked = causal ? (key > qrow + off) : (key >= Lk);
             if (masked) sacc[b][j] = -INFINITY;
           }
       }
@@ -180,7 +193,8 @@ __global__ __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW) void attn_fwd_bf16_
       const bool upd = mt > m_run + RESCALE_LOG2;
       if (__any(upd)) {
         const float m_new = upd ? mt : m_run;
-        const float alpha = exp2_fast(m_run - m_new);
+        // a row that has seen no key yet keeps m = -inf (cross-attention only): factor 1, not NaN
+        const float alpha = (CROSS && m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
 #pragma unroll
@@ -188,12 +202,13 @@ __global__ __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW) void attn_fwd_bf16_
       }
       float ls = 0.f;
       bf16x8 pf[4];
+      const float m_use = (CROSS && m_run == -INFINITY) ? 0.f : m_run;   // all -inf scores -> p = 0
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int j = 0; j < 16; j += 2) {
-          const float p0 = exp2_fast(fmaf(sacc[b][j], scale_log2, -m_run));
-          const float p1 = exp2_fast(fmaf(sacc[b][j + 1], scale_log2, -m_run));
+          const float p0 = exp2_fast(fmaf(sacc[b][j], scale_log2, -m_use));
+          const float p1 = exp2_fast(fmaf(sacc[b][j + 1], scale_log2, -m_use));
           ls += p0 + p1;
           const uint32_t pk = pack_bf16x2(p0, p1);
           i32x4 u = __builtin_bit_cast(i32x4, pf[2 * b + (j >> 3)]);
@@ -229,7 +244,7 @@ __global__ __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW) void attn_fwd_bf16_
   // ---- epilogue: O = Oᵀ / l, LSE = (m + log2 l)·ln 2
   const float l_tot = wave_sum_xor32(l_run);
   if (qrow < L) {
-    const float inv = 1.f / l_tot;
+    const float inv = (CROSS && !(l_tot > 0.f)) ? 0.f : 1.f / l_tot;
     __bf16* dst = o + ((size_t)(s0 + qrow) * hq + h) * D + 4 * half;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -240,7 +255,9 @@ __global__ __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW) void attn_fwd_bf16_
         u.y = (int)pack_bf16x2(oacc[db][4 * jg + 2] * inv, oacc[db][4 * jg + 3] * inv);
         *(i32x2*)(dst + 32 * db + 8 * jg) = u;
       }
-    if (half == 0) lse[(size_t)h * total_tokens + s0 + qrow] = (m_run + __log2f(l_tot)) * LN2;
+    if (half == 0)
+      lse[(size_t)h * total_tokens + s0 + qrow] =
+          (CROSS && !(l_tot > 0.f)) ? -INFINITY : (m_run + __log2f(l_tot)) * LN2;
   }
 }
 
@@ -311,7 +328,7 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(
 // ------------------------------------------------------------------ launchers
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, const Plan& plan_any,
                            const int* pref_base, int total_tokens, int hq, int hkv, int d, float scale, int causal,
-                           hipStream_t stream) {
+                           hipStream_t stream, const int2* kdoc) {
   const int G = hq / hkv;
   const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
   const int nw = (d == 128) ? 8 : 4;              // waves per workgroup (one K/V tile for all of them)
@@ -331,8 +348,12 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   __bf16* O = (__bf16*)o;
 #define CFA_FWD_LAUNCH(DD, HH, NN)                                                                         \
   do {                                                                                                     \
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<DD, HH, NN>), dim3((unsigned)grid), dim3(64 * NN), 0, stream, Q, K, \
-                       V, O, lse, plan, total_tokens, hq, hkv, n_hb, sl2, causal);                         \
+    if (kdoc)                                                                                              \
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<DD, HH, NN, true>), dim3((unsigned)grid), dim3(64 * NN), 0, stream, \
+                         Q, K, V, O, lse, plan, total_tokens, hq, hkv, n_hb, sl2, causal, kdoc);          \
+    else                                                                                                   \
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<DD, HH, NN, false>), dim3((unsigned)grid), dim3(64 * NN), 0,      \
+                         stream, Q, K, V, O, lse, plan, total_tokens, hq, hkv, n_hb, sl2, causal, kdoc);  \
   } while (0)
   if (d == 128) {
     if (hpw == 4) CFA_FWD_LAUNCH(128, 4, 8);

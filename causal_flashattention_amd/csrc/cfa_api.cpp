@@ -388,6 +388,129 @@ int mx_quantize(const void* x, int total_tokens, int h, int d, const int32_t* cu
                    "mx_quantize_t");
 }
 
+// ---------------------------------------------------------------- cross-attention (bf16)
+namespace {
+struct CrossLayout {
+  size_t plan_k, delta, dkdv_part, total;
+  int n_split;
+};
+// [plan on the query documents][plan on the key documents][bwd: D][bwd: head-split partial sums]
+CrossLayout cross_layout(int pass, int Tq, int Tk, int n_docs, int hq, int hkv, int d) {
+  CrossLayout l{};
+  const cfa::PlanLayout pl(n_docs);
+  l.plan_k = pl.end;
+  size_t off = l.plan_k + pl.end;
+  l.n_split = 1;
+  if (pass == 1) {
+    l.delta = off;
+    off = cfa::align256(off + sizeof(float) * (size_t)hq * Tq);
+    l.n_split = cfa::dkdv_head_split(hq, hkv, d);
+    if (l.n_split > 1) {
+      l.dkdv_part = off;
+      off = cfa::align256(off + sizeof(float) * 2 * (size_t)l.n_split * Tk * hkv * d);
+    }
+  }
+  l.total = off;
+  return l;
+}
+int check_cross(int pass, int Tq, int Tk, int n_docs, int hq, int hkv, int d) {
+  if (Tk < 0) return fail(CFA_ERR_SHAPE, "total_k = %d < 0", Tk);
+  const Sizes s{Tq, n_docs, hq, hkv, d, CFA_BF16};
+  if (int st = check_sizes(s, pass == 1)) return st;
+  if ((long)Tk * hkv * d > 0x7fffffffL * 8L) return fail(CFA_ERR_SHAPE, "tensor too large");
+  return CFA_OK;
+}
+cfa::Plan plan_at(void* ws, size_t off, int n_docs) { return make_plan((char*)ws + off, n_docs); }
+}  // namespace
+
+size_t cfa_cross_workspace_bytes(int pass, int total_q, int total_k, int n_docs, int hq, int hkv, int d) {
+  if ((pass != 0 && pass != 1) || check_cross(pass, total_q, total_k, n_docs, hq, hkv, d) != CFA_OK) return 0;
+  return cross_layout(pass, total_q, total_k, n_docs, hq, hkv, d).total;
+}
+
+int attn_fwd_cross(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens_q,
+                   const int32_t* cu_seqlens_k, const int32_t* cu_seqlens_q_host, const int32_t* cu_seqlens_k_host,
+                   int n_docs, int total_q, int total_k, int hq, int hkv, int d, float scale, int causal,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (int st = check_cross(0, total_q, total_k, n_docs, hq, hkv, d)) return st;
+  if (!cu_seqlens_q || !cu_seqlens_k || !workspace)
+    return fail(CFA_ERR_NULL, "cu_seqlens_q, cu_seqlens_k and workspace must not be NULL");
+  if (total_q > 0 && (!q || !o || !lse)) return fail(CFA_ERR_NULL, "q, o and lse must not be NULL");
+  if (total_k > 0 && (!k || !v)) return fail(CFA_ERR_NULL, "k and v must not be NULL");
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(CFA_ERR_SHAPE, "scale must be finite and > 0");
+  for (const void* p : {q, k, v, (const void*)o, (const void*)lse, (const void*)cu_seqlens_q, (const void*)cu_seqlens_k})
+    if (!aligned(p, 16)) return fail(CFA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (!aligned(workspace, 256)) return fail(CFA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const CrossLayout cl = cross_layout(0, total_q, total_k, n_docs, hq, hkv, d);
+  if (workspace_bytes < cl.total)
+    return fail(CFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, cl.total);
+  if (int st = check_cu_host(cu_seqlens_q_host, n_docs, total_q, 0)) return st;
+  if (int st = check_cu_host(cu_seqlens_k_host, n_docs, total_k, 0)) return st;
+  hipStream_t st = (hipStream_t)stream;
+  if (int r = check_hip(cfa::launch_plan(cu_seqlens_q, n_docs, total_q, workspace, st), "plan kernel (queries)")) return r;
+  if (int r = check_hip(cfa::launch_plan(cu_seqlens_k, n_docs, total_k, (char*)workspace + cl.plan_k, st),
+                        "plan kernel (keys)"))
+    return r;
+  if (total_q == 0) return CFA_OK;
+  const cfa::Plan pq = make_plan(workspace, n_docs);
+  const cfa::Plan pk = plan_at(workspace, cl.plan_k, n_docs);
+  mark(0, 0, st);
+  hipError_t e = cfa::launch_fwd_bf16(q, k, v, o, lse, pq, pq.pref, total_q, hq, hkv, d, scale, causal, st, pk.docinfo);
+  mark(0, 1, st);
+  return check_hip(e, "cross-attention forward kernel");
+}
+
+int attn_bwd_cross(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   const float* dlse, void* dq, void* dk, void* dv, const int32_t* cu_seqlens_q,
+                   const int32_t* cu_seqlens_k, const int32_t* cu_seqlens_q_host, const int32_t* cu_seqlens_k_host,
+                   int n_docs, int total_q, int total_k, int hq, int hkv, int d, float scale, int causal,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (int st = check_cross(1, total_q, total_k, n_docs, hq, hkv, d)) return st;
+  if (!cu_seqlens_q || !cu_seqlens_k || !workspace)
+    return fail(CFA_ERR_NULL, "cu_seqlens_q, cu_seqlens_k and workspace must not be NULL");
+  if (total_q > 0 && (!q || !o || !lse || !dout || !dq)) return fail(CFA_ERR_NULL, "q, o, lse, dout, dq must not be NULL");
+  if (total_k > 0 && (!k || !v || !dk || !dv)) return fail(CFA_ERR_NULL, "k, v, dk, dv must not be NULL");
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(CFA_ERR_SHAPE, "scale must be finite and > 0");
+  for (const void* p : {q, k, v, o, (const void*)lse, dout, (const void*)dlse, (const void*)dq, (const void*)dk,
+                        (const void*)dv, (const void*)cu_seqlens_q, (const void*)cu_seqlens_k})
+    if (!aligned(p, 16)) return fail(CFA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (!aligned(workspace, 256)) return fail(CFA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const CrossLayout cl = cross_layout(1, total_q, total_k, n_docs, hq, hkv, d);
+  if (workspace_bytes < cl.total)
+    return fail(CFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, cl.total);
+  if (int st = check_cu_host(cu_seqlens_q_host, n_docs, total_q, 0)) return st;
+  if (int st = check_cu_host(cu_seqlens_k_host, n_docs, total_k, 0)) return st;
+  hipStream_t st = (hipStream_t)stream;
+  if (int r = check_hip(cfa::launch_plan(cu_seqlens_q, n_docs, total_q, workspace, st), "plan kernel (queries)")) return r;
+  if (int r = check_hip(cfa::launch_plan(cu_seqlens_k, n_docs, total_k, (char*)workspace + cl.plan_k, st),
+                        "plan kernel (keys)"))
+    return r;
+  const cfa::Plan pq = make_plan(workspace, n_docs);
+  const cfa::Plan pk = plan_at(workspace, cl.plan_k, n_docs);
+  float* delta = (float*)((char*)workspace + cl.delta);
+  mark(0, 0, st);
+  if (int r = check_hip(cfa::launch_bwd_pre(o, dout, dlse, delta, total_q, hq, d, st), "bwd preprocess")) return r;
+  mark(0, 1, st);
+  mark(1, 0, st);
+  if (total_k > 0) {   // dK/dV: key tiles; keys of an empty query document get zero gradients
+    if (int r = check_hip(cfa::launch_bwd_dkdv(q, k, v, dout, lse, delta, dk, dv, pk, pk.pref, total_q, hq, hkv, d,
+                                               scale, causal, cl.n_split, (float*)((char*)workspace + cl.dkdv_part),
+                                               st, pq.docinfo, total_k),
+                          "cross-attention dK/dV kernel"))
+      return r;
+  }
+  mark(1, 1, st);
+  mark(2, 0, st);
+  hipError_t e = hipSuccess;
+  if (total_q > 0)
+    e = cfa::launch_bwd_dq(q, k, v, dout, lse, delta, dq, pq, pq.pref, total_q, hq, hkv, d, scale, causal, st,
+                           pk.docinfo);
+  mark(2, 1, st);
+  return check_hip(e, "cross-attention dQ kernel");
+}
+
 int mx_quantize_fp4(const void* x, int total_tokens, int h, int d, uint8_t* codes, uint8_t* scales, void* stream) {
   g_err[0] = 0;
   if (total_tokens < 0 || h < 1) return fail(CFA_ERR_SHAPE, "total_tokens = %d, h = %d", total_tokens, h);

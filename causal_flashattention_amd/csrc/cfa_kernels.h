@@ -14,9 +14,11 @@ struct MxOperands {
 
 hipError_t launch_plan(const int* cu, int n_docs, int total_tokens, void* ws, hipStream_t stream);
 
+// kdoc != nullptr: cross-attention; the plan is built on the query documents and kdoc[n] =
+// (first key row, key count) of document n.
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, const Plan& plan,
                            const int* pref_base, int total_tokens, int hq, int hkv, int d, float scale, int causal,
-                           hipStream_t stream);
+                           hipStream_t stream, const int2* kdoc = nullptr);
 
 hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, const Plan& plan,
                           const int* pref_base, int total_tokens, int hq, int hkv, int d, float scale, int causal,
@@ -25,13 +27,16 @@ hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, 
 hipError_t launch_bwd_pre(const void* o, const void* dout, const float* dlse, float* delta, int total_tokens, int hq,
                           int d, hipStream_t stream);
 
+// Cross-attention (qdoc / kdoc != nullptr): the dK/dV plan is built on the key documents and
+// qdoc[n] = (first query row, query count); the dQ plan on the query documents and kdoc[n] =
+// (first key row, key count); T counts query rows, Tk key rows.
 // n_split > 1: the query heads of each group are split over n_split workgroups whose fp32
 // partial sums go to `part` (2·n_split·T·hkv·d floats, see dkdv_head_split) and are reduced in
 // split order.
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                            const float* delta, void* dk, void* dv, const Plan& plan, const int* pref_base, int T,
                            int hq, int hkv, int d, float scale, int causal, int n_split, float* part,
-                           hipStream_t stream);
+                           hipStream_t stream, const int2* qdoc = nullptr, int Tk = 0);
 
 // Head split of the bf16 dK/dV pass (1 = none): with fewer than 8 kv heads the (key tile,
 // kv head) grid is split further over the query heads of each group, up to 8 workgroups per key
@@ -41,7 +46,8 @@ int dkdv_head_split(int hq, int hkv, int d);
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                          const float* delta, void* dq, const Plan& plan, const int* pref_base, int T, int hq,
-                         int hkv, int d, float scale, int causal, hipStream_t stream);
+                         int hkv, int d, float scale, int causal, hipStream_t stream,
+                         const int2* kdoc = nullptr);
 
 // Decoding over a packed KV cache (bf16 or MX codes + E8M0 scales): per-chunk partials, then
 // their merge in chunk order. part_o: float [slots][hq][d], part_ml: float2 [slots][hq], with

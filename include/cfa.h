@@ -137,6 +137,33 @@ int mx_quantize(const void* x, int total_tokens, int h, int d,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Cross-attention (bf16): packed query documents attend to their own packed key/value documents.
+ * Document n owns query rows cu_seqlens_q[n] .. cu_seqlens_q[n+1]-1 of q, o, dout, dq (total_q
+ * rows) and key rows cu_seqlens_k[n] .. cu_seqlens_k[n+1]-1 of k, v, dk, dv (total_k rows); both
+ * arrays follow the cu_seqlens rules (device memory, optional host copies validated first).
+ * causal != 0: with Lq, Lk the document's lengths, query i sees key j iff j <= i + (Lk - Lq) --
+ * the queries are the last Lq positions of the Lk keys, which is the rule of "GPT Kernel
+ * Programlama" §4 when Lq = Lk and decoding when Lq = 1. A query that sees no key (i < Lq - Lk,
+ * or Lk = 0) gets o = 0, lse = -inf and no gradient. lse: [hq, total_q]; dlse as in attn_bwd.
+ * d = 64, 128 or 256. The pages do not name cross-attention; the definitions are those of
+ * attn_fwd / attn_bwd with the mask above.
+ * Scratch: cfa_cross_workspace_bytes(pass 0 = forward, 1 = backward, ...). cfa_device_error on
+ * this workspace reports cu_seqlens_q only (a malformed device cu_seqlens_k is clamped the same
+ * way, its documents becoming empty).
+ */
+size_t cfa_cross_workspace_bytes(int pass, int total_q, int total_k, int n_docs, int hq, int hkv, int d);
+int attn_fwd_cross(const void* q, const void* k, const void* v, void* o, float* lse,
+                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                   const int32_t* cu_seqlens_q_host, const int32_t* cu_seqlens_k_host,
+                   int n_docs, int total_q, int total_k, int hq, int hkv, int d, float scale, int causal,
+                   void* workspace, size_t workspace_bytes, void* stream);
+int attn_bwd_cross(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, const float* dlse, void* dq, void* dk, void* dv,
+                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                   const int32_t* cu_seqlens_q_host, const int32_t* cu_seqlens_k_host,
+                   int n_docs, int total_q, int total_k, int hq, int hkv, int d, float scale, int causal,
+                   void* workspace, size_t workspace_bytes, void* stream);
+/*
  * MXFP4 quantiser along d: bf16 x [total_tokens, h, d] -> E2M1 codes packed two per byte
  * (element 2i in the low nibble) [total_tokens, h, d/2] + E8M0 scales [total_tokens, h, d/32].
  * Per 32-channel block: e = floor(log2 amax) - 2 clamped to [-127, 127] (-127 for a zero block);
