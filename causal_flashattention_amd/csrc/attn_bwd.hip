@@ -317,7 +317,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
 // the query rows, off = Lk - Lq and key j is seen by query i iff j <= i + off; LSE = -inf (a query
 // that sees no key) is read as +inf so that its P is 0. total_tokens counts query rows (LSE, D),
 // total_k key rows (partial sums).
-template <int D, int NP, bool CROSS>
+template <int D, int NP, bool CROSS, bool SPLIT>
 __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
@@ -339,7 +339,8 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
   __shared__ f32x4 xp_b[XP];
   __shared__ f32x4 xp_c[XP];
 
-  const int p = blockIdx.x / (hkv * n_split), g = blockIdx.x % hkv, split = (blockIdx.x / hkv) % n_split;
+  const int ns = SPLIT ? n_split : 1;             // the unsplit instantiation keeps plain indexing
+  const int p = blockIdx.x / (hkv * ns), g = blockIdx.x % hkv, split = SPLIT ? (blockIdx.x / hkv) % ns : 0;
   int s0, L, t, doc;
   if (!decode_item(plan, p, KT, false, s0, L, t, &doc)) return;
   // key rows [s0, s0 + L); query rows [q_s0, q_s0 + Lq); off = L - Lq (0 for self-attention)
@@ -354,8 +355,8 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
   const int pair = w % NP;
   const bool ds_wave = w >= NP;
   const int G = hq / hkv;
-  const int h_lo = g * G + (G * split) / n_split;              // this split's query heads
-  const int n_h = g * G + (G * (split + 1)) / n_split - h_lo;
+  const int h_lo = SPLIT ? g * G + (G * split) / ns : g * G;  // this split's query heads
+  const int n_h = SPLIT ? g * G + (G * (split + 1)) / ns - h_lo : G;
   const int kw0 = t * KT + 32 * pair;             // first doc-local key of this pair
   const int mykey = kw0 + (lane & 31);
   const float sl2 = scale * LOG2E;
@@ -547,7 +548,7 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
   // dS wave: dK = scale·dKᵀ; P wave: dV (lane: key mykey, d = 32 db + 8 jg + 4·half + 0..3)
   if (mykey < L) {
     const size_t row = ((size_t)(s0 + mykey) * hkv + g) * D + 4 * half;
-    if (n_split > 1) {
+    if (SPLIT) {
       float* dst = (ds_wave ? part_dk : part_dv) + (size_t)split * (CROSS ? total_k : total_tokens) * hkv * D + row;
 #pragma unroll
       for (int dbk = 0; dbk < C::DB; ++dbk)
@@ -806,9 +807,14 @@ static hipError_t launch_dkdv_d(const void* q, const void* k, const void* v, con
     const long n = (long)Tk * hkv * D;
     float* pdk = n_split > 1 ? part : nullptr;
     float* pdv = n_split > 1 ? part + (size_t)n_split * n : nullptr;
-    hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<D, NP, CROSS>), dim3((unsigned)grid), dim3(128 * NP), 0, stream,
-                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, lse, delta,
-                       (__bf16*)dk, (__bf16*)dv, plan, T, hq, hkv, scale, causal, n_split, pdk, pdv, qdoc, Tk);
+    if (n_split > 1)
+      hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<D, NP, CROSS, true>), dim3((unsigned)grid), dim3(128 * NP), 0,
+                         stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, lse, delta,
+                         (__bf16*)dk, (__bf16*)dv, plan, T, hq, hkv, scale, causal, n_split, pdk, pdv, qdoc, Tk);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<D, NP, CROSS, false>), dim3((unsigned)grid), dim3(128 * NP), 0,
+                         stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, lse, delta,
+                         (__bf16*)dk, (__bf16*)dv, plan, T, hq, hkv, scale, causal, 1, pdk, pdv, qdoc, Tk);
     if (n_split > 1 && n > 0)
       hipLaunchKernelGGL(dkdv_split_reduce_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, stream, pdk,
                          pdv, (__bf16*)dk, (__bf16*)dv, n, n_split, scale);
