@@ -230,7 +230,8 @@ def measure(w, mx, steps, warmup):
     dom_peak = mixed_peak(MX_UNIT_FORMATS[dom], qk_fmt) if mx else PEAK_TFLOPS["bf16"]
     achieved = dom_flops / (kern[dom]["ms"] * 1e-3) / 1e12
     roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": dom_peak, "unit": "TFLOP/s",
-            "frac": achieved / dom_peak, "traffic": traffic_for(dom, w.name),
+            "frac": achieved / dom_peak,
+            "traffic": traffic_for(dom, w.name.replace("mxfp8", "mxfp4") if mx == "mxfp4" else w.name),
             "algorithmic_flop_per_launch": dom_flops, "mean_launch_ms": kern[dom]["ms"]}
     res = {"value": value, "ms_per_step": elapsed / K * 1e3, "pct_of_peak": 100.0 * value / peak, "peak": peak,
            "config": {"workload": w.name, "total_tokens": T, "n_docs": w.n_docs, "hq": hq, "hkv": hkv, "d": d,
