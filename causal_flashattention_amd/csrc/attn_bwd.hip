@@ -297,10 +297,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
 
 // ------------------------------------------------------------------ dK / dV, d = 128 / 256, wave pairs
 // 2·NP waves own 32·NP keys of one kv head, as NP pairs of 32 keys (d = 128: 4 pairs, two waves
-// per SIMD; d = 256: 2 pairs, one wave per SIMD with twice the registers). In a pair, the "P wave" (w < 4)
-// holds K and computes S = Q Kᵀ, P = exp(S − LSE), dVᵀ += dOᵀ P; the "dS wave" (w + 4) holds V
-// and computes dP = dO Vᵀ, dS = P (dP − D), dKᵀ += Qᵀ dS with the fp32 P that its partner left
-// in LDS one step earlier. Running the dS wave one step behind removes every wait between the
+// per SIMD; d = 256: 2 pairs, one wave per SIMD with twice the registers). In a pair, the "P wave" (w < NP)
+// holds K and computes S = Q Kᵀ, P = exp(S − LSE), dVᵀ += dOᵀ P; the "dS wave" (w + NP) holds V
+// and computes dP = dO Vᵀ, dS = P (dP − D), dKᵀ += Qᵀ dS with the bf16 P that its partner left
+// in LDS one step earlier. A step is 64 queries (d = 128; 32 for d = 256) of one query head,
+// taken as two 32-query blocks: the longer step leaves the copies of the next one more time. Running the dS wave one step behind removes every wait between the
 // two inside a step; the two waves of a pair sit on the same SIMD, so one wave's exponentials
 // and packing overlap the other's matrix products. Each wave holds one accumulator (dVᵀ or
 // dKᵀ) and one operand set (K or V), which is what brings two waves per SIMD within the
@@ -326,18 +327,19 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
     const int2* __restrict__ qdoc, int total_k) {
   using C = BwdTile<D>;
   constexpr int KT = 32 * NP;                     // keys per workgroup
-  constexpr int BM = 32;                          // queries per step
-  constexpr int TILE = BM * C::RSTR;              // 8 KB (d = 256: 16 KB)
+  constexpr int QBS = D == 128 ? 2 : 1;           // 32-query blocks per step (a longer step hides the copies)
+  constexpr int BM = 32 * QBS;                    // queries per step
+  constexpr int TILE = BM * C::RSTR;              // 16 KB
   constexpr int STAGE = 2 * TILE + 2 * BM * 4;    // Q, dO, LSE·log2 e, D
-  constexpr int XP = NP * 4 * 64;                 // f32x4 per exchange buffer: [pair][j/4][lane]
+  constexpr int XP = NP * QBS * 2 * 64;           // i32x4 per exchange buffer: bf16 P [pair][qb][u][lane]
   constexpr int SB = D == 256 ? 4 : C::DS;        // k-steps per operand batch
   constexpr int DBC = D == 256 ? 4 : C::DB;       // d blocks per transposed-read batch
   __shared__ __attribute__((aligned(16))) char st_a[STAGE];
   __shared__ __attribute__((aligned(16))) char st_b[STAGE];
   __shared__ __attribute__((aligned(16))) char st_c[STAGE];
-  __shared__ f32x4 xp_a[XP];
-  __shared__ f32x4 xp_b[XP];
-  __shared__ f32x4 xp_c[XP];
+  __shared__ i32x4 xp_a[XP];
+  __shared__ i32x4 xp_b[XP];
+  __shared__ i32x4 xp_c[XP];
 
   const int ns = SPLIT ? n_split : 1;             // the unsplit instantiation keeps plain indexing
   const int p = blockIdx.x / (hkv * ns), g = blockIdx.x % hkv, split = SPLIT ? (blockIdx.x / hkv) % ns : 0;
@@ -410,117 +412,127 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
     return q0 + BM - 1 >= wave_first_q && kw0 < L;
   };
 
-  // P wave, step st: S, P (to the exchange buffer and, as bf16, to the dV product), dVᵀ += dOᵀ P
-  auto step_p = [&](int st, const char* buf, f32x4* xw) __attribute__((always_inline)) {
+  // P wave, step st: per 32-query block, S, P (bf16, to the exchange buffer and the dV product),
+  // dVᵀ += dOᵀ P
+  auto step_p = [&](int st, const char* buf, i32x4* xw) __attribute__((always_inline)) {
     const int q0 = q_begin + (st % n_qt) * BM;
     const char* ob = buf + TILE;
     const f32x4* l2 = (const f32x4*)(buf + 2 * TILE);
-    f32x16 sacc = f32x16{};
+    const bool masked = (causal && q0 + off < kw0 + 31) || q0 + BM > Lq;   // wave-uniform
 #pragma unroll
-    for (int sc = 0; sc < C::DS; sc += SB) {
-      i32x4 fq[SB];
+    for (int qb = 0; qb < QBS; ++qb) {
+      f32x16 sacc = f32x16{};
 #pragma unroll
-      for (int s = 0; s < SB; ++s) fq[s] = *(const i32x4*)(buf + so.row[sc + s]);
+      for (int sc = 0; sc < C::DS; sc += SB) {
+        i32x4 fq[SB];
 #pragma unroll
-      for (int s = 0; s < SB; ++s) sacc = mfma32(as_bf16x8(fq[s]), kv[sc + s], sacc);
-      if constexpr (D == 128) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+        for (int s = 0; s < SB; ++s) fq[s] = *(const i32x4*)(buf + 32 * qb * C::RSTR + so.row[sc + s]);
+#pragma unroll
+        for (int s = 0; s < SB; ++s) sacc = mfma32(as_bf16x8(fq[s]), kv[sc + s], sacc);
+        if constexpr (D == 128) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+        }
       }
-    }
-    // masked scores -> -inf (wave-uniform branch: only steps that cross the diagonal or the
-    // document end), so P = 2^(s·c − LSE·log2 e) is exactly 0 there
-    if ((causal && q0 + off < kw0 + 31) || q0 + BM > Lq) {
+      // masked scores -> -inf, so P = 2^(s·c − LSE·log2 e) is exactly 0 there
+      if (masked) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int qi = q0 + 8 * (j >> 2) + 4 * half + (j & 3);
-        if ((causal && mykey > qi + off) || qi >= Lq) sacc[j] = -INFINITY;
+        for (int j = 0; j < 16; ++j) {
+          const int qi = q0 + 32 * qb + 8 * (j >> 2) + 4 * half + (j & 3);
+          if ((causal && mykey > qi + off) || qi >= Lq) sacc[j] = -INFINITY;
+        }
       }
-    }
-    float x[16];
-    bf16x8 pf[2];
+      i32x4 pw[2];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {              // rows 8·jj + 4·half + u
-      const f32x4 lr = l2[2 * jj + half];
+      for (int jj = 0; jj < 4; ++jj) {            // rows 32·qb + 8·jj + 4·half + u
+        const f32x4 lr = l2[8 * qb + 2 * jj + half];
+        float x[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) x[4 * jj + u] = exp2_fast(fmaf(sacc[4 * jj + u], sl2, -lr[u]));
-      xw[(pair * 4 + jj) * 64 + lane] = f32x4{x[4 * jj], x[4 * jj + 1], x[4 * jj + 2], x[4 * jj + 3]};
-      i32x4 up = __builtin_bit_cast(i32x4, pf[jj >> 1]);
-      up[2 * (jj & 1)] = (int)pack_bf16x2(x[4 * jj], x[4 * jj + 1]);
-      up[2 * (jj & 1) + 1] = (int)pack_bf16x2(x[4 * jj + 2], x[4 * jj + 3]);
-      pf[jj >> 1] = __builtin_bit_cast(bf16x8, up);
-    }
+        for (int u = 0; u < 4; ++u) x[u] = exp2_fast(fmaf(sacc[4 * jj + u], sl2, -lr[u]));
+        pw[jj >> 1][2 * (jj & 1)] = (int)pack_bf16x2(x[0], x[1]);
+        pw[jj >> 1][2 * (jj & 1) + 1] = (int)pack_bf16x2(x[2], x[3]);
+      }
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int rb = 16 * kk * C::RSTR;
+      for (int u = 0; u < 2; ++u) xw[((pair * QBS + qb) * 2 + u) * 64 + lane] = pw[u];
 #pragma unroll
-      for (int dc = 0; dc < C::DB; dc += DBC) {
-        bf16x8 ao[DBC];
+      for (int kk = 0; kk < 2; ++kk) {
+        const int rb = (32 * qb + 16 * kk) * C::RSTR;
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, pw[kk]);
 #pragma unroll
-        for (int i = 0; i < DBC; ++i)
-          ao[i] = concat_tr(lds_read_tr16(ob + rb + so.tr0[dc + i]), lds_read_tr16(ob + rb + so.tr1[dc + i]));
+        for (int dc = 0; dc < C::DB; dc += DBC) {
+          bf16x8 ao[DBC];
 #pragma unroll
-        for (int i = 0; i < DBC; ++i) acc[dc + i] = mfma32(ao[i], pf[kk], acc[dc + i]);
+          for (int i = 0; i < DBC; ++i)
+            ao[i] = concat_tr(lds_read_tr16(ob + rb + so.tr0[dc + i]), lds_read_tr16(ob + rb + so.tr1[dc + i]));
+#pragma unroll
+          for (int i = 0; i < DBC; ++i) acc[dc + i] = mfma32(ao[i], pf, acc[dc + i]);
+        }
       }
     }
   };
 
-  // dS wave, step st (one iteration after its P wave): dP, dS = P (dP − D), dKᵀ += Qᵀ dS
-  auto step_ds = [&](int st, const char* buf, const f32x4* xr) __attribute__((always_inline)) {
+  // dS wave, step st (one iteration after its P wave): per 32-query block, dP, dS = P (dP − D)
+  // with the bf16 P of its partner, dKᵀ += Qᵀ dS
+  auto step_ds = [&](int st, const char* buf, const i32x4* xr) __attribute__((always_inline)) {
     const char* ob = buf + TILE;
     const f32x4* db = (const f32x4*)(buf + 2 * TILE + BM * 4);
-    f32x16 pacc = f32x16{};
 #pragma unroll
-    for (int sc = 0; sc < C::DS; sc += SB) {
-      i32x4 fo[SB];
+    for (int qb = 0; qb < QBS; ++qb) {
+      f32x16 pacc = f32x16{};
 #pragma unroll
-      for (int s = 0; s < SB; ++s) fo[s] = *(const i32x4*)(ob + so.row[sc + s]);
+      for (int sc = 0; sc < C::DS; sc += SB) {
+        i32x4 fo[SB];
 #pragma unroll
-      for (int s = 0; s < SB; ++s) pacc = mfma32(as_bf16x8(fo[s]), kv[sc + s], pacc);
-      if constexpr (D == 128) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+        for (int s = 0; s < SB; ++s) fo[s] = *(const i32x4*)(ob + 32 * qb * C::RSTR + so.row[sc + s]);
+#pragma unroll
+        for (int s = 0; s < SB; ++s) pacc = mfma32(as_bf16x8(fo[s]), kv[sc + s], pacc);
+        if constexpr (D == 128) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+        }
       }
-    }
-    bf16x8 sf[2];
+      bf16x8 sf[2];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const f32x4 pv = xr[(pair * 4 + jj) * 64 + lane];
-      const f32x4 dd = db[2 * jj + half];
-      float dsv[4];
+      for (int u = 0; u < 2; ++u) {
+        const i32x4 pw = xr[((pair * QBS + qb) * 2 + u) * 64 + lane];
+        i32x4 us;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) dsv[u] = pv[u] * (pacc[4 * jj + u] - dd[u]);
-      i32x4 us = __builtin_bit_cast(i32x4, sf[jj >> 1]);
-      us[2 * (jj & 1)] = (int)pack_bf16x2(dsv[0], dsv[1]);
-      us[2 * (jj & 1) + 1] = (int)pack_bf16x2(dsv[2], dsv[3]);
-      sf[jj >> 1] = __builtin_bit_cast(bf16x8, us);
-    }
+        for (int e = 0; e < 4; ++e) {             // word e: rows of jj = 2u + e/2, values (e%2)·2, +1
+          const int jj = 2 * u + (e >> 1), j0 = 4 * jj + 2 * (e & 1);
+          const f32x4 dd = db[8 * qb + 2 * jj + half];
+          const float p0 = __builtin_bit_cast(float, (uint32_t)pw[e] << 16);
+          const float p1 = __builtin_bit_cast(float, (uint32_t)pw[e] & 0xFFFF0000u);
+          us[e] = (int)pack_bf16x2(p0 * (pacc[j0] - dd[2 * (e & 1)]), p1 * (pacc[j0 + 1] - dd[2 * (e & 1) + 1]));
+        }
+        sf[u] = __builtin_bit_cast(bf16x8, us);
+      }
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int rb = 16 * kk * C::RSTR;
+      for (int kk = 0; kk < 2; ++kk) {
+        const int rb = (32 * qb + 16 * kk) * C::RSTR;
 #pragma unroll
-      for (int dc = 0; dc < C::DB; dc += DBC) {
-        bf16x8 aq[DBC];
+        for (int dc = 0; dc < C::DB; dc += DBC) {
+          bf16x8 aq[DBC];
 #pragma unroll
-        for (int i = 0; i < DBC; ++i)
-          aq[i] = concat_tr(lds_read_tr16(buf + rb + so.tr0[dc + i]), lds_read_tr16(buf + rb + so.tr1[dc + i]));
+          for (int i = 0; i < DBC; ++i)
+            aq[i] = concat_tr(lds_read_tr16(buf + rb + so.tr0[dc + i]), lds_read_tr16(buf + rb + so.tr1[dc + i]));
 #pragma unroll
-        for (int i = 0; i < DBC; ++i) acc[dc + i] = mfma32(aq[i], sf[kk], acc[dc + i]);
+          for (int i = 0; i < DBC; ++i) acc[dc + i] = mfma32(aq[i], sf[kk], acc[dc + i]);
+        }
       }
     }
   };
 
   // Iteration i: copy step i+1 into `nxt`; P waves run step i on `cur`; dS waves run step i-1
   // on `prv`. The conditions depend on i only, so every wave meets the same barriers.
-  auto iter = [&](int i, char* cur, char* prv, char* nxt, f32x4* xcur, const f32x4* xprv)
+  auto iter = [&](int i, char* cur, char* prv, char* nxt, i32x4* xcur, const i32x4* xprv)
       __attribute__((always_inline)) {
     if (i + 1 < n_steps) stage(i + 1, nxt);
     if (!ds_wave) {
