@@ -18,6 +18,12 @@ null when the kernel source changed since they were taken.
 
 ``cpu_baseline`` times the float64 oracle (naive two-pass attention with an explicit mask)
 on a bounded sample of the same workload on the host cores, and reports its causal FLOP rate.
+
+The same line carries the MX paths on the 65K-token packed workload: ``mxfp8`` (E4M3 operands)
+and ``mxfp4`` (E2M1 score product, the rest as mxfp8), each with its own ``roofline``; peaks of
+mixed-format kernels are n / Σ 1/peak over their counted GEMM units.
+
+    python bench.py --decode      # decoding over a packed KV cache: GB/s against HBM peak
 """
 import argparse
 import hashlib
