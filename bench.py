@@ -42,10 +42,11 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0, "fp32": 157.3}   #
 # Counted GEMM units per MX kernel and the format each runs in ("qk": the score product, E4M3 on
 # the MXFP8 path and E2M1 on the MXFP4/FP8 path). A mixed kernel's peak is the rate at which its
 # counted units would run if each ran at its format's peak: n / Σ 1/peak.
-MX_UNIT_FORMATS = {"attn_fwd_mx_kernel": ["qk", "fp8"], "attn_bwd_dkdv_mx_kernel": ["qk", "fp8", "fp8", "fp8"],
-                   "attn_bwd_dq_mx_kernel": ["fp8"]}
-# the whole fwd+bwd step under the 3.5× convention: S twice (fwd, bwd recompute), 5 other units
-MX_STEP_FORMATS = ["qk", "qk", "fp8", "fp8", "fp8", "fp8", "fp8"]
+# dK = dSᵀQ and dQ = dS·K run as bf16 products on the MX paths (bf16 dS and bf16 Q / K rows)
+MX_UNIT_FORMATS = {"attn_fwd_mx_kernel": ["qk", "fp8"], "attn_bwd_dkdv_mx_kernel": ["qk", "fp8", "fp8", "bf16"],
+                   "attn_bwd_dq_mx_kernel": ["bf16"]}
+# the whole fwd+bwd step under the 3.5× convention: S twice (fwd, bwd recompute), PV, dP, dV, dK, dQ
+MX_STEP_FORMATS = ["qk", "qk", "fp8", "fp8", "fp8", "bf16", "bf16"]
 
 
 def mixed_peak(formats, qk_fmt):
@@ -365,7 +366,7 @@ def main():
     if args.mx_workload:
         wm = W.make_workload(args.mx_workload)
         mres = measure(wm, True, args.steps, args.warmup)
-        mres["dtype"] = "mxfp8 (E4M3 + E8M0 per 32; bf16 diagonal tiles)"
+        mres["dtype"] = "mxfp8 (E4M3 + E8M0 per 32; bf16 diagonal tiles and dS products)"
         mres["unit"] = "TFLOP/s"
         out["mxfp8"] = mres
     if args.mx4_workload:

@@ -6,26 +6,23 @@
 // consistency), each product blocked along its contraction axis:
 //  * S = Q_d K_dᵀ from the forward's own Q_d/K_d bytes, so P = exp(S − LSE) reproduces the
 //    forward's probabilities; dP = dO_d V_dᵀ. Both contract over d (scale per token).
-//  * dV += Pᵀ dO, dK += dSᵀ Q, dQ += dS K contract over tokens. Off the diagonal 128×128 tile
-//    they use the token-blocked copies dO_t, Q_t, K_t (one scale per channel and 32 doc-local
-//    tokens). P (normalised, so ~1/L) is encoded E4M3 with an MX scale computed in registers
-//    per 32 contraction elements; dS as two E4M3 terms (value and rounding residual, each with
-//    its own MX scale), two MFMAs with the same A operand, since a single E4M3 rounding of dS
-//    (relative error up to 2^-4) alone costs ~3% rel-L2 in dQ and dK when most pairs are off
-//    the diagonal. On the diagonal tile everything token-contracted
-//    stays bf16 (bf16 MFMA, transposing LDS reads), so no scale spans a query's future.
+//  * dV += Pᵀ dO contracts over tokens. Off the diagonal 128×128 tile it uses the token-blocked
+//    copy dO_t (one scale per channel and 32 doc-local tokens) and P (normalised, so ~1/L)
+//    encoded E4M3 with an MX scale computed in registers per 32 contraction elements; on the
+//    diagonal tile it stays bf16 (bf16 MFMA, transposing LDS reads), so no scale spans a
+//    query's future.
+//  * dK += dSᵀ Q and dQ += dS K take bf16 dS and the bf16 Q / K rows on every tile. dS needs
+//    about 8 significant bits here (one E4M3 rounding, relative error up to 2^-4, alone costs
+//    ~3% rel-L2 in dQ and dK), and on gfx950 two E4M3 products (value and rounding residual)
+//    over 64 contraction elements take exactly the matrix-core time of bf16 products over the
+//    same 64, while the second term's block maxima, encoding and residual cost ~75 vector
+//    instructions per 32×32 block; the bf16 pack costs 8.
 // Token-blocked tiles are staged with the 4-byte chunk order (0,2,4,6,1,3,5,7) per 32-token
-// block so that the A operand read at offset 16h matches the lane's P / dS register order.
+// block so that the A operand read at offset 16h matches the lane's P register order.
 #include "cfa_device.h"
 #include "cfa_kernels.h"
 
 namespace cfa {
-
-__device__ inline int mx_exp_of(float amax) {
-  if (!(amax > 0.f)) return -127;
-  const int ex = __builtin_amdgcn_frexp_expf(amax);
-  return min(max(ex - 1 - 8, -127), 127);
-}
 
 // One 32-element contraction block, this lane's 16 values: encode x·2^-e into the 4 words the
 // lane contributes to a B operand (exponents from fit_exp keep |x|·2^-e <= 448).
@@ -37,27 +34,6 @@ __device__ inline i32x4 encode16(const f32x16& x, int e) {
   return r;
 }
 
-// x -= decode(c)·2^e in place (the rounding residual of encode16).
-__device__ inline void residual16(f32x16& x, const i32x4& c, int e) {
-  const float s = pow2i(e);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const f32x2 a01 = unpack_fp8x2_scaled<false>(c[k], s), a23 = unpack_fp8x2_scaled<true>(c[k], s);
-    x[4 * k + 0] -= a01.x;
-    x[4 * k + 1] -= a01.y;
-    x[4 * k + 2] -= a23.x;
-    x[4 * k + 3] -= a23.y;
-  }
-}
-
-// Encode 2 × 16 values (two 32-element contraction blocks, 16 per lane each) as the B operand:
-// bytes 0-15 block 0 with exponent e0, bytes 16-31 block 1 with exponent e1 (exponents from
-// fit_exp, so every scaled value lies within ±448).
-__device__ inline i32x8 encode_b_fp8(const f32x16& x0, const f32x16& x1, int e0, int e1) {
-  const i32x4 a = encode16(x0, e0), b = encode16(x1, e1);
-  return i32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-}
-
 __device__ inline float amax16(const f32x16& x) {
   float m = 0.f;
 #pragma unroll
@@ -65,54 +41,15 @@ __device__ inline float amax16(const f32x16& x) {
   return m;
 }
 
-// Block exponent for values quantised inside the kernel (P, dS): the smallest power of two
-// that maps amax to at most 448, so the largest element is never clipped (the operand rule
-// of mx_quantize may clip it by up to 1/8, which the oracle models for Q/K/V/dO but not here).
+// Block exponent for values quantised inside the kernel (P): the smallest e with
+// amax·2^-e <= 448, so the largest element is never clipped (the operand rule of mx_quantize
+// may clip it by up to 1/8, which the oracle models for Q/K/V/dO but not here). Read off the
+// bits of amax >= 0: for amax in [2^E, 2^(E+1)), amax·2^-(E-8) = 1.m·2^8 exceeds 448 = 1.75·2^8
+// exactly when the mantissa field exceeds 0x600000. Zero and subnormal amax give -127.
 __device__ inline int fit_exp(float amax) {
-  int e = mx_exp_of(amax);
-  if (amax > 0.f && __builtin_amdgcn_ldexpf(amax, -e) > 448.f) e += 1;
-  return e;
-}
-
-// Exponents of the two 32-element contraction blocks held by a lane pair (l, l^32).
-__device__ inline void block_exps(const f32x16& x0, const f32x16& x1, int& e0, int& e1) {
-  float a0 = amax16(x0), a1 = amax16(x1);
-  a0 = wave_max_xor32(a0);
-  a1 = wave_max_xor32(a1);
-  e0 = fit_exp(a0);
-  e1 = fit_exp(a1);
-}
-
-// Two E4M3 terms for one B operand: x ≈ hi·2^e + lo·2^(e−4), e the block exponent from
-// fit_exp. With every |x|·2^-e <= 448 the rounding residual of hi is at most 16·2^e (half the
-// E4M3 spacing 32 of [256, 448]), so residual·2^(4−e) <= 256 fits E4M3 without a second block
-// maximum. One E4M3 rounding has a relative error up to 2^-4; the residual term brings it to
-// ~2^-8.
-struct Fp8Pair {
-  i32x8 hi, lo;
-  int shi, slo;  // this lane's scale bytes (k-block = l/32)
-};
-
-// Two-term encoding of block b (0 or 1) of a B operand: consumes x (its
-// storage becomes the residual), writes words 4b..4b+3 of hi and lo and, in the lane group
-// that supplies block b's scale (half == b), the two scale bytes.
-__device__ inline void encode_two_term_block(f32x16& x, int b, int half, Fp8Pair& r) {
-  float a = amax16(x);
-  a = wave_max_xor32(a);
-  const int e = fit_exp(a);
-  const i32x4 h4 = encode16(x, e);
-  residual16(x, h4, e);
-  const int f = max(e - 4, -127);
-  const i32x4 l4 = encode16(x, f);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    r.hi[4 * b + k] = h4[k];
-    r.lo[4 * b + k] = l4[k];
-  }
-  if (half == b) {
-    r.shi = e + 127;
-    r.slo = f + 127;
-  }
+  const uint32_t b = __builtin_bit_cast(uint32_t, amax);
+  const int e = (int)(b >> 23) - 135 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return min(max(e, -127), 127);
 }
 
 __device__ inline i32x8 load_a_fp8(const char* row, int half) {
@@ -128,10 +65,10 @@ __device__ inline i32x8 load_a_fp8(const char* row, int half) {
 //    P to the exchange buffer (bf16), dVᵀ += dO_tᵀ P with P MX-encoded per 32-query block, or
 //    dOᵀ P in bf16 on diagonal steps.
 //  * dS wave (w + 4), one step behind: V_d in registers. dP = dO_d V_dᵀ, dS = P (dP − D) with
-//    its partner's P, dKᵀ += Q_tᵀ dS (two-term E4M3) or Qᵀ dS in bf16 on diagonal steps.
+//    its partner's P, dKᵀ += Qᵀ dS in bf16 (transposing reads of the bf16 Q rows).
 // Each role stages its own operands by direct global -> LDS copies into two static buffers:
 //   P wave:  [Q_d codes 64 × 128 B][Q_d scales 64 × 4][LSE·log2 e][dO_t 128 × 64 B + 2 × 128 scales | bf16 dO rows]
-//   dS wave: [dO_d codes][dO_d scales][D][Q_t + scales | bf16 Q rows]
+//   dS wave: [dO_d codes][dO_d scales][D][bf16 Q rows]
 // Iteration i: P waves copy step i+1 and compute step i; dS waves copy step i and compute step
 // i−1 (P of step i−1 sits in exchange buffer (i−1) mod 2). Every buffer is a separate static
 // array and the loop is unrolled twice, so no copy in flight aliases a buffer being read.
@@ -151,9 +88,8 @@ template <bool FP4>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
     const uint8_t* __restrict__ qd, const uint8_t* __restrict__ qd_sc, const uint8_t* __restrict__ kd,
     const uint8_t* __restrict__ kd_sc, const uint8_t* __restrict__ dod, const uint8_t* __restrict__ dod_sc,
-    const uint8_t* __restrict__ vd, const uint8_t* __restrict__ vd_sc, const uint8_t* __restrict__ qt,
-    const uint8_t* __restrict__ qt_sc, const uint8_t* __restrict__ dot, const uint8_t* __restrict__ dot_sc,
-    const __bf16* __restrict__ q, const __bf16* __restrict__ dout, const float* __restrict__ lse,
+    const uint8_t* __restrict__ vd, const uint8_t* __restrict__ vd_sc, const uint8_t* __restrict__ dot,
+    const uint8_t* __restrict__ dot_sc, const __bf16* __restrict__ q, const __bf16* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, __bf16* __restrict__ dk, __bf16* __restrict__ dv, Plan plan,
     const int* __restrict__ padoff, int total_tokens, int t_pad, int hq, int hkv, float scale, int causal) {
   using C = MxDkdvTile;
@@ -243,10 +179,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
     if (pair == 0)
       g2lds4((ds_wave ? dod_sc : qd_sc) + tok0 * 4 + (uint32_t)min(lane, rmax) * (uint32_t)hq * 4, buf + C::OFF_SC);
     if (pair == 1) rreg = (ds_wave ? delta : lse)[(size_t)h * total_tokens + s0 + q0 + min(lane, rmax)];
-    if (step_is_diag(st)) {
+    if (ds_wave || step_is_diag(st)) {
       stage_rows_lds<BM>(buf + C::OFF_U, (const char*)((ds_wave ? q : dout) + tok0 * D), tok_b * 2, rmax, pair, lane);
     } else {
-      const uint8_t* tsrc = (ds_wave ? qt : dot) + (size_t)h * D * t_pad + pcol + q0;
+      const uint8_t* tsrc = dot + (size_t)h * D * t_pad + pcol + q0;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {             // token-blocked codes: 8 blocks of 16 channel rows
         const int I = 2 * pair + j, r = 16 * I + (lane >> 2);
@@ -255,8 +191,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
       }
       if (pair == 2 && lane < 16) {
         const int blk = min((q0 >> 5) + (lane >> 3), lp / 32 - 1);
-        g2lds16((ds_wave ? qt_sc : dot_sc) + ((size_t)h * (t_pad / 32) + (pcol >> 5) + blk) * D + 16 * (lane & 7),
-                buf + C::OFF_TSC);
+        g2lds16(dot_sc + ((size_t)h * (t_pad / 32) + (pcol >> 5) + blk) * D + 16 * (lane & 7), buf + C::OFF_TSC);
       }
     }
   };
@@ -353,17 +288,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
 
   // dS wave, step st (one iteration after its P wave); the query blocks one after the other
   auto step_ds = [&](int st, const char* buf, const i32x4* xr) __attribute__((always_inline)) {
-    const bool diag = step_is_diag(st);
     const f32x4* dd = (const f32x4*)(buf + C::OFF_ROW);
-    bf16x8 sf[4];                               // diagonal steps: bf16 dS
-    Fp8Pair ds2;                                // other steps: two-term E4M3 dS
-    ds2.shi = ds2.slo = 127;
+    bf16x8 sf[4];                               // bf16 dS, B operands of the dK product
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x16 x = dscores(buf, qb);              // dP
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const i32x4 pw = xr[(pair * 4 + 2 * qb + u) * 64 + lane];
+        i32x4 us;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           const f32x4 dr = dd[8 * qb + 2 * (2 * u + jj) + half];
@@ -371,47 +304,24 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
           for (int e = 0; e < 2; ++e) {
             const uint32_t word = (uint32_t)pw[2 * jj + e];
             const int j = 8 * u + 4 * jj + 2 * e;
-            x[j] = __builtin_bit_cast(float, word << 16) * (x[j] - dr[2 * e]);
-            x[j + 1] = __builtin_bit_cast(float, word & 0xFFFF0000u) * (x[j + 1] - dr[2 * e + 1]);
+            us[2 * jj + e] = (int)pack_bf16x2(__builtin_bit_cast(float, word << 16) * (x[j] - dr[2 * e]),
+                                              __builtin_bit_cast(float, word & 0xFFFF0000u) * (x[j + 1] - dr[2 * e + 1]));
           }
         }
-      }
-      if (diag) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          i32x4 us;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) us[e] = (int)pack_bf16x2(x[8 * u + 2 * e], x[8 * u + 2 * e + 1]);
-          sf[2 * qb + u] = __builtin_bit_cast(bf16x8, us);
-        }
-      } else {
-        encode_two_term_block(x, qb, half, ds2);
+        sf[2 * qb + u] = __builtin_bit_cast(bf16x8, us);
       }
     }
-    if (diag) {
-      const SwzOffsets<D> so(lane);
-      const char* qb_ = buf + C::OFF_U;
+    const SwzOffsets<D> so(lane);
+    const char* qb_ = buf + C::OFF_U;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int rb = (32 * (kk >> 1) + 16 * (kk & 1)) * 256;
-        bf16x8 aq[4];
+    for (int kk = 0; kk < 4; ++kk) {
+      const int rb = (32 * (kk >> 1) + 16 * (kk & 1)) * 256;
+      bf16x8 aq[4];
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-          aq[db] = concat_tr(lds_read_tr16(qb_ + rb + so.tr0[db]), lds_read_tr16(qb_ + rb + so.tr1[db]));
+      for (int db = 0; db < 4; ++db)
+        aq[db] = concat_tr(lds_read_tr16(qb_ + rb + so.tr0[db]), lds_read_tr16(qb_ + rb + so.tr1[db]));
 #pragma unroll
-        for (int db = 0; db < 4; ++db) acc[db] = mfma32(aq[db], sf[kk], acc[db]);
-      }
-    } else {
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int ch = 32 * db + r32;
-        const char* rp = buf + C::OFF_U + ch * 64;
-        const i32x4 lo = *(const i32x4*)(rp + to[0]), hi = *(const i32x4*)(rp + to[1]);
-        const i32x8 aq = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        const int sa = *(const uint8_t*)(buf + C::OFF_TSC + half * 128 + ch);
-        acc[db] = mfma32_mx(aq, sa, ds2.hi, ds2.shi, acc[db]);
-        acc[db] = mfma32_mx(aq, sa, ds2.lo, ds2.slo, acc[db]);
-      }
+      for (int db = 0; db < 4; ++db) acc[db] = mfma32(aq[db], sf[kk], acc[db]);
     }
   };
 
@@ -470,16 +380,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
 // ------------------------------------------------------------------ dQ
 // A wave owns 32 queries of one head (Q_d, dO_d in registers as B operands); the workgroup
 // walks key tiles of 64, staged by direct global -> LDS copies into two static buffers:
-//   [K_d codes 64 × 128 B][K_d scales 64 × 4][V_d codes][V_d scales]
-//   [diagonal: K bf16 rows (SwzTile<128>) | otherwise: K_t codes 128 channel rows × 64 B, scales 2 × 128]
-// (code rows XOR-swizzled as in the MX forward kernel).
+//   [K_d codes 64 × 128 B][K_d scales 64 × 4][V_d codes][V_d scales][K bf16 rows (SwzTile<128>)]
+// (code rows XOR-swizzled as in the MX forward kernel). S and dP are scaled fp8 products; dQ
+// takes bf16 dS and the bf16 K rows (transposing reads) on every tile.
 struct MxDqTile {
   static constexpr int BN = 64;
   static constexpr int OFF_KDSC = BN * 128;
   static constexpr int OFF_VD = OFF_KDSC + BN * 4;
   static constexpr int OFF_VDSC = OFF_VD + BN * 128;
   static constexpr int OFF_U = OFF_VDSC + BN * 4;
-  static constexpr int OFF_KTSC = OFF_U + 128 * 64;
   static constexpr int STAGE = OFF_U + BN * 256;
 };
 
@@ -489,10 +398,9 @@ template <bool FP4>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
     const uint8_t* __restrict__ qd, const uint8_t* __restrict__ qd_sc, const uint8_t* __restrict__ kd,
     const uint8_t* __restrict__ kd_sc, const uint8_t* __restrict__ dod, const uint8_t* __restrict__ dod_sc,
-    const uint8_t* __restrict__ vd, const uint8_t* __restrict__ vd_sc, const uint8_t* __restrict__ kt,
-    const uint8_t* __restrict__ kt_sc, const __bf16* __restrict__ k, const float* __restrict__ lse,
-    const float* __restrict__ delta, __bf16* __restrict__ dq, Plan plan, const int* __restrict__ padoff,
-    int total_tokens, int t_pad, int hq, int hkv, float scale, int causal) {
+    const uint8_t* __restrict__ vd, const uint8_t* __restrict__ vd_sc, const __bf16* __restrict__ k,
+    const float* __restrict__ lse, const float* __restrict__ delta, __bf16* __restrict__ dq, Plan plan,
+    int total_tokens, int hq, int hkv, float scale, int causal) {
   using C = MxDqTile;
   constexpr int D = 128, BN = C::BN;
   __shared__ __attribute__((aligned(16))) char lds_a[C::STAGE];
@@ -501,8 +409,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
   const int p = blockIdx.x / hq, h = blockIdx.x % hq;
   int s0, L, t, doc;
   if (!decode_item(plan, p, 128, true, s0, L, t, &doc)) return;
-  const int pcol = padoff[doc];
-  const int lp = 32 * ((L + 31) / 32);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5, r32 = lane & 31;
   const int g = h / (hq / hkv);
   const int wr0 = t * 128 + 32 * w;
@@ -511,14 +417,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
   const int n_kt = (kv_end + BN - 1) / BN;
   const int wave_last_key = causal ? min(L, wr0 + 32) - 1 : L - 1;
   const float sl2 = scale * LOG2E;
-  auto tile_is_diag = [&](int ktile) { return causal && ((ktile * BN) / 128 == t); };
-  int ko[2][2], to[2];
+  int ko[2][2];
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int u = 0; u < 2; ++u) ko[s][u] = 16 * ((4 * s + 2 * u + half) ^ kd_swz(r32));
-#pragma unroll
-  for (int u = 0; u < 2; ++u) to[u] = 16 * ((2 * u + half) ^ vt_swz(r32));
   int kq[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) kq[s] = 16 * ((2 * s + half) ^ vt_swz(r32));
@@ -548,8 +451,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
 #pragma unroll
   for (int b = 0; b < 4; ++b) dqa[b] = f32x16{};
 
-  // key tile -> LDS; keys past kv_end are clamped into the document (K_d, V_d, bf16 K) or its
-  // last token block (K_t); they are masked (P = 0)
+  // key tile -> LDS; keys past kv_end are clamped into the document; they are masked (P = 0)
   // Addresses: a wave-uniform 64-bit tile base plus a 32-bit lane offset within the tile.
   const uint32_t krow_b = (uint32_t)hkv * D;      // bytes between consecutive tokens (codes, bf16/2)
   auto stage = [&](int ktile, char* tb) {
@@ -573,21 +475,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
     const uint32_t soff = (uint32_t)min(lane, rmax) * (uint32_t)hkv * 4;
     if (w == 0) g2lds4(kd_sc + tok0 * 4 + soff, tb + C::OFF_KDSC);
     if (w == 1) g2lds4(vd_sc + tok0 * 4 + soff, tb + C::OFF_VDSC);
-    if (tile_is_diag(ktile)) {
-      stage_rows_lds<BN>(tb + C::OFF_U, (const char*)(k + tok0 * D), krow_b * 2, rmax, w, lane);
-    } else {
-      const uint8_t* ktb = kt + (size_t)g * D * t_pad + pcol + k0;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {             // K_t codes: 8 blocks of 16 channel rows
-        const int I = 2 * w + j, r = 16 * I + (lane >> 2);
-        const int col = min(16 * ((lane & 3) ^ vt_swz(r)), lp - 16 - k0);
-        g2lds16(ktb + (uint32_t)(r * t_pad + col), tb + C::OFF_U + I * 1024);
-      }
-      if (w == 2 && lane < 16) {
-        const int blk = min((k0 >> 5) + (lane >> 3), lp / 32 - 1);
-        g2lds16(kt_sc + ((size_t)g * (t_pad / 32) + (pcol >> 5) + blk) * D + 16 * (lane & 7), tb + C::OFF_KTSC);
-      }
-    }
+    stage_rows_lds<BN>(tb + C::OFF_U, (const char*)(k + tok0 * D), krow_b * 2, rmax, w, lane);
   };
 
   // dS of one 32-key block b of the tile (this lane: query qrow, keys k0 + 32b + 8(j/4) + 4·half + j%4)
@@ -625,8 +513,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
     return x;
   };
 
-  // diagonal tile: bf16 dS and bf16 K (transposing reads)
-  auto tile_diag = [&](const char* tb, int k0, bool need_mask) __attribute__((always_inline)) {
+  // one key tile: bf16 dS and bf16 K (transposing reads)
+  auto tile = [&](const char* tb, int k0, bool need_mask) __attribute__((always_inline)) {
     bf16x8 sf[4];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -653,34 +541,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
     }
   };
 
-  // other tiles: two-term E4M3 dS and token-blocked K_t
-  auto tile_off = [&](const char* tb, int k0, bool need_mask) __attribute__((always_inline)) {
-    Fp8Pair ds2;
-    ds2.shi = ds2.slo = 127;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      f32x16 x = ds_block(tb, k0, b, need_mask);
-      encode_two_term_block(x, b, half, ds2);
-    }
-#pragma unroll
-    for (int dbk = 0; dbk < 4; ++dbk) {
-      const int ch = 32 * dbk + r32;
-      const char* kr = tb + C::OFF_U + ch * 64;
-      const i32x4 lo = *(const i32x4*)(kr + to[0]), hi = *(const i32x4*)(kr + to[1]);
-      const i32x8 ak = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      const int ksa = *(const uint8_t*)(tb + C::OFF_KTSC + half * 128 + ch);
-      dqa[dbk] = mfma32_mx(ak, ksa, ds2.hi, ds2.shi, dqa[dbk]);
-      dqa[dbk] = mfma32_mx(ak, ksa, ds2.lo, ds2.slo, dqa[dbk]);
-    }
-  };
-
   auto iter = [&](int ktile, const char* tb, char* nxt) __attribute__((always_inline)) {
     const int k0 = ktile * BN;
     if (ktile + 1 < n_kt) stage(ktile + 1, nxt);
     if (k0 <= wave_last_key) {
       const bool need_mask = causal ? (k0 + BN - 1 > wr0) : (k0 + BN > L);
-      if (tile_is_diag(ktile)) tile_diag(tb, k0, need_mask);
-      else tile_off(tb, k0, need_mask);
+      tile(tb, k0, need_mask);
     }
     wait_vmem();
     __syncthreads();
@@ -720,14 +586,14 @@ hipError_t launch_bwd_dkdv_mx(const MxOperands& m, const void* q, const void* do
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
   auto kern = fp4 ? attn_bwd_dkdv_mx_kernel<true> : attn_bwd_dkdv_mx_kernel<false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), 0, stream, m.qd, m.qd_sc, m.kd, m.kd_sc, m.dod, m.dod_sc,
-                     m.vd, m.vd_sc, m.qt, m.qt_sc, m.dot, m.dot_sc, (const __bf16*)q, (const __bf16*)dout, lse, delta,
+                     m.vd, m.vd_sc, m.dot, m.dot_sc, (const __bf16*)q, (const __bf16*)dout, lse, delta,
                      (__bf16*)dk, (__bf16*)dv, plan, padoff, T, t_pad, hq, hkv, scale, causal);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq_mx(const MxOperands& m, const void* k, const float* lse, const float* delta, void* dq,
-                            const Plan& plan_any, const int* pref_base, const int* padoff, int T, int t_pad, int hq,
-                            int hkv, float scale, int causal, bool fp4, hipStream_t stream) {
+                            const Plan& plan_any, const int* pref_base, int T, int hq, int hkv, float scale,
+                            int causal, bool fp4, hipStream_t stream) {
   Plan plan = plan_any;
   plan.pref = pref_base + pref_slot(128) * (plan.n_docs + 1);
   const long grid = ((long)(T + 127) / 128 + plan.n_docs) * hq;
@@ -735,8 +601,7 @@ hipError_t launch_bwd_dq_mx(const MxOperands& m, const void* k, const float* lse
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
   auto kern = fp4 ? attn_bwd_dq_mx_kernel<true> : attn_bwd_dq_mx_kernel<false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, m.qd, m.qd_sc, m.kd, m.kd_sc, m.dod, m.dod_sc,
-                     m.vd, m.vd_sc, m.kt, m.kt_sc, (const __bf16*)k, lse, delta, (__bf16*)dq, plan, padoff, T, t_pad, hq,
-                     hkv, scale, causal);
+                     m.vd, m.vd_sc, (const __bf16*)k, lse, delta, (__bf16*)dq, plan, T, hq, hkv, scale, causal);
   return hipGetLastError();
 }
 

@@ -111,7 +111,7 @@ struct WsLayout {
   size_t dkdv_part;         // bwd bf16 with a head split: float [2][n_split][T][hkv][d]
   int n_split;
   MxBuf vt;                 // fwd MX: V along tokens
-  MxBuf dod, dot, vd, qt, kt;  // bwd MX
+  MxBuf dod, dot, vd;       // bwd MX
   size_t total;
 };
 
@@ -139,8 +139,6 @@ WsLayout ws_layout(int pass, const Sizes& s) {
       off = add_mx_d(off, s, s.hq, w.dod);
       off = add_mx_t(off, s, s.hq, w.dot);
       off = add_mx_d(off, s, s.hkv, w.vd);
-      off = add_mx_t(off, s, s.hq, w.qt);
-      off = add_mx_t(off, s, s.hkv, w.kt);
     }
   }
   w.total = off;
@@ -311,8 +309,6 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
     hipError_t e = cfa::launch_mx_quantize_d(dout, (long)total_tokens * hq * d, U(wl.dod, true), U(wl.dod, false), st);
     if (!e) e = cfa::launch_mx_quantize_t(dout, total_tokens, hq, d, ws, n_docs, U(wl.dot, true), U(wl.dot, false), tp, true, st);
     if (!e) e = cfa::launch_mx_quantize_d(v, (long)total_tokens * hkv * d, U(wl.vd, true), U(wl.vd, false), st);
-    if (!e) e = cfa::launch_mx_quantize_t(q, total_tokens, hq, d, ws, n_docs, U(wl.qt, true), U(wl.qt, false), tp, true, st);
-    if (!e) e = cfa::launch_mx_quantize_t(k, total_tokens, hkv, d, ws, n_docs, U(wl.kt, true), U(wl.kt, false), tp, true, st);
     mark(3, 1, st);
     if (int r = check_hip(e, "backward quantisation")) return r;
     cfa::MxOperands m;
@@ -320,8 +316,6 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
     m.kd = (const uint8_t*)sv + sl.kd.codes; m.kd_sc = (const uint8_t*)sv + sl.kd.scales;
     m.dod = U(wl.dod, true); m.dod_sc = U(wl.dod, false);
     m.vd = U(wl.vd, true); m.vd_sc = U(wl.vd, false);
-    m.qt = U(wl.qt, true); m.qt_sc = U(wl.qt, false);
-    m.kt = U(wl.kt, true); m.kt_sc = U(wl.kt, false);
     m.dot = U(wl.dot, true); m.dot_sc = U(wl.dot, false);
     mark(1, 0, st);
     if (int r = check_hip(cfa::launch_bwd_dkdv_mx(m, q, dout, lse, delta, dk, dv, plan, plan.pref, padoff, total_tokens,
@@ -330,8 +324,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
       return r;
     mark(1, 1, st);
     mark(2, 0, st);
-    int r = check_hip(cfa::launch_bwd_dq_mx(m, k, lse, delta, dq, plan, plan.pref, padoff, total_tokens, tp, hq, hkv,
-                                            scale, causal, dtype == CFA_MXFP4, st),
+    int r = check_hip(cfa::launch_bwd_dq_mx(m, k, lse, delta, dq, plan, plan.pref, total_tokens, hq, hkv, scale,
+                                            causal, dtype == CFA_MXFP4, st),
                       "MX dQ kernel");
     mark(2, 1, st);
     return r;

@@ -9,7 +9,7 @@ namespace cfa {
 // MX-quantised operands of the MXFP8 backward (codes + scales): d-blocked *_d, token-blocked *_t.
 struct MxOperands {
   const uint8_t *qd, *qd_sc, *kd, *kd_sc, *dod, *dod_sc, *vd, *vd_sc;
-  const uint8_t *qt, *qt_sc, *kt, *kt_sc, *dot, *dot_sc;
+  const uint8_t *dot, *dot_sc;
 };
 
 hipError_t launch_plan(const int* cu, int n_docs, int total_tokens, void* ws, hipStream_t stream);
@@ -80,7 +80,7 @@ hipError_t launch_bwd_dkdv_mx(const MxOperands& m, const void* q, const void* do
                               const int* padoff, int T, int t_pad, int hq, int hkv, float scale, int causal, bool fp4, hipStream_t stream);
 
 hipError_t launch_bwd_dq_mx(const MxOperands& m, const void* k, const float* lse, const float* delta, void* dq,
-                            const Plan& plan, const int* pref_base, const int* padoff, int T, int t_pad, int hq,
-                            int hkv, float scale, int causal, bool fp4, hipStream_t stream);
+                            const Plan& plan, const int* pref_base, int T, int hq, int hkv, float scale, int causal,
+                            bool fp4, hipStream_t stream);
 
 }  // namespace cfa

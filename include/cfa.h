@@ -208,7 +208,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const u
  * calls record events[2*i] on their stream just before launching their i-th main kernel and
  * events[2*i+1] just after it (the work-list kernel is not counted). Kernel order:
  *   attn_fwd: 0 = forward attention, 1 = (MXFP8) the Q, K, V quantisation passes together;
- *   attn_bwd: 0 = D = rowsum(dO*O), 1 = dK/dV, 2 = dQ, 3 = (MXFP8) the dO, V, Q, K
+ *   attn_bwd: 0 = D = rowsum(dO*O), 1 = dK/dV, 2 = dQ, 3 = (MXFP8) the dO (both axes) and V
  *             quantisation passes together;
  *   attn_decode: 0 = chunk partials, 1 = their merge.
  * Entries may be NULL (not recorded). The caller owns the hipEvent_t handles and keeps the

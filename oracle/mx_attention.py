@@ -7,14 +7,18 @@ operands are reused across matrix orientations (token-block scaling), with safeg
 a shared scale never carries a later token's data into an earlier query, and with the forward
 and backward passes numerically consistent. The page gives no mechanism; the reading here is:
 
-* Every GEMM is blocked along its contraction axis. QKᵀ and dO·Vᵀ contract over the head dim:
-  their operands are the d-blocked copies ``X_d``. P·V, Pᵀ·dO, dS·K and dSᵀ·Q contract over
-  tokens: their operands are the token-blocked, document-local copies ``X_t``.
+* Every MX GEMM is blocked along its contraction axis. QKᵀ and dO·Vᵀ contract over the head
+  dim: their operands are the d-blocked copies ``X_d``. P·V and Pᵀ·dO contract over tokens:
+  their V / dO operands are the token-blocked, document-local copies ``X_t``.
 * A d-block holds one token's channels, so it cannot leak. A token block can: its scale mixes
   32 neighbouring tokens. Pairs (i, j) lying in the same doc-local C×C tile (C = 128) -- the
   diagonal tiles of the causal mask -- therefore use the unquantised bf16 values ``X_b`` in
   every token-contracted GEMM, and only pairs in off-diagonal tiles use ``X_t``. When
   ``causal`` is false no tile is treated as diagonal.
+* The two products with dS (dS·K and dSᵀ·Q) are not MX products: the page fixes no precision
+  per product, dS needs more significant bits than one E4M3 rounding keeps, and a two-term
+  E4M3 dS costs the matrix cores as much as bf16 on the target hardware. Their K / Q operands
+  are the bf16 values ``X_b`` for every pair.
 * The backward reuses the forward's ``Q_d``/``K_d`` bytes, so it sees the same scores.
 
 Computed exactly in float64 from the decoded copies (the decoding is exact):
@@ -24,8 +28,8 @@ Computed exactly in float64 from the decoded copies (the decoding is exact):
     dP_ij = dO_d[i]·V_d[j]                              D_i = dO_b[i]·O[i]
     dS_ij = P_ij·(dP_ij − D_i) + P_ij·dLSE_i             (dLSE optional, else 0)
     dV[j] = Σ_{h in group} Σ_i P_ij·(diag ? dO_b[i] : dO_t[i])
-    dQ[i] = scale·Σ_j dS_ij·(diag ? K_b[j] : K_t[j])
-    dK[j] = scale·Σ_{h in group} Σ_i dS_ij·(diag ? Q_b[i] : Q_t[i])
+    dQ[i] = scale·Σ_j dS_ij·K_b[j]
+    dK[j] = scale·Σ_{h in group} Σ_i dS_ij·Q_b[i]
 
 Not modelled: the rounding of P and dS before a matrix-core product and fp32 accumulation on
 the device.
@@ -113,8 +117,6 @@ def attn_mx_bwd(q_b, k_b, v_b, do_b, cu_seqlens, scale, causal=True, tile=DIAG_T
     T, hq, d = q_b.shape
     hkv = k_b.shape[1]
     group = hq // hkv
-    _, q_t = operand_copies(q_b, cu)
-    _, k_t = operand_copies(k_b, cu)
     q_d, k_d = qk_copy(q_b, qk), qk_copy(k_b, qk)
     v_d, v_t = operand_copies(v_b, cu)
     do_d, do_t = operand_copies(do_b, cu)
@@ -139,10 +141,9 @@ def attn_mx_bwd(q_b, k_b, v_b, do_b, cu_seqlens, scale, causal=True, tile=DIAG_T
                 D = np.sum(do_b[rows, h] * o, axis=1)
                 dp = do_d[rows, h] @ v_d[s0:s1, g].T
                 ds = p * (dp - D[:, None]) + p * dlse[h, rows][:, None]
-                ds_diag, ds_off = np.where(dg, ds, 0.0), np.where(dg, 0.0, ds)
                 dv[s0:s1, g] += p_diag.T @ do_b[rows, h] + p_off.T @ do_t[rows, h]
-                dq[rows, h] = scale * (ds_diag @ k_b[s0:s1, g] + ds_off @ k_t[s0:s1, g])
-                dk[s0:s1, g] += scale * (ds_diag.T @ q_b[rows, h] + ds_off.T @ q_t[rows, h])
+                dq[rows, h] = scale * (ds @ k_b[s0:s1, g])
+                dk[s0:s1, g] += scale * (ds.T @ q_b[rows, h])
     return dq, dk, dv
 
 
@@ -164,8 +165,6 @@ def attn_mx_rows(q_b, k_b, v_b, do_b, rows, scale, causal=True, tile=DIAG_TILE, 
     hkv = k_b.shape[1]
     group = hq // hkv
     cu = np.array([0, L])
-    _, q_t = operand_copies(q_b, cu)
-    _, k_t = operand_copies(k_b, cu)
     q_d, k_d = qk_copy(q_b, qk), qk_copy(k_b, qk)
     v_d, v_t = operand_copies(v_b, cu)
     do_d, do_t = operand_copies(do_b, cu)
@@ -198,8 +197,7 @@ def attn_mx_rows(q_b, k_b, v_b, do_b, rows, scale, causal=True, tile=DIAG_TILE, 
             lse[h, r0:r0 + len(rs)] = m + np.log(l)
             D = np.sum(do_b[rs, h] * ob, axis=1)
             ds = p * (do_d[rs, h] @ v_d[:, g].T - D[:, None])
-            ds_diag, ds_off = np.where(dg, ds, 0.0), np.where(dg, 0.0, ds)
-            dq[r0:r0 + len(rs), h] = scale * (ds_diag @ k_b[:, g] + ds_off @ k_t[:, g])
-            dk[:, g] += scale * (ds_diag.T @ q_b[rs, h] + ds_off.T @ q_t[rs, h])
+            dq[r0:r0 + len(rs), h] = scale * (ds @ k_b[:, g])
+            dk[:, g] += scale * (ds.T @ q_b[rs, h])
             dv[:, g] += p_diag.T @ do_b[rs, h] + p_off.T @ do_t[rs, h]
     return o, lse, dq, dk, dv

@@ -7,6 +7,8 @@
 * Isolation: a packed run equals each document run alone.
 * The diagonal-tile rule: moving a token-blocked copy away from the bf16 values changes only
   off-diagonal contributions.
+* The dS products take the bf16 Q and K: on inputs whose d-blocked copies are exact but whose
+  token-blocked Q/K copies are not, dQ and dK still equal the plain oracle's.
 """
 
 import numpy as np
@@ -148,3 +150,40 @@ def test_mx_rows_match_full_mx_oracle():
     _, _, _, pdk, pdv = mxa.attn_mx_rows(q, k, v, do, np.arange(200, L), 0.2)
     np.testing.assert_allclose(pdk[200:], dk[200:], atol=1e-12)
     np.testing.assert_allclose(pdv[200:], dv[200:], atol=1e-12)
+
+
+def test_ds_products_take_bf16_q_and_k():
+    """Q, K: each token row is c·2^(8·(i % 3)) with |c| in {1, 1.25, ..., 3.5} (3 mantissa bits,
+    largest element <= 1.75·2^k), so every d-block (one token) is exact in E4M3, while a token
+    block spans a 2^16 range and rounds its small tokens. V, dO take values in {0, ±1, ±2, ±4},
+    exact under either blocking. Every MX copy the forward, dP and dV use is then exact, and the
+    MX oracle must equal the plain oracle in all three gradients."""
+    rng = np.random.default_rng(11)
+    lengths = [300, 90]
+    T = sum(lengths)
+    cu = np.array([0, 300, 390])
+    mags = np.array([1.0, 1.25, 1.5, 1.75, 2.0, 2.5, 3.0, 3.5])
+    loc = np.concatenate([np.arange(n) for n in lengths])
+
+    def big_range(h):
+        x = rng.choice(mags, size=(T, h, 64)) * rng.choice([-1.0, 1.0], size=(T, h, 64))
+        return x * (2.0 ** (8 * (loc % 3)))[:, None, None]
+
+    def pow2(h):
+        return rng.choice([0.0, 1.0, -1.0, 2.0, -2.0, 4.0, -4.0], size=(T, h, 64))
+    q, k, v, do = big_range(2), big_range(1), pow2(1), pow2(2)
+    for x in (q, k):
+        xd, xt = mxa.operand_copies(x, cu)
+        assert np.array_equal(xd, x) and not np.array_equal(xt, x)
+    for x in (v, do):
+        xd, xt = mxa.operand_copies(x, cu)
+        assert np.array_equal(xd, x) and np.array_equal(xt, x)
+    sc = 2.0 ** -36                       # scores of the largest rows O(1), the rest near 0
+    g = mxa.attn_mx_bwd(q, k, v, do, cu, sc)
+    g0 = att.attn_bwd(q, k, v, do, cu, sc)
+    for a, b in zip(g, g0):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12 * np.abs(b).max())
+    assert np.abs(g0[1]).max() > 0 and np.abs(g0[0]).max() > 0
+    rows = np.array([0, 2, 130, 299])
+    _, _, rdq, _, _ = mxa.attn_mx_rows(q[:300], k[:300], v[:300], do[:300], rows, sc)
+    np.testing.assert_allclose(rdq, g0[0][rows], rtol=0, atol=1e-12 * np.abs(g0[0]).max())
