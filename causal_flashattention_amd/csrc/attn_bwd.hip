@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     Lq = qd.y;
   }
   const int off = CROSS ? L - Lq : 0;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), half = lane >> 5;
   const int G = hq / hkv;
   const int kw0 = t * 128 + 32 * w;              // first doc-local key of this wave
   const int mykey = kw0 + (lane & 31);
@@ -440,10 +440,14 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
       }
       // masked scores -> -inf, so P = 2^(s·c − LSE·log2 e) is exactly 0 there
       if (masked) {
+        // element j holds query qb0 + c_j, c_j = 8(j/4) + j%4: masked below lo (causal: the
+        // query precedes this lane's key) or above hi (past the document end)
+        const int qb0 = q0 + 32 * qb + 4 * half;
+        const int lo = causal ? mykey - off - qb0 : -1, hi = Lq - 1 - qb0;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int qi = q0 + 32 * qb + 8 * (j >> 2) + 4 * half + (j & 3);
-          if ((causal && mykey > qi + off) || qi >= Lq) sacc[j] = -INFINITY;
+          const int c = 8 * (j >> 2) + (j & 3);
+          if ((c < lo) | (c > hi)) sacc[j] = -INFINITY;
         }
       }
       i32x4 pw[2];
@@ -632,7 +636,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_bwd_dq_kernel(
     Lk = kd.y;
   }
   const int off = CROSS ? Lk - L : 0;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), half = lane >> 5;
   const int g = h / (hq / hkv);
   const int wr0 = t * 128 + 32 * w;
   const int qrow = wr0 + (lane & 31);
@@ -730,11 +734,11 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_bwd_dq_kernel(
         // masked scores -> -inf (wave-uniform branch: diagonal or document-end tiles only),
         // so P = 2^(s·c − LSE·log2 e) is exactly 0 there
         if (need_mask) {
+          // keys above lim are masked; element j holds key k0 + 32b + 4·half + 8(j/4) + j%4
+          const int r = (causal ? qrow + off : Lk - 1) - (k0 + 32 * b + 4 * half);
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = k0 + 32 * b + 8 * (j >> 2) + 4 * half + (j & 3);
-            if (causal ? (key > qrow + off) : (key >= Lk)) sacc[j] = -INFINITY;
-          }
+          for (int j = 0; j < 16; ++j)
+            if (8 * (j >> 2) + (j & 3) > r) sacc[j] = -INFINITY;
         }
 #pragma unroll
         for (int j = 0; j < 16; j += 2) {

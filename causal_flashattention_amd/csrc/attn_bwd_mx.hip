@@ -235,10 +235,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
     for (int qb = 0; qb < 2; ++qb) {
       f32x16 x = dscores(buf, qb);
       if (masked) {
+        // element j holds query qb0 + 8(j/4) + j%4: masked below lo (causal) or above hi
+        const int qb0 = q0 + 32 * qb + 4 * half;
+        const int lo = causal ? mykey - qb0 : -1, hi = L - 1 - qb0;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int qi = q0 + 32 * qb + 8 * (j >> 2) + 4 * half + (j & 3);
-          if ((causal && mykey > qi) || qi >= L) x[j] = -INFINITY;
+          const int c = 8 * (j >> 2) + (j & 3);
+          if ((c < lo) | (c > hi)) x[j] = -INFINITY;
         }
       }
 #pragma unroll
@@ -409,7 +412,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
   const int p = blockIdx.x / hq, h = blockIdx.x % hq;
   int s0, L, t, doc;
   if (!decode_item(plan, p, 128, true, s0, L, t, &doc)) return;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5, r32 = lane & 31;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), half = lane >> 5, r32 = lane & 31;
   const int g = h / (hq / hkv);
   const int wr0 = t * 128 + 32 * w;
   const int qrow = wr0 + r32;
@@ -501,11 +504,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
                        (vsc >> (8 * (2 * s + half))) & 0xFF, oa[s], os[s], pacc);
     }
     if (need_mask) {                     // wave-uniform: diagonal or document-end tiles
+      const int r = (causal ? qrow : L - 1) - (k0 + 32 * b + 4 * half);   // keys above are masked
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = k0 + 32 * b + 8 * (j >> 2) + 4 * half + (j & 3);
-        if (causal ? (key > qrow) : (key >= L)) sacc[j] = -INFINITY;
-      }
+      for (int j = 0; j < 16; ++j)
+        if (8 * (j >> 2) + (j & 3) > r) sacc[j] = -INFINITY;
     }
     f32x16 x;
 #pragma unroll

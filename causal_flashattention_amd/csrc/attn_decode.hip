@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(
   const int g = (r % HB) / n_hb, hb = (r % HB) % n_hb;
   int s0, L, t, b;
   if (!decode_item(plan, p, DEC_CHUNK, false, s0, L, t, &b)) return;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), half = lane >> 5;
   const int G = hq / hkv;
   const int col = lane & 31;                            // query column: head g·G + 32·hb + col
   const bool col_ok = 32 * hb + col < G;

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW) void attn_fwd_bf16_
     Lk = kd.y;
   }
   const int off = CROSS ? Lk - L : 0;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = hq / hkv;
   const int h = hb * HPW + (w % HPW);
   const int g = h / G;
@@ -172,14 +172,16 @@ __global__ __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW) void attn_fwd_bf16_
       // document end.
       const bool need_mask = causal ? (k0 + C::BN - 1 > wr0 + off) : (k0 + C::BN > Lk);
       if (need_mask) {
+        // keys above lim are masked; element j of block b holds key k0 + 32b + 4·half + c_j,
+        // c_j = 8(j/4) + j%4, so one compare of the constant c_j per element
+        const int lim = causal ? qrow + off : Lk - 1;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 2; ++b) {
+          const int r = lim - (k0 + 32 * b + 4 * half);
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = k0 + 32 * b + 8 * (j >> 2) + 4 * half + (j & 3);
-            const bool masked = causal ? (key > qrow + off) : (key >= Lk);
-            if (masked) sacc[b][j] = -INFINITY;
-          }
+          for (int j = 0; j < 16; ++j)
+            if (8 * (j >> 2) + (j & 3) > r) sacc[b][j] = -INFINITY;
+        }
       }
       float mt = -INFINITY;
 #pragma unroll

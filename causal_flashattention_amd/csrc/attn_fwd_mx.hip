@@ -8,8 +8,9 @@
 //    32 channels (a scale never mixes tokens), on every tile, through
 //    v_mfma_scale_f32_32x32x64_f8f6f4. The backward reuses the very same Q_d/K_d bytes.
 //  * O += P V contracts over keys. Off the diagonal, V_t carries one scale per channel and
-//    32 doc-local keys, and P̃ (in [0, 1] after the running-max shift) is encoded E4M3 with the
-//    fixed scale 2^-8 (P̃·2^8 <= 256 < 448; the 2^8 is folded into the exponent). On the
+//    32 doc-local keys, and P̃ (at most 2^0.8 after the lazily moved running-max shift) is
+//    encoded E4M3 with the fixed scale 2^-8 (P̃·2^8 <= 445.7 < 448; the 2^8 is folded into the
+//    exponent). On the
 //    diagonal 128×128 tile of each document the token blocks would share a scale between a
 //    query and keys after it, so there P and V stay bf16 and use v_mfma_f32_32x32x16_bf16.
 // Work list, online softmax, Sᵀ orientation and the two static LDS buffers filled by direct
@@ -30,11 +31,13 @@
 
 namespace cfa {
 
-// The running maximum moves as soon as a tile's maximum exceeds it (threshold 0, log2 units),
-// so P̃ <= 1 and P̃·2^8 fits E4M3 with 2^-8 as its fixed scale; a larger threshold would push
-// typical probabilities into E4M3's subnormal range. Only the rescaling of O is skipped when
-// no lane's maximum grew.
-constexpr float RESCALE_LOG2_MX = 0.f;
+// The running maximum moves only when a tile's maximum exceeds it by more than 0.8 (log2
+// units), so P̃ <= 2^0.8 = 1.741 and P̃·2^8 <= 445.7 still fits E4M3 (max 448) with the same
+// fixed scale 2^-8: small probabilities keep exactly the range they have with threshold 0,
+// while the rescaling of O (64 multiplies per lane) runs on far fewer tiles. A larger
+// threshold would need a smaller fixed scale and push small probabilities into E4M3's
+// subnormal range.
+constexpr float RESCALE_LOG2_MX = 0.8f;
 
 template <bool FP4>
 struct MxFwdTile {
@@ -66,7 +69,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
   if (!decode_item(plan, p, BMW, true, s0, L, t, &doc)) return;
   const int pcol = padoff[doc];                 // first token-blocked column of the document
   const int lp = 32 * ((L + 31) / 32);          // padded document length (columns)
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5, r32 = lane & 31;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), half = lane >> 5, r32 = lane & 31;
   const int G = hq / hkv;
   const int h = hb * HPW + (w % HPW);
   const int g = h / G;
@@ -180,13 +183,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
       // exponent, masks only on tiles crossing the diagonal or the document end (wave-uniform)
       const bool need_mask = causal ? (k0 + C::BN - 1 > wr0) : (k0 + C::BN > L);
       if (need_mask) {
+        const int lim = causal ? qrow : L - 1;      // keys above lim are masked (see attn_fwd.hip)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 2; ++b) {
+          const int r = lim - (k0 + 32 * b + 4 * half);
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = k0 + 32 * b + 8 * (j >> 2) + 4 * half + (j & 3);
-            if (causal ? (key > qrow) : (key >= L)) sacc[b][j] = -INFINITY;
-          }
+          for (int j = 0; j < 16; ++j)
+            if (8 * (j >> 2) + (j & 3) > r) sacc[b][j] = -INFINITY;
+        }
       }
       float mt = -INFINITY;
 #pragma unroll

@@ -64,13 +64,15 @@ __device__ inline bool decode_item(const Plan& pl, int p, int tile_rows, bool ex
     int mid = (lo + hi + 1) >> 1;
     if (pl.pref[mid] <= p) lo = mid; else hi = mid - 1;
   }
-  const int doc = pl.order[lo];
+  // every value here is the same in all lanes (p is per workgroup); readfirstlane tells the
+  // compiler so, which keeps the work-item arithmetic and everything derived from it scalar
+  const int doc = __builtin_amdgcn_readfirstlane(pl.order[lo]);
   if (doc_out) *doc_out = doc;
   const int2 di = pl.docinfo[doc];
-  s0 = di.x;
-  L = di.y;
+  s0 = __builtin_amdgcn_readfirstlane(di.x);
+  L = __builtin_amdgcn_readfirstlane(di.y);
   const int nt = (L + tile_rows - 1) / tile_rows;
-  const int j = p - pl.pref[lo];
+  const int j = p - __builtin_amdgcn_readfirstlane(pl.pref[lo]);
   tile = expensive_first ? (nt - 1 - j) : j;
   return true;
 }
