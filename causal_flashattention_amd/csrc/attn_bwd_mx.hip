@@ -34,11 +34,17 @@ __device__ inline i32x4 encode16(const f32x16& x, int e) {
   return r;
 }
 
-__device__ inline float amax16(const f32x16& x) {
-  float m = 0.f;
+// Largest of 16 non-negative values (probabilities): two v_max3 chains, then their maximum.
+__device__ inline float max16_nonneg(const f32x16& x) {
+  float m[2];
 #pragma unroll
-  for (int j = 0; j < 16; j += 2) m = fmaxf(m, fmaxf(fabsf(x[j]), fabsf(x[j + 1])));   // v_max3 with |.|
-  return m;
+  for (int k = 0; k < 2; ++k) {
+    m[k] = fmaxf(fmaxf(x[8 * k], x[8 * k + 1]), x[8 * k + 2]);
+    m[k] = fmaxf(fmaxf(m[k], x[8 * k + 3]), x[8 * k + 4]);
+    m[k] = fmaxf(fmaxf(m[k], x[8 * k + 5]), x[8 * k + 6]);
+    m[k] = fmaxf(m[k], x[8 * k + 7]);
+  }
+  return fmaxf(m[0], m[1]);
 }
 
 // Block exponent for values quantised inside the kernel (P): the smallest e with
@@ -255,7 +261,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
       xw[(pair * 4 + 2 * qb) * 64 + lane] = pw[2 * qb];
       xw[(pair * 4 + 2 * qb + 1) * 64 + lane] = pw[2 * qb + 1];
       if (!diag) {                              // MX block of 32 queries: exponent over the lane pair
-        float a = amax16(x);
+        float a = max16_nonneg(x);
         a = wave_max_xor32(a);
         const int e = fit_exp(a);
         const i32x4 c = encode16(x, e);

@@ -183,12 +183,7 @@ __global__ __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW) void attn_fwd_bf16_
             if (8 * (j >> 2) + (j & 3) > r) sacc[b][j] = -INFINITY;
         }
       }
-      float mt = -INFINITY;
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) mt = fmaxf(mt, fmaxf(sacc[b][j], sacc[b][j + 1]));
-      mt = wave_max_xor32(mt) * scale_log2;
+      const float mt = wave_max_xor32(max32(sacc[0], sacc[1])) * scale_log2;
       // Lazy rescaling: the reference maximum only moves when the tile's maximum exceeds it
       // by more than RESCALE_LOG2 (then P <= 2^RESCALE_LOG2, harmless in fp32 / bf16); LSE and
       // O are exact for any reference value.
@@ -202,7 +197,7 @@ __global__ __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW) void attn_fwd_bf16_
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
       }
-      float ls = 0.f;
+      float ls4[4] = {0.f, 0.f, 0.f, 0.f};          // four partial row sums (short add chains)
       bf16x8 pf[4];
       const float m_use = (CROSS && m_run == -INFINITY) ? 0.f : m_run;   // all -inf scores -> p = 0
 #pragma unroll
@@ -211,13 +206,13 @@ __global__ __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW) void attn_fwd_bf16_
         for (int j = 0; j < 16; j += 2) {
           const float p0 = exp2_fast(fmaf(sacc[b][j], scale_log2, -m_use));
           const float p1 = exp2_fast(fmaf(sacc[b][j + 1], scale_log2, -m_use));
-          ls += p0 + p1;
+          ls4[(j >> 1) & 3] += p0 + p1;
           const uint32_t pk = pack_bf16x2(p0, p1);
           i32x4 u = __builtin_bit_cast(i32x4, pf[2 * b + (j >> 3)]);
           u[(j & 7) >> 1] = (int)pk;
           pf[2 * b + (j >> 3)] = __builtin_bit_cast(bf16x8, u);
         }
-      l_run += ls;
+      l_run += (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
       // ---- Oᵀ += Vᵀ Pᵀ; Vᵀ fragments via transposing LDS reads
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {

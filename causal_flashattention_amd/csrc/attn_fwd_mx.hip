@@ -192,12 +192,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
             if (8 * (j >> 2) + (j & 3) > r) sacc[b][j] = -INFINITY;
         }
       }
-      float mt = -INFINITY;
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) mt = fmaxf(mt, fmaxf(sacc[b][j], sacc[b][j + 1]));
-      mt = wave_max_xor32(mt) * scale_log2;
+      const float mt = wave_max_xor32(max32(sacc[0], sacc[1])) * scale_log2;
       const bool upd = mt > m_run + RESCALE_LOG2_MX;
       if (__any(upd)) {
         const float m_new = upd ? mt : m_run;
@@ -210,15 +205,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
       const bool diag = tile_is_diag(kt);
       // diagonal tiles: P̃ (bf16); other tiles: P̃·2^8 (E4M3 with scale 2^-8)
       const float bias = diag ? -m_run : 8.f - m_run;
-      float ls = 0.f;
+      float ls4[4] = {0.f, 0.f, 0.f, 0.f};          // four partial row sums (short add chains)
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const float pj = exp2_fast(fmaf(sacc[b][j], scale_log2, bias));
           sacc[b][j] = pj;
-          ls += pj;
+          ls4[j & 3] += pj;
         }
+      const float ls = (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
       l_run += diag ? ls : ls * (1.f / 256.f);
       if (diag) {
         bf16x8 pf[4];

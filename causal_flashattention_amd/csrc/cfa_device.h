@@ -120,8 +120,10 @@ __device__ inline f32x16 mfma32_mx_fp4(i32x8 a, int sa, i32x8 b, int sb, f32x16 
 __device__ inline i32x8 fp4_operand(i32x4 u) { return i32x8{u.x, u.y, u.z, u.w, 0, 0, 0, 0}; }
 
 // Four floats -> four E4M3 bytes (round to nearest even; inputs must already lie in ±448).
+// The first conversion writes bytes 0-1 and keeps bytes 2-3 of its `old` operand, which the
+// second one overwrites: any register will do, and b's (usually dead afterwards) saves a move.
 __device__ inline int pack_fp8x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, b), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
@@ -130,7 +132,8 @@ typedef __attribute__((ext_vector_type(2))) short i16x2;
 // Four floats -> four E4M3 bytes of x / s for a power of two s, in two v_cvt_scalef32_pk_fp8_f32
 // (round to nearest even, no saturation: callers keep |x / s| <= 448).
 __device__ inline int pack_fp8x4_scaled(float a, float b, float c, float d, float s) {
-  i16x2 w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2{0, 0}, a, b, s, false);
+  // `old` as in pack_fp8x4: its bytes 2-3 are overwritten by the second conversion
+  i16x2 w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(i16x2, b), a, b, s, false);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, s, true);
   return __builtin_bit_cast(int, w);
 }
@@ -263,6 +266,20 @@ __device__ inline bf16x8 as_bf16x8(const i32x4& u) { return __builtin_bit_cast(b
 // 2^x with the bare v_exp_f32: results below 2^-126 may flush to zero, which is negligible in
 // every use here (probabilities and rescale factors next to a row sum of at least 1).
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Maximum of the 32 values of two 16-element accumulators: four independent v_max3 chains of
+// 8 values (short dependency chains), then their maximum. Exact, so the order does not matter.
+__device__ inline float max32(const f32x16& a, const f32x16& b) {
+  float m[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    m[k] = fmaxf(fmaxf(a[4 * k], a[4 * k + 1]), a[4 * k + 2]);
+    m[k] = fmaxf(fmaxf(m[k], a[4 * k + 3]), b[4 * k]);
+    m[k] = fmaxf(fmaxf(m[k], b[4 * k + 1]), b[4 * k + 2]);
+    m[k] = fmaxf(m[k], b[4 * k + 3]);
+  }
+  return fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
+}
 
 // Reductions over the lane pair (l, l ^ 32) with one v_permlane32_swap (no LDS round trip).
 // With x in both operands, the first result holds, in the upper half-wave, the lower half's
