@@ -1,4 +1,4 @@
-"""Reference MX (microscaling) quantiser: FP8 E4M3 (or FP4 E2M1) elements with one E8M0 scale per 32.
+"""Reference MX (microscaling) quantiser: FP8 E4M3 (or FP4 E2M1, FP6 E2M3) elements with one E8M0 scale per 32.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
@@ -161,6 +161,90 @@ def dequantize_d_fp4(codes, scales):
     """Values of d-blocked E2M1 codes [T, h, d] (unpacked) with scales [T, h, d/32]."""
     T, h, d = codes.shape
     v = e2m1_decode(codes).reshape(T, h, d // BLOCK, BLOCK) * e8m0_decode(scales)[..., None]
+    return v.reshape(T, h, d)
+
+
+# ---------------------------------------------------------------- E2M3 (MXFP6) elements
+# E2M3: 1 sign, 2 exponent (bias 1), 3 mantissa bits; no infinities or NaN. Exponent field 0
+# is subnormal (m/8); field E >= 1 gives (1 + m/8)·2^(E-1): 0 .. 0.875 and 1 .. 1.875 in steps
+# of 1/8, 2 .. 3.75 in steps of 1/4, 4 .. 7.5 in steps of 1/2. Same block rule as the other
+# element types with the format's own top exponent: e = floor(log2 amax) - 2 (2 is the
+# exponent of 4, the largest E2M3 power of two), elements x·2^-e saturated to ±7.5 and rounded
+# to the nearest E2M3 value, ties to the even code. A block holding a NaN or an infinity gets
+# scale byte 0xFF and codes 0.
+E2M3_MAX = 7.5
+E2M3_EMAX = 2
+
+
+def e2m3_decode(codes):
+    """Value of each 6-bit E2M3 code (float64); bit 5 is the sign."""
+    c = np.asarray(codes, dtype=np.int64)
+    E, m = (c >> 3) & 3, c & 7
+    mag = np.where(E == 0, m / 8.0, (1.0 + m / 8.0) * np.ldexp(1.0, E - 1))
+    return np.where(c & 32, -mag, mag)
+
+
+E2M3_VALUES = e2m3_decode(np.arange(32))
+
+
+def _e2m3_encode_scaled(y):
+    """Round already-scaled, finite values y (|y| <= 7.5) to E2M3 codes, RNE, sign kept."""
+    a = np.abs(np.asarray(y, dtype=np.float64))
+    d = np.abs(a[..., None] - E2M3_VALUES)
+    best = np.argmin(d, axis=-1)
+    dmin = np.take_along_axis(d, best[..., None], axis=-1)[..., 0]
+    nxt = np.minimum(best + 1, 31)
+    tie_up = (best + 1 <= 31) & (np.abs(a - E2M3_VALUES[nxt]) == dmin)
+    best = np.where(tie_up & (best % 2 == 1), best + 1, best)
+    return (best | np.where(np.signbit(y), 32, 0)).astype(np.int64)
+
+
+def quantize_blocks_fp6(x):
+    """Quantise rows of 32 values to E2M3 codes (one int per element, 0..63) and E8M0 scale bytes."""
+    x = np.asarray(x, dtype=np.float64)
+    finite = np.all(np.isfinite(x), axis=-1)
+    xs = np.where(np.isfinite(x), x, 0.0)
+    amax = np.max(np.abs(xs), axis=-1)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    e = np.clip(ex - 1 - E2M3_EMAX, -127, 127)
+    e = np.where(amax > 0, e, -127)
+    y = np.clip(np.ldexp(xs, -e[..., None]), -E2M3_MAX, E2M3_MAX)
+    codes = np.where(finite[..., None], _e2m3_encode_scaled(y), 0)
+    scales = np.where(finite, e + 127, 0xFF)
+    return codes.astype(np.uint8), scales.astype(np.uint8)
+
+
+def quantize_d_fp6(x):
+    """Blocks of 32 channels: x [T, h, d] -> E2M3 codes [T, h, d] (0..63), scales [T, h, d/32]."""
+    x = np.asarray(x, dtype=np.float64)
+    T, h, d = x.shape
+    assert d % BLOCK == 0
+    codes, scales = quantize_blocks_fp6(x.reshape(T, h, d // BLOCK, BLOCK))
+    return codes.reshape(T, h, d), scales
+
+
+def pack_fp6(codes):
+    """Storage layout of E2M3 codes [..., d] (d a multiple of 32) -> [..., 3d/4] uint8.
+
+    Block b (channels 32b .. 32b+31) is the 192-bit little-endian number whose bits 6i .. 6i+5
+    hold code i; its bytes 0-15 go to [16b, 16b+16) and bytes 16-23 to [d/2 + 8b, d/2 + 8b + 8)
+    of the row (a 16-byte part per block, then an 8-byte part per block).
+    """
+    c = np.asarray(codes, dtype=np.uint8)
+    d = c.shape[-1]
+    nb = d // BLOCK
+    blocks = c.reshape(c.shape[:-1] + (nb, BLOCK))
+    bits = (blocks[..., None] >> np.arange(6, dtype=np.uint8)) & 1          # [..., nb, 32, 6]
+    by = np.packbits(bits.reshape(bits.shape[:-2] + (192,)).reshape(bits.shape[:-2] + (24, 8)),
+                     axis=-1, bitorder="little")[..., 0]                    # [..., nb, 24]
+    return np.concatenate([by[..., :16].reshape(c.shape[:-1] + (16 * nb,)),
+                           by[..., 16:].reshape(c.shape[:-1] + (8 * nb,))], axis=-1)
+
+
+def dequantize_d_fp6(codes, scales):
+    """Values of d-blocked E2M3 codes [T, h, d] (unpacked) with scales [T, h, d/32]."""
+    T, h, d = codes.shape
+    v = e2m3_decode(codes).reshape(T, h, d // BLOCK, BLOCK) * e8m0_decode(scales)[..., None]
     return v.reshape(T, h, d)
 
 
