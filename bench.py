@@ -19,9 +19,9 @@ null when the kernel source changed since they were taken.
 ``cpu_baseline`` times the float64 oracle (naive two-pass attention with an explicit mask)
 on a bounded sample of the same workload on the host cores, and reports its causal FLOP rate.
 
-The same line carries the MX paths on the 65K-token packed workload: ``mxfp8`` (E4M3 operands)
-and ``mxfp4`` (E2M1 score product, the rest as mxfp8), each with its own ``roofline``; peaks of
-mixed-format kernels are n / Σ 1/peak over their counted GEMM units.
+The same line carries the MX paths on the 65K-token packed workload: ``mxfp8`` (E4M3 operands),
+``mxfp4`` and ``mxfp6`` (E2M1 / E2M3 score product, the rest as mxfp8), each with its own
+``roofline``; peaks of mixed-format kernels are n / Σ 1/peak over their counted GEMM units.
 
     python bench.py --decode      # decoding over a packed KV cache: GB/s against HBM peak
 """
@@ -38,7 +38,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0, "fp32": 157.3}   # MI355X dense MFMA / vector fp32
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp6": 10100.0, "fp4": 10100.0, "fp32": 157.3}   # MI355X dense MFMA / vector fp32
 # Counted GEMM units per MX kernel and the format each runs in ("qk": the score product, E4M3 on
 # the MXFP8 path and E2M1 on the MXFP4/FP8 path). A mixed kernel's peak is the rate at which its
 # counted units would run if each ran at its format's peak: n / Σ 1/peak.
@@ -93,6 +93,8 @@ def parse():
                     help="MXFP8 workload reported under 'mxfp8' (0 = skip)")
     ap.add_argument("--mx4-workload", type=int, default=4, choices=[0, 4, 5],
                     help="MXFP4/FP8 workload reported under 'mxfp4' (0 = skip)")
+    ap.add_argument("--mx6-workload", type=int, default=4, choices=[0, 4, 5],
+                    help="MXFP6/FP8 workload reported under 'mxfp6' (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 3 times (to scale the "
@@ -170,8 +172,8 @@ def measure(w, mx, steps, warmup):
     cu = torch.from_numpy(w.cu_seqlens).to(dev)
     cu_h = torch.from_numpy(w.cu_seqlens)
     T, hq, hkv, d = w.total_tokens, w.hq, w.hkv, w.d
-    dt = cfa.CFA_MXFP4 if mx == "mxfp4" else (cfa.CFA_MXFP8 if mx else cfa.CFA_BF16)
-    qk_fmt = "fp4" if mx == "mxfp4" else "fp8"
+    dt = {"mxfp4": cfa.CFA_MXFP4, "mxfp6": cfa.CFA_MXFP6}.get(mx, cfa.CFA_MXFP8 if mx else cfa.CFA_BF16)
+    qk_fmt = {"mxfp4": "fp4", "mxfp6": "fp6"}.get(mx, "fp8")
     o = torch.empty_like(q)
     lse = torch.empty((hq, T), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -238,7 +240,7 @@ def measure(w, mx, steps, warmup):
     achieved = dom_flops / (kern[dom]["ms"] * 1e-3) / 1e12
     roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": dom_peak, "unit": "TFLOP/s",
             "frac": achieved / dom_peak,
-            "traffic": traffic_for(dom, w.name.replace("mxfp8", "mxfp4") if mx == "mxfp4" else w.name),
+            "traffic": traffic_for(dom, w.name.replace("mxfp8", mx) if mx in ("mxfp4", "mxfp6") else w.name),
             "algorithmic_flop_per_launch": dom_flops, "mean_launch_ms": kern[dom]["ms"]}
     res = {"value": value, "ms_per_step": elapsed / K * 1e3, "pct_of_peak": 100.0 * value / peak, "peak": peak,
            "config": {"workload": w.name, "total_tokens": T, "n_docs": w.n_docs, "hq": hq, "hkv": hkv, "d": d,
@@ -376,6 +378,13 @@ def main():
         mres["unit"] = "TFLOP/s"
         mres["peak_note"] = "peaks are n / sum(1/peak) over the counted GEMM units (fp4 10.1, fp8 5.0 PFLOP/s)"
         out["mxfp4"] = mres
+    if args.mx6_workload:
+        wm = W.make_workload(args.mx6_workload)
+        mres = measure(wm, "mxfp6", args.steps, args.warmup)
+        mres["dtype"] = "mxfp6/fp8 (QK^T on E2M3 + E8M0 per 32, the rest as mxfp8)"
+        mres["unit"] = "TFLOP/s"
+        mres["peak_note"] = "peaks are n / sum(1/peak) over the counted GEMM units (fp6 10.1, fp8 5.0 PFLOP/s)"
+        out["mxfp6"] = mres
     print(json.dumps(out))
 
 

@@ -88,9 +88,11 @@ struct MxDkdvTile {
   static constexpr int XP = 4 * 4 * 64;              // exchange: i32x4 [pair][2·qb + u][lane]
 };
 
-// FP4 = true (MXFP4/FP8 path): the P wave's score product takes E2M1 Q_d rows (64 bytes, swizzled
-// with (row / 4) % 4) and E2M1 K_d registers; everything else is unchanged.
-template <bool FP4>
+// QF = 1 (MXFP4/FP8 path): the P wave's score product takes E2M1 Q_d rows (64 bytes, swizzled
+// with (row / 4) % 4) and E2M1 K_d registers; QF = 2 (MXFP6/FP8): E2M3 rows, whose 16-byte parts
+// are staged like the E2M1 rows and whose 8-byte parts follow chunk-major (two 16-byte chunks
+// per row); everything else is unchanged.
+template <int QF>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
     const uint8_t* __restrict__ qd, const uint8_t* __restrict__ qd_sc, const uint8_t* __restrict__ kd,
     const uint8_t* __restrict__ kd_sc, const uint8_t* __restrict__ dod, const uint8_t* __restrict__ dod_sc,
@@ -128,7 +130,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
   for (int u = 0; u < 2; ++u) to[u] = 16 * ((2 * u + half) ^ vt_swz(r32));
 #pragma unroll
   for (int s = 0; s < 2; ++s) kq[s] = 16 * ((2 * s + half) ^ vt_swz(r32));
-  const bool fp4_role = FP4 && !ds_wave;          // this wave's score operands are E2M1
+  constexpr bool FP4 = QF == 1, FP6 = QF == 2;
+  constexpr int QROW = FP4 ? 64 : FP6 ? 96 : 128;  // bytes of one Q_d / K_d row in HBM
+  const bool narrow_role = QF != 0 && !ds_wave;    // this wave's score operands are E2M1 / E2M3
 
   // B operand rows of key mykey: K_d (P wave) or V_d (dS wave)
   i32x8 kvb[2];
@@ -140,8 +144,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
     const size_t row = (size_t)(s0 + (ok ? mykey : 0)) * hkv + g;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      if (fp4_role)
+      if (FP4 && narrow_role)
         kvb[s] = ok ? fp4_operand(*(const i32x4*)(kd + row * (D / 2) + 32 * s + 16 * half)) : i32x8{};
+      else if (FP6 && narrow_role)
+        kvb[s] = ok ? fp6_operand(*(const i32x4*)(kd + row * QROW + 16 * (2 * s + half)),
+                                  *(const i32x2*)(kd + row * QROW + D / 2 + 8 * (2 * s + half)))
+                    : i32x8{};
       else
         kvb[s] = ok ? load_a_fp8((const char*)(src + row * D + 64 * s), half) : i32x8{};
       kvs[s] = ok ? ssrc[row * 4 + 2 * s + half] : 127;
@@ -170,10 +178,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
     const int rmax = L - 1 - q0;
     const size_t tok0 = (size_t)(s0 + q0) * hq + h;
     const uint32_t tok_b = (uint32_t)hq * D;
-    if (fp4_role) {                             // E2M1 Q_d codes: 4 blocks of 16 rows of 64 B
-      const uint8_t* dsrc = qd + tok0 * (D / 2);
+    if (narrow_role) {                          // E2M1 / E2M3 Q_d codes: 4 blocks of 16 rows of 64 B
+      const uint8_t* dsrc = qd + tok0 * QROW;
+      const uint32_t rs = (uint32_t)hq * QROW;
       const int r = 16 * pair + (lane >> 2);
-      g2lds16(dsrc + ((uint32_t)min(r, rmax) * (tok_b / 2) + 16 * ((lane & 3) ^ vt_swz(r))), buf + pair * 1024);
+      g2lds16(dsrc + ((uint32_t)min(r, rmax) * rs + 16 * ((lane & 3) ^ vt_swz(r))), buf + pair * 1024);
+      if (FP6 && pair < 2)                      // E2M3 8-byte parts: chunk `pair` of every row
+        g2lds16(dsrc + ((uint32_t)min(lane, rmax) * rs + D / 2 + 16 * pair), buf + 4096 + pair * 1024);
     } else {
       const uint8_t* dsrc = (ds_wave ? dod : qd) + tok0 * D;
 #pragma unroll
@@ -210,12 +221,18 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
     const int qr = 32 * qb + r32;
     const int sc = *(const int*)(buf + C::OFF_SC + qr * 4);
     f32x16 a = f32x16{};
-    if (fp4_role) {
+    if (FP4 && narrow_role) {
       const char* rp = buf + qr * (D / 2);
 #pragma unroll
       for (int s = 0; s < 2; ++s)
         a = mfma32_mx_fp4(fp4_operand(*(const i32x4*)(rp + kq[s])), (sc >> (8 * (2 * s + half))) & 0xFF, kvb[s],
                           kvs[s], a);
+    } else if (FP6 && narrow_role) {
+      const char* rp = buf + qr * (D / 2);
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        a = mfma32_mx_fp6(fp6_operand(*(const i32x4*)(rp + kq[s]), *(const i32x2*)(buf + 4096 + 16 * (64 * s + qr) + 8 * half)),
+                          (sc >> (8 * (2 * s + half))) & 0xFF, kvb[s], kvs[s], a);
     } else {
       const char* rp = buf + qr * 128;
 #pragma unroll
@@ -401,9 +418,9 @@ struct MxDqTile {
   static constexpr int STAGE = OFF_U + BN * 256;
 };
 
-// FP4 = true: the score product takes E2M1 K_d rows (64 bytes, swizzled with (row / 4) % 4) and E2M1
-// Q_d registers.
-template <bool FP4>
+// QF = 1: the score product takes E2M1 K_d rows (64 bytes, swizzled with (row / 4) % 4) and E2M1
+// Q_d registers; QF = 2: E2M3 rows, their 8-byte parts chunk-major after the 16-byte parts.
+template <int QF>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
     const uint8_t* __restrict__ qd, const uint8_t* __restrict__ qd_sc, const uint8_t* __restrict__ kd,
     const uint8_t* __restrict__ kd_sc, const uint8_t* __restrict__ dod, const uint8_t* __restrict__ dod_sc,
@@ -412,6 +429,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
     int total_tokens, int hq, int hkv, float scale, int causal) {
   using C = MxDqTile;
   constexpr int D = 128, BN = C::BN;
+  constexpr bool FP4 = QF == 1, FP6 = QF == 2;
+  constexpr int QROW = FP4 ? 64 : FP6 ? 96 : 128;  // bytes of one Q_d / K_d row in HBM
   __shared__ __attribute__((aligned(16))) char lds_a[C::STAGE];
   __shared__ __attribute__((aligned(16))) char lds_b[C::STAGE];
 
@@ -445,6 +464,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
     for (int s = 0; s < 2; ++s) {
       if constexpr (FP4)
         qa[s] = ok ? fp4_operand(*(const i32x4*)(qd + row * (D / 2) + 32 * s + 16 * half)) : i32x8{};
+      else if constexpr (FP6)
+        qa[s] = ok ? fp6_operand(*(const i32x4*)(qd + row * QROW + 16 * (2 * s + half)),
+                                 *(const i32x2*)(qd + row * QROW + D / 2 + 8 * (2 * s + half)))
+                   : i32x8{};
       else
         qa[s] = ok ? load_a_fp8((const char*)(qd + row * D + 64 * s), half) : i32x8{};
       oa[s] = ok ? load_a_fp8((const char*)(dod + row * D + 64 * s), half) : i32x8{};
@@ -473,13 +496,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
     for (int j = 0; j < 2; ++j) {               // K_d and V_d codes: 8 blocks of 8 rows each
       const int I = 2 * w + j, r = 8 * I + (lane >> 3);
       const uint32_t off = (uint32_t)min(r, rmax) * krow_b + 16 * ((lane & 7) ^ kd_swz(r));
-      if constexpr (!FP4) g2lds16(kdb + off, tb + I * 1024);
+      if constexpr (QF == 0) g2lds16(kdb + off, tb + I * 1024);
       g2lds16(vdb + off, tb + C::OFF_VD + I * 1024);
     }
-    if constexpr (FP4) {                        // E2M1 K_d codes: 4 blocks of 16 rows of 64 B
+    if constexpr (QF != 0) {                    // E2M1 / E2M3 K_d codes: 4 blocks of 16 rows of 64 B
+      const uint32_t rs = (uint32_t)hkv * QROW;
       const int r = 16 * w + (lane >> 2);
-      g2lds16(kd + tok0 * (D / 2) + ((uint32_t)min(r, rmax) * (krow_b / 2) + 16 * ((lane & 3) ^ vt_swz(r))),
-              tb + w * 1024);
+      g2lds16(kd + tok0 * QROW + ((uint32_t)min(r, rmax) * rs + 16 * ((lane & 3) ^ vt_swz(r))), tb + w * 1024);
+      if (FP6 && w < 2)                         // E2M3 8-byte parts: chunk w of every row
+        g2lds16(kd + tok0 * QROW + ((uint32_t)min(lane, rmax) * rs + D / 2 + 16 * w), tb + 4096 + w * 1024);
     }
     const uint32_t soff = (uint32_t)min(lane, rmax) * (uint32_t)hkv * 4;
     if (w == 0) g2lds4(kd_sc + tok0 * 4 + soff, tb + C::OFF_KDSC);
@@ -499,6 +524,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
       const i32x4 vlo = *(const i32x4*)(vp + ko[s][0]), vhi = *(const i32x4*)(vp + ko[s][1]);
       if constexpr (FP4) {
         sacc = mfma32_mx_fp4(fp4_operand(*(const i32x4*)(tb + kr * (D / 2) + kq[s])),
+                             (ksc >> (8 * (2 * s + half))) & 0xFF, qa[s], qs[s], sacc);
+      } else if constexpr (FP6) {
+        sacc = mfma32_mx_fp6(fp6_operand(*(const i32x4*)(tb + kr * (D / 2) + kq[s]),
+                                         *(const i32x2*)(tb + 4096 + 16 * (64 * s + kr) + 8 * half)),
                              (ksc >> (8 * (2 * s + half))) & 0xFF, qa[s], qs[s], sacc);
       } else {
         const char* kp = tb + kr * 128;
@@ -586,13 +615,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
 hipError_t launch_bwd_dkdv_mx(const MxOperands& m, const void* q, const void* dout, const float* lse,
                               const float* delta, void* dk, void* dv, const Plan& plan_any, const int* pref_base,
                               const int* padoff, int T, int t_pad, int hq, int hkv, float scale, int causal,
-                              bool fp4, hipStream_t stream) {
+                              int qf, hipStream_t stream) {
   Plan plan = plan_any;
   plan.pref = pref_base + pref_slot(128) * (plan.n_docs + 1);
   const long grid = ((long)(T + 127) / 128 + plan.n_docs) * hkv;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  auto kern = fp4 ? attn_bwd_dkdv_mx_kernel<true> : attn_bwd_dkdv_mx_kernel<false>;
+  auto kern = qf == 1 ? attn_bwd_dkdv_mx_kernel<1> : qf == 2 ? attn_bwd_dkdv_mx_kernel<2> : attn_bwd_dkdv_mx_kernel<0>;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), 0, stream, m.qd, m.qd_sc, m.kd, m.kd_sc, m.dod, m.dod_sc,
                      m.vd, m.vd_sc, m.dot, m.dot_sc, (const __bf16*)q, (const __bf16*)dout, lse, delta,
                      (__bf16*)dk, (__bf16*)dv, plan, padoff, T, t_pad, hq, hkv, scale, causal);
@@ -601,13 +630,13 @@ hipError_t launch_bwd_dkdv_mx(const MxOperands& m, const void* q, const void* do
 
 hipError_t launch_bwd_dq_mx(const MxOperands& m, const void* k, const float* lse, const float* delta, void* dq,
                             const Plan& plan_any, const int* pref_base, int T, int hq, int hkv, float scale,
-                            int causal, bool fp4, hipStream_t stream) {
+                            int causal, int qf, hipStream_t stream) {
   Plan plan = plan_any;
   plan.pref = pref_base + pref_slot(128) * (plan.n_docs + 1);
   const long grid = ((long)(T + 127) / 128 + plan.n_docs) * hq;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  auto kern = fp4 ? attn_bwd_dq_mx_kernel<true> : attn_bwd_dq_mx_kernel<false>;
+  auto kern = qf == 1 ? attn_bwd_dq_mx_kernel<1> : qf == 2 ? attn_bwd_dq_mx_kernel<2> : attn_bwd_dq_mx_kernel<0>;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, m.qd, m.qd_sc, m.kd, m.kd_sc, m.dod, m.dod_sc,
                      m.vd, m.vd_sc, (const __bf16*)k, lse, delta, (__bf16*)dq, plan, T, hq, hkv, scale, causal);
   return hipGetLastError();

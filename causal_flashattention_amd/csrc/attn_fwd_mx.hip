@@ -16,9 +16,12 @@
 // Work list, online softmax, Sᵀ orientation and the two static LDS buffers filled by direct
 // global -> LDS copies follow the bf16 kernel in attn_fwd.hip.
 //
-// MXFP4/FP8 (FP4 = true): the score product takes E2M1 copies Q_d, K_d (two codes per byte,
+// MXFP4/FP8 (QF = 1): the score product takes E2M1 copies Q_d, K_d (two codes per byte,
 // 64-byte rows for d = 128, blocks of 32 channels with E8M0 scales) through the same
 // instruction with format code 4 on both operands; the rest is the MXFP8 path unchanged.
+// MXFP6/FP8 (QF = 2): E2M3 copies, 96-byte rows whose blocks are a 16-byte part (the first 64
+// bytes, staged and read exactly like the E2M1 rows) and an 8-byte part (the last 32 bytes,
+// staged as two 16-byte chunks per row, chunk-major), format code 2.
 //
 // LDS tile (64 keys): K_d codes as 128-byte rows whose 16-byte chunks are XOR-swizzled with
 // (row / 2) % 8 (FP4: 64-byte rows swizzled with (row / 4) % 4), then 4 scale bytes per key; then either the bf16 V rows of a diagonal tile
@@ -39,25 +42,28 @@ namespace cfa {
 // subnormal range.
 constexpr float RESCALE_LOG2_MX = 0.8f;
 
-template <bool FP4>
+template <int QF>
 struct MxFwdTile {
   static constexpr int BN = 64;
   static constexpr int D = 128;
-  static constexpr int KROW = FP4 ? D / 2 : D;       // bytes of one K_d row
-  static constexpr int OFF_KSC = BN * KROW;          // K_d codes: 64 rows
+  static constexpr int KROW = QF == 0 ? D : D / 2;   // bytes of one K_d row (E2M3: its 16-byte parts)
+  static constexpr int OFF_KB = BN * KROW;           // K_d codes: 64 rows
+  static constexpr int OFF_KSC = OFF_KB + (QF == 2 ? BN * D / 4 : 0);   // E2M3: 8-byte parts [chunk][row]
   static constexpr int OFF_V = OFF_KSC + BN * 4;     // K_d scales: 4 B per key
   static constexpr int OFF_VTSC = OFF_V + D * 64;    // V_t codes: 128 channel rows × 64 B
   static constexpr int STAGE = OFF_V + BN * 256;     // union with the bf16 V rows (64 × 256 B)
 };
 
-template <int HPW, bool FP4>
+template <int HPW, int QF>
 __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
     const uint8_t* __restrict__ qd, const uint8_t* __restrict__ qd_sc, const uint8_t* __restrict__ kd,
     const uint8_t* __restrict__ kd_sc, const uint8_t* __restrict__ vt, const uint8_t* __restrict__ vt_sc,
     const __bf16* __restrict__ v, __bf16* __restrict__ o, float* __restrict__ lse, Plan plan,
     const int* __restrict__ padoff, int total_tokens, int t_pad, int hq, int hkv, int n_hb, float scale_log2,
     int causal) {
-  using C = MxFwdTile<FP4>;
+  using C = MxFwdTile<QF>;
+  constexpr bool FP4 = QF == 1, FP6 = QF == 2, NARROW = QF != 0;
+  constexpr int QROW = FP4 ? 64 : FP6 ? 96 : 128;     // bytes of one Q_d / K_d row in HBM
   constexpr int D = C::D;
   constexpr int BMW = 128 / HPW;
   __shared__ __attribute__((aligned(16))) char lds_a[C::STAGE];
@@ -86,7 +92,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-      ko[s][u] = FP4 ? 16 * ((2 * s + half) ^ vt_swz(r32)) : 16 * ((4 * s + 2 * u + half) ^ kd_swz(r32));
+      ko[s][u] = NARROW ? 16 * ((2 * s + half) ^ vt_swz(r32)) : 16 * ((4 * s + 2 * u + half) ^ kd_swz(r32));
 #pragma unroll
   for (int u = 0; u < 2; ++u) vo[u] = 16 * ((2 * u + half) ^ vt_swz(r32));
 
@@ -100,6 +106,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
     for (int s = 0; s < 2; ++s) {
       if constexpr (FP4) {   // channels 64s + 32·half .. +31: 16 bytes
         qa[s] = fp4_operand(ok ? *(const i32x4*)(qd + row * (D / 2) + 32 * s + 16 * half) : i32x4{0, 0, 0, 0});
+      } else if constexpr (FP6) {   // block 2s + half: 16-byte and 8-byte parts
+        const uint8_t* rp = qd + row * QROW;
+        qa[s] = fp6_operand(ok ? *(const i32x4*)(rp + 16 * (2 * s + half)) : i32x4{0, 0, 0, 0},
+                            ok ? *(const i32x2*)(rp + D / 2 + 8 * (2 * s + half)) : i32x2{0, 0});
       } else {
         const i32x4 lo = ok ? *(const i32x4*)(qd + row * D + 64 * s + 16 * half) : i32x4{0, 0, 0, 0};
         const i32x4 hi = ok ? *(const i32x4*)(qd + row * D + 64 * s + 32 + 16 * half) : i32x4{0, 0, 0, 0};
@@ -122,10 +132,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
     const int k0 = kt * C::BN;
     const int rmax = kv_end - 1 - k0;
     const size_t tok0 = (size_t)(s0 + k0) * hkv + g;
-    if constexpr (FP4) {                        // K_d codes: 4 blocks of 16 rows, 1 per wave
-      const uint8_t* kdb = kd + tok0 * (D / 2);
+    if constexpr (NARROW) {                     // K_d codes: 4 blocks of 16 rows, 1 per wave
+      const uint8_t* kdb = kd + tok0 * QROW;
+      const uint32_t rs = (uint32_t)hkv * QROW;
       const int r = 16 * w + (lane >> 2);
-      g2lds16(kdb + ((uint32_t)min(r, rmax) * (tok_b / 2) + 16 * ((lane & 3) ^ vt_swz(r))), tb + w * 1024);
+      g2lds16(kdb + ((uint32_t)min(r, rmax) * rs + 16 * ((lane & 3) ^ vt_swz(r))), tb + w * 1024);
+      if (FP6 && w < 2)                         // 8-byte parts: chunk w of every row (lane = row)
+        g2lds16(kdb + ((uint32_t)min(lane, rmax) * rs + D / 2 + 16 * w), tb + C::OFF_KB + w * 1024);
     } else {
       const uint8_t* kdb = kd + tok0 * D;
 #pragma unroll
@@ -173,6 +186,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
           const int sa = (ksc[b] >> (8 * (2 * s + half))) & 0xFF;
           if constexpr (FP4) {
             sacc[b] = mfma32_mx_fp4(fp4_operand(*(const i32x4*)(kr + ko[s][0])), sa, qa[s], qs[s], sacc[b]);
+          } else if constexpr (FP6) {
+            const i32x2 hi = *(const i32x2*)(tb + C::OFF_KB + 16 * (64 * s + 32 * b + r32) + 8 * half);
+            sacc[b] = mfma32_mx_fp6(fp6_operand(*(const i32x4*)(kr + ko[s][0]), hi), sa, qa[s], qs[s], sacc[b]);
           } else {
             const i32x4 lo = *(const i32x4*)(kr + ko[s][0]);
             const i32x4 hi = *(const i32x4*)(kr + ko[s][1]);
@@ -283,7 +299,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
 hipError_t launch_fwd_mx(const uint8_t* qd, const uint8_t* qd_sc, const uint8_t* kd, const uint8_t* kd_sc,
                          const uint8_t* vt, const uint8_t* vt_sc, const void* v, void* o, float* lse,
                          const Plan& plan_any, const int* pref_base, const int* padoff, int total_tokens, int t_pad,
-                         int hq, int hkv, float scale, int causal, bool fp4, hipStream_t stream) {
+                         int hq, int hkv, float scale, int causal, int qf, hipStream_t stream) {
   const int G = hq / hkv;
   const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
   const int rows = 128 / hpw;
@@ -298,14 +314,18 @@ hipError_t launch_fwd_mx(const uint8_t* qd, const uint8_t* qd_sc, const uint8_t*
   hipLaunchKernelGGL((attn_fwd_mx_kernel<HH, F4>), dim3((unsigned)grid), dim3(256), 0, stream, qd, qd_sc, kd, kd_sc,  \
                      vt, vt_sc, (const __bf16*)v, (__bf16*)o, lse, plan, padoff, total_tokens, t_pad, hq, hkv, n_hb, sl2, \
                      causal)
-  if (fp4) {
-    if (hpw == 4) CFA_MXF_LAUNCH(4, true);
-    else if (hpw == 2) CFA_MXF_LAUNCH(2, true);
-    else CFA_MXF_LAUNCH(1, true);
+  if (qf == 1) {
+    if (hpw == 4) CFA_MXF_LAUNCH(4, 1);
+    else if (hpw == 2) CFA_MXF_LAUNCH(2, 1);
+    else CFA_MXF_LAUNCH(1, 1);
+  } else if (qf == 2) {
+    if (hpw == 4) CFA_MXF_LAUNCH(4, 2);
+    else if (hpw == 2) CFA_MXF_LAUNCH(2, 2);
+    else CFA_MXF_LAUNCH(1, 2);
   } else {
-    if (hpw == 4) CFA_MXF_LAUNCH(4, false);
-    else if (hpw == 2) CFA_MXF_LAUNCH(2, false);
-    else CFA_MXF_LAUNCH(1, false);
+    if (hpw == 4) CFA_MXF_LAUNCH(4, 0);
+    else if (hpw == 2) CFA_MXF_LAUNCH(2, 0);
+    else CFA_MXF_LAUNCH(1, 0);
   }
 #undef CFA_MXF_LAUNCH
   return hipGetLastError();

@@ -66,9 +66,10 @@ int check_sizes(const Sizes& s, bool bwd) {
   if (s.hq < 1 || s.hkv < 1) return fail(CFA_ERR_SHAPE, "hq = %d, hkv = %d must be >= 1", s.hq, s.hkv);
   if (s.hq % s.hkv) return fail(CFA_ERR_SHAPE, "hq = %d is not a multiple of hkv = %d", s.hq, s.hkv);
   if ((long)s.T * s.hq * s.d > 0x7fffffffL * 8L) return fail(CFA_ERR_SHAPE, "tensor too large");
-  if (s.dtype != CFA_F32 && s.dtype != CFA_BF16 && s.dtype != CFA_MXFP8 && s.dtype != CFA_MXFP4)
+  if (s.dtype != CFA_F32 && s.dtype != CFA_BF16 && s.dtype != CFA_MXFP8 && s.dtype != CFA_MXFP4 &&
+      s.dtype != CFA_MXFP6)
     return fail(CFA_ERR_UNSUPPORTED, "dtype %d unknown", s.dtype);
-  if (s.dtype == CFA_MXFP8 || s.dtype == CFA_MXFP4) {
+  if (s.dtype == CFA_MXFP8 || s.dtype == CFA_MXFP4 || s.dtype == CFA_MXFP6) {
     if (s.d != 128) return fail(CFA_ERR_UNSUPPORTED, "the MX paths support d = 128 only (got %d)", s.d);
   } else if (s.dtype == CFA_F32 && s.d != 64 && s.d != 128) {
     return fail(CFA_ERR_UNSUPPORTED, "the fp32 path supports d = 64 or 128 (got %d)", s.d);
@@ -86,12 +87,16 @@ struct MxBuf {
 
 int t_pad_of(const Sizes& s) { return (s.T + 31) / 32 * 32 + 32 * s.n_docs; }
 
-bool is_mx(int dtype) { return dtype == CFA_MXFP8 || dtype == CFA_MXFP4; }
+bool is_mx(int dtype) { return dtype == CFA_MXFP8 || dtype == CFA_MXFP4 || dtype == CFA_MXFP6; }
 
-// d-blocked copy of a [T, h, d] tensor: codes [T, h, d] (E2M1: [T, h, d/2]), scales [T, h, d/32]
-size_t add_mx_d(size_t off, const Sizes& s, int h, MxBuf& b, bool fp4 = false) {
+// element format of the score product's copies: 0 = E4M3, 1 = E2M1, 2 = E2M3
+int score_format(int dtype) { return dtype == CFA_MXFP4 ? 1 : dtype == CFA_MXFP6 ? 2 : 0; }
+
+// d-blocked copy of a [T, h, d] tensor: codes [T, h, d] (E2M1: [T, h, d/2]; E2M3: [T, h, 3d/4]),
+// scales [T, h, d/32]
+size_t add_mx_d(size_t off, const Sizes& s, int h, MxBuf& b, int qf = 0) {
   b.codes = off;
-  off = cfa::align256(off + (size_t)s.T * h * (fp4 ? s.d / 2 : s.d));
+  off = cfa::align256(off + (size_t)s.T * h * (qf == 1 ? s.d / 2 : qf == 2 ? 3 * s.d / 4 : s.d));
   b.scales = off;
   return cfa::align256(off + (size_t)s.T * h * (s.d / 32));
 }
@@ -145,7 +150,7 @@ WsLayout ws_layout(int pass, const Sizes& s) {
   return w;
 }
 
-// forward-to-backward buffer of the MX paths: Q_d and K_d (E4M3, or E2M1 for CFA_MXFP4)
+// forward-to-backward buffer of the MX paths: Q_d and K_d (E4M3, E2M1 for CFA_MXFP4, E2M3 for CFA_MXFP6)
 struct SavedLayout {
   MxBuf qd, kd;
   size_t total;
@@ -154,9 +159,9 @@ struct SavedLayout {
 SavedLayout saved_layout(const Sizes& s) {
   SavedLayout v{};
   size_t off = 0;
-  const bool fp4 = s.dtype == CFA_MXFP4;
-  off = add_mx_d(off, s, s.hq, v.qd, fp4);
-  off = add_mx_d(off, s, s.hkv, v.kd, fp4);
+  const int qf = score_format(s.dtype);
+  off = add_mx_d(off, s, s.hq, v.qd, qf);
+  off = add_mx_d(off, s, s.hkv, v.kd, qf);
   v.total = off;
   return v;
 }
@@ -237,8 +242,12 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, c
     const SavedLayout sl = saved_layout(s);
     const cfa::PlanLayout pl(n_docs);
     const int tp = t_pad_of(s);
-    const bool fp4 = dtype == CFA_MXFP4;
-    auto quant_d = fp4 ? cfa::launch_mx_quantize_d_fp4 : cfa::launch_mx_quantize_d;
+    const int qf = score_format(dtype);
+    auto quant_d = [&](const void* x, long n, uint8_t* c, uint8_t* sc, hipStream_t str) {
+      return qf == 1 ? cfa::launch_mx_quantize_d_fp4(x, n, c, sc, str)
+           : qf == 2 ? cfa::launch_mx_quantize_d_fp6(x, n, d, c, sc, str)
+                     : cfa::launch_mx_quantize_d(x, n, c, sc, str);
+    };
     mark(1, 0, st);
     if (int r = check_hip(quant_d(q, (long)total_tokens * hq * d, (uint8_t*)sv + sl.qd.codes,
                                   (uint8_t*)sv + sl.qd.scales, st), "quantize Q"))
@@ -254,7 +263,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, c
     e = cfa::launch_fwd_mx((const uint8_t*)sv + sl.qd.codes, (const uint8_t*)sv + sl.qd.scales,
                            (const uint8_t*)sv + sl.kd.codes, (const uint8_t*)sv + sl.kd.scales,
                            (const uint8_t*)ws + wl.vt.codes, (const uint8_t*)ws + wl.vt.scales, v, o, lse, plan,
-                           plan.pref, (const int*)(ws + pl.padoff), total_tokens, tp, hq, hkv, scale, causal, fp4, st);
+                           plan.pref, (const int*)(ws + pl.padoff), total_tokens, tp, hq, hkv, scale, causal, qf, st);
     mark(0, 1, st);
     return check_hip(e, "MX forward kernel");
   }
@@ -319,13 +328,13 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
     m.dot = U(wl.dot, true); m.dot_sc = U(wl.dot, false);
     mark(1, 0, st);
     if (int r = check_hip(cfa::launch_bwd_dkdv_mx(m, q, dout, lse, delta, dk, dv, plan, plan.pref, padoff, total_tokens,
-                                                  tp, hq, hkv, scale, causal, dtype == CFA_MXFP4, st),
+                                                  tp, hq, hkv, scale, causal, score_format(dtype), st),
                           "MX dK/dV kernel"))
       return r;
     mark(1, 1, st);
     mark(2, 0, st);
     int r = check_hip(cfa::launch_bwd_dq_mx(m, k, lse, delta, dq, plan, plan.pref, total_tokens, hq, hkv, scale,
-                                            causal, dtype == CFA_MXFP4, st),
+                                            causal, score_format(dtype), st),
                       "MX dQ kernel");
     mark(2, 1, st);
     return r;
@@ -515,6 +524,18 @@ int mx_quantize_fp4(const void* x, int total_tokens, int h, int d, uint8_t* code
   if (total_tokens == 0) return CFA_OK;
   return check_hip(cfa::launch_mx_quantize_d_fp4(x, (long)total_tokens * h * d, codes, scales, (hipStream_t)stream),
                    "mx_quantize_d_fp4");
+}
+
+int mx_quantize_fp6(const void* x, int total_tokens, int h, int d, uint8_t* codes, uint8_t* scales, void* stream) {
+  g_err[0] = 0;
+  if (total_tokens < 0 || h < 1) return fail(CFA_ERR_SHAPE, "total_tokens = %d, h = %d", total_tokens, h);
+  if (d != 64 && d != 128) return fail(CFA_ERR_UNSUPPORTED, "mx_quantize_fp6 supports d = 64 or 128 (got %d)", d);
+  if (total_tokens > 0 && (!x || !codes || !scales)) return fail(CFA_ERR_NULL, "x, codes and scales must not be NULL");
+  for (const void* p : {x, (const void*)codes})
+    if (!aligned(p, 16)) return fail(CFA_ERR_ALIGN, "x and codes must be 16-byte aligned");
+  if (total_tokens == 0) return CFA_OK;
+  return check_hip(cfa::launch_mx_quantize_d_fp6(x, (long)total_tokens * h * d, d, codes, scales, (hipStream_t)stream),
+                   "mx_quantize_d_fp6");
 }
 
 // ---------------------------------------------------------------- decoding over a KV cache

@@ -62,6 +62,9 @@ hipError_t launch_decode_combine(const float* part_o, const void* part_ml, void*
 hipError_t launch_mx_quantize_d(const void* x, long n_elems, uint8_t* codes, uint8_t* scales, hipStream_t stream);
 // E2M1 codes packed two per byte ([n_elems / 2] bytes), E8M0 scales [n_elems / 32].
 hipError_t launch_mx_quantize_d_fp4(const void* x, long n_elems, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+// E2M3 codes [n_elems/d rows][3d/4 bytes] (each block of 32 as a 16-byte and an 8-byte part)
+hipError_t launch_mx_quantize_d_fp6(const void* x, long n_elems, int d, uint8_t* codes, uint8_t* scales,
+                                    hipStream_t stream);
 
 // kernel_layout: the attention kernels' internal token-blocked layout (pieces of 4 tokens in
 // the order 0,2,4,6,1,3,5,7 within each 32-token block; scales [h, t_pad/32, d]); otherwise the
@@ -73,14 +76,14 @@ hipError_t launch_mx_quantize_t(const void* x, int total_tokens, int h, int d, c
 hipError_t launch_fwd_mx(const uint8_t* qd, const uint8_t* qd_sc, const uint8_t* kd, const uint8_t* kd_sc,
                          const uint8_t* vt, const uint8_t* vt_sc, const void* v, void* o, float* lse,
                          const Plan& plan, const int* pref_base, const int* padoff, int total_tokens, int t_pad,
-                         int hq, int hkv, float scale, int causal, bool fp4, hipStream_t stream);
+                         int hq, int hkv, float scale, int causal, int qf, hipStream_t stream);
 
 hipError_t launch_bwd_dkdv_mx(const MxOperands& m, const void* q, const void* dout, const float* lse,
                               const float* delta, void* dk, void* dv, const Plan& plan, const int* pref_base,
-                              const int* padoff, int T, int t_pad, int hq, int hkv, float scale, int causal, bool fp4, hipStream_t stream);
+                              const int* padoff, int T, int t_pad, int hq, int hkv, float scale, int causal, int qf, hipStream_t stream);
 
 hipError_t launch_bwd_dq_mx(const MxOperands& m, const void* k, const float* lse, const float* delta, void* dq,
                             const Plan& plan, const int* pref_base, int T, int hq, int hkv, float scale, int causal,
-                            bool fp4, hipStream_t stream);
+                            int qf, hipStream_t stream);
 
 }  // namespace cfa

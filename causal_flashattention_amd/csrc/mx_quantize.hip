@@ -123,6 +123,67 @@ __global__ __launch_bounds__(256) void mx_quantize_d_fp4_kernel(const __bf16* __
   if (sub == 0) scales[blk] = badi ? 0xFF : (uint8_t)(e + 127);
 }
 
+// E2M3 (FP6) element of an already-scaled value |y| <= 7.5: the magnitudes form a grid of step
+// 1/8 on [0, 2), 1/4 on [2, 4) and 1/2 on [4, 7.5], one code per grid point, so rounding the
+// position within the binade to the nearest even integer is round-to-nearest, ties to the even
+// code. y is a bf16 value times a power of two: every product and difference below is exact.
+__device__ inline int e2m3_code(float y) {
+  const float a = fabsf(y);
+  const int c = a < 2.f ? (int)rintf(a * 8.f) : a < 4.f ? 16 + (int)rintf((a - 2.f) * 4.f)
+                                                          : 24 + (int)rintf((a - 4.f) * 2.f);
+  return c | (__builtin_signbit(y) ? 32 : 0);
+}
+
+// Four lanes per block of 32 elements, 8 elements each. Block b of a row is the 192-bit
+// little-endian number whose bits 6i..6i+5 hold code i; lane `sub` owns its bytes 6·sub ..
+// 6·sub+5 and writes them as three 16-bit pieces: bytes 0-15 of the block go to the row's
+// 16-byte part [16b, 16b+16), bytes 16-23 to its 8-byte part [d/2 + 8b, d/2 + 8b + 8); a row
+// (one token and head) is 3d/4 bytes. Same block rule as E2M1 (top exponent 2).
+__global__ __launch_bounds__(256) void mx_quantize_d_fp6_kernel(const __bf16* __restrict__ x,
+                                                                uint8_t* __restrict__ codes,
+                                                                uint8_t* __restrict__ scales, long n_blocks, int nb) {
+  const long blk = (long)blockIdx.x * 64 + threadIdx.x / 4;
+  const int sub = threadIdx.x & 3;
+  float v[8];
+  float amax = 0.f;
+  bool bad = false;
+  if (blk < n_blocks) {
+    const bf16x8 u = __builtin_bit_cast(bf16x8, *(const i32x4*)(x + blk * 32 + sub * 8));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[e] = (float)u[e];
+      bad |= !__builtin_isfinite(v[e]);
+      amax = fmaxf(amax, fabsf(v[e]));
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  int badi = bad ? 1 : 0;
+  badi |= __shfl_xor(badi, 1);
+  badi |= __shfl_xor(badi, 2);
+  if (blk >= n_blocks) return;
+  const int e = mx_exponent_fp4(amax);           // E2M3 and E2M1 share the top exponent 2
+  uint64_t bits = 0;
+  if (!badi) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      bits |= (uint64_t)e2m3_code(fminf(fmaxf(__builtin_amdgcn_ldexpf(v[j], -e), -7.5f), 7.5f)) << (6 * j);
+  }
+  const long row = blk / nb;
+  const int b = (int)(blk % nb);
+  uint8_t* rowp = codes + row * (long)(24 * nb);
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int o = 6 * sub + 2 * k;               // byte of the block; a piece never straddles 16
+    const int dst = o < 16 ? 16 * b + o : 16 * nb + 8 * b + (o - 16);
+    *(uint16_t*)(rowp + dst) = (uint16_t)(bits >> (16 * k));
+  }
+  if (sub == 0) scales[blk] = badi ? 0xFF : (uint8_t)(e + 127);
+}
+
 // grid: (padded 32-token blocks upper bound) × h; block 256 threads; D = head dim (64 or 128).
 // The 32 × D tile is read with 16-byte loads along channels into LDS, then each lane of the
 // first 2·D threads reduces 16 tokens of one channel; the two lanes of a channel meet in LDS.
@@ -225,6 +286,17 @@ hipError_t launch_mx_quantize_d_fp4(const void* x, long n_elems, uint8_t* codes,
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(mx_quantize_d_fp4_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)x, codes,
                      scales, n_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quantize_d_fp6(const void* x, long n_elems, int d, uint8_t* codes, uint8_t* scales,
+                                    hipStream_t stream) {
+  const long n_blocks = n_elems / 32;
+  if (n_blocks == 0) return hipSuccess;
+  const long grid = (n_blocks + 63) / 64;
+  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(mx_quantize_d_fp6_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)x, codes,
+                     scales, n_blocks, d / 32);
   return hipGetLastError();
 }
 

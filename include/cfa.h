@@ -53,8 +53,8 @@ extern "C" {
 
 /* CFA_MXFP4: the MXFP8 path with the score product QK^T on E2M1 copies of Q and K (mx_quantize_fp4),
  * a reading of the mixed NVFP4/FP8 path the FLAMIA page names ("FLAMIA Mimarisi ve Temel Tasarım
- * İlkeleri"). */
-typedef enum { CFA_F32 = 0, CFA_BF16 = 1, CFA_MXFP8 = 2, CFA_MXFP4 = 3 } cfa_dtype;
+ * İlkeleri"). CFA_MXFP6: the same with E2M3 copies (mx_quantize_fp6). */
+typedef enum { CFA_F32 = 0, CFA_BF16 = 1, CFA_MXFP8 = 2, CFA_MXFP4 = 3, CFA_MXFP6 = 4 } cfa_dtype;
 
 typedef enum {
   CFA_OK = 0,
@@ -79,9 +79,9 @@ const char* cfa_last_error(void);
  * on the sizes, never on the values of cu_seqlens. Returns 0 for invalid sizes. */
 size_t cfa_workspace_bytes(int pass, int total_tokens, int n_docs, int hq, int hkv, int d, int dtype);
 
-/* Bytes of the forward-to-backward buffer `saved` (MXFP8 only: the d-blocked E4M3 copies of Q
- * and K with their scales, reused by the backward so both passes see identical scores).
- * 0 for the other dtypes. */
+/* Bytes of the forward-to-backward buffer `saved` (the MX dtypes only: the d-blocked E4M3, E2M1
+ * or E2M3 copies of Q and K with their scales, reused by the backward so both passes see
+ * identical scores). 0 for the other dtypes. */
 size_t cfa_saved_bytes(int total_tokens, int n_docs, int hq, int hkv, int d, int dtype);
 
 /*
@@ -90,8 +90,9 @@ size_t cfa_saved_bytes(int total_tokens, int n_docs, int hq, int hkv, int d, int
  *   scale      : multiplier of Q K^T (usually 1/sqrt(d)); finite and > 0.
  *   dtype      : CFA_F32 (d = 64 or 128), CFA_BF16 (d = 64, 128 or 256; 256 is FlashAttention-2's
  *                extension, "FlashAttention (HU)", FlashAttention-2 (2023)), CFA_MXFP8 (d = 128).
- *                CFA_MXFP4 (d = 128): as CFA_MXFP8 with an E2M1 score product.
- *   saved      : CFA_MXFP8 / CFA_MXFP4: cfa_saved_bytes() bytes written here for attn_bwd; otherwise NULL.
+ *                CFA_MXFP4 / CFA_MXFP6 (d = 128): as CFA_MXFP8 with an E2M1 / E2M3 score product.
+ *   saved      : CFA_MXFP8 / CFA_MXFP4 / CFA_MXFP6: cfa_saved_bytes() bytes written here for attn_bwd;
+ *                otherwise NULL.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
@@ -101,13 +102,13 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Backward pass: dq, dk, dv (same layouts and element type as q, k, v) from q, k, v, the
- * forward's o and lse, and the upstream gradients dout (of O) and dlse (of LSE). dtype CFA_BF16
- * or CFA_MXFP8 (CFA_F32 is forward-only).
+ * forward's o and lse, and the upstream gradients dout (of O) and dlse (of LSE). dtype CFA_BF16,
+ * CFA_MXFP8, CFA_MXFP4 or CFA_MXFP6 (CFA_F32 is forward-only).
  *   dlse  : float32 [hq, total_tokens] like lse, or NULL for no gradient into lse. The pages do
  *           not name it; it is the exact derivative of the lse output the forward returns:
  *           d lse_i / d S_ij = P_ij, so it enters as dS_ij = P_ij (dP_ij - (D_i - dlse_i)) with
  *           D_i = sum_r dout_ir o_ir. Shares the 16-byte alignment rule.
- *   saved : CFA_MXFP8: the buffer attn_fwd filled, unmodified; otherwise NULL.
+ *   saved : the MX dtypes: the buffer attn_fwd filled, unmodified; otherwise NULL.
  * Deterministic: two calls on the same inputs give bit-identical outputs.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -172,6 +173,19 @@ int attn_bwd_cross(const void* q, const void* k, const void* v, const void* o, c
  * score operands of the CFA_MXFP4 attention path are these copies of Q and K.
  */
 int mx_quantize_fp4(const void* x, int total_tokens, int h, int d, uint8_t* codes, uint8_t* scales, void* stream);
+/*
+ * MXFP6 quantiser along d (E2M3 elements: 1 sign, 2 exponent bits with bias 1, 3 mantissa bits;
+ * magnitudes 0..1.875 in steps of 1/8, 2..3.75 in 1/4, 4..7.5 in 1/2): bf16 x [total_tokens, h,
+ * d] -> codes [total_tokens, h, 3d/4] bytes + E8M0 scales [total_tokens, h, d/32]. Per 32-channel
+ * block b: e = floor(log2 amax) - 2 clamped to [-127, 127] (-127 for a zero block); elements
+ * x * 2^-e saturated to +-7.5 and rounded to the nearest E2M3 value (ties to the even code; sign of
+ * zero kept); a NaN/Inf block gets scale 0xFF and codes 0. Block b is the 192-bit little-endian
+ * number with code i in bits 6i..6i+5; its bytes 0-15 are stored at [16b, 16b+16) of the row and
+ * its bytes 16-23 at [d/2 + 8b, d/2 + 8b + 8) -- the two parts of the matrix-core operand of
+ * v_mfma_scale_f32_32x32x64_f8f6f4 with format code 2. x and codes: 16-byte aligned. The score
+ * operands of the CFA_MXFP6 attention path are these copies of Q and K.
+ */
+int mx_quantize_fp6(const void* x, int total_tokens, int h, int d, uint8_t* codes, uint8_t* scales, void* stream);
 /* Upper bound of P_{n_docs} for any cu_seqlens with these sizes, rounded up to 32:
  * 32*ceil(total_tokens/32) + 32*n_docs. */
 int mx_padded_tokens(int total_tokens, int n_docs);

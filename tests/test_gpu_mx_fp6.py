@@ -1,0 +1,132 @@
+"""GPU parity of the MXFP6/FP8 path (E2M3 score product, the rest MXFP8) against the MX oracle
+with ``qk="e2m3"``, through the C ABI.
+
+Tolerances as for MXFP8: O (and dQ, dK, dV) rel-L2 <= 3e-2; LSE max-abs <= 1e-3 (the scores come
+from identical E2M3 operands and scales on both sides). Bit-identity on the GPU: causality,
+document isolation and reruns.
+"""
+import numpy as np
+import pytest
+import torch
+
+import causal_flashattention_amd as cfa
+from causal_flashattention_amd import workloads as W
+from oracle import mx_attention as mxa
+from gpu_helpers import announce, rel_l2, to_f64, upload
+
+pytestmark = pytest.mark.gpu
+
+MX_TOL = 3e-2
+LSE_TOL = 1e-3
+
+
+def _fwd(w, dev):
+    o, lse, saved = cfa.attn_fwd(dev["q"], dev["k"], dev["v"], dev["cu"], scale=w.scale, causal=w.causal,
+                                 cu_seqlens_host=dev["cu_host"], mx="mxfp6")
+    torch.cuda.synchronize()
+    return o, lse, saved
+
+
+@pytest.mark.parametrize("lengths,hq,hkv,causal", [
+    ([1, 5, 64, 127, 129, 300], 2, 2, True),
+    ([513, 31, 200, 33], 4, 2, True),
+    ([700, 1], 4, 1, True),
+    ([100, 257], 2, 1, False),
+])
+def test_fp6_forward_random_documents(lengths, hq, hkv, causal):
+    w = W.make_random(seed=1800 + sum(lengths), lengths=lengths, hq=hq, hkv=hkv, causal=causal)
+    announce("mxfp6 fwd random", lengths, hq, hkv, causal)
+    o, lse, _ = _fwd(w, upload(w))
+    ro, rl = mxa.attn_mx_fwd(w.f64("q"), w.f64("k"), w.f64("v"), w.cu_seqlens, w.scale, causal, qk="e2m3")
+    r8, _ = mxa.attn_mx_fwd(w.f64("q"), w.f64("k"), w.f64("v"), w.cu_seqlens, w.scale, causal)
+    err = rel_l2(to_f64(o), ro)
+    print("rel-L2 o", err, "fp6 vs fp8 oracle", rel_l2(ro, r8))
+    assert err <= MX_TOL
+    assert np.max(np.abs(to_f64(lse) - rl)) <= LSE_TOL
+
+
+def test_fp6_forward_causality_isolation_determinism():
+    lengths = [300, 129, 1, 64, 700]
+    w = W.make_random(seed=1844, lengths=lengths, hq=4, hkv=2)
+    announce("mxfp6 fwd invariants", lengths)
+    dev = upload(w)
+    o1, l1, _ = _fwd(w, dev)
+    o2, l2, _ = _fwd(w, dev)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    cu = w.cu_seqlens
+    for n in range(len(lengths)):
+        s0, s1 = int(cu[n]), int(cu[n + 1])
+        sub = W.Workload(name="doc", total_tokens=s1 - s0, hq=4, hkv=2, d=128, dtype="bf16", scale=w.scale,
+                         cu_seqlens=np.array([0, s1 - s0], np.int32), q=w.q[s0:s1], k=w.k[s0:s1], v=w.v[s0:s1])
+        oa, la, _ = _fwd(sub, upload(sub))
+        assert torch.equal(oa, o1[s0:s1]) and torch.equal(la, l1[:, s0:s1])
+    for jl in (0, 31, 32, 100, 127, 128, 200, 699):
+        j = int(cu[4]) + jl
+        dev2 = {kk: vv.clone() for kk, vv in dev.items()}
+        for name in ("q", "k", "v"):
+            dev2[name][j] = dev2[name][j] * 7.5 + 30.0
+        o3, l3, _ = _fwd(w, dev2)
+        assert torch.equal(o3[:j], o1[:j]) and torch.equal(l3[:, :j], l1[:, :j]), jl
+
+
+def test_fp6_forward_workload_4_one_head():
+    w = W.make_workload(4, with_grad=False)
+    announce("mxfp6 fwd workload 4", w.n_docs)
+    o, lse, _ = _fwd(w, upload(w))
+    o, lse = to_f64(o), to_f64(lse)
+    hh = 5
+    ro, rl = mxa.attn_mx_fwd(w.f64("q")[:, [hh]], w.f64("k")[:, [hh]], w.f64("v")[:, [hh]], w.cu_seqlens, w.scale,
+                             qk="e2m3")
+    assert rel_l2(o[:, [hh]], ro) <= MX_TOL
+    assert np.max(np.abs(lse[[hh]] - rl)) <= LSE_TOL
+
+
+def _fwd_bwd(w, dev):
+    o, lse, saved = _fwd(w, dev)
+    dq, dk, dv = cfa.attn_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], dev["cu"], scale=w.scale,
+                              causal=w.causal, cu_seqlens_host=dev["cu_host"], mx="mxfp6", saved=saved)
+    torch.cuda.synchronize()
+    return o, lse, dq, dk, dv
+
+
+@pytest.mark.parametrize("lengths,hq,hkv,causal", [
+    ([1, 5, 64, 127, 129, 300], 2, 2, True),
+    ([513, 31, 200, 33], 4, 2, True),
+    ([700, 1], 4, 1, True),
+    ([100, 257], 2, 1, False),
+])
+def test_fp6_backward_random_documents(lengths, hq, hkv, causal):
+    w = W.make_random(seed=1900 + sum(lengths), lengths=lengths, hq=hq, hkv=hkv, causal=causal)
+    announce("mxfp6 bwd random", lengths, hq, hkv, causal)
+    _, _, dq, dk, dv = _fwd_bwd(w, upload(w))
+    ref = mxa.attn_mx_bwd(w.f64("q"), w.f64("k"), w.f64("v"), w.f64("do"), w.cu_seqlens, w.scale, causal, qk="e2m3")
+    errs = [rel_l2(to_f64(a), b) for a, b in zip((dq, dk, dv), ref)]
+    print("rel-L2 dq dk dv", errs)
+    assert max(errs) <= MX_TOL
+
+
+def test_fp6_backward_causality_isolation_determinism():
+    lengths = [300, 129, 1, 64, 700]
+    w = W.make_random(seed=1944, lengths=lengths, hq=4, hkv=2)
+    announce("mxfp6 bwd invariants", lengths)
+    dev = upload(w)
+    r1 = _fwd_bwd(w, dev)
+    r2 = _fwd_bwd(w, dev)
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+    cu = w.cu_seqlens
+    for n in range(len(lengths)):
+        s0, s1 = int(cu[n]), int(cu[n + 1])
+        sub = W.Workload(name="doc", total_tokens=s1 - s0, hq=4, hkv=2, d=128, dtype="bf16", scale=w.scale,
+                         cu_seqlens=np.array([0, s1 - s0], np.int32), q=w.q[s0:s1], k=w.k[s0:s1], v=w.v[s0:s1],
+                         do=w.do[s0:s1])
+        ra = _fwd_bwd(sub, upload(sub))
+        for a, b in zip(ra[2:], r1[2:]):
+            assert torch.equal(a, b[s0:s1])
+    for jl in (0, 31, 32, 127, 128, 699):
+        j = int(cu[4]) + jl
+        dev2 = {kk: vv.clone() for kk, vv in dev.items()}
+        for name in ("q", "k", "v", "do"):
+            dev2[name][j] = dev2[name][j] * 7.5 + 30.0
+        r3 = _fwd_bwd(w, dev2)
+        assert torch.equal(r3[2][:j], r1[2][:j]), jl

@@ -91,3 +91,23 @@ def test_mx_quantize_fp4_bit_exact(d):
         rc, rs = mx.quantize_d_fp4(W.bf16_bits_to_f64(xin))
         assert np.array_equal(c.cpu().numpy(), mx.pack_fp4(rc))
         assert np.array_equal(s.cpu().numpy(), rs)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_mx_quantize_fp6_bit_exact(d):
+    """E2M3 codes (packed) and scale bytes bit-identical to the reference, special values included;
+    plus a tensor whose scaled elements sit exactly on E2M3 midpoints (ties to the even code)."""
+    T, h = 97, 3
+    xb = _special_tensor(T, h, d, seed=50 + d)
+    rng = np.random.default_rng(51)
+    grid = np.concatenate([np.arange(16) / 8.0, 2.0 + np.arange(8) / 4.0, 4.0 + np.arange(8) / 2.0])
+    mids = np.concatenate([(grid[:-1] + grid[1:]) / 2, -(grid[:-1] + grid[1:]) / 2, grid, [0.0]]).astype(np.float32)
+    xm = rng.choice(mids, size=(T, h, d)).astype(np.float32)
+    xm[:, :, ::32] = 7.5                       # block max 7.5: e = 0, elements are the midpoints themselves
+    for xin in (xb, W.f32_to_bf16_bits(xm)):
+        announce("mx_quantize_fp6", d)
+        c, s = cfa.mx_quantize_fp6(to_dev(xin))
+        torch.cuda.synchronize()
+        rc, rs = mx.quantize_d_fp6(W.bf16_bits_to_f64(xin))
+        assert np.array_equal(c.cpu().numpy(), mx.pack_fp6(rc))
+        assert np.array_equal(s.cpu().numpy(), rs)
