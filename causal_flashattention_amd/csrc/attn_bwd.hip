@@ -609,12 +609,15 @@ __global__ __launch_bounds__(256) void dkdv_split_reduce_kernel(const float* __r
 
 // ------------------------------------------------------------------ dQ
 // Cross-attention (CROSS = true): work list on the query documents, `kdoc[doc]` = key rows.
-template <int D, bool CROSS>
-__global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_bwd_dq_kernel(
+// HPB query heads of one kv group per workgroup (4 waves each, 32 queries per wave): the K/V
+// tiles are staged once for all of them (HPB = 2 halves the copies per product).
+template <int D, bool CROSS, int HPB>
+__global__ __launch_bounds__(256 * HPB, D == 256 ? 1 : 2 / HPB) void attn_bwd_dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     __bf16* __restrict__ dq, Plan plan, int total_tokens, int hq, int hkv, float scale, int causal,
     const int2* __restrict__ kdoc) {
+  static_assert(HPB == 1 || D == 128, "two heads per workgroup at d = 128 only");
   using C = BwdTile<D>;
   constexpr int BN = 64;
   constexpr int TILE = BN * C::RSTR;
@@ -626,7 +629,8 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_bwd_dq_kernel(
   __shared__ __attribute__((aligned(16))) char lds_a[STAGE];
   __shared__ __attribute__((aligned(16))) char lds_b[STAGE];
 
-  const int p = blockIdx.x / hq, h = blockIdx.x % hq;
+  const int n_hb = hq / HPB;
+  const int p = blockIdx.x / n_hb, hb = blockIdx.x % n_hb;
   int s0, L, t, doc;
   if (!decode_item(plan, p, 128, true, s0, L, t, &doc)) return;
   int k_s0 = s0, Lk = L;                         // key rows (cross-attention: their own documents)
@@ -637,8 +641,9 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_bwd_dq_kernel(
   }
   const int off = CROSS ? Lk - L : 0;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), half = lane >> 5;
+  const int h = hb * HPB + (w >> 2);             // this wave's query head
   const int g = h / (hq / hkv);
-  const int wr0 = t * 128 + 32 * w;
+  const int wr0 = t * 128 + 32 * (w & 3);
   const int qrow = wr0 + (lane & 31);
   const int kv_end = causal ? (CROSS ? min(Lk, min(L, (t + 1) * 128) + off) : min(L, (t + 1) * 128)) : Lk;
   const int n_kt = (CROSS && kv_end <= 0) ? 0 : (kv_end + BN - 1) / BN;
@@ -673,8 +678,8 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_bwd_dq_kernel(
     if constexpr (D >= 128) {
       const size_t row0 = ((size_t)(k_s0 + k0) * hkv + g) * D;
       const uint32_t stride = (uint32_t)hkv * D * 2;
-      stage_rows_lds<BN, 4, D>(kb, (const char*)(k + row0), stride, kv_end - 1 - k0, w, lane);
-      stage_rows_lds<BN, 4, D>(vb, (const char*)(v + row0), stride, kv_end - 1 - k0, w, lane);
+      stage_rows_lds<BN, 4 * HPB, D>(kb, (const char*)(k + row0), stride, kv_end - 1 - k0, w, lane);
+      stage_rows_lds<BN, 4 * HPB, D>(vb, (const char*)(v + row0), stride, kv_end - 1 - k0, w, lane);
     } else {
       i32x4 kreg[PT], vreg[PT];
 #pragma unroll
@@ -855,10 +860,14 @@ static hipError_t launch_dq_d(const void* q, const void* k, const void* v, const
                               const float* delta, void* dq, const Plan& plan, int T, int hq, int hkv, float scale,
                               int causal, hipStream_t stream, const int2* kdoc) {
   const long items = (long)(T + 127) / 128 + plan.n_docs;
-  auto kern = kdoc ? attn_bwd_dq_kernel<D, true> : attn_bwd_dq_kernel<D, false>;
-  const long grid = items * hq;
+  // two query heads of a kv group per workgroup where the group has an even size (d = 128)
+  constexpr int HP2 = D == 128 ? 2 : 1;
+  const int hpb = (D == 128 && (hq / hkv) % 2 == 0) ? 2 : 1;
+  auto kern = hpb == 2 ? (kdoc ? attn_bwd_dq_kernel<D, true, HP2> : attn_bwd_dq_kernel<D, false, HP2>)
+                       : (kdoc ? attn_bwd_dq_kernel<D, true, 1> : attn_bwd_dq_kernel<D, false, 1>);
+  const long grid = items * (hq / hpb);
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)q, (const __bf16*)k,
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256 * hpb), 0, stream, (const __bf16*)q, (const __bf16*)k,
                      (const __bf16*)v, (const __bf16*)dout, lse, delta, (__bf16*)dq, plan, T, hq, hkv, scale, causal,
                      kdoc);
   return hipGetLastError();
