@@ -7,16 +7,15 @@
 //   P_ij  = exp(scale·q_i·k_j − LSE_i)           (0 where key j is masked)
 //   D_i   = Σ_r dO_ir O_ir − dLSE_i               -- bwd_pre_kernel (dLSE optional, else 0)
 //   dP_ij = dO_i·v_j,  dS_ij = P_ij (dP_ij − D_i)
-//   dV_j  = Σ_{h in group} Σ_i P_ij dO_i           -- attn_bwd_dkdv_kernel
-//   dK_j  = scale Σ_{h in group} Σ_i dS_ij q_i     -- attn_bwd_dkdv_kernel
+//   dV_j  = Σ_{h in group} Σ_i P_ij dO_i           -- attn_bwd_dkdv_pair_kernel
+//   dK_j  = scale Σ_{h in group} Σ_i dS_ij q_i     -- attn_bwd_dkdv_pair_kernel
 //   dQ_i  = scale Σ_j dS_ij k_j                    -- attn_bwd_dq_kernel (separate pass)
 // No floating-point atomics: each output element is summed by one lane in a fixed order, so
 // reruns are bit-identical and a token never receives contributions through shared state.
 //
-// dK/dV kernel: a workgroup owns 128 keys of one kv head (4 waves × 32 keys). Each wave keeps
-// its K and V rows in registers as MFMA B operands and accumulates dKᵀ and dVᵀ (d × 32 keys).
-// It walks the query tiles (64 queries, double-buffered in LDS with their LSE and D) of every
-// query head of the group, from the diagonal to the end of the document:
+// dK/dV kernel: wave pairs own 32 keys of one kv head each (K or V rows in registers as MFMA B
+// operands) and walk the query tiles of every query head of the group, from the diagonal to the
+// end of the document (details at the kernel):
 //   S  = Q Kᵀ        A = Q tile rows (LDS)          -> lane holds one key, 16 queries
 //   dP = dO Vᵀ       A = dO tile rows (LDS)
 //   dVᵀ += dOᵀ P     A = dOᵀ via ds_read_b64_tr_b16, B = P as computed (bf16)
@@ -63,244 +62,14 @@ struct BwdTile {
   static constexpr int RSTR = S::STR;
   static constexpr int DS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int QB = 1;              // 32-query blocks per dK/dV step
-  static constexpr int BM = 32 * QB;        // queries per dK/dV step
-  static constexpr int DKDV_STAGE = 2 * BM * RSTR + 2 * BM * 4;   // Q, dO tiles, lse2, D
 };
 
-// ------------------------------------------------------------------ dK / dV
-template <int D, bool CROSS>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    __bf16* __restrict__ dk, __bf16* __restrict__ dv, Plan plan, int total_tokens, int hq, int hkv,
-    float scale, int causal, const int2* __restrict__ qdoc) {
-  using C = BwdTile<D>;
-  constexpr int BM = C::BM;                      // queries per step
-  constexpr int QB = C::QB;
-  constexpr int TILE = BM * C::RSTR;             // bytes of one Q (or dO) tile
-  constexpr int STAGE = C::DKDV_STAGE;           // Q, dO, lse2, delta
-  constexpr int CH = BM * D / 8;                 // 16-byte chunks per tile
-  constexpr int PT = (CH + 255) / 256;
-  __shared__ __attribute__((aligned(16))) char lds_a[STAGE];
-  __shared__ __attribute__((aligned(16))) char lds_b[STAGE];
-
-  const int p = blockIdx.x / hkv, g = blockIdx.x % hkv;
-  int s0, L, t, doc;
-  if (!decode_item(plan, p, 128, false, s0, L, t, &doc)) return;
-  // key rows [s0, s0 + L); query rows [q_s0, q_s0 + Lq); off = L - Lq (0 for self-attention)
-  int q_s0 = s0, Lq = L;
-  if constexpr (CROSS) {
-    const int2 qd = qdoc[doc];
-    q_s0 = qd.x;
-    Lq = qd.y;
-  }
-  const int off = CROSS ? L - Lq : 0;
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), half = lane >> 5;
-  const int G = hq / hkv;
-  const int kw0 = t * 128 + 32 * w;              // first doc-local key of this wave
-  const int mykey = kw0 + (lane & 31);
-  const float sl2 = scale * LOG2E;
-  const SwzOffsets<D> so(lane);
-
-  // K and V rows of this wave as B operands (lane: key mykey, d = 16s + 8·half ..)
-  bf16x8 kf[C::DS], vf[C::DS];
-  {
-    const bool ok = mykey < L;
-    const size_t ro = ((size_t)(s0 + (ok ? mykey : 0)) * hkv + g) * D + 8 * half;
-#pragma unroll
-    for (int s = 0; s < C::DS; ++s) {
-      kf[s] = __builtin_bit_cast(bf16x8, ok ? *(const i32x4*)(k + ro + 16 * s) : i32x4{0, 0, 0, 0});
-      vf[s] = __builtin_bit_cast(bf16x8, ok ? *(const i32x4*)(v + ro + 16 * s) : i32x4{0, 0, 0, 0});
-    }
-  }
-  f32x16 dka[C::DB], dva[C::DB];
-#pragma unroll
-  for (int b = 0; b < C::DB; ++b) { dka[b] = f32x16{}; dva[b] = f32x16{}; }
-
-  // first query that can see this tile (self-attention: BM-aligned) and the query tiles per head
-  const int q_begin = causal ? (CROSS ? max(0, t * 128 - off) : t * 128) : 0;
-  const int n_qt = CROSS ? max(0, (Lq - q_begin + BM - 1) / BM) : (L - q_begin + BM - 1) / BM;
-  const int n_steps = n_qt * G;
-  const int wave_first_q = causal ? kw0 - off : 0;
-
-  // Staging of one step (Q and dO rows of one query head, their LSE and D) into an LDS buffer.
-  // d = 128: direct global -> LDS copies. Rows past the document end are clamped into it and
-  // masked in the arithmetic (P = 0), so nothing depends on their values.
-  float lreg = 0.f, dreg = 0.f;
-  auto stage = [&](int st, char* qb) {
-    const int h = g * G + st / n_qt;
-    const int q0 = q_begin + (st % n_qt) * BM;
-    char* ob = qb + TILE;
-    char* lb = ob + TILE;
-    if constexpr (D == 128) {
-      const size_t row0 = ((size_t)(q_s0 + q0) * hq + h) * D;
-      const uint32_t stride = (uint32_t)hq * D * 2;
-      stage_rows_lds<BM>(qb, (const char*)(q + row0), stride, Lq - 1 - q0, w, lane);
-      stage_rows_lds<BM>(ob, (const char*)(dout + row0), stride, Lq - 1 - q0, w, lane);
-      if (threadIdx.x < BM) {   // LSE and D through registers, written to LDS by stage_finish
-        const size_t li = (size_t)h * total_tokens + q_s0 + min(q0 + (int)threadIdx.x, Lq - 1);
-        lreg = lse[li];
-        if (CROSS && lreg == -INFINITY) lreg = INFINITY;   // a row that sees no key: P = 0
-        dreg = delta[li];
-      }
-    } else {
-      i32x4 qreg[PT], oreg[PT];
-#pragma unroll
-      for (int i = 0; i < PT; ++i) {
-        const int c = min(threadIdx.x + 256 * i, CH - 1);
-        const int row = c / (D / 8), col = c % (D / 8);
-        const size_t eo = ((size_t)(q_s0 + min(q0 + row, Lq - 1)) * hq + h) * D + col * 8;
-        qreg[i] = *(const i32x4*)(q + eo);
-        oreg[i] = *(const i32x4*)(dout + eo);
-      }
-#pragma unroll
-      for (int i = 0; i < PT; ++i) {
-        const int c = threadIdx.x + 256 * i;
-        const int row = c / (D / 8), col = c % (D / 8);
-        if (c < CH) {
-          *(i32x4*)(qb + C::S::chunk(row, col)) = qreg[i];
-          *(i32x4*)(ob + C::S::chunk(row, col)) = oreg[i];
-        }
-      }
-      if (threadIdx.x < BM) {
-        const size_t li = (size_t)h * total_tokens + q_s0 + min(q0 + (int)threadIdx.x, Lq - 1);
-        const float lv = lse[li];
-        ((float*)lb)[threadIdx.x] = (CROSS && lv == -INFINITY) ? INFINITY : lv;
-        ((float*)lb)[BM + threadIdx.x] = delta[li];
-      }
-    }
-  };
-
-  auto stage_finish = [&](char* qb) {   // d = 128: LSE and D registers -> LDS (after compute)
-    if constexpr (D == 128) {
-      if (threadIdx.x < BM) {
-        float* lb = (float*)(qb + 2 * TILE);
-        lb[threadIdx.x] = lreg;
-        lb[BM + threadIdx.x] = dreg;
-      }
-    }
-  };
-
-  auto iter = [&](int st, const char* qb, char* nxt) __attribute__((always_inline)) {
-    if (st + 1 < n_steps) stage(st + 1, nxt);
-    const int q0 = q_begin + (st % n_qt) * BM;
-    if (q0 + BM - 1 >= wave_first_q && kw0 < L) {
-      const char* ob = qb + TILE;
-      const float* lb = (const float*)(ob + TILE);
-      const float* db = lb + BM;
-      const bool need_mask = causal && (q0 + off < kw0 + 31);
-      const bool ragged = q0 + BM > Lq;
-      // ---- S = Q Kᵀ and dP = dO Vᵀ for the two 32-query blocks (operand rows read as a batch)
-      f32x16 sacc[QB], pacc[QB];
-#pragma unroll
-      for (int qb2 = 0; qb2 < QB; ++qb2) {
-        i32x4 fq[C::DS], fo[C::DS];
-#pragma unroll
-        for (int s = 0; s < C::DS; ++s) {
-          fq[s] = *(const i32x4*)(qb + qb2 * 32 * C::RSTR + so.row[s]);
-          fo[s] = *(const i32x4*)(ob + qb2 * 32 * C::RSTR + so.row[s]);
-        }
-        sacc[qb2] = f32x16{};
-        pacc[qb2] = f32x16{};
-#pragma unroll
-        for (int s = 0; s < C::DS; ++s) {
-          sacc[qb2] = mfma32(as_bf16x8(fq[s]), kf[s], sacc[qb2]);
-          pacc[qb2] = mfma32(as_bf16x8(fo[s]), vf[s], pacc[qb2]);
-        }
-        // issue the operand reads well ahead of the products they feed
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // 8 LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
-      }
-      // ---- P = exp(S - LSE) (masked), dS = P (dP - D), packed to bf16 B operands
-      bf16x8 pf[2 * QB], sf[2 * QB];
-#pragma unroll
-      for (int qb2 = 0; qb2 < QB; ++qb2)
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) {
-          float pv[2], dsv[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int qi_t = 32 * qb2 + 8 * ((j + u) >> 2) + 4 * half + ((j + u) & 3);  // tile-local query
-            float x = exp2_fast(fmaf(sacc[qb2][j + u], sl2, -lb[qi_t] * LOG2E));
-            if (need_mask && mykey > q0 + qi_t + off) x = 0.f;
-            if (ragged && q0 + qi_t >= Lq) x = 0.f;     // rows past the document end
-            pv[u] = x;
-            dsv[u] = x * (pacc[qb2][j + u] - db[qi_t]);
-          }
-          const int fi = 2 * qb2 + (j >> 3);
-          i32x4 up = __builtin_bit_cast(i32x4, pf[fi]);
-          i32x4 us = __builtin_bit_cast(i32x4, sf[fi]);
-          up[(j & 7) >> 1] = (int)pack_bf16x2(pv[0], pv[1]);
-          us[(j & 7) >> 1] = (int)pack_bf16x2(dsv[0], dsv[1]);
-          pf[fi] = __builtin_bit_cast(bf16x8, up);
-          sf[fi] = __builtin_bit_cast(bf16x8, us);
-        }
-      // ---- dVᵀ += dOᵀ P, dKᵀ += Qᵀ dS (A operands through transposing LDS reads, batched per kk)
-#pragma unroll
-      for (int kk = 0; kk < 2 * QB; ++kk) {
-        const int rb = (32 * (kk >> 1) + 16 * (kk & 1)) * C::RSTR;
-        bf16x8 ao[C::DB], aq[C::DB];
-#pragma unroll
-        for (int dbk = 0; dbk < C::DB; ++dbk) {
-          ao[dbk] = concat_tr(lds_read_tr16(ob + rb + so.tr0[dbk]), lds_read_tr16(ob + rb + so.tr1[dbk]));
-          aq[dbk] = concat_tr(lds_read_tr16(qb + rb + so.tr0[dbk]), lds_read_tr16(qb + rb + so.tr1[dbk]));
-        }
-#pragma unroll
-        for (int dbk = 0; dbk < C::DB; ++dbk) {
-          dva[dbk] = mfma32(ao[dbk], pf[kk], dva[dbk]);
-          dka[dbk] = mfma32(aq[dbk], sf[kk], dka[dbk]);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // 8 transposed reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-      }
-    }
-    if (st + 1 < n_steps) stage_finish(nxt);
-    wait_vmem();
-    __syncthreads();
-  };
-
-  if (n_steps > 0) {
-    stage(0, lds_a);
-    stage_finish(lds_a);
-  }
-  wait_vmem();
-  __syncthreads();
-  for (int st = 0; st < n_steps; st += 2) {
-    iter(st, lds_a, lds_b);
-    if (st + 1 < n_steps) iter(st + 1, lds_b, lds_a);
-  }
-
-  // write dK = scale·dKᵀ and dV (lane: key mykey, d = 32 db + 8 jg + 4·half + 0..3)
-  if (mykey < L) {
-    const size_t base = ((size_t)(s0 + mykey) * hkv + g) * D + 4 * half;
-#pragma unroll
-    for (int dbk = 0; dbk < C::DB; ++dbk)
-#pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        i32x2 uk, uv;
-        uk.x = (int)pack_bf16x2(dka[dbk][4 * jg] * scale, dka[dbk][4 * jg + 1] * scale);
-        uk.y = (int)pack_bf16x2(dka[dbk][4 * jg + 2] * scale, dka[dbk][4 * jg + 3] * scale);
-        uv.x = (int)pack_bf16x2(dva[dbk][4 * jg], dva[dbk][4 * jg + 1]);
-        uv.y = (int)pack_bf16x2(dva[dbk][4 * jg + 2], dva[dbk][4 * jg + 3]);
-        *(i32x2*)(dk + base + 32 * dbk + 8 * jg) = uk;
-        *(i32x2*)(dv + base + 32 * dbk + 8 * jg) = uv;
-      }
-  }
-}
-
-// ------------------------------------------------------------------ dK / dV, d = 128 / 256, wave pairs
-// 2·NP waves own 32·NP keys of one kv head, as NP pairs of 32 keys (d = 128: 4 pairs, two waves
-// per SIMD; d = 256: 2 pairs, one wave per SIMD with twice the registers). In a pair, the "P wave" (w < NP)
+// ------------------------------------------------------------------ dK / dV, wave pairs
+// 2·NP waves own 32·NP keys of one kv head, as NP pairs of 32 keys (d = 64 and 128: 4 pairs, two
+// waves per SIMD; d = 256: 2 pairs, one wave per SIMD with twice the registers). In a pair, the "P wave" (w < NP)
 // holds K and computes S = Q Kᵀ, P = exp(S − LSE), dVᵀ += dOᵀ P; the "dS wave" (w + NP) holds V
 // and computes dP = dO Vᵀ, dS = P (dP − D), dKᵀ += Qᵀ dS with the bf16 P that its partner left
-// in LDS one step earlier. A step is 64 queries (d = 128; 32 for d = 256) of one query head,
+// in LDS one step earlier. A step is 64 queries (d = 64, 128; 32 for d = 256) of one query head,
 // taken as two 32-query blocks: the longer step leaves the copies of the next one more time. Running the dS wave one step behind removes every wait between the
 // two inside a step; the two waves of a pair sit on the same SIMD, so one wave's exponentials
 // and packing overlap the other's matrix products. Each wave holds one accumulator (dVᵀ or
@@ -327,7 +96,7 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
     const int2* __restrict__ qdoc, int total_k) {
   using C = BwdTile<D>;
   constexpr int KT = 32 * NP;                     // keys per workgroup
-  constexpr int QBS = D == 128 ? 2 : 1;           // 32-query blocks per step (a longer step hides the copies)
+  constexpr int QBS = D <= 128 ? 2 : 1;           // 32-query blocks per step (a longer step hides the copies)
   constexpr int BM = 32 * QBS;                    // queries per step
   constexpr int TILE = BM * C::RSTR;              // 16 KB
   constexpr int STAGE = 2 * TILE + 2 * BM * 4;    // Q, dO, LSE·log2 e, D
@@ -387,12 +156,24 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
   // lanes 0..31 of wave 0 fetch LSE and D into registers, written by stage_finish. Rows past
   // the document end are clamped into it and masked (P = 0).
   float lreg = 0.f, dreg = 0.f;
+  // d = 64: 144-byte padded rows (no swizzle), staged through registers: the role's NP waves
+  // load the BM × D tile as 16-byte chunks (TR per lane) and stage_finish writes them
+  constexpr int TR = D < 128 ? BM * D / 8 / (64 * NP) : 1;
+  i32x4 treg[TR];
   auto stage = [&](int st, char* buf) {
     const int h = h_lo + st / n_qt;
     const int q0 = q_begin + (st % n_qt) * BM;
     const __bf16* src = ds_wave ? dout : q;
-    stage_rows_lds<BM, NP, D>(buf + (ds_wave ? TILE : 0), (const char*)(src + ((size_t)(q_s0 + q0) * hq + h) * D),
-                              (uint32_t)hq * D * 2, Lq - 1 - q0, pair, lane);
+    if constexpr (D >= 128) {
+      stage_rows_lds<BM, NP, D>(buf + (ds_wave ? TILE : 0), (const char*)(src + ((size_t)(q_s0 + q0) * hq + h) * D),
+                                (uint32_t)hq * D * 2, Lq - 1 - q0, pair, lane);
+    } else {
+#pragma unroll
+      for (int i = 0; i < TR; ++i) {
+        const int c = pair * 64 + lane + 64 * NP * i, row = c / (D / 8), col = c % (D / 8);
+        treg[i] = *(const i32x4*)(src + ((size_t)(q_s0 + q0 + min(row, Lq - 1 - q0)) * hq + h) * D + 8 * col);
+      }
+    }
     if (threadIdx.x < BM) {
       const size_t li = (size_t)h * total_tokens + q_s0 + min(q0 + (int)threadIdx.x, Lq - 1);
       lreg = lse[li];
@@ -401,6 +182,13 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
     }
   };
   auto stage_finish = [&](char* buf) {
+    if constexpr (D < 128) {
+#pragma unroll
+      for (int i = 0; i < TR; ++i) {
+        const int c = pair * 64 + lane + 64 * NP * i;
+        *(i32x4*)(buf + (ds_wave ? TILE : 0) + C::S::chunk(c / (D / 8), c % (D / 8))) = treg[i];
+      }
+    }
     if (threadIdx.x < BM) {
       float* lb = (float*)(buf + 2 * TILE);
       lb[threadIdx.x] = lreg * LOG2E;
@@ -817,12 +605,12 @@ static hipError_t launch_dkdv_d(const void* q, const void* k, const void* v, con
                                 const float* delta, void* dk, void* dv, const Plan& plan_any, const int* pref_base,
                                 int T, int hq, int hkv, float scale, int causal, int n_split, float* part,
                                 hipStream_t stream, const int2* qdoc, int Tk) {
-  constexpr int NP = D == 256 ? 2 : 4;            // wave pairs (d = 64: waves) per workgroup
+  constexpr int NP = D == 256 ? 2 : 4;            // wave pairs per workgroup
   constexpr int KT = D == 256 ? 64 : 128;         // keys per workgroup
   Plan plan = plan_any;
   plan.pref = pref_base + pref_slot(KT) * (plan.n_docs + 1);
   const long items = (long)(Tk + KT - 1) / KT + plan.n_docs;   // key tiles (plan on the key documents)
-  if constexpr (D >= 128) {
+  {
     const long grid = items * hkv * n_split;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
     const long n = (long)Tk * hkv * D;
@@ -839,18 +627,12 @@ static hipError_t launch_dkdv_d(const void* q, const void* k, const void* v, con
     if (n_split > 1 && n > 0)
       hipLaunchKernelGGL(dkdv_split_reduce_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, stream, pdk,
                          pdv, (__bf16*)dk, (__bf16*)dv, n, n_split, scale);
-  } else {
-    const long grid = items * hkv;
-    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CROSS>), dim3((unsigned)grid), dim3(256), 0, stream,
-                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, lse, delta,
-                       (__bf16*)dk, (__bf16*)dv, plan, T, hq, hkv, scale, causal, qdoc);
   }
   return hipGetLastError();
 }
 
 int dkdv_head_split(int hq, int hkv, int d) {
-  if (d != 128 && d != 256) return 1;
+  (void)d;
   const int G = hq / hkv;
   return std::max(1, std::min(G, 8 / hkv));
 }

@@ -35,6 +35,9 @@ def _fwd_bwd(w, dev):
     ([77, 256, 1000], 4, 4, 64, True),
     ([33, 2, 190], 6, 3, 128, True),
     ([100, 257], 2, 1, 128, False),
+    ([513, 31, 200], 8, 2, 64, True),          # d = 64 with the GQA head split
+    ([700, 1], 4, 1, 64, True),                 # d = 64 MQA
+    ([100, 257], 2, 1, 64, False),
 ])
 def test_bf16_grads_random_documents(lengths, hq, hkv, d, causal):
     w = W.make_random(seed=7 + sum(lengths), lengths=lengths, hq=hq, hkv=hkv, d=d, causal=causal)
@@ -96,10 +99,11 @@ def test_bf16_grads_gqa_workload_3_sampled():
         assert abs(tq.sum() - tk.sum()) <= 4 * 2.0 ** -8 * (np.sqrt(np.sum(tq ** 2)) + np.sqrt(np.sum(tk ** 2)))
 
 
-def test_bf16_bwd_determinism_isolation_causality():
+@pytest.mark.parametrize("d", [128, 64])
+def test_bf16_bwd_determinism_isolation_causality(d):
     lengths = [300, 129, 1, 64, 700]
-    w = W.make_random(seed=21, lengths=lengths, hq=4, hkv=2)
-    announce("bwd bf16 invariants", lengths)
+    w = W.make_random(seed=21, lengths=lengths, hq=4, hkv=2, d=d)
+    announce("bwd bf16 invariants", lengths, d)
     dev = upload(w)
     r1 = _fwd_bwd(w, dev)
     r2 = _fwd_bwd(w, dev)
@@ -108,7 +112,7 @@ def test_bf16_bwd_determinism_isolation_causality():
     cu = w.cu_seqlens
     for n in range(len(lengths)):
         s0, s1 = int(cu[n]), int(cu[n + 1])
-        sub = W.Workload(name="doc", total_tokens=s1 - s0, hq=4, hkv=2, d=128, dtype="bf16", scale=w.scale,
+        sub = W.Workload(name="doc", total_tokens=s1 - s0, hq=4, hkv=2, d=d, dtype="bf16", scale=w.scale,
                          cu_seqlens=np.array([0, s1 - s0], np.int32), q=w.q[s0:s1], k=w.k[s0:s1], v=w.v[s0:s1],
                          do=w.do[s0:s1])
         ra = _fwd_bwd(sub, upload(sub))
