@@ -134,54 +134,63 @@ __device__ inline int e2m3_code(float y) {
   return c | (__builtin_signbit(y) ? 32 : 0);
 }
 
-// Four lanes per block of 32 elements, 8 elements each. Block b of a row is the 192-bit
-// little-endian number whose bits 6i..6i+5 hold code i; lane `sub` owns its bytes 6·sub ..
-// 6·sub+5 and writes them as three 16-bit pieces: bytes 0-15 of the block go to the row's
+// Two lanes per block of 32 elements, 16 elements (96 code bits) each. Block b of a row is the
+// 192-bit little-endian number whose bits 6i..6i+5 hold code i; its bytes 0-15 go to the row's
 // 16-byte part [16b, 16b+16), bytes 16-23 to its 8-byte part [d/2 + 8b, d/2 + 8b + 8); a row
-// (one token and head) is 3d/4 bytes. Same block rule as E2M1 (top exponent 2).
+// (one token and head) is 3d/4 bytes. Lane 0 owns bytes 0-11 (one 12-byte store), lane 1 bytes
+// 12-23 (4 bytes ending the 16-byte part, 8 bytes the 8-byte part). Same block rule as E2M1
+// (top exponent 2).
 __global__ __launch_bounds__(256) void mx_quantize_d_fp6_kernel(const __bf16* __restrict__ x,
                                                                 uint8_t* __restrict__ codes,
                                                                 uint8_t* __restrict__ scales, long n_blocks, int nb) {
-  const long blk = (long)blockIdx.x * 64 + threadIdx.x / 4;
-  const int sub = threadIdx.x & 3;
-  float v[8];
+  const long blk = (long)blockIdx.x * 128 + threadIdx.x / 2;
+  const int sub = threadIdx.x & 1;
+  float v[16];
   float amax = 0.f;
   bool bad = false;
   if (blk < n_blocks) {
-    const bf16x8 u = __builtin_bit_cast(bf16x8, *(const i32x4*)(x + blk * 32 + sub * 8));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      v[e] = (float)u[e];
-      bad |= !__builtin_isfinite(v[e]);
-      amax = fmaxf(amax, fabsf(v[e]));
+    for (int hh = 0; hh < 2; ++hh) {
+      const bf16x8 u = __builtin_bit_cast(bf16x8, *(const i32x4*)(x + blk * 32 + sub * 16 + 8 * hh));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[8 * hh + e] = (float)u[e];
+        bad |= !__builtin_isfinite(v[8 * hh + e]);
+        amax = fmaxf(amax, fabsf(v[8 * hh + e]));
+      }
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    for (int e = 0; e < 16; ++e) v[e] = 0.f;
   }
   amax = fmaxf(amax, __shfl_xor(amax, 1));
-  amax = fmaxf(amax, __shfl_xor(amax, 2));
   int badi = bad ? 1 : 0;
   badi |= __shfl_xor(badi, 1);
-  badi |= __shfl_xor(badi, 2);
   if (blk >= n_blocks) return;
   const int e = mx_exponent_fp4(amax);           // E2M3 and E2M1 share the top exponent 2
-  uint64_t bits = 0;
+  uint32_t w[3] = {0u, 0u, 0u};                  // this lane's 96 code bits, little endian
   if (!badi) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      bits |= (uint64_t)e2m3_code(fminf(fmaxf(__builtin_amdgcn_ldexpf(v[j], -e), -7.5f), 7.5f)) << (6 * j);
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t c = (uint32_t)e2m3_code(fminf(fmaxf(__builtin_amdgcn_ldexpf(v[j], -e), -7.5f), 7.5f));
+      const int bit = 6 * j;
+      w[bit >> 5] |= c << (bit & 31);
+      if ((bit & 31) > 26) w[(bit >> 5) + 1] |= c >> (32 - (bit & 31));   // a code across two words
+    }
   }
   const long row = blk / nb;
   const int b = (int)(blk % nb);
   uint8_t* rowp = codes + row * (long)(24 * nb);
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    const int o = 6 * sub + 2 * k;               // byte of the block; a piece never straddles 16
-    const int dst = o < 16 ? 16 * b + o : 16 * nb + 8 * b + (o - 16);
-    *(uint16_t*)(rowp + dst) = (uint16_t)(bits >> (16 * k));
+  if (sub == 0) {
+    uint32_t* dst = (uint32_t*)(rowp + 16 * b);
+    dst[0] = w[0];
+    dst[1] = w[1];
+    dst[2] = w[2];
+    scales[blk] = badi ? 0xFF : (uint8_t)(e + 127);
+  } else {
+    *(uint32_t*)(rowp + 16 * b + 12) = w[0];
+    *(i32x2*)(rowp + 16 * nb + 8 * b) = i32x2{(int)w[1], (int)w[2]};
   }
-  if (sub == 0) scales[blk] = badi ? 0xFF : (uint8_t)(e + 127);
 }
 
 // grid: (padded 32-token blocks upper bound) × h; block 256 threads; D = head dim (64 or 128).
@@ -293,7 +302,7 @@ hipError_t launch_mx_quantize_d_fp6(const void* x, long n_elems, int d, uint8_t*
                                     hipStream_t stream) {
   const long n_blocks = n_elems / 32;
   if (n_blocks == 0) return hipSuccess;
-  const long grid = (n_blocks + 63) / 64;
+  const long grid = (n_blocks + 127) / 128;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(mx_quantize_d_fp6_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)x, codes,
                      scales, n_blocks, d / 32);
