@@ -130,3 +130,26 @@ def test_fp4_backward_causality_isolation_determinism():
             dev2[name][j] = dev2[name][j] * 7.5 + 30.0
         r3 = _fwd_bwd(w, dev2)
         assert torch.equal(r3[2][:j], r1[2][:j]), jl
+
+
+def test_fp4_backward_workload_4_sampled():
+    w = W.make_workload(4)
+    announce("mxfp4 bwd workload 4", w.n_docs)
+    dev = upload(w)
+    _, _, dq, dk, dv = _fwd_bwd(w, dev)
+    L_all = np.diff(w.cu_seqlens)
+    n = int(np.argmax(L_all))
+    s0, L = int(w.cu_seqlens[n]), int(L_all[n])
+    hh = 7
+    sl = slice(s0, s0 + L)
+    q, k, v, do = (W.bf16_bits_to_f64(getattr(w, x)[sl][:, [hh]]) for x in ("q", "k", "v", "do"))
+    rows = np.unique(np.array([0, 1, 127, 128, 255, 256, L // 2, L - 129, L - 1]))
+    _, _, rdq, _, _ = mxa.attn_mx_rows(q, k, v, do, rows, w.scale, qk="e2m1")
+    e_dq = rel_l2(to_f64(dq[sl][rows][:, [hh]]), rdq)
+    # keys in the last 200 rows see only queries among those rows: their dK, dV are complete
+    tail = np.arange(L - 200, L)
+    _, _, _, pdk, pdv = mxa.attn_mx_rows(q, k, v, do, tail, w.scale, qk="e2m1")
+    e_dk = rel_l2(to_f64(dk[sl][L - 200:, [hh]]), pdk[L - 200:])
+    e_dv = rel_l2(to_f64(dv[sl][L - 200:, [hh]]), pdv[L - 200:])
+    print("rel-L2 dq dk dv (sampled)", e_dq, e_dk, e_dv)
+    assert max(e_dq, e_dk, e_dv) <= MX_TOL
