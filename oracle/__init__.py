@@ -25,7 +25,7 @@ Sources (web pages; cited by title and section):
 Modules:
 
 * ``attention``     -- naive two-pass forward with an explicit mask, and its exact gradient.
-* ``mx``            -- E4M3 (also E2M1, E2M3) / E8M0 block quantiser (along the head dim, or along
+* ``mx``            -- E4M3 (also E2M1, E2M3, E3M2) / E8M0 block quantiser (along the head dim, or along
   doc-local tokens).
 * ``mx_attention``  -- the attention oracle fed with the quantised operand copies.
 * ``decode``        -- one query per sequence over a packed (optionally MX-quantised) KV cache.

@@ -199,32 +199,74 @@ def _e2m3_encode_scaled(y):
     return (best | np.where(np.signbit(y), 32, 0)).astype(np.int64)
 
 
-def quantize_blocks_fp6(x):
-    """Quantise rows of 32 values to E2M3 codes (one int per element, 0..63) and E8M0 scale bytes."""
+# ---------------------------------------------------------------- E3M2 (MXFP6) elements
+# E3M2: 1 sign, 3 exponent (bias 3), 2 mantissa bits; no infinities or NaN. Exponent field 0
+# is subnormal (m/4 · 2^-2); field E >= 1 gives (1 + m/4)·2^(E-3): 0 .. 0.4375 in steps of 1/16,
+# then four values per binade up to 16 .. 28 in steps of 4. Block rule as for E2M3 with the
+# top exponent 4 (16 is the largest E3M2 power of two): e = floor(log2 amax) - 4, elements
+# x·2^-e saturated to ±28, nearest E3M2 value, ties to the even code.
+E3M2_MAX = 28.0
+E3M2_EMAX = 4
+
+
+def e3m2_decode(codes):
+    """Value of each 6-bit E3M2 code (float64); bit 5 is the sign."""
+    c = np.asarray(codes, dtype=np.int64)
+    E, m = (c >> 2) & 7, c & 3
+    mag = np.where(E == 0, m / 4.0 * 0.25, (1.0 + m / 4.0) * np.ldexp(1.0, E - 3))
+    return np.where(c & 32, -mag, mag)
+
+
+E3M2_VALUES = e3m2_decode(np.arange(32))
+
+
+def _e3m2_encode_scaled(y):
+    """Round already-scaled, finite values y (|y| <= 28) to E3M2 codes, RNE, sign kept."""
+    a = np.abs(np.asarray(y, dtype=np.float64))
+    d = np.abs(a[..., None] - E3M2_VALUES)
+    best = np.argmin(d, axis=-1)
+    dmin = np.take_along_axis(d, best[..., None], axis=-1)[..., 0]
+    nxt = np.minimum(best + 1, 31)
+    tie_up = (best + 1 <= 31) & (np.abs(a - E3M2_VALUES[nxt]) == dmin)
+    best = np.where(tie_up & (best % 2 == 1), best + 1, best)
+    return (best | np.where(np.signbit(y), 32, 0)).astype(np.int64)
+
+
+# the two 6-bit element types: (top exponent, largest value, encoder, decoder)
+FP6_FORMATS = {
+    "e2m3": (E2M3_EMAX, E2M3_MAX, _e2m3_encode_scaled, e2m3_decode),
+    "e3m2": (E3M2_EMAX, E3M2_MAX, _e3m2_encode_scaled, e3m2_decode),
+}
+
+
+def quantize_blocks_fp6(x, fmt="e2m3"):
+    """Quantise rows of 32 values to 6-bit codes of ``fmt`` ("e2m3" or "e3m2"; one int per
+    element, 0..63) and E8M0 scale bytes."""
+    emax, vmax, encode, _ = FP6_FORMATS[fmt]
     x = np.asarray(x, dtype=np.float64)
     finite = np.all(np.isfinite(x), axis=-1)
     xs = np.where(np.isfinite(x), x, 0.0)
     amax = np.max(np.abs(xs), axis=-1)
     _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
-    e = np.clip(ex - 1 - E2M3_EMAX, -127, 127)
+    e = np.clip(ex - 1 - emax, -127, 127)
     e = np.where(amax > 0, e, -127)
-    y = np.clip(np.ldexp(xs, -e[..., None]), -E2M3_MAX, E2M3_MAX)
-    codes = np.where(finite[..., None], _e2m3_encode_scaled(y), 0)
+    y = np.clip(np.ldexp(xs, -e[..., None]), -vmax, vmax)
+    codes = np.where(finite[..., None], encode(y), 0)
     scales = np.where(finite, e + 127, 0xFF)
     return codes.astype(np.uint8), scales.astype(np.uint8)
 
 
-def quantize_d_fp6(x):
-    """Blocks of 32 channels: x [T, h, d] -> E2M3 codes [T, h, d] (0..63), scales [T, h, d/32]."""
+def quantize_d_fp6(x, fmt="e2m3"):
+    """Blocks of 32 channels: x [T, h, d] -> 6-bit codes [T, h, d] (0..63), scales [T, h, d/32]."""
     x = np.asarray(x, dtype=np.float64)
     T, h, d = x.shape
     assert d % BLOCK == 0
-    codes, scales = quantize_blocks_fp6(x.reshape(T, h, d // BLOCK, BLOCK))
+    codes, scales = quantize_blocks_fp6(x.reshape(T, h, d // BLOCK, BLOCK), fmt)
     return codes.reshape(T, h, d), scales
 
 
 def pack_fp6(codes):
-    """Storage layout of E2M3 codes [..., d] (d a multiple of 32) -> [..., 3d/4] uint8.
+    """Storage layout of 6-bit codes (E2M3 or E3M2) [..., d] (d a multiple of 32) -> [..., 3d/4] uint8.
 
     Block b (channels 32b .. 32b+31) is the 192-bit little-endian number whose bits 6i .. 6i+5
     hold code i; its bytes 0-15 go to [16b, 16b+16) and bytes 16-23 to [d/2 + 8b, d/2 + 8b + 8)
@@ -241,10 +283,11 @@ def pack_fp6(codes):
                            by[..., 16:].reshape(c.shape[:-1] + (8 * nb,))], axis=-1)
 
 
-def dequantize_d_fp6(codes, scales):
-    """Values of d-blocked E2M3 codes [T, h, d] (unpacked) with scales [T, h, d/32]."""
+def dequantize_d_fp6(codes, scales, fmt="e2m3"):
+    """Values of d-blocked 6-bit codes of ``fmt`` [T, h, d] (unpacked) with scales [T, h, d/32]."""
     T, h, d = codes.shape
-    v = e2m3_decode(codes).reshape(T, h, d // BLOCK, BLOCK) * e8m0_decode(scales)[..., None]
+    decode = FP6_FORMATS[fmt][3]
+    v = decode(codes).reshape(T, h, d // BLOCK, BLOCK) * e8m0_decode(scales)[..., None]
     return v.reshape(T, h, d)
 
 

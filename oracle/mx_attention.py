@@ -38,7 +38,7 @@ MXFP4/FP8 variant (``qk="e2m1"``): the page names a mixed NVFP4/FP8 path without
 products take FP4. The reading here: the score product QKᵀ -- the one whose operands both
 passes share through ``saved`` -- takes E2M1 d-blocked copies ``Q_d``, ``K_d`` (same block rule
 with the E2M1 top exponent, see ``oracle.mx``); every other product is the MXFP8 path above.
-MXFP6/FP8 variant (``qk="e2m3"``): the same with E2M3 copies of Q and K.
+MXFP6/FP8 variants (``qk="e2m3"`` or ``"e3m2"``): the same with E2M3 or E3M2 copies of Q and K.
 """
 
 import numpy as np
@@ -57,13 +57,14 @@ def operand_copies(x_b, cu_seqlens):
 
 
 def qk_copy(x_b, qk):
-    """Decoded d-blocked copy used by QKᵀ: E4M3 (``qk="e4m3"``), E2M1 (``"e2m1"``) or E2M3 (``"e2m3"``)."""
+    """Decoded d-blocked copy used by QKᵀ: E4M3 (``qk="e4m3"``), E2M1 (``"e2m1"``), E2M3
+    (``"e2m3"``) or E3M2 (``"e3m2"``)."""
     if qk == "e2m1":
         c, s = _mx.quantize_d_fp4(x_b)
         return _mx.dequantize_d_fp4(c, s)
-    if qk == "e2m3":
-        c, s = _mx.quantize_d_fp6(x_b)
-        return _mx.dequantize_d_fp6(c, s)
+    if qk in ("e2m3", "e3m2"):
+        c, s = _mx.quantize_d_fp6(x_b, qk)
+        return _mx.dequantize_d_fp6(c, s, qk)
     assert qk == "e4m3"
     c, s = _mx.quantize_d(x_b)
     return _mx.dequantize_d(c, s)

@@ -1,7 +1,10 @@
-"""Pins for the E2M3 (MXFP6) quantiser, its storage packing and the MXFP6/FP8 attention oracle.
+"""Pins for the 6-bit (MXFP6: E2M3 and E3M2) quantisers, their storage packing and the
+MXFP6/FP8 attention oracles.
 
 * Format facts of E2M3 (1 sign, 2 exponent bits with bias 1, 3 mantissa bits): the 32
-  magnitudes form a grid of step 1/8 on [0, 2), 1/4 on [2, 4) and 1/2 on [4, 7.5].
+  magnitudes form a grid of step 1/8 on [0, 2), 1/4 on [2, 4) and 1/2 on [4, 7.5]. E3M2 (1
+  sign, 3 exponent bits with bias 3, 2 mantissa bits): step 1/16 on [0, 0.5), then four values
+  per binade [2^k, 2^(k+1)) up to 28.
 * Rounding: every representable value round-trips; midpoints go to the even code; just above
   or below a midpoint goes to the nearer code; saturation at ±7.5.
 * Block rule checked against an independent exhaustive formulation (nearest grid point).
@@ -45,16 +48,16 @@ def test_round_trip_midpoints_saturation():
     assert mx.e2m3_decode(codes[0, 0]) == 0.5                        # 7/16 = 0.4375: tie -> even (0.5)
 
 
-def _independent_block(x):
+def _independent_block(x, grid=None, emax=2):
     amax = max(abs(float(v)) for v in x)
     if amax == 0:
         return [0] * len(x), 0
-    e = int(np.floor(np.log2(amax))) - 2
+    e = int(np.floor(np.log2(amax))) - emax
     e = max(-127, min(127, e))
-    mags = list(_grid())
+    mags = list(_grid() if grid is None else grid)
     codes = []
     for v in x:
-        y = min(abs(float(v)) / 2.0 ** e, 7.5)
+        y = min(abs(float(v)) / 2.0 ** e, mags[-1])
         dist = [abs(y - m) for m in mags]
         best = min(range(32), key=lambda i: (dist[i], i % 2))
         codes.append(best | (32 if np.signbit(v) else 0))
@@ -152,3 +155,93 @@ def test_fp6_oracle_between_fp4_and_fp8_and_keeps_causality():
         o5, _ = mxa.attn_mx_fwd(q2, k2, v2, cu, 0.125, qk="e2m3")
         dq2, _, _ = mxa.attn_mx_bwd(q2, k2, v2, do2, cu, 0.125, qk="e2m3")
         assert np.array_equal(o5[:j], o6[:j]) and np.array_equal(dq2[:j], dq[:j]), j
+
+
+# ------------------------------------------------------------------------------- E3M2
+def _grid_e3m2():
+    sub = np.arange(4) / 16.0
+    normal = [2.0 ** k * (1 + m / 4) for k in range(-2, 5) for m in range(4)]
+    return np.concatenate([sub, normal])
+
+
+def test_e3m2_values():
+    want = _grid_e3m2()
+    assert want[-1] == 28.0 and len(want) == 32 and np.all(np.diff(want) > 0)
+    np.testing.assert_array_equal(mx.e3m2_decode(np.arange(32)), want)
+    np.testing.assert_array_equal(mx.e3m2_decode(np.arange(32) | 32), -want)
+    # bit fields: code 0b0_111_11 is the largest value, 0b0_001_00 the smallest normal
+    assert mx.e3m2_decode(0b011111) == 28.0 and mx.e3m2_decode(0b000100) == 0.25
+
+
+def test_e3m2_round_trip_midpoints_saturation():
+    vals = _grid_e3m2()
+    enc = mx._e3m2_encode_scaled
+    assert np.array_equal(enc(vals), np.arange(32))
+    assert np.array_equal(enc(-vals[1:]), np.arange(1, 32) | 32)
+    for c in range(31):
+        mid = (vals[c] + vals[c + 1]) / 2
+        want = c if c % 2 == 0 else c + 1
+        assert enc(np.array([mid]))[0] == want, c
+        assert enc(np.array([np.nextafter(mid, 100)]))[0] == c + 1
+        assert enc(np.array([np.nextafter(mid, -100)]))[0] == c
+    # amax 31 -> e = 4 - 4 = 0: 18 is halfway 16 (even code) / 20, 22 halfway 20 / 24 (even)
+    codes, sc = mx.quantize_blocks_fp6(np.array([[31.0, 18.0, 22.0, 0.09375, -17.0] + [0.0] * 27]), "e3m2")
+    assert sc[0] == 127
+    assert list(mx.e3m2_decode(codes[0, :5])) == [28.0, 16.0, 24.0, 0.125, -16.0]
+    # amax 1000 -> e = 9 - 4 = 5: 1000/32 saturates, 100/32 = 3.125 -> 3, 27/32 -> 0.875
+    codes, sc = mx.quantize_blocks_fp6(np.array([[1000.0, 100.0, 27.0] + [0.0] * 29]), "e3m2")
+    assert sc[0] == 127 + 5
+    assert list(mx.e3m2_decode(codes[0, :3])) == [28.0, 3.0, 0.875]
+
+
+def test_e3m2_block_rule_against_exhaustive_formulation():
+    rng = np.random.default_rng(15)
+    grid = _grid_e3m2()
+    for trial in range(300):
+        scale = 2.0 ** rng.integers(-20, 20)
+        x = rng.standard_normal(32) * scale
+        if trial % 3 == 0:
+            x = np.round(x / scale * 32) / 32 * scale       # many exact midpoints
+        if trial % 5 == 0:
+            x[rng.integers(32)] *= 40                       # wide blocks: small values go subnormal
+        c, s = mx.quantize_blocks_fp6(x[None, :], "e3m2")
+        wc, ws = _independent_block(x, grid, emax=4)
+        assert s[0] == ws and list(c[0]) == wc, trial
+    c, s = mx.quantize_blocks_fp6(np.zeros((1, 32)), "e3m2")
+    assert s[0] == 0 and not np.any(c)
+    c, s = mx.quantize_blocks_fp6(np.array([[np.nan] + [1.0] * 31]), "e3m2")
+    assert s[0] == 0xFF and not np.any(c)
+
+
+def test_e3m2_oracle_reduces_on_exact_inputs():
+    # amax 4 or 6 -> e = -2: the values times 4 are 0, 4, 8, 12, 16, 24, all E3M2 values
+    q, k, v, do, cu = _exact_case([130, 7, 70], 2, 1, 64, seed=18)
+    for x in (q, k):
+        c, s = mx.quantize_d_fp6(x, "e3m2")
+        assert np.array_equal(mx.dequantize_d_fp6(c, s, "e3m2"), x)
+    sc = 2.0 ** -9
+    o3, l3 = mxa.attn_mx_fwd(q, k, v, cu, sc, qk="e3m2")
+    o8, l8 = mxa.attn_mx_fwd(q, k, v, cu, sc)
+    np.testing.assert_array_equal(o3, o8)
+    np.testing.assert_array_equal(l3, l8)
+    for a, b in zip(mxa.attn_mx_bwd(q, k, v, do, cu, sc, qk="e3m2"), mxa.attn_mx_bwd(q, k, v, do, cu, sc)):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_e3m2_oracle_accuracy_order_and_causality():
+    rng = np.random.default_rng(19)
+    cu = np.array([0, 200])
+    mk = lambda h: np.round(rng.standard_normal((200, h, 64)) * 128) / 128
+    q, k, v, do = mk(2), mk(1), mk(1), mk(2)
+    o = {f: mxa.attn_mx_fwd(q, k, v, cu, 0.125, qk=f)[0] for f in ("e4m3", "e2m3", "e3m2", "e2m1")}
+    err = {f: np.linalg.norm(o[f] - o["e4m3"]) for f in o}
+    # two mantissa bits: between E2M3 (three) and E2M1 (one)
+    assert err["e2m3"] < err["e3m2"] < err["e2m1"], err
+    dq, _, _ = mxa.attn_mx_bwd(q, k, v, do, cu, 0.125, qk="e3m2")
+    for j in (0, 31, 32, 128, 150):
+        q2, k2, v2, do2 = q.copy(), k.copy(), v.copy(), do.copy()
+        for a in (q2, k2, v2, do2):
+            a[j] = a[j] * 7.5 + 30.0
+        o5, _ = mxa.attn_mx_fwd(q2, k2, v2, cu, 0.125, qk="e3m2")
+        dq2, _, _ = mxa.attn_mx_bwd(q2, k2, v2, do2, cu, 0.125, qk="e3m2")
+        assert np.array_equal(o5[:j], o["e3m2"][:j]) and np.array_equal(dq2[:j], dq[:j]), j
