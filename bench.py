@@ -22,6 +22,7 @@ on a bounded sample of the same workload on the host cores, and reports its caus
 The same line carries the MX paths on the 65K-token packed workload: ``mxfp8`` (E4M3 operands),
 ``mxfp4`` and ``mxfp6`` (E2M1 / E2M3 score product, the rest as mxfp8), each with its own
 ``roofline``; peaks of mixed-format kernels are n / Σ 1/peak over their counted GEMM units.
+``--mx6-e3m2-workload 4`` adds ``mxfp6_e3m2`` (E3M2 score product), off by default.
 
     python bench.py --decode      # decoding over a packed KV cache: GB/s against HBM peak
 """
@@ -95,6 +96,8 @@ def parse():
                     help="MXFP4/FP8 workload reported under 'mxfp4' (0 = skip)")
     ap.add_argument("--mx6-workload", type=int, default=4, choices=[0, 4, 5],
                     help="MXFP6/FP8 workload reported under 'mxfp6' (0 = skip)")
+    ap.add_argument("--mx6-e3m2-workload", type=int, default=0, choices=[0, 4, 5],
+                    help="MXFP6/FP8 with E3M2 score operands, reported under 'mxfp6_e3m2' (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 3 times (to scale the "
@@ -172,8 +175,9 @@ def measure(w, mx, steps, warmup):
     cu = torch.from_numpy(w.cu_seqlens).to(dev)
     cu_h = torch.from_numpy(w.cu_seqlens)
     T, hq, hkv, d = w.total_tokens, w.hq, w.hkv, w.d
-    dt = {"mxfp4": cfa.CFA_MXFP4, "mxfp6": cfa.CFA_MXFP6}.get(mx, cfa.CFA_MXFP8 if mx else cfa.CFA_BF16)
-    qk_fmt = {"mxfp4": "fp4", "mxfp6": "fp6"}.get(mx, "fp8")
+    dt = {"mxfp4": cfa.CFA_MXFP4, "mxfp6": cfa.CFA_MXFP6, "mxfp6_e3m2": cfa.CFA_MXFP6_E3M2}.get(
+        mx, cfa.CFA_MXFP8 if mx else cfa.CFA_BF16)
+    qk_fmt = {"mxfp4": "fp4", "mxfp6": "fp6", "mxfp6_e3m2": "fp6"}.get(mx, "fp8")
     o = torch.empty_like(q)
     lse = torch.empty((hq, T), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -240,7 +244,7 @@ def measure(w, mx, steps, warmup):
     achieved = dom_flops / (kern[dom]["ms"] * 1e-3) / 1e12
     roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": dom_peak, "unit": "TFLOP/s",
             "frac": achieved / dom_peak,
-            "traffic": traffic_for(dom, w.name.replace("mxfp8", mx) if mx in ("mxfp4", "mxfp6") else w.name),
+            "traffic": traffic_for(dom, w.name.replace("mxfp8", mx) if mx in ("mxfp4", "mxfp6", "mxfp6_e3m2") else w.name),
             "algorithmic_flop_per_launch": dom_flops, "mean_launch_ms": kern[dom]["ms"]}
     res = {"value": value, "ms_per_step": elapsed / K * 1e3, "pct_of_peak": 100.0 * value / peak, "peak": peak,
            "config": {"workload": w.name, "total_tokens": T, "n_docs": w.n_docs, "hq": hq, "hkv": hkv, "d": d,
@@ -385,6 +389,13 @@ def main():
         mres["unit"] = "TFLOP/s"
         mres["peak_note"] = "peaks are n / sum(1/peak) over the counted GEMM units (fp6 10.1, fp8 5.0 PFLOP/s)"
         out["mxfp6"] = mres
+    if args.mx6_e3m2_workload:
+        wm = W.make_workload(args.mx6_e3m2_workload)
+        mres = measure(wm, "mxfp6_e3m2", args.steps, args.warmup)
+        mres["dtype"] = "mxfp6/fp8 (QK^T on E3M2 + E8M0 per 32, the rest as mxfp8)"
+        mres["unit"] = "TFLOP/s"
+        mres["peak_note"] = "peaks are n / sum(1/peak) over the counted GEMM units (fp6 10.1, fp8 5.0 PFLOP/s)"
+        out["mxfp6_e3m2"] = mres
     print(json.dumps(out))
 
 

@@ -16,10 +16,10 @@ import math
 import torch
 
 from . import _lib
-from ._lib import CFA_BF16, CFA_F32, CFA_MXFP4, CFA_MXFP6, CFA_MXFP8, CfaError
+from ._lib import CFA_BF16, CFA_F32, CFA_MXFP4, CFA_MXFP6, CFA_MXFP6_E3M2, CFA_MXFP8, CfaError
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_fwd_cross", "attn_bwd_cross", "attn_decode", "mx_quantize", "mx_quantize_fp4", "mx_quantize_fp6", "workspace_bytes", "saved_bytes", "CfaError",
-           "CFA_F32", "CFA_BF16", "CFA_MXFP8", "CFA_MXFP4", "CFA_MXFP6", "library_path"]
+__all__ = ["attn_fwd", "attn_bwd", "attn_fwd_cross", "attn_bwd_cross", "attn_decode", "mx_quantize", "mx_quantize_fp4", "mx_quantize_fp6", "mx_quantize_fp6_e3m2", "workspace_bytes", "saved_bytes", "CfaError",
+           "CFA_F32", "CFA_BF16", "CFA_MXFP8", "CFA_MXFP4", "CFA_MXFP6", "CFA_MXFP6_E3M2", "library_path"]
 
 
 def library_path():
@@ -44,7 +44,7 @@ def _host_cu(cu_seqlens, cu_seqlens_host):
 
 def _dtype_code(x, mx):
     """mx: False (bf16 / fp32 by x.dtype), True or "mxfp8" (MXFP8), "mxfp4" (MXFP4/FP8),
-    "mxfp6" (MXFP6/FP8)."""
+    "mxfp6" (MXFP6/FP8, E2M3 score operands), "mxfp6_e3m2" (MXFP6/FP8, E3M2 score operands)."""
     if mx:
         if x.dtype != torch.bfloat16:
             raise TypeError("the MX paths take bf16 inputs")
@@ -52,6 +52,8 @@ def _dtype_code(x, mx):
             return CFA_MXFP4
         if mx == "mxfp6":
             return CFA_MXFP6
+        if mx == "mxfp6_e3m2":
+            return CFA_MXFP6_E3M2
         if mx is True or mx == "mxfp8":
             return CFA_MXFP8
         raise ValueError(f"unknown MX path {mx!r}")
@@ -236,10 +238,7 @@ def mx_quantize_fp4(x, *, codes=None, scales=None):
     return codes, scales
 
 
-def mx_quantize_fp6(x, *, codes=None, scales=None):
-    """MXFP6 (E2M3 + E8M0) quantisation of bf16 ``x [T, h, d]`` in blocks of 32 channels.
-    Returns (codes [T, h, 3d/4] uint8 -- per block a 16-byte part, then per block an 8-byte
-    part, see ``mx_quantize_fp6`` in include/cfa.h -- and scales [T, h, d/32] uint8)."""
+def _quantize_fp6(fn, x, codes, scales):
     L = _lib.lib()
     _check_dev(x, codes, scales)
     if x.dtype != torch.bfloat16:
@@ -247,8 +246,20 @@ def mx_quantize_fp6(x, *, codes=None, scales=None):
     T, h, d = x.shape
     codes = torch.empty((T, h, 3 * d // 4), dtype=torch.uint8, device=x.device) if codes is None else codes
     scales = torch.empty((T, h, d // 32), dtype=torch.uint8, device=x.device) if scales is None else scales
-    _lib.check(L.mx_quantize_fp6(_ptr(x), T, h, d, _ptr(codes), _ptr(scales), _stream()))
+    _lib.check(getattr(L, fn)(_ptr(x), T, h, d, _ptr(codes), _ptr(scales), _stream()))
     return codes, scales
+
+
+def mx_quantize_fp6(x, *, codes=None, scales=None):
+    """MXFP6 (E2M3 + E8M0) quantisation of bf16 ``x [T, h, d]`` in blocks of 32 channels.
+    Returns (codes [T, h, 3d/4] uint8 -- per block a 16-byte part, then per block an 8-byte
+    part, see ``mx_quantize_fp6`` in include/cfa.h -- and scales [T, h, d/32] uint8)."""
+    return _quantize_fp6("mx_quantize_fp6", x, codes, scales)
+
+
+def mx_quantize_fp6_e3m2(x, *, codes=None, scales=None):
+    """MXFP6 with E3M2 elements (top exponent 4, largest value 28); storage as ``mx_quantize_fp6``."""
+    return _quantize_fp6("mx_quantize_fp6_e3m2", x, codes, scales)
 
 
 def mx_quantize(x, cu_seqlens, axis, *, cu_seqlens_host=None, t_pad=None, codes=None, scales=None,

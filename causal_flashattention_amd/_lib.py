@@ -9,7 +9,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcfa.so")
 
-CFA_F32, CFA_BF16, CFA_MXFP8, CFA_MXFP4, CFA_MXFP6 = 0, 1, 2, 3, 4
+CFA_F32, CFA_BF16, CFA_MXFP8, CFA_MXFP4, CFA_MXFP6, CFA_MXFP6_E3M2 = 0, 1, 2, 3, 4, 5
 STATUS = {0: "CFA_OK", 1: "CFA_ERR_NULL", 2: "CFA_ERR_SHAPE", 3: "CFA_ERR_UNSUPPORTED",
           4: "CFA_ERR_ALIGN", 5: "CFA_ERR_WORKSPACE", 6: "CFA_ERR_HIP"}
 
@@ -27,6 +27,7 @@ SIGNATURES = {
     "mx_quantize": (_I, [_P, _I, _I, _I, _P, _P, _I, _I, _P, _P, _I, _P, _S, _P]),
     "mx_quantize_fp4": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "mx_quantize_fp6": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "mx_quantize_fp6_e3m2": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "mx_padded_tokens": (_I, [_I, _I]),
     "mx_workspace_bytes": (_S, [_I]),
     "cfa_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I]),

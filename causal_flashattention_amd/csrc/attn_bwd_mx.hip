@@ -91,7 +91,7 @@ struct MxDkdvTile {
 // QF = 1 (MXFP4/FP8 path): the P wave's score product takes E2M1 Q_d rows (64 bytes, swizzled
 // with (row / 4) % 4) and E2M1 K_d registers; QF = 2 (MXFP6/FP8): E2M3 rows, whose 16-byte parts
 // are staged like the E2M1 rows and whose 8-byte parts follow chunk-major (two 16-byte chunks
-// per row); everything else is unchanged.
+// per row); QF = 3: E3M2 in the same storage; everything else is unchanged.
 template <int QF>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
     const uint8_t* __restrict__ qd, const uint8_t* __restrict__ qd_sc, const uint8_t* __restrict__ kd,
@@ -130,7 +130,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
   for (int u = 0; u < 2; ++u) to[u] = 16 * ((2 * u + half) ^ vt_swz(r32));
 #pragma unroll
   for (int s = 0; s < 2; ++s) kq[s] = 16 * ((2 * s + half) ^ vt_swz(r32));
-  constexpr bool FP4 = QF == 1, FP6 = QF == 2;
+  constexpr bool FP4 = QF == 1, FP6 = QF >= 2;   // QF 2, 3: E2M3, E3M2
+  constexpr int F6 = FP6 ? QF : 2;                // 6-bit format code (any valid one when unused)
   constexpr int QROW = FP4 ? 64 : FP6 ? 96 : 128;  // bytes of one Q_d / K_d row in HBM
   const bool narrow_role = QF != 0 && !ds_wave;    // this wave's score operands are E2M1 / E2M3
 
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
       const char* rp = buf + qr * (D / 2);
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        a = mfma32_mx_fp6(fp6_operand(*(const i32x4*)(rp + kq[s]), *(const i32x2*)(buf + 4096 + 16 * (64 * s + qr) + 8 * half)),
+        a = mfma32_mx_fp6<F6>(fp6_operand(*(const i32x4*)(rp + kq[s]), *(const i32x2*)(buf + 4096 + 16 * (64 * s + qr) + 8 * half)),
                           (sc >> (8 * (2 * s + half))) & 0xFF, kvb[s], kvs[s], a);
     } else {
       const char* rp = buf + qr * 128;
@@ -419,7 +420,8 @@ struct MxDqTile {
 };
 
 // QF = 1: the score product takes E2M1 K_d rows (64 bytes, swizzled with (row / 4) % 4) and E2M1
-// Q_d registers; QF = 2: E2M3 rows, their 8-byte parts chunk-major after the 16-byte parts.
+// Q_d registers; QF = 2 (E2M3), 3 (E3M2): 6-bit rows, their 8-byte parts chunk-major after the
+// 16-byte parts.
 template <int QF>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
     const uint8_t* __restrict__ qd, const uint8_t* __restrict__ qd_sc, const uint8_t* __restrict__ kd,
@@ -429,7 +431,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
     int total_tokens, int hq, int hkv, float scale, int causal) {
   using C = MxDqTile;
   constexpr int D = 128, BN = C::BN;
-  constexpr bool FP4 = QF == 1, FP6 = QF == 2;
+  constexpr bool FP4 = QF == 1, FP6 = QF >= 2;   // QF 2, 3: E2M3, E3M2
+  constexpr int F6 = FP6 ? QF : 2;                // 6-bit format code (any valid one when unused)
   constexpr int QROW = FP4 ? 64 : FP6 ? 96 : 128;  // bytes of one Q_d / K_d row in HBM
   __shared__ __attribute__((aligned(16))) char lds_a[C::STAGE];
   __shared__ __attribute__((aligned(16))) char lds_b[C::STAGE];
@@ -526,7 +529,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
         sacc = mfma32_mx_fp4(fp4_operand(*(const i32x4*)(tb + kr * (D / 2) + kq[s])),
                              (ksc >> (8 * (2 * s + half))) & 0xFF, qa[s], qs[s], sacc);
       } else if constexpr (FP6) {
-        sacc = mfma32_mx_fp6(fp6_operand(*(const i32x4*)(tb + kr * (D / 2) + kq[s]),
+        sacc = mfma32_mx_fp6<F6>(fp6_operand(*(const i32x4*)(tb + kr * (D / 2) + kq[s]),
                                          *(const i32x2*)(tb + 4096 + 16 * (64 * s + kr) + 8 * half)),
                              (ksc >> (8 * (2 * s + half))) & 0xFF, qa[s], qs[s], sacc);
       } else {
@@ -621,7 +624,10 @@ hipError_t launch_bwd_dkdv_mx(const MxOperands& m, const void* q, const void* do
   const long grid = ((long)(T + 127) / 128 + plan.n_docs) * hkv;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  auto kern = qf == 1 ? attn_bwd_dkdv_mx_kernel<1> : qf == 2 ? attn_bwd_dkdv_mx_kernel<2> : attn_bwd_dkdv_mx_kernel<0>;
+  auto kern = qf == 1   ? attn_bwd_dkdv_mx_kernel<1>
+              : qf == 2 ? attn_bwd_dkdv_mx_kernel<2>
+              : qf == 3 ? attn_bwd_dkdv_mx_kernel<3>
+                        : attn_bwd_dkdv_mx_kernel<0>;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), 0, stream, m.qd, m.qd_sc, m.kd, m.kd_sc, m.dod, m.dod_sc,
                      m.vd, m.vd_sc, m.dot, m.dot_sc, (const __bf16*)q, (const __bf16*)dout, lse, delta,
                      (__bf16*)dk, (__bf16*)dv, plan, padoff, T, t_pad, hq, hkv, scale, causal);
@@ -636,7 +642,10 @@ hipError_t launch_bwd_dq_mx(const MxOperands& m, const void* k, const float* lse
   const long grid = ((long)(T + 127) / 128 + plan.n_docs) * hq;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  auto kern = qf == 1 ? attn_bwd_dq_mx_kernel<1> : qf == 2 ? attn_bwd_dq_mx_kernel<2> : attn_bwd_dq_mx_kernel<0>;
+  auto kern = qf == 1   ? attn_bwd_dq_mx_kernel<1>
+              : qf == 2 ? attn_bwd_dq_mx_kernel<2>
+              : qf == 3 ? attn_bwd_dq_mx_kernel<3>
+                        : attn_bwd_dq_mx_kernel<0>;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, m.qd, m.qd_sc, m.kd, m.kd_sc, m.dod, m.dod_sc,
                      m.vd, m.vd_sc, (const __bf16*)k, lse, delta, (__bf16*)dq, plan, T, hq, hkv, scale, causal);
   return hipGetLastError();

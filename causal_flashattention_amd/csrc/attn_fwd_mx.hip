@@ -21,7 +21,8 @@
 // instruction with format code 4 on both operands; the rest is the MXFP8 path unchanged.
 // MXFP6/FP8 (QF = 2): E2M3 copies, 96-byte rows whose blocks are a 16-byte part (the first 64
 // bytes, staged and read exactly like the E2M1 rows) and an 8-byte part (the last 32 bytes,
-// staged as two 16-byte chunks per row, chunk-major), format code 2.
+// staged as two 16-byte chunks per row, chunk-major), format code 2. QF = 3: E3M2 copies in
+// the same storage, format code 3.
 //
 // LDS tile (64 keys): K_d codes as 128-byte rows whose 16-byte chunks are XOR-swizzled with
 // (row / 2) % 8 (FP4: 64-byte rows swizzled with (row / 4) % 4), then 4 scale bytes per key; then either the bf16 V rows of a diagonal tile
@@ -46,9 +47,9 @@ template <int QF>
 struct MxFwdTile {
   static constexpr int BN = 64;
   static constexpr int D = 128;
-  static constexpr int KROW = QF == 0 ? D : D / 2;   // bytes of one K_d row (E2M3: its 16-byte parts)
+  static constexpr int KROW = QF == 0 ? D : D / 2;   // bytes of one K_d row (6-bit: its 16-byte parts)
   static constexpr int OFF_KB = BN * KROW;           // K_d codes: 64 rows
-  static constexpr int OFF_KSC = OFF_KB + (QF == 2 ? BN * D / 4 : 0);   // E2M3: 8-byte parts [chunk][row]
+  static constexpr int OFF_KSC = OFF_KB + (QF >= 2 ? BN * D / 4 : 0);   // 6-bit: 8-byte parts [chunk][row]
   static constexpr int OFF_V = OFF_KSC + BN * 4;     // K_d scales: 4 B per key
   static constexpr int OFF_VTSC = OFF_V + D * 64;    // V_t codes: 128 channel rows × 64 B
   static constexpr int STAGE = OFF_V + BN * 256;     // union with the bf16 V rows (64 × 256 B)
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
     const int* __restrict__ padoff, int total_tokens, int t_pad, int hq, int hkv, int n_hb, float scale_log2,
     int causal) {
   using C = MxFwdTile<QF>;
-  constexpr bool FP4 = QF == 1, FP6 = QF == 2, NARROW = QF != 0;
+  constexpr bool FP4 = QF == 1, FP6 = QF >= 2, NARROW = QF != 0;   // QF 2, 3: E2M3, E3M2
   constexpr int QROW = FP4 ? 64 : FP6 ? 96 : 128;     // bytes of one Q_d / K_d row in HBM
   constexpr int D = C::D;
   constexpr int BMW = 128 / HPW;
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
             sacc[b] = mfma32_mx_fp4(fp4_operand(*(const i32x4*)(kr + ko[s][0])), sa, qa[s], qs[s], sacc[b]);
           } else if constexpr (FP6) {
             const i32x2 hi = *(const i32x2*)(tb + C::OFF_KB + 16 * (64 * s + 32 * b + r32) + 8 * half);
-            sacc[b] = mfma32_mx_fp6(fp6_operand(*(const i32x4*)(kr + ko[s][0]), hi), sa, qa[s], qs[s], sacc[b]);
+            sacc[b] = mfma32_mx_fp6<QF>(fp6_operand(*(const i32x4*)(kr + ko[s][0]), hi), sa, qa[s], qs[s], sacc[b]);
           } else {
             const i32x4 lo = *(const i32x4*)(kr + ko[s][0]);
             const i32x4 hi = *(const i32x4*)(kr + ko[s][1]);
@@ -322,6 +323,10 @@ hipError_t launch_fwd_mx(const uint8_t* qd, const uint8_t* qd_sc, const uint8_t*
     if (hpw == 4) CFA_MXF_LAUNCH(4, 2);
     else if (hpw == 2) CFA_MXF_LAUNCH(2, 2);
     else CFA_MXF_LAUNCH(1, 2);
+  } else if (qf == 3) {
+    if (hpw == 4) CFA_MXF_LAUNCH(4, 3);
+    else if (hpw == 2) CFA_MXF_LAUNCH(2, 3);
+    else CFA_MXF_LAUNCH(1, 3);
   } else {
     if (hpw == 4) CFA_MXF_LAUNCH(4, 0);
     else if (hpw == 2) CFA_MXF_LAUNCH(2, 0);

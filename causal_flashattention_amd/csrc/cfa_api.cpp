@@ -60,16 +60,19 @@ struct Sizes {
   int T, n_docs, hq, hkv, d, dtype;
 };
 
+bool is_mx(int dtype) {
+  return dtype == CFA_MXFP8 || dtype == CFA_MXFP4 || dtype == CFA_MXFP6 || dtype == CFA_MXFP6_E3M2;
+}
+
 int check_sizes(const Sizes& s, bool bwd) {
   if (s.T < 0) return fail(CFA_ERR_SHAPE, "total_tokens = %d < 0", s.T);
   if (s.n_docs < 1) return fail(CFA_ERR_SHAPE, "n_docs = %d < 1", s.n_docs);
   if (s.hq < 1 || s.hkv < 1) return fail(CFA_ERR_SHAPE, "hq = %d, hkv = %d must be >= 1", s.hq, s.hkv);
   if (s.hq % s.hkv) return fail(CFA_ERR_SHAPE, "hq = %d is not a multiple of hkv = %d", s.hq, s.hkv);
   if ((long)s.T * s.hq * s.d > 0x7fffffffL * 8L) return fail(CFA_ERR_SHAPE, "tensor too large");
-  if (s.dtype != CFA_F32 && s.dtype != CFA_BF16 && s.dtype != CFA_MXFP8 && s.dtype != CFA_MXFP4 &&
-      s.dtype != CFA_MXFP6)
+  if (s.dtype != CFA_F32 && s.dtype != CFA_BF16 && !is_mx(s.dtype))
     return fail(CFA_ERR_UNSUPPORTED, "dtype %d unknown", s.dtype);
-  if (s.dtype == CFA_MXFP8 || s.dtype == CFA_MXFP4 || s.dtype == CFA_MXFP6) {
+  if (is_mx(s.dtype)) {
     if (s.d != 128) return fail(CFA_ERR_UNSUPPORTED, "the MX paths support d = 128 only (got %d)", s.d);
   } else if (s.dtype == CFA_F32 && s.d != 64 && s.d != 128) {
     return fail(CFA_ERR_UNSUPPORTED, "the fp32 path supports d = 64 or 128 (got %d)", s.d);
@@ -87,16 +90,17 @@ struct MxBuf {
 
 int t_pad_of(const Sizes& s) { return (s.T + 31) / 32 * 32 + 32 * s.n_docs; }
 
-bool is_mx(int dtype) { return dtype == CFA_MXFP8 || dtype == CFA_MXFP4 || dtype == CFA_MXFP6; }
+// element format of the score product's copies: 0 = E4M3, 1 = E2M1, 2 = E2M3, 3 = E3M2 (for the
+// 6-bit types, the matrix instruction's format code)
+int score_format(int dtype) {
+  return dtype == CFA_MXFP4 ? 1 : dtype == CFA_MXFP6 ? 2 : dtype == CFA_MXFP6_E3M2 ? 3 : 0;
+}
 
-// element format of the score product's copies: 0 = E4M3, 1 = E2M1, 2 = E2M3
-int score_format(int dtype) { return dtype == CFA_MXFP4 ? 1 : dtype == CFA_MXFP6 ? 2 : 0; }
-
-// d-blocked copy of a [T, h, d] tensor: codes [T, h, d] (E2M1: [T, h, d/2]; E2M3: [T, h, 3d/4]),
+// d-blocked copy of a [T, h, d] tensor: codes [T, h, d] (E2M1: [T, h, d/2]; 6-bit: [T, h, 3d/4]),
 // scales [T, h, d/32]
 size_t add_mx_d(size_t off, const Sizes& s, int h, MxBuf& b, int qf = 0) {
   b.codes = off;
-  off = cfa::align256(off + (size_t)s.T * h * (qf == 1 ? s.d / 2 : qf == 2 ? 3 * s.d / 4 : s.d));
+  off = cfa::align256(off + (size_t)s.T * h * (qf == 1 ? s.d / 2 : qf >= 2 ? 3 * s.d / 4 : s.d));
   b.scales = off;
   return cfa::align256(off + (size_t)s.T * h * (s.d / 32));
 }
@@ -150,7 +154,8 @@ WsLayout ws_layout(int pass, const Sizes& s) {
   return w;
 }
 
-// forward-to-backward buffer of the MX paths: Q_d and K_d (E4M3, E2M1 for CFA_MXFP4, E2M3 for CFA_MXFP6)
+// forward-to-backward buffer of the MX paths: Q_d and K_d (E4M3, E2M1 for CFA_MXFP4, E2M3 for CFA_MXFP6,
+// E3M2 for CFA_MXFP6_E3M2)
 struct SavedLayout {
   MxBuf qd, kd;
   size_t total;
@@ -245,7 +250,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, c
     const int qf = score_format(dtype);
     auto quant_d = [&](const void* x, long n, uint8_t* c, uint8_t* sc, hipStream_t str) {
       return qf == 1 ? cfa::launch_mx_quantize_d_fp4(x, n, c, sc, str)
-           : qf == 2 ? cfa::launch_mx_quantize_d_fp6(x, n, d, c, sc, str)
+           : qf >= 2 ? cfa::launch_mx_quantize_d_fp6(x, n, d, qf, c, sc, str)
                      : cfa::launch_mx_quantize_d(x, n, c, sc, str);
     };
     mark(1, 0, st);
@@ -526,16 +531,28 @@ int mx_quantize_fp4(const void* x, int total_tokens, int h, int d, uint8_t* code
                    "mx_quantize_d_fp4");
 }
 
-int mx_quantize_fp6(const void* x, int total_tokens, int h, int d, uint8_t* codes, uint8_t* scales, void* stream) {
+namespace {
+int quantize_fp6(const char* name, int fmt, const void* x, int total_tokens, int h, int d, uint8_t* codes,
+                 uint8_t* scales, void* stream) {
   g_err[0] = 0;
   if (total_tokens < 0 || h < 1) return fail(CFA_ERR_SHAPE, "total_tokens = %d, h = %d", total_tokens, h);
-  if (d != 64 && d != 128) return fail(CFA_ERR_UNSUPPORTED, "mx_quantize_fp6 supports d = 64 or 128 (got %d)", d);
+  if (d != 64 && d != 128) return fail(CFA_ERR_UNSUPPORTED, "%s supports d = 64 or 128 (got %d)", name, d);
   if (total_tokens > 0 && (!x || !codes || !scales)) return fail(CFA_ERR_NULL, "x, codes and scales must not be NULL");
   for (const void* p : {x, (const void*)codes})
     if (!aligned(p, 16)) return fail(CFA_ERR_ALIGN, "x and codes must be 16-byte aligned");
   if (total_tokens == 0) return CFA_OK;
-  return check_hip(cfa::launch_mx_quantize_d_fp6(x, (long)total_tokens * h * d, d, codes, scales, (hipStream_t)stream),
-                   "mx_quantize_d_fp6");
+  return check_hip(
+      cfa::launch_mx_quantize_d_fp6(x, (long)total_tokens * h * d, d, fmt, codes, scales, (hipStream_t)stream), name);
+}
+}  // namespace
+
+int mx_quantize_fp6(const void* x, int total_tokens, int h, int d, uint8_t* codes, uint8_t* scales, void* stream) {
+  return quantize_fp6("mx_quantize_fp6", 2, x, total_tokens, h, d, codes, scales, stream);
+}
+
+int mx_quantize_fp6_e3m2(const void* x, int total_tokens, int h, int d, uint8_t* codes, uint8_t* scales,
+                         void* stream) {
+  return quantize_fp6("mx_quantize_fp6_e3m2", 3, x, total_tokens, h, d, codes, scales, stream);
 }
 
 // ---------------------------------------------------------------- decoding over a KV cache

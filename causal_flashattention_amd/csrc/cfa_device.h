@@ -119,12 +119,15 @@ __device__ inline f32x16 mfma32_mx_fp4(i32x8 a, int sa, i32x8 b, int sb, f32x16 
 }
 __device__ inline i32x8 fp4_operand(i32x4 u) { return i32x8{u.x, u.y, u.z, u.w, 0, 0, 0, 0}; }
 
-// Scaled MFMA with E2M3 (FP6, format code 2) A and B: per lane l, row/column l%32, k = 32·(l/32)
-// + i for the code at bits 6i..6i+5 of the 192-bit little-endian operand in dwords 0-5 (pinned
-// by a probe against a CPU product with per-block scales); scales as above. The operand is
+// Scaled MFMA with 6-bit A and B, FMT = the instruction's format code: 2 = E2M3, 3 = E3M2. Per
+// lane l, row/column l%32, k = 32·(l/32) + i for the code at bits 6i..6i+5 of the 192-bit
+// little-endian operand in dwords 0-5 (pinned for E2M3 by a probe against a CPU product with
+// per-block scales; E3M2 differs only in how a code decodes); scales as above. The operand is
 // assembled from a block's 16-byte part (dwords 0-3) and 8-byte part (dwords 4-5).
+template <int FMT>
 __device__ inline f32x16 mfma32_mx_fp6(i32x8 a, int sa, i32x8 b, int sb, f32x16 c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 2, 0, sa, 0, sb);
+  static_assert(FMT == 2 || FMT == 3, "6-bit format codes are 2 (E2M3) and 3 (E3M2)");
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 0, sa, 0, sb);
 }
 __device__ inline i32x8 fp6_operand(i32x4 lo, i32x2 hi) { return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, 0, 0}; }
 

@@ -62,8 +62,9 @@ hipError_t launch_decode_combine(const float* part_o, const void* part_ml, void*
 hipError_t launch_mx_quantize_d(const void* x, long n_elems, uint8_t* codes, uint8_t* scales, hipStream_t stream);
 // E2M1 codes packed two per byte ([n_elems / 2] bytes), E8M0 scales [n_elems / 32].
 hipError_t launch_mx_quantize_d_fp4(const void* x, long n_elems, uint8_t* codes, uint8_t* scales, hipStream_t stream);
-// E2M3 codes [n_elems/d rows][3d/4 bytes] (each block of 32 as a 16-byte and an 8-byte part)
-hipError_t launch_mx_quantize_d_fp6(const void* x, long n_elems, int d, uint8_t* codes, uint8_t* scales,
+// 6-bit codes [n_elems/d rows][3d/4 bytes] (each block of 32 as a 16-byte and an 8-byte part);
+// fmt = MFMA format code: 2 = E2M3, 3 = E3M2
+hipError_t launch_mx_quantize_d_fp6(const void* x, long n_elems, int d, int fmt, uint8_t* codes, uint8_t* scales,
                                     hipStream_t stream);
 
 // kernel_layout: the attention kernels' internal token-blocked layout (pieces of 4 tokens in

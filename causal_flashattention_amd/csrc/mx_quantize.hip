@@ -134,12 +134,34 @@ __device__ inline int e2m3_code(float y) {
   return c | (__builtin_signbit(y) ? 32 : 0);
 }
 
+// E3M2 (FP6) element of an already-scaled value |y| <= 28: four codes per binade [2^t, 2^(t+1))
+// for t >= -2 (step 2^(t-2)), and step 1/16 on [0, 0.5) (subnormals and the first binade), so
+// code = round(|y|·2^(2-t)) + 4t + 8 with t = max(floor(log2 |y|), -2); a round-up to the next
+// power of two lands on that binade's first code. rintf ties to even, and 4t + 8 is even, so
+// ties go to the even code. Every product is exact (scaling by a power of two).
+__device__ inline int e3m2_code(float y) {
+  const float a = fabsf(y);
+  const int t = a < 0.25f ? -2 : __builtin_amdgcn_frexp_expf(a) - 1;
+  const int c = (int)rintf(__builtin_amdgcn_ldexpf(a, 2 - t)) + 4 * t + 8;
+  return c | (__builtin_signbit(y) ? 32 : 0);
+}
+
+// Block exponent with top exponent EMAX: floor(log2 amax) - EMAX clamped to [-127, 127], -127
+// for a zero block.
+template <int EMAX>
+__device__ inline int mx_exponent_top(float amax) {
+  if (!(amax > 0.f)) return -127;
+  const int ex = __builtin_amdgcn_frexp_expf(amax);
+  return min(max(ex - 1 - EMAX, -127), 127);
+}
+
 // Two lanes per block of 32 elements, 16 elements (96 code bits) each. Block b of a row is the
 // 192-bit little-endian number whose bits 6i..6i+5 hold code i; its bytes 0-15 go to the row's
 // 16-byte part [16b, 16b+16), bytes 16-23 to its 8-byte part [d/2 + 8b, d/2 + 8b + 8); a row
 // (one token and head) is 3d/4 bytes. Lane 0 owns bytes 0-11 (one 12-byte store), lane 1 bytes
-// 12-23 (4 bytes ending the 16-byte part, 8 bytes the 8-byte part). Same block rule as E2M1
-// (top exponent 2).
+// 12-23 (4 bytes ending the 16-byte part, 8 bytes the 8-byte part). FMT 2: E2M3 (top exponent
+// 2, saturation at 7.5); FMT 3: E3M2 (top exponent 4, saturation at 28).
+template <int FMT>
 __global__ __launch_bounds__(256) void mx_quantize_d_fp6_kernel(const __bf16* __restrict__ x,
                                                                 uint8_t* __restrict__ codes,
                                                                 uint8_t* __restrict__ scales, long n_blocks, int nb) {
@@ -167,12 +189,14 @@ __global__ __launch_bounds__(256) void mx_quantize_d_fp6_kernel(const __bf16* __
   int badi = bad ? 1 : 0;
   badi |= __shfl_xor(badi, 1);
   if (blk >= n_blocks) return;
-  const int e = mx_exponent_fp4(amax);           // E2M3 and E2M1 share the top exponent 2
+  constexpr float VMAX = FMT == 2 ? 7.5f : 28.f;
+  const int e = mx_exponent_top<FMT == 2 ? 2 : 4>(amax);
   uint32_t w[3] = {0u, 0u, 0u};                  // this lane's 96 code bits, little endian
   if (!badi) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const uint32_t c = (uint32_t)e2m3_code(fminf(fmaxf(__builtin_amdgcn_ldexpf(v[j], -e), -7.5f), 7.5f));
+      const float y = fminf(fmaxf(__builtin_amdgcn_ldexpf(v[j], -e), -VMAX), VMAX);
+      const uint32_t c = (uint32_t)(FMT == 2 ? e2m3_code(y) : e3m2_code(y));
       const int bit = 6 * j;
       w[bit >> 5] |= c << (bit & 31);
       if ((bit & 31) > 26) w[(bit >> 5) + 1] |= c >> (32 - (bit & 31));   // a code across two words
@@ -298,14 +322,15 @@ hipError_t launch_mx_quantize_d_fp4(const void* x, long n_elems, uint8_t* codes,
   return hipGetLastError();
 }
 
-hipError_t launch_mx_quantize_d_fp6(const void* x, long n_elems, int d, uint8_t* codes, uint8_t* scales,
+hipError_t launch_mx_quantize_d_fp6(const void* x, long n_elems, int d, int fmt, uint8_t* codes, uint8_t* scales,
                                     hipStream_t stream) {
   const long n_blocks = n_elems / 32;
   if (n_blocks == 0) return hipSuccess;
+  if (fmt != 2 && fmt != 3) return hipErrorInvalidValue;
   const long grid = (n_blocks + 127) / 128;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(mx_quantize_d_fp6_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)x, codes,
-                     scales, n_blocks, d / 32);
+  hipLaunchKernelGGL(fmt == 2 ? mx_quantize_d_fp6_kernel<2> : mx_quantize_d_fp6_kernel<3>, dim3((unsigned)grid),
+                     dim3(256), 0, stream, (const __bf16*)x, codes, scales, n_blocks, d / 32);
   return hipGetLastError();
 }
 

@@ -53,8 +53,16 @@ extern "C" {
 
 /* CFA_MXFP4: the MXFP8 path with the score product QK^T on E2M1 copies of Q and K (mx_quantize_fp4),
  * a reading of the mixed NVFP4/FP8 path the FLAMIA page names ("FLAMIA Mimarisi ve Temel Tasarım
- * İlkeleri"). CFA_MXFP6: the same with E2M3 copies (mx_quantize_fp6). */
-typedef enum { CFA_F32 = 0, CFA_BF16 = 1, CFA_MXFP8 = 2, CFA_MXFP4 = 3, CFA_MXFP6 = 4 } cfa_dtype;
+ * İlkeleri"). CFA_MXFP6: the same with E2M3 copies (mx_quantize_fp6); CFA_MXFP6_E3M2: with E3M2
+ * copies (mx_quantize_fp6_e3m2), the other 6-bit MX element type. */
+typedef enum {
+  CFA_F32 = 0,
+  CFA_BF16 = 1,
+  CFA_MXFP8 = 2,
+  CFA_MXFP4 = 3,
+  CFA_MXFP6 = 4,
+  CFA_MXFP6_E3M2 = 5
+} cfa_dtype;
 
 typedef enum {
   CFA_OK = 0,
@@ -90,8 +98,9 @@ size_t cfa_saved_bytes(int total_tokens, int n_docs, int hq, int hkv, int d, int
  *   scale      : multiplier of Q K^T (usually 1/sqrt(d)); finite and > 0.
  *   dtype      : CFA_F32 (d = 64 or 128), CFA_BF16 (d = 64, 128 or 256; 256 is FlashAttention-2's
  *                extension, "FlashAttention (HU)", FlashAttention-2 (2023)), CFA_MXFP8 (d = 128).
- *                CFA_MXFP4 / CFA_MXFP6 (d = 128): as CFA_MXFP8 with an E2M1 / E2M3 score product.
- *   saved      : CFA_MXFP8 / CFA_MXFP4 / CFA_MXFP6: cfa_saved_bytes() bytes written here for attn_bwd;
+ *                CFA_MXFP4 / CFA_MXFP6 / CFA_MXFP6_E3M2 (d = 128): as CFA_MXFP8 with an E2M1 / E2M3
+ *                / E3M2 score product.
+ *   saved      : the MX dtypes: cfa_saved_bytes() bytes written here for attn_bwd;
  *                otherwise NULL.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -103,7 +112,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 /*
  * Backward pass: dq, dk, dv (same layouts and element type as q, k, v) from q, k, v, the
  * forward's o and lse, and the upstream gradients dout (of O) and dlse (of LSE). dtype CFA_BF16,
- * CFA_MXFP8, CFA_MXFP4 or CFA_MXFP6 (CFA_F32 is forward-only).
+ * CFA_MXFP8, CFA_MXFP4, CFA_MXFP6 or CFA_MXFP6_E3M2 (CFA_F32 is forward-only).
  *   dlse  : float32 [hq, total_tokens] like lse, or NULL for no gradient into lse. The pages do
  *           not name it; it is the exact derivative of the lse output the forward returns:
  *           d lse_i / d S_ij = P_ij, so it enters as dS_ij = P_ij (dP_ij - (D_i - dlse_i)) with
@@ -186,6 +195,15 @@ int mx_quantize_fp4(const void* x, int total_tokens, int h, int d, uint8_t* code
  * operands of the CFA_MXFP6 attention path are these copies of Q and K.
  */
 int mx_quantize_fp6(const void* x, int total_tokens, int h, int d, uint8_t* codes, uint8_t* scales, void* stream);
+/*
+ * The same quantiser and storage with E3M2 elements (1 sign, 3 exponent bits with bias 3, 2
+ * mantissa bits; magnitudes 0..0.4375 in steps of 1/16, then four per binade [2^k, 2^(k+1)) up
+ * to 16, 20, 24, 28): e = floor(log2 amax) - 4, elements saturated to +-28 and rounded to the
+ * nearest E3M2 value (ties to the even code). Matrix-core format code 3. The score operands of
+ * the CFA_MXFP6_E3M2 attention path are these copies of Q and K.
+ */
+int mx_quantize_fp6_e3m2(const void* x, int total_tokens, int h, int d, uint8_t* codes, uint8_t* scales,
+                         void* stream);
 /* Upper bound of P_{n_docs} for any cu_seqlens with these sizes, rounded up to 32:
  * 32*ceil(total_tokens/32) + 32*n_docs. */
 int mx_padded_tokens(int total_tokens, int n_docs);

@@ -111,3 +111,23 @@ def test_mx_quantize_fp6_bit_exact(d):
         rc, rs = mx.quantize_d_fp6(W.bf16_bits_to_f64(xin))
         assert np.array_equal(c.cpu().numpy(), mx.pack_fp6(rc))
         assert np.array_equal(s.cpu().numpy(), rs)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_mx_quantize_fp6_e3m2_bit_exact(d):
+    """E3M2 codes (packed) and scale bytes bit-identical to the reference, special values included;
+    plus a tensor whose scaled elements sit exactly on E3M2 midpoints (ties to the even code)."""
+    T, h = 97, 3
+    xb = _special_tensor(T, h, d, seed=60 + d)
+    rng = np.random.default_rng(61)
+    grid = np.concatenate([np.arange(4) / 16.0, [2.0 ** k * (1 + m / 4) for k in range(-2, 5) for m in range(4)]])
+    mids = np.concatenate([(grid[:-1] + grid[1:]) / 2, -(grid[:-1] + grid[1:]) / 2, grid, [0.0]]).astype(np.float32)
+    xm = rng.choice(mids, size=(T, h, d)).astype(np.float32)
+    xm[:, :, ::32] = 28.0                      # block max 28: e = 0, elements are the midpoints themselves
+    for xin in (xb, W.f32_to_bf16_bits(xm)):
+        announce("mx_quantize_fp6_e3m2", d)
+        c, s = cfa.mx_quantize_fp6_e3m2(to_dev(xin))
+        torch.cuda.synchronize()
+        rc, rs = mx.quantize_d_fp6(W.bf16_bits_to_f64(xin), "e3m2")
+        assert np.array_equal(c.cpu().numpy(), mx.pack_fp6(rc))
+        assert np.array_equal(s.cpu().numpy(), rs)
