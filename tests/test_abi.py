@@ -62,7 +62,8 @@ def _fwd(**over):
     (dict(q=None), 1), (dict(cu=None), 1), (dict(ws=None), 1),
     (dict(hkv=3), 2), (dict(n_docs=0), 2), (dict(T=-1), 2), (dict(scale=float("nan")), 2), (dict(scale=0.0), 2),
     (dict(d=96), 3), (dict(dtype=7), 3), (dict(dtype=2, d=64), 3), (dict(dtype=0, d=256), 3),
-    (dict(dtype=2, d=256), 3),
+    (dict(dtype=2, d=256), 3), (dict(dtype=3, d=64), 3), (dict(dtype=4, d=64), 3), (dict(dtype=5, d=64), 3),
+    (dict(dtype=6), 3),
     (dict(q=FAKE + 8), 4), (dict(ws=FAKE + 16), 4),
     (dict(wsb=16), 5),
 ])
@@ -128,3 +129,20 @@ def test_decode_rejects():
     assert call(wsb=64) == 5
     assert L.cfa_decode_workspace_bytes(2, 100, 8, 2, 128, 2) > 0
     assert L.cfa_decode_workspace_bytes(2, 100, 8, 2, 96, 2) == 0
+
+
+def test_narrow_mx_sizes_and_quantiser_rejects():
+    L = _lib.lib()
+    # saved buffer: Q_d and K_d copies; E2M1 rows d/2 bytes, both 6-bit types 3d/4, E4M3 d
+    sb = {dt: L.cfa_saved_bytes(4096, 3, 8, 2, 128, dt) for dt in (2, 3, 4, 5)}
+    assert sb[4] == sb[5] and sb[3] < sb[4] < sb[2]
+    assert L.cfa_saved_bytes(4096, 3, 8, 2, 128, 1) == 0          # bf16 saves nothing
+    assert L.cfa_saved_bytes(4096, 3, 8, 2, 64, 5) == 0           # the MX paths take d = 128 only
+    for fn in (L.mx_quantize_fp4, L.mx_quantize_fp6, L.mx_quantize_fp6_e3m2):
+        assert fn(FAKE, 100, 2, 96, FAKE, FAKE, None) == 3        # head dim
+        assert fn(FAKE, -1, 2, 128, FAKE, FAKE, None) == 2        # negative token count
+        assert fn(None, 100, 2, 128, FAKE, FAKE, None) == 1       # NULL input
+        assert fn(FAKE + 8, 100, 2, 128, FAKE, FAKE, None) == 4   # misaligned input
+        assert fn(FAKE, 0, 2, 128, FAKE, FAKE, None) == 0         # nothing to do: no launch
+        assert L.cfa_last_error() is not None
+
