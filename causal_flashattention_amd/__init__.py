@@ -74,6 +74,40 @@ def _check_dev(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _expect(t, shape, dtype, name):
+    """Metadata check of an optional tensor argument (the library sees only pointers and sizes)."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+
+
+def _check_qkv(q, k, v, same_tokens):
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q, k, v must be [tokens, heads, head_dim]")
+    _expect(v, k.shape, k.dtype, "v")
+    if k.dtype != q.dtype:
+        raise TypeError(f"k: dtype {k.dtype}, q: {q.dtype}")
+    if k.shape[2] != q.shape[2] or (same_tokens and k.shape[0] != q.shape[0]):
+        raise ValueError(f"k {tuple(k.shape)} does not match q {tuple(q.shape)}")
+
+
+def _check_cu(cu, name="cu_seqlens"):
+    if cu.dtype != torch.int32 or cu.dim() != 1 or cu.numel() < 2:
+        raise ValueError(f"{name} must be int32 [n_docs + 1]")
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _at_least(t, n, name):
+    if t is not None and _nbytes(t) < n:
+        raise ValueError(f"{name} holds {_nbytes(t)} bytes, needs {n}")
+
+
 def workspace_bytes(pass_, total_tokens, n_docs, hq, hkv, d, dtype):
     return _lib.lib().cfa_workspace_bytes(pass_, total_tokens, n_docs, hq, hkv, d, dtype)
 
@@ -86,11 +120,17 @@ def attn_fwd(q, k, v, cu_seqlens, *, scale=None, causal=True, cu_seqlens_host=No
              mx=False, out=None, lse=None, saved=None, workspace=None):
     """Forward pass. Returns (o, lse, saved); ``saved`` is None unless ``mx``."""
     L = _lib.lib()
-    _check_dev(q, k, v, cu_seqlens)
+    _check_qkv(q, k, v, True)
+    _check_cu(cu_seqlens)
     T, hq, d = q.shape
     hkv = k.shape[1]
     n_docs = cu_seqlens.numel() - 1
     dt = _dtype_code(q, mx)
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, (hq, T), torch.float32, "lse")
+    if mx:
+        _at_least(saved, L.cfa_saved_bytes(T, n_docs, hq, hkv, d, dt), "saved")
+    _check_dev(q, k, v, cu_seqlens, out, lse, saved, workspace)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dev = q.device
     if out is None:
@@ -106,7 +146,7 @@ def attn_fwd(q, k, v, cu_seqlens, *, scale=None, causal=True, cu_seqlens_host=No
     _lib.check(L.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens),
                           _ptr(hcu) if hcu is not None else None, n_docs, T, int(max_seqlen), hq, hkv, d,
                           scale, int(bool(causal)), dt, _ptr(saved) if mx else None, _ptr(workspace),
-                          workspace.numel(), _stream()))
+                          _nbytes(workspace), _stream()))
     return out, lse, saved
 
 
@@ -117,13 +157,23 @@ def attn_bwd(q, k, v, o, lse, dout, cu_seqlens, *, scale=None, causal=True, cu_s
     ``dlse`` (float32 ``[hq, T]``, optional) is the gradient flowing into the forward's lse.
     """
     L = _lib.lib()
-    _check_dev(q, k, v, o, lse, dout, cu_seqlens, saved, dlse)
-    if dlse is not None and (dlse.dtype != torch.float32 or dlse.shape != lse.shape):
-        raise ValueError("dlse must be float32 with the shape of lse")
+    _check_qkv(q, k, v, True)
+    _check_cu(cu_seqlens)
     T, hq, d = q.shape
     hkv = k.shape[1]
     n_docs = cu_seqlens.numel() - 1
     dt = _dtype_code(q, mx)
+    for t, name in ((o, "o"), (dout, "dout"), (dq, "dq")):
+        _expect(t, q.shape, q.dtype, name)
+    for t, name in ((dk, "dk"), (dv, "dv")):
+        _expect(t, k.shape, k.dtype, name)
+    _expect(lse, (hq, T), torch.float32, "lse")
+    _expect(dlse, (hq, T), torch.float32, "dlse")
+    if mx:
+        if saved is None:
+            raise ValueError("the MX paths need the forward's saved buffer")
+        _at_least(saved, L.cfa_saved_bytes(T, n_docs, hq, hkv, d, dt), "saved")
+    _check_dev(q, k, v, o, lse, dout, cu_seqlens, saved, dlse, dq, dk, dv, workspace)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
@@ -136,7 +186,7 @@ def attn_bwd(q, k, v, o, lse, dout, cu_seqlens, *, scale=None, causal=True, cu_s
                           _ptr(dlse) if dlse is not None else None, _ptr(saved) if saved is not None else None, _ptr(dq), _ptr(dk), _ptr(dv),
                           _ptr(cu_seqlens), _ptr(hcu) if hcu is not None else None, n_docs, T,
                           int(max_seqlen), hq, hkv, d, scale, int(bool(causal)), dt, _ptr(workspace),
-                          workspace.numel(), _stream()))
+                          _nbytes(workspace), _stream()))
     return dq, dk, dv
 
 
@@ -145,11 +195,18 @@ def attn_fwd_cross(q, k, v, cu_seqlens_q, cu_seqlens_k, *, scale=None, causal=Tr
     """Cross-attention forward (bf16): query documents on their own key/value documents.
     ``q [Tq, hq, d]``, ``k, v [Tk, hkv, d]``. Returns (o, lse [hq, Tq])."""
     L = _lib.lib()
-    _check_dev(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    _check_qkv(q, k, v, False)
+    _check_cu(cu_seqlens_q, "cu_seqlens_q")
+    _check_cu(cu_seqlens_k, "cu_seqlens_k")
+    if cu_seqlens_k.numel() != cu_seqlens_q.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must list the same number of documents")
     if q.dtype != torch.bfloat16:
         raise TypeError("cross-attention takes bf16 inputs")
     Tq, hq, d = q.shape
     Tk, hkv = k.shape[0], k.shape[1]
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, (hq, Tq), torch.float32, "lse")
+    _check_dev(q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse, workspace)
     n_docs = cu_seqlens_q.numel() - 1
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     out = torch.empty_like(q) if out is None else out
@@ -161,7 +218,7 @@ def attn_fwd_cross(q, k, v, cu_seqlens_q, cu_seqlens_k, *, scale=None, causal=Tr
     _lib.check(L.attn_fwd_cross(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
                                 _ptr(cu_seqlens_k), _ptr(hq_cu) if hq_cu is not None else None,
                                 _ptr(hk_cu) if hk_cu is not None else None, n_docs, Tq, Tk, hq, hkv, d, scale,
-                                int(bool(causal)), _ptr(workspace), workspace.numel(), _stream()))
+                                int(bool(causal)), _ptr(workspace), _nbytes(workspace), _stream()))
     return out, lse
 
 
@@ -170,9 +227,20 @@ def attn_bwd_cross(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, *, scale=N
                    workspace=None):
     """Cross-attention backward (bf16). Returns (dq, dk, dv)."""
     L = _lib.lib()
-    _check_dev(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, dlse)
+    _check_qkv(q, k, v, False)
+    _check_cu(cu_seqlens_q, "cu_seqlens_q")
+    _check_cu(cu_seqlens_k, "cu_seqlens_k")
+    if cu_seqlens_k.numel() != cu_seqlens_q.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must list the same number of documents")
     Tq, hq, d = q.shape
     Tk, hkv = k.shape[0], k.shape[1]
+    for t, name in ((o, "o"), (dout, "dout"), (dq, "dq")):
+        _expect(t, q.shape, q.dtype, name)
+    for t, name in ((dk, "dk"), (dv, "dv")):
+        _expect(t, k.shape, k.dtype, name)
+    _expect(lse, (hq, Tq), torch.float32, "lse")
+    _expect(dlse, (hq, Tq), torch.float32, "dlse")
+    _check_dev(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, dlse, dq, dk, dv, workspace)
     n_docs = cu_seqlens_q.numel() - 1
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dq = torch.empty_like(q) if dq is None else dq
@@ -186,7 +254,7 @@ def attn_bwd_cross(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, *, scale=N
                                 _ptr(dlse) if dlse is not None else None, _ptr(dq), _ptr(dk), _ptr(dv),
                                 _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(hq_cu) if hq_cu is not None else None,
                                 _ptr(hk_cu) if hk_cu is not None else None, n_docs, Tq, Tk, hq, hkv, d, scale,
-                                int(bool(causal)), _ptr(workspace), workspace.numel(), _stream()))
+                                int(bool(causal)), _ptr(workspace), _nbytes(workspace), _stream()))
     return dq, dk, dv
 
 
@@ -196,9 +264,21 @@ def attn_decode(q, k_cache, v_cache, cu_seqlens_k, *, k_scales=None, v_scales=No
     ``[Tk, hkv, d]`` is bf16, or uint8 E4M3 codes with ``k_scales, v_scales [Tk, hkv, d/32]``
     uint8 E8M0 bytes. Returns (o [B, hq, d] bf16, lse [hq, B] float32)."""
     L = _lib.lib()
-    _check_dev(q, k_cache, v_cache, cu_seqlens_k, k_scales, v_scales)
+    if q.dim() != 3 or k_cache.dim() != 3:
+        raise ValueError("q [n_seqs, hq, d] and the caches [total_k, hkv, d] must be 3-D")
+    _expect(v_cache, k_cache.shape, k_cache.dtype, "v_cache")
+    if k_cache.shape[2] != q.shape[2]:
+        raise ValueError(f"cache {tuple(k_cache.shape)} does not match q {tuple(q.shape)}")
+    _check_cu(cu_seqlens_k, "cu_seqlens_k")
     B, hq, d = q.shape
     Tk, hkv = k_cache.shape[0], k_cache.shape[1]
+    if cu_seqlens_k.numel() != B + 1:
+        raise ValueError(f"cu_seqlens_k has {cu_seqlens_k.numel()} entries for {B} sequences")
+    for t, name in ((k_scales, "k_scales"), (v_scales, "v_scales")):
+        _expect(t, (Tk, hkv, d // 32), torch.uint8, name)
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, (hq, B), torch.float32, "lse")
+    _check_dev(q, k_cache, v_cache, cu_seqlens_k, k_scales, v_scales, out, lse, workspace)
     if q.dtype != torch.bfloat16:
         raise TypeError("q must be bf16")
     if k_cache.dtype == torch.uint8:
@@ -220,7 +300,7 @@ def attn_decode(q, k_cache, v_cache, cu_seqlens_k, *, k_scales=None, v_scales=No
     hcu = _host_cu(cu_seqlens_k, cu_seqlens_k_host)
     _lib.check(L.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales), _ptr(out),
                              _ptr(lse), _ptr(cu_seqlens_k), _ptr(hcu) if hcu is not None else None, B, Tk, hq, hkv,
-                             d, scale, kv, _ptr(workspace), workspace.numel(), _stream()))
+                             d, scale, kv, _ptr(workspace), _nbytes(workspace), _stream()))
     return out, lse
 
 
@@ -228,10 +308,12 @@ def mx_quantize_fp4(x, *, codes=None, scales=None):
     """MXFP4 (E2M1 + E8M0) quantisation of bf16 ``x [T, h, d]`` in blocks of 32 channels.
     Returns (codes [T, h, d/2] uint8, two per byte, scales [T, h, d/32] uint8)."""
     L = _lib.lib()
-    _check_dev(x, codes, scales)
-    if x.dtype != torch.bfloat16:
-        raise TypeError("x must be bf16")
+    if x.dtype != torch.bfloat16 or x.dim() != 3:
+        raise TypeError("x must be bf16 [T, h, d]")
     T, h, d = x.shape
+    _expect(codes, (T, h, d // 2), torch.uint8, "codes")
+    _expect(scales, (T, h, d // 32), torch.uint8, "scales")
+    _check_dev(x, codes, scales)
     codes = torch.empty((T, h, d // 2), dtype=torch.uint8, device=x.device) if codes is None else codes
     scales = torch.empty((T, h, d // 32), dtype=torch.uint8, device=x.device) if scales is None else scales
     _lib.check(L.mx_quantize_fp4(_ptr(x), T, h, d, _ptr(codes), _ptr(scales), _stream()))
@@ -240,10 +322,12 @@ def mx_quantize_fp4(x, *, codes=None, scales=None):
 
 def _quantize_fp6(fn, x, codes, scales):
     L = _lib.lib()
-    _check_dev(x, codes, scales)
-    if x.dtype != torch.bfloat16:
-        raise TypeError("x must be bf16")
+    if x.dtype != torch.bfloat16 or x.dim() != 3:
+        raise TypeError("x must be bf16 [T, h, d]")
     T, h, d = x.shape
+    _expect(codes, (T, h, 3 * d // 4), torch.uint8, "codes")
+    _expect(scales, (T, h, d // 32), torch.uint8, "scales")
+    _check_dev(x, codes, scales)
     codes = torch.empty((T, h, 3 * d // 4), dtype=torch.uint8, device=x.device) if codes is None else codes
     scales = torch.empty((T, h, d // 32), dtype=torch.uint8, device=x.device) if scales is None else scales
     _lib.check(getattr(L, fn)(_ptr(x), T, h, d, _ptr(codes), _ptr(scales), _stream()))
@@ -270,19 +354,26 @@ def mx_quantize(x, cu_seqlens, axis, *, cu_seqlens_host=None, t_pad=None, codes=
     [h, d, t_pad] / [h, d, t_pad/32] for axis 1 (t_pad defaults to the size bound).
     """
     L = _lib.lib()
-    _check_dev(x, cu_seqlens)
-    if x.dtype != torch.bfloat16:
-        raise TypeError("mx_quantize takes bf16 input")
+    if x.dtype != torch.bfloat16 or x.dim() != 3:
+        raise TypeError("mx_quantize takes bf16 input [T, h, d]")
+    _check_cu(cu_seqlens)
     T, h, d = x.shape
     n_docs = cu_seqlens.numel() - 1
+    if axis == 0:
+        _expect(codes, (T, h, d), torch.uint8, "codes")
+        _expect(scales, (T, h, d // 32), torch.uint8, "scales")
+    else:
+        if t_pad is None:
+            t_pad = L.mx_padded_tokens(T, n_docs)
+        _expect(codes, (h, d, t_pad), torch.uint8, "codes")
+        _expect(scales, (h, d, t_pad // 32), torch.uint8, "scales")
+    _check_dev(x, cu_seqlens, codes, scales, workspace)
     dev = x.device
     if axis == 0:
         t_pad = 0
         codes = torch.empty((T, h, d), dtype=torch.uint8, device=dev) if codes is None else codes
         scales = torch.empty((T, h, d // 32), dtype=torch.uint8, device=dev) if scales is None else scales
     else:
-        if t_pad is None:
-            t_pad = L.mx_padded_tokens(T, n_docs)
         codes = torch.zeros((h, d, t_pad), dtype=torch.uint8, device=dev) if codes is None else codes
         scales = torch.zeros((h, d, t_pad // 32), dtype=torch.uint8, device=dev) if scales is None else scales
         if workspace is None:
@@ -291,5 +382,5 @@ def mx_quantize(x, cu_seqlens, axis, *, cu_seqlens_host=None, t_pad=None, codes=
     _lib.check(L.mx_quantize(_ptr(x), T, h, d, _ptr(cu_seqlens), _ptr(hcu) if hcu is not None else None,
                              n_docs, axis, _ptr(codes), _ptr(scales), int(t_pad),
                              _ptr(workspace) if workspace is not None else None,
-                             workspace.numel() if workspace is not None else 0, _stream()))
+                             _nbytes(workspace) if workspace is not None else 0, _stream()))
     return codes, scales
