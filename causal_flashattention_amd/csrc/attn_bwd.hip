@@ -192,7 +192,7 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
     if (threadIdx.x < BM) {
       float* lb = (float*)(buf + 2 * TILE);
       lb[threadIdx.x] = lreg * LOG2E;
-      lb[BM + threadIdx.x] = dreg;
+      lb[BM + threadIdx.x] = -dreg;               // -D: the dP accumulator starts from it
     }
   };
   auto active = [&](int st) {
@@ -267,14 +267,21 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
     }
   };
 
-  // dS wave, step st (one iteration after its P wave): per 32-query block, dP, dS = P (dP − D)
-  // with the bf16 P of its partner, dKᵀ += Qᵀ dS
+  // dS wave, step st (one iteration after its P wave): per 32-query block, dP − D (the product
+  // accumulates onto −D, read from the stage as the accumulator's start), dS = P (dP − D) with the
+  // bf16 P of its partner, dKᵀ += Qᵀ dS
   auto step_ds = [&](int st, const char* buf, const i32x4* xr) __attribute__((always_inline)) {
     const char* ob = buf + TILE;
     const f32x4* db = (const f32x4*)(buf + 2 * TILE + BM * 4);
 #pragma unroll
     for (int qb = 0; qb < QBS; ++qb) {
-      f32x16 pacc = f32x16{};
+      f32x16 pacc;                                // element 4jj + u: query 32qb + 8jj + 4·half + u
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 nd = db[8 * qb + 2 * jj + half];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) pacc[4 * jj + u] = nd[u];
+      }
 #pragma unroll
       for (int sc = 0; sc < C::DS; sc += SB) {
         i32x4 fo[SB];
@@ -299,10 +306,9 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {             // word e: rows of jj = 2u + e/2, values (e%2)·2, +1
           const int jj = 2 * u + (e >> 1), j0 = 4 * jj + 2 * (e & 1);
-          const f32x4 dd = db[8 * qb + 2 * jj + half];
           const float p0 = __builtin_bit_cast(float, (uint32_t)pw[e] << 16);
           const float p1 = __builtin_bit_cast(float, (uint32_t)pw[e] & 0xFFFF0000u);
-          us[e] = (int)pack_bf16x2(p0 * (pacc[j0] - dd[2 * (e & 1)]), p1 * (pacc[j0 + 1] - dd[2 * (e & 1) + 1]));
+          us[e] = (int)pack_bf16x2(p0 * pacc[j0], p1 * pacc[j0 + 1]);
         }
         sf[u] = __builtin_bit_cast(bf16x8, us);
       }
