@@ -214,14 +214,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
     }
   };
   auto stage_finish = [&](char* buf) {
-    if (pair == 1) ((float*)(buf + C::OFF_ROW))[lane] = ds_wave ? rreg : rreg * LOG2E;
+    if (pair == 1) ((float*)(buf + C::OFF_ROW))[lane] = ds_wave ? -rreg : rreg * LOG2E;   // dS wave: -D
   };
 
-  // scores of 32-query block qb of the step against this pair's keys (A = d-blocked rows)
-  auto dscores = [&](const char* buf, int qb) __attribute__((always_inline)) {
+  // scores of 32-query block qb of the step against this pair's keys (A = d-blocked rows),
+  // accumulated onto a0
+  auto dscores = [&](const char* buf, int qb, f32x16 a0) __attribute__((always_inline)) {
     const int qr = 32 * qb + r32;
     const int sc = *(const int*)(buf + C::OFF_SC + qr * 4);
-    f32x16 a = f32x16{};
+    f32x16 a = a0;
     if (FP4 && narrow_role) {
       const char* rp = buf + qr * (D / 2);
 #pragma unroll
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
     int psc = 127;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      f32x16 x = dscores(buf, qb);
+      f32x16 x = dscores(buf, qb, f32x16{});
       if (masked) {
         // element j holds query qb0 + 8(j/4) + j%4: masked below lo (causal) or above hi
         const int qb0 = q0 + 32 * qb + 4 * half;
@@ -313,26 +314,33 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
     }
   };
 
-  // dS wave, step st (one iteration after its P wave); the query blocks one after the other
+  // dS wave, step st (one iteration after its P wave); the query blocks one after the other.
+  // The dP product accumulates onto -D (stored negated in the stage), so x = dP - D.
   auto step_ds = [&](int st, const char* buf, const i32x4* xr) __attribute__((always_inline)) {
     const f32x4* dd = (const f32x4*)(buf + C::OFF_ROW);
     bf16x8 sf[4];                               // bf16 dS, B operands of the dK product
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      f32x16 x = dscores(buf, qb);              // dP
+      f32x16 nd;                                // element 4m + c: query 32qb + 8m + 4·half + c
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f32x4 v4 = dd[8 * qb + 2 * m + half];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) nd[4 * m + c] = v4[c];
+      }
+      f32x16 x = dscores(buf, qb, nd);          // dP - D
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const i32x4 pw = xr[(pair * 4 + 2 * qb + u) * 64 + lane];
         i32x4 us;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-          const f32x4 dr = dd[8 * qb + 2 * (2 * u + jj) + half];
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const uint32_t word = (uint32_t)pw[2 * jj + e];
             const int j = 8 * u + 4 * jj + 2 * e;
-            us[2 * jj + e] = (int)pack_bf16x2(__builtin_bit_cast(float, word << 16) * (x[j] - dr[2 * e]),
-                                              __builtin_bit_cast(float, word & 0xFFFF0000u) * (x[j + 1] - dr[2 * e + 1]));
+            us[2 * jj + e] = (int)pack_bf16x2(__builtin_bit_cast(float, word << 16) * x[j],
+                                              __builtin_bit_cast(float, word & 0xFFFF0000u) * x[j + 1]);
           }
         }
         sf[2 * qb + u] = __builtin_bit_cast(bf16x8, us);
