@@ -237,6 +237,11 @@ def measure(w, mx, steps, warmup):
     unit_flops = w.flops_fwd() / 2.0
     kern = {n: {"ms": float(np.mean([a.elapsed_time(b) for a, b in ev[n]])), "units": u}
             for n, (_, _, u) in kernels.items()}
+    # per-step spread from the same events: first forward kernel's start to the last backward
+    # kernel's end (the forward's plan launch, ~13 us, precedes the span)
+    first = "mx_quantize_fwd" if mx else "attn_fwd_bf16_kernel"      # launch order, not event slot
+    last = "attn_bwd_dq_mx_kernel" if mx else "attn_bwd_dq_kernel"
+    spans = [ev[first][i][0].elapsed_time(ev[last][i][1]) for i in range(K)]
     dom = max(kern, key=lambda n: kern[n]["ms"])
     dom_flops = kern[dom]["units"] * unit_flops
     peak = mixed_peak(MX_STEP_FORMATS, qk_fmt) if mx else PEAK_TFLOPS["bf16"]
@@ -246,7 +251,10 @@ def measure(w, mx, steps, warmup):
             "frac": achieved / dom_peak,
             "traffic": traffic_for(dom, w.name.replace("mxfp8", mx) if mx in ("mxfp4", "mxfp6", "mxfp6_e3m2") else w.name),
             "algorithmic_flop_per_launch": dom_flops, "mean_launch_ms": kern[dom]["ms"]}
-    res = {"value": value, "ms_per_step": elapsed / K * 1e3, "pct_of_peak": 100.0 * value / peak, "peak": peak,
+    res = {"value": value, "ms_per_step": elapsed / K * 1e3,
+           "step_ms_events": {"median": float(np.median(spans)), "min": float(np.min(spans)),
+                              "max": float(np.max(spans))},
+           "pct_of_peak": 100.0 * value / peak, "peak": peak,
            "config": {"workload": w.name, "total_tokens": T, "n_docs": w.n_docs, "hq": hq, "hkv": hkv, "d": d,
                       "causal": True, "seed": w.info["seed"], "causal_tflop_per_step": flops / 1e12},
            "kernels_ms": {n: round(kern[n]["ms"], 4) for n in kern}, "roofline": roof}
@@ -365,6 +373,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "pct_of_peak": head["pct_of_peak"],
         "config": head["config"], "kernels_ms": head["kernels_ms"], "roofline": head["roofline"],
+        "step_ms_events": head["step_ms_events"],
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
