@@ -87,9 +87,9 @@ const char* cfa_last_error(void);
  * on the sizes, never on the values of cu_seqlens. Returns 0 for invalid sizes. */
 size_t cfa_workspace_bytes(int pass, int total_tokens, int n_docs, int hq, int hkv, int d, int dtype);
 
-/* Bytes of the forward-to-backward buffer `saved` (the MX dtypes only: the d-blocked E4M3, E2M1
- * or E2M3 copies of Q and K with their scales, reused by the backward so both passes see
- * identical scores). 0 for the other dtypes. */
+/* Bytes of the forward-to-backward buffer `saved` (the MX dtypes only: the d-blocked E4M3, E2M1,
+ * E2M3 or E3M2 copies of Q and K with their scales, reused by the backward so both passes see
+ * identical scores). 0 for the other dtypes and for invalid sizes. */
 size_t cfa_saved_bytes(int total_tokens, int n_docs, int hq, int hkv, int d, int dtype);
 
 /*
