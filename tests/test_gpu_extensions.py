@@ -160,3 +160,23 @@ def test_head_dim_256_determinism_isolation_causality():
         r3 = _run(w, dev2, False)
         assert torch.equal(r3[0][:j], r1[0][:j]), jl       # O of earlier queries
         assert torch.equal(r3[2][:j], r1[2][:j]), jl       # dQ of earlier queries
+
+
+@pytest.mark.parametrize("mx,qk", [("mxfp4", "e2m1"), ("mxfp6", "e2m3"), ("mxfp6_e3m2", "e3m2")])
+def test_narrow_mx_mqa_with_lse_gradient(mx, qk):
+    """The narrow score formats on MQA (16 query heads, one kv head) with a dlse input, against
+    the MX oracle with the same score format."""
+    lengths = [700, 129, 1, 300]
+    w = W.make_random(seed=340, lengths=lengths, hq=16, hkv=1, causal=True)
+    dlse = _dlse(w, seed=341)
+    announce("mqa narrow mx fwd+bwd dlse", lengths, mx)
+    dev = upload(w)
+    o, lse, dq, dk, dv = _run(w, dev, mx, dlse)
+    ro, rl = mxa.attn_mx_fwd(w.f64("q"), w.f64("k"), w.f64("v"), w.cu_seqlens, w.scale, qk=qk)
+    assert rel_l2(to_f64(o), ro) <= MX_TOL
+    assert np.max(np.abs(to_f64(lse) - rl)) <= LSE_TOL
+    g = mxa.attn_mx_bwd(w.f64("q"), w.f64("k"), w.f64("v"), w.f64("do"), w.cu_seqlens, w.scale,
+                        dlse=dlse.astype(np.float64), qk=qk)
+    errs = [rel_l2(to_f64(a), b) for a, b in zip((dq, dk, dv), g)]
+    print("rel-L2 dq dk dv", errs)
+    assert max(errs) <= MX_TOL, errs
