@@ -44,6 +44,22 @@ def test_fp32_single_document():
     assert np.max(np.abs(to_f64(lse) - rl)) <= 1e-5
 
 
+@pytest.mark.parametrize("lengths,hq,hkv,d,causal", [
+    ([1, 5, 64, 127, 129, 300], 2, 2, 128, True),
+    ([77, 256, 33, 1], 4, 2, 64, True),
+    ([100, 257], 2, 1, 128, False),
+])
+def test_fp32_random_documents(lengths, hq, hkv, d, causal):
+    """The fp32 path beyond workload 1: packed ragged documents, GQA, d = 64 and 128, non-causal."""
+    w = W.make_random(seed=700 + sum(lengths), lengths=lengths, hq=hq, hkv=hkv, d=d, dtype="f32", causal=causal)
+    announce("fwd fp32 random", lengths, hq, hkv, d, causal)
+    o, lse = _fwd(w, upload(w))
+    assert o.dtype == torch.float32
+    ro, rl = ref.attn_fwd(w.f64("q"), w.f64("k"), w.f64("v"), w.cu_seqlens, w.scale, causal)
+    assert np.max(np.abs(to_f64(o) - ro)) <= 1e-5
+    assert np.max(np.abs(to_f64(lse) - rl)) <= 1e-5
+
+
 @pytest.mark.parametrize("lengths,hq,hkv,d", [
     ([1, 5, 64, 127, 129, 300], 2, 2, 128),
     ([513, 31, 200], 8, 2, 128),
