@@ -18,7 +18,7 @@ import torch
 from . import _lib
 from ._lib import CFA_BF16, CFA_F32, CFA_MXFP4, CFA_MXFP6, CFA_MXFP6_E3M2, CFA_MXFP8, CfaError
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_fwd_cross", "attn_bwd_cross", "attn_decode", "mx_quantize", "mx_quantize_fp4", "mx_quantize_fp6", "mx_quantize_fp6_e3m2", "workspace_bytes", "saved_bytes", "CfaError",
+__all__ = ["attn_fwd", "attn_bwd", "device_error", "attn_fwd_cross", "attn_bwd_cross", "attn_decode", "mx_quantize", "mx_quantize_fp4", "mx_quantize_fp6", "mx_quantize_fp6_e3m2", "workspace_bytes", "saved_bytes", "CfaError",
            "CFA_F32", "CFA_BF16", "CFA_MXFP8", "CFA_MXFP4", "CFA_MXFP6", "CFA_MXFP6_E3M2", "library_path"]
 
 
@@ -106,6 +106,16 @@ def _nbytes(t):
 def _at_least(t, n, name):
     if t is not None and _nbytes(t) < n:
         raise ValueError(f"{name} holds {_nbytes(t)} bytes, needs {n}")
+
+
+def device_error(workspace):
+    """The validation flag the last call left in ``workspace`` (synchronises the current stream):
+    0 for a well-formed device cu_seqlens, else bit 0 = cu[0] != 0, bit 1 = a decreasing entry,
+    bit 2 = cu[n_docs] != total_tokens (every document was then treated as empty)."""
+    _check_dev(workspace)
+    flag = ctypes.c_int(-1)
+    _lib.check(_lib.lib().cfa_device_error(_ptr(workspace), _stream(), ctypes.byref(flag)))
+    return flag.value
 
 
 def workspace_bytes(pass_, total_tokens, n_docs, hq, hkv, d, dtype):
@@ -348,10 +358,12 @@ def mx_quantize_fp6_e3m2(x, *, codes=None, scales=None):
 
 def mx_quantize(x, cu_seqlens, axis, *, cu_seqlens_host=None, t_pad=None, codes=None, scales=None,
                 workspace=None):
-    """MX-quantise bf16 ``x [T, h, d]``. axis 0: blocks along d; axis 1: doc-local token blocks.
+    """MX-quantise bf16 ``x [T, h, d]``. axis 0: blocks along d; axis 1: doc-local token blocks;
+    axis 2: the same token blocks in the attention kernels' internal layout.
 
-    Returns (codes uint8, scales uint8): [T, h, d] / [T, h, d/32] for axis 0, and
-    [h, d, t_pad] / [h, d, t_pad/32] for axis 1 (t_pad defaults to the size bound).
+    Returns (codes uint8, scales uint8): [T, h, d] / [T, h, d/32] for axis 0,
+    [h, d, t_pad] / [h, d, t_pad/32] for axis 1 and [h, d, t_pad] / [h, t_pad/32, d] for axis 2
+    (t_pad defaults to the size bound).
     """
     L = _lib.lib()
     if x.dtype != torch.bfloat16 or x.dim() != 3:
@@ -365,8 +377,9 @@ def mx_quantize(x, cu_seqlens, axis, *, cu_seqlens_host=None, t_pad=None, codes=
     else:
         if t_pad is None:
             t_pad = L.mx_padded_tokens(T, n_docs)
+        sshape = (h, t_pad // 32, d) if axis == 2 else (h, d, t_pad // 32)
         _expect(codes, (h, d, t_pad), torch.uint8, "codes")
-        _expect(scales, (h, d, t_pad // 32), torch.uint8, "scales")
+        _expect(scales, sshape, torch.uint8, "scales")
     _check_dev(x, cu_seqlens, codes, scales, workspace)
     dev = x.device
     if axis == 0:
@@ -375,7 +388,7 @@ def mx_quantize(x, cu_seqlens, axis, *, cu_seqlens_host=None, t_pad=None, codes=
         scales = torch.empty((T, h, d // 32), dtype=torch.uint8, device=dev) if scales is None else scales
     else:
         codes = torch.zeros((h, d, t_pad), dtype=torch.uint8, device=dev) if codes is None else codes
-        scales = torch.zeros((h, d, t_pad // 32), dtype=torch.uint8, device=dev) if scales is None else scales
+        scales = torch.zeros(sshape, dtype=torch.uint8, device=dev) if scales is None else scales
         if workspace is None:
             workspace = torch.empty(max(L.mx_workspace_bytes(n_docs), 256), dtype=torch.uint8, device=dev)
     hcu = _host_cu(cu_seqlens, cu_seqlens_host)

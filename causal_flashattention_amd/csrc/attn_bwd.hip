@@ -383,13 +383,15 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
 }
 
 // Sum of the head-split partial sums in split order: dK = scale·Σ_s part_dk[s], dV = Σ_s part_dv[s]
-// (bf16). One lane per 4 consecutive elements.
+// (bf16). One lane per 4 consecutive elements. Nothing is written when the plan flagged a
+// malformed cu_seqlens (every document empty: no partial sum was produced).
 __global__ __launch_bounds__(256) void dkdv_split_reduce_kernel(const float* __restrict__ part_dk,
                                                                 const float* __restrict__ part_dv,
                                                                 __bf16* __restrict__ dk, __bf16* __restrict__ dv,
-                                                                long n, int n_split, float scale) {
+                                                                long n, int n_split, float scale,
+                                                                const int* __restrict__ flag) {
   const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i >= n) return;
+  if (i >= n || *flag != 0) return;
   f32x4 a = *(const f32x4*)(part_dk + i), b = *(const f32x4*)(part_dv + i);
   for (int sp = 1; sp < n_split; ++sp) {
     a += *(const f32x4*)(part_dk + (size_t)sp * n + i);
@@ -632,7 +634,7 @@ static hipError_t launch_dkdv_d(const void* q, const void* k, const void* v, con
                          (__bf16*)dk, (__bf16*)dv, plan, T, hq, hkv, scale, causal, 1, pdk, pdv, qdoc, Tk);
     if (n_split > 1 && n > 0)
       hipLaunchKernelGGL(dkdv_split_reduce_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, stream, pdk,
-                         pdv, (__bf16*)dk, (__bf16*)dv, n, n_split, scale);
+                         pdv, (__bf16*)dk, (__bf16*)dv, n, n_split, scale, plan.header);
   }
   return hipGetLastError();
 }

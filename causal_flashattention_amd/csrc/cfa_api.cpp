@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "cfa.h"
@@ -32,6 +33,13 @@ int fail(int status, const char* fmt, ...) {
   vsnprintf(g_err, sizeof g_err, fmt, ap);
   va_end(ap);
   return status;
+}
+
+// CFA_SCHED=naive: documents in index order instead of longest first (a diagnostic that shows
+// the scheduler's effect; results are bit-identical either way).
+bool sched_naive() {
+  const char* e = getenv("CFA_SCHED");
+  return e && strcmp(e, "naive") == 0;
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -74,6 +82,10 @@ int check_sizes(const Sizes& s, bool bwd) {
     return fail(CFA_ERR_UNSUPPORTED, "dtype %d unknown", s.dtype);
   if (is_mx(s.dtype)) {
     if (s.d != 128) return fail(CFA_ERR_UNSUPPORTED, "the MX paths support d = 128 only (got %d)", s.d);
+    // token-blocked rows are addressed as channel·t_pad + column in 32 bits
+    if ((long)((s.T + 31) / 32 * 32 + 32L * s.n_docs) * s.d > 0x7fffffffL)
+      return fail(CFA_ERR_UNSUPPORTED, "the MX paths need d·(32·ceil(T/32) + 32·n_docs) < 2^31 (T = %d, n_docs = %d)",
+                  s.T, s.n_docs);
   } else if (s.dtype == CFA_F32 && s.d != 64 && s.d != 128) {
     return fail(CFA_ERR_UNSUPPORTED, "the fp32 path supports d = 64 or 128 (got %d)", s.d);
   } else if (s.d != 64 && s.d != 128 && s.d != 256) {
@@ -175,6 +187,7 @@ cfa::Plan make_plan(void* ws, int n_docs) {
   cfa::PlanLayout pl(n_docs);
   char* b = (char*)ws;
   cfa::Plan p;
+  p.header = (const int*)(b + pl.header);
   p.docinfo = (const int2*)(b + pl.docinfo);
   p.order = (const int*)(b + pl.order);
   p.pref = (const int*)(b + pl.pref);
@@ -237,7 +250,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, c
   if (int st = check_cu_host(cu_seqlens_host, n_docs, total_tokens, max_seqlen)) return st;
 
   hipStream_t st = (hipStream_t)stream;
-  if (int r = check_hip(cfa::launch_plan(cu_seqlens, n_docs, total_tokens, workspace, st), "plan kernel")) return r;
+  if (int r = check_hip(cfa::launch_plan(cu_seqlens, n_docs, total_tokens, workspace, st, sched_naive()), "plan kernel")) return r;
   if (total_tokens == 0) return CFA_OK;
   const cfa::Plan plan = make_plan(workspace, n_docs);
   hipError_t e;
@@ -304,7 +317,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   if (int st = check_cu_host(cu_seqlens_host, n_docs, total_tokens, max_seqlen)) return st;
 
   hipStream_t st = (hipStream_t)stream;
-  if (int r = check_hip(cfa::launch_plan(cu_seqlens, n_docs, total_tokens, workspace, st), "plan kernel")) return r;
+  if (int r = check_hip(cfa::launch_plan(cu_seqlens, n_docs, total_tokens, workspace, st, sched_naive()), "plan kernel")) return r;
   if (total_tokens == 0) return CFA_OK;
   const cfa::Plan plan = make_plan(workspace, n_docs);
   float* delta = (float*)((char*)workspace + wl.delta);
@@ -372,7 +385,7 @@ int mx_quantize(const void* x, int total_tokens, int h, int d, const int32_t* cu
   g_err[0] = 0;
   if (total_tokens < 0 || h < 1) return fail(CFA_ERR_SHAPE, "total_tokens = %d, h = %d", total_tokens, h);
   if (d != 64 && d != 128) return fail(CFA_ERR_UNSUPPORTED, "mx_quantize supports d = 64 or 128 (got %d)", d);
-  if (axis != 0 && axis != 1) return fail(CFA_ERR_SHAPE, "axis must be 0 or 1 (got %d)", axis);
+  if (axis < 0 || axis > 2) return fail(CFA_ERR_SHAPE, "axis must be 0, 1 or 2 (got %d)", axis);
   if (total_tokens > 0 && (!x || !codes || !scales)) return fail(CFA_ERR_NULL, "x, codes and scales must not be NULL");
   for (const void* p : {x, (const void*)codes})
     if (!aligned(p, 16)) return fail(CFA_ERR_ALIGN, "x and codes must be 16-byte aligned");
@@ -382,7 +395,8 @@ int mx_quantize(const void* x, int total_tokens, int h, int d, const int32_t* cu
     return check_hip(cfa::launch_mx_quantize_d(x, (long)total_tokens * h * d, codes, scales, st), "mx_quantize_d");
   }
   if (n_docs < 1) return fail(CFA_ERR_SHAPE, "n_docs = %d < 1", n_docs);
-  if (!cu_seqlens || !workspace) return fail(CFA_ERR_NULL, "cu_seqlens and workspace must not be NULL for axis 1");
+  if (!cu_seqlens || !workspace) return fail(CFA_ERR_NULL, "cu_seqlens and workspace must not be NULL for axes 1, 2");
+  if ((long)t_pad * d > 0x7fffffffL) return fail(CFA_ERR_UNSUPPORTED, "t_pad·d must stay below 2^31");
   if (t_pad % 32 || t_pad < mx_padded_tokens(total_tokens, n_docs))
     return fail(CFA_ERR_SHAPE, "t_pad = %d must be a multiple of 32 and >= %d", t_pad,
                 mx_padded_tokens(total_tokens, n_docs));
@@ -390,9 +404,10 @@ int mx_quantize(const void* x, int total_tokens, int h, int d, const int32_t* cu
   if (workspace_bytes < mx_workspace_bytes(n_docs))
     return fail(CFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, mx_workspace_bytes(n_docs));
   if (int r = check_cu_host(cu_seqlens_host, n_docs, total_tokens, 0)) return r;
-  if (int r = check_hip(cfa::launch_plan(cu_seqlens, n_docs, total_tokens, workspace, st), "plan kernel")) return r;
+  if (int r = check_hip(cfa::launch_plan(cu_seqlens, n_docs, total_tokens, workspace, st, sched_naive()), "plan kernel")) return r;
   if (total_tokens == 0) return CFA_OK;
-  return check_hip(cfa::launch_mx_quantize_t(x, total_tokens, h, d, workspace, n_docs, codes, scales, t_pad, false, st),
+  return check_hip(cfa::launch_mx_quantize_t(x, total_tokens, h, d, workspace, n_docs, codes, scales, t_pad, axis == 2,
+                                             st),
                    "mx_quantize_t");
 }
 
@@ -456,8 +471,8 @@ int attn_fwd_cross(const void* q, const void* k, const void* v, void* o, float* 
   if (int st = check_cu_host(cu_seqlens_q_host, n_docs, total_q, 0)) return st;
   if (int st = check_cu_host(cu_seqlens_k_host, n_docs, total_k, 0)) return st;
   hipStream_t st = (hipStream_t)stream;
-  if (int r = check_hip(cfa::launch_plan(cu_seqlens_q, n_docs, total_q, workspace, st), "plan kernel (queries)")) return r;
-  if (int r = check_hip(cfa::launch_plan(cu_seqlens_k, n_docs, total_k, (char*)workspace + cl.plan_k, st),
+  if (int r = check_hip(cfa::launch_plan(cu_seqlens_q, n_docs, total_q, workspace, st, sched_naive()), "plan kernel (queries)")) return r;
+  if (int r = check_hip(cfa::launch_plan(cu_seqlens_k, n_docs, total_k, (char*)workspace + cl.plan_k, st, sched_naive()),
                         "plan kernel (keys)"))
     return r;
   if (total_q == 0) return CFA_OK;
@@ -491,8 +506,8 @@ int attn_bwd_cross(const void* q, const void* k, const void* v, const void* o, c
   if (int st = check_cu_host(cu_seqlens_q_host, n_docs, total_q, 0)) return st;
   if (int st = check_cu_host(cu_seqlens_k_host, n_docs, total_k, 0)) return st;
   hipStream_t st = (hipStream_t)stream;
-  if (int r = check_hip(cfa::launch_plan(cu_seqlens_q, n_docs, total_q, workspace, st), "plan kernel (queries)")) return r;
-  if (int r = check_hip(cfa::launch_plan(cu_seqlens_k, n_docs, total_k, (char*)workspace + cl.plan_k, st),
+  if (int r = check_hip(cfa::launch_plan(cu_seqlens_q, n_docs, total_q, workspace, st, sched_naive()), "plan kernel (queries)")) return r;
+  if (int r = check_hip(cfa::launch_plan(cu_seqlens_k, n_docs, total_k, (char*)workspace + cl.plan_k, st, sched_naive()),
                         "plan kernel (keys)"))
     return r;
   const cfa::Plan pq = make_plan(workspace, n_docs);
@@ -609,7 +624,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const u
   if (int st = check_cu_host(cu_seqlens_k_host, n_seqs, total_k, 0)) return st;
 
   hipStream_t st = (hipStream_t)stream;
-  if (int r = check_hip(cfa::launch_plan(cu_seqlens_k, n_seqs, total_k, workspace, st), "plan kernel")) return r;
+  if (int r = check_hip(cfa::launch_plan(cu_seqlens_k, n_seqs, total_k, workspace, st, sched_naive()), "plan kernel")) return r;
   const cfa::Plan plan = make_plan(workspace, n_seqs);
   float* part_o = (float*)((char*)workspace + dl.part_o);
   void* part_ml = (char*)workspace + dl.part_ml;

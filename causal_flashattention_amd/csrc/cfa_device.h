@@ -20,7 +20,8 @@ constexpr float LN2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------- workspace layout
 // All sections 256-byte aligned. The plan part is shared by every pass:
-//   header   int[64]              flag (bit0 cu[0]!=0, bit1 decreasing, bit2 cu[n]!=T), spare
+//   header   int[64]              flag (bit0 cu[0]!=0, bit1 decreasing, bit2 cu[n]!=T;
+//                                  non-zero: every document was made empty), spare
 //   docinfo  int2[n_docs]         (first packed row, length) after clamping
 //   order    int[n_docs]          documents sorted by length, longest first
 //   pref     int[4][n_docs+1]     item prefix over `order` for tiles of 32, 64, 128, 256 rows
@@ -40,6 +41,7 @@ struct PlanLayout {
 };
 
 struct Plan {
+  const int* header;     // header[0]: the validation flag (non-zero: every document is empty)
   const int2* docinfo;
   const int* order;
   const int* pref;  // prefix for the kernel's tile size, n_docs+1 entries

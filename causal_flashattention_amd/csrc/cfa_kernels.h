@@ -12,7 +12,9 @@ struct MxOperands {
   const uint8_t *dot, *dot_sc;
 };
 
-hipError_t launch_plan(const int* cu, int n_docs, int total_tokens, void* ws, hipStream_t stream);
+// naive: documents in index order (a diagnostic for the scheduler's effect); otherwise longest
+// first, ties by document index.
+hipError_t launch_plan(const int* cu, int n_docs, int total_tokens, void* ws, hipStream_t stream, bool naive = false);
 
 // kdoc != nullptr: cross-attention; the plan is built on the query documents and kdoc[n] =
 // (first key row, key count) of document n.

@@ -2,9 +2,16 @@
 //
 // Documents are independent and a document's tiles cost up to its length, so long documents
 // go first (workload-aware scheduling over packed documents: FLAMIA page, "FLAMIA Mimarisi ve
-// Temel Tasarım İlkeleri"). Documents are bucketed by ceil(L/128) (capped), bucket order is
-// descending; the order inside a bucket is whatever the atomics give: it only decides *which*
-// workgroup computes a tile, never how, so results stay bit-identical between runs.
+// Temel Tasarım İlkeleri"). Documents are bucketed by ceil(L/128) (capped); buckets run in
+// descending order and documents of one bucket in ascending index order (a stable counting
+// sort), so the schedule itself is a function of cu_seqlens alone. The order only decides
+// *which* workgroup computes a tile, never how, so results are bit-identical under any order.
+// `naive` (a diagnostic) keeps the documents in index order instead.
+//
+// A device-only cu_seqlens is validated here: any malformed entry (cu[0] != 0, a decrease,
+// cu[n] != total) raises a flag bit and makes every document empty, so no kernel of the pass
+// reads or writes a token row (overlapping documents could otherwise write one row from
+// several workgroups, and their padded MX offsets could run past the workspace).
 #include "cfa_device.h"
 
 namespace cfa {
@@ -68,8 +75,10 @@ __device__ inline void block_prefix(int n, F f, int* out, int* tmp) {
   __syncthreads();
 }
 
+__device__ inline int length_bucket(int L) { return min((L + 127) / 128, PLAN_BUCKETS - 1); }
+
 __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int* __restrict__ cu, int n_docs, int total_tokens,
-                                                            char* __restrict__ ws) {
+                                                            int naive, char* __restrict__ ws) {
   __shared__ int hist[PLAN_BUCKETS];
   __shared__ int tmp[PLAN_THREADS];
   __shared__ int sflag;
@@ -79,11 +88,11 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int* __restric
   int* order = (int*)(ws + lay.order);
   int* pref = (int*)(ws + lay.pref);
   int* padoff = (int*)(ws + lay.padoff);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < PLAN_BUCKETS; i += PLAN_THREADS) hist[i] = 0;
   if (tid == 0) sflag = 0;
   __syncthreads();
-  // 1. validate and clamp documents; histogram of length buckets
+  // 1. validate; clamp each document into [0, total]
   int flag = 0;
   for (int n = tid; n < n_docs; n += PLAN_THREADS) {
     int a = cu[n], b = cu[n + 1];
@@ -92,37 +101,55 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int* __restric
     if (n == n_docs - 1 && b != total_tokens) flag |= 4;
     int s0 = min(max(a, 0), total_tokens);
     int s1 = min(max(b, 0), total_tokens);
-    int L = max(s1 - s0, 0);
-    docinfo[n] = make_int2(s0, L);
-    int key = min((L + 127) / 128, PLAN_BUCKETS - 1);
-    atomicAdd(&hist[key], 1);
+    docinfo[n] = make_int2(s0, max(s1 - s0, 0));
   }
   if (flag) atomicOr(&sflag, flag);
   __syncthreads();
-  // 2. bucket start positions, longest bucket first
-  block_exclusive_scan_desc(hist, PLAN_BUCKETS, tmp);
-  // 3. place documents
+  // 2. a malformed cu_seqlens empties every document; histogram of length buckets
+  const bool bad = sflag != 0;
   for (int n = tid; n < n_docs; n += PLAN_THREADS) {
-    int L = docinfo[n].y;
-    int key = min((L + 127) / 128, PLAN_BUCKETS - 1);
-    int pos = atomicAdd(&hist[key], 1);
-    order[pos] = n;
+    int2 di = docinfo[n];
+    if (bad) docinfo[n] = make_int2(di.x, 0);
+    atomicAdd(&hist[length_bucket(bad ? 0 : di.y)], 1);
+  }
+  __syncthreads();
+  // 3. bucket start positions, longest bucket first
+  block_exclusive_scan_desc(hist, PLAN_BUCKETS, tmp);
+  // 4. place documents: bucket start + the number of lower-indexed documents of the same bucket
+  //    (chunks of PLAN_THREADS in index order; rank within a wave by lane exchange, then the
+  //    waves of a chunk in turn)
+  for (int base = 0; base < n_docs; base += PLAN_THREADS) {
+    const int n = base + tid;
+    const bool ok = n < n_docs;
+    const int key = ok ? length_bucket(docinfo[n].y) : -1;
+    int rank = 0;
+    for (int j = 0; j < 64; ++j) {
+      const int other = __shfl(key, j, 64);
+      rank += (j < lane && other == key) ? 1 : 0;
+    }
+    for (int w = 0; w < PLAN_THREADS / 64; ++w) {
+      if (wave == w && ok) order[naive ? n : hist[key] + rank] = n;
+      __syncthreads();
+      if (wave == w && ok) atomicAdd(&hist[key], 1);
+      __syncthreads();
+    }
   }
   __threadfence_block();
   __syncthreads();
-  // 4. item prefixes for tile heights 32, 64, 128, 256 over the sorted order
+  // 5. item prefixes for tile heights 32, 64, 128, 256 over the sorted order
   for (int s = 0; s < 4; ++s) {
     const int rows = 32 << s;
     block_prefix(n_docs, [&](int i) { int L = docinfo[order[i]].y; return (L + rows - 1) / rows; },
                  pref + s * (n_docs + 1), tmp);
   }
-  // 5. MX token-block column offsets, document order
+  // 6. MX token-block column offsets, document order
   block_prefix(n_docs, [&](int i) { int L = docinfo[i].y; return (L + 31) / 32 * 32; }, padoff, tmp);
   if (tid == 0) header[0] = sflag;
 }
 
-hipError_t launch_plan(const int* cu, int n_docs, int total_tokens, void* ws, hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, cu, n_docs, total_tokens, (char*)ws);
+hipError_t launch_plan(const int* cu, int n_docs, int total_tokens, void* ws, hipStream_t stream, bool naive) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, cu, n_docs, total_tokens, naive ? 1 : 0,
+                     (char*)ws);
   return hipGetLastError();
 }
 

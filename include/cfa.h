@@ -38,8 +38,13 @@
  *    cfa_workspace_bytes(...) bytes, 256-byte aligned.
  *  - Errors: every precondition the host can check is checked before any launch; on failure the
  *    call returns a non-zero cfa_status, writes nothing, and cfa_last_error() describes it.
- *    A device-only cu_seqlens that turns out malformed is clamped (bad documents become empty)
- *    and a flag is raised in the workspace, readable with cfa_device_error().
+ *    A device-only cu_seqlens that turns out malformed (cu[0] != 0, a decreasing entry or
+ *    cu[n_docs] != total_tokens) raises a flag in the workspace, readable with
+ *    cfa_device_error(), and makes every document empty: attn_fwd / attn_bwd / the cross calls
+ *    then write no row of o, lse, dq, dk, dv (decoding writes each sequence's empty result,
+ *    o = 0 and lse = -inf).
+ *  - CFA_SCHED=naive in the environment (a diagnostic) schedules documents in index order
+ *    instead of longest first; results are bit-identical either way.
  */
 #ifndef CFA_H
 #define CFA_H
@@ -139,7 +144,15 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
  *            block holds only its own tokens; padding columns get code 0x00 and belong to no
  *            scale. t_pad is the row stride of both outputs: a multiple of 32 and at least
  *            mx_padded_tokens(total_tokens, n_docs) (columns past P_{n_docs} are left as is).
- * workspace: at least mx_workspace_bytes(n_docs) bytes (axis 1 only; may be NULL for axis 0).
+ *   axis 2 : the axis-1 blocks in the layout the attention kernels stage for themselves: codes
+ *            [h, d, t_pad] with the 4-token pieces of each 32-token block stored in the order
+ *            0,2,4,6,1,3,5,7 (bytes 16g..16g+15 of a block hold the tokens a matrix-core lane
+ *            group g reads), scales block-major [h, t_pad/32, d].
+ * d·t_pad must stay below 2^31 (axes 1, 2).
+ * Token-block scaling of this kind, with blocks that never cross a document, is the FLAMIA
+ * page's document-local scaling ("FLAMIA Mimarisi ve Temel Tasarım İlkeleri"); the element and
+ * scale rules are the OCP MX definitions of E4M3 and E8M0 (the page names MXFP8 only).
+ * workspace: at least mx_workspace_bytes(n_docs) bytes (axes 1, 2; may be NULL for axis 0).
  */
 int mx_quantize(const void* x, int total_tokens, int h, int d,
                 const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int n_docs, int axis,

@@ -189,6 +189,52 @@ def attn_rows(q, k, v, do, rows, scale, causal=True):
     return o, lse, dq, dk, dv
 
 
+def attn_key_block(q, k, v, do, k0, k1, scale, causal=True, row_block=256, q_range=None):
+    """dK and dV of keys k0..k1-1 of ONE document (doc-local arrays), summed over every query.
+
+    For documents too long for the full oracle, when a block of keys is to be checked
+    completely: dK_j and dV_j sum over all queries i that see key j (i >= j when causal), and
+    each term needs that query's whole softmax row (its normaliser) and its O_i (for D_i). So
+    every query row that can see the block is formed in full, as in ``attn_bwd`` -- scores of
+    the keys the row may see, explicit mask, two-pass softmax ("GPT Kernel Programlama"
+    §3-§6) -- and only the block's columns of P and dS enter the sums (the derivatives of
+    ``attn_bwd``). A causal row i is formed over keys 0..r1-1 of its row block (r1 > i): the
+    keys past i are masked, so their probabilities are exact zeros either way.
+    ``q, do [L, hq, d]``, ``k, v [L, hkv, d]``. Returns ``dk, dv [k1 - k0, hkv, d]``.
+    ``q_range = (a, b)`` sums over queries a..b-1 only (the sums split by query ranges add up
+    to the whole).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    do = np.asarray(do, np.float64)
+    L, hq, d = q.shape
+    hkv = k.shape[1]
+    group = hq // hkv
+    assert 0 <= k0 <= k1 <= L
+    nk = k1 - k0
+    dk = np.zeros((nk, hkv, d))
+    dv = np.zeros((nk, hkv, d))
+    first_row = k0 if causal else 0
+    qa, qb = (0, L) if q_range is None else q_range
+    for h in range(hq):
+        g = h // group
+        for r0 in range(max(first_row, qa), qb, row_block):
+            r1 = min(qb, r0 + row_block)
+            cols = r1 if causal else L
+            p, _ = _probabilities(q[r0:r1, h], k[:cols, g], scale, r0, causal)
+            o = p @ v[:cols, g]
+            D = np.sum(do[r0:r1, h] * o, axis=1)
+            pb = np.zeros((r1 - r0, nk))
+            c1 = min(k1, cols)
+            pb[:, :c1 - k0] = p[:, k0:c1]
+            dp = do[r0:r1, h] @ v[k0:k1, g].T
+            ds = pb * (dp - D[:, None])
+            dv[:, g] += pb.T @ do[r0:r1, h]
+            dk[:, g] += scale * (ds.T @ q[r0:r1, h])
+    return dk, dv
+
+
 # ---------------------------------------------------------------- cross-attention
 def cross_mask(Lq, Lk, causal):
     """Explicit additive mask of one document with separate query and key lengths.

@@ -98,7 +98,8 @@ def test_bwd_rejects():
 
 def test_mx_quantize_rejects():
     L = _lib.lib()
-    assert L.mx_quantize(FAKE, 100, 2, 128, FAKE, None, 1, 2, FAKE, FAKE, 0, None, 0, None) == 2   # axis
+    assert L.mx_quantize(FAKE, 100, 2, 128, FAKE, None, 1, 3, FAKE, FAKE, 0, None, 0, None) == 2   # axis
+    assert L.mx_quantize(FAKE, 100, 2, 128, FAKE, None, 1, 2, FAKE, FAKE, 160, None, 0, None) == 1   # workspace
     assert L.mx_quantize(FAKE, 100, 2, 96, FAKE, None, 1, 0, FAKE, FAKE, 0, None, 0, None) == 3    # d
     assert L.mx_quantize(FAKE, 100, 2, 128, FAKE, None, 1, 1, FAKE, FAKE, 100, FAKE, 1 << 20, None) == 2  # t_pad
     assert L.mx_quantize(FAKE, 100, 2, 128, FAKE, None, 1, 1, FAKE, FAKE, 160, None, 0, None) == 1   # workspace
@@ -146,3 +147,16 @@ def test_narrow_mx_sizes_and_quantiser_rejects():
         assert fn(FAKE, 0, 2, 128, FAKE, FAKE, None) == 0         # nothing to do: no launch
         assert L.cfa_last_error() is not None
 
+
+
+def test_mx_paths_reject_token_counts_past_32_bit_column_offsets():
+    """Token-blocked MX rows are addressed as channel·t_pad + column in 32 bits: d·t_pad must
+    stay below 2^31 (t_pad = 32·ceil(T/32) + 32·n_docs), checked before any launch."""
+    L = _lib.lib()
+    big = (1 << 31) // 128                              # t_pad·128 = 2^31 exactly at one document
+    for dt in (2, 3, 4, 5):
+        assert _fwd(dtype=dt, T=big - 32, n_docs=1, cu_h=None, hq=1, hkv=1, saved=FAKE) == 3
+        assert b"2^31" in L.cfa_last_error()
+        assert L.cfa_workspace_bytes(0, big - 32, 1, 1, 1, 128, dt) == 0
+        assert L.cfa_workspace_bytes(0, big - 64, 1, 1, 1, 128, dt) > 0   # t_pad·d = 2^31 − 4096
+    assert L.cfa_workspace_bytes(0, big - 32, 1, 1, 1, 128, 1) > 0       # bf16 has no such rows

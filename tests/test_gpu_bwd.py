@@ -12,7 +12,7 @@ import torch
 import causal_flashattention_amd as cfa
 from causal_flashattention_amd import workloads as W
 from oracle import attention as ref
-from gpu_helpers import announce, head_group, rel_l2, to_f64, upload
+from gpu_helpers import announce, head_group, key_block_threaded, rel_l2, to_f64, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -81,6 +81,12 @@ def test_bf16_grads_gqa_workload_3_sampled():
     _, _, _, pdk, pdv = ref.attn_rows(q, k, v, do, tail, w.scale)
     assert rel_l2(dk[L - 300:, [g]], pdk[L - 300:]) <= GRAD_TOL
     assert rel_l2(dv[L - 300:, [g]], pdv[L - 300:]) <= GRAD_TOL
+    # key tile 0 complete: the keys every one of the 32768 queries of the four heads sees, which
+    # the dK/dV pass accumulates over its longest query loop
+    bk, bv = key_block_threaded(q, k, v, do, 0, 128, w.scale)
+    print("rel-L2 dK, dV of keys 0..127", rel_l2(dk[:128, [g]], bk), rel_l2(dv[:128, [g]], bv))
+    assert rel_l2(dk[:128, [g]], bk) <= GRAD_TOL
+    assert rel_l2(dv[:128, [g]], bv) <= GRAD_TOL
     # invariants at full size, every kv head: Σ_j dK_j = 0; Σ_j dV_j = Σ_{h in group} Σ_i dO_i;
     # Σ_h <Q, dQ> = <K, dK>  (tolerances relative to the magnitudes involved)
     do_all = w.f64("do")

@@ -131,3 +131,27 @@ def test_mx_quantize_fp6_e3m2_bit_exact(d):
         rc, rs = mx.quantize_d_fp6(W.bf16_bits_to_f64(xin), "e3m2")
         assert np.array_equal(c.cpu().numpy(), mx.pack_fp6(rc))
         assert np.array_equal(s.cpu().numpy(), rs)
+
+
+PIECES = np.array([0, 2, 4, 6, 1, 3, 5, 7])      # stored 4-token piece p holds logical piece PIECES[p]
+
+
+@pytest.mark.parametrize("lengths", [[1, 31, 32, 33, 0, 100, 7], [300, 1, 1, 1], [4000, 129, 2]])
+def test_mx_quantize_kernel_layout_bit_exact(lengths):
+    """axis 2 (the token-blocked copies the attention kernels use, V in the forward and dO in the
+    backward): after undoing the documented piece order and the block-major scale layout the
+    bytes equal the reference quantiser's doc-local token blocks."""
+    h, d = 3, 128
+    T = sum(lengths)
+    xb = _special_tensor(T, h, d, seed=90 + len(lengths))
+    cu = W.cu_from_lengths(lengths)
+    announce("mx_quantize kernel layout", lengths)
+    c2, s2 = cfa.mx_quantize(to_dev(xb), torch.from_numpy(cu).to(DEV), 2, cu_seqlens_host=cu)
+    torch.cuda.synchronize()
+    rc, rs = mx.quantize_t(W.bf16_bits_to_f64(xb), cu)
+    tp = rc.shape[2]
+    c2 = c2.cpu().numpy()[:, :, :tp].reshape(h, d, tp // 32, 8, 4)
+    logical = np.empty_like(c2)
+    logical[:, :, :, PIECES] = c2
+    assert np.array_equal(logical.reshape(h, d, tp), rc)
+    assert np.array_equal(np.transpose(s2.cpu().numpy()[:, :tp // 32], (0, 2, 1)), rs)

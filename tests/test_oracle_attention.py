@@ -331,3 +331,29 @@ def test_row_subset_matches_full_oracle():
     np.testing.assert_allclose(pdv[100:], dv[100:], atol=1e-12)
     _, _, _, fdk, fdv = att.attn_rows(q, k, v, do, np.arange(150), 0.3, causal=True)
     np.testing.assert_allclose(fdk, dk, atol=1e-12)
+
+
+def test_key_block_gradients_equal_full_oracle():
+    """attn_key_block (every query, a block of keys) against the full backward, causal and not,
+    GQA, blocks at the start, in the middle, crossing row blocks and at the end."""
+    rng = np.random.default_rng(77)
+    L, hq, hkv, d = 700, 4, 2, 16
+    q, k, v, do = (rng.standard_normal((L, h, d)) for h in (hq, hkv, hkv, hq))
+    cu = np.array([0, L])
+    for causal in (True, False):
+        _, dk, dv = att.attn_bwd(q, k, v, do, cu, 0.3, causal)
+        for k0, k1 in ((0, 128), (100, 101), (250, 520), (600, 700), (0, 700)):
+            bk, bv = att.attn_key_block(q, k, v, do, k0, k1, 0.3, causal, row_block=96)
+            np.testing.assert_allclose(bk, dk[k0:k1], rtol=0, atol=1e-12 * np.abs(dk).max())
+            np.testing.assert_allclose(bv, dv[k0:k1], rtol=0, atol=1e-12 * np.abs(dv).max())
+
+
+def test_key_block_query_ranges_add_up():
+    rng = np.random.default_rng(78)
+    L, d = 300, 8
+    q, k, v, do = (rng.standard_normal((L, 2, d)) for _ in range(4))
+    k, v = k[:, :1], v[:, :1]
+    whole = att.attn_key_block(q, k, v, do, 40, 170, 0.5)
+    parts = [att.attn_key_block(q, k, v, do, 40, 170, 0.5, q_range=r) for r in ((0, 90), (90, 91), (91, 300))]
+    for i in range(2):
+        np.testing.assert_allclose(sum(p[i] for p in parts), whole[i], rtol=0, atol=1e-12 * np.abs(whole[i]).max())
