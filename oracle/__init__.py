@@ -29,7 +29,6 @@ Modules:
   doc-local tokens).
 * ``mx_attention``  -- the attention oracle fed with the quantised operand copies.
 * ``decode``        -- one query per sequence over a packed (optionally MX-quantised) KV cache.
-* ``baseline``      -- wall-clock timing of the oracle on host cores (CPU baseline only).
 
 Every function states the passage it follows; the readings taken where the pages are silent
 are listed in the repository's design notes.
