@@ -104,7 +104,7 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 3 times (to scale the "
                          "FETCH_SIZE/WRITE_SIZE counters against a kernel of known traffic) and exit")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
     ap.add_argument("--decode", action="store_true",
                     help="instead: time decoding over a packed KV cache (bf16 and MX caches; one JSON line)")
     return ap.parse_args()
