@@ -18,7 +18,7 @@ import torch
 from . import _lib
 from ._lib import CFA_BF16, CFA_F32, CFA_MXFP4, CFA_MXFP6, CFA_MXFP6_E3M2, CFA_MXFP8, CfaError
 
-__all__ = ["attn_fwd", "attn_bwd", "device_error", "attn_fwd_cross", "attn_bwd_cross", "attn_decode", "mx_quantize", "mx_quantize_fp4", "mx_quantize_fp6", "mx_quantize_fp6_e3m2", "workspace_bytes", "saved_bytes", "CfaError",
+__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_noalloc", "device_error", "attn_fwd_cross", "attn_bwd_cross", "attn_decode", "mx_quantize", "mx_quantize_fp4", "mx_quantize_fp6", "mx_quantize_fp6_e3m2", "workspace_bytes", "saved_bytes", "CfaError",
            "CFA_F32", "CFA_BF16", "CFA_MXFP8", "CFA_MXFP4", "CFA_MXFP6", "CFA_MXFP6_E3M2", "library_path"]
 
 
@@ -197,6 +197,38 @@ def attn_bwd(q, k, v, o, lse, dout, cu_seqlens, *, scale=None, causal=True, cu_s
                           _ptr(cu_seqlens), _ptr(hcu) if hcu is not None else None, n_docs, T,
                           int(max_seqlen), hq, hkv, d, scale, int(bool(causal)), dt, _ptr(workspace),
                           _nbytes(workspace), _stream()))
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, cu_seqlens, *, dq, dk, dv, scale=None, causal=True,
+                     cu_seqlens_host=None, max_seqlen=0, mx=False, saved=None, dlse=None):
+    """``attn_bwd`` whose scratch is the library's fixed per-GPU array (no workspace, no
+    allocation by the library). The caller passes the outputs ``dq, dk, dv``; calls that overlap
+    on one GPU race (they share the array)."""
+    L = _lib.lib()
+    _check_qkv(q, k, v, True)
+    _check_cu(cu_seqlens)
+    T, hq, d = q.shape
+    n_docs = cu_seqlens.numel() - 1
+    dt = _dtype_code(q, mx)
+    for t, name in ((o, "o"), (dout, "dout"), (dq, "dq")):
+        _expect(t, q.shape, q.dtype, name)
+    for t, name in ((dk, "dk"), (dv, "dv")):
+        _expect(t, k.shape, k.dtype, name)
+    _expect(lse, (hq, T), torch.float32, "lse")
+    _expect(dlse, (hq, T), torch.float32, "dlse")
+    if mx:
+        if saved is None:
+            raise ValueError("the MX paths need the forward's saved buffer")
+        _at_least(saved, L.cfa_saved_bytes(T, n_docs, hq, k.shape[1], d, dt), "saved")
+    _check_dev(q, k, v, o, lse, dout, cu_seqlens, saved, dlse, dq, dk, dv)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    hcu = _host_cu(cu_seqlens, cu_seqlens_host)
+    _lib.check(L.attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                  _ptr(dlse) if dlse is not None else None,
+                                  _ptr(saved) if saved is not None else None, _ptr(dq), _ptr(dk), _ptr(dv),
+                                  _ptr(cu_seqlens), _ptr(hcu) if hcu is not None else None, n_docs, T,
+                                  int(max_seqlen), hq, k.shape[1], d, scale, int(bool(causal)), dt, _stream()))
     return dq, dk, dv
 
 

@@ -38,6 +38,8 @@ SIGNATURES = {
                             _P, _S, _P]),
     "cfa_set_kernel_events": (_I, [_P, _I]),
     "cfa_device_error": (_I, [_P, _P, ctypes.POINTER(ctypes.c_int)]),
+    "attn_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I,
+                              _P]),
 }
 
 _lib = None

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "cfa.h"
 #include "cfa_device.h"
@@ -658,6 +659,56 @@ int cfa_device_error(const void* workspace, void* stream, int* flag) {
   if (int r = check_hip(hipStreamSynchronize(st), "synchronize")) return r;
   *flag = host;
   return CFA_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- backward without allocation
+namespace {
+// Scratch of attn_bwd_noalloc: one copy per GPU the library runs on, held until the process ends.
+// In host code this name is only a stand-in for the device array, never a device address: kernels
+// get the pointer hipGetSymbolAddress returns for the current device.
+constexpr size_t STATIC_SCRATCH_BYTES = size_t(64) << 20;
+static __device__ __align__(256) char scratch[STATIC_SCRATCH_BYTES];
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// The device address of `scratch` on the current device, looked up once per device (with that
+// device current) and kept.
+int scratch_for_current_device(void** out) {
+  int dev = 0;
+  if (int r = check_hip(hipGetDevice(&dev), "hipGetDevice")) return r;
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(CFA_ERR_UNSUPPORTED, "device index %d >= %d", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (int r = check_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)")) return r;
+    if (!p || !aligned(p, 256)) return fail(CFA_ERR_HIP, "scratch array address %p is not 256-byte aligned", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CFA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                     const float* dlse, const void* saved, void* dq, void* dk, void* dv, const int32_t* cu_seqlens,
+                     const int32_t* cu_seqlens_host, int n_docs, int total_tokens, int max_seqlen, int hq, int hkv,
+                     int d, float scale, int causal, int dtype, void* stream) {
+  g_err[0] = 0;
+  const Sizes s{total_tokens, n_docs, hq, hkv, d, dtype};
+  if (int st = check_sizes(s, true)) return st;
+  const size_t need = ws_layout(1, s).total;
+  if (need > STATIC_SCRATCH_BYTES)
+    return fail(CFA_ERR_WORKSPACE, "attn_bwd_noalloc: these sizes need %zu bytes of scratch, above its fixed %zu",
+                need, STATIC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (int r = scratch_for_current_device(&ws)) return r;
+  return attn_bwd(q, k, v, o, lse, dout, dlse, saved, dq, dk, dv, cu_seqlens, cu_seqlens_host, n_docs, total_tokens,
+                  max_seqlen, hq, hkv, d, scale, causal, dtype, ws, STATIC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

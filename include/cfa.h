@@ -268,6 +268,25 @@ int cfa_set_kernel_events(void* const* events, int n_pairs);
  */
 int cfa_device_error(const void* workspace, void* stream, int* flag);
 
+/*
+ * attn_bwd for callers that cannot allocate device memory (code under stream capture, serving
+ * loops, harnesses that forbid hipMalloc): the same computation, outputs and errors as attn_bwd,
+ * with the scratch taken from a fixed array inside the library instead of a caller workspace.
+ * Each GPU the library runs on holds one such array of 64 MiB (67108864 bytes) until the
+ * process ends; its address is looked up once per device on the first call
+ * with that device current (no allocation). Sizes whose workspace (cfa_workspace_bytes with pass
+ * 1) exceeds the array are rejected with CFA_ERR_WORKSPACE before any launch. Every call on one
+ * GPU shares that GPU's array: calls that overlap on one GPU (other streams, other threads) race
+ * and must be serialised by the caller. Nothing in the array needs to start at zero (every call
+ * writes what it reads). The validation flag of a device-only cu_seqlens is kept in the array
+ * and is not readable through cfa_device_error.
+ */
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, const float* dlse, const void* saved, void* dq, void* dk, void* dv,
+                     const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                     int n_docs, int total_tokens, int max_seqlen, int hq, int hkv, int d,
+                     float scale, int causal, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -160,3 +160,14 @@ def test_mx_paths_reject_token_counts_past_32_bit_column_offsets():
         assert L.cfa_workspace_bytes(0, big - 32, 1, 1, 1, 128, dt) == 0
         assert L.cfa_workspace_bytes(0, big - 64, 1, 1, 1, 128, dt) > 0   # t_pad·d = 2^31 − 4096
     assert L.cfa_workspace_bytes(0, big - 32, 1, 1, 1, 128, 1) > 0       # bf16 has no such rows
+
+
+def test_noalloc_backward_rejects_sizes_beyond_its_array():
+    """attn_bwd_noalloc checks the workspace its sizes need against its fixed 64 MiB array before
+    any HIP call: 2^20 tokens × 32 heads of D alone is 128 MiB."""
+    L = _lib.lib()
+    args = [FAKE] * 6 + [None, None] + [FAKE] * 3 + [FAKE, None, 1, 1 << 20, 0, 32, 8, 128, 0.088, 1, 1, None]
+    assert L.attn_bwd_noalloc(*args) == 5
+    assert b"64" in L.cfa_last_error() or b"67108864" in L.cfa_last_error()
+    bad = list(args); bad[21] = 0                        # fp32 is forward-only, checked first
+    assert L.attn_bwd_noalloc(*bad) == 3
