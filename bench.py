@@ -12,8 +12,8 @@ timed region. ``value`` is causal TFLOP/s with the FLOP convention 3.5 × 4·d·
 per launch divided by its mean launch time, both measured here with HIP events recorded by
 the library around that kernel on the bench stream during the timed steps. Algorithmic FLOPs
 per kernel follow the same convention: forward = 2 GEMM units (S, PV); dK/dV = 4 units
-(S, dP, dV, dK); dQ = 1 unit (dQ; its S/dP recompute is not counted); one unit = 2·d·hq·Σ
-L(L+1)/2. ``traffic`` comes from committed rocprofv3 counter summaries (profiles/), and is
+(S, dP, dV, dK); dQ = 1 unit (dQ; its S/dP recompute is not counted); with CFA_DQ_MODE=fused the
+bf16 backward at d = 128 runs dK, dV and dQ in one pass, 5 units; one unit = 2·d·hq·Σ L(L+1)/2. ``traffic`` comes from committed rocprofv3 counter summaries (profiles/), and is
 null when the kernel source changed since they were taken.
 
 ``cpu_baseline`` times the float64 oracle (naive two-pass attention with an explicit mask)
@@ -64,6 +64,13 @@ KERNELS_BF16 = {
     "attn_bwd_dkdv_kernel": ("bwd", 1, 4.0),
     "attn_bwd_dq_kernel": ("bwd", 2, 1.0),
 }
+# d = 128 bf16 backward with dQ summed inside the dK/dV pass (CFA_DQ_MODE=fused; the default is
+# the separate dQ pass above): S, dP, dV, dK and dQ, 5 units
+KERNELS_BF16_FUSED = {
+    "attn_fwd_bf16_kernel": ("fwd", 0, 2.0),
+    "bwd_pre_kernel": ("bwd", 0, 0.0),
+    "attn_bwd_dkdv_dq_kernel": ("bwd", 1, 5.0),
+}
 KERNELS_MX = {
     "attn_fwd_mx_kernel": ("fwd", 0, 2.0),
     "mx_quantize_fwd": ("fwd", 1, 0.0),
@@ -77,6 +84,7 @@ KERNEL_SOURCES = {
     "bwd_pre_kernel": "attn_bwd.hip",
     "attn_bwd_dkdv_kernel": "attn_bwd.hip",
     "attn_bwd_dq_kernel": "attn_bwd.hip",
+    "attn_bwd_dkdv_dq_kernel": "attn_bwd.hip",
     "attn_fwd_mx_kernel": "attn_fwd_mx.hip",
     "attn_bwd_dkdv_mx_kernel": "attn_bwd_mx.hip",
     "attn_bwd_dq_mx_kernel": "attn_bwd_mx.hip",
@@ -211,7 +219,8 @@ def measure(w, mx, steps, warmup):
     saved = torch.empty(max(cfa.saved_bytes(T, w.n_docs, hq, hkv, d, dt), 256), dtype=torch.uint8, device=dev) \
         if mx else None
     L = _lib.lib()
-    kernels = KERNELS_MX if mx else KERNELS_BF16
+    fused = not mx and d == 128 and os.environ.get("CFA_DQ_MODE") == "fused"
+    kernels = KERNELS_MX if mx else (KERNELS_BF16_FUSED if fused else KERNELS_BF16)
 
     def fwd():
         cfa.attn_fwd(q, k, v, cu, scale=w.scale, cu_seqlens_host=cu_h, out=o, lse=lse, workspace=ws_f, mx=mx,
@@ -265,7 +274,7 @@ def measure(w, mx, steps, warmup):
     # per-step spread from the same events: first forward kernel's start to the last backward
     # kernel's end (the forward's plan launch, ~13 us, precedes the span)
     first = "mx_quantize_fwd" if mx else "attn_fwd_bf16_kernel"      # launch order, not event slot
-    last = "attn_bwd_dq_mx_kernel" if mx else "attn_bwd_dq_kernel"
+    last = "attn_bwd_dq_mx_kernel" if mx else ("attn_bwd_dkdv_dq_kernel" if fused else "attn_bwd_dq_kernel")
     spans = [ev[first][i][0].elapsed_time(ev[last][i][1]) for i in range(K)]
     dom = max(kern, key=lambda n: kern[n]["ms"])
     dom_flops = kern[dom]["units"] * unit_flops

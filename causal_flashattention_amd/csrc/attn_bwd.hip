@@ -87,33 +87,123 @@ struct BwdTile {
 // the query rows, off = Lk - Lq and key j is seen by query i iff j <= i + off; LSE = -inf (a query
 // that sees no key) is read as +inf so that its P is 0. total_tokens counts query rows (LSE, D),
 // total_k key rows (partial sums).
-template <int D, int NP, bool CROSS, bool SPLIT>
-__global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
+//
+// dQ inside this pass (FQ, self-attention at d = 128): dQ_i = scale·Σ_j dS_ij k_j is the one
+// gradient that sums over key tiles, which different workgroups own. Each workgroup adds its key
+// tile's part of every (query head, 64-query tile) block into an fp32 sum in the workspace, and
+// the tiles of a document add in key-tile order 0, 1, 2, ...: tile t waits until tile t − 1 has
+// added (a count per block piece), so the sum has one fixed order and reruns are bit-identical.
+// Tile 0 writes the block, the last tile that sees it (the diagonal one when causal) writes dQ
+// as bf16. To keep tile t just behind tile t − 1, every key tile of a document walks the same
+// query tiles in the same order: from the document end down to its own diagonal, query heads
+// inner. The part itself, dQᵀ = Kᵀ dSᵀ over the workgroup's 128 keys, is split over the 8 waves by
+// head-dim columns (16 each, v_mfma_f32_16x16x32_bf16): A = Kᵀ (registers, read once from a
+// staged K tile), B = dSᵀ, which the dS wave writes over its partner's P in the exchange tile
+// (rows = keys), so no extra LDS is needed. Waits: a tile waits only on the tile of its
+// document handed out just before it, which a running workgroup holds (see the claim below),
+// so every wait ends; each one is bounded anyway and raises bit 3 of the plan flag if it gives up.
+struct FusedDq {
+  float* acc;                 // [T][hq][D] fp32 running dQ / scale of the key tiles added so far
+  int* cnt;                   // [t_pad/32][hq][8]: key tiles that have added into each 16-column piece
+  __bf16* dq;                 // dQ output [T][hq][D]
+  const int* padoff;          // plan: first 32-token block of each document
+  int* header;                // plan header: [0] flag, [2] chain counter, [16, 48) per-XCD claim words
+  i32x4* kt;                  // [grid][8 waves][4 pairs][64 lanes]: each workgroup's Kᵀ operands
+  unsigned long long acc_bytes;
+  int n_chains;               // documents × kv heads × head splits
+};
+
+constexpr int FUSED_MAX_GRID = 256;           // persistent workgroups (Kᵀ operand slots) at most
+
+constexpr int SPIN_LIMIT = 1 << 20;          // ~1 s of polling: far beyond any legitimate wait
+constexpr int SC1 = 16;                       // buffer access cache policy: device scope (sc1)
+constexpr int CLAIM_END = 0x7fffffff;
+
+// Index of the XCD (accelerator complex die) the calling wave runs on; the CUs of one XCD share
+// one L2 cache.
+__device__ inline int xcc_id() {
+  int x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(x));
+  return x;
+}
+
+// Byte offset of bf16 column c (c % 4 == 0) of row r in a 128-row × 64-column exchange tile with
+// 128-byte rows whose 32-byte units are XOR-swizzled by f(r): the transposing reads of the dQ
+// product (rows 8g + 0..3 of four lane groups, 32 bytes each) then fall into distinct bank
+// groups within each half of the wave.
+__device__ inline int xt_off(int r, int c) {
+  const int f = ((r >> 1) & 1) | (((r >> 3) & 1) << 1);
+  return r * 128 + ((((c >> 4) ^ f) & 3) << 5) + ((c & 15) << 1);
+}
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// The exchange tile's LDS address as an opaque scalar: the three exchange buffers are then
+// addressed through one set of lane offsets (plus immediates) instead of a set per buffer.
+__device__ inline lds_char* lds_opaque(const void* p) {
+  uint32_t a = (uint32_t)(uintptr_t)(const lds_char*)p;
+  asm volatile("" : "+s"(a));
+  return (lds_char*)(uintptr_t)a;
+}
+
+// The lane index as a value the compiler cannot hoist: addresses derived from it are recomputed
+// where they are used instead of being held in registers across the whole persistent loop.
+__device__ inline int lane_here() {
+  int l = threadIdx.x & 63;
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
+// Wait until *cnt >= target (device-coherent polling); bounded. A wait that gives up raises bit 3
+// of the plan flag, after which every wait returns at once (the results are then invalid, and the
+// pass still ends promptly).
+__device__ inline void wait_count(const int* cnt, int target, int* flag) {
+  for (int n = 0;; ++n) {
+    const int c = __builtin_amdgcn_readfirstlane(__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (c >= target) return;
+    if ((n & 255) == 255 &&
+        (__builtin_amdgcn_readfirstlane(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) & 8))
+      return;
+    if (n >= SPIN_LIMIT) {
+      if ((threadIdx.x & 63) == 0) atomicOr(flag, 8);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+template <int D, int NP>
+struct DkdvLds {
+  using C = BwdTile<D>;
+  static constexpr int QBS = D <= 128 ? 2 : 1;
+  static constexpr int BM = 32 * QBS;
+  static constexpr int TILE = BM * C::RSTR;
+  static constexpr int STAGE = 2 * TILE + 2 * BM * 4;   // Q, dO, LSE·log2 e, D
+  static constexpr int XP = NP * QBS * 2 * 64;          // i32x4 per exchange buffer (16 KB at d = 128)
+};
+
+// One work item: 32·NP keys [t·32·NP, ...) of document `doc` (rows s0 .. s0 + L − 1), kv head g,
+// head split `split`.
+template <int D, int NP, bool CROSS, bool SPLIT, bool FQ>
+__device__ __forceinline__ void dkdv_item(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    __bf16* __restrict__ dk, __bf16* __restrict__ dv, Plan plan, int total_tokens, int hq, int hkv,
-    float scale, int causal, int n_split, float* __restrict__ part_dk, float* __restrict__ part_dv,
-    const int2* __restrict__ qdoc, int total_k) {
+    __bf16* __restrict__ dk, __bf16* __restrict__ dv, int total_tokens, int hq, int hkv, float scale, int causal,
+    int n_split, float* __restrict__ part_dk, float* __restrict__ part_dv, const int2* __restrict__ qdoc,
+    int total_k, const FusedDq& fq, int s0, int L, int t, int doc, int g, int split, char* st_a, char* st_b,
+    char* st_c, i32x4* xp_a, i32x4* xp_b, i32x4* xp_c) {
   using C = BwdTile<D>;
+  using X = DkdvLds<D, NP>;
+  static_assert(!FQ || (D == 128 && NP == 4 && !CROSS), "dQ inside the pass: self-attention at d = 128");
   constexpr int KT = 32 * NP;                     // keys per workgroup
-  constexpr int QBS = D <= 128 ? 2 : 1;           // 32-query blocks per step (a longer step hides the copies)
-  constexpr int BM = 32 * QBS;                    // queries per step
-  constexpr int TILE = BM * C::RSTR;              // 16 KB
-  constexpr int STAGE = 2 * TILE + 2 * BM * 4;    // Q, dO, LSE·log2 e, D
-  constexpr int XP = NP * QBS * 2 * 64;           // i32x4 per exchange buffer: bf16 P [pair][qb][u][lane]
-  constexpr int SB = D == 256 ? 4 : C::DS;        // k-steps per operand batch
+  constexpr int QBS = X::QBS;                     // 32-query blocks per step (a longer step hides the copies)
+  constexpr int BM = X::BM;                       // queries per step
+  constexpr int TILE = X::TILE;                   // 16 KB
+  // k-steps per operand batch (fused mode: 4, leaving room for the dQ product's operands)
+  constexpr int SB = (D == 256 || FQ) ? 4 : C::DS;
   constexpr int DBC = D == 256 ? 4 : C::DB;       // d blocks per transposed-read batch
-  __shared__ __attribute__((aligned(16))) char st_a[STAGE];
-  __shared__ __attribute__((aligned(16))) char st_b[STAGE];
-  __shared__ __attribute__((aligned(16))) char st_c[STAGE];
-  __shared__ i32x4 xp_a[XP];
-  __shared__ i32x4 xp_b[XP];
-  __shared__ i32x4 xp_c[XP];
 
   const int ns = SPLIT ? n_split : 1;             // the unsplit instantiation keeps plain indexing
-  const int p = blockIdx.x / (hkv * ns), g = blockIdx.x % hkv, split = SPLIT ? (blockIdx.x / hkv) % ns : 0;
-  int s0, L, t, doc;
-  if (!decode_item(plan, p, KT, false, s0, L, t, &doc)) return;
   // key rows [s0, s0 + L); query rows [q_s0, q_s0 + Lq); off = L - Lq (0 for self-attention)
   int q_s0 = s0, Lq = L;
   if constexpr (CROSS) {
@@ -152,6 +242,56 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
   const int n_steps = n_qt * n_h;
   const int wave_first_q = causal ? kw0 - off : 0;
 
+  // step st -> (query head, first doc-local query of the step): query heads outer and query tiles
+  // ascending from the diagonal; with dQ inside the pass, query tiles from the document end down
+  // to the diagonal with the heads inner (the order every key tile of the document shares)
+  auto step_at = [&](int st, int& h, int& q0) {
+    if constexpr (FQ) {
+      h = h_lo + st % n_h;
+      q0 = q_begin + (n_qt - 1 - st / n_h) * BM;
+    } else {
+      h = h_lo + st / n_qt;
+      q0 = q_begin + (st % n_qt) * BM;
+    }
+  };
+
+  // dQ product A operands: element e of operand kk is K[key 32kk + 8(lane/16) + e][d 16w + lane%16]
+  // (keys of this workgroup; zero past the document end), read transposed from the K tile staged
+  // once into a free stage buffer and kept in this workgroup's slot of the workspace (registers
+  // are full), from where each dQ part reloads them (coalesced, from L2)
+  i32x4* const kt_slot = FQ ? fq.kt + (size_t)blockIdx.x * (8 * NP * 64) : nullptr;
+  if constexpr (FQ) {
+    stage_rows_lds<KT, 2 * NP, D>(st_c, (const char*)(k + ((size_t)(s0 + t * KT) * hkv + g) * D),
+                                  (uint32_t)hkv * D * 2, L - 1 - t * KT, w, lane);
+    wait_vmem();
+    __syncthreads();
+    const int gi = lane >> 4, ii = lane & 15;
+#pragma unroll
+    for (int kk = 0; kk < NP; ++kk) {
+      const int r = 32 * kk + 8 * gi + (ii >> 2), col = 16 * w + 4 * (ii & 3);
+      i32x4 u = __builtin_bit_cast(i32x4, concat_tr(lds_read_tr16(st_c + C::S::elem(r, col)),
+                                                    lds_read_tr16(st_c + C::S::elem(r + 4, col))));
+      const int key0 = t * KT + 32 * kk + 8 * gi;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (key0 + e >= L) u[e >> 1] &= (e & 1) ? 0x0000FFFF : (int)0xFFFF0000;
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc(kt_slot + w * NP * 64, 0, NP * 64 * 16, 0x00020000);
+      __builtin_amdgcn_raw_buffer_store_b128(u, rk, (kk * 64 + lane) * 16, 0, SC1);
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // exchange-tile lane offset (xt_off with the row swizzle folded in) of this lane's key row and
+  // 32-byte unit u (u = 2qb + jj/2) of its P / dS words (+16 bytes for odd jj)
+  auto xo = [&](int u) {
+    const int l = lane_here();
+    const int xrow = 32 * pair + (l & 31);
+    const int fx = ((xrow >> 1) & 1) | (((xrow >> 3) & 1) << 1);
+    return xrow * 128 + (((u ^ fx) & 3) << 5) + 8 * (l >> 5);
+  };
+
   // Step st -> buffer: P waves copy the Q tile, dS waves the dO tile (direct global -> LDS);
   // lanes 0..31 of wave 0 fetch LSE and D into registers, written by stage_finish. Rows past
   // the document end are clamped into it and masked (P = 0).
@@ -161,8 +301,8 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
   constexpr int TR = D < 128 ? BM * D / 8 / (64 * NP) : 1;
   i32x4 treg[TR];
   auto stage = [&](int st, char* buf) {
-    const int h = h_lo + st / n_qt;
-    const int q0 = q_begin + (st % n_qt) * BM;
+    int h, q0;
+    step_at(st, h, q0);
     const __bf16* src = ds_wave ? dout : q;
     if constexpr (D >= 128) {
       stage_rows_lds<BM, NP, D>(buf + (ds_wave ? TILE : 0), (const char*)(src + ((size_t)(q_s0 + q0) * hq + h) * D),
@@ -196,14 +336,16 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
     }
   };
   auto active = [&](int st) {
-    const int q0 = q_begin + (st % n_qt) * BM;
+    int h, q0;
+    step_at(st, h, q0);
     return q0 + BM - 1 >= wave_first_q && kw0 < L;
   };
 
   // P wave, step st: per 32-query block, S, P (bf16, to the exchange buffer and the dV product),
   // dVᵀ += dOᵀ P
   auto step_p = [&](int st, const char* buf, i32x4* xw) __attribute__((always_inline)) {
-    const int q0 = q_begin + (st % n_qt) * BM;
+    int h_unused, q0;
+    step_at(st, h_unused, q0);
     const char* ob = buf + TILE;
     const f32x4* l2 = (const f32x4*)(buf + 2 * TILE);
     const bool masked = (causal && q0 + off < kw0 + 31) || q0 + BM > Lq;   // wave-uniform
@@ -212,12 +354,12 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
       f32x16 sacc = f32x16{};
 #pragma unroll
       for (int sc = 0; sc < C::DS; sc += SB) {
-        i32x4 fq[SB];
+        i32x4 fq_[SB];
 #pragma unroll
-        for (int s = 0; s < SB; ++s) fq[s] = *(const i32x4*)(buf + 32 * qb * C::RSTR + so.row[sc + s]);
+        for (int s = 0; s < SB; ++s) fq_[s] = *(const i32x4*)(buf + 32 * qb * C::RSTR + so.row[sc + s]);
 #pragma unroll
-        for (int s = 0; s < SB; ++s) sacc = mfma32(as_bf16x8(fq[s]), kv[sc + s], sacc);
-        if constexpr (D == 128) {
+        for (int s = 0; s < SB; ++s) sacc = mfma32(as_bf16x8(fq_[s]), kv[sc + s], sacc);
+        if constexpr (D == 128 && !FQ) {
           __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -248,8 +390,16 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
         pw[jj >> 1][2 * (jj & 1)] = (int)pack_bf16x2(x[0], x[1]);
         pw[jj >> 1][2 * (jj & 1) + 1] = (int)pack_bf16x2(x[2], x[3]);
       }
+      if constexpr (FQ) {                         // rows = keys: the dS wave overwrites them in place
+        lds_char* xb = lds_opaque(xw);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) xw[((pair * QBS + qb) * 2 + u) * 64 + lane] = pw[u];
+        for (int jj = 0; jj < 4; ++jj)
+          *(__attribute__((address_space(3))) i32x2*)(xb + xo(2 * qb + (jj >> 1)) + 16 * (jj & 1)) =
+              i32x2{pw[jj >> 1][2 * (jj & 1)], pw[jj >> 1][2 * (jj & 1) + 1]};
+      } else {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) xw[((pair * QBS + qb) * 2 + u) * 64 + lane] = pw[u];
+      }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int rb = (32 * qb + 16 * kk) * C::RSTR;
@@ -269,10 +419,12 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
 
   // dS wave, step st (one iteration after its P wave): per 32-query block, dP − D (the product
   // accumulates onto −D, read from the stage as the accumulator's start), dS = P (dP − D) with the
-  // bf16 P of its partner, dKᵀ += Qᵀ dS
-  auto step_ds = [&](int st, const char* buf, const i32x4* xr) __attribute__((always_inline)) {
+  // bf16 P of its partner, dKᵀ += Qᵀ dS; with dQ inside the pass, dS (bf16) replaces P in the
+  // exchange tile for the dQ product
+  auto step_ds = [&](int st, const char* buf, i32x4* xr) __attribute__((always_inline)) {
     const char* ob = buf + TILE;
     const f32x4* db = (const f32x4*)(buf + 2 * TILE + BM * 4);
+    lds_char* xb = FQ ? lds_opaque(xr) : nullptr;
 #pragma unroll
     for (int qb = 0; qb < QBS; ++qb) {
       f32x16 pacc;                                // element 4jj + u: query 32qb + 8jj + 4·half + u
@@ -289,7 +441,7 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
         for (int s = 0; s < SB; ++s) fo[s] = *(const i32x4*)(ob + 32 * qb * C::RSTR + so.row[sc + s]);
 #pragma unroll
         for (int s = 0; s < SB; ++s) pacc = mfma32(as_bf16x8(fo[s]), kv[sc + s], pacc);
-        if constexpr (D == 128) {
+        if constexpr (D == 128 && !FQ) {
           __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -301,7 +453,16 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
       bf16x8 sf[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const i32x4 pw = xr[((pair * QBS + qb) * 2 + u) * 64 + lane];
+        i32x4 pw;
+        if constexpr (FQ) {
+          typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+          const int o = xo(2 * qb + u);
+          const i32x2 a = *(const lds_i32x2*)(xb + o);
+          const i32x2 b = *(const lds_i32x2*)(xb + o + 16);
+          pw = i32x4{a.x, a.y, b.x, b.y};
+        } else {
+          pw = xr[((pair * QBS + qb) * 2 + u) * 64 + lane];
+        }
         i32x4 us;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {             // word e: rows of jj = 2u + e/2, values (e%2)·2, +1
@@ -311,6 +472,12 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
           us[e] = (int)pack_bf16x2(p0 * pacc[j0], p1 * pacc[j0 + 1]);
         }
         sf[u] = __builtin_bit_cast(bf16x8, us);
+        if constexpr (FQ) {                       // each lane rewrites exactly the words it read
+          typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+          const int o = xo(2 * qb + u);
+          *(lds_i32x2*)(xb + o) = i32x2{us[0], us[1]};
+          *(lds_i32x2*)(xb + o + 16) = i32x2{us[2], us[3]};
+        }
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -328,17 +495,98 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
     }
   };
 
+  // dQ part of step s for this wave's 16 head-dim columns 16w .. 16w + 15 over the 64 queries of
+  // the step, from the dSᵀ tile `xt` of that step: wait for the previous key tile's part, add this
+  // tile's, hand over (or write dQ). Lane l holds columns 16w + 4(l/16) + 0..3 of query row
+  // q0 + 16·sb + l%16 (sub-block sb of 16 queries).
+  auto dq_phase = [&](int s, const void* xt_buf) __attribute__((always_inline)) {
+    const lds_char* xt = lds_opaque(xt_buf);
+    int h, q0;
+    step_at(s, h, q0);
+    const int l = lane_here(), gi = l >> 4, ii = l & 15;
+    const int kt_last = causal ? q0 / KT : (L + KT - 1) / KT - 1;
+    const bool first = t == 0, last = t == kt_last;
+    int* cnt = fq.cnt + ((size_t)(fq.padoff[doc] / 32 + q0 / 32) * hq + h) * 8 + w;
+    const size_t row0 = (size_t)(s0 + q0) * hq + h;
+    // the block's rows q0 .. q0 + 63 of head h: buffer offsets from row q0 (raw buffer accesses
+    // past the end of the buffer read 0 / write nothing)
+    const unsigned long long rem = fq.acc_bytes - row0 * D * sizeof(float);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        fq.acc + row0 * D, 0, (int)(rem < 0x7fffffffull ? rem : 0x7fffffffull), 0x00020000);
+    const int lo0 = (ii * hq * D + 16 * w + 4 * gi) * (int)sizeof(float), sb_step = 16 * hq * D * (int)sizeof(float);
+    // Hand-over, reading side: the sums travel as device-scope accesses (sc1), coherent on their
+    // own whichever CU or XCD wrote them (a plain load could hit an older copy left in this CU's
+    // L1 by an earlier tile of the chain)
+    if (!first) wait_count(cnt, t, fq.header);
+    f32x4 c[4];                                   // the products accumulate onto the running sums
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb)
+      c[sb] = first ? f32x4{}
+                    : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo0 + sb * sb_step, 0,
+                                                                                     SC1));
+    // this wave's Kᵀ operands (written by this wave at the item's start)
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(kt_slot + w * NP * 64, 0, NP * 64 * 16, 0x00020000);
+    bf16x8 kT[NP];
+#pragma unroll
+    for (int kk = 0; kk < NP; ++kk)
+      kT[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, (kk * 64 + l) * 16, 0, SC1));
+    const int rr = 8 * gi + (ii >> 2);
+    const int fd = ((rr >> 1) & 1) | (((rr >> 3) & 1) << 1);
+#pragma unroll
+    for (int kk = 0; kk < NP; ++kk) {
+      const int pk0 = t * KT + 32 * kk;           // pair kk's first key
+      if ((causal ? q0 + BM - 1 >= pk0 : true) && pk0 < L) {
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+          // rows 32kk + 8(l/16) + (l%16)/4 and + 4 (keys), columns 16sb + 4(l%4) (queries)
+          typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+          const lds_char* a0 = xt + rr * 128 + (((sb ^ fd) & 3) << 5) + 8 * (ii & 3) + 4096 * kk;
+          const bf16x8 b = concat_tr(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0),
+                                     __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 512)));
+          c[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kT[kk], b, c[sb], 0, 0, 0);
+          // one operand pair in flight per product: the phase runs beside the partner wave's
+          // step, with little register room left
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+      }
+    }
+    if (last) {
+      const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(fq.dq + row0 * D, 0, 0x7fffffff, 0x00020000);
+      const int qo0 = (ii * hq * D + 16 * w + 4 * gi) * 2, qsb = 16 * hq * D * 2;
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb)
+        if (q0 + 16 * sb + ii < L)
+          __builtin_amdgcn_raw_buffer_store_b64(
+              i32x2{(int)pack_bf16x2(c[sb][0] * scale, c[sb][1] * scale), (int)pack_bf16x2(c[sb][2] * scale, c[sb][3] * scale)},
+              rq, qo0 + sb * qsb, 0, 0);
+    } else {
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb)
+        if (q0 + 16 * sb + ii < L)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, c[sb]), rs, lo0 + sb * sb_step, 0, SC1);
+    }
+    wait_vmem();                                  // this wave's stores are done before the hand-over
+    if (!last && l == 0) __hip_atomic_store(cnt, t + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+
   // Iteration i: copy step i+1 into `nxt`; P waves run step i on `cur`; dS waves run step i-1
-  // on `prv`. The conditions depend on i only, so every wave meets the same barriers.
-  auto iter = [&](int i, char* cur, char* prv, char* nxt, i32x4* xcur, const i32x4* xprv)
+  // on `prv`; with dQ inside the pass, every wave then adds its dQ part of step i-2 (dSᵀ in
+  // `xdq`; one call site for both roles keeps the register count within two waves per SIMD).
+  // The conditions depend on i only, so every wave meets the same barriers.
+  auto iter = [&](int i, char* cur, char* prv, char* nxt, i32x4* xcur, i32x4* xprv, const i32x4* xdq)
       __attribute__((always_inline)) {
     if (i + 1 < n_steps) stage(i + 1, nxt);
     if (!ds_wave) {
       if (i < n_steps && active(i)) step_p(i, cur, xcur);
     } else {
-      if (i >= 1 && active(i - 1)) step_ds(i - 1, prv, xprv);
+      if (i >= 1 && i - 1 < n_steps && active(i - 1)) step_ds(i - 1, prv, xprv);
     }
     if (i + 1 < n_steps) stage_finish(nxt);
+    if constexpr (FQ) {
+      if (i >= 2 && i - 2 < n_steps) dq_phase(i - 2, xdq);
+    }
     wait_vmem();
     __syncthreads();
   };
@@ -349,10 +597,11 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
   }
   wait_vmem();
   __syncthreads();
-  for (int i = 0; i <= n_steps; i += 3) {
-    iter(i, st_a, st_c, st_b, xp_a, xp_c);
-    if (i + 1 <= n_steps) iter(i + 1, st_b, st_a, st_c, xp_b, xp_a);
-    if (i + 2 <= n_steps) iter(i + 2, st_c, st_b, st_a, xp_c, xp_b);
+  const int last_i = n_steps + (FQ ? 1 : 0);
+  for (int i = 0; i <= last_i; i += 3) {
+    iter(i, st_a, st_c, st_b, xp_a, xp_c, xp_b);
+    if (i + 1 <= last_i) iter(i + 1, st_b, st_a, st_c, xp_b, xp_a, xp_c);
+    if (i + 2 <= last_i) iter(i + 2, st_c, st_b, st_a, xp_c, xp_b, xp_a);
   }
 
   // dS wave: dK = scale·dKᵀ; P wave: dV (lane: key mykey, d = 32 db + 8 jg + 4·half + 0..3)
@@ -380,6 +629,120 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
         }
     }
   }
+}
+
+// One workgroup per (key tile, head split, kv head) of the work list.
+template <int D, int NP, bool CROSS, bool SPLIT>
+__global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    __bf16* __restrict__ dk, __bf16* __restrict__ dv, Plan plan, int total_tokens, int hq, int hkv,
+    float scale, int causal, int n_split, float* __restrict__ part_dk, float* __restrict__ part_dv,
+    const int2* __restrict__ qdoc, int total_k) {
+  using X = DkdvLds<D, NP>;
+  __shared__ __attribute__((aligned(16))) char st_a[X::STAGE];
+  __shared__ __attribute__((aligned(16))) char st_b[X::STAGE];
+  __shared__ __attribute__((aligned(16))) char st_c[X::STAGE];
+  __shared__ i32x4 xp_a[X::XP];
+  __shared__ i32x4 xp_b[X::XP];
+  __shared__ i32x4 xp_c[X::XP];
+  const int ns = SPLIT ? n_split : 1;
+  const int p = blockIdx.x / (hkv * ns), g = blockIdx.x % hkv, split = SPLIT ? (blockIdx.x / hkv) % ns : 0;
+  int s0, L, t, doc;
+  if (!decode_item(plan, p, 32 * NP, false, s0, L, t, &doc)) return;
+  dkdv_item<D, NP, CROSS, SPLIT, false>(q, k, v, dout, lse, delta, dk, dv, total_tokens, hq, hkv, scale, causal,
+                                               n_split, part_dk, part_dv, qdoc, total_k, FusedDq{}, s0, L, t, doc, g,
+                                               split, st_a, st_b, st_c, xp_a, xp_b, xp_c);
+}
+
+// Claims the next key tile for this XCD (one thread of the workgroup). Chains are (document,
+// kv head, head split) in longest-first document order; a chain's key tiles are handed out in
+// order from a 64-bit word of this XCD (high half: chain + 1, low half: next tile) by atomic
+// increment, so all tiles of a chain go to workgroups of one XCD and tile t is handed out after
+// tile t − 1, to a running workgroup. The thread that draws the first tile past a chain's end
+// takes the next chain from the global counter and publishes it (with tile 0 taken); threads
+// that drew later wait for the word to change. Returns false when no chain is left.
+__device__ inline bool claim_tile(const FusedDq& fq, const Plan& pl, int per_doc, int kt, int& chain, int& tile) {
+  unsigned long long* word = (unsigned long long*)(fq.header + 16) + (xcc_id() & 15);
+  auto tiles_of = [&](int c) { return (pl.docinfo[pl.order[c / per_doc]].y + kt - 1) / kt; };
+  for (int spins = 0;;) {
+    const unsigned long long old = atomicAdd(word, 1ull);
+    const int hi = (int)(old >> 32), lo = (int)(old & 0xffffffffull);
+    if (hi == CLAIM_END) return false;
+    const int n = hi == 0 ? 0 : tiles_of(hi - 1);
+    if (lo < n) {
+      chain = hi - 1;
+      tile = lo;
+      return true;
+    }
+    if (lo == n) {
+      for (;;) {
+        const int c = atomicAdd(fq.header + 2, 1);
+        if (c >= fq.n_chains) {
+          atomicExch(word, (unsigned long long)CLAIM_END << 32);
+          return false;
+        }
+        if (tiles_of(c) > 0) {
+          atomicExch(word, ((unsigned long long)(c + 1) << 32) | 1ull);
+          chain = c;
+          tile = 0;
+          return true;
+        }
+      }
+    }
+    while ((int)(__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32) == hi) {
+      if (++spins > SPIN_LIMIT) {
+        atomicOr(fq.header, 8);
+        return false;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+}
+
+// dK, dV and dQ in one pass (self-attention, d = 128): a persistent grid, one workgroup per CU,
+// each claiming key tiles of its XCD until none is left.
+template <bool SPLIT>
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_dq_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    __bf16* __restrict__ dk, __bf16* __restrict__ dv, Plan plan, int total_tokens, int hq, int hkv,
+    float scale, int causal, int n_split, float* __restrict__ part_dk, float* __restrict__ part_dv, FusedDq fq) {
+  using X = DkdvLds<128, 4>;
+  __shared__ __attribute__((aligned(16))) char st_a[X::STAGE];
+  __shared__ __attribute__((aligned(16))) char st_b[X::STAGE];
+  __shared__ __attribute__((aligned(16))) char st_c[X::STAGE];
+  __shared__ i32x4 xp_a[X::XP];
+  __shared__ i32x4 xp_b[X::XP];
+  __shared__ i32x4 xp_c[X::XP];
+  __shared__ int claim[2];
+  const int ns = SPLIT ? n_split : 1;
+  const int per_doc = hkv * ns;
+  for (;;) {
+    if (threadIdx.x == 0) {
+      int c = -1, tl = 0;
+      if (!claim_tile(fq, plan, per_doc, 128, c, tl)) c = -1;
+      claim[0] = c;
+      claim[1] = tl;
+    }
+    __syncthreads();
+    const int c = __builtin_amdgcn_readfirstlane(claim[0]), t = __builtin_amdgcn_readfirstlane(claim[1]);
+    __syncthreads();
+    if (c < 0) return;
+    const int doc = __builtin_amdgcn_readfirstlane(plan.order[c / per_doc]);
+    const int r = c % per_doc;
+    const int2 di = plan.docinfo[doc];
+    dkdv_item<128, 4, false, SPLIT, true>(
+        q, k, v, dout, lse, delta, dk, dv, total_tokens, hq, hkv, scale, causal, n_split, part_dk, part_dv, nullptr,
+        total_tokens, fq, __builtin_amdgcn_readfirstlane(di.x), __builtin_amdgcn_readfirstlane(di.y), t, doc, r % hkv,
+        r / hkv, st_a, st_b, st_c, xp_a, xp_b, xp_c);
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_i32_kernel(int* __restrict__ p, long n) {
+  const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i + 4 <= n) *(i32x4*)(p + i) = i32x4{0, 0, 0, 0};
+  else for (long j = i; j < n; ++j) p[j] = 0;
 }
 
 // Sum of the head-split partial sums in split order: dK = scale·Σ_s part_dk[s], dV = Σ_s part_dv[s]
@@ -636,6 +999,38 @@ static hipError_t launch_dkdv_d(const void* q, const void* k, const void* v, con
       hipLaunchKernelGGL(dkdv_split_reduce_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, stream, pdk,
                          pdv, (__bf16*)dk, (__bf16*)dv, n, n_split, scale, plan.header);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                              const float* delta, void* dq, void* dk, void* dv, const Plan& plan, int T, int hq, int hkv,
+                              float scale, int causal, int n_split, float* part, float* dq_acc, int* cnt, long n_cnt,
+                              const int* padoff, int* header, void* kt, int n_cu, hipStream_t stream) {
+  if (n_cnt > 0)
+    hipLaunchKernelGGL(zero_i32_kernel, dim3((unsigned)((n_cnt / 4 + 255) / 256 + 1)), dim3(256), 0, stream, cnt, n_cnt);
+  FusedDq fq;
+  fq.acc = dq_acc;
+  fq.cnt = cnt;
+  fq.dq = (__bf16*)dq;
+  fq.padoff = padoff;
+  fq.header = header;
+  fq.kt = (i32x4*)kt;
+  fq.acc_bytes = (unsigned long long)T * hq * 128 * sizeof(float);
+  fq.n_chains = plan.n_docs * hkv * n_split;
+  const long n = (long)T * hkv * 128;
+  float* pdk = n_split > 1 ? part : nullptr;
+  float* pdv = n_split > 1 ? part + (size_t)n_split * n : nullptr;
+  const dim3 grid((unsigned)std::max(1, std::min(n_cu, FUSED_MAX_GRID))), block(512);
+#define CFA_FUSED(SP)                                                                                     \
+  hipLaunchKernelGGL((attn_bwd_dkdv_dq_kernel<SP>), grid, block, 0, stream, (const __bf16*)q, (const __bf16*)k, \
+                     (const __bf16*)v, (const __bf16*)dout, lse, delta, (__bf16*)dk, (__bf16*)dv, plan, T, hq, hkv, \
+                     scale, causal, n_split, pdk, pdv, fq)
+  if (n_split > 1) CFA_FUSED(true);
+  else CFA_FUSED(false);
+#undef CFA_FUSED
+  if (n_split > 1 && n > 0)
+    hipLaunchKernelGGL(dkdv_split_reduce_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, stream, pdk, pdv,
+                       (__bf16*)dk, (__bf16*)dv, n, n_split, scale, plan.header);
   return hipGetLastError();
 }
 

@@ -43,6 +43,28 @@ bool sched_naive() {
   return e && strcmp(e, "naive") == 0;
 }
 
+// CFA_DQ_MODE=fused: the bf16 backward at d = 128 sums dQ inside the dK/dV pass in key-tile order
+// instead of running a separate dQ pass that recomputes S and dP (measured slower on MI355X: the
+// hand-over of the fp32 sums between key tiles sits on each step's critical path).
+bool dq_fused_requested() {
+  const char* e = getenv("CFA_DQ_MODE");
+  return e && strcmp(e, "fused") == 0;
+}
+
+// Compute units of the current device (the fused backward's persistent grid), looked up once per
+// device.
+int cu_count() {
+  static int counts[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (counts[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    counts[dev] = n;
+  }
+  return counts[dev];
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 int check_hip(hipError_t e, const char* what) {
@@ -131,13 +153,20 @@ struct WsLayout {
   size_t plan_end;
   size_t delta;             // bwd: float [hq, T]
   size_t dkdv_part;         // bwd bf16 with a head split: float [2][n_split][T][hkv][d]
+  size_t dq_acc, dq_cnt;    // bwd bf16 at d = 128, dQ inside the dK/dV pass: float [T][hq][d], int [t_pad/32][hq][8]
+  size_t dq_kt;             // and the pass's Kᵀ operand slots (FUSED_KT_BYTES)
+  long n_cnt;
+  bool fused_dq;
   int n_split;
   MxBuf vt;                 // fwd MX: V along tokens
   MxBuf dod, dot, vd;       // bwd MX
   size_t total;
 };
 
-WsLayout ws_layout(int pass, const Sizes& s) {
+
+// fused_dq: the bf16 backward at d = 128 sums dQ inside the dK/dV pass (its workspace holds the
+// fp32 sums, their counts and Kᵀ operand slots); otherwise a separate dQ pass recomputes S and dP
+WsLayout ws_layout(int pass, const Sizes& s, bool fused_dq = false) {
   WsLayout w{};
   cfa::PlanLayout pl(s.n_docs);
   w.plan_end = pl.end;
@@ -151,6 +180,16 @@ WsLayout ws_layout(int pass, const Sizes& s) {
       if (w.n_split > 1) {
         w.dkdv_part = off;
         off = cfa::align256(off + sizeof(float) * 2 * (size_t)w.n_split * s.T * s.hkv * s.d);
+      }
+      if (fused_dq && s.d == 128) {
+        w.fused_dq = true;
+        w.dq_acc = off;
+        off = cfa::align256(off + sizeof(float) * (size_t)s.T * s.hq * s.d);
+        w.n_cnt = (long)(t_pad_of(s) / 32) * s.hq * 8;
+        w.dq_cnt = off;
+        off = cfa::align256(off + sizeof(int) * (size_t)w.n_cnt);
+        w.dq_kt = off;
+        off = cfa::align256(off + cfa::FUSED_KT_BYTES);
       }
     }
   }
@@ -220,7 +259,7 @@ const char* cfa_last_error(void) { return g_err; }
 size_t cfa_workspace_bytes(int pass, int total_tokens, int n_docs, int hq, int hkv, int d, int dtype) {
   Sizes s{total_tokens, n_docs, hq, hkv, d, dtype};
   if ((pass != 0 && pass != 1) || check_sizes(s, pass == 1) != CFA_OK) return 0;
-  return ws_layout(pass, s).total;
+  return ws_layout(pass, s, dq_fused_requested()).total;
 }
 
 size_t cfa_saved_bytes(int total_tokens, int n_docs, int hq, int hkv, int d, int dtype) {
@@ -295,10 +334,12 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, c
   return check_hip(e, "forward kernel");
 }
 
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+namespace {
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
              const float* dlse, const void* saved, void* dq, void* dk, void* dv, const int32_t* cu_seqlens,
              const int32_t* cu_seqlens_host, int n_docs, int total_tokens, int max_seqlen, int hq, int hkv, int d,
-             float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+             float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream,
+             bool allow_fused) {
   g_err[0] = 0;
   const Sizes s{total_tokens, n_docs, hq, hkv, d, dtype};
   if (int st = check_sizes(s, true)) return st;
@@ -312,7 +353,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
                         (const void*)dv, (const void*)cu_seqlens})
     if (!aligned(p, 16)) return fail(CFA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
   if (!aligned(workspace, 256)) return fail(CFA_ERR_ALIGN, "workspace must be 256-byte aligned");
-  const WsLayout wl = ws_layout(1, s);
+  const WsLayout wl = ws_layout(1, s, allow_fused);
   if (workspace_bytes < wl.total)
     return fail(CFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, wl.total);
   if (int st = check_cu_host(cu_seqlens_host, n_docs, total_tokens, max_seqlen)) return st;
@@ -358,6 +399,18 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
     mark(2, 1, st);
     return r;
   }
+  if (wl.fused_dq) {
+    char* ws = (char*)workspace;
+    const cfa::PlanLayout pl(n_docs);
+    mark(1, 0, st);
+    int r = check_hip(cfa::launch_bwd_dkdv_dq(q, k, v, dout, lse, delta, dq, dk, dv, plan, total_tokens, hq, hkv, scale,
+                                              causal, wl.n_split, (float*)(ws + wl.dkdv_part), (float*)(ws + wl.dq_acc),
+                                              (int*)(ws + wl.dq_cnt), wl.n_cnt, (const int*)(ws + pl.padoff),
+                                              (int*)(ws + pl.header), ws + wl.dq_kt, cu_count(), st),
+                      "dK/dV/dQ kernel");
+    mark(1, 1, st);
+    return r;
+  }
   mark(1, 0, st);
   if (int r = check_hip(cfa::launch_bwd_dkdv(q, k, v, dout, lse, delta, dk, dv, plan, plan.pref, total_tokens, hq,
                                              hkv, d, scale, causal, wl.n_split,
@@ -371,6 +424,16 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
                     "dQ kernel");
   mark(2, 1, st);
   return r;
+}
+}  // namespace
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+             const float* dlse, const void* saved, void* dq, void* dk, void* dv, const int32_t* cu_seqlens,
+             const int32_t* cu_seqlens_host, int n_docs, int total_tokens, int max_seqlen, int hq, int hkv, int d,
+             float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(q, k, v, o, lse, dout, dlse, saved, dq, dk, dv, cu_seqlens, cu_seqlens_host, n_docs, total_tokens,
+                  max_seqlen, hq, hkv, d, scale, causal, dtype, workspace, workspace_bytes, stream,
+                  dq_fused_requested());
 }
 
 int mx_padded_tokens(int total_tokens, int n_docs) {
@@ -701,14 +764,17 @@ int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
   g_err[0] = 0;
   const Sizes s{total_tokens, n_docs, hq, hkv, d, dtype};
   if (int st = check_sizes(s, true)) return st;
-  const size_t need = ws_layout(1, s).total;
+  // attn_bwd's own plan when it fits (then the results are attn_bwd's bit for bit), else dQ as
+  // its own pass, which needs no fp32 dQ sums (results within rounding of attn_bwd's)
+  const bool fused = dq_fused_requested() && ws_layout(1, s, true).total <= STATIC_SCRATCH_BYTES;
+  const size_t need = ws_layout(1, s, fused).total;
   if (need > STATIC_SCRATCH_BYTES)
     return fail(CFA_ERR_WORKSPACE, "attn_bwd_noalloc: these sizes need %zu bytes of scratch, above its fixed %zu",
                 need, STATIC_SCRATCH_BYTES);
   void* ws = nullptr;
   if (int r = scratch_for_current_device(&ws)) return r;
-  return attn_bwd(q, k, v, o, lse, dout, dlse, saved, dq, dk, dv, cu_seqlens, cu_seqlens_host, n_docs, total_tokens,
-                  max_seqlen, hq, hkv, d, scale, causal, dtype, ws, STATIC_SCRATCH_BYTES, stream);
+  return bwd_impl(q, k, v, o, lse, dout, dlse, saved, dq, dk, dv, cu_seqlens, cu_seqlens_host, n_docs, total_tokens,
+                  max_seqlen, hq, hkv, d, scale, causal, dtype, ws, STATIC_SCRATCH_BYTES, stream, fused);
 }
 
 }  // extern "C"

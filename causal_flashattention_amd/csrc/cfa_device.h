@@ -20,8 +20,10 @@ constexpr float LN2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------- workspace layout
 // All sections 256-byte aligned. The plan part is shared by every pass:
-//   header   int[64]              flag (bit0 cu[0]!=0, bit1 decreasing, bit2 cu[n]!=T;
-//                                  non-zero: every document was made empty), spare
+//   header   int[64]              [0] flag (bit0 cu[0]!=0, bit1 decreasing, bit2 cu[n]!=T:
+//                                  every document was made empty; bit3: a bounded wait of the
+//                                  fused backward gave up), [2] chain counter, [16, 48) per-XCD
+//                                  claim words of the fused backward; all but [0] zeroed by the plan
 //   docinfo  int2[n_docs]         (first packed row, length) after clamping
 //   order    int[n_docs]          documents sorted by length, longest first
 //   pref     int[4][n_docs+1]     item prefix over `order` for tiles of 32, 64, 128, 256 rows

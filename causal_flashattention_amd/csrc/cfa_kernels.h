@@ -40,7 +40,20 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
                            int hq, int hkv, int d, float scale, int causal, int n_split, float* part,
                            hipStream_t stream, const int2* qdoc = nullptr, int Tk = 0);
 
-// Head split of the bf16 dK/dV pass (1 = none): with fewer than 8 kv heads the (key tile,
+// dK, dV and dQ in one pass (bf16 self-attention, d = 128): dQ is summed over the key tiles in a
+// fixed order in dq_acc (float [T][hq][128]) with the counts `cnt` (n_cnt = (t_pad/32)·hq·8 ints,
+// zeroed here) and written as bf16 by the last key tile of each query block. `header` is the
+// plan header (claim words and chain counter, zeroed by the plan kernel; bit 3 of header[0]
+// reports a bounded wait that gave up). kt: FUSED_KT_BYTES of scratch. n_cu: workgroups of the
+// persistent grid (at most 256).
+hipError_t launch_bwd_dkdv_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                              const float* delta, void* dq, void* dk, void* dv, const Plan& plan, int T, int hq, int hkv,
+                              float scale, int causal, int n_split, float* part, float* dq_acc, int* cnt, long n_cnt,
+                              const int* padoff, int* header, void* kt, int n_cu, hipStream_t stream);
+// Bytes of the fused pass's per-workgroup Kᵀ operand slots (256 workgroups × 32 KB).
+constexpr size_t FUSED_KT_BYTES = size_t(256) * 8 * 4 * 64 * 16;
+
+// Head split of the bf16 dK/dV pass// Head split of the bf16 dK/dV pass (1 = none): with fewer than 8 kv heads the (key tile,
 // kv head) grid is split further over the query heads of each group, up to 8 workgroups per key
 // tile (MQA: min(hq, 8)). It depends on the head configuration only, never on the token count or
 // the documents, so a document's dK/dV are bit-identical whatever it is packed with.

@@ -91,6 +91,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int* __restric
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < PLAN_BUCKETS; i += PLAN_THREADS) hist[i] = 0;
   if (tid == 0) sflag = 0;
+  if (tid > 0 && tid < 64) header[tid] = 0;       // chain counter and claim words of the fused backward
   __syncthreads();
   // 1. validate; clamp each document into [0, total]
   int flag = 0;

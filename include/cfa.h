@@ -89,7 +89,12 @@ const char* cfa_status_string(int status);
 const char* cfa_last_error(void);
 
 /* Scratch bytes needed by attn_fwd (pass 0) or attn_bwd (pass 1) for these sizes. Depends only
- * on the sizes, never on the values of cu_seqlens. Returns 0 for invalid sizes. */
+ * on the sizes (and, for the bf16 backward at d = 128, on CFA_DQ_MODE below), never on the values
+ * of cu_seqlens. Returns 0 for invalid sizes.
+ * CFA_DQ_MODE=fused in the environment: the bf16 backward at d = 128 sums dQ inside the dK/dV
+ * pass, in key-tile order (deterministic), instead of a separate dQ pass that recomputes S and dP;
+ * its workspace then also holds fp32 dQ sums [total_tokens, hq, d]. Measured slower on MI355X, so
+ * it is off by default. */
 size_t cfa_workspace_bytes(int pass, int total_tokens, int n_docs, int hq, int hkv, int d, int dtype);
 
 /* Bytes of the forward-to-backward buffer `saved` (the MX dtypes only: the d-blocked E4M3, E2M1,
@@ -274,12 +279,15 @@ int cfa_device_error(const void* workspace, void* stream, int* flag);
  * with the scratch taken from a fixed array inside the library instead of a caller workspace.
  * Each GPU the library runs on holds one such array of 64 MiB (67108864 bytes) until the
  * process ends; its address is looked up once per device on the first call
- * with that device current (no allocation). Sizes whose workspace (cfa_workspace_bytes with pass
- * 1) exceeds the array are rejected with CFA_ERR_WORKSPACE before any launch. Every call on one
- * GPU shares that GPU's array: calls that overlap on one GPU (other streams, other threads) race
- * and must be serialised by the caller. Nothing in the array needs to start at zero (every call
- * writes what it reads). The validation flag of a device-only cu_seqlens is kept in the array
- * and is not readable through cfa_device_error.
+ * with that device current (no allocation). Where attn_bwd's workspace for these sizes fits in
+ * the array the results are attn_bwd's bit for bit; under CFA_DQ_MODE=fused a bf16 call at
+ * d = 128 whose fp32 dQ sums do not fit runs dQ as a separate pass instead (results within
+ * rounding of attn_bwd's); sizes that do not fit either way are rejected with CFA_ERR_WORKSPACE
+ * before any launch. Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (other streams, other threads)
+ * race and must be serialised by the caller. Nothing in the array needs to start at zero (every
+ * call clears or writes what it reads). The validation flag of a device-only cu_seqlens is kept
+ * in the array and is not readable through cfa_device_error.
  */
 int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
                      const void* dout, const float* dlse, const void* saved, void* dq, void* dk, void* dv,
