@@ -109,6 +109,9 @@ def parse():
     ap.add_argument("--mx6-e3m2-workload", type=int, default=0, choices=[0, 4, 5],
                     help="MXFP6/FP8 with E3M2 score operands, reported under 'mxfp6_e3m2' (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--doc-order", default="drawn", choices=["drawn", "longest-last"],
+                    help="pack each workload's documents as drawn, or sorted shortest first (the order "
+                         "that is worst for handing out work by document index)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 3 times (to scale the "
                          "FETCH_SIZE/WRITE_SIZE counters against a kernel of known traffic) and exit")
@@ -298,7 +301,9 @@ def measure(w, mx, steps, warmup):
                "pct_of_mixed_peak": 100.0 * value / mixed_peak(MX_STEP_FORMATS, qk_fmt),
                "mixed_peak": mixed_peak(MX_STEP_FORMATS, qk_fmt)} if mx else {}),
            "config": {"workload": w.name, "total_tokens": T, "n_docs": w.n_docs, "hq": hq, "hkv": hkv, "d": d,
-                      "causal": True, "seed": w.info["seed"], "causal_tflop_per_step": flops / 1e12},
+                      "causal": True, "seed": w.info["seed"], "causal_tflop_per_step": flops / 1e12,
+                      **({"doc_order": w.info["doc_order"]} if "doc_order" in w.info else {}),
+                      **({"schedule": "naive"} if os.environ.get("CFA_SCHED") == "naive" else {})},
            "kernels_ms": {n: round(kern[n]["ms"], 4) for n in kern}, "roofline": roof}
     del q, k, v, do, o, lse, dq, dk, dv, ws_f, ws_b, saved
     torch.cuda.empty_cache()
@@ -408,7 +413,11 @@ def main():
         return
     from causal_flashattention_amd import workloads as W
 
-    w = W.make_workload(args.workload)
+    def load(k):
+        wk = W.make_workload(k)
+        return W.longest_last(wk) if args.doc_order == "longest-last" else wk
+
+    w = load(args.workload)
     head = measure(w, False, args.steps, args.warmup)
     out = {
         "metric": METRIC, "value": head["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -421,27 +430,27 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
     del w
     if args.mx_workload:
-        wm = W.make_workload(args.mx_workload)
+        wm = load(args.mx_workload)
         mres = measure(wm, True, args.steps, args.warmup)
         mres["dtype"] = "mxfp8 (E4M3 + E8M0 per 32; the dS products dK = dS^T Q and dQ = dS K and the diagonal tiles in bf16)"
         mres["unit"] = "TFLOP/s"
         out["mxfp8"] = mres
     if args.mx4_workload:
-        wm = W.make_workload(args.mx4_workload)
+        wm = load(args.mx4_workload)
         mres = measure(wm, "mxfp4", args.steps, args.warmup)
         mres["dtype"] = "mxfp4/fp8 (QK^T on E2M1 + E8M0 per 32, the rest as mxfp8)"
         mres["unit"] = "TFLOP/s"
         mres["peak_note"] = "pct_of_peak against fp4 10.1 PFLOP/s; mixed_peak = n / sum(1/peak) over the counted GEMM units"
         out["mxfp4"] = mres
     if args.mx6_workload:
-        wm = W.make_workload(args.mx6_workload)
+        wm = load(args.mx6_workload)
         mres = measure(wm, "mxfp6", args.steps, args.warmup)
         mres["dtype"] = "mxfp6/fp8 (QK^T on E2M3 + E8M0 per 32, the rest as mxfp8)"
         mres["unit"] = "TFLOP/s"
         mres["peak_note"] = "pct_of_peak against fp6 10.1 PFLOP/s; mixed_peak = n / sum(1/peak) over the counted GEMM units"
         out["mxfp6"] = mres
     if args.mx6_e3m2_workload:
-        wm = W.make_workload(args.mx6_e3m2_workload)
+        wm = load(args.mx6_e3m2_workload)
         mres = measure(wm, "mxfp6_e3m2", args.steps, args.warmup)
         mres["dtype"] = "mxfp6/fp8 (QK^T on E3M2 + E8M0 per 32, the rest as mxfp8)"
         mres["unit"] = "TFLOP/s"

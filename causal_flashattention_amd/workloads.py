@@ -242,3 +242,31 @@ def decode_batch_lengths(seed, n_seqs, lo=512, hi=32768):
     """Context lengths of a serving batch: floor(exp(U(ln lo, ln hi))) per sequence."""
     rng = np.random.Generator(np.random.PCG64(seed))
     return [int(math.floor(math.exp(rng.uniform(math.log(lo), math.log(hi))))) for _ in range(n_seqs)]
+
+
+def reorder_documents(w, order):
+    """The same documents packed in another order: document ``order[i]`` of ``w`` becomes
+    document ``i``, its tokens moving with it (Q, K, V and dO rows alike)."""
+    cu = np.asarray(w.cu_seqlens, dtype=np.int64)
+    order = [int(i) for i in order]
+    if sorted(order) != list(range(w.n_docs)):
+        raise ValueError("order must be a permutation of the document indices")
+    rows = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in order]) if order else np.zeros(0, np.int64)
+
+    def take(a):
+        return None if a is None else np.ascontiguousarray(a[rows])
+    lengths = [int(cu[i + 1] - cu[i]) for i in order]
+    info = dict(w.info)
+    info["doc_order"] = "permuted"
+    return Workload(name=w.name, total_tokens=w.total_tokens, hq=w.hq, hkv=w.hkv, d=w.d, dtype=w.dtype,
+                    scale=w.scale, cu_seqlens=cu_from_lengths(lengths), q=take(w.q), k=take(w.k),
+                    v=take(w.v), do=take(w.do), causal=w.causal, info=info)
+
+
+def longest_last(w):
+    """``w`` with its documents sorted by length, shortest first (ties keep their order): the
+    packing order that is worst for a scheduler that hands out work in document order."""
+    L = np.diff(np.asarray(w.cu_seqlens, dtype=np.int64))
+    out = reorder_documents(w, np.argsort(L, kind="stable"))
+    out.info["doc_order"] = "longest_last"
+    return out

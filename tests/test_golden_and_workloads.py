@@ -65,3 +65,18 @@ def test_flop_count():
     assert W.causal_flops_fwd_bwd(cu, 2, 8) == 3.5 * 4 * 8 * 2 * 16
     w3_pairs = 32768 * 32769 / 2
     assert W.causal_flops_fwd(np.array([0, 32768]), 32, 128) == 4 * 128 * 32 * w3_pairs
+
+
+def test_longest_last_moves_whole_documents():
+    w = W.make_random(3, [5, 17, 2, 9, 17], hq=2, hkv=1, d=64)
+    r = W.longest_last(w)
+    L = list(np.diff(r.cu_seqlens))
+    assert L == [2, 5, 9, 17, 17] and r.info["doc_order"] == "longest_last"
+    cu = w.cu_seqlens
+    for new, old in enumerate([2, 0, 3, 1, 4]):          # stable: the first 17 stays before the second
+        a, b = r.cu_seqlens[new], r.cu_seqlens[new + 1]
+        for name in ("q", "k", "v", "do"):
+            assert np.array_equal(getattr(r, name)[a:b], getattr(w, name)[cu[old]:cu[old + 1]])
+    assert r.flops_fwd_bwd() == w.flops_fwd_bwd()
+    with pytest.raises(ValueError):
+        W.reorder_documents(w, [0, 0, 1, 2, 3])
