@@ -71,13 +71,14 @@ KERNELS_BF16_FUSED = {
     "bwd_pre_kernel": ("bwd", 0, 0.0),
     "attn_bwd_dkdv_dq_kernel": ("bwd", 1, 5.0),
 }
+# MX: one operand pass per direction -- mx_prep_fwd_kernel writes Q_d, K_d, V_d and V_t from one
+# read of Q, K and V; mx_prep_bwd_kernel writes D, dO_d and dO_t from one read of O and dO
 KERNELS_MX = {
     "attn_fwd_mx_kernel": ("fwd", 0, 2.0),
-    "mx_quantize_fwd": ("fwd", 1, 0.0),
-    "bwd_pre_kernel": ("bwd", 0, 0.0),
+    "mx_prep_fwd_kernel": ("fwd", 1, 0.0),
+    "mx_prep_bwd_kernel": ("bwd", 0, 0.0),
     "attn_bwd_dkdv_mx_kernel": ("bwd", 1, 4.0),
     "attn_bwd_dq_mx_kernel": ("bwd", 2, 1.0),
-    "mx_quantize_bwd": ("bwd", 3, 0.0),
 }
 KERNEL_SOURCES = {
     "attn_fwd_bf16_kernel": "attn_fwd.hip",
@@ -88,8 +89,8 @@ KERNEL_SOURCES = {
     "attn_fwd_mx_kernel": "attn_fwd_mx.hip",
     "attn_bwd_dkdv_mx_kernel": "attn_bwd_mx.hip",
     "attn_bwd_dq_mx_kernel": "attn_bwd_mx.hip",
-    "mx_quantize_fwd": "mx_quantize.hip",
-    "mx_quantize_bwd": "mx_quantize.hip",
+    "mx_prep_fwd_kernel": "mx_quantize.hip",
+    "mx_prep_bwd_kernel": "mx_quantize.hip",
 }
 
 
@@ -195,6 +196,29 @@ def _f64(a):
     return W.bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
 
 
+def operand_pass_rates(w, qk_fmt, kern):
+    """Algorithmic HBM bytes of the two MX operand passes (every input read once, every copy
+    written once, padding columns of the token-blocked copies included) over their event time."""
+    T, hq, hkv, d = w.total_tokens, w.hq, w.hkv, w.d
+    t_pad = 32 * ((T + 31) // 32) + 32 * w.n_docs
+    code = {"fp8": 1.0, "fp4": 0.5, "fp6": 0.75}[qk_fmt]
+    sc = 1.0 / 32
+    fwd = (2 * T * (hq + 2 * hkv) * d                       # Q, K, V read (bf16)
+           + T * (hq + hkv) * d * (code + sc)                # Q_d, K_d (score format)
+           + T * hkv * d * (1 + sc)                          # V_d (E4M3)
+           + hkv * d * t_pad * (1 + sc))                     # V_t (E4M3, padded columns)
+    bwd = (2 * 2 * T * hq * d                                # O, dO read (bf16)
+           + 4 * T * hq                                      # D written (fp32)
+           + T * hq * d * (1 + sc)                           # dO_d
+           + hq * d * t_pad * (1 + sc))                      # dO_t
+    out = {}
+    for name, nbytes in (("mx_prep_fwd_kernel", fwd), ("mx_prep_bwd_kernel", bwd)):
+        ms = kern[name]["ms"]
+        out[name] = {"algorithmic_bytes": nbytes, "ms": ms, "GB_per_s": nbytes / (ms * 1e-3) / 1e9,
+                     "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return out
+
+
 def measure(w, mx, steps, warmup):
     """Warm up, then time `steps` fwd+bwd steps; per-kernel HIP events inside the timed region."""
     import ctypes
@@ -276,7 +300,7 @@ def measure(w, mx, steps, warmup):
             for n, (_, _, u) in kernels.items()}
     # per-step spread from the same events: first forward kernel's start to the last backward
     # kernel's end (the forward's plan launch, ~13 us, precedes the span)
-    first = "mx_quantize_fwd" if mx else "attn_fwd_bf16_kernel"      # launch order, not event slot
+    first = "mx_prep_fwd_kernel" if mx else "attn_fwd_bf16_kernel"      # launch order, not event slot
     last = "attn_bwd_dq_mx_kernel" if mx else ("attn_bwd_dkdv_dq_kernel" if fused else "attn_bwd_dq_kernel")
     spans = [ev[first][i][0].elapsed_time(ev[last][i][1]) for i in range(K)]
     dom = max(kern, key=lambda n: kern[n]["ms"])
@@ -305,6 +329,8 @@ def measure(w, mx, steps, warmup):
                       **({"doc_order": w.info["doc_order"]} if "doc_order" in w.info else {}),
                       **({"schedule": "naive"} if os.environ.get("CFA_SCHED") == "naive" else {})},
            "kernels_ms": {n: round(kern[n]["ms"], 4) for n in kern}, "roofline": roof}
+    if mx:
+        res["operand_passes"] = operand_pass_rates(w, qk_fmt, kern)
     del q, k, v, do, o, lse, dq, dk, dv, ws_f, ws_b, saved
     torch.cuda.empty_cache()
     return res

@@ -105,6 +105,8 @@ int check_sizes(const Sizes& s, bool bwd) {
     return fail(CFA_ERR_UNSUPPORTED, "dtype %d unknown", s.dtype);
   if (is_mx(s.dtype)) {
     if (s.d != 128) return fail(CFA_ERR_UNSUPPORTED, "the MX paths support d = 128 only (got %d)", s.d);
+    // the operand passes address a 32-token block's rows as a 32-bit offset r·hq·d
+    if (s.hq > 65536) return fail(CFA_ERR_UNSUPPORTED, "the MX paths take hq <= 65536 (got %d)", s.hq);
     // token-blocked rows are addressed as channel·t_pad + column in 32 bits
     if ((long)((s.T + 31) / 32 * 32 + 32L * s.n_docs) * s.d > 0x7fffffffL)
       return fail(CFA_ERR_UNSUPPORTED, "the MX paths need d·(32·ceil(T/32) + 32·n_docs) < 2^31 (T = %d, n_docs = %d)",
@@ -159,7 +161,7 @@ struct WsLayout {
   bool fused_dq;
   int n_split;
   MxBuf vt;                 // fwd MX: V along tokens
-  MxBuf dod, dot, vd;       // bwd MX
+  MxBuf dod, dot;           // bwd MX
   size_t total;
 };
 
@@ -199,7 +201,6 @@ WsLayout ws_layout(int pass, const Sizes& s, bool fused_dq = false) {
     } else {
       off = add_mx_d(off, s, s.hq, w.dod);
       off = add_mx_t(off, s, s.hq, w.dot);
-      off = add_mx_d(off, s, s.hkv, w.vd);
     }
   }
   w.total = off;
@@ -207,9 +208,9 @@ WsLayout ws_layout(int pass, const Sizes& s, bool fused_dq = false) {
 }
 
 // forward-to-backward buffer of the MX paths: Q_d and K_d (E4M3, E2M1 for CFA_MXFP4, E2M3 for CFA_MXFP6,
-// E3M2 for CFA_MXFP6_E3M2)
+// E3M2 for CFA_MXFP6_E3M2) and V_d (E4M3, the dP operand), written by the forward's one pass over V
 struct SavedLayout {
-  MxBuf qd, kd;
+  MxBuf qd, kd, vd;
   size_t total;
 };
 
@@ -219,6 +220,7 @@ SavedLayout saved_layout(const Sizes& s) {
   const int qf = score_format(s.dtype);
   off = add_mx_d(off, s, s.hq, v.qd, qf);
   off = add_mx_d(off, s, s.hkv, v.kd, qf);
+  off = add_mx_d(off, s, s.hkv, v.vd);
   v.total = off;
   return v;
 }
@@ -301,20 +303,12 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, c
     const cfa::PlanLayout pl(n_docs);
     const int tp = t_pad_of(s);
     const int qf = score_format(dtype);
-    auto quant_d = [&](const void* x, long n, uint8_t* c, uint8_t* sc, hipStream_t str) {
-      return qf == 1 ? cfa::launch_mx_quantize_d_fp4(x, n, c, sc, str)
-           : qf >= 2 ? cfa::launch_mx_quantize_d_fp6(x, n, d, qf, c, sc, str)
-                     : cfa::launch_mx_quantize_d(x, n, c, sc, str);
-    };
+    auto S = [&](size_t off) { return (uint8_t*)sv + off; };
+    cfa::MxPrepOut po{S(sl.qd.codes), S(sl.qd.scales), S(sl.kd.codes), S(sl.kd.scales), S(sl.vd.codes),
+                      S(sl.vd.scales), (uint8_t*)ws + wl.vt.codes, (uint8_t*)ws + wl.vt.scales};
     mark(1, 0, st);
-    if (int r = check_hip(quant_d(q, (long)total_tokens * hq * d, (uint8_t*)sv + sl.qd.codes,
-                                  (uint8_t*)sv + sl.qd.scales, st), "quantize Q"))
-      return r;
-    if (int r = check_hip(quant_d(k, (long)total_tokens * hkv * d, (uint8_t*)sv + sl.kd.codes,
-                                  (uint8_t*)sv + sl.kd.scales, st), "quantize K"))
-      return r;
-    if (int r = check_hip(cfa::launch_mx_quantize_t(v, total_tokens, hkv, d, ws, n_docs, (uint8_t*)ws + wl.vt.codes,
-                                                    (uint8_t*)ws + wl.vt.scales, tp, true, st), "quantize V"))
+    if (int r = check_hip(cfa::launch_mx_prep_fwd(q, k, v, total_tokens, hq, hkv, ws, n_docs, qf, po, tp, st),
+                          "quantize Q, K, V"))
       return r;
     mark(1, 1, st);
     mark(0, 0, st);
@@ -363,9 +357,12 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   if (total_tokens == 0) return CFA_OK;
   const cfa::Plan plan = make_plan(workspace, n_docs);
   float* delta = (float*)((char*)workspace + wl.delta);
-  mark(0, 0, st);
-  if (int r = check_hip(cfa::launch_bwd_pre(o, dout, dlse, delta, total_tokens, hq, d, st), "bwd preprocess")) return r;
-  mark(0, 1, st);
+  if (!is_mx(dtype)) {
+    mark(0, 0, st);
+    if (int r = check_hip(cfa::launch_bwd_pre(o, dout, dlse, delta, total_tokens, hq, d, st), "bwd preprocess"))
+      return r;
+    mark(0, 1, st);
+  }
   if (is_mx(dtype)) {
     char* ws = (char*)workspace;
     const char* sv = (const char*)saved;
@@ -374,17 +371,19 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
     const int tp = t_pad_of(s);
     const int* padoff = (const int*)(ws + pl.padoff);
     auto U = [&](const MxBuf& b, bool codes) { return (uint8_t*)ws + (codes ? b.codes : b.scales); };
-    mark(3, 0, st);
-    hipError_t e = cfa::launch_mx_quantize_d(dout, (long)total_tokens * hq * d, U(wl.dod, true), U(wl.dod, false), st);
-    if (!e) e = cfa::launch_mx_quantize_t(dout, total_tokens, hq, d, ws, n_docs, U(wl.dot, true), U(wl.dot, false), tp, true, st);
-    if (!e) e = cfa::launch_mx_quantize_d(v, (long)total_tokens * hkv * d, U(wl.vd, true), U(wl.vd, false), st);
-    mark(3, 1, st);
-    if (int r = check_hip(e, "backward quantisation")) return r;
+    // D and both dO copies in one pass over O and dO (V_d came with the forward's pass over V)
+    cfa::MxPrepOut po{U(wl.dod, true), U(wl.dod, false), nullptr, nullptr, nullptr, nullptr, U(wl.dot, true),
+                      U(wl.dot, false)};
+    mark(0, 0, st);
+    if (int r = check_hip(cfa::launch_mx_prep_bwd(o, dout, dlse, delta, total_tokens, hq, ws, n_docs, po, tp, st),
+                          "backward preparation"))
+      return r;
+    mark(0, 1, st);
     cfa::MxOperands m;
     m.qd = (const uint8_t*)sv + sl.qd.codes; m.qd_sc = (const uint8_t*)sv + sl.qd.scales;
     m.kd = (const uint8_t*)sv + sl.kd.codes; m.kd_sc = (const uint8_t*)sv + sl.kd.scales;
     m.dod = U(wl.dod, true); m.dod_sc = U(wl.dod, false);
-    m.vd = U(wl.vd, true); m.vd_sc = U(wl.vd, false);
+    m.vd = (const uint8_t*)sv + sl.vd.codes; m.vd_sc = (const uint8_t*)sv + sl.vd.scales;
     m.dot = U(wl.dot, true); m.dot_sc = U(wl.dot, false);
     mark(1, 0, st);
     if (int r = check_hip(cfa::launch_bwd_dkdv_mx(m, q, dout, lse, delta, dk, dv, plan, plan.pref, padoff, total_tokens,
@@ -461,6 +460,9 @@ int mx_quantize(const void* x, int total_tokens, int h, int d, const int32_t* cu
   if (n_docs < 1) return fail(CFA_ERR_SHAPE, "n_docs = %d < 1", n_docs);
   if (!cu_seqlens || !workspace) return fail(CFA_ERR_NULL, "cu_seqlens and workspace must not be NULL for axes 1, 2");
   if ((long)t_pad * d > 0x7fffffffL) return fail(CFA_ERR_UNSUPPORTED, "t_pad·d must stay below 2^31");
+  if (h > 65536) return fail(CFA_ERR_UNSUPPORTED, "axes 1 and 2 take h <= 65536 heads (got %d)", h);
+  if ((long)((t_pad + 127) / 128) * h > 0x7fffffffL)
+    return fail(CFA_ERR_UNSUPPORTED, "axes 1 and 2 need h·ceil(t_pad/128) < 2^31 workgroups");
   if (t_pad % 32 || t_pad < mx_padded_tokens(total_tokens, n_docs))
     return fail(CFA_ERR_SHAPE, "t_pad = %d must be a multiple of 32 and >= %d", t_pad,
                 mx_padded_tokens(total_tokens, n_docs));

@@ -42,6 +42,12 @@ struct PlanLayout {
   }
 };
 
+// Output sections of the fused MX operand preparation kernels: up to three d-blocked copies
+// (a, b, c: codes and scales) and one kernel-layout token-blocked copy (t).
+struct MxPrepOut {
+  uint8_t *a_codes, *a_scales, *b_codes, *b_scales, *c_codes, *c_scales, *t_codes, *t_scales;
+};
+
 struct Plan {
   const int* header;     // header[0]: the validation flag (non-zero: every document is empty)
   const int2* docinfo;

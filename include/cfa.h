@@ -45,6 +45,8 @@
  *    o = 0 and lse = -inf).
  *  - CFA_SCHED=naive in the environment (a diagnostic) schedules documents in index order
  *    instead of longest first; results are bit-identical either way.
+ *  - Size limits of the MX dtypes (CFA_ERR_UNSUPPORTED otherwise): d = 128, hq <= 65536 and
+ *    d·(32·ceil(total_tokens/32) + 32·n_docs) < 2^31.
  */
 #ifndef CFA_H
 #define CFA_H
@@ -97,9 +99,16 @@ const char* cfa_last_error(void);
  * it is off by default. */
 size_t cfa_workspace_bytes(int pass, int total_tokens, int n_docs, int hq, int hkv, int d, int dtype);
 
-/* Bytes of the forward-to-backward buffer `saved` (the MX dtypes only: the d-blocked E4M3, E2M1,
+/* Bytes of the forward-to-backward buffer `saved` (the MX dtypes only): the d-blocked E4M3, E2M1,
  * E2M3 or E3M2 copies of Q and K with their scales, reused by the backward so both passes see
- * identical scores). 0 for the other dtypes and for invalid sizes. */
+ * identical scores, and the d-blocked E4M3 copy of V (the backward's dP operand), which the
+ * forward writes in the same pass that reads V for its token-blocked copy -- quantised operands
+ * reused in another orientation instead of being quantised again (FLAMIA page, "FLAMIA Mimarisi
+ * ve Temel Tasarım İlkeleri": token-block scaling, fused quantisation). Layout, each section
+ * starting at a 256-byte boundary: Q_d codes [T, hq, c], Q_d scales [T, hq, d/32], K_d codes
+ * [T, hkv, c], K_d scales [T, hkv, d/32], V_d codes [T, hkv, d], V_d scales [T, hkv, d/32], with
+ * c = d (E4M3), d/2 (E2M1) or 3d/4 (6-bit) bytes as mx_quantize and mx_quantize_fp4/fp6 store
+ * them. 0 for the other dtypes and for invalid sizes. */
 size_t cfa_saved_bytes(int total_tokens, int n_docs, int hq, int hkv, int d, int dtype);
 
 /*
@@ -153,7 +162,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
  *            [h, d, t_pad] with the 4-token pieces of each 32-token block stored in the order
  *            0,2,4,6,1,3,5,7 (bytes 16g..16g+15 of a block hold the tokens a matrix-core lane
  *            group g reads), scales block-major [h, t_pad/32, d].
- * d·t_pad must stay below 2^31 (axes 1, 2).
+ * d·t_pad must stay below 2^31 and h at most 65536 (axes 1, 2; CFA_ERR_UNSUPPORTED otherwise).
  * Token-block scaling of this kind, with blocks that never cross a document, is the FLAMIA
  * page's document-local scaling ("FLAMIA Mimarisi ve Temel Tasarım İlkeleri"); the element and
  * scale rules are the OCP MX definitions of E4M3 and E8M0 (the page names MXFP8 only).
@@ -257,9 +266,9 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const u
  * Per-kernel timing for measurement tools. While set on the calling thread, the attention
  * calls record events[2*i] on their stream just before launching their i-th main kernel and
  * events[2*i+1] just after it (the work-list kernel is not counted). Kernel order:
- *   attn_fwd: 0 = forward attention, 1 = (MXFP8) the Q, K, V quantisation passes together;
- *   attn_bwd: 0 = D = rowsum(dO*O), 1 = dK/dV, 2 = dQ, 3 = (MXFP8) the dO (both axes) and V
- *             quantisation passes together;
+ *   attn_fwd: 0 = forward attention, 1 = (MX dtypes) the one pass that quantises Q, K and V;
+ *   attn_bwd: 0 = D = rowsum(dO*O) (MX dtypes: the one pass that also writes both dO copies),
+ *             1 = dK/dV, 2 = dQ;
  *   attn_decode: 0 = chunk partials, 1 = their merge.
  * Entries may be NULL (not recorded). The caller owns the hipEvent_t handles and keeps the
  * array alive while it is set; n_pairs = 0 (events NULL) switches recording off.
