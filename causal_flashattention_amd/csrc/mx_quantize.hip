@@ -479,6 +479,63 @@ __device__ inline void quant_d_chunks(const i32x4* raw, const BlockGroup& bg, in
   }
 }
 
+// 6-bit score copies (QF 2: E2M3, 3: E3M2), one whole 32-channel block per lane: v_cvt_scalef32_pk32_
+// {fp6,bf6}_bf16 divides 32 bf16 values by 2^e, rounds to nearest even, saturates at the format's
+// largest value (7.5 / 28) and packs code i at bits 6i..6i+5 of 192 -- the block layout the score
+// product reads. An in-bounds probe over every bf16 pattern (in groups of 32) and block exponents
+// -127..125 matched the software encoders (e2m3_code / e3m2_code after the clamp) bit for bit.
+// Lane mapping: (row, block) pair tid + 256 j (j = 0, 1) is row 64 j + tid/4, block tid % 4; the
+// row's 32-token block is 2 j + tid/128 and its row within it (tid/4) % 32.
+template <int D>
+__device__ inline void load_blocks6(const __bf16* __restrict__ x, int h, int head, const BlockGroup& bg,
+                                    i32x4 (&raw)[2][4]) {
+  const int kb = threadIdx.x % 4, r = (threadIdx.x / 4) % 32, hi = threadIdx.x >= 128;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int b0 = 2 * j;                         // block 2j (tid < 128) or 2j + 1
+    const int tok0 = hi ? bg.tok0[b0 + 1] : bg.tok0[b0], nt = hi ? bg.ntok[b0 + 1] : bg.ntok[b0];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) raw[j][c] = load_row_chunk<D, false>(x, h, head, tok0, r, nt, 4 * kb + c);
+  }
+}
+
+template <int QF>
+__device__ inline void quant6_blocks(const i32x4 (&raw)[2][4], const BlockGroup& bg, int h, int head,
+                                     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  constexpr int D = 128;
+  typedef __attribute__((ext_vector_type(32))) __bf16 bf16x32;
+  typedef __attribute__((ext_vector_type(6))) unsigned u32x6;
+  const int kb = threadIdx.x % 4, r = (threadIdx.x / 4) % 32, hi = threadIdx.x >= 128;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int b0 = 2 * j;
+    const int tok0 = hi ? bg.tok0[b0 + 1] : bg.tok0[b0], nt = hi ? bg.ntok[b0 + 1] : bg.ntok[b0];
+    if (r >= nt) continue;
+    uint32_t w[16];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      w[4 * c] = (uint32_t)raw[j][c].x;
+      w[4 * c + 1] = (uint32_t)raw[j][c].y;
+      w[4 * c + 2] = (uint32_t)raw[j][c].z;
+      w[4 * c + 3] = (uint32_t)raw[j][c].w;
+    }
+    const uint32_t ab = amax_bits<16>(w);
+    const bool bad = ab >= 0x7F80u;
+    // floor(log2 amax) - top exponent (2 for E2M3, 4 for E3M2), clamped below at -127
+    const int e = max((int)(ab >> 7) - (QF == 2 ? 129 : 131), -127);
+    const bf16x32 xv = __builtin_bit_cast(bf16x32, w);
+    const float sc = __builtin_amdgcn_ldexpf(1.f, e);
+    u32x6 cw = QF == 2 ? __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(xv, sc)
+                       : __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(xv, sc);
+    if (bad) cw = u32x6{0u, 0u, 0u, 0u, 0u, 0u};
+    const size_t row0 = (size_t)tok0 * h + head;
+    uint8_t* rowp = codes + row0 * (3 * D / 4) + (uint32_t)(r * h) * (3 * D / 4);
+    *(i32x4*)(rowp + 16 * kb) = i32x4{(int)cw[0], (int)cw[1], (int)cw[2], (int)cw[3]};
+    *(i32x2*)(rowp + D / 2 + 8 * kb) = i32x2{(int)cw[4], (int)cw[5]};
+    scales[row0 * (D / 32) + (uint32_t)(r * h) * (D / 32) + kb] = bad ? 0xFF : (uint8_t)(e + 127);
+  }
+}
+
 // The lane's eight chunks (row tid/16 + 16 i, 16-byte chunk tid % 16) of one head and group; MASK:
 // zeros in rows past a block's tokens (needed only where the rows feed a token-blocked tile).
 template <int D, bool MASK>
@@ -509,15 +566,28 @@ __global__ __launch_bounds__(256, 3) void mx_prep_fwd_kernel(const __bf16* __res
   const BlockGroup bg = block_group(g, docinfo, padoff, n_docs);
   if (!bg.live[0]) return;
   const bool kv = head < hkv;
-  i32x4 rq[8], rk[8], rv[8];
-  load_chunks<D, false>(q, hq, head, bg, rq);
-  if (kv) {
-    load_chunks<D, false>(k, hkv, head, bg, rk);
-    load_chunks<D, true>(v, hkv, head, bg, rv);
+  i32x4 rv[8];
+  if constexpr (QF >= 2) {                        // 6-bit score copies: one block per lane
+    i32x4 rq[2][4], rk[2][4];
+    load_blocks6<D>(q, hq, head, bg, rq);
+    if (kv) {
+      load_blocks6<D>(k, hkv, head, bg, rk);
+      load_chunks<D, true>(v, hkv, head, bg, rv);
+    }
+    quant6_blocks<QF>(rq, bg, hq, head, out.a_codes, out.a_scales);
+    if (!kv) return;
+    quant6_blocks<QF>(rk, bg, hkv, head, out.b_codes, out.b_scales);
+  } else {
+    i32x4 rq[8], rk[8];
+    load_chunks<D, false>(q, hq, head, bg, rq);
+    if (kv) {
+      load_chunks<D, false>(k, hkv, head, bg, rk);
+      load_chunks<D, true>(v, hkv, head, bg, rv);
+    }
+    quant_d_chunks<QF>(rq, bg, hq, head, out.a_codes, out.a_scales);
+    if (!kv) return;
+    quant_d_chunks<QF>(rk, bg, hkv, head, out.b_codes, out.b_scales);
   }
-  quant_d_chunks<QF>(rq, bg, hq, head, out.a_codes, out.a_scales);
-  if (!kv) return;
-  quant_d_chunks<QF>(rk, bg, hkv, head, out.b_codes, out.b_scales);
   quant_d_chunks<0>(rv, bg, hkv, head, out.c_codes, out.c_scales);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
