@@ -71,8 +71,9 @@ KERNELS_BF16_FUSED = {
     "bwd_pre_kernel": ("bwd", 0, 0.0),
     "attn_bwd_dkdv_dq_kernel": ("bwd", 1, 5.0),
 }
-# MX: one operand pass per direction -- mx_prep_fwd_kernel writes Q_d, K_d, V_d and V_t from one
-# read of Q, K and V; mx_prep_bwd_kernel writes D, dO_d and dO_t from one read of O and dO
+# MX: one operand pass per direction -- mx_prep_fwd_kernel writes K_d, V_d and V_t from one read of
+# K and V (the MX forward kernel quantises Q from the rows it reads); mx_prep_bwd_kernel writes D,
+# dO_d and dO_t from one read of O and dO
 KERNELS_MX = {
     "attn_fwd_mx_kernel": ("fwd", 0, 2.0),
     "mx_prep_fwd_kernel": ("fwd", 1, 0.0),
@@ -203,8 +204,8 @@ def operand_pass_rates(w, qk_fmt, kern):
     t_pad = 32 * ((T + 31) // 32) + 32 * w.n_docs
     code = {"fp8": 1.0, "fp4": 0.5, "fp6": 0.75}[qk_fmt]
     sc = 1.0 / 32
-    fwd = (2 * T * (hq + 2 * hkv) * d                       # Q, K, V read (bf16)
-           + T * (hq + hkv) * d * (code + sc)                # Q_d, K_d (score format)
+    fwd = (2 * T * (2 * hkv) * d                            # K, V read (bf16); Q is quantised by
+           + T * hkv * d * (code + sc)                       # K_d (score format)   the forward kernel
            + T * hkv * d * (1 + sc)                          # V_d (E4M3)
            + hkv * d * t_pad * (1 + sc))                     # V_t (E4M3, padded columns)
     bwd = (2 * 2 * T * hq * d                                # O, dO read (bf16)
@@ -429,10 +430,18 @@ def main():
         import torch
         a = torch.empty(args.copy_calibration // 2, dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
         b = torch.empty_like(a)
-        for _ in range(3):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record()
+        for i in range(3):
             b.copy_(a)
+            ev[i + 1].record()
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": a.numel() * 2}))
+        ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(3)]
+        nb = a.numel() * 2
+        # the device copy's own rate (read + write bytes over its time): the practical ceiling of a
+        # pass that reads and writes comparable amounts, next to the 8 TB/s datasheet figure
+        print(json.dumps({"copy_calibration_bytes": nb, "copy_ms": ms,
+                          "copy_GB_per_s": 2 * nb / (min(ms[1:]) * 1e-3) / 1e9}))
         return
     if args.decode:
         main_decode(args)

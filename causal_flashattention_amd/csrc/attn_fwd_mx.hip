@@ -32,6 +32,7 @@
 // layout (mx_quantize.hip): the bytes 16g..16g+15 of each 32-key block hold exactly the keys
 // whose probabilities lane group g holds, so no data is permuted on chip.
 #include "cfa_device.h"
+#include "cfa_mx.h"
 
 namespace cfa {
 
@@ -57,7 +58,7 @@ struct MxFwdTile {
 
 template <int HPW, int QF>
 __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
-    const uint8_t* __restrict__ qd, const uint8_t* __restrict__ qd_sc, const uint8_t* __restrict__ kd,
+    const __bf16* __restrict__ q, uint8_t* __restrict__ qd, uint8_t* __restrict__ qd_sc, const uint8_t* __restrict__ kd,
     const uint8_t* __restrict__ kd_sc, const uint8_t* __restrict__ vt, const uint8_t* __restrict__ vt_sc,
     const __bf16* __restrict__ v, __bf16* __restrict__ o, float* __restrict__ lse, Plan plan,
     const int* __restrict__ padoff, int total_tokens, int t_pad, int hq, int hkv, int n_hb, float scale_log2,
@@ -97,26 +98,83 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
 #pragma unroll
   for (int u = 0; u < 2; ++u) vo[u] = 16 * ((2 * u + half) ^ vt_swz(r32));
 
-  // ---- Q_d fragments (B operand of Sᵀ = K Qᵀ): two 64-channel halves
+  // ---- Q quantised here, from the bf16 rows this wave owns (fused quantisation: Q is read once,
+  // by the kernel that uses it), into the B operand of Sᵀ = K Qᵀ for the two 64-channel halves s,
+  // and written out as the d-blocked Q_d (and scales) that the backward reuses. Lane (qrow, half)
+  // supplies the scale of block 2s + half. E4M3: the operand holds channels 64s + 16·half + 0..15
+  // (block 2s) and 64s + 32 + 16·half + 0..15 (block 2s + 1), so each block's maximum meets its
+  // other 16 channels in the partner lane (l ^ 32); E2M1 / 6-bit: the lane holds all 32 channels
+  // of block 2s + half.
   i32x8 qa[2];
   int qs[2];
   {
     const bool ok = qrow < L;
     const size_t row = (size_t)(s0 + (ok ? qrow : 0)) * hq + h;
+    const __bf16* qr = q + row * D;
+    auto ld = [&](int c) { return ok ? *(const i32x4*)(qr + c) : i32x4{0, 0, 0, 0}; };   // 8 channels from c
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      if constexpr (FP4) {   // channels 64s + 32·half .. +31: 16 bytes
-        qa[s] = fp4_operand(ok ? *(const i32x4*)(qd + row * (D / 2) + 32 * s + 16 * half) : i32x4{0, 0, 0, 0});
-      } else if constexpr (FP6) {   // block 2s + half: 16-byte and 8-byte parts
-        const uint8_t* rp = qd + row * QROW;
-        qa[s] = fp6_operand(ok ? *(const i32x4*)(rp + 16 * (2 * s + half)) : i32x4{0, 0, 0, 0},
-                            ok ? *(const i32x2*)(rp + D / 2 + 8 * (2 * s + half)) : i32x2{0, 0});
-      } else {
-        const i32x4 lo = ok ? *(const i32x4*)(qd + row * D + 64 * s + 16 * half) : i32x4{0, 0, 0, 0};
-        const i32x4 hi = ok ? *(const i32x4*)(qd + row * D + 64 * s + 32 + 16 * half) : i32x4{0, 0, 0, 0};
+      if constexpr (QF == 0) {
+        uint32_t wa[8], wb[8];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const i32x4 ua = ld(64 * s + 16 * half + 8 * c), ub = ld(64 * s + 32 + 16 * half + 8 * c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            wa[4 * c + e] = (uint32_t)ua[e];
+            wb[4 * c + e] = (uint32_t)ub[e];
+          }
+        }
+        const uint32_t ma = pair_max32_u(amax_bits<8>(wa)), mb = pair_max32_u(amax_bits<8>(wb));
+        const int ea = e4m3_block_exp(ma), eb = e4m3_block_exp(mb);
+        const bool bada = ma >= 0x7F80u, badb = mb >= 0x7F80u;
+        const i32x4 lo = {bad_or(bada, 0x7F7F7F7F, e4m3_encode4(wa[0], wa[1], ea)),
+                          bad_or(bada, 0x7F7F7F7F, e4m3_encode4(wa[2], wa[3], ea)),
+                          bad_or(bada, 0x7F7F7F7F, e4m3_encode4(wa[4], wa[5], ea)),
+                          bad_or(bada, 0x7F7F7F7F, e4m3_encode4(wa[6], wa[7], ea))};
+        const i32x4 hi = {bad_or(badb, 0x7F7F7F7F, e4m3_encode4(wb[0], wb[1], eb)),
+                          bad_or(badb, 0x7F7F7F7F, e4m3_encode4(wb[2], wb[3], eb)),
+                          bad_or(badb, 0x7F7F7F7F, e4m3_encode4(wb[4], wb[5], eb)),
+                          bad_or(badb, 0x7F7F7F7F, e4m3_encode4(wb[6], wb[7], eb))};
         qa[s] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        qs[s] = half ? (badb ? 0xFF : eb + 127) : (bada ? 0xFF : ea + 127);
+        if (ok) {
+          *(i32x4*)(qd + row * D + 64 * s + 16 * half) = lo;
+          *(i32x4*)(qd + row * D + 64 * s + 32 + 16 * half) = hi;
+        }
+      } else {
+        uint32_t w[16];                           // block 2s + half: channels 64s + 32·half + 0..31
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const i32x4 u = ld(64 * s + 32 * half + 8 * c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[4 * c + e] = (uint32_t)u[e];
+        }
+        const uint32_t m = amax_bits<16>(w);
+        const bool bad = m >= 0x7F80u;
+        if constexpr (FP4) {
+          const int e = e2m1_block_exp(m);
+          const i32x4 c4 = {bad_or(bad, 0, (int)e2m1_encode8(w, e)), bad_or(bad, 0, (int)e2m1_encode8(w + 4, e)),
+                            bad_or(bad, 0, (int)e2m1_encode8(w + 8, e)), bad_or(bad, 0, (int)e2m1_encode8(w + 12, e))};
+          qa[s] = fp4_operand(c4);
+          qs[s] = bad ? 0xFF : e + 127;
+          if (ok) *(i32x4*)(qd + row * (D / 2) + 32 * s + 16 * half) = c4;
+        } else {
+          const int e = e6_block_exp<QF>(m);
+          u32x6 cw = e6_encode32<QF>(w, e);
+          if (bad) cw = u32x6{0u, 0u, 0u, 0u, 0u, 0u};
+          const i32x4 lo = {(int)cw[0], (int)cw[1], (int)cw[2], (int)cw[3]};
+          const i32x2 hi = {(int)cw[4], (int)cw[5]};
+          qa[s] = fp6_operand(lo, hi);
+          qs[s] = bad ? 0xFF : e + 127;
+          if (ok) {
+            uint8_t* rp = qd + row * QROW;
+            *(i32x4*)(rp + 16 * (2 * s + half)) = lo;
+            *(i32x2*)(rp + D / 2 + 8 * (2 * s + half)) = hi;
+          }
+        }
       }
-      qs[s] = ok ? qd_sc[row * 4 + 2 * s + half] : 127;
+      if (ok) qd_sc[row * 4 + 2 * s + half] = (uint8_t)qs[s];
     }
   }
   f32x16 oacc[4];
@@ -297,7 +355,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
   }
 }
 
-hipError_t launch_fwd_mx(const uint8_t* qd, const uint8_t* qd_sc, const uint8_t* kd, const uint8_t* kd_sc,
+hipError_t launch_fwd_mx(const void* q, uint8_t* qd, uint8_t* qd_sc, const uint8_t* kd, const uint8_t* kd_sc,
                          const uint8_t* vt, const uint8_t* vt_sc, const void* v, void* o, float* lse,
                          const Plan& plan_any, const int* pref_base, const int* padoff, int total_tokens, int t_pad,
                          int hq, int hkv, float scale, int causal, int qf, hipStream_t stream) {
@@ -312,7 +370,8 @@ hipError_t launch_fwd_mx(const uint8_t* qd, const uint8_t* qd_sc, const uint8_t*
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
   const float sl2 = scale * LOG2E;
 #define CFA_MXF_LAUNCH(HH, F4)                                                                                 \
-  hipLaunchKernelGGL((attn_fwd_mx_kernel<HH, F4>), dim3((unsigned)grid), dim3(256), 0, stream, qd, qd_sc, kd, kd_sc,  \
+  hipLaunchKernelGGL((attn_fwd_mx_kernel<HH, F4>), dim3((unsigned)grid), dim3(256), 0, stream, (const __bf16*)q, qd,   \
+                     qd_sc, kd, kd_sc,                                                                           \
                      vt, vt_sc, (const __bf16*)v, (__bf16*)o, lse, plan, padoff, total_tokens, t_pad, hq, hkv, n_hb, sl2, \
                      causal)
   if (qf == 1) {

@@ -304,15 +304,15 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, c
     const int tp = t_pad_of(s);
     const int qf = score_format(dtype);
     auto S = [&](size_t off) { return (uint8_t*)sv + off; };
-    cfa::MxPrepOut po{S(sl.qd.codes), S(sl.qd.scales), S(sl.kd.codes), S(sl.kd.scales), S(sl.vd.codes),
-                      S(sl.vd.scales), (uint8_t*)ws + wl.vt.codes, (uint8_t*)ws + wl.vt.scales};
+    cfa::MxPrepOut po{nullptr, nullptr, S(sl.kd.codes), S(sl.kd.scales), S(sl.vd.codes), S(sl.vd.scales),
+                      (uint8_t*)ws + wl.vt.codes, (uint8_t*)ws + wl.vt.scales};
     mark(1, 0, st);
-    if (int r = check_hip(cfa::launch_mx_prep_fwd(q, k, v, total_tokens, hq, hkv, ws, n_docs, qf, po, tp, st),
-                          "quantize Q, K, V"))
+    if (int r = check_hip(cfa::launch_mx_prep_fwd(k, v, total_tokens, hkv, ws, n_docs, qf, po, tp, st),
+                          "quantize K, V"))
       return r;
     mark(1, 1, st);
     mark(0, 0, st);
-    e = cfa::launch_fwd_mx((const uint8_t*)sv + sl.qd.codes, (const uint8_t*)sv + sl.qd.scales,
+    e = cfa::launch_fwd_mx(q, S(sl.qd.codes), S(sl.qd.scales),
                            (const uint8_t*)sv + sl.kd.codes, (const uint8_t*)sv + sl.kd.scales,
                            (const uint8_t*)ws + wl.vt.codes, (const uint8_t*)ws + wl.vt.scales, v, o, lse, plan,
                            plan.pref, (const int*)(ws + pl.padoff), total_tokens, tp, hq, hkv, scale, causal, qf, st);

@@ -88,17 +88,18 @@ hipError_t launch_mx_quantize_d_fp6(const void* x, long n_elems, int d, int fmt,
 hipError_t launch_mx_quantize_t(const void* x, int total_tokens, int h, int d, const void* ws, int n_docs,
                                 uint8_t* codes, uint8_t* scales, int t_pad, bool kernel_layout, hipStream_t stream);
 // Fused MX operand preparation (one pass each, grid ceil(t_pad/128) × hq):
-//   forward : out.a = Q_d, out.b = K_d (score format qf), out.c = V_d (E4M3), out.t = V_t;
+//   forward : out.b = K_d (score format qf), out.c = V_d (E4M3), out.t = V_t (grid over kv heads;
+//             Q is quantised by the MX forward kernel itself);
 //   backward: delta = rowsum(dO∘O) − dLSE, out.a = dO_d, out.t = dO_t (E4M3).
-hipError_t launch_mx_prep_fwd(const void* q, const void* k, const void* v, int total_tokens, int hq, int hkv,
-                              const void* ws, int n_docs, int qf, const MxPrepOut& out, int t_pad,
-                              hipStream_t stream);
+hipError_t launch_mx_prep_fwd(const void* k, const void* v, int total_tokens, int hkv, const void* ws, int n_docs,
+                              int qf, const MxPrepOut& out, int t_pad, hipStream_t stream);
 hipError_t launch_mx_prep_bwd(const void* o, const void* dout, const float* dlse, float* delta, int total_tokens,
                               int hq, const void* ws, int n_docs, const MxPrepOut& out, int t_pad,
                               hipStream_t stream);
 
 // fp4: Q_d, K_d are E2M1 copies (mx_quantize_fp4 layout) and the score product runs on FP4.
-hipError_t launch_fwd_mx(const uint8_t* qd, const uint8_t* qd_sc, const uint8_t* kd, const uint8_t* kd_sc,
+// The MX forward quantises Q itself (bf16 q in; Q_d codes and scales written to qd, qd_sc).
+hipError_t launch_fwd_mx(const void* q, uint8_t* qd, uint8_t* qd_sc, const uint8_t* kd, const uint8_t* kd_sc,
                          const uint8_t* vt, const uint8_t* vt_sc, const void* v, void* o, float* lse,
                          const Plan& plan, const int* pref_base, const int* padoff, int total_tokens, int t_pad,
                          int hq, int hkv, float scale, int causal, int qf, hipStream_t stream);

@@ -26,74 +26,13 @@
 //  * along doc-local tokens: a workgroup per (128 padded columns, head) stages the 128 × d tile
 //    in LDS and each lane encodes whole 32-token blocks of one channel (details at
 //    encode_t_group);
-//  * fused: one pass per direction writes every copy the attention kernels need (details at
-//    mx_prep_fwd_kernel and mx_prep_bwd_kernel).
+//  * fused: one pass per direction writes the copies the attention kernels need but do not make
+//    themselves (details at mx_prep_fwd_kernel and mx_prep_bwd_kernel; the MX forward kernel
+//    quantises Q from the rows it reads).
 #include "cfa_device.h"
+#include "cfa_mx.h"
 
 namespace cfa {
-
-// ---------------------------------------------------------------- bf16-domain encoders
-typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
-typedef __attribute__((ext_vector_type(2))) short s16x2;
-
-__device__ inline uint32_t max_u16x2(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
-                                                                  __builtin_bit_cast(u16x2, b)));
-}
-__device__ inline uint32_t min_u16x2(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
-                                                                  __builtin_bit_cast(u16x2, b)));
-}
-
-// Largest magnitude bit pattern (0..0x7FFF) of the bf16 pairs w[0..n).
-template <int N>
-__device__ inline uint32_t amax_bits(const uint32_t* w) {
-  uint32_t m = w[0] & 0x7FFF7FFFu;
-#pragma unroll
-  for (int i = 1; i < N; ++i) m = max_u16x2(m, w[i] & 0x7FFF7FFFu);
-  return max(m & 0xFFFFu, m >> 16);
-}
-
-// Block exponents from the largest magnitude's bf16 bits: floor(log2 amax) - top exponent,
-// clamped below at -127 (zero and bf16 subnormal blocks give -127; no finite block reaches 127).
-__device__ inline int e4m3_block_exp(uint32_t ab) { return max((int)(ab >> 7) - 135, -127); }
-__device__ inline int e2m1_block_exp(uint32_t ab) { return max((int)(ab >> 7) - 129, -127); }
-
-// Four E4M3 codes (little-endian) of the bf16 pairs a, b (elements a.lo, a.hi, b.lo, b.hi) in a
-// block with exponent e.
-__device__ inline int e4m3_encode4(uint32_t a, uint32_t b, int e) {
-  const uint32_t c = ((uint32_t)(e + 135) << 7) | 0x60u;      // bf16 bits of 448·2^e
-  const uint32_t cc = c | (c << 16);
-  const float s = __builtin_amdgcn_ldexpf(1.f, e);
-  const uint32_t ac = min_u16x2(a & 0x7FFF7FFFu, cc) | (a & 0x80008000u);
-  const uint32_t bc = min_u16x2(b & 0x7FFF7FFFu, cc) | (b & 0x80008000u);
-  // the first conversion writes bits 15:0 and the second bits 31:16, so the first call's
-  // pass-through half may hold anything (here the input itself: no register to clear)
-  s16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(__builtin_bit_cast(s16x2, ac), __builtin_bit_cast(bf16x2, ac),
-                                                      s, false);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, bc), s, true);
-  return __builtin_bit_cast(int, r);
-}
-
-// max over the four lanes 4k..4k+3 (lane swaps 1 and 2 as DPP quad permutations: no LDS trip)
-__device__ inline uint32_t quad_max(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // [2,3,0,1]
-  return v;
-}
-
-// c, or the NaN/Inf block's code word k where bad (a select, not a branch)
-__device__ inline int bad_or(bool bad, int k, int c) { return bad ? k : c; }
-
-// Eight E2M1 codes (element 2i in the low nibble of byte i) of the bf16 pairs w[0..4).
-__device__ inline uint32_t e2m1_encode8(const uint32_t* w, int e) {
-  const float s = __builtin_amdgcn_ldexpf(1.f, e);
-  uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf16x2, w[0]), s, 0);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, w[1]), s, 1);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, w[2]), s, 2);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, w[3]), s, 3);
-  return r;
-}
 
 __global__ __launch_bounds__(256) void mx_quantize_d_kernel(const __bf16* __restrict__ x, uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales, long n_blocks) {
@@ -479,11 +418,7 @@ __device__ inline void quant_d_chunks(const i32x4* raw, const BlockGroup& bg, in
   }
 }
 
-// 6-bit score copies (QF 2: E2M3, 3: E3M2), one whole 32-channel block per lane: v_cvt_scalef32_pk32_
-// {fp6,bf6}_bf16 divides 32 bf16 values by 2^e, rounds to nearest even, saturates at the format's
-// largest value (7.5 / 28) and packs code i at bits 6i..6i+5 of 192 -- the block layout the score
-// product reads. An in-bounds probe over every bf16 pattern (in groups of 32) and block exponents
-// -127..125 matched the software encoders (e2m3_code / e3m2_code after the clamp) bit for bit.
+// 6-bit score copies, one whole 32-channel block per lane (e6_encode32, cfa_mx.h).
 // Lane mapping: (row, block) pair tid + 256 j (j = 0, 1) is row 64 j + tid/4, block tid % 4; the
 // row's 32-token block is 2 j + tid/128 and its row within it (tid/4) % 32.
 template <int D>
@@ -503,8 +438,6 @@ template <int QF>
 __device__ inline void quant6_blocks(const i32x4 (&raw)[2][4], const BlockGroup& bg, int h, int head,
                                      uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   constexpr int D = 128;
-  typedef __attribute__((ext_vector_type(32))) __bf16 bf16x32;
-  typedef __attribute__((ext_vector_type(6))) unsigned u32x6;
   const int kb = threadIdx.x % 4, r = (threadIdx.x / 4) % 32, hi = threadIdx.x >= 128;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -521,12 +454,8 @@ __device__ inline void quant6_blocks(const i32x4 (&raw)[2][4], const BlockGroup&
     }
     const uint32_t ab = amax_bits<16>(w);
     const bool bad = ab >= 0x7F80u;
-    // floor(log2 amax) - top exponent (2 for E2M3, 4 for E3M2), clamped below at -127
-    const int e = max((int)(ab >> 7) - (QF == 2 ? 129 : 131), -127);
-    const bf16x32 xv = __builtin_bit_cast(bf16x32, w);
-    const float sc = __builtin_amdgcn_ldexpf(1.f, e);
-    u32x6 cw = QF == 2 ? __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(xv, sc)
-                       : __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(xv, sc);
+    const int e = e6_block_exp<QF>(ab);
+    u32x6 cw = e6_encode32<QF>(w, e);
     if (bad) cw = u32x6{0u, 0u, 0u, 0u, 0u, 0u};
     const size_t row0 = (size_t)tok0 * h + head;
     uint8_t* rowp = codes + row0 * (3 * D / 4) + (uint32_t)(r * h) * (3 * D / 4);
@@ -547,45 +476,34 @@ __device__ inline void load_chunks(const __bf16* __restrict__ x, int h, int head
   }
 }
 
-// Forward operand copies in one pass over Q, K and V (each read once): workgroup (g, head) writes Q_d of query head `head` and, for head < hkv, K_d, V_d and the
-// kernel-layout V_t of kv head `head`, all over the tokens of padded columns [128g, 128g + 128).
-// Workgroup g·hq + head of hq·ceil(t_pad/128): heads vary fastest.
-// Q_d and K_d take the score format QF; V_d (for dP in the backward) and V_t are E4M3.
+// Forward operand copies in one pass over K and V (each read once): workgroup g·hkv + head of
+// hkv·ceil(t_pad/128) (heads fastest) writes K_d (score format QF), V_d (E4M3, the dP operand of
+// the backward) and the kernel-layout V_t (E4M3) of kv head `head` over the tokens of padded
+// columns [128g, 128g + 128). Q is quantised by the MX forward kernel, which reads it anyway.
 template <int QF>
-__global__ __launch_bounds__(256, 3) void mx_prep_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+__global__ __launch_bounds__(256, 3) void mx_prep_fwd_kernel(const __bf16* __restrict__ k,
                                                           const __bf16* __restrict__ v, MxPrepOut out,
                                                           const int2* __restrict__ docinfo,
-                                                          const int* __restrict__ padoff, int n_docs, int hq, int hkv,
+                                                          const int* __restrict__ padoff, int n_docs, int hkv,
                                                           int t_pad) {
   constexpr int D = 128, RSTR = D + 8;
   __shared__ __attribute__((aligned(16))) __bf16 tile[128 * RSTR];   // staging rows alias it
   uint8_t* ost = (uint8_t*)tile;
   static_assert(D * 144 <= 128 * RSTR * 2, "staging rows fit in the tile");
-  const int g = blockIdx.x / hq;
-  const int head = blockIdx.x % hq;
+  const int g = blockIdx.x / hkv;
+  const int head = blockIdx.x % hkv;
   const BlockGroup bg = block_group(g, docinfo, padoff, n_docs);
   if (!bg.live[0]) return;
-  const bool kv = head < hkv;
   i32x4 rv[8];
   if constexpr (QF >= 2) {                        // 6-bit score copies: one block per lane
-    i32x4 rq[2][4], rk[2][4];
-    load_blocks6<D>(q, hq, head, bg, rq);
-    if (kv) {
-      load_blocks6<D>(k, hkv, head, bg, rk);
-      load_chunks<D, true>(v, hkv, head, bg, rv);
-    }
-    quant6_blocks<QF>(rq, bg, hq, head, out.a_codes, out.a_scales);
-    if (!kv) return;
+    i32x4 rk[2][4];
+    load_blocks6<D>(k, hkv, head, bg, rk);
+    load_chunks<D, true>(v, hkv, head, bg, rv);
     quant6_blocks<QF>(rk, bg, hkv, head, out.b_codes, out.b_scales);
   } else {
-    i32x4 rq[8], rk[8];
-    load_chunks<D, false>(q, hq, head, bg, rq);
-    if (kv) {
-      load_chunks<D, false>(k, hkv, head, bg, rk);
-      load_chunks<D, true>(v, hkv, head, bg, rv);
-    }
-    quant_d_chunks<QF>(rq, bg, hq, head, out.a_codes, out.a_scales);
-    if (!kv) return;
+    i32x4 rk[8];
+    load_chunks<D, false>(k, hkv, head, bg, rk);
+    load_chunks<D, true>(v, hkv, head, bg, rv);
     quant_d_chunks<QF>(rk, bg, hkv, head, out.b_codes, out.b_scales);
   }
   quant_d_chunks<0>(rv, bg, hkv, head, out.c_codes, out.c_scales);
@@ -694,19 +612,18 @@ hipError_t launch_mx_quantize_t(const void* x, int total_tokens, int h, int d, c
   return hipGetLastError();
 }
 
-hipError_t launch_mx_prep_fwd(const void* q, const void* k, const void* v, int total_tokens, int hq, int hkv,
-                              const void* ws, int n_docs, int qf, const MxPrepOut& out, int t_pad,
-                              hipStream_t stream) {
+hipError_t launch_mx_prep_fwd(const void* k, const void* v, int total_tokens, int hkv, const void* ws, int n_docs,
+                              int qf, const MxPrepOut& out, int t_pad, hipStream_t stream) {
   const PlanLayout lay(n_docs);
   const char* b = (const char*)ws;
   const long ng = ((long)t_pad + 127) / 128;
   if (ng == 0 || total_tokens == 0) return hipSuccess;
-  if (ng * hq > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)(ng * hq));            // heads fastest: neighbouring workgroups read one token row
+  if (ng * hkv > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)(ng * hkv));           // heads fastest: neighbouring workgroups read one token row
   auto kern = qf == 1 ? mx_prep_fwd_kernel<1> : qf == 2 ? mx_prep_fwd_kernel<2> : qf == 3 ? mx_prep_fwd_kernel<3>
                                                                                          : mx_prep_fwd_kernel<0>;
-  hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, out,
-                     (const int2*)(b + lay.docinfo), (const int*)(b + lay.padoff), n_docs, hq, hkv, t_pad);
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, (const __bf16*)k, (const __bf16*)v, out,
+                     (const int2*)(b + lay.docinfo), (const int*)(b + lay.padoff), n_docs, hkv, t_pad);
   return hipGetLastError();
 }
 

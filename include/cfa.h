@@ -101,10 +101,11 @@ size_t cfa_workspace_bytes(int pass, int total_tokens, int n_docs, int hq, int h
 
 /* Bytes of the forward-to-backward buffer `saved` (the MX dtypes only): the d-blocked E4M3, E2M1,
  * E2M3 or E3M2 copies of Q and K with their scales, reused by the backward so both passes see
- * identical scores, and the d-blocked E4M3 copy of V (the backward's dP operand), which the
- * forward writes in the same pass that reads V for its token-blocked copy -- quantised operands
- * reused in another orientation instead of being quantised again (FLAMIA page, "FLAMIA Mimarisi
- * ve Temel Tasarım İlkeleri": token-block scaling, fused quantisation). Layout, each section
+ * identical scores (Q_d is written by the forward attention kernel from the Q rows it quantises
+ * for itself), and the d-blocked E4M3 copy of V (the backward's dP operand), which the forward
+ * writes in the same pass that reads V for its token-blocked copy -- quantised operands reused in
+ * another orientation instead of being quantised again (FLAMIA page, "FLAMIA Mimarisi ve Temel
+ * Tasarım İlkeleri": token-block scaling, fused quantisation). Layout, each section
  * starting at a 256-byte boundary: Q_d codes [T, hq, c], Q_d scales [T, hq, d/32], K_d codes
  * [T, hkv, c], K_d scales [T, hkv, d/32], V_d codes [T, hkv, d], V_d scales [T, hkv, d/32], with
  * c = d (E4M3), d/2 (E2M1) or 3d/4 (6-bit) bytes as mx_quantize and mx_quantize_fp4/fp6 store
@@ -266,7 +267,8 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const u
  * Per-kernel timing for measurement tools. While set on the calling thread, the attention
  * calls record events[2*i] on their stream just before launching their i-th main kernel and
  * events[2*i+1] just after it (the work-list kernel is not counted). Kernel order:
- *   attn_fwd: 0 = forward attention, 1 = (MX dtypes) the one pass that quantises Q, K and V;
+ *   attn_fwd: 0 = forward attention (MX dtypes: it also quantises Q), 1 = (MX dtypes) the one pass
+ *             that quantises K and V;
  *   attn_bwd: 0 = D = rowsum(dO*O) (MX dtypes: the one pass that also writes both dO copies),
  *             1 = dK/dV, 2 = dQ;
  *   attn_decode: 0 = chunk partials, 1 = their merge.
