@@ -171,3 +171,15 @@ def test_noalloc_backward_rejects_sizes_beyond_its_array():
     assert b"64" in L.cfa_last_error() or b"67108864" in L.cfa_last_error()
     bad = list(args); bad[21] = 0                        # fp32 is forward-only, checked first
     assert L.attn_bwd_noalloc(*bad) == 3
+
+
+def test_mx_head_limits_of_the_operand_passes():
+    """The operand passes address a block's rows as a 32-bit offset r·h·d (r < 32): the MX paths
+    take hq <= 65536, and mx_quantize axes 1, 2 take h <= 65536, rejected before any launch."""
+    L = _lib.lib()
+    assert _fwd(dtype=2, T=64, n_docs=1, cu_h=None, hq=65536 * 2, hkv=1, saved=FAKE) == 3
+    assert b"65536" in L.cfa_last_error()
+    assert L.cfa_workspace_bytes(0, 64, 1, 65536 * 2, 1, 128, 2) == 0
+    assert L.cfa_workspace_bytes(0, 64, 1, 65536, 1, 128, 2) > 0
+    assert L.mx_quantize(FAKE, 64, 65537, 128, FAKE, None, 1, 1, FAKE, FAKE, 96, FAKE, 1 << 20, None) == 3
+    assert b"65536" in L.cfa_last_error()
