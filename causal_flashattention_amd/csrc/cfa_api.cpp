@@ -72,6 +72,23 @@ int check_hip(hipError_t e, const char* what) {
   return CFA_OK;
 }
 
+// Launches the plan kernel for a device cu_seqlens (`flag_ws`: the workspace region the plan and
+// its check flag live in). CFA_DEBUG_CHECK=1 in the environment (a diagnostic) then reads the flag
+// synchronously and fails the call before any other kernel runs when the device check raised it;
+// without the switch the call goes on with every document empty, and cfa_device_error reads the
+// flag later.
+int run_plan(const int32_t* cu, int n, int total, void* flag_ws, hipStream_t st, const char* what) {
+  if (int r = check_hip(cfa::launch_plan(cu, n, total, flag_ws, st, sched_naive()), what)) return r;
+  const char* e = getenv("CFA_DEBUG_CHECK");
+  if (!(e && strcmp(e, "1") == 0)) return CFA_OK;
+  int flag = 0;
+  if (int r = check_hip(hipMemcpyAsync(&flag, flag_ws, sizeof(int), hipMemcpyDeviceToHost, st), "read the plan flag"))
+    return r;
+  if (int r = check_hip(hipStreamSynchronize(st), "synchronize")) return r;
+  if (flag) return fail(CFA_ERR_SHAPE, "%s: the device check of cu_seqlens failed (flag %d)", what, flag);
+  return CFA_OK;
+}
+
 // Host mirror of cu_seqlens: cu[0] = 0, non-decreasing, cu[n] = total.
 int check_cu_host(const int32_t* cu, int n_docs, int total, int max_seqlen) {
   if (!cu) return CFA_OK;
@@ -292,7 +309,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, c
   if (int st = check_cu_host(cu_seqlens_host, n_docs, total_tokens, max_seqlen)) return st;
 
   hipStream_t st = (hipStream_t)stream;
-  if (int r = check_hip(cfa::launch_plan(cu_seqlens, n_docs, total_tokens, workspace, st, sched_naive()), "plan kernel")) return r;
+  if (int r = run_plan(cu_seqlens, n_docs, total_tokens, workspace, st, "plan kernel")) return r;
   if (total_tokens == 0) return CFA_OK;
   const cfa::Plan plan = make_plan(workspace, n_docs);
   hipError_t e;
@@ -353,7 +370,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   if (int st = check_cu_host(cu_seqlens_host, n_docs, total_tokens, max_seqlen)) return st;
 
   hipStream_t st = (hipStream_t)stream;
-  if (int r = check_hip(cfa::launch_plan(cu_seqlens, n_docs, total_tokens, workspace, st, sched_naive()), "plan kernel")) return r;
+  if (int r = run_plan(cu_seqlens, n_docs, total_tokens, workspace, st, "plan kernel")) return r;
   if (total_tokens == 0) return CFA_OK;
   const cfa::Plan plan = make_plan(workspace, n_docs);
   float* delta = (float*)((char*)workspace + wl.delta);
@@ -470,7 +487,7 @@ int mx_quantize(const void* x, int total_tokens, int h, int d, const int32_t* cu
   if (workspace_bytes < mx_workspace_bytes(n_docs))
     return fail(CFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, mx_workspace_bytes(n_docs));
   if (int r = check_cu_host(cu_seqlens_host, n_docs, total_tokens, 0)) return r;
-  if (int r = check_hip(cfa::launch_plan(cu_seqlens, n_docs, total_tokens, workspace, st, sched_naive()), "plan kernel")) return r;
+  if (int r = run_plan(cu_seqlens, n_docs, total_tokens, workspace, st, "plan kernel")) return r;
   if (total_tokens == 0) return CFA_OK;
   return check_hip(cfa::launch_mx_quantize_t(x, total_tokens, h, d, workspace, n_docs, codes, scales, t_pad, axis == 2,
                                              st),
@@ -537,9 +554,8 @@ int attn_fwd_cross(const void* q, const void* k, const void* v, void* o, float* 
   if (int st = check_cu_host(cu_seqlens_q_host, n_docs, total_q, 0)) return st;
   if (int st = check_cu_host(cu_seqlens_k_host, n_docs, total_k, 0)) return st;
   hipStream_t st = (hipStream_t)stream;
-  if (int r = check_hip(cfa::launch_plan(cu_seqlens_q, n_docs, total_q, workspace, st, sched_naive()), "plan kernel (queries)")) return r;
-  if (int r = check_hip(cfa::launch_plan(cu_seqlens_k, n_docs, total_k, (char*)workspace + cl.plan_k, st, sched_naive()),
-                        "plan kernel (keys)"))
+  if (int r = run_plan(cu_seqlens_q, n_docs, total_q, workspace, st, "plan kernel (queries)")) return r;
+  if (int r = run_plan(cu_seqlens_k, n_docs, total_k, (char*)workspace + cl.plan_k, st, "plan kernel (keys)"))
     return r;
   if (total_q == 0) return CFA_OK;
   const cfa::Plan pq = make_plan(workspace, n_docs);
@@ -572,9 +588,8 @@ int attn_bwd_cross(const void* q, const void* k, const void* v, const void* o, c
   if (int st = check_cu_host(cu_seqlens_q_host, n_docs, total_q, 0)) return st;
   if (int st = check_cu_host(cu_seqlens_k_host, n_docs, total_k, 0)) return st;
   hipStream_t st = (hipStream_t)stream;
-  if (int r = check_hip(cfa::launch_plan(cu_seqlens_q, n_docs, total_q, workspace, st, sched_naive()), "plan kernel (queries)")) return r;
-  if (int r = check_hip(cfa::launch_plan(cu_seqlens_k, n_docs, total_k, (char*)workspace + cl.plan_k, st, sched_naive()),
-                        "plan kernel (keys)"))
+  if (int r = run_plan(cu_seqlens_q, n_docs, total_q, workspace, st, "plan kernel (queries)")) return r;
+  if (int r = run_plan(cu_seqlens_k, n_docs, total_k, (char*)workspace + cl.plan_k, st, "plan kernel (keys)"))
     return r;
   const cfa::Plan pq = make_plan(workspace, n_docs);
   const cfa::Plan pk = plan_at(workspace, cl.plan_k, n_docs);
@@ -690,7 +705,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const u
   if (int st = check_cu_host(cu_seqlens_k_host, n_seqs, total_k, 0)) return st;
 
   hipStream_t st = (hipStream_t)stream;
-  if (int r = check_hip(cfa::launch_plan(cu_seqlens_k, n_seqs, total_k, workspace, st, sched_naive()), "plan kernel")) return r;
+  if (int r = run_plan(cu_seqlens_k, n_seqs, total_k, workspace, st, "plan kernel")) return r;
   const cfa::Plan plan = make_plan(workspace, n_seqs);
   float* part_o = (float*)((char*)workspace + dl.part_o);
   void* part_ml = (char*)workspace + dl.part_ml;

@@ -45,6 +45,10 @@
  *    o = 0 and lse = -inf).
  *  - CFA_SCHED=naive in the environment (a diagnostic) schedules documents in index order
  *    instead of longest first; results are bit-identical either way.
+ *  - CFA_DEBUG_CHECK=1 in the environment (a diagnostic) makes every call that checks a device
+ *    cu_seqlens synchronise on `stream` right after that check and, when it raised the flag,
+ *    return CFA_ERR_SHAPE before any other kernel runs (outputs untouched). Not for stream
+ *    capture: the check reads the flag back to the host.
  *  - Size limits of the MX dtypes (CFA_ERR_UNSUPPORTED otherwise): d = 128, hq <= 65536 and
  *    d·(32·ceil(total_tokens/32) + 32·n_docs) < 2^31.
  */

@@ -94,3 +94,38 @@ def test_naive_schedule_gives_identical_results(mx):
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32),
                            y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("mx", [False, "mxfp8"])
+def test_debug_check_fails_malformed_call_before_any_kernel(monkeypatch, mx):
+    """CFA_DEBUG_CHECK=1: a malformed device cu_seqlens fails the call with CFA_ERR_SHAPE (the
+    flag read back right after the plan kernel); a well-formed one runs as without the switch."""
+    announce("debug check", mx)
+    T, hq, hkv = 200, 4, 1
+    q, k, v, do, sc = _inputs(T, hq, hkv, 33)
+    dt = cfa.CFA_MXFP8 if mx else cfa.CFA_BF16
+    good = torch.tensor([0, 100, 100, 200], dtype=torch.int32, device=DEV)
+    ref_o, ref_lse, ref_saved = cfa.attn_fwd(q, k, v, good, scale=sc, mx=mx)
+    ref_grads = cfa.attn_bwd(q, k, v, ref_o, ref_lse, do, good, scale=sc, mx=mx, saved=ref_saved)
+    monkeypatch.setenv("CFA_DEBUG_CHECK", "1")
+    bad = torch.tensor([0, 100, 50, 200], dtype=torch.int32, device=DEV)
+    ws0 = torch.empty(cfa.workspace_bytes(0, T, 3, hq, hkv, 128, dt), dtype=torch.uint8, device=DEV)
+    o = torch.full_like(q, SENT)
+    lse = torch.full((hq, T), SENT, dtype=torch.float32, device=DEV)
+    with pytest.raises(cfa.CfaError) as ei:
+        cfa.attn_fwd(q, k, v, bad, scale=sc, mx=mx, out=o, lse=lse, workspace=ws0)
+    assert ei.value.name == "CFA_ERR_SHAPE" and "flag 2" in str(ei.value)
+    torch.cuda.synchronize()
+    assert bool(torch.all(o == SENT)) and bool(torch.all(lse == SENT))
+    dq, dk, dv = torch.full_like(q, SENT), torch.full_like(k, SENT), torch.full_like(v, SENT)
+    with pytest.raises(cfa.CfaError):
+        cfa.attn_bwd(q, k, v, ref_o, ref_lse, do, bad, scale=sc, mx=mx, saved=ref_saved, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert bool(torch.all(t == SENT))
+    o2, lse2, saved2 = cfa.attn_fwd(q, k, v, good, scale=sc, mx=mx)
+    grads2 = cfa.attn_bwd(q, k, v, o2, lse2, do, good, scale=sc, mx=mx, saved=saved2)
+    assert torch.equal(o2, ref_o) and torch.equal(lse2, ref_lse)
+    for a, b in zip(grads2, ref_grads):
+        assert torch.equal(a, b)
