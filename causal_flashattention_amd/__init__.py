@@ -165,6 +165,8 @@ def attn_bwd(q, k, v, o, lse, dout, cu_seqlens, *, scale=None, causal=True, cu_s
     """Backward pass. Returns (dq, dk, dv) with the layouts and dtype of (q, k, v).
 
     ``dlse`` (float32 ``[hq, T]``, optional) is the gradient flowing into the forward's lse.
+    ``mx`` without ``saved``: the library quantises Q, K and V again (the forward's bytes) into a
+    workspace that also holds ``saved_bytes(...)``.
     """
     L = _lib.lib()
     _check_qkv(q, k, v, True)
@@ -179,9 +181,7 @@ def attn_bwd(q, k, v, o, lse, dout, cu_seqlens, *, scale=None, causal=True, cu_s
         _expect(t, k.shape, k.dtype, name)
     _expect(lse, (hq, T), torch.float32, "lse")
     _expect(dlse, (hq, T), torch.float32, "dlse")
-    if mx:
-        if saved is None:
-            raise ValueError("the MX paths need the forward's saved buffer")
+    if mx and saved is not None:
         _at_least(saved, L.cfa_saved_bytes(T, n_docs, hq, hkv, d, dt), "saved")
     _check_dev(q, k, v, o, lse, dout, cu_seqlens, saved, dlse, dq, dk, dv, workspace)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -190,6 +190,8 @@ def attn_bwd(q, k, v, o, lse, dout, cu_seqlens, *, scale=None, causal=True, cu_s
     dv = torch.empty_like(v) if dv is None else dv
     if workspace is None:
         nb = L.cfa_workspace_bytes(1, T, n_docs, hq, hkv, d, dt)
+        if mx and saved is None:
+            nb += L.cfa_saved_bytes(T, n_docs, hq, hkv, d, dt)
         workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device)
     hcu = _host_cu(cu_seqlens, cu_seqlens_host)
     _lib.check(L.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
@@ -217,9 +219,7 @@ def attn_bwd_noalloc(q, k, v, o, lse, dout, cu_seqlens, *, dq, dk, dv, scale=Non
         _expect(t, k.shape, k.dtype, name)
     _expect(lse, (hq, T), torch.float32, "lse")
     _expect(dlse, (hq, T), torch.float32, "dlse")
-    if mx:
-        if saved is None:
-            raise ValueError("the MX paths need the forward's saved buffer")
+    if mx and saved is not None:
         _at_least(saved, L.cfa_saved_bytes(T, n_docs, hq, k.shape[1], d, dt), "saved")
     _check_dev(q, k, v, o, lse, dout, cu_seqlens, saved, dlse, dq, dk, dv)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)

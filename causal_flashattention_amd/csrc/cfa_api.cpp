@@ -358,15 +358,19 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   if (total_tokens > 0 && (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv))
     return fail(CFA_ERR_NULL, "q, k, v, o, lse, dout, dq, dk and dv must not be NULL");
   if (!(std::isfinite(scale) && scale > 0.f)) return fail(CFA_ERR_SHAPE, "scale must be finite and > 0");
-  if (is_mx(dtype) && !saved) return fail(CFA_ERR_NULL, "the MX paths need the forward's `saved` buffer");
-  if (is_mx(dtype) && !aligned(saved, 256)) return fail(CFA_ERR_ALIGN, "saved must be 256-byte aligned");
+  // MX without `saved`: Q_d, K_d and V_d are quantised again into the workspace, after its own
+  // sections (the quantisers give the bytes the forward wrote)
+  const bool requant = is_mx(dtype) && !saved;
+  if (is_mx(dtype) && saved && !aligned(saved, 256)) return fail(CFA_ERR_ALIGN, "saved must be 256-byte aligned");
   for (const void* p : {q, k, v, o, (const void*)lse, dout, (const void*)dlse, (const void*)dq, (const void*)dk,
                         (const void*)dv, (const void*)cu_seqlens})
     if (!aligned(p, 16)) return fail(CFA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
   if (!aligned(workspace, 256)) return fail(CFA_ERR_ALIGN, "workspace must be 256-byte aligned");
   const WsLayout wl = ws_layout(1, s, allow_fused);
-  if (workspace_bytes < wl.total)
-    return fail(CFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, wl.total);
+  const size_t ws_need = wl.total + (requant ? saved_layout(s).total : 0);
+  if (workspace_bytes < ws_need)
+    return fail(CFA_ERR_WORKSPACE, "workspace %zu bytes < required %zu%s", workspace_bytes, ws_need,
+                requant ? " (MX without saved: cfa_workspace_bytes + cfa_saved_bytes)" : "");
   if (int st = check_cu_host(cu_seqlens_host, n_docs, total_tokens, max_seqlen)) return st;
 
   hipStream_t st = (hipStream_t)stream;
@@ -384,6 +388,21 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
     char* ws = (char*)workspace;
     const char* sv = (const char*)saved;
     const SavedLayout sl = saved_layout(s);
+    if (requant) {
+      uint8_t* rq = (uint8_t*)ws + wl.total;
+      const int qf = score_format(dtype);
+      auto quant_d = [&](const void* x, int h, const MxBuf& b, int fmt) {
+        const long n = (long)total_tokens * h * d;
+        return fmt == 1 ? cfa::launch_mx_quantize_d_fp4(x, n, rq + b.codes, rq + b.scales, st)
+             : fmt >= 2 ? cfa::launch_mx_quantize_d_fp6(x, n, d, fmt, rq + b.codes, rq + b.scales, st)
+                        : cfa::launch_mx_quantize_d(x, n, rq + b.codes, rq + b.scales, st);
+      };
+      hipError_t e = quant_d(q, hq, sl.qd, qf);
+      if (!e) e = quant_d(k, hkv, sl.kd, qf);
+      if (!e) e = quant_d(v, hkv, sl.vd, 0);
+      if (int r = check_hip(e, "backward requantisation of Q, K, V")) return r;
+      sv = (const char*)rq;
+    }
     const cfa::PlanLayout pl(n_docs);
     const int tp = t_pad_of(s);
     const int* padoff = (const int*)(ws + pl.padoff);
@@ -784,7 +803,7 @@ int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
   // attn_bwd's own plan when it fits (then the results are attn_bwd's bit for bit), else dQ as
   // its own pass, which needs no fp32 dQ sums (results within rounding of attn_bwd's)
   const bool fused = dq_fused_requested() && ws_layout(1, s, true).total <= STATIC_SCRATCH_BYTES;
-  const size_t need = ws_layout(1, s, fused).total;
+  const size_t need = ws_layout(1, s, fused).total + (is_mx(dtype) && !saved ? saved_layout(s).total : 0);
   if (need > STATIC_SCRATCH_BYTES)
     return fail(CFA_ERR_WORKSPACE, "attn_bwd_noalloc: these sizes need %zu bytes of scratch, above its fixed %zu",
                 need, STATIC_SCRATCH_BYTES);

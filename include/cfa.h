@@ -141,7 +141,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *           not name it; it is the exact derivative of the lse output the forward returns:
  *           d lse_i / d S_ij = P_ij, so it enters as dS_ij = P_ij (dP_ij - (D_i - dlse_i)) with
  *           D_i = sum_r dout_ir o_ir. Shares the 16-byte alignment rule.
- *   saved : the MX dtypes: the buffer attn_fwd filled, unmodified; otherwise NULL.
+ *   saved : the MX dtypes: the buffer attn_fwd filled, unmodified; otherwise NULL. An MX call
+ *           may also pass NULL: the backward then quantises Q, K and V again (the same bytes
+ *           the forward wrote, so the results are bit-identical) into the workspace, which must
+ *           then hold cfa_workspace_bytes(1, ...) + cfa_saved_bytes(...) bytes.
  * Deterministic: two calls on the same inputs give bit-identical outputs.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -94,6 +94,15 @@ def test_bwd_rejects():
     assert L.attn_bwd(*bad) == 5
     bad = list(args); bad[6] = FAKE + 4                  # a misaligned dlse
     assert L.attn_bwd(*bad) == 4
+    # MX without saved: the workspace must also hold the re-quantised Q_d, K_d, V_d
+    ws1 = L.cfa_workspace_bytes(1, 100, 1, 4, 2, 128, 2)
+    sv = L.cfa_saved_bytes(100, 1, 4, 2, 128, 2)
+    assert sv > 0
+    bad = list(args); bad[7] = None; bad[21] = 2; bad[23] = ws1
+    assert L.attn_bwd(*bad) == 5
+    assert b"cfa_saved_bytes" in L.cfa_last_error()
+    bad = list(args); bad[7] = FAKE + 16; bad[21] = 2   # a given saved must be 256-byte aligned
+    assert L.attn_bwd(*bad) == 4
 
 
 def test_mx_quantize_rejects():

@@ -48,8 +48,6 @@ def test_bwd_metadata():
         cfa.attn_bwd(q, k, v, o, lse, do, cu, dk=torch.zeros_like(q))
     with pytest.raises(ValueError, match="dlse: shape"):
         cfa.attn_bwd(q, k, v, o, lse, do, cu, dlse=torch.zeros(4, 63))
-    with pytest.raises(ValueError, match="saved buffer"):
-        cfa.attn_bwd(q, k, v, o, lse, do, cu, mx=True)
     with pytest.raises(ValueError, match="saved holds"):
         cfa.attn_bwd(q, k, v, o, lse, do, cu, mx="mxfp4", saved=torch.zeros(8, dtype=torch.uint8))
 

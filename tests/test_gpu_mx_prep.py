@@ -82,3 +82,26 @@ def test_forward_pass_saved_copies_bit_exact(name, specials):
     rc, rs = mx.quantize_d(W.bf16_bits_to_f64(vb))
     assert np.array_equal(sec[4], rc.reshape(-1))
     assert np.array_equal(sec[5], rs.reshape(-1))
+
+
+@pytest.mark.parametrize("name", list(FORMATS))
+def test_backward_without_saved_requantises_bit_identically(name):
+    """attn_bwd with saved = NULL quantises Q, K and V again into its workspace: the gradients
+    equal those of the call that reuses the forward's buffer, bit for bit (also through the
+    no-allocation entry point)."""
+    dt, _ = FORMATS[name]
+    lengths = [33, 0, 300, 129, 64]
+    T, hq, hkv = sum(lengths), 4, 2
+    cu = W.cu_from_lengths(lengths)
+    w = W.make_random(seed=41, lengths=lengths, hq=hq, hkv=hkv)
+    q, k, v, do = (to_dev(a) for a in (w.q, w.k, w.v, w.do))
+    cu_d = torch.from_numpy(cu).to(DEV)
+    announce("mx backward without saved", name, lengths)
+    o, lse, saved = cfa.attn_fwd(q, k, v, cu_d, scale=w.scale, mx=name)
+    ref = cfa.attn_bwd(q, k, v, o, lse, do, cu_d, scale=w.scale, mx=name, saved=saved)
+    got = cfa.attn_bwd(q, k, v, o, lse, do, cu_d, scale=w.scale, mx=name)
+    na = [torch.empty_like(t) for t in (q, k, v)]
+    cfa.attn_bwd_noalloc(q, k, v, o, lse, do, cu_d, dq=na[0], dk=na[1], dv=na[2], scale=w.scale, mx=name)
+    torch.cuda.synchronize()
+    for a, b, c in zip(ref, got, na):
+        assert torch.equal(a, b) and torch.equal(a, c)
