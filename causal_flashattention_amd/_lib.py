@@ -30,6 +30,7 @@ SIGNATURES = {
     "mx_quantize_fp6_e3m2": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "mx_padded_tokens": (_I, [_I, _I]),
     "mx_workspace_bytes": (_S, [_I]),
+    "mx_quantize_bytes": (_S, [_I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]),
     "cfa_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I]),
     "attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "cfa_cross_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I]),

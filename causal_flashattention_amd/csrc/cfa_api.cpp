@@ -478,6 +478,14 @@ int mx_padded_tokens(int total_tokens, int n_docs) {
 
 size_t mx_workspace_bytes(int n_docs) { return n_docs >= 1 ? cfa::PlanLayout(n_docs).end : 0; }
 
+size_t mx_quantize_bytes(int axis, int total_tokens, int n_docs, int h, int d, size_t* scale_bytes) {
+  size_t codes = 0;
+  if (total_tokens >= 0 && n_docs >= 1 && h >= 1 && (d == 64 || d == 128) && axis >= 0 && axis <= 2)
+    codes = (size_t)h * d * (axis == 0 ? (size_t)total_tokens : (size_t)mx_padded_tokens(total_tokens, n_docs));
+  if (scale_bytes) *scale_bytes = codes / 32;
+  return codes;
+}
+
 int mx_quantize(const void* x, int total_tokens, int h, int d, const int32_t* cu_seqlens,
                 const int32_t* cu_seqlens_host, int n_docs, int axis, uint8_t* codes, uint8_t* scales, int t_pad,
                 void* workspace, size_t workspace_bytes, void* stream) {

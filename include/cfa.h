@@ -246,6 +246,13 @@ int mx_padded_tokens(int total_tokens, int n_docs);
 /* Scratch bytes of mx_quantize along tokens. */
 size_t mx_workspace_bytes(int n_docs);
 
+/* Output sizes of mx_quantize: returns the bytes of `codes` and, when scale_bytes is not NULL,
+ * stores the bytes of `scales` there (one E8M0 byte per 32 codes). Axis 0: h·d·total_tokens
+ * codes; axes 1, 2: h·d·t_pad codes with t_pad = mx_padded_tokens(total_tokens, n_docs), the
+ * smallest row stride that holds any cu_seqlens of these sizes. 0 (and 0 scale bytes) for an
+ * invalid axis or sizes (n_docs < 1, h < 1, d other than 64 or 128, as mx_quantize). */
+size_t mx_quantize_bytes(int axis, int total_tokens, int n_docs, int h, int d, size_t* scale_bytes);
+
 /*
  * Decoding: one new query token per sequence over a packed KV cache (the current token's K/V
  * already appended), the last row of a causal document -- "GPT Kernel Programlama" §4-§6 -- read

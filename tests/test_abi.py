@@ -45,6 +45,13 @@ def test_workspace_sizes():
     assert L.cfa_workspace_bytes(1, 256, 1, 1, 1, 64, 0) == 0          # fp32 is forward-only
     assert L.cfa_workspace_bytes(2, 256, 1, 1, 1, 64, 1) == 0          # no such pass
     assert L.mx_padded_tokens(100, 3) == 128 + 96
+    sb = ctypes.c_size_t(0)
+    assert L.mx_quantize_bytes(0, 100, 3, 2, 128, ctypes.byref(sb)) == 100 * 2 * 128 and sb.value == 100 * 2 * 4
+    for axis in (1, 2):
+        assert L.mx_quantize_bytes(axis, 100, 3, 2, 128, ctypes.byref(sb)) == 2 * 128 * (128 + 96)
+        assert sb.value == 2 * 128 * (128 + 96) // 32
+    assert L.mx_quantize_bytes(3, 100, 3, 2, 128, ctypes.byref(sb)) == 0 and sb.value == 0
+    assert L.mx_quantize_bytes(0, 100, 3, 2, 96, None) == 0
 
 
 def _fwd(**over):
