@@ -300,13 +300,15 @@ __device__ __forceinline__ void dkdv_item(
   // load the BM × D tile as 16-byte chunks (TR per lane) and stage_finish writes them
   constexpr int TR = D < 128 ? BM * D / 8 / (64 * NP) : 1;
   i32x4 treg[TR];
+  // d >= 128: the step tiles' copies (lane offsets fixed for the whole item)
+  const RowCopies<BM, NP, D >= 128 ? D : 128> rc((uint32_t)hq * D * 2, pair, lane);
   auto stage = [&](int st, char* buf) {
     int h, q0;
     step_at(st, h, q0);
     const __bf16* src = ds_wave ? dout : q;
     if constexpr (D >= 128) {
-      stage_rows_lds<BM, NP, D>(buf + (ds_wave ? TILE : 0), (const char*)(src + ((size_t)(q_s0 + q0) * hq + h) * D),
-                                (uint32_t)hq * D * 2, Lq - 1 - q0, pair, lane);
+      // rows past the document end read zeros (those queries are masked: P = 0, dS = 0)
+      rc.copy(buf + (ds_wave ? TILE : 0), src + ((size_t)(q_s0 + q0) * hq + h) * D, Lq - 1 - q0, pair);
     } else {
 #pragma unroll
       for (int i = 0; i < TR; ++i) {
@@ -831,14 +833,16 @@ __global__ __launch_bounds__(256 * HPB, D == 256 ? 1 : 2 / HPB) void attn_bwd_dq
   for (int b = 0; b < C::DB; ++b) dqa[b] = f32x16{};
 
   // K/V tile kt -> LDS buffer; keys past kv_end are clamped into the document (masked, P = 0)
+  // d >= 128: lane offsets of the tile copies, fixed for the whole key loop
+  const RowCopies<BN, 4 * HPB, D >= 128 ? D : 128> rc((uint32_t)hkv * D * 2, w, lane);
   auto stage = [&](int kt, char* kb) {
     const int k0 = kt * BN;
     char* vb = kb + TILE;
     if constexpr (D >= 128) {
+      // keys past kv_end read zeros (masked: P = 0)
       const size_t row0 = ((size_t)(k_s0 + k0) * hkv + g) * D;
-      const uint32_t stride = (uint32_t)hkv * D * 2;
-      stage_rows_lds<BN, 4 * HPB, D>(kb, (const char*)(k + row0), stride, kv_end - 1 - k0, w, lane);
-      stage_rows_lds<BN, 4 * HPB, D>(vb, (const char*)(v + row0), stride, kv_end - 1 - k0, w, lane);
+      rc.copy(kb, k + row0, kv_end - 1 - k0, w);
+      rc.copy(vb, v + row0, kv_end - 1 - k0, w);
     } else {
       i32x4 kreg[PT], vreg[PT];
 #pragma unroll

@@ -118,12 +118,12 @@ int check_sizes(const Sizes& s, bool bwd) {
   if (s.hq < 1 || s.hkv < 1) return fail(CFA_ERR_SHAPE, "hq = %d, hkv = %d must be >= 1", s.hq, s.hkv);
   if (s.hq % s.hkv) return fail(CFA_ERR_SHAPE, "hq = %d is not a multiple of hkv = %d", s.hq, s.hkv);
   if ((long)s.T * s.hq * s.d > 0x7fffffffL * 8L) return fail(CFA_ERR_SHAPE, "tensor too large");
+  // the kernels address the rows of one staged tile as 32-bit offsets row·hq·d·2 bytes
+  if (s.hq > 65536) return fail(CFA_ERR_UNSUPPORTED, "hq = %d above 65536", s.hq);
   if (s.dtype != CFA_F32 && s.dtype != CFA_BF16 && !is_mx(s.dtype))
     return fail(CFA_ERR_UNSUPPORTED, "dtype %d unknown", s.dtype);
   if (is_mx(s.dtype)) {
     if (s.d != 128) return fail(CFA_ERR_UNSUPPORTED, "the MX paths support d = 128 only (got %d)", s.d);
-    // the operand passes address a 32-token block's rows as a 32-bit offset r·hq·d
-    if (s.hq > 65536) return fail(CFA_ERR_UNSUPPORTED, "the MX paths take hq <= 65536 (got %d)", s.hq);
     // token-blocked rows are addressed as channel·t_pad + column in 32 bits
     if ((long)((s.T + 31) / 32 * 32 + 32L * s.n_docs) * s.d > 0x7fffffffL)
       return fail(CFA_ERR_UNSUPPORTED, "the MX paths need d·(32·ceil(T/32) + 32·n_docs) < 2^31 (T = %d, n_docs = %d)",

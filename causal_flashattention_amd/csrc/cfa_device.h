@@ -242,6 +242,21 @@ __device__ inline void g2lds4(const void* gsrc, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 4, 0, 0);
 }
 
+// Raw buffer resource over the `bytes` bytes from `base` (reads past them return zeros). Both are
+// read from the first lane, so the resource lives in scalar registers: they must be the same in
+// every lane.
+__device__ inline __amdgpu_buffer_rsrc_t rsrc_at(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  const uint64_t u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)u, 0, __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
+}
+// g2lds16 through a buffer resource: the source is the resource base + voff (a 32-bit lane
+// offset), so copies whose lane offsets repeat need no per-copy address arithmetic.
+__device__ inline void b2lds16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, 0, 0, 0);
+}
+
 // XOR swizzles of the 16-byte chunks of E4M3 code tiles in LDS, chosen so that the 16 rows
 // read by a 16-lane group at one logical chunk land in 16 distinct 16-byte bank groups:
 // d-blocked rows of 128 bytes (8 chunks): rows r and r+1 share a 256-byte bank window, so the
@@ -282,6 +297,33 @@ __device__ inline void stage_rows_lds(char* tile, const char* base, uint32_t str
     g2lds16(base + ((uint32_t)min(r, rmax) * stride + c * 16), tile + I * 1024);
   }
 }
+
+// The copies of stage_rows_lds<ROWS, NW, D> as buffer loads: the lane offsets from a tile's first
+// row are computed once (they repeat from tile to tile), and each tile gets a scalar resource
+// that ends after row rmax, so rows past it read zeros instead of repeating row rmax (callers
+// mask those rows). No per-copy address arithmetic is left in a loop over tiles.
+template <int ROWS, int NW, int D>
+struct RowCopies {
+  static_assert(D == 128 || D == 256, "rows of 256 or 512 bytes");
+  static constexpr int LPR = D / 8, RB = 64 / LPR, PER_WAVE = ROWS / (RB * NW);
+  static_assert(ROWS % (RB * NW) == 0, "NW waves × RB rows per block");
+  uint32_t off[PER_WAVE];
+  uint32_t stride;
+  __device__ RowCopies(uint32_t row_stride, int wave, int lane) : stride(row_stride) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int r = RB * (wave * PER_WAVE + j) + lane / LPR, pc = lane % LPR;
+      off[j] = (uint32_t)r * stride + 16 * (uint32_t)((pc & 16) | ((pc & 15) ^ SwzTile<D>::f(r)));
+    }
+  }
+  // tile rows 0..ROWS-1 from `base` (row r at base + r·stride; wave-uniform), rows past rmax zero
+  __device__ void copy(char* tile, const void* base, int rmax, int wave) const {
+    const uint32_t bytes = rmax >= ROWS - 1 ? 0x7fffffffu : rmax < 0 ? 0u : (uint32_t)rmax * stride + D * 2;
+    const auto rs = rsrc_at(base, bytes);
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) b2lds16(rs, off[j], tile + (wave * PER_WAVE + j) * 1024);
+  }
+};
 
 __device__ inline bf16x8 as_bf16x8(const i32x4& u) { return __builtin_bit_cast(bf16x8, u); }
 

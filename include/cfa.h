@@ -49,6 +49,8 @@
  *    cu_seqlens synchronise on `stream` right after that check and, when it raised the flag,
  *    return CFA_ERR_SHAPE before any other kernel runs (outputs untouched). Not for stream
  *    capture: the check reads the flag back to the host.
+ *  - hq <= 65536 on every path (the kernels address the rows of a staged tile with 32-bit
+ *    offsets; CFA_ERR_UNSUPPORTED otherwise).
  *  - Size limits of the MX dtypes (CFA_ERR_UNSUPPORTED otherwise): d = 128, hq <= 65536 and
  *    d·(32·ceil(total_tokens/32) + 32·n_docs) < 2^31.
  */

@@ -199,3 +199,14 @@ def test_mx_head_limits_of_the_operand_passes():
     assert L.cfa_workspace_bytes(0, 64, 1, 65536, 1, 128, 2) > 0
     assert L.mx_quantize(FAKE, 64, 65537, 128, FAKE, None, 1, 1, FAKE, FAKE, 96, FAKE, 1 << 20, None) == 3
     assert b"65536" in L.cfa_last_error()
+
+
+def test_head_limit_of_the_tile_copies():
+    """Every attention path stages a tile's rows at 32-bit offsets row·hq·d·2 bytes: hq above 65536
+    is rejected before any launch (bf16 forward and backward, cross-attention), 65536 is taken."""
+    L = _lib.lib()
+    assert _fwd(dtype=1, T=64, n_docs=1, cu_h=None, hq=65537, hkv=1) == 3
+    assert b"65536" in L.cfa_last_error()
+    assert L.cfa_workspace_bytes(1, 64, 1, 65537, 1, 128, 1) == 0
+    assert L.cfa_workspace_bytes(1, 64, 1, 65536, 1, 128, 1) > 0
+    assert L.cfa_cross_workspace_bytes(1, 64, 64, 1, 65537, 1, 128) == 0
