@@ -173,19 +173,60 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
   // Lanes 0..63 of the first wave of each role fetch LSE or D into a register (stage_finish
   // writes it after the step's compute).
   float rreg = 0.f;
+  // Lane offsets of the copies from a step's first row (first column for the token-blocked
+  // copy), the same for every step; a step whose 64 queries all lie inside the document uses
+  // them as they are (rows past the document end only occur on its last step, which clamps).
+  const uint32_t tok_b = (uint32_t)hq * D;
+  const uint32_t nrs = (uint32_t)hq * QROW;       // narrow Q_d row stride
+  uint32_t dof[2], tof[2];
+  const uint32_t nof = (uint32_t)(16 * pair + (lane >> 2)) * nrs + 16 * ((lane & 3) ^ vt_swz(16 * pair + (lane >> 2)));
+  const uint32_t nof6 = (uint32_t)lane * nrs + D / 2 + 16 * pair;
+  const uint32_t sof = (uint32_t)lane * (uint32_t)hq * 4;
+  const uint32_t tsof = (uint32_t)(lane >> 3) * D + 16 * (lane & 7);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int I = 2 * pair + j, r = 8 * I + (lane >> 3), rt = 16 * I + (lane >> 2);
+    dof[j] = (uint32_t)r * tok_b + 16 * ((lane & 7) ^ kd_swz(r));
+    tof[j] = (uint32_t)(rt * t_pad) + 16 * ((lane & 3) ^ vt_swz(rt));
+  }
+  const RowCopies<BM, 4, 128> rows((uint32_t)hq * D * 2, pair, lane);
   auto stage = [&](int st, char* buf) {
     const int h = g * G + st / n_qt;
     const int q0 = q0_of(st);
     const int rmax = L - 1 - q0;
     const size_t tok0 = (size_t)(s0 + q0) * hq + h;
-    const uint32_t tok_b = (uint32_t)hq * D;
+    if (rmax >= BM - 1) {                       // the whole step lies inside the document
+      if (narrow_role) {
+        const auto rs = rsrc_at(qd + tok0 * QROW, 0x7fffffffu);
+        b2lds16(rs, nof, buf + pair * 1024);
+        if (FP6 && pair < 2) b2lds16(rs, nof6, buf + 4096 + pair * 1024);
+      } else {
+        const auto rs = rsrc_at((ds_wave ? dod : qd) + tok0 * D, 0x7fffffffu);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) b2lds16(rs, dof[j], buf + (2 * pair + j) * 1024);
+      }
+      if (pair == 0) b2lds4(rsrc_at((ds_wave ? dod_sc : qd_sc) + tok0 * 4, 0x7fffffffu), sof, buf + C::OFF_SC);
+      if (pair == 1) rreg = (ds_wave ? delta : lse)[(size_t)h * total_tokens + s0 + q0 + lane];
+      if (ds_wave || step_is_diag(st)) {
+        rows.copy(buf + C::OFF_U, (ds_wave ? q : dout) + tok0 * D, rmax, pair);
+      } else {
+        const auto rs = rsrc_at(dot + (size_t)h * D * t_pad + pcol + q0, 0x7fffffffu);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) b2lds16(rs, tof[j], buf + C::OFF_U + (2 * pair + j) * 1024);
+        if (pair == 2 && lane < 16)
+          b2lds16(rsrc_at(dot_sc + ((size_t)h * (t_pad / 32) + ((pcol + q0) >> 5)) * D, 0x7fffffffu), tsof,
+                  buf + C::OFF_TSC);
+      }
+      return;
+    }
+    // the document's last step: rows past its end are clamped into it (d-blocked, bf16) or into
+    // its last token block (token-blocked); they are masked
     if (narrow_role) {                          // E2M1 / E2M3 Q_d codes: 4 blocks of 16 rows of 64 B
       const uint8_t* dsrc = qd + tok0 * QROW;
-      const uint32_t rs = (uint32_t)hq * QROW;
       const int r = 16 * pair + (lane >> 2);
-      g2lds16(dsrc + ((uint32_t)min(r, rmax) * rs + 16 * ((lane & 3) ^ vt_swz(r))), buf + pair * 1024);
+      g2lds16(dsrc + ((uint32_t)min(r, rmax) * nrs + 16 * ((lane & 3) ^ vt_swz(r))), buf + pair * 1024);
       if (FP6 && pair < 2)                      // E2M3 8-byte parts: chunk `pair` of every row
-        g2lds16(dsrc + ((uint32_t)min(lane, rmax) * rs + D / 2 + 16 * pair), buf + 4096 + pair * 1024);
+        g2lds16(dsrc + ((uint32_t)min(lane, rmax) * nrs + D / 2 + 16 * pair), buf + 4096 + pair * 1024);
     } else {
       const uint8_t* dsrc = (ds_wave ? dod : qd) + tok0 * D;
 #pragma unroll
@@ -494,33 +535,42 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
 #pragma unroll
   for (int b = 0; b < 4; ++b) dqa[b] = f32x16{};
 
-  // key tile -> LDS; keys past kv_end are clamped into the document; they are masked (P = 0)
-  // Addresses: a wave-uniform 64-bit tile base plus a 32-bit lane offset within the tile.
+  // key tile -> LDS through buffer resources that end after the document's last row: keys past
+  // kv_end read zeros and are masked (P = 0). The lane offsets from a tile's first row are the
+  // same for every tile.
   const uint32_t krow_b = (uint32_t)hkv * D;      // bytes between consecutive tokens (codes, bf16/2)
+  const uint32_t nrs = (uint32_t)hkv * QROW;      // narrow K_d row stride
+  uint32_t dof[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 8 * (2 * w + j) + (lane >> 3);
+    dof[j] = (uint32_t)r * krow_b + 16 * ((lane & 7) ^ kd_swz(r));
+  }
+  const uint32_t nof = (uint32_t)(16 * w + (lane >> 2)) * nrs + 16 * ((lane & 3) ^ vt_swz(16 * w + (lane >> 2)));
+  const uint32_t nof6 = (uint32_t)lane * nrs + D / 2 + 16 * w;
+  const uint32_t sof = (uint32_t)lane * (uint32_t)hkv * 4;
+  const RowCopies<BN, 4, 128> rows(krow_b * 2, w, lane);
   auto stage = [&](int ktile, char* tb) {
     const int k0 = ktile * BN;
     const int rmax = kv_end - 1 - k0;             // last row inside the document
     const size_t tok0 = (size_t)(s0 + k0) * hkv + g;
-    const uint8_t* kdb = kd + tok0 * D;
-    const uint8_t* vdb = vd + tok0 * D;
+    auto ends = [&](uint32_t stride, uint32_t row_bytes) {
+      return rmax >= BN - 1 ? 0x7fffffffu : (uint32_t)rmax * stride + row_bytes;
+    };
+    const auto rv = rsrc_at(vd + tok0 * D, ends(krow_b, D));
 #pragma unroll
     for (int j = 0; j < 2; ++j) {               // K_d and V_d codes: 8 blocks of 8 rows each
-      const int I = 2 * w + j, r = 8 * I + (lane >> 3);
-      const uint32_t off = (uint32_t)min(r, rmax) * krow_b + 16 * ((lane & 7) ^ kd_swz(r));
-      if constexpr (QF == 0) g2lds16(kdb + off, tb + I * 1024);
-      g2lds16(vdb + off, tb + C::OFF_VD + I * 1024);
+      if constexpr (QF == 0) b2lds16(rsrc_at(kd + tok0 * D, ends(krow_b, D)), dof[j], tb + (2 * w + j) * 1024);
+      b2lds16(rv, dof[j], tb + C::OFF_VD + (2 * w + j) * 1024);
     }
     if constexpr (QF != 0) {                    // E2M1 / E2M3 K_d codes: 4 blocks of 16 rows of 64 B
-      const uint32_t rs = (uint32_t)hkv * QROW;
-      const int r = 16 * w + (lane >> 2);
-      g2lds16(kd + tok0 * QROW + ((uint32_t)min(r, rmax) * rs + 16 * ((lane & 3) ^ vt_swz(r))), tb + w * 1024);
-      if (FP6 && w < 2)                         // E2M3 8-byte parts: chunk w of every row
-        g2lds16(kd + tok0 * QROW + ((uint32_t)min(lane, rmax) * rs + D / 2 + 16 * w), tb + 4096 + w * 1024);
+      const auto rk = rsrc_at(kd + tok0 * QROW, ends(nrs, QROW));
+      b2lds16(rk, nof, tb + w * 1024);
+      if (FP6 && w < 2) b2lds16(rk, nof6, tb + 4096 + w * 1024);   // E2M3 8-byte parts: chunk w of every row
     }
-    const uint32_t soff = (uint32_t)min(lane, rmax) * (uint32_t)hkv * 4;
-    if (w == 0) g2lds4(kd_sc + tok0 * 4 + soff, tb + C::OFF_KDSC);
-    if (w == 1) g2lds4(vd_sc + tok0 * 4 + soff, tb + C::OFF_VDSC);
-    stage_rows_lds<BN>(tb + C::OFF_U, (const char*)(k + tok0 * D), krow_b * 2, rmax, w, lane);
+    if (w == 0) b2lds4(rsrc_at(kd_sc + tok0 * 4, ends(hkv * 4, 4)), sof, tb + C::OFF_KDSC);
+    if (w == 1) b2lds4(rsrc_at(vd_sc + tok0 * 4, ends(hkv * 4, 4)), sof, tb + C::OFF_VDSC);
+    rows.copy(tb + C::OFF_U, k + tok0 * D, rmax, w);
   };
 
   // dS of one 32-key block b of the tile (this lane: query qrow, keys k0 + 32b + 8(j/4) + 4·half + j%4)

@@ -256,6 +256,9 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc_at(const void* base, uint32_t byte
 __device__ inline void b2lds16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, void* lds_wave_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, 0, 0, 0);
 }
+__device__ inline void b2lds4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_wave_base, 4, voff, 0, 0, 0);
+}
 
 // XOR swizzles of the 16-byte chunks of E4M3 code tiles in LDS, chosen so that the 16 rows
 // read by a 16-lane group at one logical chunk land in 16 distinct 16-byte bank groups:
