@@ -834,15 +834,19 @@ __global__ __launch_bounds__(256 * HPB, D == 256 ? 1 : 2 / HPB) void attn_bwd_dq
 
   // K/V tile kt -> LDS buffer; keys past kv_end are clamped into the document (masked, P = 0)
   // d >= 128: lane offsets of the tile copies, fixed for the whole key loop
-  const RowCopies<BN, 4 * HPB, D >= 128 ? D : 128> rc((uint32_t)hkv * D * 2, w, lane);
+  // two heads per workgroup: only waves 0..3 copy, so the other wave of each SIMD starts its
+  // products while they issue the copies
+  const RowCopies<BN, 4, D >= 128 ? D : 128> rc((uint32_t)hkv * D * 2, w & 3, lane);
   auto stage = [&](int kt, char* kb) {
     const int k0 = kt * BN;
     char* vb = kb + TILE;
     if constexpr (D >= 128) {
       // keys past kv_end read zeros (masked: P = 0)
       const size_t row0 = ((size_t)(k_s0 + k0) * hkv + g) * D;
-      rc.copy(kb, k + row0, kv_end - 1 - k0, w);
-      rc.copy(vb, v + row0, kv_end - 1 - k0, w);
+      if (w < 4) {
+        rc.copy(kb, k + row0, kv_end - 1 - k0, w);
+        rc.copy(vb, v + row0, kv_end - 1 - k0, w);
+      }
     } else {
       i32x4 kreg[PT], vreg[PT];
 #pragma unroll

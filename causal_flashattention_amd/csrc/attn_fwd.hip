@@ -107,15 +107,20 @@ __global__ __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW) void attn_fwd_bf16_
   // d = 64: through registers. Keys past kv_end are clamped into the document: they are masked
   // (P = 0).
   // d >= 128: lane offsets of the tile copies, fixed for the whole key loop
-  const RowCopies<C::BN, NW, D >= 128 ? D : 128> rc((uint32_t)hkv * D * 2, w, lane);
+  // with two waves per SIMD (NW = 8), only waves 0..3 copy: the other wave of each SIMD starts
+  // its products while they issue the copies
+  constexpr int CW = NW == 8 ? 4 : NW;
+  const RowCopies<C::BN, CW, D >= 128 ? D : 128> rc((uint32_t)hkv * D * 2, w % CW, lane);
   auto stage = [&](int kt, char* kb) {
     const int k0 = kt * C::BN;
     char* vb = kb + C::KBYTES;
     if constexpr (D >= 128) {
       // keys past kv_end read zeros (masked: P = 0)
       const size_t row0 = ((size_t)(k_s0 + k0) * hkv + g) * D;
-      rc.copy(kb, k + row0, kv_end - 1 - k0, w);
-      rc.copy(vb, v + row0, kv_end - 1 - k0, w);
+      if (w < CW) {
+        rc.copy(kb, k + row0, kv_end - 1 - k0, w);
+        rc.copy(vb, v + row0, kv_end - 1 - k0, w);
+      }
     } else {
       i32x4 kreg[C::PER_THREAD], vreg[C::PER_THREAD];
 #pragma unroll
