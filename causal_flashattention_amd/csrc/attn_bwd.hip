@@ -208,16 +208,17 @@ __device__ __forceinline__ void dkdv_item(
   int q_s0 = s0, Lq = L;
   if constexpr (CROSS) {
     const int2 qd = qdoc[doc];
-    q_s0 = qd.x;
-    Lq = qd.y;
+    q_s0 = __builtin_amdgcn_readfirstlane(qd.x);
+    Lq = __builtin_amdgcn_readfirstlane(qd.y);
   }
   const int off = CROSS ? L - Lq : 0;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), half = lane >> 5;
   const int pair = w % NP;
   const bool ds_wave = w >= NP;
-  const int G = hq / hkv;
-  const int h_lo = SPLIT ? g * G + (G * split) / ns : g * G;  // this split's query heads
-  const int n_h = SPLIT ? g * G + (G * (split + 1)) / ns - h_lo : G;
+  const int G = __builtin_amdgcn_readfirstlane(hq / hkv);
+  // this split's query heads
+  const int h_lo = SPLIT ? __builtin_amdgcn_readfirstlane(g * G + (G * split) / ns) : g * G;
+  const int n_h = SPLIT ? __builtin_amdgcn_readfirstlane(g * G + (G * (split + 1)) / ns) - h_lo : G;
   const int kw0 = t * KT + 32 * pair;             // first doc-local key of this pair
   const int mykey = kw0 + (lane & 31);
   const float sl2 = scale * LOG2E;
@@ -238,21 +239,35 @@ __device__ __forceinline__ void dkdv_item(
   for (int b = 0; b < C::DB; ++b) acc[b] = f32x16{};
 
   const int q_begin = causal ? (CROSS ? max(0, t * KT - off) : t * KT) : 0;
-  const int n_qt = CROSS ? max(0, (Lq - q_begin + BM - 1) / BM) : (L - q_begin + BM - 1) / BM;
+  const int n_qt =
+      __builtin_amdgcn_readfirstlane(CROSS ? max(0, (Lq - q_begin + BM - 1) / BM) : (L - q_begin + BM - 1) / BM);
   const int n_steps = n_qt * n_h;
   const int wave_first_q = causal ? kw0 - off : 0;
 
-  // step st -> (query head, first doc-local query of the step): query heads outer and query tiles
-  // ascending from the diagonal; with dQ inside the pass, query tiles from the document end down
-  // to the diagonal with the heads inner (the order every key tile of the document shares)
-  auto step_at = [&](int st, int& h, int& q0) {
+  // A step's position (query head, first doc-local query of the step). Steps run the query heads
+  // outer and the query tiles ascending from the diagonal; with dQ inside the pass, the query
+  // tiles from the document end down to the diagonal with the heads inner (the order every key
+  // tile of the document shares). The loop walks them one per iteration (uniform values, no
+  // division per step).
+  struct Pos {
+    int h, q0;
+  };
+  const Pos first_pos{h_lo, FQ ? q_begin + (n_qt - 1) * BM : q_begin};
+  const int q_end = q_begin + n_qt * BM;
+  auto next_pos = [&](Pos ps) {
     if constexpr (FQ) {
-      h = h_lo + st % n_h;
-      q0 = q_begin + (n_qt - 1 - st / n_h) * BM;
+      if (++ps.h == h_lo + n_h) {
+        ps.h = h_lo;
+        ps.q0 -= BM;
+      }
     } else {
-      h = h_lo + st / n_qt;
-      q0 = q_begin + (st % n_qt) * BM;
+      ps.q0 += BM;
+      if (ps.q0 >= q_end) {
+        ps.q0 = q_begin;
+        ++ps.h;
+      }
     }
+    return ps;
   };
 
   // dQ product A operands: element e of operand kk is K[key 32kk + 8(lane/16) + e][d 16w + lane%16]
@@ -302,9 +317,8 @@ __device__ __forceinline__ void dkdv_item(
   i32x4 treg[TR];
   // d >= 128: the step tiles' copies (lane offsets fixed for the whole item)
   const RowCopies<BM, NP, D >= 128 ? D : 128> rc((uint32_t)hq * D * 2, pair, lane);
-  auto stage = [&](int st, char* buf) {
-    int h, q0;
-    step_at(st, h, q0);
+  auto stage = [&](Pos ps, char* buf) {
+    const int h = ps.h, q0 = ps.q0;
     const __bf16* src = ds_wave ? dout : q;
     if constexpr (D >= 128) {
       // rows past the document end read zeros (those queries are masked: P = 0, dS = 0)
@@ -337,17 +351,11 @@ __device__ __forceinline__ void dkdv_item(
       lb[BM + threadIdx.x] = -dreg;               // -D: the dP accumulator starts from it
     }
   };
-  auto active = [&](int st) {
-    int h, q0;
-    step_at(st, h, q0);
-    return q0 + BM - 1 >= wave_first_q && kw0 < L;
-  };
+  auto active = [&](Pos ps) { return ps.q0 + BM - 1 >= wave_first_q && kw0 < L; };
 
   // P wave, step st: per 32-query block, S, P (bf16, to the exchange buffer and the dV product),
   // dVᵀ += dOᵀ P
-  auto step_p = [&](int st, const char* buf, i32x4* xw) __attribute__((always_inline)) {
-    int h_unused, q0;
-    step_at(st, h_unused, q0);
+  auto step_p = [&](int q0, const char* buf, i32x4* xw) __attribute__((always_inline)) {
     const char* ob = buf + TILE;
     const f32x4* l2 = (const f32x4*)(buf + 2 * TILE);
     const bool masked = (causal && q0 + off < kw0 + 31) || q0 + BM > Lq;   // wave-uniform
@@ -423,7 +431,7 @@ __device__ __forceinline__ void dkdv_item(
   // accumulates onto −D, read from the stage as the accumulator's start), dS = P (dP − D) with the
   // bf16 P of its partner, dKᵀ += Qᵀ dS; with dQ inside the pass, dS (bf16) replaces P in the
   // exchange tile for the dQ product
-  auto step_ds = [&](int st, const char* buf, i32x4* xr) __attribute__((always_inline)) {
+  auto step_ds = [&](const char* buf, i32x4* xr) __attribute__((always_inline)) {
     const char* ob = buf + TILE;
     const f32x4* db = (const f32x4*)(buf + 2 * TILE + BM * 4);
     lds_char* xb = FQ ? lds_opaque(xr) : nullptr;
@@ -501,10 +509,9 @@ __device__ __forceinline__ void dkdv_item(
   // the step, from the dSᵀ tile `xt` of that step: wait for the previous key tile's part, add this
   // tile's, hand over (or write dQ). Lane l holds columns 16w + 4(l/16) + 0..3 of query row
   // q0 + 16·sb + l%16 (sub-block sb of 16 queries).
-  auto dq_phase = [&](int s, const void* xt_buf) __attribute__((always_inline)) {
+  auto dq_phase = [&](Pos ps, const void* xt_buf) __attribute__((always_inline)) {
     const lds_char* xt = lds_opaque(xt_buf);
-    int h, q0;
-    step_at(s, h, q0);
+    const int h = ps.h, q0 = ps.q0;
     const int l = lane_here(), gi = l >> 4, ii = l & 15;
     const int kt_last = causal ? q0 / KT : (L + KT - 1) / KT - 1;
     const bool first = t == 0, last = t == kt_last;
@@ -577,26 +584,34 @@ __device__ __forceinline__ void dkdv_item(
   // on `prv`; with dQ inside the pass, every wave then adds its dQ part of step i-2 (dSᵀ in
   // `xdq`; one call site for both roles keeps the register count within two waves per SIMD).
   // The conditions depend on i only, so every wave meets the same barriers.
+  // Positions of steps i + 1 (staged in iteration i), i (P waves), i − 1 (dS waves) and i − 2
+  // (dQ parts), shifted by one step per iteration.
+  Pos p_next = first_pos, p_cur = first_pos, p_prv = first_pos, p_dq = first_pos;
   auto iter = [&](int i, char* cur, char* prv, char* nxt, i32x4* xcur, i32x4* xprv, const i32x4* xdq)
       __attribute__((always_inline)) {
-    if (i + 1 < n_steps) stage(i + 1, nxt);
-    if (!ds_wave) {
-      if (i < n_steps && active(i)) step_p(i, cur, xcur);
+    if (i + 1 < n_steps) stage(p_next, nxt);
+    if (!per_lane(ds_wave)) {
+      if (i < n_steps && active(p_cur)) step_p(p_cur.q0, cur, xcur);
     } else {
-      if (i >= 1 && i - 1 < n_steps && active(i - 1)) step_ds(i - 1, prv, xprv);
+      if (i >= 1 && i - 1 < n_steps && active(p_prv)) step_ds(prv, xprv);
     }
     if (i + 1 < n_steps) stage_finish(nxt);
     if constexpr (FQ) {
-      if (i >= 2 && i - 2 < n_steps) dq_phase(i - 2, xdq);
+      if (i >= 2 && i - 2 < n_steps) dq_phase(p_dq, xdq);
     }
+    p_dq = p_prv;
+    p_prv = p_cur;
+    p_cur = p_next;
+    p_next = next_pos(p_next);
     wait_vmem();
     __syncthreads();
   };
 
   if (n_steps > 0) {
-    stage(0, st_a);
+    stage(first_pos, st_a);
     stage_finish(st_a);
   }
+  p_next = next_pos(first_pos);
   wait_vmem();
   __syncthreads();
   const int last_i = n_steps + (FQ ? 1 : 0);
@@ -649,7 +664,11 @@ __global__ __launch_bounds__(128 * NP, 1) void attn_bwd_dkdv_pair_kernel(
   __shared__ i32x4 xp_b[X::XP];
   __shared__ i32x4 xp_c[X::XP];
   const int ns = SPLIT ? n_split : 1;
-  const int p = blockIdx.x / (hkv * ns), g = blockIdx.x % hkv, split = SPLIT ? (blockIdx.x / hkv) % ns : 0;
+  // work-item values are the same in every lane; readfirstlane keeps them (and all derived from
+  // them) in scalar registers
+  const int p = __builtin_amdgcn_readfirstlane(blockIdx.x / (hkv * ns));
+  const int g = __builtin_amdgcn_readfirstlane(blockIdx.x % hkv);
+  const int split = SPLIT ? __builtin_amdgcn_readfirstlane((blockIdx.x / hkv) % ns) : 0;
   int s0, L, t, doc;
   if (!decode_item(plan, p, 32 * NP, false, s0, L, t, &doc)) return;
   dkdv_item<D, NP, CROSS, SPLIT, false>(q, k, v, dout, lse, delta, dk, dv, total_tokens, hq, hkv, scale, causal,

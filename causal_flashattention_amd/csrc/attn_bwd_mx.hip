@@ -109,15 +109,16 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
   __shared__ __attribute__((aligned(16))) char sb_a[C::BUF];
   __shared__ __attribute__((aligned(16))) char sb_b[C::BUF];
 
-  const int p = blockIdx.x / hkv, g = blockIdx.x % hkv;
+  const int p = __builtin_amdgcn_readfirstlane(blockIdx.x / hkv), g = __builtin_amdgcn_readfirstlane(blockIdx.x % hkv);
   int s0, L, t, doc;
   if (!decode_item(plan, p, 128, false, s0, L, t, &doc)) return;
   const int pcol = padoff[doc];
   const int lp = 32 * ((L + 31) / 32);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, half = lane >> 5, r32 = lane & 31;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), half = lane >> 5,
+            r32 = lane & 31;
   const int pair = w & 3;
   const bool ds_wave = w >= 4;
-  const int G = hq / hkv;
+  const int G = __builtin_amdgcn_readfirstlane(hq / hkv);
   const int kw0 = t * 128 + 32 * pair;
   const int mykey = kw0 + r32;
   const float sl2 = scale * LOG2E;
@@ -161,17 +162,30 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
   for (int b = 0; b < 4; ++b) acc[b] = f32x16{};
 
   const int q_begin = causal ? t * 128 : 0;
-  const int n_qt = (L - q_begin + BM - 1) / BM;
+  const int n_qt = __builtin_amdgcn_readfirstlane((L - q_begin + BM - 1) / BM);
   const int n_steps = n_qt * G;
   const int wave_first_q = causal ? kw0 : 0;
-  auto q0_of = [&](int st) { return q_begin + (st % n_qt) * BM; };
-  auto step_is_diag = [&](int st) { return causal && (q0_of(st) / 128 == t); };
-  auto active = [&](int st) { return q0_of(st) + BM - 1 >= wave_first_q && kw0 < L; };
+  // A step's position: its query head and first doc-local query. Steps run query tiles ascending
+  // from the diagonal with the heads outer; each role walks them one per iteration (uniform
+  // values, no division per step).
+  struct Pos {
+    int h, q0;
+  };
+  auto next_pos = [&](Pos ps) {
+    ps.q0 += BM;
+    if (ps.q0 >= L) {
+      ps.q0 = q_begin;
+      ++ps.h;
+    }
+    return ps;
+  };
+  auto step_is_diag = [&](int q0) { return causal && (q0 >> 7) == t; };
+  auto active = [&](int q0) { return q0 + BM - 1 >= wave_first_q && kw0 < L; };
 
-  // Operands of step st for this wave's role -> buffer. Rows past the document end are clamped
-  // into it (d-blocked, bf16) or into its last token block (token-blocked); they are masked.
-  // Lanes 0..63 of the first wave of each role fetch LSE or D into a register (stage_finish
-  // writes it after the step's compute).
+  // Operands of the step at position ps for this wave's role -> buffer. Rows past the document
+  // end are clamped into it (d-blocked, bf16) or into its last token block (token-blocked); they
+  // are masked. Each wave fetches the step's 64 LSE or D values into a register; the second
+  // wave of each role writes them to the buffer after the step's compute (stage_finish).
   float rreg = 0.f;
   // Lane offsets of the copies from a step's first row (first column for the token-blocked
   // copy), the same for every step; a step whose 64 queries all lie inside the document uses
@@ -190,11 +204,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
     tof[j] = (uint32_t)(rt * t_pad) + 16 * ((lane & 3) ^ vt_swz(rt));
   }
   const RowCopies<BM, 4, 128> rows((uint32_t)hq * D * 2, pair, lane);
-  auto stage = [&](int st, char* buf) {
-    const int h = g * G + st / n_qt;
-    const int q0 = q0_of(st);
+  auto stage = [&](Pos ps, char* buf) {
+    const int h = ps.h, q0 = ps.q0;
     const int rmax = L - 1 - q0;
     const size_t tok0 = (size_t)(s0 + q0) * hq + h;
+    // every wave loads the step's LSE or D row (one load site, so the register needs no copy
+    // between the two staging paths below, which would wait for the tile copies); pair 1 stores it
+    rreg = (ds_wave ? delta : lse)[(size_t)h * total_tokens + s0 + q0 + min(lane, rmax)];
     if (rmax >= BM - 1) {                       // the whole step lies inside the document
       if (narrow_role) {
         const auto rs = rsrc_at(qd + tok0 * QROW, 0x7fffffffu);
@@ -206,8 +222,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
         for (int j = 0; j < 2; ++j) b2lds16(rs, dof[j], buf + (2 * pair + j) * 1024);
       }
       if (pair == 0) b2lds4(rsrc_at((ds_wave ? dod_sc : qd_sc) + tok0 * 4, 0x7fffffffu), sof, buf + C::OFF_SC);
-      if (pair == 1) rreg = (ds_wave ? delta : lse)[(size_t)h * total_tokens + s0 + q0 + lane];
-      if (ds_wave || step_is_diag(st)) {
+      if (ds_wave || step_is_diag(q0)) {
         rows.copy(buf + C::OFF_U, (ds_wave ? q : dout) + tok0 * D, rmax, pair);
       } else {
         const auto rs = rsrc_at(dot + (size_t)h * D * t_pad + pcol + q0, 0x7fffffffu);
@@ -237,8 +252,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
     }
     if (pair == 0)
       g2lds4((ds_wave ? dod_sc : qd_sc) + tok0 * 4 + (uint32_t)min(lane, rmax) * (uint32_t)hq * 4, buf + C::OFF_SC);
-    if (pair == 1) rreg = (ds_wave ? delta : lse)[(size_t)h * total_tokens + s0 + q0 + min(lane, rmax)];
-    if (ds_wave || step_is_diag(st)) {
+    if (ds_wave || step_is_diag(q0)) {
       stage_rows_lds<BM>(buf + C::OFF_U, (const char*)((ds_wave ? q : dout) + tok0 * D), tok_b * 2, rmax, pair, lane);
     } else {
       const uint8_t* tsrc = dot + (size_t)h * D * t_pad + pcol + q0;
@@ -289,9 +303,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
   };
 
   // P wave, step st; the two query blocks one after the other
-  auto step_p = [&](int st, const char* buf, i32x4* xw) __attribute__((always_inline)) {
-    const int q0 = q0_of(st);
-    const bool diag = step_is_diag(st);
+  auto step_p = [&](int q0, const char* buf, i32x4* xw) __attribute__((always_inline)) {
+    const bool diag = per_lane(step_is_diag(q0));
     const bool masked = (causal && q0 < kw0 + 31) || q0 + BM > L;   // wave-uniform
     const f32x4* l2 = (const f32x4*)(buf + C::OFF_ROW);
     i32x4 pw[4];                                // bf16 P: exchange words and diagonal B operands
@@ -357,7 +370,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
 
   // dS wave, step st (one iteration after its P wave); the query blocks one after the other.
   // The dP product accumulates onto -D (stored negated in the stage), so x = dP - D.
-  auto step_ds = [&](int st, const char* buf, const i32x4* xr) __attribute__((always_inline)) {
+  auto step_ds = [&](const char* buf, const i32x4* xr) __attribute__((always_inline)) {
     const f32x4* dd = (const f32x4*)(buf + C::OFF_ROW);
     bf16x8 sf[4];                               // bf16 dS, B operands of the dK product
 #pragma unroll
@@ -403,26 +416,34 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
 
   // Iteration i. The two roles run separate loops (so each keeps only its own addresses live);
   // both execute one barrier per iteration, n_steps + 1 iterations after the prologue barrier.
+  // pc: position of the step this wave computes in the iteration (P: i, dS: i - 1); pn: of the
+  // step it stages (P: i + 1, dS: i).
+  Pos pc{g * G, q_begin}, pn = pc;
   auto iter_p = [&](int i, const char* pcur, char* pnxt, i32x4* xw) __attribute__((always_inline)) {
-    if (i + 1 < n_steps) stage(i + 1, pnxt);
-    if (i < n_steps && active(i)) step_p(i, pcur, xw);
+    if (i + 1 < n_steps) stage(pn, pnxt);
+    if (i < n_steps && active(pc.q0)) step_p(pc.q0, pcur, xw);
     if (i + 1 < n_steps) stage_finish(pnxt);
+    pc = pn;
+    pn = next_pos(pn);
     wait_vmem();
     __syncthreads();
   };
   auto iter_ds = [&](int i, char* sload, const char* suse, const i32x4* xr) __attribute__((always_inline)) {
-    if (i < n_steps) stage(i, sload);
-    if (i >= 1 && active(i - 1)) step_ds(i - 1, suse, xr);
+    if (i < n_steps) stage(pn, sload);
+    if (i >= 1 && active(pc.q0)) step_ds(suse, xr);
     if (i < n_steps) stage_finish(sload);
+    pc = pn;
+    pn = next_pos(pn);
     wait_vmem();
     __syncthreads();
   };
 
   if (!ds_wave) {
     if (n_steps > 0) {
-      stage(0, pb_a);
+      stage(pn, pb_a);
       stage_finish(pb_a);
     }
+    pn = next_pos(pn);
     wait_vmem();
     __syncthreads();
     for (int i = 0; i <= n_steps; i += 2) {
@@ -430,6 +451,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
       if (i + 1 <= n_steps) iter_p(i + 1, pb_b, pb_a, xp_b);
     }
   } else {
+    wait_vmem();                                // the V_d registers have landed
     __syncthreads();
     for (int i = 0; i <= n_steps; i += 2) {
       iter_ds(i, sb_a, sb_b, xp_b);

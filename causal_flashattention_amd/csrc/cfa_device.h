@@ -83,7 +83,7 @@ __device__ inline bool decode_item(const Plan& pl, int p, int tile_rows, bool ex
   L = __builtin_amdgcn_readfirstlane(di.y);
   const int nt = (L + tile_rows - 1) / tile_rows;
   const int j = p - __builtin_amdgcn_readfirstlane(pl.pref[lo]);
-  tile = expensive_first ? (nt - 1 - j) : j;
+  tile = __builtin_amdgcn_readfirstlane(expensive_first ? (nt - 1 - j) : j);
   return true;
 }
 
@@ -267,7 +267,23 @@ __device__ inline void b2lds4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, void* ld
 __device__ inline int kd_swz(int r) { return (r >> 1) & 7; }
 __device__ inline int vt_swz(int r) { return (r >> 2) & 3; }
 
-__device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// A wave-uniform condition handed to the compiler as a per-lane value: a branch on it is then
+// compiled with exec masks and both arms keep one register assignment (on a scalar branch the
+// register allocator may copy every accumulator register at the join of the two arms).
+__device__ inline bool per_lane(bool b) {
+  int v = b;
+  asm volatile("" : "+v"(v));
+  return v != 0;
+}
+
+// Wait until every vector-memory operation of this wave has completed. The builtin lets the
+// compiler's wait insertion know that every earlier load has landed, so it adds no wait of its
+// own for them later; the empty asm statements keep memory accesses from moving across it.
+__device__ inline void wait_vmem() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt not waited for
+  asm volatile("" ::: "memory");
+}
 // Wait until at most N vector-memory operations of this wave are outstanding (the N most recent
 // may still be in flight).
 template <int N>
