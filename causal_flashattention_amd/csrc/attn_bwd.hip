@@ -810,19 +810,20 @@ __global__ __launch_bounds__(256 * HPB, D == 256 ? 1 : 2 / HPB) void attn_bwd_dq
   __shared__ __attribute__((aligned(16))) char lds_b[STAGE];
 
   const int n_hb = hq / HPB;
-  const int p = blockIdx.x / n_hb, hb = blockIdx.x % n_hb;
+  // work-item values are the same in every lane; readfirstlane keeps them in scalar registers
+  const int p = __builtin_amdgcn_readfirstlane(blockIdx.x / n_hb), hb = __builtin_amdgcn_readfirstlane(blockIdx.x % n_hb);
   int s0, L, t, doc;
   if (!decode_item(plan, p, 128, true, s0, L, t, &doc)) return;
   int k_s0 = s0, Lk = L;                         // key rows (cross-attention: their own documents)
   if constexpr (CROSS) {
     const int2 kd = kdoc[doc];
-    k_s0 = kd.x;
-    Lk = kd.y;
+    k_s0 = __builtin_amdgcn_readfirstlane(kd.x);
+    Lk = __builtin_amdgcn_readfirstlane(kd.y);
   }
   const int off = CROSS ? Lk - L : 0;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), half = lane >> 5;
   const int h = hb * HPB + (w >> 2);             // this wave's query head
-  const int g = h / (hq / hkv);
+  const int g = __builtin_amdgcn_readfirstlane(h / (hq / hkv));
   const int wr0 = t * 128 + 32 * (w & 3);
   const int qrow = wr0 + (lane & 31);
   const int kv_end = causal ? (CROSS ? min(Lk, min(L, (t + 1) * 128) + off) : min(L, (t + 1) * 128)) : Lk;

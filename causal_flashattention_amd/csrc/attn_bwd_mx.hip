@@ -508,11 +508,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
   __shared__ __attribute__((aligned(16))) char lds_a[C::STAGE];
   __shared__ __attribute__((aligned(16))) char lds_b[C::STAGE];
 
-  const int p = blockIdx.x / hq, h = blockIdx.x % hq;
+  // work-item values are the same in every lane; readfirstlane keeps them in scalar registers
+  const int p = __builtin_amdgcn_readfirstlane(blockIdx.x / hq), h = __builtin_amdgcn_readfirstlane(blockIdx.x % hq);
   int s0, L, t, doc;
   if (!decode_item(plan, p, 128, true, s0, L, t, &doc)) return;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), half = lane >> 5, r32 = lane & 31;
-  const int g = h / (hq / hkv);
+  const int g = __builtin_amdgcn_readfirstlane(h / (hq / hkv));
   const int wr0 = t * 128 + 32 * w;
   const int qrow = wr0 + r32;
   const int kv_end = causal ? min(L, (t + 1) * 128) : L;

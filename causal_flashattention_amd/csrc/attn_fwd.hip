@@ -60,21 +60,22 @@ __global__ __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW) void attn_fwd_bf16_
   __shared__ __attribute__((aligned(16))) char lds_b[C::STAGE];
 
   const int wid = blockIdx.x;
-  const int p = wid / n_hb, hb = wid % n_hb;
+  // work-item values are the same in every lane; readfirstlane keeps them in scalar registers
+  const int p = __builtin_amdgcn_readfirstlane(wid / n_hb), hb = __builtin_amdgcn_readfirstlane(wid % n_hb);
   int s0, L, t, doc;
   if (!decode_item(plan, p, BMW, true, s0, L, t, &doc)) return;
   // query rows [s0, s0 + L), key rows [k_s0, k_s0 + Lk); off = 0 for self-attention
   int k_s0 = s0, Lk = L;
   if constexpr (CROSS) {
     const int2 kd = kdoc[doc];
-    k_s0 = kd.x;
-    Lk = kd.y;
+    k_s0 = __builtin_amdgcn_readfirstlane(kd.x);
+    Lk = __builtin_amdgcn_readfirstlane(kd.y);
   }
   const int off = CROSS ? Lk - L : 0;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int G = hq / hkv;
+  const int G = __builtin_amdgcn_readfirstlane(hq / hkv);
   const int h = hb * HPW + (w % HPW);
-  const int g = h / G;
+  const int g = __builtin_amdgcn_readfirstlane(h / G);
   const int wr0 = t * BMW + 32 * (w / HPW);      // first doc-local row of this wave
   const int wg_rows_end = min(L, (t + 1) * BMW);
   // keys the workgroup needs (cross-attention: possibly none)

@@ -72,15 +72,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
   __shared__ __attribute__((aligned(16))) char lds_b[C::STAGE];
 
   const int wid = blockIdx.x;
-  const int p = wid / n_hb, hb = wid % n_hb;
+  // work-item values are the same in every lane; readfirstlane keeps them in scalar registers
+  const int p = __builtin_amdgcn_readfirstlane(wid / n_hb), hb = __builtin_amdgcn_readfirstlane(wid % n_hb);
   int s0, L, t, doc;
   if (!decode_item(plan, p, BMW, true, s0, L, t, &doc)) return;
   const int pcol = padoff[doc];                 // first token-blocked column of the document
   const int lp = 32 * ((L + 31) / 32);          // padded document length (columns)
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), half = lane >> 5, r32 = lane & 31;
-  const int G = hq / hkv;
+  const int G = __builtin_amdgcn_readfirstlane(hq / hkv);
   const int h = hb * HPW + (w % HPW);
-  const int g = h / G;
+  const int g = __builtin_amdgcn_readfirstlane(h / G);
   const int wr0 = t * BMW + 32 * (w / HPW);
   const int wg_rows_end = min(L, (t + 1) * BMW);
   const int kv_end = causal ? wg_rows_end : L;
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
 #pragma unroll
         for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
       }
-      const bool diag = tile_is_diag(kt);
+      const bool diag = per_lane(tile_is_diag(kt));
       // diagonal tiles: P̃ (bf16); other tiles: P̃·2^8 (E4M3 with scale 2^-8)
       const float bias = diag ? -m_run : 8.f - m_run;
       float ls4[4] = {0.f, 0.f, 0.f, 0.f};          // four partial row sums (short add chains)
