@@ -9,11 +9,11 @@
 //
 // The pass is bound by reading the cache once from HBM (no reuse across sequences), so the
 // design keeps every cache byte to one read and makes the arithmetic cheap next to it:
-//  * Workgroup = (256-key chunk of one sequence, kv head g, block of up to 32 query heads of g's
+//  * Workgroup = (512-key chunk of one sequence, kv head g, block of up to 32 query heads of g's
 //    group). The group's query heads play the 32 query columns of the forward kernel's
 //    transposed product, so each K/V byte read serves all of them.
-//  * 4 waves × 64 keys. A wave loads its keys' rows 32 at a time into registers (the next
-//    block's loads in flight during the current block's products), converts them to bf16
+//  * 4 waves × 128 keys. A wave loads its keys' rows 32 at a time into registers (the next
+//    blocks' loads in flight during the current block's products), converts them to bf16
 //    (MX: v_cvt_scalef32_pk_bf16_fp8 with the block scale; E4M3 × 2^e is exact in bf16) into its
 //    own swizzled LDS region, then Sᵀ = K Qᵀ and Oᵀ += Vᵀ Pᵀ with v_mfma_f32_32x32x16_bf16 and an
 //    online softmax per column. No barrier inside the key loop.
@@ -23,11 +23,11 @@
 
 namespace cfa {
 
-constexpr int DEC_CHUNK = 256;  // keys per workgroup
+constexpr int DEC_CHUNK = 512;  // keys per workgroup
 constexpr int DEC_SUB = 32;     // keys per wave block
 
 // Partial slot of chunk t of a sequence whose cache starts at token s0 (sequence index b):
-// floor((s0 + 256 t) / 256) + b, injective over all (b, t) and below ceil(Tk/256) + n_seqs.
+// floor((s0 + 512 t) / 512) + b, injective over all (b, t) and below ceil(Tk/512) + n_seqs.
 __device__ inline int dec_slot(int s0, int t, int b) { return (s0 + DEC_CHUNK * t) / DEC_CHUNK + b; }
 
 template <int D, bool MX>
@@ -69,7 +69,8 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(
   const bool col_ok = 32 * hb + col < G;
   const int h = g * G + 32 * hb + col;
   const int k1 = min(L, (t + 1) * DEC_CHUNK);           // end of this chunk's keys
-  const int kw0 = t * DEC_CHUNK + 64 * w;               // this wave's first key
+  constexpr int WK = DEC_CHUNK / 4, NB = WK / DEC_SUB;  // keys and 32-key blocks per wave
+  const int kw0 = t * DEC_CHUNK + WK * w;               // this wave's first key
   const SwzOffsets<D> so(lane);
   char* kt = lds + w * 2 * SUBB;
   char* vt = kt + SUBB;
@@ -86,9 +87,9 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(
   for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // ---- raw rows of a 32-key block (keys past k1 repeat key k1 - 1: masked below). MX: both of
-  // the wave's blocks are loaded up front (two blocks of codes in flight per wave); bf16: one
-  // block ahead (its rows take twice the registers).
+  // ---- raw rows of a 32-key block (keys past k1 repeat key k1 - 1: masked below). MX: two
+  // blocks of codes in flight ahead of the block being converted; bf16: one block ahead (its rows
+  // take twice the registers).
   constexpr int NBUF = MX ? 2 : 1;
   i32x4 kraw[NBUF][LD::NL], vraw[NBUF][LD::NL];
   int kscw[NBUF][LD::NL], vscw[NBUF][LD::NL];   // MX: the row's D/32 scale bytes (D = 128: one word)
@@ -186,16 +187,19 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(
   };
 
   if (kw0 < k1) {
-    const bool second = kw0 + DEC_SUB < k1;
+    const int nb = min(NB, (k1 - kw0 + DEC_SUB - 1) / DEC_SUB);   // this wave's blocks (1 .. NB)
     load(kw0, 0);
-    if (MX && second) load(kw0 + DEC_SUB, NBUF - 1);   // MX: both blocks in flight at once
-    store(0);
-    if (!MX && second) load(kw0 + DEC_SUB, 0);         // bf16: in flight during the first block
-    block(kw0);
-    if (second) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's tile reads are done
-      store(NBUF - 1);
-      block(kw0 + DEC_SUB);
+    if (MX && nb > 1) load(kw0 + DEC_SUB, 1);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (i < nb) {
+        if (i > 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's tile reads are done
+        store(MX ? (i & 1) : 0);
+        // refill the raw registers just converted: block i + 2 (MX) or i + 1 (bf16)
+        if (MX && i + 2 < nb) load(kw0 + (i + 2) * DEC_SUB, i & 1);
+        if (!MX && i + 1 < nb) load(kw0 + (i + 1) * DEC_SUB, 0);
+        block(kw0 + i * DEC_SUB);
+      }
     }
   }
 
