@@ -9,10 +9,10 @@
 //
 // The pass is bound by reading the cache once from HBM (no reuse across sequences), so the
 // design keeps every cache byte to one read and makes the arithmetic cheap next to it:
-//  * Workgroup = (512-key chunk of one sequence, kv head g, block of up to 32 query heads of g's
+//  * Workgroup = (1024-key chunk of one sequence, kv head g, block of up to 32 query heads of g's
 //    group). The group's query heads play the 32 query columns of the forward kernel's
 //    transposed product, so each K/V byte read serves all of them.
-//  * 4 waves × 128 keys. A wave loads its keys' rows 32 at a time into registers (the next
+//  * 4 waves × 256 keys. A wave loads its keys' rows 32 at a time into registers (the next
 //    blocks' loads in flight during the current block's products), converts them to bf16
 //    (MX: v_cvt_scalef32_pk_bf16_fp8 with the block scale; E4M3 × 2^e is exact in bf16) into its
 //    own swizzled LDS region, then Sᵀ = K Qᵀ and Oᵀ += Vᵀ Pᵀ with v_mfma_f32_32x32x16_bf16 and an
@@ -23,11 +23,11 @@
 
 namespace cfa {
 
-constexpr int DEC_CHUNK = 512;  // keys per workgroup
+constexpr int DEC_CHUNK = 1024;  // keys per workgroup
 constexpr int DEC_SUB = 32;     // keys per wave block
 
 // Partial slot of chunk t of a sequence whose cache starts at token s0 (sequence index b):
-// floor((s0 + 512 t) / 512) + b, injective over all (b, t) and below ceil(Tk/512) + n_seqs.
+// floor((s0 + 1024 t) / 1024) + b, injective over all (b, t) and below ceil(Tk/1024) + n_seqs.
 __device__ inline int dec_slot(int s0, int t, int b) { return (s0 + DEC_CHUNK * t) / DEC_CHUNK + b; }
 
 template <int D, bool MX>

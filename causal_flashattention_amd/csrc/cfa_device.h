@@ -37,7 +37,7 @@ struct PlanLayout {
     docinfo = align256(header + 64 * sizeof(int));
     order = align256(docinfo + size_t(n_docs) * 2 * sizeof(int));
     pref = align256(order + size_t(n_docs) * sizeof(int));
-    padoff = align256(pref + 5 * size_t(n_docs + 1) * sizeof(int));
+    padoff = align256(pref + 6 * size_t(n_docs + 1) * sizeof(int));
     end = align256(padoff + size_t(n_docs + 1) * sizeof(int));
   }
 };
@@ -57,7 +57,7 @@ struct Plan {
 };
 
 __host__ __device__ inline int pref_slot(int tile_rows) {
-  return tile_rows == 32 ? 0 : tile_rows == 64 ? 1 : tile_rows == 128 ? 2 : tile_rows == 256 ? 3 : 4;
+  return tile_rows == 32 ? 0 : tile_rows == 64 ? 1 : tile_rows == 128 ? 2 : tile_rows == 256 ? 3 : tile_rows == 512 ? 4 : 5;
 }
 
 // Decode work item p (0-based position in the longest-first list) into a document and a tile.

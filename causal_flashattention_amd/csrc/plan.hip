@@ -137,8 +137,8 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int* __restric
   }
   __threadfence_block();
   __syncthreads();
-  // 5. item prefixes for tile heights 32, 64, 128, 256, 512 over the sorted order
-  for (int s = 0; s < 5; ++s) {
+  // 5. item prefixes for tile heights 32, 64, ..., 1024 over the sorted order
+  for (int s = 0; s < 6; ++s) {
     const int rows = 32 << s;
     block_prefix(n_docs, [&](int i) { int L = docinfo[order[i]].y; return (L + rows - 1) / rows; },
                  pref + s * (n_docs + 1), tmp);

@@ -270,7 +270,7 @@ size_t mx_quantize_bytes(int axis, int total_tokens, int n_docs, int h, int d, s
  *                 owns cache rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 and its query sees all
  *                 of them. A sequence with no rows gets o = 0 and lse = -inf.
  *   d           : 64 or 128. Query head h reads kv head h / (hq / hkv).
- * Work is split over 512-key chunks; the chunk partials are merged in chunk order, so results
+ * Work is split over 1024-key chunks; the chunk partials are merged in chunk order, so results
  * are deterministic. Scratch: cfa_decode_workspace_bytes() bytes (256-byte aligned); no other
  * allocation. Errors as for the other calls.
  */
