@@ -19,59 +19,73 @@ namespace cfa {
 constexpr int PLAN_THREADS = 1024;
 constexpr int PLAN_BUCKETS = 4096;
 
+// Inclusive sum over the lanes of a wave up to this lane (lane shuffles, no barrier).
+__device__ inline int wave_incl_sum(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off, 64);
+    if (lane >= off) v += u;
+  }
+  return v;
+}
+
+// Exclusive sum of one value per thread over the threads of the block in thread order, and the
+// block total. `wt` is LDS scratch of PLAN_THREADS / 64 ints. Two barriers (the second lets the
+// next call reuse `wt`).
+__device__ inline int block_excl_sum(int v, int* wt, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_incl_sum(v);
+  if (lane == 63) wt[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < PLAN_THREADS / 64; ++w) {
+    const int x = wt[w];
+    before += w < wave ? x : 0;
+    all += x;
+  }
+  __syncthreads();
+  total = all;
+  return before + incl - v;
+}
+
 __device__ inline void block_exclusive_scan_desc(int* a, int n, int* tmp) {
-  // exclusive scan of a[0..n) in DESCENDING index order: a[i] <- sum_{j>i} a[j]; n <= 4096
-  const int tid = threadIdx.x;
+  // exclusive scan of a[0..n) in DESCENDING index order: a[i] <- sum_{j>i} a[j]; n <= 4096.
+  // Thread t holds the PER buckets from (PLAN_THREADS - 1 - t)·PER up, so the threads before it
+  // hold exactly the higher buckets.
   constexpr int PER = PLAN_BUCKETS / PLAN_THREADS;  // 4
+  const int r = PLAN_THREADS - 1 - (int)threadIdx.x;
   int loc[PER];
   int s = 0;
   for (int e = PER - 1; e >= 0; --e) {
-    int i = tid * PER + e;
-    int v = (i < n) ? a[i] : 0;
+    const int i = r * PER + e;
+    const int v = (i < n) ? a[i] : 0;
     loc[e] = s;
     s += v;
   }
-  tmp[tid] = s;
-  __syncthreads();
-  // suffix sums over threads (Hillis-Steele)
-  for (int off = 1; off < PLAN_THREADS; off <<= 1) {
-    int v = (tid + off < PLAN_THREADS) ? tmp[tid + off] : 0;
-    __syncthreads();
-    tmp[tid] += v;
-    __syncthreads();
-  }
-  int after = (tid + 1 < PLAN_THREADS) ? tmp[tid + 1] : 0;
-  __syncthreads();
+  int total;
+  const int after = block_excl_sum(s, tmp, total);
   for (int e = 0; e < PER; ++e) {
-    int i = tid * PER + e;
+    const int i = r * PER + e;
     if (i < n) a[i] = loc[e] + after;
   }
   __syncthreads();
 }
 
 // Exclusive prefix (ascending) of values produced by f(i) for i in [0, n), written to out[0..n]
-// (out[n] = total). Chunks of PLAN_THREADS; `carry` and `tmp` are LDS scratch.
+// (out[n] = total). Chunks of PLAN_THREADS; `tmp` is LDS scratch.
 template <typename F>
 __device__ inline void block_prefix(int n, F f, int* out, int* tmp) {
-  const int tid = threadIdx.x;
   int carry = 0;
   for (int base = 0; base < n; base += PLAN_THREADS) {
-    int i = base + tid;
-    int v = (i < n) ? f(i) : 0;
-    tmp[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < PLAN_THREADS; off <<= 1) {
-      int u = (tid >= off) ? tmp[tid - off] : 0;
-      __syncthreads();
-      tmp[tid] += u;
-      __syncthreads();
-    }
-    if (i < n) out[i] = carry + tmp[tid] - v;
-    int chunk_total = tmp[PLAN_THREADS - 1];
-    __syncthreads();
-    carry += chunk_total;
+    const int i = base + (int)threadIdx.x;
+    const int v = (i < n) ? f(i) : 0;
+    int total;
+    const int ex = block_excl_sum(v, tmp, total);
+    if (i < n) out[i] = carry + ex;
+    carry += total;
   }
-  if (tid == 0) out[n] = carry;
+  if (threadIdx.x == 0) out[n] = carry;
   __syncthreads();
 }
 
@@ -128,7 +142,8 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int* __restric
       const int other = __shfl(key, j, 64);
       rank += (j < lane && other == key) ? 1 : 0;
     }
-    for (int w = 0; w < PLAN_THREADS / 64; ++w) {
+    const int n_waves = min(PLAN_THREADS, n_docs - base + 63) / 64;   // waves holding documents
+    for (int w = 0; w < n_waves; ++w) {
       if (wave == w && ok) order[naive ? n : hist[key] + rank] = n;
       __syncthreads();
       if (wave == w && ok) atomicAdd(&hist[key], 1);
