@@ -49,6 +49,39 @@ __device__ inline int block_excl_sum(int v, int* wt, int& total) {
   return before + incl - v;
 }
 
+// block_excl_sum for N values per thread at once (one exchange of wave totals for all N).
+// `wt` holds N · PLAN_THREADS / 64 ints.
+template <int N>
+__device__ inline void block_excl_sum_n(const int (&v)[N], int (&ex)[N], int (&total)[N], int* wt) {
+  constexpr int NW = PLAN_THREADS / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl[N];
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    incl[c] = wave_incl_sum(v[c]);
+    if (lane == 63) wt[c * NW + wave] = incl[c];
+  }
+  __syncthreads();
+  int before[N], all[N];
+#pragma unroll
+  for (int c = 0; c < N; ++c) before[c] = all[c] = 0;
+#pragma unroll 1
+  for (int w = 0; w < NW; ++w) {
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+      const int x = wt[c * NW + w];
+      before[c] += w < wave ? x : 0;
+      all[c] += x;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    ex[c] = before[c] + incl[c] - v[c];
+    total[c] = all[c];
+  }
+  __syncthreads();
+}
+
 __device__ inline void block_exclusive_scan_desc(int* a, int n, int* tmp) {
   // exclusive scan of a[0..n) in DESCENDING index order: a[i] <- sum_{j>i} a[j]; n <= 4096.
   // Thread t holds the PER buckets from (PLAN_THREADS - 1 - t)·PER up, so the threads before it
@@ -69,23 +102,6 @@ __device__ inline void block_exclusive_scan_desc(int* a, int n, int* tmp) {
     const int i = r * PER + e;
     if (i < n) a[i] = loc[e] + after;
   }
-  __syncthreads();
-}
-
-// Exclusive prefix (ascending) of values produced by f(i) for i in [0, n), written to out[0..n]
-// (out[n] = total). Chunks of PLAN_THREADS; `tmp` is LDS scratch.
-template <typename F>
-__device__ inline void block_prefix(int n, F f, int* out, int* tmp) {
-  int carry = 0;
-  for (int base = 0; base < n; base += PLAN_THREADS) {
-    const int i = base + (int)threadIdx.x;
-    const int v = (i < n) ? f(i) : 0;
-    int total;
-    const int ex = block_excl_sum(v, tmp, total);
-    if (i < n) out[i] = carry + ex;
-    carry += total;
-  }
-  if (threadIdx.x == 0) out[n] = carry;
   __syncthreads();
 }
 
@@ -152,14 +168,33 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int* __restric
   }
   __threadfence_block();
   __syncthreads();
-  // 5. item prefixes for tile heights 32, 64, ..., 1024 over the sorted order
-  for (int s = 0; s < 6; ++s) {
-    const int rows = 32 << s;
-    block_prefix(n_docs, [&](int i) { int L = docinfo[order[i]].y; return (L + rows - 1) / rows; },
-                 pref + s * (n_docs + 1), tmp);
+  // 5. item prefixes for tile heights 32, 64, ..., 1024 over the sorted order, and 6. the MX
+  // token-block column offsets in document order: one pass (each document's lengths are read
+  // once; the seven scans share it)
+  constexpr int NS = 6;
+  int carry[NS + 1];
+#pragma unroll
+  for (int c = 0; c <= NS; ++c) carry[c] = 0;
+  for (int base = 0; base < n_docs; base += PLAN_THREADS) {
+    const int i = base + tid;
+    const bool ok = i < n_docs;
+    const int Ls = ok ? docinfo[order[i]].y : 0;     // sorted order
+    const int Li = ok ? docinfo[i].y : 0;            // document order
+    int v[NS + 1], ex[NS + 1], total[NS + 1];
+#pragma unroll
+    for (int c = 0; c < NS; ++c) v[c] = (Ls + (32 << c) - 1) / (32 << c);
+    v[NS] = (Li + 31) / 32 * 32;
+    block_excl_sum_n<NS + 1>(v, ex, total, tmp);
+#pragma unroll
+    for (int c = 0; c <= NS; ++c) {
+      if (ok) (c < NS ? pref + c * (n_docs + 1) : padoff)[i] = carry[c] + ex[c];
+      carry[c] += total[c];
+    }
   }
-  // 6. MX token-block column offsets, document order
-  block_prefix(n_docs, [&](int i) { int L = docinfo[i].y; return (L + 31) / 32 * 32; }, padoff, tmp);
+  if (tid == 0) {
+    for (int c = 0; c < NS; ++c) pref[c * (n_docs + 1) + n_docs] = carry[c];
+    padoff[n_docs] = carry[NS];
+  }
   if (tid == 0) header[0] = sflag;
 }
 
