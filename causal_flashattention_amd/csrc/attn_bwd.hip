@@ -307,9 +307,9 @@ __device__ __forceinline__ void dkdv_item(
     return xrow * 128 + (((u ^ fx) & 3) << 5) + 8 * (l >> 5);
   };
 
-  // The step at position ps -> buffer: P waves copy the Q tile, dS waves the dO tile (direct
-  // global -> LDS); the first BM threads (wave 0) fetch the step's LSE and D into registers,
-  // written by stage_finish. Rows past the document end are clamped into it and masked (P = 0).
+  // Step st -> buffer: P waves copy the Q tile, dS waves the dO tile (direct global -> LDS);
+  // lanes 0..31 of wave 0 fetch LSE and D into registers, written by stage_finish. Rows past
+  // the document end are clamped into it and masked (P = 0).
   float lreg = 0.f, dreg = 0.f;
   // d = 64: 144-byte padded rows (no swizzle), staged through registers: the role's NP waves
   // load the BM × D tile as 16-byte chunks (TR per lane) and stage_finish writes them
@@ -353,8 +353,8 @@ __device__ __forceinline__ void dkdv_item(
   };
   auto active = [&](Pos ps) { return ps.q0 + BM - 1 >= wave_first_q && kw0 < L; };
 
-  // P wave, the step whose first query is q0: per 32-query block, S, P (bf16, to the exchange
-  // buffer and the dV product), dVᵀ += dOᵀ P
+  // P wave, step st: per 32-query block, S, P (bf16, to the exchange buffer and the dV product),
+  // dVᵀ += dOᵀ P
   auto step_p = [&](int q0, const char* buf, i32x4* xw) __attribute__((always_inline)) {
     const char* ob = buf + TILE;
     const f32x4* l2 = (const f32x4*)(buf + 2 * TILE);
@@ -427,8 +427,8 @@ __device__ __forceinline__ void dkdv_item(
     }
   };
 
-  // dS wave, one step behind its P wave (the previous iteration's step): per 32-query block,
-  // dP − D (the product accumulates onto −D, read from the stage as the accumulator's start), dS = P (dP − D) with the
+  // dS wave, step st (one iteration after its P wave): per 32-query block, dP − D (the product
+  // accumulates onto −D, read from the stage as the accumulator's start), dS = P (dP − D) with the
   // bf16 P of its partner, dKᵀ += Qᵀ dS; with dQ inside the pass, dS (bf16) replaces P in the
   // exchange tile for the dQ product
   auto step_ds = [&](const char* buf, i32x4* xr) __attribute__((always_inline)) {

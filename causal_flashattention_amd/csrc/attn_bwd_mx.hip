@@ -302,7 +302,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
     return a;
   };
 
-  // P wave, the step whose first query is q0; the two query blocks one after the other
+  // P wave, step st; the two query blocks one after the other
   auto step_p = [&](int q0, const char* buf, i32x4* xw) __attribute__((always_inline)) {
     const bool diag = per_lane(step_is_diag(q0));
     const bool masked = (causal && q0 < kw0 + 31) || q0 + BM > L;   // wave-uniform
@@ -368,8 +368,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
     }
   };
 
-  // dS wave, one step behind its P wave (the previous iteration's step); the query blocks one
-  // after the other.
+  // dS wave, step st (one iteration after its P wave); the query blocks one after the other.
   // The dP product accumulates onto -D (stored negated in the stage), so x = dP - D.
   auto step_ds = [&](const char* buf, const i32x4* xr) __attribute__((always_inline)) {
     const f32x4* dd = (const f32x4*)(buf + C::OFF_ROW);
