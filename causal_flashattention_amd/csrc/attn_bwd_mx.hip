@@ -276,27 +276,28 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mx_kernel(
   // accumulated onto a0
   auto dscores = [&](const char* buf, int qb, f32x16 a0) __attribute__((always_inline)) {
     const int qr = 32 * qb + r32;
-    const int sc = *(const int*)(buf + C::OFF_SC + qr * 4);
+    // the row's four block scales; this lane's blocks are 2s + half (s = 0, 1): bytes 2s of scw
+    const int scw = *(const int*)(buf + C::OFF_SC + qr * 4) >> (8 * half);
     f32x16 a = a0;
     if (FP4 && narrow_role) {
       const char* rp = buf + qr * (D / 2);
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        a = mfma32_mx_fp4(fp4_operand(*(const i32x4*)(rp + kq[s])), (sc >> (8 * (2 * s + half))) & 0xFF, kvb[s],
-                          kvs[s], a);
+        a = mfma32_scale_byte<4, 4>(fp4_operand(*(const i32x4*)(rp + kq[s])), scw, 2 * s, kvb[s], kvs[s], a);
     } else if (FP6 && narrow_role) {
       const char* rp = buf + qr * (D / 2);
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        a = mfma32_mx_fp6<F6>(fp6_operand(*(const i32x4*)(rp + kq[s]), *(const i32x2*)(buf + 4096 + 16 * (64 * s + qr) + 8 * half)),
-                          (sc >> (8 * (2 * s + half))) & 0xFF, kvb[s], kvs[s], a);
+        a = mfma32_scale_byte<F6, F6>(
+            fp6_operand(*(const i32x4*)(rp + kq[s]), *(const i32x2*)(buf + 4096 + 16 * (64 * s + qr) + 8 * half)),
+            scw, 2 * s, kvb[s], kvs[s], a);
     } else {
       const char* rp = buf + qr * 128;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const i32x4 lo = *(const i32x4*)(rp + ko[s][0]), hi = *(const i32x4*)(rp + ko[s][1]);
-        a = mfma32_mx(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, (sc >> (8 * (2 * s + half))) & 0xFF,
-                      kvb[s], kvs[s], a);
+        a = mfma32_scale_byte<0, 0>(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, scw, 2 * s, kvb[s],
+                                    kvs[s], a);
       }
     }
     return a;
@@ -599,28 +600,29 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mx_kernel(
   // dS of one 32-key block b of the tile (this lane: query qrow, keys k0 + 32b + 8(j/4) + 4·half + j%4)
   auto ds_block = [&](const char* tb, int k0, int b, bool need_mask) __attribute__((always_inline)) {
     const int kr = 32 * b + r32;
-    const int ksc = *(const int*)(tb + C::OFF_KDSC + kr * 4);
-    const int vsc = *(const int*)(tb + C::OFF_VDSC + kr * 4);
+    // the key's four block scales; this lane's blocks are 2s + half (s = 0, 1): bytes 2s
+    const int ksc = *(const int*)(tb + C::OFF_KDSC + kr * 4) >> (8 * half);
+    const int vsc = *(const int*)(tb + C::OFF_VDSC + kr * 4) >> (8 * half);
     f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const char* vp = tb + C::OFF_VD + kr * 128;
       const i32x4 vlo = *(const i32x4*)(vp + ko[s][0]), vhi = *(const i32x4*)(vp + ko[s][1]);
       if constexpr (FP4) {
-        sacc = mfma32_mx_fp4(fp4_operand(*(const i32x4*)(tb + kr * (D / 2) + kq[s])),
-                             (ksc >> (8 * (2 * s + half))) & 0xFF, qa[s], qs[s], sacc);
+        sacc = mfma32_scale_byte<4, 4>(fp4_operand(*(const i32x4*)(tb + kr * (D / 2) + kq[s])), ksc, 2 * s, qa[s],
+                                       qs[s], sacc);
       } else if constexpr (FP6) {
-        sacc = mfma32_mx_fp6<F6>(fp6_operand(*(const i32x4*)(tb + kr * (D / 2) + kq[s]),
-                                         *(const i32x2*)(tb + 4096 + 16 * (64 * s + kr) + 8 * half)),
-                             (ksc >> (8 * (2 * s + half))) & 0xFF, qa[s], qs[s], sacc);
+        sacc = mfma32_scale_byte<F6, F6>(fp6_operand(*(const i32x4*)(tb + kr * (D / 2) + kq[s]),
+                                                 *(const i32x2*)(tb + 4096 + 16 * (64 * s + kr) + 8 * half)),
+                                     ksc, 2 * s, qa[s], qs[s], sacc);
       } else {
         const char* kp = tb + kr * 128;
         const i32x4 klo = *(const i32x4*)(kp + ko[s][0]), khi = *(const i32x4*)(kp + ko[s][1]);
-        sacc = mfma32_mx(i32x8{klo.x, klo.y, klo.z, klo.w, khi.x, khi.y, khi.z, khi.w},
-                         (ksc >> (8 * (2 * s + half))) & 0xFF, qa[s], qs[s], sacc);
+        sacc = mfma32_scale_byte<0, 0>(i32x8{klo.x, klo.y, klo.z, klo.w, khi.x, khi.y, khi.z, khi.w}, ksc, 2 * s,
+                                       qa[s], qs[s], sacc);
       }
-      pacc = mfma32_mx(i32x8{vlo.x, vlo.y, vlo.z, vlo.w, vhi.x, vhi.y, vhi.z, vhi.w},
-                       (vsc >> (8 * (2 * s + half))) & 0xFF, oa[s], os[s], pacc);
+      pacc = mfma32_scale_byte<0, 0>(i32x8{vlo.x, vlo.y, vlo.z, vlo.w, vhi.x, vhi.y, vhi.z, vhi.w}, vsc, 2 * s,
+                                     oa[s], os[s], pacc);
     }
     if (need_mask) {                     // wave-uniform: diagonal or document-end tiles
       const int r = (causal ? qrow : L - 1) - (k0 + 32 * b + 4 * half);   // keys above are masked

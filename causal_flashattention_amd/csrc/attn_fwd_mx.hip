@@ -237,22 +237,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
       int ksc[2];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) ksc[b] = *(const int*)(tb + C::OFF_KSC + (32 * b + r32) * 4);
+      for (int b = 0; b < 2; ++b) ksc[b] = *(const int*)(tb + C::OFF_KSC + (32 * b + r32) * 4) >> (8 * half);
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
           const char* kr = tb + (32 * b + r32) * C::KROW;
-          const int sa = (ksc[b] >> (8 * (2 * s + half))) & 0xFF;
+          // key block 2s + half's scale: byte 2s of the shifted word (the product's byte select)
           if constexpr (FP4) {
-            sacc[b] = mfma32_mx_fp4(fp4_operand(*(const i32x4*)(kr + ko[s][0])), sa, qa[s], qs[s], sacc[b]);
+            sacc[b] = mfma32_scale_byte<4, 4>(fp4_operand(*(const i32x4*)(kr + ko[s][0])), ksc[b], 2 * s, qa[s], qs[s],
+                                              sacc[b]);
           } else if constexpr (FP6) {
             const i32x2 hi = *(const i32x2*)(tb + C::OFF_KB + 16 * (64 * s + 32 * b + r32) + 8 * half);
-            sacc[b] = mfma32_mx_fp6<QF>(fp6_operand(*(const i32x4*)(kr + ko[s][0]), hi), sa, qa[s], qs[s], sacc[b]);
+            sacc[b] = mfma32_scale_byte<QF, QF>(fp6_operand(*(const i32x4*)(kr + ko[s][0]), hi), ksc[b], 2 * s, qa[s],
+                                                qs[s], sacc[b]);
           } else {
             const i32x4 lo = *(const i32x4*)(kr + ko[s][0]);
             const i32x4 hi = *(const i32x4*)(kr + ko[s][1]);
-            sacc[b] = mfma32_mx(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, sa, qa[s], qs[s], sacc[b]);
+            sacc[b] = mfma32_scale_byte<0, 0>(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, ksc[b], 2 * s,
+                                              qa[s], qs[s], sacc[b]);
           }
         }
       // ---- online softmax: maximum on the raw scores (scale_log2 > 0), scale folded into the

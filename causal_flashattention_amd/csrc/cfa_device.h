@@ -141,6 +141,19 @@ __device__ inline f32x16 mfma32_mx_fp6(i32x8 a, int sa, i32x8 b, int sb, f32x16 
 }
 __device__ inline i32x8 fp6_operand(i32x4 lo, i32x2 hi) { return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, 0, 0}; }
 
+// Scaled MFMA (A format FA, B format FB) whose A scale is byte `sel` of `sa_word`, picked by the
+// instruction's byte select, so a lane holding a token's four block scales in one word needs no
+// shift and mask per product. `sel` must be a compile-time constant after unrolling.
+template <int FA, int FB>
+__device__ inline f32x16 mfma32_scale_byte(i32x8 a, int sa_word, int sel, i32x8 b, int sb, f32x16 c) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, sa_word, 0, sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 1, sa_word, 0, sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 2, sa_word, 0, sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 3, sa_word, 0, sb);
+  }
+}
+
 // Four floats -> four E4M3 bytes (round to nearest even; inputs must already lie in ±448).
 // The first conversion writes bytes 0-1 and keeps bytes 2-3 of its `old` operand, which the
 // second one overwrites: any register will do, and b's (usually dead afterwards) saves a move.
