@@ -205,7 +205,9 @@ __global__ __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW) void attn_fwd_bf16_
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
       }
-      float ls4[4] = {0.f, 0.f, 0.f, 0.f};          // four partial row sums (short add chains)
+      // four partial row sums (short add chains), each started by its first term rather than by
+      // adding it to 0 (the terms are >= +0, so the sums are the same)
+      float ls4[4];
       bf16x8 pf[4];
       const float m_use = (CROSS && m_run == -INFINITY) ? 0.f : m_run;   // all -inf scores -> p = 0
 #pragma unroll
@@ -214,7 +216,8 @@ __global__ __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW) void attn_fwd_bf16_
         for (int j = 0; j < 16; j += 2) {
           const float p0 = exp2_fast(fmaf(sacc[b][j], scale_log2, -m_use));
           const float p1 = exp2_fast(fmaf(sacc[b][j + 1], scale_log2, -m_use));
-          ls4[(j >> 1) & 3] += p0 + p1;
+          if (b == 0 && j < 8) ls4[j >> 1] = p0 + p1;
+          else ls4[(j >> 1) & 3] += p0 + p1;
           const uint32_t pk = pack_bf16x2(p0, p1);
           i32x4 u = __builtin_bit_cast(i32x4, pf[2 * b + (j >> 3)]);
           u[(j & 7) >> 1] = (int)pk;

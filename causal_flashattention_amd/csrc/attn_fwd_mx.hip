@@ -284,14 +284,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(
       const bool diag = per_lane(tile_is_diag(kt));
       // diagonal tiles: P̃ (bf16); other tiles: P̃·2^8 (E4M3 with scale 2^-8)
       const float bias = diag ? -m_run : 8.f - m_run;
-      float ls4[4] = {0.f, 0.f, 0.f, 0.f};          // four partial row sums (short add chains)
+      // four partial row sums (short add chains), each started by its first term rather than by
+      // adding it to 0 (the terms are >= +0, so the sums are the same)
+      float ls4[4];
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const float pj = exp2_fast(fmaf(sacc[b][j], scale_log2, bias));
           sacc[b][j] = pj;
-          ls4[j & 3] += pj;
+          if (b == 0 && j < 4) ls4[j] = pj;
+          else ls4[j & 3] += pj;
         }
       const float ls = (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
       l_run += diag ? ls : ls * (1.f / 256.f);
